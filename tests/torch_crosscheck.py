@@ -1,0 +1,66 @@
+"""An independent CPU formulation of the Block Transformer, built from torch's
+library routines (layer_norm, scaled_dot_product_attention, gelu, linear) and a
+complex-number rotary embedding.  It is used only to cross-check the numpy
+oracle; it shares no code with it.
+
+It follows the same pages ("Block Transformer: Global-to-Local Language Modeling
+for Fast Inference", §3.2 and §3.4): a concatenating embedder, a causal block
+decoder, a prefix projection and a causal token decoder over [prefix, block].
+"""
+from __future__ import annotations
+
+import torch
+import torch.nn.functional as F
+
+
+def _t(a):
+    return torch.as_tensor(a, dtype=torch.float64)
+
+
+def rope_complex(x: torch.Tensor, pos: torch.Tensor, base: float) -> torch.Tensor:
+    """x [B, H, n, d]: rotate the complex numbers x_i + 1j*x_{i+d/2} by exp(1j*pos*base^(-2i/d))."""
+    d = x.shape[-1]
+    z = torch.complex(x[..., : d // 2], x[..., d // 2:])
+    freqs = base ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+    rot = torch.polar(torch.ones(len(pos), d // 2, dtype=torch.float64),
+                      pos.to(torch.float64)[:, None] * freqs[None, :])
+    z = z * rot
+    return torch.cat([z.real, z.imag], dim=-1)
+
+
+def layer(W, name, h, pos, n_heads, eps, base):
+    B, n, D = h.shape
+    dh = D // n_heads
+    a = F.layer_norm(h, (D,), _t(W[f"{name}.ln1.g"]), _t(W[f"{name}.ln1.b"]), eps)
+    m = F.layer_norm(h, (D,), _t(W[f"{name}.ln2.g"]), _t(W[f"{name}.ln2.b"]), eps)
+    qkv = F.linear(a, _t(W[f"{name}.attn.qkv.w"]).T, _t(W[f"{name}.attn.qkv.b"]))
+    q, k, v = qkv.split(D, dim=-1)
+    heads = lambda t: t.reshape(B, n, n_heads, dh).transpose(1, 2)   # noqa: E731
+    q, k, v = heads(q), heads(k), heads(v)
+    q, k = rope_complex(q, pos, base), rope_complex(k, pos, base)
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+    o = o.transpose(1, 2).reshape(B, n, D)
+    attn = F.linear(o, _t(W[f"{name}.attn.out.w"]).T, _t(W[f"{name}.attn.out.b"]))
+    u = F.gelu(F.linear(m, _t(W[f"{name}.mlp.up.w"]).T, _t(W[f"{name}.mlp.up.b"])), approximate="none")
+    mlp = F.linear(u, _t(W[f"{name}.mlp.down.w"]).T, _t(W[f"{name}.mlp.down.b"]))
+    return h + attn + mlp
+
+
+def stack(W, pre, n_layers, h, cfg):
+    pos = torch.arange(h.shape[1])
+    for l in range(n_layers):
+        h = layer(W, f"{pre}.{l}", h, pos, cfg.n_heads, cfg.ln_eps, cfg.rope_base)
+    return F.layer_norm(h, (cfg.d_model,), _t(W[f"{pre}.lnf.g"]), _t(W[f"{pre}.lnf.b"]), cfg.ln_eps)
+
+
+def block_logits(W, cfg, tokens, k):
+    """Logits [B, L_B, V] for the L_B tokens of block k >= 1 of ``tokens`` [B, S] (teacher forced)."""
+    L, P, D = cfg.block_len, cfg.prefix_len, cfg.d_model
+    x = torch.as_tensor(tokens, dtype=torch.long)
+    B = x.shape[0]
+    e = _t(W["emb_block"])[x[:, : k * L]].reshape(B, k, D)
+    c = stack(W, "blk", cfg.n_block_layers, e, cfg)[:, k - 1]
+    prefix = F.linear(c, _t(W["prefix.w"]).T, _t(W["prefix.b"])).reshape(B, P, D)
+    z = torch.cat([prefix, _t(W["emb_token"])[x[:, k * L: k * L + L - 1]]], dim=1)
+    y = stack(W, "tok", cfg.n_token_layers, z, cfg)[:, P - 1:]
+    return (y @ _t(W["head.w"]).T).numpy()
