@@ -13,6 +13,8 @@ inputs stand in for them at the same shapes (timing does not depend on values).
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace, asdict
 from typing import Dict, List, Tuple
 
@@ -152,6 +154,20 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return x
 
 
+def _draw(cfg: Config, seed: int, i: int, shape, kind: str, ln_jitter: bool, std: float) -> np.ndarray:
+    rng = np.random.default_rng([seed, i])
+    if kind == "normal" or ln_jitter:
+        a = rng.standard_normal(shape, dtype=np.float32)
+        a *= np.float32(std)
+        if kind == "ln_gain":
+            a += np.float32(1.0)
+    elif kind == "ln_gain":
+        a = np.ones(shape, np.float32)
+    else:
+        a = np.zeros(shape, np.float32)
+    return round_bf16(a) if cfg.dtype == "bf16" else a
+
+
 def make_weights(cfg: Config, seed: int = 0, ln_jitter: bool = False,
                  std: float = 0.02) -> Dict[str, np.ndarray]:
     """Random-init parameters as float32 arrays (bf16-representable when cfg.dtype is bf16).
@@ -159,23 +175,14 @@ def make_weights(cfg: Config, seed: int = 0, ln_jitter: bool = False,
     Tensor #i of weight_specs() is drawn from numpy.random.default_rng([seed, i]).
     LayerNorm gains are 1 and biases 0, unless ``ln_jitter`` draws them as
     1 + N(0, std^2) and N(0, std^2) to exercise the affine part of LayerNorm.
+    Tensors are drawn on a thread pool; each has its own generator, so the
+    result does not depend on the scheduling.
     """
-    out: Dict[str, np.ndarray] = {}
-    for i, (name, shape, kind) in enumerate(weight_specs(cfg)):
-        rng = np.random.default_rng([seed, i])
-        if kind == "normal" or ln_jitter:
-            a = rng.standard_normal(shape, dtype=np.float32)
-            a *= np.float32(std)
-            if kind == "ln_gain":
-                a += np.float32(1.0)
-        elif kind == "ln_gain":
-            a = np.ones(shape, np.float32)
-        else:
-            a = np.zeros(shape, np.float32)
-        if cfg.dtype == "bf16":
-            a = round_bf16(a)
-        out[name] = a
-    return out
+    specs = weight_specs(cfg)
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        arrays = list(ex.map(lambda t: _draw(cfg, seed, t[0], t[1][1], t[1][2], ln_jitter, std),
+                             enumerate(specs)))
+    return {name: a for (name, _, _), a in zip(specs, arrays)}
 
 
 def make_prompt(cfg: Config, batch: int | None = None, T: int | None = None,

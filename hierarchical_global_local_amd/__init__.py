@@ -1,0 +1,231 @@
+"""Block Transformer batched inference on one MI355X (gfx950).
+
+A thin ctypes binding over libbt.so (include/bt.h): it marshals arguments and
+owns device memory through PyTorch tensors; every step of the inference path
+runs in the library's HIP kernels.  Importing this package does not load the
+library; the first use does, and fails loudly if it has not been built
+(``python -m hierarchical_global_local_amd.build`` or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Iterable, List, Mapping, Optional, Sequence
+
+import numpy as np
+
+__all__ = ["BtConfig", "BlockTransformer", "lib", "pack_weights", "weight_names", "BtError",
+           "BT_FP32", "BT_BF16", "PROFILE_KINDS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libbt.so")
+
+BT_FP32, BT_BF16 = 0, 1
+PROFILE_KINDS = ["embed", "layernorm", "gemm_qkv_up", "gemm_out_down", "gemm_prefix", "gemm_head",
+                 "attn_prefill", "rope_scatter", "attn_block_decode", "attn_local", "finalize"]
+
+
+class BtError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libbt error {code}: {msg}")
+        self.code = code
+
+
+class BtConfig(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("d_mlp", ctypes.c_int32), ("n_block_layers", ctypes.c_int32), ("n_token_layers", ctypes.c_int32),
+                ("block_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32), ("pad_id", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+    @classmethod
+    def make(cls, model, max_batch: int, max_tokens: int) -> "BtConfig":
+        """From any object with the model fields (vocab, d_model, ..., dtype "fp32"/"bf16")."""
+        return cls(model.vocab, model.d_model, model.n_heads, model.d_mlp, model.n_block_layers,
+                   model.n_token_layers, model.block_len, model.prefix_len, max_batch, max_tokens,
+                   BT_FP32 if model.dtype == "fp32" else BT_BF16, model.pad_id, model.ln_eps, model.rope_base)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libbt.so; raises if it was not built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build the HIP library first "
+                          "(python -m hierarchical_global_local_amd.build)")
+    L = ctypes.CDLL(_LIB_PATH)
+    c_p, c_i32, c_sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(BtConfig)
+    L.bt_weights_bytes.argtypes, L.bt_weights_bytes.restype = [cfgp], c_sz
+    L.bt_workspace_bytes.argtypes, L.bt_workspace_bytes.restype = [cfgp], c_sz
+    L.bt_init.argtypes = [cfgp, c_p, c_p, c_sz, c_p, ctypes.POINTER(c_p)]
+    L.bt_prefill.argtypes = [c_p, c_p, c_i32, c_i32, c_p, c_p]
+    L.bt_decode_step.argtypes = [c_p, c_p, c_p]
+    L.bt_cache_lengths.argtypes = [c_p, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
+    L.bt_workspace_region.argtypes = [cfgp, c_i32, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz), ctypes.POINTER(c_i32)]
+    L.bt_destroy.argtypes = [c_p]
+    L.bt_last_error.argtypes, L.bt_last_error.restype = [], ctypes.c_char_p
+    L.bt_profile_enable.argtypes = [c_p, c_i32]
+    L.bt_profile_read.argtypes = [c_p, c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.bt_test_gemm.argtypes = [c_i32, c_p, c_p, c_p, c_i32, c_i32, c_i32, ctypes.c_float, c_p]
+    for f in ("bt_init", "bt_prefill", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
+              "bt_profile_enable", "bt_profile_read", "bt_test_gemm"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def check(code: int) -> None:
+    if code != 0:
+        raise BtError(code, lib().bt_last_error().decode())
+
+
+def weight_names(model) -> List[str]:
+    """Canonical tensor names in weights-blob order (include/bt.h)."""
+    layer = ["ln1.g", "ln1.b", "attn.qkv.w", "attn.qkv.b", "attn.out.w", "attn.out.b", "ln2.g", "ln2.b",
+             "mlp.up.w", "mlp.up.b", "mlp.down.w", "mlp.down.b"]
+    names = ["emb_block"]
+    names += [f"blk.{l}.{n}" for l in range(model.n_block_layers) for n in layer]
+    names += ["blk.lnf.g", "blk.lnf.b", "prefix.w", "prefix.b", "emb_token"]
+    names += [f"tok.{l}.{n}" for l in range(model.n_token_layers) for n in layer]
+    names += ["tok.lnf.g", "tok.lnf.b", "head.w"]
+    return names
+
+
+def pack_weights(model, weights: Mapping[str, np.ndarray]) -> np.ndarray:
+    """Concatenate the parameters into the canonical blob (uint8), fp32 or bf16 (round to nearest even)."""
+    import torch
+    parts = []
+    for name in weight_names(model):
+        a = torch.from_numpy(np.ascontiguousarray(weights[name], dtype=np.float32)).reshape(-1)
+        if model.dtype == "bf16":
+            a = a.to(torch.bfloat16)
+        parts.append(a.view(torch.uint8))
+    return torch.cat(parts).numpy()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class BlockTransformer:
+    """One model instance bound to a CUDA/HIP stream.  Device memory is owned by torch tensors."""
+
+    def __init__(self, model, weights: Mapping[str, np.ndarray], max_batch: int, max_tokens: int,
+                 device: str = "cuda:0", stream=None):
+        import torch
+        self.torch = torch
+        L = lib()
+        self.model = model
+        self.cfg = BtConfig.make(model, max_batch, max_tokens)
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        wbytes = L.bt_weights_bytes(ctypes.byref(self.cfg))
+        if wbytes == 0:
+            raise BtError(-1, L.bt_last_error().decode())
+        blob = pack_weights(model, weights)
+        if blob.nbytes != wbytes:
+            raise BtError(-1, f"packed weights are {blob.nbytes} bytes, the library expects {wbytes}")
+        ws_bytes = L.bt_workspace_bytes(ctypes.byref(self.cfg))
+        with torch.cuda.stream(self.stream):
+            d_blob = torch.from_numpy(blob).to(self.device)
+            self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        check(L.bt_init(ctypes.byref(self.cfg), d_blob.data_ptr(), self.workspace.data_ptr(), ws_bytes,
+                        self.stream.cuda_stream, ctypes.byref(h)))
+        self.stream.synchronize()
+        del d_blob
+        self.h = h
+        self.batch = 0
+
+    def close(self) -> None:
+        if getattr(self, "h", None):
+            lib().bt_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------ inference
+    def prefill(self, prompt, out=None, logits=None):
+        """prompt: int32 device tensor [B, T]; writes the first generated ids into ``out`` [B]."""
+        torch = self.torch
+        assert prompt.dtype == torch.int32 and prompt.is_contiguous() and prompt.dim() == 2
+        B, T = prompt.shape
+        if out is None:
+            out = torch.empty(B, dtype=torch.int32, device=self.device)
+        check(lib().bt_prefill(self.h, prompt.data_ptr(), B, T, out.data_ptr(), _ptr(logits)))
+        self.batch = B
+        return out
+
+    def decode_step(self, out=None, logits=None):
+        torch = self.torch
+        if out is None:
+            out = torch.empty(self.batch, dtype=torch.int32, device=self.device)
+        check(lib().bt_decode_step(self.h, out.data_ptr(), _ptr(logits)))
+        return out
+
+    def generate(self, prompt, G: int, logits_steps: Iterable[int] = ()):
+        """Greedy generation of G tokens: ids [G, B] (device int32) and {step: logits [B, V] fp32}."""
+        torch = self.torch
+        B = prompt.shape[0]
+        steps = set(int(s) for s in logits_steps)
+        ids = torch.empty((G, B), dtype=torch.int32, device=self.device)
+        logits: Dict[int, "torch.Tensor"] = {}
+        with torch.cuda.stream(self.stream):
+            for g in range(G):
+                lg = None
+                if g in steps:
+                    lg = torch.empty((B, self.model.vocab), dtype=torch.float32, device=self.device)
+                    logits[g] = lg
+                if g == 0:
+                    self.prefill(prompt, ids[0], lg)
+                else:
+                    self.decode_step(ids[g], lg)
+        return ids, logits
+
+    # ------------------------------------------------------------------ introspection
+    def cache_lengths(self):
+        a, b = ctypes.c_int32(), ctypes.c_int32()
+        check(lib().bt_cache_lengths(self.h, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
+
+    def cache_view(self, which: int):
+        """Block-KV (which=0) or local-KV (1) region as a typed tensor view, plus its per-head capacity."""
+        torch = self.torch
+        off, nb, cap = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+        check(lib().bt_workspace_region(ctypes.byref(self.cfg), which, ctypes.byref(off), ctypes.byref(nb),
+                                        ctypes.byref(cap)))
+        dt = torch.float32 if self.model.dtype == "fp32" else torch.float16
+        raw = self.workspace[off.value: off.value + nb.value]
+        return raw.view(dt), cap.value
+
+    def profile(self, on: bool) -> None:
+        check(lib().bt_profile_enable(self.h, 1 if on else 0))
+
+    def profile_read(self) -> Dict[str, tuple]:
+        n = len(PROFILE_KINDS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        check(lib().bt_profile_read(self.h, n, ms, cnt))
+        return {k: (ms[i], cnt[i]) for i, k in enumerate(PROFILE_KINDS)}
+
+
+def gemm(a, w, scale: float = 1.0, stream=None):
+    """C = scale * a @ w.T in fp32 through the library's GEMM kernels (a, w: fp32 or fp16 device tensors)."""
+    import torch
+    assert a.dtype == w.dtype and a.dtype in (torch.float32, torch.float16)
+    M, K = a.shape
+    N = w.shape[0]
+    c = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    st = stream if stream is not None else torch.cuda.current_stream(a.device)
+    check(lib().bt_test_gemm(BT_FP32 if a.dtype == torch.float32 else BT_BF16, a.data_ptr(), w.data_ptr(),
+                             c.data_ptr(), M, N, K, scale, st.cuda_stream))
+    return c

@@ -1,0 +1,629 @@
+// Host orchestrator and C-ABI of libbt: config validation, workspace layout, weight repack,
+// and the per-call launch schedules of prefill and decode.
+//
+// The schedules follow "Block Transformer: Global-to-Local Language Modeling for Fast Inference"
+// (summary page, §3.2 and §3.4): prefill embeds all prompt blocks and runs the block decoder over
+// them (writing the block-KV cache), then runs the token decoder over the P prefix slots only;
+// each decode step either runs one token-decoder position against the local KV, or — when the
+// previous L_B tokens complete a block — embeds that block, runs one block-decoder position
+// against the block-KV cache and restarts the token decoder from a fresh prefix.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "bt.h"
+#include "bt_internal.h"
+#include "bt_test.h"
+
+namespace {
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+}  // namespace
+
+namespace bt {
+
+std::string plan_layout(const bt_config& c, Layout& lo) {
+  if (c.dtype != BT_FP32 && c.dtype != BT_BF16) return "dtype must be BT_FP32 or BT_BF16";
+  if (c.vocab < 1 || c.d_model < 1 || c.n_heads < 1 || c.d_mlp < 1) return "vocab, d_model, n_heads, d_mlp must be >= 1";
+  if (c.d_model % c.n_heads) return "d_model must be a multiple of n_heads";
+  const int dh = c.d_model / c.n_heads;
+  const bool f32 = c.dtype == BT_FP32;
+  if (!(dh == 64 || dh == 128 || (f32 && dh == 32)))
+    return f32 ? "d_head must be 32, 64 or 128" : "d_head must be 64 or 128 for BT_BF16";
+  if (c.block_len < 1 || c.prefix_len < 1) return "block_len and prefix_len must be >= 1";
+  if (c.d_model % c.block_len) return "d_model must be a multiple of block_len";
+  if (c.prefix_len + c.block_len > 32) return "prefix_len + block_len must be <= 32";
+  if (c.n_block_layers < 1 || c.n_token_layers < 1) return "n_block_layers and n_token_layers must be >= 1";
+  if (c.d_model > 4096) return "d_model must be <= 4096";
+  if (!f32 && (c.d_model % 64 || c.d_mlp % 64)) return "BT_BF16 needs d_model and d_mlp multiples of 64";
+  if (c.max_batch < 1) return "max_batch must be >= 1";
+  if (c.max_tokens < c.block_len + 1) return "max_tokens must be > block_len";
+  if (!(c.ln_eps > 0.f) || !(c.rope_base > 0.f)) return "ln_eps and rope_base must be > 0";
+  const int nblk = (c.max_tokens + c.block_len - 1) / c.block_len;
+  if (nblk > 131072) return "max_tokens / block_len must be <= 131072";
+
+  lo.V = c.vocab;
+  lo.D = c.d_model;
+  lo.H = c.n_heads;
+  lo.dh = dh;
+  lo.F = c.d_mlp;
+  lo.L = c.block_len;
+  lo.P = c.prefix_len;
+  lo.Nb = c.n_block_layers;
+  lo.Nt = c.n_token_layers;
+  lo.De = c.d_model / c.block_len;
+  lo.Bmax = c.max_batch;
+  lo.max_tokens = c.max_tokens;
+  lo.f32 = f32;
+  lo.elem = f32 ? 4 : 2;
+  lo.tab_elem = f32 ? 4 : 2;
+  lo.ncap = (int)align_up((size_t)nblk, 64);
+  lo.lcap = lo.P + lo.L;
+  lo.npos = std::max(lo.ncap, lo.lcap);
+  lo.Vpad = (int)align_up((size_t)lo.V, 128);
+  lo.Mmax = std::max<int64_t>((int64_t)lo.Bmax * nblk, (int64_t)lo.Bmax * lo.P);
+
+  const size_t D = lo.D, F = lo.F, V = lo.V, P = lo.P, E = lo.elem, TE = lo.tab_elem;
+  // ---- canonical blob
+  size_t o = 0;
+  auto take = [&](size_t n) { size_t r = o; o += n * TE; return r; };
+  lo.bl_emb_block = take(V * lo.De);
+  auto blob_layer = [&]() {
+    Layout::BlobLayer b;
+    b.ln1g = take(D); b.ln1b = take(D); b.qkvw = take(D * 3 * D); b.qkvb = take(3 * D);
+    b.outw = take(D * D); b.outb = take(D); b.ln2g = take(D); b.ln2b = take(D);
+    b.upw = take(D * F); b.upb = take(F); b.downw = take(F * D); b.downb = take(D);
+    return b;
+  };
+  lo.bl_blk.clear();
+  lo.bl_tok.clear();
+  for (int l = 0; l < lo.Nb; ++l) lo.bl_blk.push_back(blob_layer());
+  lo.bl_lnf_blk_g = take(D);
+  lo.bl_lnf_blk_b = take(D);
+  lo.bl_prefix_w = take(D * P * D);
+  lo.bl_prefix_b = take(P * D);
+  lo.bl_emb_tok = take(V * D);
+  for (int l = 0; l < lo.Nt; ++l) lo.bl_tok.push_back(blob_layer());
+  lo.bl_lnf_tok_g = take(D);
+  lo.bl_lnf_tok_b = take(D);
+  lo.bl_head = take(V * D);
+  lo.bl_total = o;
+
+  // ---- workspace
+  size_t w = 0;
+  auto region = [&](size_t bytes) { size_t r = w; w = align_up(w + bytes, 256); return r; };
+  lo.emb_block = region(V * lo.De * TE);
+  lo.emb_tok = region(V * D * TE);
+  lo.head = region((size_t)lo.Vpad * D * E);
+  lo.lnf_blk = region(2 * D * 4);
+  lo.lnf_tok = region(2 * D * 4);
+  lo.prefix_w = region(P * D * D * E);
+  lo.prefix_b = region(P * D * 4);
+  lo.rope = region((size_t)lo.npos * (lo.dh / 2) * sizeof(float2));
+  auto layer = [&]() {
+    LayerOff L;
+    L.ln = region(4 * D * 4);
+    L.w1 = region((3 * D + F) * D * E);
+    L.b1 = region((3 * D + F) * 4);
+    L.w2 = region(D * (D + F) * E);
+    L.b2 = region(2 * D * 4);
+    return L;
+  };
+  lo.blk.clear();
+  lo.tok.clear();
+  for (int l = 0; l < lo.Nb; ++l) lo.blk.push_back(layer());
+  for (int l = 0; l < lo.Nt; ++l) lo.tok.push_back(layer());
+  lo.block_kv_bytes = (size_t)lo.Nb * 2 * lo.Bmax * lo.H * lo.ncap * lo.dh * E;
+  lo.local_kv_bytes = (size_t)lo.Nt * 2 * lo.Bmax * lo.H * lo.lcap * lo.dh * E;
+  lo.block_kv = region(lo.block_kv_bytes);
+  lo.local_kv = region(lo.local_kv_bytes);
+  const size_t M = (size_t)lo.Mmax;
+  lo.X = region(M * D * 4);
+  lo.LN = region(2 * M * D * E);
+  lo.QKV = region(M * 3 * D * E);
+  lo.ACT = region(M * (D + F) * E);
+  lo.part_bytes = (size_t)lo.Bmax * lo.H * 32 * (lo.dh + 2) * 4;
+  lo.part = region(lo.part_bytes);
+  lo.keys = region((size_t)lo.Bmax * 8);
+  lo.cur = region((size_t)lo.Bmax * lo.L * 4);
+  lo.total = w;
+  return "";
+}
+
+}  // namespace bt
+
+using namespace bt;
+
+struct bt_handle {
+  bt_config cfg;
+  Layout lo;
+  char* ws = nullptr;
+  hipStream_t st = nullptr;
+  int B = 0, Tp = 0;
+  int n_blocks = 0;   // block-KV entries per layer
+  int local_len = 0;  // local-KV entries per layer
+  int g = 0;          // tokens emitted since the prefill
+  bool ready = false, broken = false;
+  // optional per-kernel-class event timing
+  bool prof = false;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<std::pair<int, int>> ev_used;  // (kind, index of the start event)
+  size_t ev_next = 0;
+};
+
+namespace {
+
+enum ProfKind { PK_EMBED = 0, PK_LN, PK_GEMM_QKV, PK_GEMM_OUT, PK_GEMM_PREFIX, PK_GEMM_HEAD, PK_ATTN_PREFILL,
+                PK_ROPE_SCATTER, PK_ATTN_DECODE, PK_ATTN_LOCAL, PK_FINALIZE, PK_COUNT };
+
+struct Prof {
+  bt_handle* h;
+  int kind;
+  int idx = -1;
+  Prof(bt_handle* h_, int k) : h(h_), kind(k) {
+    if (!h->prof) return;
+    if (h->ev_next + 2 > h->ev_pool.size()) {
+      for (int i = 0; i < 256; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        h->ev_pool.push_back(e);
+      }
+    }
+    idx = (int)h->ev_next;
+    h->ev_next += 2;
+    (void)hipEventRecord(h->ev_pool[idx], h->st);
+  }
+  ~Prof() {
+    if (idx < 0) return;
+    (void)hipEventRecord(h->ev_pool[idx + 1], h->st);
+    h->ev_used.push_back({kind, idx});
+  }
+};
+
+inline char* P_(bt_handle* h, size_t off) { return h->ws + off; }
+
+int hip_fail(bt_handle* h, hipError_t e, const char* what) {
+  if (h) h->broken = true;
+  return fail(BT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define BT_CHECK(h, expr, what)                    \
+  do {                                             \
+    hipError_t e_ = (expr);                        \
+    if (e_ != hipSuccess) return hip_fail(h, e_, what); \
+  } while (0)
+
+void* block_k(bt_handle* h, int l) {
+  const Layout& lo = h->lo;
+  size_t per = (size_t)lo.Bmax * lo.H * lo.ncap * lo.dh * lo.elem;
+  return P_(h, lo.block_kv + (size_t)(2 * l) * per);
+}
+void* block_v(bt_handle* h, int l) {
+  const Layout& lo = h->lo;
+  size_t per = (size_t)lo.Bmax * lo.H * lo.ncap * lo.dh * lo.elem;
+  return P_(h, lo.block_kv + (size_t)(2 * l + 1) * per);
+}
+void* local_k(bt_handle* h, int l) {
+  const Layout& lo = h->lo;
+  size_t per = (size_t)lo.Bmax * lo.H * lo.lcap * lo.dh * lo.elem;
+  return P_(h, lo.local_kv + (size_t)(2 * l) * per);
+}
+void* local_v(bt_handle* h, int l) {
+  const Layout& lo = h->lo;
+  size_t per = (size_t)lo.Bmax * lo.H * lo.lcap * lo.dh * lo.elem;
+  return P_(h, lo.local_kv + (size_t)(2 * l + 1) * per);
+}
+void* ln_buf(bt_handle* h, int which) {
+  const Layout& lo = h->lo;
+  return P_(h, lo.LN + (size_t)which * lo.Mmax * lo.D * lo.elem);
+}
+
+float wscale(const Layout& lo) { return lo.f32 ? 1.0f : kWeightUnscale; }
+
+// LN1/LN2 -> [q|k|v|up] GEMM with bias (+GELU on the up part)
+int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows) {
+  const Layout& lo = h->lo;
+  const float* lnp = (const float*)P_(h, w.ln);
+  {
+    Prof p(h, PK_LN);
+    BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), rows, lo.D, 1, 0, lnp, ln_buf(h, 0), lnp + 2 * lo.D,
+                                 ln_buf(h, 1), lo.f32, h->cfg.ln_eps, nullptr, 0, h->st),
+             "layernorm");
+  }
+  Epi ep{};
+  ep.wscale = wscale(lo);
+  ep.bias = (const float*)P_(h, w.b1);
+  ep.out0 = P_(h, lo.QKV);
+  ep.ld0 = 3 * lo.D;
+  ep.out1 = P_(h, lo.ACT);
+  ep.ld1 = lo.D + lo.F;
+  ep.n_split = 3 * lo.D;
+  ep.act_col0 = lo.D;
+  Prof p(h, PK_GEMM_QKV);
+  BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), rows, 3 * lo.D + lo.F, lo.D,
+                          EPI_QKV_GELU, ep, h->st),
+           "gemm qkv|up");
+  return BT_OK;
+}
+
+// [attn | gelu(up)] x [W_o ; W_down] + b_o + b_down added into the residual stream
+int run_out(bt_handle* h, const LayerOff& w, int rows) {
+  const Layout& lo = h->lo;
+  Epi ep{};
+  ep.wscale = wscale(lo);
+  ep.bias = (const float*)P_(h, w.b2);
+  ep.bias2 = (const float*)P_(h, w.b2) + lo.D;
+  ep.out0 = P_(h, lo.X);
+  ep.ld0 = lo.D;
+  Prof p(h, PK_GEMM_OUT);
+  BT_CHECK(h, launch_gemm(lo.f32, P_(h, lo.ACT), nullptr, lo.D + lo.F, P_(h, w.w2), rows, lo.D, lo.D + lo.F,
+                          EPI_RESID, ep, h->st),
+           "gemm out|down");
+  return BT_OK;
+}
+
+// token decoder over new local slots [s0, s0 + m) of every row (rows = B * m in X)
+int run_token_decoder(bt_handle* h, int m, int s0) {
+  const Layout& lo = h->lo;
+  const int rows = h->B * m;
+  for (int l = 0; l < lo.Nt; ++l) {
+    int r = run_ln_qkv(h, lo.tok[l], rows);
+    if (r) return r;
+    {
+      Prof p(h, PK_ATTN_LOCAL);
+      BT_CHECK(h, launch_local_attention(lo.f32, P_(h, lo.QKV), h->B, m, s0, lo.D, lo.H, lo.dh,
+                                         (const float2*)P_(h, lo.rope), local_k(h, l), local_v(h, l), lo.lcap,
+                                         P_(h, lo.ACT), lo.D + lo.F, h->st),
+               "local attention");
+    }
+    r = run_out(h, lo.tok[l], rows);
+    if (r) return r;
+  }
+  return BT_OK;
+}
+
+// final LN of the token decoder at rows (b, slot) of X [B][m][D], then classifier + argmax
+int run_head(bt_handle* h, int m, int slot, int j, int32_t* d_next, float* d_logits) {
+  const Layout& lo = h->lo;
+  {
+    Prof p(h, PK_LN);
+    BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_tok),
+                                 ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps,
+                                 (unsigned long long*)P_(h, lo.keys), h->B, h->st),
+             "final layernorm");
+  }
+  Epi ep{};
+  ep.wscale = wscale(lo);
+  ep.out0 = d_logits;
+  ep.ld0 = lo.V;
+  ep.n_valid = lo.V;
+  ep.keys = (unsigned long long*)P_(h, lo.keys);
+  {
+    Prof p(h, PK_GEMM_HEAD);
+    BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.head), h->B, lo.f32 ? lo.V : lo.Vpad, lo.D,
+                            EPI_ARGMAX, ep, h->st),
+             "classifier");
+  }
+  Prof p(h, PK_FINALIZE);
+  BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->B, d_next, (int32_t*)P_(h, lo.cur), lo.L,
+                              j, h->st),
+           "finalize");
+  return BT_OK;
+}
+
+// context embedding of rows (b, slot) of X [B][m][D] -> prefix rows X [B][P][D]
+int run_prefix(bt_handle* h, int m, int slot) {
+  const Layout& lo = h->lo;
+  {
+    Prof p(h, PK_LN);
+    BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_blk),
+                                 ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps, nullptr, 0, h->st),
+             "context layernorm");
+  }
+  Epi ep{};
+  ep.wscale = wscale(lo);
+  ep.bias = (const float*)P_(h, lo.prefix_b);
+  ep.out0 = P_(h, lo.X);
+  ep.ld0 = lo.P * lo.D;
+  Prof p(h, PK_GEMM_PREFIX);
+  BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.prefix_w), h->B, lo.P * lo.D, lo.D, EPI_STORE,
+                          ep, h->st),
+           "prefix projection");
+  return BT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bt_last_error(void) { return g_last_error.c_str(); }
+
+size_t bt_weights_bytes(const bt_config* cfg) {
+  if (!cfg) return (size_t)fail(0, "cfg is NULL");
+  Layout lo;
+  std::string e = plan_layout(*cfg, lo);
+  if (!e.empty()) return (size_t)fail(0, e);
+  return lo.bl_total;
+}
+
+size_t bt_workspace_bytes(const bt_config* cfg) {
+  if (!cfg) return (size_t)fail(0, "cfg is NULL");
+  Layout lo;
+  std::string e = plan_layout(*cfg, lo);
+  if (!e.empty()) return (size_t)fail(0, e);
+  return lo.total;
+}
+
+int bt_workspace_region(const bt_config* cfg, int32_t which, size_t* offset, size_t* bytes, int32_t* capacity) {
+  if (!cfg || !offset || !bytes || !capacity) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  Layout lo;
+  std::string e = plan_layout(*cfg, lo);
+  if (!e.empty()) return fail(BT_ERR_INVALID_ARG, e);
+  if (which == 0) {
+    *offset = lo.block_kv;
+    *bytes = lo.block_kv_bytes;
+    *capacity = lo.ncap;
+  } else if (which == 1) {
+    *offset = lo.local_kv;
+    *bytes = lo.local_kv_bytes;
+    *capacity = lo.lcap;
+  } else {
+    return fail(BT_ERR_INVALID_ARG, "which must be 0 (block KV) or 1 (local KV)");
+  }
+  return BT_OK;
+}
+
+int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size_t ws_bytes, void* hip_stream,
+            bt_handle** out) {
+  if (!cfg || !d_weights || !d_workspace || !out) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  *out = nullptr;
+  Layout lo;
+  std::string e = plan_layout(*cfg, lo);
+  if (!e.empty()) return fail(BT_ERR_INVALID_ARG, e);
+  if (ws_bytes < lo.total) return fail(BT_ERR_INVALID_ARG, "workspace smaller than bt_workspace_bytes");
+  if ((uintptr_t)d_workspace % 256) return fail(BT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if ((uintptr_t)d_weights % 16) return fail(BT_ERR_INVALID_ARG, "weights blob must be 16-byte aligned");
+  bt_handle* h = new (std::nothrow) bt_handle();
+  if (!h) return fail(BT_ERR_INVALID_ARG, "out of host memory");
+  h->cfg = *cfg;
+  h->lo = lo;
+  h->ws = (char*)d_workspace;
+  h->st = (hipStream_t)hip_stream;
+  const char* wb = (const char*)d_weights;
+  const bool bf = !lo.f32;
+  const bool f32 = lo.f32;
+  const float sc = f32 ? 1.0f : kWeightScale;
+  const int D = lo.D, F = lo.F;
+  auto fin = [&](hipError_t err, const char* what) -> int {
+    if (err == hipSuccess) return 0;
+    delete h;
+    return fail(BT_ERR_HIP, std::string("bt_init ") + what + ": " + hipGetErrorString(err));
+  };
+#define INIT_CHECK(expr, what) \
+  if (int r_ = fin((expr), what)) return r_;
+  // caches and step state start at zero: every value ever read from them is then finite
+  INIT_CHECK(hipMemsetAsync(h->ws + lo.block_kv, 0, lo.block_kv_bytes, h->st), "memset");
+  INIT_CHECK(hipMemsetAsync(h->ws + lo.local_kv, 0, lo.local_kv_bytes, h->st), "memset");
+  INIT_CHECK(hipMemsetAsync(h->ws + lo.cur, 0, (size_t)lo.Bmax * lo.L * 4, h->st), "memset");
+  INIT_CHECK(hipMemcpyAsync(h->ws + lo.emb_block, wb + lo.bl_emb_block, (size_t)lo.V * lo.De * lo.tab_elem,
+                            hipMemcpyDeviceToDevice, h->st),
+             "copy");
+  INIT_CHECK(hipMemcpyAsync(h->ws + lo.emb_tok, wb + lo.bl_emb_tok, (size_t)lo.V * D * lo.tab_elem,
+                            hipMemcpyDeviceToDevice, h->st),
+             "copy");
+  auto repack_layer = [&](const Layout::BlobLayer& s, const LayerOff& d) -> hipError_t {
+    hipError_t err;
+    float* ln = (float*)(h->ws + d.ln);
+    if ((err = launch_to_f32(wb + s.ln1g, bf, D, ln, h->st))) return err;
+    if ((err = launch_to_f32(wb + s.ln1b, bf, D, ln + D, h->st))) return err;
+    if ((err = launch_to_f32(wb + s.ln2g, bf, D, ln + 2 * D, h->st))) return err;
+    if ((err = launch_to_f32(wb + s.ln2b, bf, D, ln + 3 * D, h->st))) return err;
+    if ((err = launch_transpose_convert(wb + s.qkvw, bf, D, 3 * D, h->ws + d.w1, f32, D, 0, 0, sc, h->st))) return err;
+    if ((err = launch_transpose_convert(wb + s.upw, bf, D, F, h->ws + d.w1, f32, D, 3 * D, 0, sc, h->st))) return err;
+    float* b1 = (float*)(h->ws + d.b1);
+    if ((err = launch_to_f32(wb + s.qkvb, bf, 3 * D, b1, h->st))) return err;
+    if ((err = launch_to_f32(wb + s.upb, bf, F, b1 + 3 * D, h->st))) return err;
+    if ((err = launch_transpose_convert(wb + s.outw, bf, D, D, h->ws + d.w2, f32, D + F, 0, 0, sc, h->st))) return err;
+    if ((err = launch_transpose_convert(wb + s.downw, bf, F, D, h->ws + d.w2, f32, D + F, 0, D, sc, h->st)))
+      return err;
+    float* b2 = (float*)(h->ws + d.b2);
+    if ((err = launch_to_f32(wb + s.outb, bf, D, b2, h->st))) return err;
+    return launch_to_f32(wb + s.downb, bf, D, b2 + D, h->st);
+  };
+  for (int l = 0; l < lo.Nb; ++l) INIT_CHECK(repack_layer(lo.bl_blk[l], lo.blk[l]), "repack block layer");
+  for (int l = 0; l < lo.Nt; ++l) INIT_CHECK(repack_layer(lo.bl_tok[l], lo.tok[l]), "repack token layer");
+  float* lnf = (float*)(h->ws + lo.lnf_blk);
+  INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_blk_g, bf, D, lnf, h->st), "repack");
+  INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_blk_b, bf, D, lnf + D, h->st), "repack");
+  lnf = (float*)(h->ws + lo.lnf_tok);
+  INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_g, bf, D, lnf, h->st), "repack");
+  INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_b, bf, D, lnf + D, h->st), "repack");
+  INIT_CHECK(launch_transpose_convert(wb + lo.bl_prefix_w, bf, D, lo.P * D, h->ws + lo.prefix_w, f32, D, 0, 0, sc,
+                                      h->st),
+             "repack prefix");
+  INIT_CHECK(launch_to_f32(wb + lo.bl_prefix_b, bf, lo.P * D, (float*)(h->ws + lo.prefix_b), h->st), "repack");
+  INIT_CHECK(launch_convert_rows(wb + lo.bl_head, bf, lo.V, D, lo.Vpad, h->ws + lo.head, f32, sc, h->st),
+             "repack head");
+  INIT_CHECK(launch_rope_table((float2*)(h->ws + lo.rope), lo.npos, lo.dh, cfg->rope_base, h->st), "rope table");
+#undef INIT_CHECK
+  *out = h;
+  return BT_OK;
+}
+
+int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int32_t* d_next, float* d_logits) {
+  if (!h || !d_prompt || !d_next) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
+  const Layout& lo = h->lo;
+  if (B < 1 || T < 1) return fail(BT_ERR_INVALID_ARG, "B and T must be >= 1");
+  if (B > lo.Bmax) return fail(BT_ERR_CAPACITY, "B exceeds max_batch");
+  const int L = lo.L;
+  const int Tp = std::max(L, (T + L - 1) / L * L);
+  if ((int64_t)Tp + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "padded prompt + 1 exceeds max_tokens");
+  h->ready = false;
+  h->B = B;
+  h->Tp = Tp;
+  const int n0 = Tp / L;
+  const int M = B * n0;
+  {
+    Prof p(h, PK_EMBED);
+    BT_CHECK(h, launch_embed_prompt(d_prompt, B, T, Tp, h->cfg.pad_id, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De, L,
+                                    (float*)P_(h, lo.X), h->st),
+             "embed prompt");
+  }
+  for (int l = 0; l < lo.Nb; ++l) {
+    int r = run_ln_qkv(h, lo.blk[l], M);
+    if (r) return r;
+    {
+      Prof p(h, PK_ROPE_SCATTER);
+      BT_CHECK(h, launch_rope_scatter(lo.f32, P_(h, lo.QKV), B, n0, 0, lo.D, lo.H, lo.dh, (const float2*)P_(h, lo.rope),
+                                      block_k(h, l), block_v(h, l), lo.ncap, true, h->st),
+               "rope scatter");
+    }
+    {
+      Prof p(h, PK_ATTN_PREFILL);
+      BT_CHECK(h, launch_prefill_attention(lo.f32, P_(h, lo.QKV), B, n0, lo.D, lo.H, lo.dh,
+                                           (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
+                                           P_(h, lo.ACT), lo.D + lo.F, h->st),
+               "prefill attention");
+    }
+    r = run_out(h, lo.blk[l], M);
+    if (r) return r;
+  }
+  int r = run_prefix(h, n0, n0 - 1);
+  if (r) return r;
+  r = run_token_decoder(h, lo.P, 0);
+  if (r) return r;
+  r = run_head(h, lo.P, lo.P - 1, 0, d_next, d_logits);
+  if (r) return r;
+  h->n_blocks = n0;
+  h->local_len = lo.P;
+  h->g = 1;
+  h->ready = true;
+  return BT_OK;
+}
+
+int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
+  if (!h || !d_next) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
+  if (!h->ready) return fail(BT_ERR_STATE, "bt_decode_step before bt_prefill");
+  const Layout& lo = h->lo;
+  const int L = lo.L, P = lo.P;
+  if ((int64_t)h->Tp + h->g + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "max_tokens reached");
+  const int j = h->g % L;
+  if (j == 0) {
+    // the previous L_B emitted tokens complete a block: one block-decoder step
+    {
+      Prof p(h, PK_EMBED);
+      BT_CHECK(h, launch_embed_block((const int32_t*)P_(h, lo.cur), h->B, L, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De,
+                                     (float*)P_(h, lo.X), h->st),
+               "embed block");
+    }
+    const int n = h->n_blocks;
+    for (int l = 0; l < lo.Nb; ++l) {
+      int r = run_ln_qkv(h, lo.blk[l], h->B);
+      if (r) return r;
+      {
+        Prof p(h, PK_ATTN_DECODE);
+        BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, n, lo.D, lo.H, lo.dh,
+                                             (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
+                                             P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part), lo.part_bytes, h->st),
+                 "block attention decode");
+      }
+      r = run_out(h, lo.blk[l], h->B);
+      if (r) return r;
+    }
+    h->n_blocks = n + 1;
+    int r = run_prefix(h, 1, 0);
+    if (r) return r;
+    r = run_token_decoder(h, P, 0);
+    if (r) return r;
+    r = run_head(h, P, P - 1, 0, d_next, d_logits);
+    if (r) return r;
+    h->local_len = P;
+  } else {
+    // one token-decoder position at local slot P + j - 1
+    {
+      Prof p(h, PK_EMBED);
+      BT_CHECK(h, launch_embed_token((const int32_t*)P_(h, lo.cur), h->B, L, j - 1, P_(h, lo.emb_tok), !lo.f32, lo.V,
+                                     lo.D, (float*)P_(h, lo.X), h->st),
+               "embed token");
+    }
+    int r = run_token_decoder(h, 1, P + j - 1);
+    if (r) return r;
+    r = run_head(h, 1, 0, j, d_next, d_logits);
+    if (r) return r;
+    h->local_len = P + j;
+  }
+  h->g += 1;
+  return BT_OK;
+}
+
+int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_kv_len) {
+  if (!h || !block_kv_len || !local_kv_len) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  *block_kv_len = h->ready ? h->n_blocks : 0;
+  *local_kv_len = h->ready ? h->local_len : 0;
+  return BT_OK;
+}
+
+int bt_destroy(bt_handle* h) {
+  if (!h) return fail(BT_ERR_INVALID_ARG, "NULL handle");
+  for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
+  delete h;
+  return BT_OK;
+}
+
+// ---------------------------------------------------------------- profiling and test entry points
+
+int bt_profile_enable(bt_handle* h, int32_t on) {
+  if (!h) return fail(BT_ERR_INVALID_ARG, "NULL handle");
+  h->prof = on != 0;
+  h->ev_used.clear();
+  h->ev_next = 0;
+  return BT_OK;
+}
+
+int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* launches) {
+  if (!h || !total_ms || !launches || n_kinds < PK_COUNT) return fail(BT_ERR_INVALID_ARG, "bad argument");
+  for (int k = 0; k < n_kinds; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  hipError_t e = hipStreamSynchronize(h->st);
+  if (e != hipSuccess) return hip_fail(h, e, "profile sync");
+  for (auto& u : h->ev_used) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, h->ev_pool[u.second], h->ev_pool[u.second + 1]) == hipSuccess) {
+      total_ms[u.first] += ms;
+      launches[u.first] += 1;
+    }
+  }
+  h->ev_used.clear();
+  h->ev_next = 0;
+  return BT_OK;
+}
+
+int bt_test_gemm(int32_t dtype, const void* d_a, const void* d_w, float* d_c, int32_t M, int32_t N, int32_t K,
+                 float scale, void* stream) {
+  if (!d_a || !d_w || !d_c) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  if (M < 1 || N < 1 || K < 1) return fail(BT_ERR_INVALID_ARG, "M, N, K must be >= 1");
+  const bool f32 = dtype == BT_FP32;
+  if (!f32 && (K % 64 || N % 32)) return fail(BT_ERR_INVALID_ARG, "fp16 GEMM needs K % 64 == 0 and N % 32 == 0");
+  Epi ep{};
+  ep.wscale = scale;
+  ep.out0 = d_c;
+  ep.ld0 = N;
+  hipError_t e = launch_gemm(f32, d_a, nullptr, K, d_w, M, N, K, EPI_STORE, ep, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(BT_ERR_HIP, std::string("gemm: ") + hipGetErrorString(e));
+  return BT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,574 @@
+// Attention kernels of libbt.
+//
+//  * k_rope_scatter: rotary embedding of prompt keys and scatter of K / V into the block-KV cache
+//    (keys [slot][dh]; values transposed [dh][slot] so that the prefill P*V product and the decode
+//    value pass read 8 consecutive keys per 16-byte load).
+//  * k_flash_prefill: causal flash attention over block positions with MFMA (fp16 operands, fp32
+//    softmax); computes S^T = K Q^T so that the probabilities come out of the MFMA already in the
+//    operand layout of O^T = V^T P^T, with no LDS round trip.
+//  * k_attn_decode: memory-bound block-attention decode: one workgroup per (row, head, key split)
+//    streams K then V^T with 16-byte loads, wave-shuffle dot products, online softmax through LDS,
+//    split-KV partials merged by k_attn_combine with log-sum-exp weights.
+//  * k_local_attn: the token decoder's local attention over at most prefix + block entries, held
+//    in LDS by one wave per (row, head).
+//  * k_attn_naive: plain prefill attention for fp32 mode.
+#include "bt_internal.h"
+#include "device_common.h"
+
+namespace bt {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 8 consecutive elements as floats
+__device__ __forceinline__ void load8(const f16* p, float* o) {
+  half8 v = *(const half8*)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8(const float* p, float* o) {
+  float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+template <typename T>
+__device__ __forceinline__ T round_t(float v) { return from_f32<T>(v); }
+
+// ---------------------------------------------------------------- rotary + scatter (prefill)
+// grid (ceil(m/64), H, B); rows (b, i) of QKV [B*m][3D] go to cache slot s0 + i.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV, int m, int s0, int D, int H, int dh,
+                                                      const float2* __restrict__ rope, T* __restrict__ Kc,
+                                                      T* __restrict__ Vc, int cap, int vt) {
+  __shared__ T vtile[64][129];
+  const int h = blockIdx.y, b = blockIdx.z, i0 = blockIdx.x * 64;
+  const int half = dh / 2, tid = threadIdx.x;
+  const size_t bh = (size_t)b * H + h;
+  const int cnt = min(64, m - i0);
+  for (int e = tid; e < cnt * half; e += 256) {
+    const int si = e / half, c = e % half, i = i0 + si, slot = s0 + i;
+    const T* kr = QKV + ((size_t)b * m + i) * 3 * D + D + h * dh;
+    const float2 cs = rope[(size_t)slot * half + c];
+    const float x1 = (float)kr[c], x2 = (float)kr[c + half];
+    T* kd = Kc + (bh * cap + slot) * dh;
+    kd[c] = round_t<T>(x1 * cs.x - x2 * cs.y);
+    kd[c + half] = round_t<T>(x2 * cs.x + x1 * cs.y);
+  }
+  if (!vt) {
+    for (int e = tid; e < cnt * dh; e += 256) {
+      const int si = e / dh, d = e % dh, i = i0 + si;
+      Vc[(bh * cap + s0 + i) * dh + d] = QKV[((size_t)b * m + i) * 3 * D + 2 * D + h * dh + d];
+    }
+    return;
+  }
+  for (int e = tid; e < cnt * dh; e += 256) {
+    const int si = e / dh, d = e % dh;
+    vtile[si][d] = QKV[((size_t)b * m + i0 + si) * 3 * D + 2 * D + h * dh + d];
+  }
+  __syncthreads();
+  for (int e = tid; e < cnt * dh; e += 256) {
+    const int d = e / cnt, si = e % cnt;
+    Vc[(bh * dh + d) * cap + s0 + i0 + si] = vtile[si][d];
+  }
+}
+
+hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
+                               const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed, hipStream_t st) {
+  if (B <= 0 || m <= 0) return hipSuccess;
+  dim3 grid((m + 63) / 64, H, B);
+  if (f32)
+    hipLaunchKernelGGL(k_rope_scatter<float>, grid, dim3(256), 0, st, (const float*)QKV, m, s0, D, H, dh, rope,
+                       (float*)Kc, (float*)Vc, cap, (int)v_transposed);
+  else
+    hipLaunchKernelGGL(k_rope_scatter<f16>, grid, dim3(256), 0, st, (const f16*)QKV, m, s0, D, H, dh, rope, (f16*)Kc,
+                       (f16*)Vc, cap, (int)v_transposed);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- MFMA flash prefill (fp16)
+// grid (ceil(n/64), H, B), 4 waves x 16 queries.  MFMA 16x16x32 layouts (lane l, g = l / 16):
+//   A operand: row l % 16, k = 8g..8g+7;  B operand: column l % 16, same k;
+//   result:    column l % 16, rows 4g..4g+3.
+template <int DH>
+__global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ QKV, int n, int D, int H,
+                                                       const float2* __restrict__ rope, const f16* __restrict__ Kc,
+                                                       const f16* __restrict__ VTc, int cap, f16* __restrict__ ACT,
+                                                       int ld_act, float scale_log2) {
+  constexpr int KS = DH / 32;   // 32-wide dh slices of q and k
+  constexpr int MT = DH / 16;   // 16-row dh tiles of O^T
+  const int qt = gridDim.x - 1 - blockIdx.x;  // longest (latest) query tiles first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int q0 = qt * 64 + wave * 16;
+  if (q0 >= n) return;
+  const int qi = q0 + c16;
+  const int qrow = min(qi, n - 1);
+  const size_t bh = (size_t)b * H + h;
+  const f16* __restrict__ K = Kc + bh * cap * DH;
+  const f16* __restrict__ VT = VTc + bh * DH * cap;
+
+  // q^T fragments with the rotary embedding: lane holds dh indices 32*ks + 8g + e; the rotation
+  // partner (index +- DH/2) sits in slice ks +- KS/2 of the same lane.
+  half8 qf[KS];
+  {
+    float x[KS][8];
+    const f16* qp = QKV + ((size_t)b * n + qrow) * 3 * D + h * DH;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load8(qp + 32 * ks + 8 * g, x[ks]);
+    const float2* rp = rope + (size_t)qrow * (DH / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 cs = rp[32 * ks + 8 * g + e];
+        const float x1 = x[ks][e], x2 = x[ks + KS / 2][e];
+        qf[ks][e] = to_f16(x1 * cs.x - x2 * cs.y);
+        qf[ks + KS / 2][e] = to_f16(x2 * cs.x + x1 * cs.y);
+      }
+  }
+
+  float4_ o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) o[mt] = float4_{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+  const int klast = min(q0 + 15, n - 1);
+
+  for (int kb = 0; kb <= klast; kb += 64) {
+    float4_ s[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      s[nt] = float4_{0.f, 0.f, 0.f, 0.f};
+      const f16* kp = K + (size_t)(kb + nt * 16 + c16) * DH + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        half8 kf = *(const half8*)(kp + 32 * ks);
+        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], s[nt], 0, 0, 0);
+      }
+    }
+    // causal mask and tile maximum for this lane's query column
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb + nt * 16 + 4 * g + i;
+        float v = s[nt][i] * scale_log2;
+        v = key <= qi ? v : -INFINITY;
+        s[nt][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrun, mx);
+    const float corr = exp2f(mrun - mnew);
+    float ls = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(s[nt][i] - mnew);
+        s[nt][i] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    lrun = lrun * corr + ls;
+    mrun = mnew;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] *= corr;
+    // O^T += V^T P^T over two 32-key slices; slot e of the k dimension is key
+    // 32*sl + 4g + e (e < 4) or 32*sl + 16 + 4g + (e - 4), for both operands.
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      half8 pf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = (f16)s[2 * sl][e];
+        pf[4 + e] = (f16)s[2 * sl + 1][e];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f16* vp = VT + (size_t)(mt * 16 + c16) * cap + kb + 32 * sl + 4 * g;
+        const half4 v0 = *(const half4*)vp;
+        const half4 v1 = *(const half4*)(vp + 16);
+        half8 vf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[e] = v0[e];
+          vf[4 + e] = v1[e];
+        }
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[mt], 0, 0, 0);
+      }
+    }
+  }
+  if (qi < n) {
+    const float inv = 1.0f / lrun;
+    f16* out = ACT + ((size_t)b * n + qi) * ld_act + h * DH;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      half4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = to_f16(o[mt][i] * inv);
+      *(half4*)(out + mt * 16 + 4 * g) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- plain prefill attention (fp32)
+// grid (n, H, B), one wave per query; scores staged in dynamic LDS.
+template <typename T>
+__global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, int n, int D, int H, int dh,
+                                                   const float2* __restrict__ rope, const T* __restrict__ Kc,
+                                                   const T* __restrict__ VTc, int cap, T* __restrict__ ACT,
+                                                   int ld_act, float scale) {
+  extern __shared__ float sm[];
+  float* q = sm;          // [dh]
+  float* sc = sm + 128;   // [n]
+  const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const size_t bh = (size_t)b * H + h;
+  const T* qp = QKV + ((size_t)b * n + qi) * 3 * D + h * dh;
+  const int half = dh / 2;
+  for (int c = lane; c < half; c += 64) {
+    const float2 cs = rope[(size_t)qi * half + c];
+    const float x1 = (float)qp[c], x2 = (float)qp[c + half];
+    q[c] = x1 * cs.x - x2 * cs.y;
+    q[c + half] = x2 * cs.x + x1 * cs.y;
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int j = lane; j <= qi; j += 64) {
+    const T* kp = Kc + (bh * cap + j) * dh;
+    float d = 0.f;
+    for (int e = 0; e < dh; ++e) d = fmaf(q[e], (float)kp[e], d);
+    sc[j] = d * scale;
+    mx = fmaxf(mx, d * scale);
+  }
+  mx = wave_max(mx);
+  float l = 0.f;
+  for (int j = lane; j <= qi; j += 64) {
+    float p = expf(sc[j] - mx);
+    sc[j] = p;
+    l += p;
+  }
+  l = wave_sum(l);
+  __syncthreads();
+  for (int d = lane; d < dh; d += 64) {
+    const T* vp = VTc + (bh * dh + d) * cap;
+    float o = 0.f;
+    for (int j = 0; j <= qi; ++j) o = fmaf(sc[j], (float)vp[j], o);
+    ACT[((size_t)b * n + qi) * ld_act + h * dh + d] = round_t<T>(o / l);
+  }
+}
+
+hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int D, int H, int dh,
+                                    const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
+                                    int ld_act, hipStream_t st) {
+  if (B <= 0 || n <= 0) return hipSuccess;
+  const float scale = 1.0f / sqrtf((float)dh);
+  if (f32) {
+    size_t lds = (128 + (size_t)n) * sizeof(float);
+    hipLaunchKernelGGL(k_attn_naive<float>, dim3(n, H, B), dim3(64), lds, st, (const float*)QKV, n, D, H, dh, rope,
+                       (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale);
+    return hipGetLastError();
+  }
+  dim3 grid((n + 63) / 64, H, B);
+  if (dh == 64)
+    hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, (const f16*)QKV, n, D, H, rope, (const f16*)Kc,
+                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e);
+  else if (dh == 128)
+    hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, (const f16*)QKV, n, D, H, rope, (const f16*)Kc,
+                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- block-attention decode
+// grid (nsplit, H, B), 256 threads.  Keys [0, n) come from the cache, key n is the new one
+// (rotated here, appended to the cache by split 0 and used from LDS by the split that owns it).
+constexpr int kMaxChunk = 4096;
+constexpr int kMaxSplit = 32;
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, int n, int D, int H,
+                                                     const float2* __restrict__ rope, T* __restrict__ Kc,
+                                                     T* __restrict__ VTc, int cap, T* __restrict__ ACT, int ld_act,
+                                                     float* __restrict__ part, int nsplit, int chunk,
+                                                     float scale_log2) {
+  constexpr int LPK = DH / 8;      // lanes per key in the score pass (8 values each)
+  constexpr int KPW = 64 / LPK;    // keys per wave per step
+  constexpr int RPL = DH / 32;     // value rows per lane in the value pass
+  constexpr int U = 4;             // loads in flight per lane
+  __shared__ float qs[DH], kn[DH], vn[DH];
+  __shared__ __attribute__((aligned(16))) float sc[kMaxChunk + 8];
+  __shared__ float red[8];
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t bh = (size_t)b * H + h;
+  T* __restrict__ K = Kc + bh * cap * DH;
+  T* __restrict__ VT = VTc + bh * DH * cap;
+  const int j0 = s * chunk, j1 = min(n + 1, j0 + chunk);  // this split's keys [j0, j1)
+  const int jc_end = min(j1, n);                           // of which cached: [j0, jc_end)
+  const bool owns_new = (n >= j0 && n < j1);
+
+  const T* row = QKV + (size_t)b * 3 * D;
+  if (tid < DH / 2) {
+    const int c = tid;
+    const float2 cs = rope[(size_t)n * (DH / 2) + c];
+    const float q1 = (float)row[h * DH + c], q2 = (float)row[h * DH + c + DH / 2];
+    qs[c] = q1 * cs.x - q2 * cs.y;
+    qs[c + DH / 2] = q2 * cs.x + q1 * cs.y;
+    const float k1 = (float)row[D + h * DH + c], k2 = (float)row[D + h * DH + c + DH / 2];
+    const T ka = round_t<T>(k1 * cs.x - k2 * cs.y), kb = round_t<T>(k2 * cs.x + k1 * cs.y);
+    kn[c] = (float)ka;
+    kn[c + DH / 2] = (float)kb;
+    if (s == 0) {
+      K[(size_t)n * DH + c] = ka;
+      K[(size_t)n * DH + c + DH / 2] = kb;
+    }
+  } else if (tid >= 64 && tid < 64 + DH) {
+    const int d = tid - 64;
+    const T v = row[2 * D + h * DH + d];
+    vn[d] = (float)v;
+    if (s == 0) VT[(size_t)d * cap + n] = v;
+  }
+  __syncthreads();
+
+  // ---- scores of the cached keys
+  const int kl = lane / LPK, pp = lane % LPK;
+  float qr[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qr[e] = qs[8 * pp + e];
+  for (int jb = j0 + wave * KPW; jb < jc_end; jb += 4 * KPW * U) {
+    float kv[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = jb + u * 4 * KPW + kl;
+      if (j < jc_end)
+        load8(K + (size_t)j * DH + 8 * pp, kv[u]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[u][e] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qr[e], kv[u][e], d);
+#pragma unroll
+      for (int o = 1; o < LPK; o <<= 1) d += __shfl_xor(d, o, 64);
+      const int j = jb + u * 4 * KPW + kl;
+      if (pp == 0 && j < jc_end) sc[j - j0] = d * scale_log2;
+    }
+  }
+  if (owns_new && wave == 0) {
+    float d = 0.f;
+    for (int e = lane; e < DH; e += 64) d = fmaf(qs[e], kn[e], d);
+    d = wave_sum(d);
+    if (lane == 0) sc[n - j0] = d * scale_log2;
+  }
+  __syncthreads();
+
+  // ---- softmax over [j0, j1)
+  const int cnt = j1 - j0;
+  float mx = -INFINITY;
+  for (int j = tid; j < cnt; j += 256) mx = fmaxf(mx, sc[j]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float ls = 0.f;
+  for (int j = tid; j < cnt; j += 256) {
+    const float p = exp2f(sc[j] - mx);
+    sc[j] = p;
+    ls += p;
+  }
+  ls = wave_sum(ls);
+  __syncthreads();  // everyone has read red[] (max) before it is reused
+  if (lane == 0) red[4 + wave] = ls;
+  __syncthreads();
+  ls = red[4] + red[5] + red[6] + red[7];
+
+  // ---- values: lane (row lane rl, chunk lane cl) owns rows r*32 + wave*8 + rl, keys cl*8 + 64t
+  const int cl = lane & 7, rl = lane >> 3;
+  float acc[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) acc[r] = 0.f;
+  for (int jc = j0 + cl * 8; jc < jc_end; jc += 64) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = (jc + e < jc_end) ? sc[jc - j0 + e] : 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int d = r * 32 + wave * 8 + rl;
+      float v[8];
+      load8(VT + (size_t)d * cap + jc, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r] = fmaf(p[e], v[e], acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) acc[r] += __shfl_xor(acc[r], o, 64);
+  }
+  if (cl == 0) {
+    const float pn = owns_new ? sc[n - j0] : 0.f;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      const int d = r * 32 + wave * 8 + rl;
+      const float o = acc[r] + pn * vn[d];
+      if (nsplit == 1) {
+        ACT[(size_t)b * ld_act + h * DH + d] = round_t<T>(o / ls);
+      } else {
+        float* pp_ = part + ((bh * nsplit) + s) * (DH + 2);
+        pp_[2 + d] = o;
+        if (d == 0) {
+          pp_[0] = mx;
+          pp_[1] = ls;
+        }
+      }
+    }
+  }
+}
+
+// merge split partials: o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+template <typename T, int DH>
+__global__ void k_attn_combine(const float* __restrict__ part, int H, int nsplit, T* __restrict__ ACT, int ld_act) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const size_t bh = (size_t)b * H + h;
+  const float* p = part + bh * nsplit * (DH + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * (DH + 2)]);
+  float l = 0.f, o = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float w = exp2f(p[s * (DH + 2)] - M);
+    l += w * p[s * (DH + 2) + 1];
+    o += w * p[s * (DH + 2) + 2 + d];
+  }
+  ACT[(size_t)b * ld_act + h * DH + d] = round_t<T>(o / l);
+}
+
+template <typename T, int DH>
+static hipError_t launch_decode_t(const void* QKV, int B, int n, int D, int H, const float2* rope, void* Kc, void* Vc,
+                                  int cap, void* ACT, int ld_act, float* part, size_t part_bytes, hipStream_t st) {
+  const int nk = n + 1;
+  // enough workgroups to cover the chip (>= 1024), at most kMaxChunk keys per split
+  int nsplit = std::max((nk + kMaxChunk - 1) / kMaxChunk, std::min((1024 + B * H - 1) / (B * H), (nk + 255) / 256));
+  nsplit = std::max(1, std::min(nsplit, kMaxSplit));
+  int chunk = (nk + nsplit - 1) / nsplit;
+  chunk = (chunk + 63) / 64 * 64;
+  nsplit = (nk + chunk - 1) / chunk;
+  if (chunk > kMaxChunk) return hipErrorInvalidValue;
+  if (nsplit > 1 && (size_t)B * H * nsplit * (DH + 2) * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  const float sl2 = kLog2e / sqrtf((float)DH);
+  hipLaunchKernelGGL((k_attn_decode<T, DH>), dim3(nsplit, H, B), dim3(256), 0, st, (const T*)QKV, n, D, H, rope,
+                     (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, part, nsplit, chunk, sl2);
+  if (nsplit > 1)
+    hipLaunchKernelGGL((k_attn_combine<T, DH>), dim3(H, B), dim3(DH), 0, st, (const float*)part, H, nsplit, (T*)ACT,
+                       ld_act);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, int n, int D, int H, int dh, const float2* rope,
+                                    void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part, size_t part_bytes,
+                                    hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+#define BT_DEC(T, DHV) \
+  if (dh == DHV) return launch_decode_t<T, DHV>(QKV, B, n, D, H, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, st);
+  if (f32) {
+    BT_DEC(float, 32) BT_DEC(float, 64) BT_DEC(float, 128)
+  } else {
+    BT_DEC(f16, 64) BT_DEC(f16, 128)
+  }
+#undef BT_DEC
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- local attention (token decoder)
+// grid (H, B), one wave.  New slots [s0, s0 + m) of row b come from QKV rows b*m + i.
+constexpr int kMaxLocal = 32;
+
+template <typename T, int DH>
+__global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, int m, int s0, int D, int H,
+                                                   const float2* __restrict__ rope, T* __restrict__ Kc,
+                                                   T* __restrict__ Vc, int cap, T* __restrict__ ACT, int ld_act,
+                                                   float scale) {
+  __shared__ float ks[kMaxLocal][DH + 1], vs[kMaxLocal][DH + 1], qs[kMaxLocal][DH + 1];
+  __shared__ float ps[64];
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const size_t bh = (size_t)b * H + h;
+  T* __restrict__ K = Kc + bh * cap * DH;
+  T* __restrict__ V = Vc + bh * cap * DH;
+  constexpr int HALF = DH / 2;
+  for (int e = lane; e < s0 * DH; e += 64) {
+    ks[e / DH][e % DH] = (float)K[e];
+    vs[e / DH][e % DH] = (float)V[e];
+  }
+  for (int e = lane; e < m * HALF; e += 64) {
+    const int i = e / HALF, c = e % HALF, slot = s0 + i;
+    const T* r = QKV + ((size_t)b * m + i) * 3 * D + h * DH;
+    const float2 cs = rope[(size_t)slot * HALF + c];
+    const float q1 = (float)r[c], q2 = (float)r[c + HALF];
+    qs[i][c] = q1 * cs.x - q2 * cs.y;
+    qs[i][c + HALF] = q2 * cs.x + q1 * cs.y;
+    const float k1 = (float)r[D + c], k2 = (float)r[D + c + HALF];
+    const T ka = round_t<T>(k1 * cs.x - k2 * cs.y), kb = round_t<T>(k2 * cs.x + k1 * cs.y);
+    ks[slot][c] = (float)ka;
+    ks[slot][c + HALF] = (float)kb;
+    K[(size_t)slot * DH + c] = ka;
+    K[(size_t)slot * DH + c + HALF] = kb;
+  }
+  for (int e = lane; e < m * DH; e += 64) {
+    const int i = e / DH, d = e % DH, slot = s0 + i;
+    const T v = QKV[((size_t)b * m + i) * 3 * D + 2 * D + h * DH + d];
+    vs[slot][d] = (float)v;
+    V[(size_t)slot * DH + d] = v;
+  }
+  __syncthreads();
+  for (int i = 0; i < m; ++i) {
+    const int nkeys = s0 + i + 1;
+    float sj = -INFINITY;
+    if (lane < nkeys) {
+      float d = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < DH; ++e) d = fmaf(qs[i][e], ks[lane][e], d);
+      sj = d * scale;
+    }
+    const float mx = wave_max(sj);
+    const float p = lane < nkeys ? expf(sj - mx) : 0.f;
+    const float l = wave_sum(p);
+    ps[lane] = p;
+    __syncthreads();
+    for (int d = lane; d < DH; d += 64) {
+      float o = 0.f;
+      for (int j = 0; j < nkeys; ++j) o = fmaf(ps[j], vs[j][d], o);
+      ACT[((size_t)b * m + i) * ld_act + h * DH + d] = round_t<T>(o / l);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
+                                  const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
+                                  hipStream_t st) {
+  if (B <= 0 || m <= 0) return hipSuccess;
+  if (s0 + m > kMaxLocal || s0 + m > cap) return hipErrorInvalidValue;
+  const float scale = 1.0f / sqrtf((float)dh);
+  dim3 grid(H, B);
+#define BT_LOC(T, DHV)                                                                                          \
+  if (dh == DHV) {                                                                                              \
+    hipLaunchKernelGGL((k_local_attn<T, DHV>), grid, dim3(64), 0, st, (const T*)QKV, m, s0, D, H, rope, (T*)Kc, \
+                       (T*)Vc, cap, (T*)ACT, ld_act, scale);                                                     \
+    return hipGetLastError();                                                                                   \
+  }
+  if (f32) {
+    BT_LOC(float, 32) BT_LOC(float, 64) BT_LOC(float, 128)
+  } else {
+    BT_LOC(f16, 64) BT_LOC(f16, 128)
+  }
+#undef BT_LOC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bt

@@ -1,0 +1,139 @@
+// Internal declarations of libbt: workspace layout and kernel launchers.
+// Device code targets gfx950 (CDNA4): wave64, MFMA f32_16x16x32_f16, 160 KB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "bt.h"
+
+namespace bt {
+
+typedef _Float16 f16;
+typedef uint16_t bf16_bits;
+
+// Pre-scale applied to fp16 weights so that every bf16 weight of magnitude
+// >= 2^-22 converts to fp16 exactly (fp16 normals start at 2^-14); the GEMM
+// epilogue multiplies the fp32 accumulator by the inverse (exact, power of 2).
+constexpr float kWeightScale = 256.0f;
+constexpr float kWeightUnscale = 1.0f / 256.0f;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct LayerOff {
+  size_t ln;  // fp32 [4][D]: ln1.g, ln1.b, ln2.g, ln2.b
+  size_t w1;  // T [N1 = 3D + F][D]: rows = output features of q | k | v | up (K-contiguous)
+  size_t b1;  // fp32 [3D + F]
+  size_t w2;  // T [D][D + F]: row n = output feature n of attn.out (k < D) and mlp.down (k >= D)
+  size_t b2;  // fp32 [2][D]: attn.out.b, mlp.down.b
+};
+
+struct Layout {
+  // model dimensions
+  int V, D, H, dh, F, L, P, Nb, Nt, De;
+  int Bmax, max_tokens;
+  int ncap;     // block-KV entries per (layer, row, head), multiple of 64
+  int lcap;     // local-KV entries per (layer, row, head) = P + L
+  int npos;     // rows of the rotary table
+  int Vpad;     // classifier rows padded to a multiple of 128
+  int64_t Mmax; // activation rows
+  bool f32;     // BT_FP32 mode (fp32 everywhere) vs fp16 operands
+  size_t elem;  // bytes per matrix / cache element (4 or 2)
+  size_t tab_elem;  // bytes per embedding-table element (blob dtype)
+  // workspace regions (byte offsets)
+  size_t emb_block, emb_tok, head, lnf_blk, lnf_tok, prefix_w, prefix_b, rope;
+  std::vector<LayerOff> blk, tok;
+  size_t block_kv, local_kv;
+  size_t X;     // fp32 [Mmax][D] residual stream
+  size_t LN;    // T [2][Mmax][D] LayerNorm outputs (ln1, ln2)
+  size_t QKV;   // T [Mmax][3D]
+  size_t ACT;   // T [Mmax][D + F]: attention output | GELU(up)
+  size_t part;  // fp32 split-KV partials of block-attention decode
+  size_t part_bytes;
+  size_t keys;  // u64 [Bmax] argmax keys
+  size_t cur;   // int32 [Bmax][L] ids of the block being generated
+  size_t total;
+  size_t block_kv_bytes, local_kv_bytes;
+  // canonical blob offsets (bytes)
+  struct BlobLayer { size_t ln1g, ln1b, qkvw, qkvb, outw, outb, ln2g, ln2b, upw, upb, downw, downb; };
+  size_t bl_emb_block, bl_lnf_blk_g, bl_lnf_blk_b, bl_prefix_w, bl_prefix_b, bl_emb_tok, bl_lnf_tok_g,
+      bl_lnf_tok_b, bl_head, bl_total;
+  std::vector<BlobLayer> bl_blk, bl_tok;
+};
+
+// Fills `lo` for cfg; returns an empty string or the reason cfg is invalid.
+std::string plan_layout(const bt_config& cfg, Layout& lo);
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `st` and return hipGetLastError().
+
+// ---- weight repack (bt_init)
+hipError_t launch_transpose_convert(const void* src, bool src_bf16, int K, int N, void* dst, bool dst_f32,
+                                    int ld_dst, int row0, int col0, float scale, hipStream_t st);
+hipError_t launch_convert_rows(const void* src, bool src_bf16, int rows, int cols, int rows_pad, void* dst,
+                               bool dst_f32, float scale, hipStream_t st);
+hipError_t launch_to_f32(const void* src, bool src_bf16, int n, float* dst, hipStream_t st);
+hipError_t launch_add_f32(float* dst, const float* a, int n, hipStream_t st);
+hipError_t launch_rope_table(float2* tab, int npos, int dh, float base, hipStream_t st);
+
+// ---- embedders
+// prompt blocks: X[b*n + i][o*De + d] = E[tok(b, i*L + o)][d], tok from the left-padded prompt
+hipError_t launch_embed_prompt(const int32_t* prompt, int B, int T, int Tp, int pad, const void* E,
+                               bool tab_bf16, int V, int De, int L, float* X, hipStream_t st);
+// one completed block per row: X[b][o*De + d] = E[cur[b*L + o]][d]
+hipError_t launch_embed_block(const int32_t* cur, int B, int L, const void* E, bool tab_bf16, int V,
+                              int De, float* X, hipStream_t st);
+// one token per row: X[b][:] = E_tok[cur[b*L + j]]
+hipError_t launch_embed_token(const int32_t* cur, int B, int L, int j, const void* E, bool tab_bf16,
+                              int V, int D, float* X, hipStream_t st);
+
+// ---- LayerNorm over rows r < rows of X[(r*stride + off)][:] -> out1 (params p1), out2 (p2, optional)
+hipError_t launch_layernorm(const float* X, int rows, int D, int stride, int off, const float* p1,
+                            void* out1, const float* p2, void* out2, bool out_f32, float eps,
+                            unsigned long long* reset_keys, int n_keys, hipStream_t st);
+
+// ---- GEMM: C[M][N] = A[M][K] * W[N][K]^T with an epilogue
+enum EpiMode { EPI_QKV_GELU = 0, EPI_RESID = 1, EPI_STORE = 2, EPI_ARGMAX = 3 };
+struct Epi {
+  float wscale;             // multiplies the accumulator
+  const float* bias;        // [N] (QKV|up, STORE), attn.out.b (RESID); unused for ARGMAX
+  const float* bias2;       // mlp.down.b (RESID)
+  void* out0;               // QKV (T, ld0) | X (fp32, ld0) | Y (fp32, ld0) | logits (fp32, ld0, may be null)
+  void* out1;               // ACT (T, ld1) for the GELU columns
+  int ld0, ld1;
+  int n_split;              // QKV_GELU: columns >= n_split take A2 and go through GELU into out1
+  int act_col0;             // QKV_GELU: first ACT column of the GELU part
+  int n_valid;              // ARGMAX: columns >= n_valid are padding
+  unsigned long long* keys; // ARGMAX: per-row packed (value, id) maxima
+};
+hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N,
+                       int K, EpiMode mode, const Epi& ep, hipStream_t st);
+
+// ---- attention
+// rotary + scatter of K (row-major [slot][dh]) and V (block cache: transposed [dh][slot]) for rows
+// (b, i) of QKV [B*m][3D] into cache slots s0 + i, at rotary positions s0 + i.
+hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
+                               const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed,
+                               hipStream_t st);
+// causal prefill attention of rows (b, i < n) at positions i over cache entries [0, i]
+hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int D, int H, int dh,
+                                    const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
+                                    int ld_act, hipStream_t st);
+// one new block-decoder position n per row: rotary, append K/V at slot n, attend over [0, n]
+hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, int n, int D, int H, int dh,
+                                    const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
+                                    float* part, size_t part_bytes, hipStream_t st);
+// local attention: new slots [s0, s0 + m) per row; rotary at slot, write to local cache, attend over [0, slot]
+hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
+                                  const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
+                                  hipStream_t st);
+
+// ---- greedy ids from argmax keys: next[b] = id, cur[b*L + j] = id
+hipError_t launch_finalize(const unsigned long long* keys, int B, int32_t* next, int32_t* cur, int L, int j,
+                           hipStream_t st);
+
+}  // namespace bt

@@ -1,0 +1,283 @@
+// GEMM kernels of libbt: C[M][N] = A[M][K] * W[N][K]^T with fused epilogues.
+//
+// fp16 operands: LDS-tiled MFMA (v_mfma_f32_16x16x32_f16, fp32 accumulation), 256 threads
+// as a WM x WN grid of waves, BK = 64 with a double-buffered LDS stage fed by 16-byte global
+// loads held in registers one K-step ahead.  Workgroup ids are remapped so that each of the 8
+// XCDs walks a contiguous range of output tiles, grouped 8 M-tiles at a time, so that A and W
+// tiles are re-read from that XCD's L2 rather than from HBM.
+// fp32 operands (BT_FP32): a plain LDS-tiled VALU kernel with the same epilogues.
+#include "bt_internal.h"
+#include "device_common.h"
+
+namespace bt {
+
+template <int MODE, typename T>
+__device__ __forceinline__ void epi_store(const Epi& ep, int row, int col, float v) {
+  if constexpr (MODE == EPI_QKV_GELU) {
+    v += ep.bias[col];
+    if (col < ep.n_split)
+      store_from_f32((T*)ep.out0 + (size_t)row * ep.ld0 + col, v);
+    else
+      store_from_f32((T*)ep.out1 + (size_t)row * ep.ld1 + ep.act_col0 + (col - ep.n_split), gelu_erf(v));
+  } else if constexpr (MODE == EPI_RESID) {
+    float* x = (float*)ep.out0 + (size_t)row * ep.ld0 + col;
+    *x += v + ep.bias[col] + ep.bias2[col];
+  } else if constexpr (MODE == EPI_STORE) {
+    ((float*)ep.out0)[(size_t)row * ep.ld0 + col] = v + (ep.bias ? ep.bias[col] : 0.f);
+  }
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m, 64);
+  hi = __shfl_xor(hi, m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Maps the hardware workgroup id to a logical tile index so that the workgroups one XCD
+// receives (ids x, x+8, x+16, ... go to XCD x) form one contiguous range of tiles.
+__device__ __forceinline__ int xcd_contiguous_tile(int bid, int nb) {
+  int per = nb >> 3, rem = nb & 7, x = bid & 7, i = bid >> 3;
+  return x * per + min(x, rem) + i;
+}
+
+template <int BM, int BN, int WM, int WN, int MODE>
+__global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, const f16* __restrict__ A2, int lda,
+                                                   const f16* __restrict__ W, int M, int N, int K, Epi ep) {
+  constexpr int BK = 64, LDK = BK + 8;  // +16 B per LDS row: conflict-free 16-byte fragment reads
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  constexpr int CA = BM * BK / 8 / 256, CB = BN * BK / 8 / 256;
+  static_assert(WM * WN == 4 && FM >= 1 && FN >= 1 && CA >= 1 && CB >= 1, "tile");
+  __shared__ __attribute__((aligned(16))) f16 As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) f16 Bs[2][BN * LDK];
+
+  const int ntm = (M + BM - 1) / BM, ntn = N / BN;
+  const int t = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  constexpr int GM = 8;
+  const int group = t / (GM * ntn), first_m = group * GM;
+  const int gm = min(GM, ntm - first_m);
+  const int r_in = t - group * GM * ntn;
+  const int tm = first_m + r_in % gm, tn = r_in / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const f16* __restrict__ A = (MODE == EPI_QKV_GELU && n0 >= ep.n_split) ? A2 : A1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  half8 ra[CA], rb[CB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      int c = tid + i * 256, r = c / (BK / 8), kc = c % (BK / 8);
+      int row = min(m0 + r, M - 1);
+      ra[i] = *(const half8*)(A + (size_t)row * lda + k0 + kc * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      int c = tid + i * 256, r = c / (BK / 8), kc = c % (BK / 8);
+      rb[i] = *(const half8*)(W + (size_t)(n0 + r) * K + k0 + kc * 8);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+      int c = tid + i * 256, r = c / (BK / 8), kc = c % (BK / 8);
+      *(half8*)&As[buf][r * LDK + kc * 8] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      int c = tid + i * 256, r = c / (BK / 8), kc = c % (BK / 8);
+      *(half8*)&Bs[buf][r * LDK + kc * 8] = rb[i];
+    }
+  };
+
+  float4_ acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = float4_{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      half8 af[FM], bw[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        af[fm] = *(const half8*)&As[buf][(wm * TM + fm * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        bw[fn] = *(const half8*)&Bs[buf][(wn * TN + fn * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds C[4*(lane/16) + i][lane % 16] of each 16 x 16 tile
+  if constexpr (MODE == EPI_ARGMAX) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+          const float v = acc[fm][fn][i] * ep.wscale;
+          if (col < ep.n_valid) {
+            if (ep.out0 && row < M) ((float*)ep.out0)[(size_t)row * ep.ld0 + col] = v;
+            unsigned long long k = argmax_key(v, col);
+            best = k > best ? k : best;
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          unsigned long long other = shfl_xor_u64(best, o);
+          best = other > best ? other : best;
+        }
+        if ((lane & 15) == 0 && row < M && best) atomicMax(ep.keys + row, best);
+      }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+          const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+          if (row < M) epi_store<MODE, f16>(ep, row, col, acc[fm][fn][i] * ep.wscale);
+        }
+  }
+}
+
+// fp32 VALU GEMM: 64 x 64 tile, 256 threads with 4 x 4 outputs each, K staged 16 at a time.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, int lda, const float* __restrict__ W,
+                                                  int M, int N, int K, Epi ep) {
+  __shared__ float As[16][64 + 4], Ws[16][64 + 4];
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int e = tid; e < 64 * 16; e += 256) {
+      int r = e / 16, kk = e % 16;
+      int gm = m0 + r, gn = n0 + r, gk = k0 + kk;
+      As[kk][r] = (gm < M && gk < K) ? A[(size_t)gm * lda + gk] : 0.f;
+      Ws[kk][r] = (gn < N && gk < K) ? W[(size_t)gn * K + gk] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = Ws[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int row = m0 + ty * 4 + i, col = n0 + tx * 4 + j;
+      if (row >= M || col >= N) continue;
+      float v = acc[i][j] * ep.wscale;
+      if constexpr (MODE == EPI_ARGMAX) {
+        if (col < ep.n_valid) {
+          if (ep.out0) ((float*)ep.out0)[(size_t)row * ep.ld0 + col] = v;
+          atomicMax(ep.keys + row, argmax_key(v, col));
+        }
+      } else {
+        epi_store<MODE, float>(ep, row, col, v);
+      }
+    }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_mfma_cfg(const void* A1, const void* A2, int lda, const void* W, int M, int N, int K,
+                                  EpiMode mode, const Epi& ep, hipStream_t st) {
+  dim3 grid(((M + BM - 1) / BM) * (N / BN)), block(256);
+  const f16 *a1 = (const f16*)A1, *a2 = (const f16*)A2, *w = (const f16*)W;
+  switch (mode) {
+    case EPI_QKV_GELU:
+      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_QKV_GELU>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
+      break;
+    case EPI_RESID:
+      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_RESID>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
+      break;
+    case EPI_STORE:
+      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_STORE>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
+      break;
+    case EPI_ARGMAX:
+      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_ARGMAX>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
+      break;
+  }
+  return hipGetLastError();
+}
+
+static hipError_t launch_f32(const float* A, int lda, const float* W, int M, int N, int K, EpiMode mode,
+                             const Epi& ep, hipStream_t st) {
+  dim3 grid((N + 63) / 64, (M + 63) / 64), block(256);
+  switch (mode) {
+    case EPI_QKV_GELU:
+      hipLaunchKernelGGL(k_gemm_f32<EPI_QKV_GELU>, grid, block, 0, st, A, lda, W, M, N, K, ep);
+      break;
+    case EPI_RESID:
+      hipLaunchKernelGGL(k_gemm_f32<EPI_RESID>, grid, block, 0, st, A, lda, W, M, N, K, ep);
+      break;
+    case EPI_STORE:
+      hipLaunchKernelGGL(k_gemm_f32<EPI_STORE>, grid, block, 0, st, A, lda, W, M, N, K, ep);
+      break;
+    case EPI_ARGMAX:
+      hipLaunchKernelGGL(k_gemm_f32<EPI_ARGMAX>, grid, block, 0, st, A, lda, W, M, N, K, ep);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N, int K,
+                       EpiMode mode, const Epi& ep, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (f32) {
+    if (mode == EPI_QKV_GELU) {
+      // two launches: the q|k|v columns from A1, then the GELU columns from A2
+      Epi e1 = ep;
+      hipError_t err = launch_f32((const float*)A1, lda, (const float*)W, M, ep.n_split, K, mode, e1, st);
+      if (err != hipSuccess) return err;
+      Epi e2 = ep;
+      e2.bias = ep.bias + ep.n_split;
+      e2.n_split = 0;
+      return launch_f32((const float*)A2, lda, (const float*)W + (size_t)ep.n_split * K, M, N - ep.n_split, K,
+                        mode, e2, st);
+    }
+    return launch_f32((const float*)A1, lda, (const float*)W, M, N, K, mode, ep, st);
+  }
+  // fp16 MFMA path: K % 64 == 0, N % 32 == 0 and n_split on a tile boundary (checked at plan time)
+  const bool split_ok128 = (mode != EPI_QKV_GELU) || (ep.n_split % 128 == 0);
+  if (M > 1024 && N % 128 == 0 && split_ok128)
+    return launch_mfma_cfg<128, 128, 2, 2>(A1, A2, lda, W, M, N, K, mode, ep, st);
+  const long tiles64 = (long)((M + 63) / 64) * (N / 64);
+  if (N % 64 == 0 && tiles64 >= 512) return launch_mfma_cfg<64, 64, 2, 2>(A1, A2, lda, W, M, N, K, mode, ep, st);
+  const long tiles6432 = (long)((M + 63) / 64) * (N / 32);
+  if (tiles6432 >= 512) return launch_mfma_cfg<64, 32, 4, 1>(A1, A2, lda, W, M, N, K, mode, ep, st);
+  return launch_mfma_cfg<32, 32, 2, 2>(A1, A2, lda, W, M, N, K, mode, ep, st);
+}
+
+}  // namespace bt

@@ -1,0 +1,152 @@
+/*
+ * bt.h — C-ABI of the Block Transformer inference library (libbt.so, gfx950).
+ *
+ * The library runs batched inference of a Block Transformer as described on
+ * the summary page "Block Transformer: Global-to-Local Language Modeling for
+ * Fast Inference" (arXiv 2406.02657):
+ *   - §3.2 "Big-Picture Architecture": embedder -> block decoder -> context
+ *     embedding -> prefix -> token decoder -> output classifier;
+ *   - §3.4 "The Inference Cost Model": inference is a prefill of the whole
+ *     prompt followed by one generated token per decode step;
+ *   - §3.4 "The Block Decoder": its KV cache holds one entry per block;
+ *   - §3.4 "The Token Decoder": its KV cache holds at most prefix + one block
+ *     and does not persist across blocks.
+ * Generation is greedy (argmax, lowest id on ties).
+ *
+ * Memory: the caller allocates and owns every device buffer (weights blob,
+ * workspace, prompt, outputs) and keeps them alive until bt_destroy.  The
+ * library never allocates device memory; it owns only the host-side handle.
+ * Calls enqueue work on the HIP stream given to bt_init and return without
+ * synchronising; outputs are valid once the caller has synchronised that
+ * stream.  A handle is not thread-safe: use it from one thread and stream.
+ *
+ * Errors: every call validates its arguments and the handle's state on the
+ * host before launching anything; on failure it returns a negative bt_status
+ * and bt_last_error() describes the cause.  After BT_ERR_HIP the handle is
+ * unusable (only bt_destroy is valid).  No exception crosses the ABI.
+ */
+#ifndef BT_H_
+#define BT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bt_handle bt_handle; /* opaque, host-side */
+
+typedef enum {
+  BT_OK = 0,
+  BT_ERR_INVALID_ARG = -1, /* malformed config, NULL pointer, size mismatch   */
+  BT_ERR_CAPACITY = -2,    /* batch or sequence beyond the configured capacity */
+  BT_ERR_STATE = -3,       /* call out of order (decode before prefill, ...)   */
+  BT_ERR_HIP = -4,         /* a HIP runtime call failed                        */
+  BT_ERR_UNSUPPORTED = -5  /* valid config this build does not handle          */
+} bt_status;
+
+typedef enum {
+  BT_FP32 = 0, /* weights, activations and caches in fp32                     */
+  BT_BF16 = 1  /* bf16 weights blob; matrix operands and KV caches held as fp16
+                  (exact for every bf16 weight after a 2^8 pre-scale), fp32
+                  accumulation, fp32 residual stream                           */
+} bt_dtype;
+
+/* Model and capacity.  Constraints (checked by bt_init and the sizing calls):
+ *   d_model % n_heads == 0, d_head = d_model / n_heads in {32, 64, 128};
+ *   d_model % block_len == 0 (embedder width d_model / block_len, even);
+ *   n_block_layers >= 1, n_token_layers >= 1, block_len >= 1, prefix_len >= 1;
+ *   BT_BF16 also needs d_model % 64 == 0 and d_mlp % 64 == 0;
+ *   max_batch >= 1; max_tokens >= block_len (padded prompt + generated). */
+typedef struct {
+  int32_t vocab, d_model, n_heads, d_mlp;
+  int32_t n_block_layers, n_token_layers;
+  int32_t block_len;  /* L_B: tokens per block                              */
+  int32_t prefix_len; /* P: prefix vectors projected from a context vector  */
+  int32_t max_batch, max_tokens;
+  int32_t dtype;      /* bt_dtype                                           */
+  int32_t pad_id;     /* token used to left-pad prompts to whole blocks     */
+  float ln_eps;       /* LayerNorm epsilon (1e-5)                           */
+  float rope_base;    /* rotary frequency base (10000)                      */
+} bt_config;
+
+/* Size in bytes of the canonical weights blob for this config.  The blob is
+ * the concatenation, without padding, of these tensors in this order, each
+ * row-major, elements of the config's dtype (bf16 or fp32):
+ *   emb_block [V, D/L_B]
+ *   per block layer l: ln1.g [D], ln1.b [D], attn.qkv.w [D, 3D] (columns: q | k | v,
+ *     head-major inside each), attn.qkv.b [3D], attn.out.w [D, D], attn.out.b [D],
+ *     ln2.g [D], ln2.b [D], mlp.up.w [D, F], mlp.up.b [F], mlp.down.w [F, D], mlp.down.b [D]
+ *   blk.lnf.g [D], blk.lnf.b [D]
+ *   prefix.w [D, P*D], prefix.b [P*D]
+ *   emb_token [V, D]
+ *   per token layer: same twelve tensors as a block layer
+ *   tok.lnf.g [D], tok.lnf.b [D]
+ *   head.w [V, D]                      (output classifier, no bias)
+ * Linear maps are y = x W + b with W stored [in, out].  Returns 0 for an
+ * invalid config (see bt_last_error). */
+size_t bt_weights_bytes(const bt_config* cfg);
+
+/* Size in bytes of the device workspace bt_init needs: repacked weights,
+ * rotary table, block-KV and local-KV caches, activations and step state.
+ * Returns 0 for an invalid config. */
+size_t bt_workspace_bytes(const bt_config* cfg);
+
+/* Repack the canonical weights blob (device pointer, bt_weights_bytes long)
+ * into the workspace (device pointer, ws_bytes >= bt_workspace_bytes, 256-byte
+ * aligned) and create a handle bound to hip_stream (a hipStream_t; NULL = the
+ * default stream).  Once the stream has synchronised, the caller may free the
+ * weights blob; the workspace must outlive the handle. */
+int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size_t ws_bytes,
+            void* hip_stream, bt_handle** out);
+
+/* Prefill (summary page §3.4 "The Inference Cost Model", prefill stage):
+ * d_prompt is a device int32 [B, T] row-major array of token ids in [0, vocab);
+ * every row has T tokens.  Rows are left padded with pad_id to T' = the next
+ * multiple of L_B (at least L_B).  Runs the embedder and the block decoder over
+ * all T'/L_B prompt blocks (filling the block-KV cache), then the token decoder
+ * over the P prefix slots of the last context embedding (resetting the local
+ * KV), and writes the first generated token of every row to d_next (device
+ * int32 [B]).  If d_logits is not NULL, the fp32 logits [B, V] of that token
+ * are written there too.  Requires 1 <= B <= max_batch, T >= 1 and
+ * T' + 1 <= max_tokens (else BT_ERR_CAPACITY). */
+int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int32_t* d_next,
+               float* d_logits);
+
+/* One decode step (summary page §3.4, decode stage): feeds back the token the
+ * previous call emitted and writes the next token of every row to d_next
+ * (device int32 [B]; B is the prefill's batch), plus its fp32 logits [B, V] if
+ * d_logits is not NULL.  When the previous L_B emitted tokens complete a block,
+ * the step first embeds that block, runs one block-decoder position against
+ * the block-KV cache, projects a new prefix and resets the local KV; otherwise
+ * it runs one token-decoder position against the local KV.  BT_ERR_STATE
+ * before a successful prefill; BT_ERR_CAPACITY once T' + generated tokens
+ * would exceed max_tokens. */
+int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits);
+
+/* Host mirror of the cache lengths after the last call: block-KV entries per
+ * block-decoder layer and local-KV entries per token-decoder layer. */
+int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_kv_len);
+
+/* Read-only introspection of the workspace layout, for tests and tools.
+ * which = 0: block-KV cache, laid out [N_blk][2 (K, V)][max_batch][n_heads][cap][d_head]
+ *            with cap = ceil(max_tokens / L_B); keys are stored after the
+ *            rotary embedding;
+ * which = 1: local-KV cache, [N_tok][2][max_batch][n_heads][P + L_B][d_head].
+ * Elements are fp16 for BT_BF16 and fp32 for BT_FP32.  Writes the byte
+ * offset from the workspace start, the byte size and the per-head capacity. */
+int bt_workspace_region(const bt_config* cfg, int32_t which, size_t* offset, size_t* bytes,
+                        int32_t* capacity);
+
+/* Free the host handle (no device memory is owned). */
+int bt_destroy(bt_handle* h);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* bt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BT_H_ */

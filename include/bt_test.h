@@ -1,0 +1,41 @@
+/*
+ * bt_test.h — diagnostic entry points of libbt for tests and benchmarks.
+ * They are not needed to run inference; see bt.h for the inference API.
+ */
+#ifndef BT_TEST_H_
+#define BT_TEST_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Kernel classes timed by the profiler, in this order (n_kinds >= 11):
+ * 0 embedder gathers, 1 LayerNorms, 2 [q|k|v|up] GEMMs (with GELU), 3 [out|down] GEMMs (residual),
+ * 4 prefix projection, 5 classifier + argmax, 6 prefill attention, 7 prefill rotary/KV scatter,
+ * 8 block-attention decode (incl. split merge), 9 local attention, 10 greedy-id finalisation. */
+#define BT_PROFILE_KINDS 11
+
+/* Start (on != 0) or stop recording a pair of HIP events around every kernel launch of the
+ * handle, on the handle's stream.  Clears what was recorded before. */
+int bt_profile_enable(bt_handle* h, int32_t on);
+
+/* Synchronise the handle's stream and return, per kernel class, the summed event time (ms) and
+ * the number of launches since bt_profile_enable; then clear the record. */
+int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* launches);
+
+/* C[M][N] = scale * A[M][K] * W[N][K]^T in fp32, on `stream` (a hipStream_t).  dtype BT_FP32:
+ * A and W fp32; BT_BF16: A and W fp16 (the library's matrix-operand type), K % 64 == 0,
+ * N % 32 == 0.  Device pointers; synchronous errors only. */
+int bt_test_gemm(int32_t dtype, const void* d_a, const void* d_w, float* d_c, int32_t M, int32_t N, int32_t K,
+                 float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BT_TEST_H_ */

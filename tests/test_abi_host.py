@@ -1,0 +1,89 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports every function the
+headers declare, validates configs on the host and sizes the weights blob and workspace."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bt_workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for h in ("bt.h", "bt_test.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+(bt_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    import hierarchical_global_local_amd as hg
+    L = hg.lib()
+    names = declared_functions()
+    assert {"bt_init", "bt_prefill", "bt_decode_step", "bt_destroy", "bt_weights_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _cfg(name, **kw):
+    import hierarchical_global_local_amd as hg
+    c = wl.get_config(name, **kw)
+    return c, hg.BtConfig.make(c, c.batch, wl.padded_len(c, c.prompt_len) + c.gen_len)
+
+
+@pytest.mark.parametrize("name", list(wl.CONFIGS))
+def test_blob_size_matches_packer(name):
+    import hierarchical_global_local_amd as hg
+    c, cfg = _cfg(name)
+    n = sum(int(np.prod(s)) for _, s, _ in wl.weight_specs(c))
+    elem = 4 if c.dtype == "fp32" else 2
+    assert hg.lib().bt_weights_bytes(ctypes.byref(cfg)) == n * elem
+    assert hg.weight_names(c) == [s[0] for s in wl.weight_specs(c)]
+
+
+def test_packed_blob_matches_declared_size():
+    import hierarchical_global_local_amd as hg
+    c, cfg = _cfg("c0_tiny")
+    blob = hg.pack_weights(c, wl.make_weights(c))
+    assert blob.nbytes == hg.lib().bt_weights_bytes(ctypes.byref(cfg))
+
+
+def test_block_kv_footprint_ratio_is_block_len():
+    """Block-KV bytes for the 8K-prompt sweep scale as 1/L_B (L_B = 1 is a token-level cache)."""
+    import hierarchical_global_local_amd as hg
+    sizes = {}
+    for name in ("c4_lb1", "c4_lb2", "c4_lb8"):
+        c, cfg = _cfg(name)
+        off, nb, cap = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+        assert hg.lib().bt_workspace_region(ctypes.byref(cfg), 0, ctypes.byref(off), ctypes.byref(nb),
+                                            ctypes.byref(cap)) == 0
+        entries = -(-(wl.padded_len(c, c.prompt_len) + c.gen_len) // c.block_len)
+        assert cap.value == -(-entries // 64) * 64
+        sizes[c.block_len] = entries * nb.value // cap.value
+    assert sizes[1] == 2 * sizes[2] == 8 * sizes[8]
+
+
+@pytest.mark.parametrize("field,value,msg", [("n_heads", 5, "multiple of n_heads"), ("block_len", 0, "block_len"),
+                                             ("dtype", 7, "dtype"), ("max_batch", 0, "max_batch"),
+                                             ("d_model", 96, "d_head"), ("prefix_len", 40, "prefix_len")])
+def test_invalid_config_rejected_on_host(field, value, msg):
+    import hierarchical_global_local_amd as hg
+    _, cfg = _cfg("c1_prefill_heavy")
+    setattr(cfg, field, value)
+    L = hg.lib()
+    assert L.bt_weights_bytes(ctypes.byref(cfg)) == 0
+    assert msg in L.bt_last_error().decode()
+    assert L.bt_workspace_bytes(ctypes.byref(cfg)) == 0
+
+
+def test_null_arguments_rejected():
+    import hierarchical_global_local_amd as hg
+    L = hg.lib()
+    assert L.bt_prefill(None, None, 1, 1, None, None) == -1
+    assert L.bt_decode_step(None, None, None) == -1
+    assert L.bt_destroy(None) == -1

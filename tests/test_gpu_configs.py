@@ -1,0 +1,44 @@
+"""Parity at the full workload sizes (C1-C4): the GPU runs the whole configuration in the launch
+configuration the benchmark times; the oracle recomputes rows 0 and B-1 teacher-forced on the GPU's
+ids at sampled steps (logits <= 2e-2 max-abs, ids within the tolerance band), and the cache lengths
+follow the closed forms."""
+import time
+
+import numpy as np
+import pytest
+
+import bt_workloads as wl
+from oracle import model as om
+from tests.gpu_harness import (BF16_TOL, check_ids_against, log, require_gpu, run_gpu, sampled_steps,
+                               teacher_forced_logits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c1_prefill_heavy", "c2_decode_heavy", "c4_lb1", "c4_lb2", "c4_lb8", "c3_1p2b"])
+def test_full_config_sampled_parity(name):
+    require_gpu()
+    cfg = wl.get_config(name)
+    t0 = time.time()
+    W = wl.make_weights(cfg)
+    prompt = wl.make_prompt(cfg)
+    G = cfg.gen_len
+    steps = sampled_steps(cfg, G, every=128 if G > 512 else 32)
+    log(f"{name}: B={cfg.batch} T={cfg.prompt_len} G={G}, {len(steps)} sampled steps")
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=steps)
+    t1 = time.time()
+    Tp = wl.padded_len(cfg, cfg.prompt_len)
+    assert model.cache_lengths() == (Tp // cfg.block_len + (G - 1) // cfg.block_len,
+                                     cfg.prefix_len + (G - 1) % cfg.block_len)
+    model.close()
+    del model
+    worst = 0.0
+    for r in (0, cfg.batch - 1):
+        ref = teacher_forced_logits(cfg, W, prompt[r], ids[r], steps)      # [S, V]
+        got = np.stack([lg[g][r] for g in steps])
+        err = float(np.abs(got - ref).max())
+        worst = max(worst, err)
+        exact = check_ids_against(ref, ids[r, steps], BF16_TOL)
+        log(f"  row {r}: max-abs logit error {err:.3e}, exact argmax {exact:.3f}")
+    log(f"  gpu {t1 - t0:.1f}s, oracle {time.time() - t1:.1f}s")
+    assert worst <= BF16_TOL

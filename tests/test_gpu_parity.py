@@ -1,0 +1,150 @@
+"""End-to-end parity of the HIP path with the oracle on small models, every generation step:
+fp32 (1e-4 max-abs logits, greedy ids identical) and bf16 (2e-2, ids within the tolerance band),
+plus the cache contents, cache lengths, determinism and host-side error paths."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import bt_workloads as wl
+from oracle import model as om
+from tests.gpu_harness import (BF16_TOL, FP32_TOL, check_ids_against, log, require_gpu, run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = wl.Config("small_bf16", "bf16", vocab=512, d_model=128, n_heads=2, d_mlp=512, n_block_layers=2,
+                       n_token_layers=2, block_len=4, prefix_len=2, batch=5, prompt_len=37, gen_len=20)
+
+
+def _fp32_case(cfg, B, T, G, seed=0):
+    log(f"fp32 case {cfg.name} L_B={cfg.block_len} P={cfg.prefix_len} B={B} T={T} G={G}")
+    W = wl.make_weights(cfg, seed=seed, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, batch=B, T=T, seed=seed)
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G))
+    W64 = om.weights_as(W, np.float64)
+    ref_ids, ref_lg, st = om.generate(W64, cfg, prompt, G, keep_logits=True)
+    gl = np.stack([lg[g] for g in range(G)], axis=1)
+    err = np.abs(gl - ref_lg).max()
+    log(f"  max-abs logit error {err:.3e}")
+    assert err <= FP32_TOL
+    np.testing.assert_array_equal(ids, ref_ids)
+    assert model.cache_lengths() == (st.block_kv_len, st.local_kv_len)
+    return model
+
+
+def test_c0_tiny_fp32_full():
+    cfg = wl.get_config("c0_tiny")
+    _fp32_case(cfg, cfg.batch, cfg.prompt_len, cfg.gen_len)
+
+
+@pytest.mark.parametrize("kw,B,T,G", [(dict(), 3, 30, 13), (dict(block_len=1, prefix_len=2), 2, 9, 7),
+                                      (dict(block_len=2, prefix_len=2), 3, 11, 10),
+                                      (dict(block_len=8, prefix_len=2), 2, 19, 18),
+                                      (dict(d_model=128, n_heads=2), 2, 8, 9),
+                                      (dict(d_model=256, n_heads=2, d_mlp=320), 2, 12, 6)])
+def test_fp32_variants(kw, B, T, G):
+    _fp32_case(wl.get_config("c0_tiny", **kw), B, T, G, seed=1)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=2), dict(block_len=1, prefix_len=1),
+                                dict(block_len=8, prefix_len=2)])
+def test_bf16_small_every_step(kw):
+    cfg = SMALL_BF16.with_(**kw)
+    log(f"bf16 case {kw}")
+    W = wl.make_weights(cfg, seed=2, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=2)
+    G = cfg.gen_len
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G))
+    W64 = om.weights_as(W, np.float64)
+    _, ref_lg, st = om.generate(W64, cfg, prompt, G, keep_logits=True, forced=ids)
+    gl = np.stack([lg[g] for g in range(G)], axis=1)
+    err = np.abs(gl - ref_lg).max()
+    exact = check_ids_against(ref_lg, ids, BF16_TOL)
+    log(f"  max-abs logit error {err:.3e}, exact argmax {exact:.3f}")
+    assert err <= BF16_TOL
+    assert model.cache_lengths() == (st.block_kv_len, st.local_kv_len)
+
+
+def test_kv_caches_hold_rotated_keys_and_values():
+    """Block-KV (keys [slot][d], values transposed) and local-KV contents equal the oracle's caches."""
+    torch = require_gpu()
+    cfg = SMALL_BF16
+    W = wl.make_weights(cfg, seed=3, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=3)
+    G = 7   # ends inside a block: local KV holds P + 2 entries
+    ids, _, model = run_gpu(cfg, W, prompt, G, max_tokens=64)
+    _, _, st = om.generate(om.weights_as(W, np.float64), cfg, prompt, G, forced=ids)
+    B, H, dh = prompt.shape[0], cfg.n_heads, cfg.d_head
+    blk, cap = model.cache_view(0)
+    blk = blk.cpu().float().numpy().reshape(cfg.n_block_layers, 2, B, H, cap, dh)
+    n = st.block_kv_len
+    for l in range(cfg.n_block_layers):
+        k_ref = st.block_caches[l].k.transpose(0, 2, 1, 3)            # [B, H, n, dh]
+        v_ref = st.block_caches[l].v.transpose(0, 2, 3, 1)            # [B, H, dh, n]
+        k_gpu = blk[l, 0, :, :, :n, :]
+        v_gpu = blk[l, 1].reshape(B, H, dh, cap)[:, :, :, :n]
+        assert np.abs(k_gpu - k_ref).max() <= 2e-2 * max(1.0, np.abs(k_ref).max())
+        assert np.abs(v_gpu - v_ref).max() <= 2e-2 * max(1.0, np.abs(v_ref).max())
+    loc, lcap = model.cache_view(1)
+    loc = loc.cpu().float().numpy().reshape(cfg.n_token_layers, 2, B, H, lcap, dh)
+    m = st.local_kv_len
+    for l in range(cfg.n_token_layers):
+        k_ref = st.local_caches[l].k.transpose(0, 2, 1, 3)
+        v_ref = st.local_caches[l].v.transpose(0, 2, 1, 3)
+        assert np.abs(loc[l, 0, :, :, :m] - k_ref).max() <= 2e-2 * max(1.0, np.abs(k_ref).max())
+        assert np.abs(loc[l, 1, :, :, :m] - v_ref).max() <= 2e-2 * max(1.0, np.abs(v_ref).max())
+
+
+def test_cache_lengths_and_ratio():
+    """Block KV grows one entry per L_B tokens (L_B times shorter than a token-level cache);
+    local KV stays within P + L_B - 1 and restarts at P every block."""
+    require_gpu()
+    for L in (1, 2, 4):
+        cfg = SMALL_BF16.with_(block_len=L, prefix_len=2)
+        W = wl.make_weights(cfg, seed=4)
+        prompt = wl.make_prompt(cfg, batch=2, T=16, seed=4)
+        import torch
+        import hierarchical_global_local_amd as hg
+        model = hg.BlockTransformer(cfg, W, max_batch=2, max_tokens=64)
+        d_prompt = torch.from_numpy(prompt).cuda()
+        model.prefill(d_prompt)
+        Tp = wl.padded_len(cfg, 16)
+        for g in range(1, 30):
+            assert model.cache_lengths() == (Tp // L + (g - 1) // L, 2 + (g - 1) % L)
+            model.decode_step()
+        torch.cuda.synchronize()
+
+
+def test_deterministic_runs():
+    cfg = SMALL_BF16
+    W = wl.make_weights(cfg, seed=5)
+    prompt = wl.make_prompt(cfg, seed=5)
+    a = run_gpu(cfg, W, prompt, 12, logits_steps=[0, 5, 11])
+    b = run_gpu(cfg, W, prompt, 12, logits_steps=[0, 5, 11])
+    np.testing.assert_array_equal(a[0], b[0])
+    for g in (0, 5, 11):
+        np.testing.assert_array_equal(a[1][g], b[1][g])
+
+
+def test_host_side_errors():
+    torch = require_gpu()
+    import hierarchical_global_local_amd as hg
+    cfg = SMALL_BF16
+    W = wl.make_weights(cfg, seed=6)
+    model = hg.BlockTransformer(cfg, W, max_batch=2, max_tokens=16)
+    with pytest.raises(hg.BtError) as e:
+        model.decode_step(out=torch.empty(2, dtype=torch.int32, device="cuda"))
+    assert e.value.code == -3
+    with pytest.raises(hg.BtError) as e:
+        model.prefill(torch.zeros((3, 8), dtype=torch.int32, device="cuda"))
+    assert e.value.code == -2
+    with pytest.raises(hg.BtError) as e:
+        model.prefill(torch.zeros((1, 16), dtype=torch.int32, device="cuda"))
+    assert e.value.code == -2
+    model.prefill(torch.zeros((2, 11), dtype=torch.int32, device="cuda"))   # padded to 12, room for 4 tokens
+    for _ in range(3):
+        model.decode_step()
+    with pytest.raises(hg.BtError) as e:
+        model.decode_step()
+    assert e.value.code == -2
+    torch.cuda.synchronize()
