@@ -1,0 +1,238 @@
+"""Throughput benchmark of Block Transformer batched inference on one MI355X.
+
+One step = one greedy generation over the batch: bt_prefill of the whole prompt, then G-1
+bt_decode_step calls (the whole hot path: embedder, block decoder, prefix, token decoder,
+classifier).  Inputs are resident in HBM before the timed region starts.  Prints one JSON line.
+
+Workloads (synthetic random-init weights N(0, 0.02^2), uniform random prompt ids):
+  c1_prefill_heavy  d=768, 6+6 layers, L_B=4, P=1, V=50304, batch 64, 2048-token prompt, 128 generated
+  c2_decode_heavy   same model, batch 256, 128-token prompt, 2048 generated (reported alongside)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "generated tokens/sec @1 MI355X (prefill- & decode-heavy); decode HBM GB/s"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 / bf16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def describe(cfg):
+    return (f"{cfg.name}: Block Transformer d={cfg.d_model} {cfg.n_block_layers}+{cfg.n_token_layers} layers "
+            f"H={cfg.n_heads} MLP={cfg.d_mlp} L_B={cfg.block_len} P={cfg.prefix_len} V={cfg.vocab}, "
+            f"batch {cfg.batch}, {cfg.prompt_len}-token prompt, {cfg.gen_len} generated")
+
+
+class Runner:
+    def __init__(self, cfg):
+        import torch
+
+        import bt_workloads as wl
+        import hierarchical_global_local_amd as hg
+        self.torch, self.cfg = torch, cfg
+        self.G = cfg.gen_len
+        W = wl.make_weights(cfg)
+        prompt = wl.make_prompt(cfg)
+        self.model = hg.BlockTransformer(cfg, W, max_batch=cfg.batch,
+                                         max_tokens=wl.padded_len(cfg, cfg.prompt_len) + self.G)
+        del W
+        self.stream = self.model.stream
+        self.prompt = torch.from_numpy(prompt).cuda()
+        self.ids = torch.empty((self.G, cfg.batch), dtype=torch.int32, device="cuda")
+
+    def step(self, ev=None):
+        """One generation; optional events mark (start, after prefill, end) on the model's stream."""
+        if ev:
+            ev[0].record(self.stream)
+        self.model.prefill(self.prompt, self.ids[0])
+        if ev:
+            ev[1].record(self.stream)
+        for g in range(1, self.G):
+            self.model.decode_step(self.ids[g])
+        if ev:
+            ev[2].record(self.stream)
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for _ in range(warmup):
+                self.step()
+            torch.cuda.synchronize()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+            t0 = time.perf_counter()
+            for e in evs:
+                self.step(e)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        pre = [e[0].elapsed_time(e[1]) for e in evs]
+        dec = [e[1].elapsed_time(e[2]) for e in evs]
+        tot = [e[0].elapsed_time(e[2]) for e in evs]
+        return dict(wall_s=wall, ms_per_step=sum(tot) / steps, prefill_ms=sum(pre) / steps,
+                    decode_ms=sum(dec) / steps)
+
+    def profiled(self, steps):
+        """Repeat the timed steps with HIP events around every launch: per-class time, bytes, flops."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            self.model.profile(True)
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                self.step()
+            prof = self.model.profile_read()
+            wall = time.perf_counter() - t0
+            self.model.profile(False)
+        for v in prof.values():
+            for k in ("ms", "launches", "bytes", "flops"):
+                v[k] /= steps
+        return prof, wall / steps * 1e3
+
+
+def classify(name):
+    """Roofline of a kernel class: prefill GEMMs and prefill attention are MFMA contractions, the rest
+    (all decode kernels, gathers, norms, scatters) move bytes."""
+    phase, kind = name.split("/")
+    if phase == "prefill" and (kind.startswith("gemm") or kind == "attn_prefill"):
+        return "mfma"
+    return "hbm"
+
+
+def roofline_of(name, rec):
+    bound = classify(name)
+    if bound == "mfma":
+        achieved = rec["flops"] / (rec["ms"] * 1e-3) / 1e12
+        peak, unit = MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
+        per_launch = rec["flops"] / max(rec["launches"], 1)
+    else:
+        achieved = rec["bytes"] / (rec["ms"] * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+        per_launch = rec["bytes"] / max(rec["launches"], 1)
+    return {"kernel_class": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None, "launches_per_step": rec["launches"],
+            "avg_launch_us": round(rec["ms"] * 1e3 / max(rec["launches"], 1), 3),
+            "algorithmic_per_launch": per_launch}
+
+
+def cpu_baseline(cfg, rows, tokens):
+    """The oracle (numpy fp32, incremental prefill + decode) on a bounded sample of the workload."""
+    import numpy as np
+
+    import bt_workloads as wl
+    from oracle import model as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    W = om.weights_as(wl.make_weights(cfg), np.float32)
+    prompt = wl.make_prompt(cfg)[:rows]
+    t0 = time.perf_counter()
+    om.generate(W, cfg, prompt, tokens)
+    dt = time.perf_counter() - t0
+    return {"value": round(rows * tokens / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{cfg.name}: rows 0..{rows - 1} of the batch, full {cfg.prompt_len}-token prompt, "
+                      f"{tokens} generated tokens (numpy fp32 incremental path), {dt:.1f} s wall",
+            "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="c1_prefill_heavy")
+    ap.add_argument("--decode-config", default="c2_decode_heavy", help="second workload reported alongside, or 'none'")
+    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the Block Transformer path shards by batch rows with no "
+              "exchange (each GPU would run this same step on its own rows); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bt_workloads as wl
+    cfg = wl.get_config(args.config)
+    log(f"[bench] {describe(cfg)}")
+    r = Runner(cfg)
+    t = r.timed(args.steps, args.warmup)
+    log(f"[bench] timed {args.steps} steps: {t['ms_per_step']:.2f} ms/step "
+        f"(prefill {t['prefill_ms']:.2f} ms, decode {t['decode_ms']:.2f} ms)")
+    prof, prof_ms = r.profiled(args.steps)
+    B, G = cfg.batch, cfg.gen_len
+    value = B * G / (t["ms_per_step"] * 1e-3)
+    dec_bytes = sum(v["bytes"] for k, v in prof.items() if k.startswith("decode/"))
+    pre_flops = sum(v["flops"] for k, v in prof.items() if k.startswith("prefill/"))
+    active = {k: v for k, v in prof.items() if v["launches"]}
+    dominant = max(active, key=lambda k: active[k]["ms"])
+    classes = {k: {"ms_per_step": round(v["ms"], 3), "launches": v["launches"],
+                   "rate": roofline_of(k, v)["achieved"], "unit": roofline_of(k, v)["unit"]}
+               for k, v in sorted(active.items(), key=lambda kv: -kv[1]["ms"])}
+    for k, v in classes.items():
+        log(f"[bench]   {k:28s} {v['ms_per_step']:9.3f} ms/step  {v['launches']:6d} launches  {v['rate']:9.1f} {v['unit']}")
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t["ms_per_step"], 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "compute": "bf16 weights; matrix operands and KV caches fp16 (exact for bf16 weights after a 2^8 "
+                   "pre-scale), fp32 accumulation, softmax, LayerNorm and residual stream",
+        "data": "synthetic (random-init N(0,0.02^2) weights, uniform random prompt ids)",
+        "config": {"workload": describe(cfg), "global_batch": B, "seq_len": cfg.prompt_len, "gen_len": G},
+        "prefill_ms": round(t["prefill_ms"], 3), "decode_ms": round(t["decode_ms"], 3),
+        "prefill_tflops": round(pre_flops / (t["prefill_ms"] * 1e-3) / 1e12, 2),
+        "decode_hbm_gbps": round(dec_bytes / (t["decode_ms"] * 1e-3) / 1e9, 1),
+        "roofline": roofline_of(dominant, prof[dominant]),
+        "profiled_ms_per_step": round(prof_ms, 3),
+        "kernel_classes": classes,
+    }
+    result["roofline"]["measured"] = ("HIP events on the library's stream around every launch of the class, "
+                                      f"over a profiled repeat of the {args.steps} timed steps")
+    del r
+    torch.cuda.empty_cache()
+    if args.decode_config != "none":
+        c2 = wl.get_config(args.decode_config)
+        log(f"[bench] {describe(c2)}")
+        r2 = Runner(c2)
+        t2 = r2.timed(1, 1)
+        prof2, _ = r2.profiled(1)
+        d_bytes = sum(v["bytes"] for k, v in prof2.items() if k.startswith("decode/"))
+        att = prof2["decode/attn_block_decode"]
+        result["decode_heavy"] = {
+            "workload": describe(c2), "value": round(c2.batch * c2.gen_len / (t2["ms_per_step"] * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(t2["ms_per_step"], 3),
+            "prefill_ms": round(t2["prefill_ms"], 3), "decode_ms": round(t2["decode_ms"], 3),
+            "decode_tokens_per_s": round(c2.batch * (c2.gen_len - 1) / (t2["decode_ms"] * 1e-3), 1),
+            "decode_hbm_gbps": round(d_bytes / (t2["decode_ms"] * 1e-3) / 1e9, 1),
+            "block_attn_decode": roofline_of("decode/attn_block_decode", att),
+        }
+        log(f"[bench] decode-heavy: {result['decode_heavy']['value']:.0f} tokens/s, "
+            f"decode {result['decode_heavy']['decode_hbm_gbps']} GB/s")
+        del r2
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_rows, cfg.batch), min(args.cpu_tokens, cfg.gen_len))
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

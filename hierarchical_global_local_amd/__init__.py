@@ -70,7 +70,8 @@ def lib() -> ctypes.CDLL:
     L.bt_destroy.argtypes = [c_p]
     L.bt_last_error.argtypes, L.bt_last_error.restype = [], ctypes.c_char_p
     L.bt_profile_enable.argtypes = [c_p, c_i32]
-    L.bt_profile_read.argtypes = [c_p, c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    dp = ctypes.POINTER(ctypes.c_double)
+    L.bt_profile_read.argtypes = [c_p, c_i32, dp, ctypes.POINTER(ctypes.c_int64), dp, dp]
     L.bt_test_gemm.argtypes = [c_i32, c_p, c_p, c_p, c_i32, c_i32, c_i32, ctypes.c_float, c_p]
     for f in ("bt_init", "bt_prefill", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
               "bt_profile_enable", "bt_profile_read", "bt_test_gemm"):
@@ -210,12 +211,18 @@ class BlockTransformer:
     def profile(self, on: bool) -> None:
         check(lib().bt_profile_enable(self.h, 1 if on else 0))
 
-    def profile_read(self) -> Dict[str, tuple]:
-        n = len(PROFILE_KINDS)
-        ms = (ctypes.c_double * n)()
+    def profile_read(self) -> Dict[str, dict]:
+        """{phase/kind: {"ms", "launches", "bytes", "flops"}} since profile(True); phase is prefill or decode."""
+        n = 2 * len(PROFILE_KINDS)
+        ms, by, fl = (ctypes.c_double * n)(), (ctypes.c_double * n)(), (ctypes.c_double * n)()
         cnt = (ctypes.c_int64 * n)()
-        check(lib().bt_profile_read(self.h, n, ms, cnt))
-        return {k: (ms[i], cnt[i]) for i, k in enumerate(PROFILE_KINDS)}
+        check(lib().bt_profile_read(self.h, n, ms, cnt, by, fl))
+        out = {}
+        for i in range(n):
+            phase = "prefill" if i < len(PROFILE_KINDS) else "decode"
+            name = f"{phase}/{PROFILE_KINDS[i % len(PROFILE_KINDS)]}"
+            out[name] = {"ms": ms[i], "launches": cnt[i], "bytes": by[i], "flops": fl[i]}
+        return out
 
 
 def gemm(a, w, scale: float = 1.0, stream=None):

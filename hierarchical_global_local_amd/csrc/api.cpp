@@ -156,8 +156,10 @@ struct bt_handle {
   // optional per-kernel-class event timing
   bool prof = false;
   std::vector<hipEvent_t> ev_pool;
-  std::vector<std::pair<int, int>> ev_used;  // (kind, index of the start event)
+  struct Rec { int kind, ev; double bytes, flops; };
+  std::vector<Rec> ev_used;
   size_t ev_next = 0;
+  bool decode_phase = false;  // classes are split by phase: prefill, decode
 };
 
 namespace {
@@ -165,11 +167,15 @@ namespace {
 enum ProfKind { PK_EMBED = 0, PK_LN, PK_GEMM_QKV, PK_GEMM_OUT, PK_GEMM_PREFIX, PK_GEMM_HEAD, PK_ATTN_PREFILL,
                 PK_ROPE_SCATTER, PK_ATTN_DECODE, PK_ATTN_LOCAL, PK_FINALIZE, PK_COUNT };
 
+// Records a pair of events around one launch with its algorithmic bytes and flops (the minimal
+// traffic and arithmetic of the operation, independent of how the kernel achieves it).
 struct Prof {
   bt_handle* h;
   int kind;
+  double bytes, flops;
   int idx = -1;
-  Prof(bt_handle* h_, int k) : h(h_), kind(k) {
+  Prof(bt_handle* h_, int k, double by = 0.0, double fl = 0.0)
+      : h(h_), kind(k + (h_->decode_phase ? PK_COUNT : 0)), bytes(by), flops(fl) {
     if (!h->prof) return;
     if (h->ev_next + 2 > h->ev_pool.size()) {
       for (int i = 0; i < 256; ++i) {
@@ -185,7 +191,7 @@ struct Prof {
   ~Prof() {
     if (idx < 0) return;
     (void)hipEventRecord(h->ev_pool[idx + 1], h->st);
-    h->ev_used.push_back({kind, idx});
+    h->ev_used.push_back({kind, idx, bytes, flops});
   }
 };
 
@@ -233,8 +239,9 @@ float wscale(const Layout& lo) { return lo.f32 ? 1.0f : kWeightUnscale; }
 int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows) {
   const Layout& lo = h->lo;
   const float* lnp = (const float*)P_(h, w.ln);
+  const double E = (double)lo.elem, D = lo.D, N1 = 3.0 * lo.D + lo.F;
   {
-    Prof p(h, PK_LN);
+    Prof p(h, PK_LN, rows * D * (4.0 + 2.0 * E), 8.0 * rows * D);
     BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), rows, lo.D, 1, 0, lnp, ln_buf(h, 0), lnp + 2 * lo.D,
                                  ln_buf(h, 1), lo.f32, h->cfg.ln_eps, nullptr, 0, h->st),
              "layernorm");
@@ -248,7 +255,7 @@ int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows) {
   ep.ld1 = lo.D + lo.F;
   ep.n_split = 3 * lo.D;
   ep.act_col0 = lo.D;
-  Prof p(h, PK_GEMM_QKV);
+  Prof p(h, PK_GEMM_QKV, N1 * D * E + 2.0 * rows * D * E + rows * N1 * E + N1 * 4.0, 2.0 * rows * N1 * D);
   BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), rows, 3 * lo.D + lo.F, lo.D,
                           EPI_QKV_GELU, ep, h->st),
            "gemm qkv|up");
@@ -264,7 +271,8 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
   ep.bias2 = (const float*)P_(h, w.b2) + lo.D;
   ep.out0 = P_(h, lo.X);
   ep.ld0 = lo.D;
-  Prof p(h, PK_GEMM_OUT);
+  const double E = (double)lo.elem, D = lo.D, K2 = (double)lo.D + lo.F;
+  Prof p(h, PK_GEMM_OUT, D * K2 * E + rows * K2 * E + 8.0 * rows * D + 8.0 * D, 2.0 * rows * D * K2);
   BT_CHECK(h, launch_gemm(lo.f32, P_(h, lo.ACT), nullptr, lo.D + lo.F, P_(h, w.w2), rows, lo.D, lo.D + lo.F,
                           EPI_RESID, ep, h->st),
            "gemm out|down");
@@ -279,7 +287,11 @@ int run_token_decoder(bt_handle* h, int m, int s0) {
     int r = run_ln_qkv(h, lo.tok[l], rows);
     if (r) return r;
     {
-      Prof p(h, PK_ATTN_LOCAL);
+      const double E = (double)lo.elem, D = lo.D, Bd = h->B;
+      double pairs = 0;
+      for (int i = 0; i < m; ++i) pairs += s0 + i + 1;
+      Prof p(h, PK_ATTN_LOCAL, Bd * s0 * 2.0 * D * E + rows * 3.0 * D * E + rows * 3.0 * D * E,
+             4.0 * Bd * lo.H * lo.dh * pairs);
       BT_CHECK(h, launch_local_attention(lo.f32, P_(h, lo.QKV), h->B, m, s0, lo.D, lo.H, lo.dh,
                                          (const float2*)P_(h, lo.rope), local_k(h, l), local_v(h, l), lo.lcap,
                                          P_(h, lo.ACT), lo.D + lo.F, h->st),
@@ -294,8 +306,9 @@ int run_token_decoder(bt_handle* h, int m, int s0) {
 // final LN of the token decoder at rows (b, slot) of X [B][m][D], then classifier + argmax
 int run_head(bt_handle* h, int m, int slot, int j, int32_t* d_next, float* d_logits) {
   const Layout& lo = h->lo;
+  const double E = (double)lo.elem, D = lo.D, Bd = h->B, V = lo.V;
   {
-    Prof p(h, PK_LN);
+    Prof p(h, PK_LN, Bd * D * (4.0 + E), 8.0 * Bd * D);
     BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_tok),
                                  ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps,
                                  (unsigned long long*)P_(h, lo.keys), h->B, h->st),
@@ -308,12 +321,12 @@ int run_head(bt_handle* h, int m, int slot, int j, int32_t* d_next, float* d_log
   ep.n_valid = lo.V;
   ep.keys = (unsigned long long*)P_(h, lo.keys);
   {
-    Prof p(h, PK_GEMM_HEAD);
+    Prof p(h, PK_GEMM_HEAD, V * D * E + Bd * D * E + (d_logits ? Bd * V * 4.0 : 0.0) + Bd * 8.0, 2.0 * Bd * V * D);
     BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.head), h->B, lo.f32 ? lo.V : lo.Vpad, lo.D,
                             EPI_ARGMAX, ep, h->st),
              "classifier");
   }
-  Prof p(h, PK_FINALIZE);
+  Prof p(h, PK_FINALIZE, Bd * 16.0, 0.0);
   BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->B, d_next, (int32_t*)P_(h, lo.cur), lo.L,
                               j, h->st),
            "finalize");
@@ -323,8 +336,9 @@ int run_head(bt_handle* h, int m, int slot, int j, int32_t* d_next, float* d_log
 // context embedding of rows (b, slot) of X [B][m][D] -> prefix rows X [B][P][D]
 int run_prefix(bt_handle* h, int m, int slot) {
   const Layout& lo = h->lo;
+  const double E = (double)lo.elem, D = lo.D, Bd = h->B, PD = (double)lo.P * lo.D;
   {
-    Prof p(h, PK_LN);
+    Prof p(h, PK_LN, Bd * D * (4.0 + E), 8.0 * Bd * D);
     BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_blk),
                                  ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps, nullptr, 0, h->st),
              "context layernorm");
@@ -334,7 +348,7 @@ int run_prefix(bt_handle* h, int m, int slot) {
   ep.bias = (const float*)P_(h, lo.prefix_b);
   ep.out0 = P_(h, lo.X);
   ep.ld0 = lo.P * lo.D;
-  Prof p(h, PK_GEMM_PREFIX);
+  Prof p(h, PK_GEMM_PREFIX, PD * D * E + Bd * D * E + Bd * PD * 4.0 + PD * 4.0, 2.0 * Bd * PD * D);
   BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.prefix_w), h->B, lo.P * lo.D, lo.D, EPI_STORE,
                           ep, h->st),
            "prefix projection");
@@ -473,8 +487,10 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
   h->Tp = Tp;
   const int n0 = Tp / L;
   const int M = B * n0;
+  h->decode_phase = false;
+  const double E = (double)lo.elem, Dd = lo.D, Md = M;
   {
-    Prof p(h, PK_EMBED);
+    Prof p(h, PK_EMBED, Md * Dd * (lo.tab_elem + 4.0) + (double)B * T * 4.0, 0.0);
     BT_CHECK(h, launch_embed_prompt(d_prompt, B, T, Tp, h->cfg.pad_id, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De, L,
                                     (float*)P_(h, lo.X), h->st),
              "embed prompt");
@@ -483,13 +499,14 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
     int r = run_ln_qkv(h, lo.blk[l], M);
     if (r) return r;
     {
-      Prof p(h, PK_ROPE_SCATTER);
+      Prof p(h, PK_ROPE_SCATTER, Md * 4.0 * Dd * E, 6.0 * Md * Dd);
       BT_CHECK(h, launch_rope_scatter(lo.f32, P_(h, lo.QKV), B, n0, 0, lo.D, lo.H, lo.dh, (const float2*)P_(h, lo.rope),
                                       block_k(h, l), block_v(h, l), lo.ncap, true, h->st),
                "rope scatter");
     }
     {
-      Prof p(h, PK_ATTN_PREFILL);
+      Prof p(h, PK_ATTN_PREFILL, Md * Dd * E * 4.0,
+             4.0 * B * lo.H * lo.dh * (double)n0 * (n0 + 1) / 2.0);
       BT_CHECK(h, launch_prefill_attention(lo.f32, P_(h, lo.QKV), B, n0, lo.D, lo.H, lo.dh,
                                            (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
                                            P_(h, lo.ACT), lo.D + lo.F, h->st),
@@ -519,10 +536,12 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
   const int L = lo.L, P = lo.P;
   if ((int64_t)h->Tp + h->g + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "max_tokens reached");
   const int j = h->g % L;
+  h->decode_phase = true;
+  const double E = (double)lo.elem, Dd = lo.D, Bd = h->B;
   if (j == 0) {
     // the previous L_B emitted tokens complete a block: one block-decoder step
     {
-      Prof p(h, PK_EMBED);
+      Prof p(h, PK_EMBED, Bd * Dd * (lo.tab_elem + 4.0) + Bd * L * 4.0, 0.0);
       BT_CHECK(h, launch_embed_block((const int32_t*)P_(h, lo.cur), h->B, L, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De,
                                      (float*)P_(h, lo.X), h->st),
                "embed block");
@@ -532,7 +551,9 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
       int r = run_ln_qkv(h, lo.blk[l], h->B);
       if (r) return r;
       {
-        Prof p(h, PK_ATTN_DECODE);
+        // keys and values of entries [0, n) read once, the new entry written, q read, output written
+        Prof p(h, PK_ATTN_DECODE, Bd * lo.H * (double)n * lo.dh * 2.0 * E + Bd * Dd * E * 6.0,
+               4.0 * Bd * lo.H * lo.dh * (double)(n + 1));
         BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, n, lo.D, lo.H, lo.dh,
                                              (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
                                              P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part), lo.part_bytes, h->st),
@@ -552,7 +573,7 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
   } else {
     // one token-decoder position at local slot P + j - 1
     {
-      Prof p(h, PK_EMBED);
+      Prof p(h, PK_EMBED, Bd * Dd * (lo.tab_elem + 4.0) + Bd * 4.0, 0.0);
       BT_CHECK(h, launch_embed_token((const int32_t*)P_(h, lo.cur), h->B, L, j - 1, P_(h, lo.emb_tok), !lo.f32, lo.V,
                                      lo.D, (float*)P_(h, lo.X), h->st),
                "embed token");
@@ -591,19 +612,23 @@ int bt_profile_enable(bt_handle* h, int32_t on) {
   return BT_OK;
 }
 
-int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* launches) {
-  if (!h || !total_ms || !launches || n_kinds < PK_COUNT) return fail(BT_ERR_INVALID_ARG, "bad argument");
+int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* launches, double* bytes,
+                    double* flops) {
+  if (!h || !total_ms || !launches || !bytes || !flops || n_kinds < 2 * PK_COUNT)
+    return fail(BT_ERR_INVALID_ARG, "bad argument");
   for (int k = 0; k < n_kinds; ++k) {
-    total_ms[k] = 0.0;
+    total_ms[k] = bytes[k] = flops[k] = 0.0;
     launches[k] = 0;
   }
   hipError_t e = hipStreamSynchronize(h->st);
   if (e != hipSuccess) return hip_fail(h, e, "profile sync");
   for (auto& u : h->ev_used) {
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, h->ev_pool[u.second], h->ev_pool[u.second + 1]) == hipSuccess) {
-      total_ms[u.first] += ms;
-      launches[u.first] += 1;
+    if (hipEventElapsedTime(&ms, h->ev_pool[u.ev], h->ev_pool[u.ev + 1]) == hipSuccess) {
+      total_ms[u.kind] += ms;
+      launches[u.kind] += 1;
+      bytes[u.kind] += u.bytes;
+      flops[u.kind] += u.flops;
     }
   }
   h->ev_used.clear();

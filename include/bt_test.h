@@ -14,19 +14,23 @@
 extern "C" {
 #endif
 
-/* Kernel classes timed by the profiler, in this order (n_kinds >= 11):
- * 0 embedder gathers, 1 LayerNorms, 2 [q|k|v|up] GEMMs (with GELU), 3 [out|down] GEMMs (residual),
- * 4 prefix projection, 5 classifier + argmax, 6 prefill attention, 7 prefill rotary/KV scatter,
- * 8 block-attention decode (incl. split merge), 9 local attention, 10 greedy-id finalisation. */
+/* Kernel classes timed by the profiler (BT_PROFILE_KINDS of them): 0 embedder gathers,
+ * 1 LayerNorms, 2 [q|k|v|up] GEMMs (with GELU), 3 [out|down] GEMMs (residual add), 4 prefix
+ * projection, 5 classifier + argmax, 6 prefill attention, 7 prefill rotary/KV scatter, 8 block-
+ * attention decode (incl. split merge), 9 local attention, 10 greedy-id finalisation.  Each class is
+ * counted separately for launches made by bt_prefill (index k) and by bt_decode_step (index 11 + k). */
 #define BT_PROFILE_KINDS 11
 
 /* Start (on != 0) or stop recording a pair of HIP events around every kernel launch of the
  * handle, on the handle's stream.  Clears what was recorded before. */
 int bt_profile_enable(bt_handle* h, int32_t on);
 
-/* Synchronise the handle's stream and return, per kernel class, the summed event time (ms) and
- * the number of launches since bt_profile_enable; then clear the record. */
-int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* launches);
+/* Synchronise the handle's stream and return, for each of the 2 * BT_PROFILE_KINDS classes (n_kinds
+ * must be at least that), the summed event time in ms, the number of launches, and the summed
+ * algorithmic bytes and flops of those launches (the minimal traffic and arithmetic of each
+ * operation: weights and KV read once, activations read and written once).  Then clear the record. */
+int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* launches, double* bytes,
+                    double* flops);
 
 /* C[M][N] = scale * A[M][K] * W[N][K]^T in fp32, on `stream` (a hipStream_t).  dtype BT_FP32:
  * A and W fp32; BT_BF16: A and W fp16 (the library's matrix-operand type), K % 64 == 0,

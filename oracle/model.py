@@ -42,6 +42,7 @@ beyond the definitions: matmuls are numpy's.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
 
@@ -64,7 +65,7 @@ def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float) -> np.nd
 
 def gelu(x: np.ndarray) -> np.ndarray:
     """Exact GELU: x * Phi(x) with the Gaussian CDF written through erf."""
-    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
 
 
 def rope_cos_sin(positions: np.ndarray, d_head: int, base: float):

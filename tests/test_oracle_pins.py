@@ -266,3 +266,12 @@ def test_golden_cost_model_numbers():
         prev = om.greedy(om.decode_step(W, cfg, st, prev))
         assert st.kv_reads_local - before <= lb["max_entries"]
         assert st.local_kv_len <= lb["max_entries"]
+
+
+def test_float32_oracle_stays_float32():
+    """The large-shape oracle runs in the dtype of its weights (no silent promotion to float64)."""
+    cfg = tiny()
+    W = om.weights_as(wl.make_weights(cfg), np.float32)
+    ids, lg, st = om.generate(W, cfg, wl.make_prompt(cfg, batch=1, T=8), 6, keep_logits=True)
+    assert lg.dtype == np.float32 and st.block_caches[0].k.dtype == np.float32
+    assert om.gelu(np.ones(3, np.float32)).dtype == np.float32
