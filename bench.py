@@ -51,6 +51,7 @@ class Runner:
         self.stream = self.model.stream
         self.prompt = torch.from_numpy(prompt).cuda()
         self.ids = torch.empty((self.G, cfg.batch), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
 
     def step(self, ev=None):
         """One generation; optional events mark (start, after prefill, end) on the model's stream."""
@@ -184,7 +185,7 @@ def main():
                    "rate": roofline_of(k, v)["achieved"], "unit": roofline_of(k, v)["unit"]}
                for k, v in sorted(active.items(), key=lambda kv: -kv[1]["ms"])}
     for k, v in classes.items():
-        log(f"[bench]   {k:28s} {v['ms_per_step']:9.3f} ms/step  {v['launches']:6d} launches  {v['rate']:9.1f} {v['unit']}")
+        log(f"[bench]   {k:28s} {v['ms_per_step']:9.3f} ms/step  {v['launches']:8.1f} launches  {v['rate']:9.1f} {v['unit']}")
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(t["ms_per_step"], 3), "higher_is_better": True,

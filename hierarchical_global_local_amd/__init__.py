@@ -73,8 +73,9 @@ def lib() -> ctypes.CDLL:
     dp = ctypes.POINTER(ctypes.c_double)
     L.bt_profile_read.argtypes = [c_p, c_i32, dp, ctypes.POINTER(ctypes.c_int64), dp, dp]
     L.bt_test_gemm.argtypes = [c_i32, c_p, c_p, c_p, c_i32, c_i32, c_i32, ctypes.c_float, c_p]
+    L.bt_set_graphs.argtypes = [c_p, c_i32]
     for f in ("bt_init", "bt_prefill", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
-              "bt_profile_enable", "bt_profile_read", "bt_test_gemm"):
+              "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -117,14 +118,15 @@ class BlockTransformer:
     """One model instance bound to a CUDA/HIP stream.  Device memory is owned by torch tensors."""
 
     def __init__(self, model, weights: Mapping[str, np.ndarray], max_batch: int, max_tokens: int,
-                 device: str = "cuda:0", stream=None):
+                 device: str = "cuda:0", stream=None, graphs: bool = True):
         import torch
         self.torch = torch
         L = lib()
         self.model = model
         self.cfg = BtConfig.make(model, max_batch, max_tokens)
         self.device = torch.device(device)
-        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        # a stream of its own: decode steps are captured into HIP graphs, which the NULL stream forbids
+        self.stream = stream if stream is not None else torch.cuda.Stream(self.device)
         wbytes = L.bt_weights_bytes(ctypes.byref(self.cfg))
         if wbytes == 0:
             raise BtError(-1, L.bt_last_error().decode())
@@ -142,6 +144,7 @@ class BlockTransformer:
         del d_blob
         self.h = h
         self.batch = 0
+        check(L.bt_set_graphs(self.h, 1 if graphs else 0))
 
     def close(self) -> None:
         if getattr(self, "h", None):
@@ -155,6 +158,16 @@ class BlockTransformer:
             pass
 
     # ------------------------------------------------------------------ inference
+    def _order(self, *tensors) -> None:
+        """Make the library's stream wait for work already queued on the caller's current stream,
+        and tell torch's allocator that the tensors are used on the library's stream."""
+        cur = self.torch.cuda.current_stream(self.device)
+        if cur != self.stream:
+            self.stream.wait_stream(cur)
+            for t in tensors:
+                if t is not None:
+                    t.record_stream(self.stream)
+
     def prefill(self, prompt, out=None, logits=None):
         """prompt: int32 device tensor [B, T]; writes the first generated ids into ``out`` [B]."""
         torch = self.torch
@@ -162,6 +175,7 @@ class BlockTransformer:
         B, T = prompt.shape
         if out is None:
             out = torch.empty(B, dtype=torch.int32, device=self.device)
+        self._order(prompt, out, logits)
         check(lib().bt_prefill(self.h, prompt.data_ptr(), B, T, out.data_ptr(), _ptr(logits)))
         self.batch = B
         return out
@@ -170,8 +184,12 @@ class BlockTransformer:
         torch = self.torch
         if out is None:
             out = torch.empty(self.batch, dtype=torch.int32, device=self.device)
+        self._order(out, logits)
         check(lib().bt_decode_step(self.h, out.data_ptr(), _ptr(logits)))
         return out
+
+    def set_graphs(self, enable: bool) -> None:
+        check(lib().bt_set_graphs(self.h, 1 if enable else 0))
 
     def generate(self, prompt, G: int, logits_steps: Iterable[int] = ()):
         """Greedy generation of G tokens: ids [G, B] (device int32) and {step: logits [B, V] fp32}."""

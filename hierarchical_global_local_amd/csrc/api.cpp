@@ -133,8 +133,11 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.ACT = region(M * (D + F) * E);
   lo.part_bytes = (size_t)lo.Bmax * lo.H * 32 * (lo.dh + 2) * 4;
   lo.part = region(lo.part_bytes);
-  lo.keys = region((size_t)lo.Bmax * 8);
+  lo.keys = region((size_t)lo.Bmax * (lo.Vpad / 4 + 64) * 8);
+  lo.rpart_rows = (int)std::min<int64_t>(lo.Mmax, 1024);
+  lo.rpart = region((size_t)16 * lo.rpart_rows * D * 4);
   lo.cur = region((size_t)lo.Bmax * lo.L * 4);
+  lo.dstate = region(64);
   lo.total = w;
   return "";
 }
@@ -160,6 +163,13 @@ struct bt_handle {
   std::vector<Rec> ev_used;
   size_t ev_next = 0;
   bool decode_phase = false;  // classes are split by phase: prefill, decode
+  ResidPending pending{};     // split-K residual update not yet folded into X (nsplit = 0: none)
+  int head_nparts = 0;        // column groups of the last classifier launch
+  int dec_nsplit = 1;         // key splits of block-attention decode for this batch size
+  // decode steps replayed from HIP graphs, one per in-block offset j (0 = block step)
+  bool use_graphs = true;
+  int graph_B = -1;
+  std::vector<hipGraphExec_t> graphs;
 };
 
 namespace {
@@ -235,6 +245,8 @@ void* ln_buf(bt_handle* h, int which) {
 
 float wscale(const Layout& lo) { return lo.f32 ? 1.0f : kWeightUnscale; }
 
+const ResidPending* pending(bt_handle* h) { return h->pending.nsplit > 0 ? &h->pending : nullptr; }
+
 // LN1/LN2 -> [q|k|v|up] GEMM with bias (+GELU on the up part)
 int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows) {
   const Layout& lo = h->lo;
@@ -242,9 +254,10 @@ int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows) {
   const double E = (double)lo.elem, D = lo.D, N1 = 3.0 * lo.D + lo.F;
   {
     Prof p(h, PK_LN, rows * D * (4.0 + 2.0 * E), 8.0 * rows * D);
-    BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), rows, lo.D, 1, 0, lnp, ln_buf(h, 0), lnp + 2 * lo.D,
-                                 ln_buf(h, 1), lo.f32, h->cfg.ln_eps, nullptr, 0, h->st),
+    BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), rows, lo.D, 1, 0, lnp, ln_buf(h, 0), lnp + 2 * lo.D,
+                                 ln_buf(h, 1), lo.f32, h->cfg.ln_eps, pending(h), h->st),
              "layernorm");
+    h->pending.nsplit = 0;
   }
   Epi ep{};
   ep.wscale = wscale(lo);
@@ -271,6 +284,16 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
   ep.bias2 = (const float*)P_(h, w.b2) + lo.D;
   ep.out0 = P_(h, lo.X);
   ep.ld0 = lo.D;
+  ep.splits = rows <= lo.rpart_rows ? resid_splits(rows, lo.D, lo.D + lo.F) : 1;
+  ep.part = (float*)P_(h, lo.rpart);
+  if (ep.splits > 1) {
+    // the partial products are summed (with both biases) by the next LayerNorm
+    h->pending.part = ep.part;
+    h->pending.nsplit = ep.splits;
+    h->pending.part_rows = rows;
+    h->pending.bias_a = ep.bias;
+    h->pending.bias_b = ep.bias2;
+  }
   const double E = (double)lo.elem, D = lo.D, K2 = (double)lo.D + lo.F;
   Prof p(h, PK_GEMM_OUT, D * K2 * E + rows * K2 * E + 8.0 * rows * D + 8.0 * D, 2.0 * rows * D * K2);
   BT_CHECK(h, launch_gemm(lo.f32, P_(h, lo.ACT), nullptr, lo.D + lo.F, P_(h, w.w2), rows, lo.D, lo.D + lo.F,
@@ -303,16 +326,16 @@ int run_token_decoder(bt_handle* h, int m, int s0) {
   return BT_OK;
 }
 
-// final LN of the token decoder at rows (b, slot) of X [B][m][D], then classifier + argmax
-int run_head(bt_handle* h, int m, int slot, int j, int32_t* d_next, float* d_logits) {
+// final LN of the token decoder at rows (b, slot) of X [B][m][D], then classifier + partial argmax
+int run_head(bt_handle* h, int m, int slot, float* d_logits) {
   const Layout& lo = h->lo;
   const double E = (double)lo.elem, D = lo.D, Bd = h->B, V = lo.V;
   {
     Prof p(h, PK_LN, Bd * D * (4.0 + E), 8.0 * Bd * D);
-    BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_tok),
-                                 ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps,
-                                 (unsigned long long*)P_(h, lo.keys), h->B, h->st),
+    BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_tok),
+                                 ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps, pending(h), h->st),
              "final layernorm");
+    h->pending.nsplit = 0;
   }
   Epi ep{};
   ep.wscale = wscale(lo);
@@ -320,15 +343,22 @@ int run_head(bt_handle* h, int m, int slot, int j, int32_t* d_next, float* d_log
   ep.ld0 = lo.V;
   ep.n_valid = lo.V;
   ep.keys = (unsigned long long*)P_(h, lo.keys);
-  {
-    Prof p(h, PK_GEMM_HEAD, V * D * E + Bd * D * E + (d_logits ? Bd * V * 4.0 : 0.0) + Bd * 8.0, 2.0 * Bd * V * D);
-    BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.head), h->B, lo.f32 ? lo.V : lo.Vpad, lo.D,
-                            EPI_ARGMAX, ep, h->st),
-             "classifier");
-  }
-  Prof p(h, PK_FINALIZE, Bd * 16.0, 0.0);
-  BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->B, d_next, (int32_t*)P_(h, lo.cur), lo.L,
-                              j, h->st),
+  ep.keys_ld = h->B;
+  ep.nparts_out = &h->head_nparts;
+  Prof p(h, PK_GEMM_HEAD, V * D * E + Bd * D * E + (d_logits ? Bd * V * 4.0 : 0.0) + Bd * 8.0, 2.0 * Bd * V * D);
+  BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.head), h->B, lo.f32 ? lo.V : lo.Vpad, lo.D,
+                          EPI_ARGMAX, ep, h->st),
+           "classifier");
+  return BT_OK;
+}
+
+// greedy ids of in-block offset j into d_next and the current-block buffer; a block step also
+// advances the device block-KV length
+int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
+  const Layout& lo = h->lo;
+  Prof p(h, PK_FINALIZE, (double)h->B * 16.0, 0.0);
+  BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->head_nparts, h->B, h->B, d_next,
+                              (int32_t*)P_(h, lo.cur), lo.L, j, (int*)P_(h, lo.dstate), n_inc, h->st),
            "finalize");
   return BT_OK;
 }
@@ -339,9 +369,10 @@ int run_prefix(bt_handle* h, int m, int slot) {
   const double E = (double)lo.elem, D = lo.D, Bd = h->B, PD = (double)lo.P * lo.D;
   {
     Prof p(h, PK_LN, Bd * D * (4.0 + E), 8.0 * Bd * D);
-    BT_CHECK(h, launch_layernorm((const float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_blk),
-                                 ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps, nullptr, 0, h->st),
+    BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_blk),
+                                 ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps, pending(h), h->st),
              "context layernorm");
+    h->pending.nsplit = 0;
   }
   Epi ep{};
   ep.wscale = wscale(lo);
@@ -352,6 +383,74 @@ int run_prefix(bt_handle* h, int m, int slot) {
   BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.prefix_w), h->B, lo.P * lo.D, lo.D, EPI_STORE,
                           ep, h->st),
            "prefix projection");
+  return BT_OK;
+}
+
+
+void drop_graphs(bt_handle* h) {
+  for (hipGraphExec_t g : h->graphs)
+    if (g) (void)hipGraphExecDestroy(g);
+  h->graphs.clear();
+  h->graph_B = -1;
+}
+
+// host mirror of what a decode step at in-block offset j does to the caches
+void advance_host_state(bt_handle* h, int j) {
+  if (j == 0) {
+    h->n_blocks += 1;
+    h->local_len = h->lo.P;
+  } else {
+    h->local_len = h->lo.P + j;
+  }
+  h->pending.nsplit = 0;
+}
+
+// Enqueues one decode step up to and including the classifier (the greedy ids are finalised
+// separately).  Kernel arguments depend only on (batch, j); the block-KV length is read on the
+// device, so the same launch sequence is valid for every step with this j.
+int enqueue_decode(bt_handle* h, int j, float* d_logits) {
+  const Layout& lo = h->lo;
+  const int L = lo.L, P = lo.P;
+  const double E = (double)lo.elem, Dd = lo.D, Bd = h->B;
+  int r;
+  if (j == 0) {
+    // the previous L_B emitted tokens complete a block: one block-decoder step
+    {
+      Prof p(h, PK_EMBED, Bd * Dd * (lo.tab_elem + 4.0) + Bd * L * 4.0, 0.0);
+      BT_CHECK(h, launch_embed_block((const int32_t*)P_(h, lo.cur), h->B, L, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De,
+                                     (float*)P_(h, lo.X), h->st),
+               "embed block");
+    }
+    const int n = h->n_blocks;  // host mirror, for the profiler's byte count only
+    for (int l = 0; l < lo.Nb; ++l) {
+      if ((r = run_ln_qkv(h, lo.blk[l], h->B))) return r;
+      {
+        // keys and values of entries [0, n) read once, the new entry written, q read, output written
+        Prof p(h, PK_ATTN_DECODE, Bd * lo.H * (double)n * lo.dh * 2.0 * E + Bd * Dd * E * 6.0,
+               4.0 * Bd * lo.H * lo.dh * (double)(n + 1));
+        BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.D, lo.H,
+                                             lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l),
+                                             lo.ncap, P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part),
+                                             lo.part_bytes, h->dec_nsplit, h->st),
+                 "block attention decode");
+      }
+      if ((r = run_out(h, lo.blk[l], h->B))) return r;
+    }
+    if ((r = run_prefix(h, 1, 0))) return r;
+    if ((r = run_token_decoder(h, P, 0))) return r;
+    if ((r = run_head(h, P, P - 1, d_logits))) return r;
+  } else {
+    // one token-decoder position at local slot P + j - 1
+    {
+      Prof p(h, PK_EMBED, Bd * Dd * (lo.tab_elem + 4.0) + Bd * 4.0, 0.0);
+      BT_CHECK(h, launch_embed_token((const int32_t*)P_(h, lo.cur), h->B, L, j - 1, P_(h, lo.emb_tok), !lo.f32, lo.V,
+                                     lo.D, (float*)P_(h, lo.X), h->st),
+               "embed token");
+    }
+    if ((r = run_token_decoder(h, 1, P + j - 1))) return r;
+    if ((r = run_head(h, 1, 0, d_logits))) return r;
+  }
+  advance_host_state(h, j);
   return BT_OK;
 }
 
@@ -483,8 +582,11 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
   const int Tp = std::max(L, (T + L - 1) / L * L);
   if ((int64_t)Tp + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "padded prompt + 1 exceeds max_tokens");
   h->ready = false;
+  if (B != h->graph_B) drop_graphs(h);
   h->B = B;
   h->Tp = Tp;
+  h->pending.nsplit = 0;
+  h->dec_nsplit = decode_splits(B, lo.H, lo.ncap);
   const int n0 = Tp / L;
   const int M = B * n0;
   h->decode_phase = false;
@@ -492,7 +594,7 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
   {
     Prof p(h, PK_EMBED, Md * Dd * (lo.tab_elem + 4.0) + (double)B * T * 4.0, 0.0);
     BT_CHECK(h, launch_embed_prompt(d_prompt, B, T, Tp, h->cfg.pad_id, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De, L,
-                                    (float*)P_(h, lo.X), h->st),
+                                    (float*)P_(h, lo.X), (int*)P_(h, lo.dstate), h->st),
              "embed prompt");
   }
   for (int l = 0; l < lo.Nb; ++l) {
@@ -519,7 +621,9 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
   if (r) return r;
   r = run_token_decoder(h, lo.P, 0);
   if (r) return r;
-  r = run_head(h, lo.P, lo.P - 1, 0, d_next, d_logits);
+  r = run_head(h, lo.P, lo.P - 1, d_logits);
+  if (r) return r;
+  r = run_finalize(h, 0, d_next, 0);
   if (r) return r;
   h->n_blocks = n0;
   h->local_len = lo.P;
@@ -533,58 +637,51 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
   if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
   if (!h->ready) return fail(BT_ERR_STATE, "bt_decode_step before bt_prefill");
   const Layout& lo = h->lo;
-  const int L = lo.L, P = lo.P;
   if ((int64_t)h->Tp + h->g + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "max_tokens reached");
-  const int j = h->g % L;
+  const int j = h->g % lo.L;
   h->decode_phase = true;
-  const double E = (double)lo.elem, Dd = lo.D, Bd = h->B;
-  if (j == 0) {
-    // the previous L_B emitted tokens complete a block: one block-decoder step
-    {
-      Prof p(h, PK_EMBED, Bd * Dd * (lo.tab_elem + 4.0) + Bd * L * 4.0, 0.0);
-      BT_CHECK(h, launch_embed_block((const int32_t*)P_(h, lo.cur), h->B, L, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De,
-                                     (float*)P_(h, lo.X), h->st),
-               "embed block");
+  int r;
+  // graphs replay everything up to the classifier; the logits variant and profiling run eagerly
+  if (h->use_graphs && !d_logits && !h->prof && h->st != nullptr) {
+    if (h->graph_B != h->B) {
+      drop_graphs(h);
+      h->graphs.assign(lo.L, nullptr);
+      h->graph_B = h->B;
     }
-    const int n = h->n_blocks;
-    for (int l = 0; l < lo.Nb; ++l) {
-      int r = run_ln_qkv(h, lo.blk[l], h->B);
-      if (r) return r;
-      {
-        // keys and values of entries [0, n) read once, the new entry written, q read, output written
-        Prof p(h, PK_ATTN_DECODE, Bd * lo.H * (double)n * lo.dh * 2.0 * E + Bd * Dd * E * 6.0,
-               4.0 * Bd * lo.H * lo.dh * (double)(n + 1));
-        BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, n, lo.D, lo.H, lo.dh,
-                                             (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
-                                             P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part), lo.part_bytes, h->st),
-                 "block attention decode");
+    if (!h->graphs[j]) {
+      hipError_t e = hipStreamBeginCapture(h->st, hipStreamCaptureModeRelaxed);
+      if (e != hipSuccess) return hip_fail(h, e, "graph capture");
+      r = enqueue_decode(h, j, nullptr);
+      hipGraph_t graph = nullptr;
+      hipError_t e2 = hipStreamEndCapture(h->st, &graph);
+      if (r) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return r;
       }
-      r = run_out(h, lo.blk[l], h->B);
-      if (r) return r;
+      if (e2 != hipSuccess) return hip_fail(h, e2, "graph capture");
+      hipGraphExec_t exec = nullptr;
+      e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      (void)hipGraphDestroy(graph);
+      if (e != hipSuccess) return hip_fail(h, e, "graph instantiate");
+      h->graphs[j] = exec;
+    } else {
+      advance_host_state(h, j);
     }
-    h->n_blocks = n + 1;
-    int r = run_prefix(h, 1, 0);
-    if (r) return r;
-    r = run_token_decoder(h, P, 0);
-    if (r) return r;
-    r = run_head(h, P, P - 1, 0, d_next, d_logits);
-    if (r) return r;
-    h->local_len = P;
+    BT_CHECK(h, hipGraphLaunch(h->graphs[j], h->st), "graph launch");
   } else {
-    // one token-decoder position at local slot P + j - 1
-    {
-      Prof p(h, PK_EMBED, Bd * Dd * (lo.tab_elem + 4.0) + Bd * 4.0, 0.0);
-      BT_CHECK(h, launch_embed_token((const int32_t*)P_(h, lo.cur), h->B, L, j - 1, P_(h, lo.emb_tok), !lo.f32, lo.V,
-                                     lo.D, (float*)P_(h, lo.X), h->st),
-               "embed token");
-    }
-    int r = run_token_decoder(h, 1, P + j - 1);
+    r = enqueue_decode(h, j, d_logits);
     if (r) return r;
-    r = run_head(h, 1, 0, j, d_next, d_logits);
-    if (r) return r;
-    h->local_len = P + j;
   }
+  r = run_finalize(h, j, d_next, j == 0 ? 1 : 0);
+  if (r) return r;
   h->g += 1;
+  return BT_OK;
+}
+
+int bt_set_graphs(bt_handle* h, int32_t enable) {
+  if (!h) return fail(BT_ERR_INVALID_ARG, "NULL handle");
+  h->use_graphs = enable != 0;
+  if (!h->use_graphs) drop_graphs(h);
   return BT_OK;
 }
 
@@ -597,6 +694,7 @@ int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_k
 
 int bt_destroy(bt_handle* h) {
   if (!h) return fail(BT_ERR_INVALID_ARG, "NULL handle");
+  drop_graphs(h);
   for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
   delete h;
   return BT_OK;

@@ -290,8 +290,8 @@ constexpr int kMaxChunk = 4096;
 constexpr int kMaxSplit = 32;
 
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, int n, int D, int H,
-                                                     const float2* __restrict__ rope, T* __restrict__ Kc,
+__global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, const int* __restrict__ n_ptr, int D,
+                                                     int H, const float2* __restrict__ rope, T* __restrict__ Kc,
                                                      T* __restrict__ VTc, int cap, T* __restrict__ ACT, int ld_act,
                                                      float* __restrict__ part, int nsplit, int chunk,
                                                      float scale_log2) {
@@ -304,6 +304,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   __shared__ float red[8];
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = *n_ptr;  // entries already cached; the new one goes to slot n
   const size_t bh = (size_t)b * H + h;
   T* __restrict__ K = Kc + bh * cap * DH;
   T* __restrict__ VT = VTc + bh * DH * cap;
@@ -343,12 +344,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
     float kv[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jb + u * 4 * KPW + kl;
-      if (j < jc_end)
-        load8(K + (size_t)j * DH + 8 * pp, kv[u]);
-      else
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kv[u][e] = 0.f;
+      // clamped rather than guarded, so that the U loads are in flight together
+      const int j = min(jb + u * 4 * KPW + kl, jc_end - 1);
+      load8(K + (size_t)j * DH + 8 * pp, kv[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -450,19 +448,17 @@ __global__ void k_attn_combine(const float* __restrict__ part, int H, int nsplit
 }
 
 template <typename T, int DH>
-static hipError_t launch_decode_t(const void* QKV, int B, int n, int D, int H, const float2* rope, void* Kc, void* Vc,
-                                  int cap, void* ACT, int ld_act, float* part, size_t part_bytes, hipStream_t st) {
-  const int nk = n + 1;
-  // enough workgroups to cover the chip (>= 1024), at most kMaxChunk keys per split
-  int nsplit = std::max((nk + kMaxChunk - 1) / kMaxChunk, std::min((1024 + B * H - 1) / (B * H), (nk + 255) / 256));
-  nsplit = std::max(1, std::min(nsplit, kMaxSplit));
-  int chunk = (nk + nsplit - 1) / nsplit;
+static hipError_t launch_decode_t(const void* QKV, int B, const int* n_ptr, int D, int H, const float2* rope, void* Kc,
+                                  void* Vc, int cap, void* ACT, int ld_act, float* part, size_t part_bytes, int nsplit,
+                                  hipStream_t st) {
+  // the split layout covers the whole capacity, so it does not depend on the current length n
+  // (which is read on the device); splits past n + 1 produce empty partials
+  int chunk = (cap + nsplit - 1) / nsplit;
   chunk = (chunk + 63) / 64 * 64;
-  nsplit = (nk + chunk - 1) / chunk;
   if (chunk > kMaxChunk) return hipErrorInvalidValue;
   if (nsplit > 1 && (size_t)B * H * nsplit * (DH + 2) * sizeof(float) > part_bytes) return hipErrorInvalidValue;
   const float sl2 = kLog2e / sqrtf((float)DH);
-  hipLaunchKernelGGL((k_attn_decode<T, DH>), dim3(nsplit, H, B), dim3(256), 0, st, (const T*)QKV, n, D, H, rope,
+  hipLaunchKernelGGL((k_attn_decode<T, DH>), dim3(nsplit, H, B), dim3(256), 0, st, (const T*)QKV, n_ptr, D, H, rope,
                      (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, part, nsplit, chunk, sl2);
   if (nsplit > 1)
     hipLaunchKernelGGL((k_attn_combine<T, DH>), dim3(H, B), dim3(DH), 0, st, (const float*)part, H, nsplit, (T*)ACT,
@@ -470,12 +466,20 @@ static hipError_t launch_decode_t(const void* QKV, int B, int n, int D, int H, c
   return hipGetLastError();
 }
 
-hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, int n, int D, int H, int dh, const float2* rope,
-                                    void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part, size_t part_bytes,
-                                    hipStream_t st) {
+int decode_splits(int B, int H, int cap) {
+  int s = (cap + kMaxChunk - 1) / kMaxChunk;                       // LDS holds at most kMaxChunk scores
+  if (B * H < 512) s = std::max(s, std::min((1024 + B * H - 1) / (B * H), (cap + 255) / 256));
+  return std::max(1, std::min(s, kMaxSplit));
+}
+
+hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int D, int H, int dh,
+                                    const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part,
+                                    size_t part_bytes, int nsplit, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-#define BT_DEC(T, DHV) \
-  if (dh == DHV) return launch_decode_t<T, DHV>(QKV, B, n, D, H, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, st);
+#define BT_DEC(T, DHV)                                                                                            \
+  if (dh == DHV)                                                                                                  \
+    return launch_decode_t<T, DHV>(QKV, B, n_ptr, D, H, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, nsplit, \
+                                   st);
   if (f32) {
     BT_DEC(float, 32) BT_DEC(float, 64) BT_DEC(float, 128)
   } else {

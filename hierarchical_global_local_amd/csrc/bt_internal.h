@@ -54,8 +54,11 @@ struct Layout {
   size_t ACT;   // T [Mmax][D + F]: attention output | GELU(up)
   size_t part;  // fp32 split-KV partials of block-attention decode
   size_t part_bytes;
-  size_t keys;  // u64 [Bmax] argmax keys
+  size_t keys;  // u64 [nparts][Bmax] partial argmax keys of the classifier
+  size_t rpart; // fp32 [16][rpart_rows][D] split-K partials of the [out|down] GEMM (decode)
+  int rpart_rows;
   size_t cur;   // int32 [Bmax][L] ids of the block being generated
+  size_t dstate;  // int32 device state: [0] = block-KV entries per layer
   size_t total;
   size_t block_kv_bytes, local_kv_bytes;
   // canonical blob offsets (bytes)
@@ -82,8 +85,9 @@ hipError_t launch_rope_table(float2* tab, int npos, int dh, float base, hipStrea
 
 // ---- embedders
 // prompt blocks: X[b*n + i][o*De + d] = E[tok(b, i*L + o)][d], tok from the left-padded prompt
+// Also sets the device block-KV length *n_state = Tp / L.
 hipError_t launch_embed_prompt(const int32_t* prompt, int B, int T, int Tp, int pad, const void* E,
-                               bool tab_bf16, int V, int De, int L, float* X, hipStream_t st);
+                               bool tab_bf16, int V, int De, int L, float* X, int* n_state, hipStream_t st);
 // one completed block per row: X[b][o*De + d] = E[cur[b*L + o]][d]
 hipError_t launch_embed_block(const int32_t* cur, int B, int L, const void* E, bool tab_bf16, int V,
                               int De, float* X, hipStream_t st);
@@ -91,10 +95,19 @@ hipError_t launch_embed_block(const int32_t* cur, int B, int L, const void* E, b
 hipError_t launch_embed_token(const int32_t* cur, int B, int L, int j, const void* E, bool tab_bf16,
                               int V, int D, float* X, hipStream_t st);
 
-// ---- LayerNorm over rows r < rows of X[(r*stride + off)][:] -> out1 (params p1), out2 (p2, optional)
-hipError_t launch_layernorm(const float* X, int rows, int D, int stride, int off, const float* p1,
-                            void* out1, const float* p2, void* out2, bool out_f32, float eps,
-                            unsigned long long* reset_keys, int n_keys, hipStream_t st);
+// ---- LayerNorm over rows r < rows of X[(r*stride + off)][:] -> out1 (params p1), out2 (p2, optional).
+// With `resid` (split-K residual update pending), the row is first completed as
+//   x = X + sum_{s < nsplit} part[s][row][:] + bias_a + bias_b   (fixed summation order)
+// and written back to X.
+struct ResidPending {
+  const float* part;    // [nsplit][part_rows][D] fp32 partial products of the [out|down] GEMM
+  int nsplit, part_rows;
+  const float* bias_a;  // attn.out.b
+  const float* bias_b;  // mlp.down.b
+};
+hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, const float* p1, void* out1,
+                            const float* p2, void* out2, bool out_f32, float eps, const ResidPending* resid,
+                            hipStream_t st);
 
 // ---- GEMM: C[M][N] = A[M][K] * W[N][K]^T with an epilogue
 enum EpiMode { EPI_QKV_GELU = 0, EPI_RESID = 1, EPI_STORE = 2, EPI_ARGMAX = 3 };
@@ -108,8 +121,16 @@ struct Epi {
   int n_split;              // QKV_GELU: columns >= n_split take A2 and go through GELU into out1
   int act_col0;             // QKV_GELU: first ACT column of the GELU part
   int n_valid;              // ARGMAX: columns >= n_valid are padding
-  unsigned long long* keys; // ARGMAX: per-row packed (value, id) maxima
+  unsigned long long* keys; // ARGMAX: packed (value, id) maxima, [nparts][keys_ld]: one entry per row
+                            // for every column group (written in full by each launch)
+  int keys_ld;
+  int* nparts_out;          // ARGMAX: receives the number of column groups
+  int splits;               // RESID: K is split over `splits` workgroups per tile (1 = no split)
+  float* part;              // RESID with splits > 1: [splits][M][N] fp32 partial products (no bias)
 };
+// Number of K splits the [out|down] GEMM uses for M rows (1 for large M); also the partial count
+// the next LayerNorm must reduce.
+int resid_splits(int M, int N, int K);
 hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N,
                        int K, EpiMode mode, const Epi& ep, hipStream_t st);
 
@@ -123,17 +144,21 @@ hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, 
 hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int D, int H, int dh,
                                     const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
                                     int ld_act, hipStream_t st);
-// one new block-decoder position n per row: rotary, append K/V at slot n, attend over [0, n]
-hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, int n, int D, int H, int dh,
+// one new block-decoder position per row: n = *n_ptr (device state) entries are cached; rotary at
+// position n, append K/V at slot n, attend over [0, n].  nsplit = decode_splits(B, H, cap) splits of
+// the capacity (fixed for a batch size, so the launch does not depend on n).
+int decode_splits(int B, int H, int cap);
+hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int D, int H, int dh,
                                     const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
-                                    float* part, size_t part_bytes, hipStream_t st);
+                                    float* part, size_t part_bytes, int nsplit, hipStream_t st);
 // local attention: new slots [s0, s0 + m) per row; rotary at slot, write to local cache, attend over [0, slot]
 hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
                                   hipStream_t st);
 
-// ---- greedy ids from argmax keys: next[b] = id, cur[b*L + j] = id
-hipError_t launch_finalize(const unsigned long long* keys, int B, int32_t* next, int32_t* cur, int L, int j,
-                           hipStream_t st);
+// ---- greedy ids from the classifier's partial maxima [nparts][ld]: next[b] = id, cur[b*L + j] = id
+// The step that completes a block also advances the device block-KV length (*n_state += n_inc).
+hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, int B, int32_t* next, int32_t* cur,
+                           int L, int j, int* n_state, int n_inc, hipStream_t st);
 
 }  // namespace bt

@@ -41,18 +41,20 @@ __device__ __forceinline__ int xcd_contiguous_tile(int bid, int nb) {
   return x * per + min(x, rem) + i;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int BM, int BN, int WM, int WN, int MODE, int STAGES>
 __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, const f16* __restrict__ A2, int lda,
                                                    const f16* __restrict__ W, int M, int N, int K, Epi ep) {
   constexpr int BK = 64, LDK = BK + 8;  // +16 B per LDS row: conflict-free 16-byte fragment reads
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
   constexpr int CA = BM * BK / 8 / 256, CB = BN * BK / 8 / 256;
   static_assert(WM * WN == 4 && FM >= 1 && FN >= 1 && CA >= 1 && CB >= 1, "tile");
+  static_assert(STAGES >= 2 && STAGES % 2 == 0, "register stages alternate the two LDS buffers");
   __shared__ __attribute__((aligned(16))) f16 As[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) f16 Bs[2][BN * LDK];
 
   const int ntm = (M + BM - 1) / BM, ntn = N / BN;
-  const int t = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int lt = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int split = lt % ep.splits, t = lt / ep.splits;  // K slices of one tile are neighbours
   constexpr int GM = 8;
   const int group = t / (GM * ntn), first_m = group * GM;
   const int gm = min(GM, ntm - first_m);
@@ -64,30 +66,32 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  half8 ra[CA], rb[CB];
-  auto gload = [&](int k0) {
+  // STAGES K-steps of global loads are kept in flight in registers; each step's tile goes through
+  // one of two LDS buffers.
+  half8 ra[STAGES][CA], rb[STAGES][CB];
+  auto gload = [&](int st, int k0) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       int c = tid + i * 256, r = c / (BK / 8), kc = c % (BK / 8);
       int row = min(m0 + r, M - 1);
-      ra[i] = *(const half8*)(A + (size_t)row * lda + k0 + kc * 8);
+      ra[st][i] = *(const half8*)(A + (size_t)row * lda + k0 + kc * 8);
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       int c = tid + i * 256, r = c / (BK / 8), kc = c % (BK / 8);
-      rb[i] = *(const half8*)(W + (size_t)(n0 + r) * K + k0 + kc * 8);
+      rb[st][i] = *(const half8*)(W + (size_t)(n0 + r) * K + k0 + kc * 8);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int st, int buf) {
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
       int c = tid + i * 256, r = c / (BK / 8), kc = c % (BK / 8);
-      *(half8*)&As[buf][r * LDK + kc * 8] = ra[i];
+      *(half8*)&As[buf][r * LDK + kc * 8] = ra[st][i];
     }
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       int c = tid + i * 256, r = c / (BK / 8), kc = c % (BK / 8);
-      *(half8*)&Bs[buf][r * LDK + kc * 8] = rb[i];
+      *(half8*)&Bs[buf][r * LDK + kc * 8] = rb[st][i];
     }
   };
 
@@ -97,30 +101,37 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = float4_{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  const int nk_all = K / BK, per = (nk_all + ep.splits - 1) / ep.splits;
+  const int kt0 = split * per, nk = min(nk_all, kt0 + per);  // this workgroup's K tiles [kt0, nk)
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      half8 af[FM], bw[FN];
+  for (int st = 0; st < STAGES; ++st)
+    if (kt0 + st < nk) gload(st, (kt0 + st) * BK);
+  for (int kb = kt0; kb < nk; kb += STAGES) {
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[fm] = *(const half8*)&As[buf][(wm * TM + fm * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
+    for (int st = 0; st < STAGES; ++st) {
+      const int kt = kb + st;
+      if (kt < nk) {
+        const int buf = st & 1;
+        sstore(st, buf);
+        if (kt + STAGES < nk) gload(st, (kt + STAGES) * BK);
+        __syncthreads();
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        bw[fn] = *(const half8*)&Bs[buf][(wn * TN + fn * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
+        for (int kk = 0; kk < BK / 32; ++kk) {
+          half8 af[FM], bw[FN];
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
+          for (int fm = 0; fm < FM; ++fm)
+            af[fm] = *(const half8*)&As[buf][(wm * TM + fm * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+          for (int fn = 0; fn < FN; ++fn)
+            bw[fn] = *(const half8*)&Bs[buf][(wn * TN + fn * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+        }
+      }
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // epilogue: lane holds C[4*(lane/16) + i][lane % 16] of each 16 x 16 tile
@@ -146,19 +157,79 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
           unsigned long long other = shfl_xor_u64(best, o);
           best = other > best ? other : best;
         }
-        if ((lane & 15) == 0 && row < M && best) atomicMax(ep.keys + row, best);
+        if ((lane & 15) == 0 && row < M) ep.keys[(size_t)(tn * WN + wn) * ep.keys_ld + row] = best;
       }
   } else {
+    // Loads the epilogue needs (biases per column, the residual per element) are issued for all of
+    // this lane's outputs before any of them is used: no load sits behind a row guard, so they
+    // overlap instead of each waiting for the previous one.  Rows past M are clamped for loads and
+    // skipped for stores.
+    float bc[FN], bc2[FN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+      bc[fn] = (MODE == EPI_STORE && !ep.bias) ? 0.f : ep.bias[col];
+      bc2[fn] = MODE == EPI_RESID ? ep.bias2[col] : 0.f;
+    }
+    if constexpr (MODE == EPI_RESID) {
+      if (ep.splits > 1) {
+        // split-K: partial products go to ep.part[split]; biases and residual are added by the consumer
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i;
-          const int col = n0 + wn * TN + fn * 16 + (lane & 15);
-          if (row < M) epi_store<MODE, f16>(ep, row, col, acc[fm][fn][i] * ep.wscale);
-        }
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+              const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+              if (row < M) ep.part[((size_t)split * M + row) * N + col] = acc[fm][fn][i] * ep.wscale;
+            }
+        return;
+      }
+      float xo[FM][FN][4];
+      float* X = (float*)ep.out0;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = min(m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i, M - 1);
+            const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+            xo[fm][fn][i] = X[(size_t)row * ep.ld0 + col];
+          }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+            const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+            if (row < M)
+              X[(size_t)row * ep.ld0 + col] = xo[fm][fn][i] + (acc[fm][fn][i] * ep.wscale + bc[fn] + bc2[fn]);
+          }
+    } else {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+            const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+            if (row >= M) continue;
+            const float v = acc[fm][fn][i] * ep.wscale + bc[fn];
+            if constexpr (MODE == EPI_QKV_GELU) {
+              if (col < ep.n_split)
+                ((f16*)ep.out0)[(size_t)row * ep.ld0 + col] = to_f16(v);
+              else
+                ((f16*)ep.out1)[(size_t)row * ep.ld1 + ep.act_col0 + (col - ep.n_split)] = to_f16(gelu_erf(v));
+            } else {
+              ((float*)ep.out0)[(size_t)row * ep.ld0 + col] = v;
+            }
+          }
+    }
   }
 }
 
@@ -170,12 +241,14 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  const int kchunk = (K + gridDim.z - 1) / gridDim.z;
+  const int kbeg = blockIdx.z * kchunk, kend = min(K, kbeg + kchunk);
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
     for (int e = tid; e < 64 * 16; e += 256) {
       int r = e / 16, kk = e % 16;
       int gm = m0 + r, gn = n0 + r, gk = k0 + kk;
-      As[kk][r] = (gm < M && gk < K) ? A[(size_t)gm * lda + gk] : 0.f;
-      Ws[kk][r] = (gn < N && gk < K) ? W[(size_t)gn * K + gk] : 0.f;
+      As[kk][r] = (gm < M && gk < kend) ? A[(size_t)gm * lda + gk] : 0.f;
+      Ws[kk][r] = (gn < N && gk < kend) ? W[(size_t)gn * K + gk] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -193,40 +266,52 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + ty * 4 + i;
+    unsigned long long best = 0ull;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int row = m0 + ty * 4 + i, col = n0 + tx * 4 + j;
+      const int col = n0 + tx * 4 + j;
       if (row >= M || col >= N) continue;
-      float v = acc[i][j] * ep.wscale;
+      const float v = acc[i][j] * ep.wscale;
       if constexpr (MODE == EPI_ARGMAX) {
         if (col < ep.n_valid) {
           if (ep.out0) ((float*)ep.out0)[(size_t)row * ep.ld0 + col] = v;
-          atomicMax(ep.keys + row, argmax_key(v, col));
+          const unsigned long long k = argmax_key(v, col);
+          best = k > best ? k : best;
         }
+      } else if constexpr (MODE == EPI_RESID) {
+        if (ep.splits > 1)
+          ep.part[((size_t)blockIdx.z * M + row) * N + col] = v;
+        else
+          epi_store<MODE, float>(ep, row, col, v);
       } else {
         epi_store<MODE, float>(ep, row, col, v);
       }
     }
+    if constexpr (MODE == EPI_ARGMAX)
+      if (row < M) ep.keys[(size_t)(blockIdx.x * 16 + tx) * ep.keys_ld + row] = best;
+  }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int STAGES>
 static hipError_t launch_mfma_cfg(const void* A1, const void* A2, int lda, const void* W, int M, int N, int K,
                                   EpiMode mode, const Epi& ep, hipStream_t st) {
-  dim3 grid(((M + BM - 1) / BM) * (N / BN)), block(256);
+  if (mode == EPI_ARGMAX && ep.nparts_out) *ep.nparts_out = (N / BN) * WN;
+  dim3 grid(((M + BM - 1) / BM) * (N / BN) * ep.splits), block(256);
   const f16 *a1 = (const f16*)A1, *a2 = (const f16*)A2, *w = (const f16*)W;
   switch (mode) {
     case EPI_QKV_GELU:
-      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_QKV_GELU>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
+      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_QKV_GELU, STAGES>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
       break;
     case EPI_RESID:
-      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_RESID>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
+      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_RESID, STAGES>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
       break;
     case EPI_STORE:
-      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_STORE>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
+      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_STORE, STAGES>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
       break;
     case EPI_ARGMAX:
-      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_ARGMAX>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
+      hipLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, EPI_ARGMAX, STAGES>), grid, block, 0, st, a1, a2, lda, w, M, N, K, ep);
       break;
   }
   return hipGetLastError();
@@ -234,7 +319,8 @@ static hipError_t launch_mfma_cfg(const void* A1, const void* A2, int lda, const
 
 static hipError_t launch_f32(const float* A, int lda, const float* W, int M, int N, int K, EpiMode mode,
                              const Epi& ep, hipStream_t st) {
-  dim3 grid((N + 63) / 64, (M + 63) / 64), block(256);
+  if (mode == EPI_ARGMAX && ep.nparts_out) *ep.nparts_out = ((N + 63) / 64) * 16;
+  dim3 grid((N + 63) / 64, (M + 63) / 64, mode == EPI_RESID ? ep.splits : 1), block(256);
   switch (mode) {
     case EPI_QKV_GELU:
       hipLaunchKernelGGL(k_gemm_f32<EPI_QKV_GELU>, grid, block, 0, st, A, lda, W, M, N, K, ep);
@@ -252,9 +338,21 @@ static hipError_t launch_f32(const float* A, int lda, const float* W, int M, int
   return hipGetLastError();
 }
 
+// Split K only where the output tiles alone cannot fill the chip (decode: M is the batch).
+int resid_splits(int M, int N, int K) {
+  if (M > 1024) return 1;
+  const int tiles = ((M + 63) / 64) * (N / 64 > 0 ? N / 64 : 1);
+  const int nk = K / 64 > 0 ? K / 64 : 1;
+  int s = std::min(std::min(16, nk), std::max(1, (512 + tiles - 1) / tiles));  // <= 16: the LayerNorm folds at most 16
+  const int per = (nk + s - 1) / s;
+  return (nk + per - 1) / per;  // every split gets at least one K tile
+}
+
 hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N, int K,
-                       EpiMode mode, const Epi& ep, hipStream_t st) {
+                       EpiMode mode, const Epi& ep_in, hipStream_t st) {
   if (M <= 0) return hipSuccess;
+  Epi ep = ep_in;
+  if (mode != EPI_RESID || ep.splits < 1) ep.splits = 1;
   if (f32) {
     if (mode == EPI_QKV_GELU) {
       // two launches: the q|k|v columns from A1, then the GELU columns from A2
@@ -271,13 +369,14 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
   }
   // fp16 MFMA path: K % 64 == 0, N % 32 == 0 and n_split on a tile boundary (checked at plan time)
   const bool split_ok128 = (mode != EPI_QKV_GELU) || (ep.n_split % 128 == 0);
-  if (M > 1024 && N % 128 == 0 && split_ok128)
-    return launch_mfma_cfg<128, 128, 2, 2>(A1, A2, lda, W, M, N, K, mode, ep, st);
+  if (M > 1024 && N % 128 == 0 && split_ok128 && ep.splits == 1)
+    return launch_mfma_cfg<128, 128, 2, 2, 2>(A1, A2, lda, W, M, N, K, mode, ep, st);
+  if (ep.splits > 1) return launch_mfma_cfg<64, 64, 2, 2, 4>(A1, A2, lda, W, M, N, K, mode, ep, st);
   const long tiles64 = (long)((M + 63) / 64) * (N / 64);
-  if (N % 64 == 0 && tiles64 >= 512) return launch_mfma_cfg<64, 64, 2, 2>(A1, A2, lda, W, M, N, K, mode, ep, st);
+  if (N % 64 == 0 && tiles64 >= 512) return launch_mfma_cfg<64, 64, 2, 2, 4>(A1, A2, lda, W, M, N, K, mode, ep, st);
   const long tiles6432 = (long)((M + 63) / 64) * (N / 32);
-  if (tiles6432 >= 512) return launch_mfma_cfg<64, 32, 4, 1>(A1, A2, lda, W, M, N, K, mode, ep, st);
-  return launch_mfma_cfg<32, 32, 2, 2>(A1, A2, lda, W, M, N, K, mode, ep, st);
+  if (tiles6432 >= 512) return launch_mfma_cfg<64, 32, 4, 1, 6>(A1, A2, lda, W, M, N, K, mode, ep, st);
+  return launch_mfma_cfg<32, 32, 2, 2, 6>(A1, A2, lda, W, M, N, K, mode, ep, st);
 }
 
 }  // namespace bt

@@ -118,8 +118,9 @@ __device__ __forceinline__ int clamp_id(int t, int V) { return t < 0 ? 0 : (t >=
 template <typename Tt>
 __global__ __launch_bounds__(256) void k_embed_prompt(const int32_t* __restrict__ prompt, int T, int Tp, int pad,
                                                       const Tt* __restrict__ E, int V, int De, int L,
-                                                      float* __restrict__ X) {
+                                                      float* __restrict__ X, int* __restrict__ n_state) {
   const int n = Tp / L;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *n_state = n;
   const int row = blockIdx.x;  // b * n + i
   const int b = row / n, i = row % n;
   const int D = De * L;
@@ -132,14 +133,14 @@ __global__ __launch_bounds__(256) void k_embed_prompt(const int32_t* __restrict_
 }
 
 hipError_t launch_embed_prompt(const int32_t* prompt, int B, int T, int Tp, int pad, const void* E,
-                               bool tab_bf16, int V, int De, int L, float* X, hipStream_t st) {
+                               bool tab_bf16, int V, int De, int L, float* X, int* n_state, hipStream_t st) {
   dim3 grid(B * (Tp / L));
   if (tab_bf16)
     hipLaunchKernelGGL(k_embed_prompt<bf16_t>, grid, dim3(256), 0, st, prompt, T, Tp, pad, (const bf16_t*)E, V,
-                       De, L, X);
+                       De, L, X, n_state);
   else
     hipLaunchKernelGGL(k_embed_prompt<float>, grid, dim3(256), 0, st, prompt, T, Tp, pad, (const float*)E, V, De,
-                       L, X);
+                       L, X, n_state);
   return hipGetLastError();
 }
 
@@ -176,95 +177,188 @@ hipError_t launch_embed_token(const int32_t* cur, int B, int L, int j, const voi
 }
 
 // ---------------------------------------------------------------- LayerNorm
-// One wave per row, the row held in registers (PER values per lane, D <= 64 * PER); biased
-// variance from the centred values (two passes over registers).  Also clears the argmax keys
-// of the classifier that follows, when asked.
-template <int PER, typename To>
-__global__ __launch_bounds__(256) void k_layernorm(const float* __restrict__ X, int rows, int D, int stride,
-                                                   int off, const float* __restrict__ p1, To* __restrict__ o1,
-                                                   const float* __restrict__ p2, To* __restrict__ o2, float eps,
-                                                   unsigned long long* __restrict__ reset_keys, int n_keys) {
-  if (reset_keys) {
-    int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n_keys) reset_keys[i] = 0ull;
+// TPR threads per row (one wave for the many-row prefill case, a whole workgroup for the few-row
+// decode case), PER values per thread held in registers (D <= TPR * PER); biased variance from the
+// centred values.  Optionally completes a pending split-K residual update first (see ResidPending).
+template <int TPR>
+__device__ __forceinline__ float row_sum(float v, float* red) {
+  v = wave_sum(v);
+  if constexpr (TPR == 64) {
+    return v;
+  } else {
+    const int w = (threadIdx.x >> 6) & (TPR / 64 - 1);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < TPR / 64; ++i) t += red[i];
+    return t;
   }
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const float* x = X + ((size_t)r * stride + off) * D;
-  float v[PER];
-  float s = 0.f;
+}
+
+template <int TPR, int PER, typename To>
+__global__ __launch_bounds__(256) void k_layernorm(float* __restrict__ X, int rows, int D, int stride, int off,
+                                                   const float* __restrict__ p1, To* __restrict__ o1,
+                                                   const float* __restrict__ p2, To* __restrict__ o2, float eps,
+                                                   ResidPending rp) {
+  __shared__ float red[4];
+  constexpr int RPB = 256 / TPR;  // rows per block
+  constexpr int MAXS = 16;        // split-K partials folded in (at most)
+  const int t = threadIdx.x % TPR;
+  const int r = blockIdx.x * RPB + threadIdx.x / TPR;
+  if (TPR == 64 && r >= rows) return;  // (TPR == 256: one row per block, always valid)
+  const size_t xr = (size_t)r * stride + off;
+  float* __restrict__ x = X + xr * D;
+  const float* __restrict__ part = rp.part;
+  // Every load is issued before any arithmetic and none sits behind a divergent branch (indices
+  // are clamped and out-of-range values masked afterwards), so the row costs one memory round trip.
+  float v[PER], g1[PER], b1[PER], g2[PER], b2[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    int c = lane + 64 * j;
-    v[j] = c < D ? x[c] : 0.f;
-    s += v[j];
+    const int c = t + TPR * j;
+    const int cc = min(c, D - 1);
+    const float xv = x[cc];
+    v[j] = c < D ? xv : 0.f;
+    g1[j] = p1[cc];
+    b1[j] = p1[D + cc];
+    if (o2) {
+      g2[j] = p2[cc];
+      b2[j] = p2[D + cc];
+    }
   }
-  s = wave_sum(s);
+  if (rp.nsplit > 0) {
+    float add[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int cc = min(t + TPR * j, D - 1);
+      add[j] = rp.bias_a[cc] + rp.bias_b[cc];
+    }
+#pragma unroll
+    for (int q = 0; q < MAXS; ++q) {
+      const int qq = min(q, rp.nsplit - 1);
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int cc = min(t + TPR * j, D - 1);
+        const float pv = part[((size_t)qq * rp.part_rows + xr) * D + cc];
+        add[j] += q < rp.nsplit ? pv : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int c = t + TPR * j;
+      if (c < D) {
+        v[j] += add[j];
+        x[c] = v[j];
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) s += v[j];
+  s = row_sum<TPR>(s, red);
   const float mean = s / (float)D;
   float q = 0.f;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    int c = lane + 64 * j;
-    float d = c < D ? v[j] - mean : 0.f;
+    const int c = t + TPR * j;
+    const float d = c < D ? v[j] - mean : 0.f;
     q += d * d;
   }
-  q = wave_sum(q);
+  q = row_sum<TPR>(q, red);
   const float rstd = 1.0f / sqrtf(q / (float)D + eps);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    int c = lane + 64 * j;
+    const int c = t + TPR * j;
     if (c < D) {
-      float y = (v[j] - mean) * rstd;
-      store_from_f32(o1 + (size_t)r * D + c, y * p1[c] + p1[D + c]);
-      if (o2) store_from_f32(o2 + (size_t)r * D + c, y * p2[c] + p2[D + c]);
+      const float y = (v[j] - mean) * rstd;
+      store_from_f32(o1 + (size_t)r * D + c, y * g1[j] + b1[j]);
+      if (o2) store_from_f32(o2 + (size_t)r * D + c, y * g2[j] + b2[j]);
     }
   }
 }
 
-template <int PER>
-static void launch_ln_per(int blocks, const float* X, int rows, int D, int stride, int off, const float* p1,
-                          void* out1, const float* p2, void* out2, bool out_f32, float eps,
-                          unsigned long long* reset_keys, int n_keys, hipStream_t st) {
+template <int TPR, int PER>
+static void launch_ln_cfg(int rows, float* X, int D, int stride, int off, const float* p1, void* out1,
+                          const float* p2, void* out2, bool out_f32, float eps, const ResidPending& rp,
+                          hipStream_t st) {
+  const int blocks = (rows + 256 / TPR - 1) / (256 / TPR);
   if (out_f32)
-    hipLaunchKernelGGL((k_layernorm<PER, float>), dim3(blocks), dim3(256), 0, st, X, rows, D, stride, off, p1,
-                       (float*)out1, p2, (float*)out2, eps, reset_keys, n_keys);
+    hipLaunchKernelGGL((k_layernorm<TPR, PER, float>), dim3(blocks), dim3(256), 0, st, X, rows, D, stride, off, p1,
+                       (float*)out1, p2, (float*)out2, eps, rp);
   else
-    hipLaunchKernelGGL((k_layernorm<PER, f16>), dim3(blocks), dim3(256), 0, st, X, rows, D, stride, off, p1,
-                       (f16*)out1, p2, (f16*)out2, eps, reset_keys, n_keys);
+    hipLaunchKernelGGL((k_layernorm<TPR, PER, f16>), dim3(blocks), dim3(256), 0, st, X, rows, D, stride, off, p1,
+                       (f16*)out1, p2, (f16*)out2, eps, rp);
 }
 
-hipError_t launch_layernorm(const float* X, int rows, int D, int stride, int off, const float* p1, void* out1,
-                            const float* p2, void* out2, bool out_f32, float eps, unsigned long long* reset_keys,
-                            int n_keys, hipStream_t st) {
-  int blocks = std::max((rows + 3) / 4, (n_keys + 255) / 256);
-  if (blocks == 0) return hipSuccess;
-  int per = (D + 63) / 64;
-  if (per <= 2)
-    launch_ln_per<2>(blocks, X, rows, D, stride, off, p1, out1, p2, out2, out_f32, eps, reset_keys, n_keys, st);
-  else if (per <= 12)
-    launch_ln_per<12>(blocks, X, rows, D, stride, off, p1, out1, p2, out2, out_f32, eps, reset_keys, n_keys, st);
-  else if (per <= 32)
-    launch_ln_per<32>(blocks, X, rows, D, stride, off, p1, out1, p2, out2, out_f32, eps, reset_keys, n_keys, st);
-  else if (per <= 64)
-    launch_ln_per<64>(blocks, X, rows, D, stride, off, p1, out1, p2, out2, out_f32, eps, reset_keys, n_keys, st);
-  else
-    return hipErrorInvalidValue;
+hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, const float* p1, void* out1,
+                            const float* p2, void* out2, bool out_f32, float eps, const ResidPending* resid,
+                            hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  ResidPending rp{};
+  if (resid) rp = *resid;
+  if (rows <= 1024) {
+    // few rows: one workgroup per row
+    const int per = (D + 255) / 256;
+    if (per <= 1)
+      launch_ln_cfg<256, 1>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 3)
+      launch_ln_cfg<256, 3>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 8)
+      launch_ln_cfg<256, 8>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 16)
+      launch_ln_cfg<256, 16>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    const int per = (D + 63) / 64;
+    if (per <= 2)
+      launch_ln_cfg<64, 2>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 12)
+      launch_ln_cfg<64, 12>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 32)
+      launch_ln_cfg<64, 32>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 64)
+      launch_ln_cfg<64, 64>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- greedy ids
-__global__ void k_finalize(const unsigned long long* __restrict__ keys, int B, int32_t* __restrict__ next,
-                           int32_t* __restrict__ cur, int L, int j) {
-  int b = blockIdx.x * 256 + threadIdx.x;
-  if (b >= B) return;
-  int id = (int)(0xFFFFFFFFu - (unsigned)(keys[b] & 0xFFFFFFFFull));
-  next[b] = id;
-  cur[b * L + j] = id;
+// One workgroup per row reduces the classifier's partial maxima (packed value/id keys) in a fixed
+// order; the largest key is the largest logit with the lowest id among equals.
+__global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __restrict__ keys, int nparts, int ld,
+                                                  int32_t* __restrict__ next, int32_t* __restrict__ cur, int L,
+                                                  int j, int* __restrict__ n_state, int n_inc) {
+  __shared__ unsigned long long red[256];
+  const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0 && n_inc) *n_state += n_inc;
+  unsigned long long best = 0ull;
+  for (int p = threadIdx.x; p < nparts; p += 256) {
+    const unsigned long long k = keys[(size_t)p * ld + b];
+    best = k > best ? k : best;
+  }
+  red[threadIdx.x] = best;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) {
+      const unsigned long long k = red[threadIdx.x + o];
+      if (k > red[threadIdx.x]) red[threadIdx.x] = k;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int id = (int)(0xFFFFFFFFu - (unsigned)(red[0] & 0xFFFFFFFFull));
+    next[b] = id;
+    cur[b * L + j] = id;
+  }
 }
-hipError_t launch_finalize(const unsigned long long* keys, int B, int32_t* next, int32_t* cur, int L, int j,
-                           hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize, dim3((B + 255) / 256), dim3(256), 0, st, keys, B, next, cur, L, j);
+hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, int B, int32_t* next, int32_t* cur,
+                           int L, int j, int* n_state, int n_inc, hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_finalize, dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j, n_state, n_inc);
   return hipGetLastError();
 }
 

@@ -125,15 +125,23 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
  * would exceed max_tokens. */
 int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits);
 
+/* Decode steps are replayed from HIP graphs captured on first use (one per position inside a
+ * block; recaptured when the batch size changes) unless logits are requested or the stream is the
+ * NULL stream.  enable = 0 launches every kernel individually instead (same results, bit for bit).
+ * Default: enabled. */
+int bt_set_graphs(bt_handle* h, int32_t enable);
+
 /* Host mirror of the cache lengths after the last call: block-KV entries per
  * block-decoder layer and local-KV entries per token-decoder layer. */
 int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_kv_len);
 
 /* Read-only introspection of the workspace layout, for tests and tools.
- * which = 0: block-KV cache, laid out [N_blk][2 (K, V)][max_batch][n_heads][cap][d_head]
- *            with cap = ceil(max_tokens / L_B); keys are stored after the
- *            rotary embedding;
- * which = 1: local-KV cache, [N_tok][2][max_batch][n_heads][P + L_B][d_head].
+ * which = 0: block-KV cache [N_blk][2 (K, V)][max_batch][n_heads][cap * d_head] with
+ *            cap = ceil(max_tokens / L_B) rounded up to a multiple of 64; per (layer,
+ *            row, head) the keys are [cap][d_head] (after the rotary embedding) and the
+ *            values are transposed, [d_head][cap];
+ * which = 1: local-KV cache [N_tok][2][max_batch][n_heads][P + L_B][d_head] (keys after
+ *            the rotary embedding, values not transposed).
  * Elements are fp16 for BT_BF16 and fp32 for BT_FP32.  Writes the byte
  * offset from the workspace start, the byte size and the per-head capacity. */
 int bt_workspace_region(const bt_config* cfg, int32_t which, size_t* offset, size_t* bytes,

@@ -46,15 +46,17 @@ def test_fp32_variants(kw, B, T, G):
     _fp32_case(wl.get_config("c0_tiny", **kw), B, T, G, seed=1)
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=2), dict(block_len=1, prefix_len=1),
-                                dict(block_len=8, prefix_len=2)])
-def test_bf16_small_every_step(kw):
+@pytest.mark.parametrize("kw,max_tokens", [(dict(), None), (dict(d_model=256, n_heads=2), None),
+                                           (dict(block_len=1, prefix_len=1), None), (dict(block_len=8, prefix_len=2), None),
+                                           (dict(), 4096)])
+def test_bf16_small_every_step(kw, max_tokens):
+    """max_tokens=4096 gives the block attention several key splits, most of them still empty."""
     cfg = SMALL_BF16.with_(**kw)
-    log(f"bf16 case {kw}")
+    log(f"bf16 case {kw} max_tokens={max_tokens}")
     W = wl.make_weights(cfg, seed=2, ln_jitter=True)
     prompt = wl.make_prompt(cfg, seed=2)
     G = cfg.gen_len
-    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G))
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G), max_tokens=max_tokens)
     W64 = om.weights_as(W, np.float64)
     _, ref_lg, st = om.generate(W64, cfg, prompt, G, keep_logits=True, forced=ids)
     gl = np.stack([lg[g] for g in range(G)], axis=1)
@@ -148,3 +150,28 @@ def test_host_side_errors():
         model.decode_step()
     assert e.value.code == -2
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(block_len=1, prefix_len=2)])
+def test_graph_replay_matches_eager(kw):
+    """Decode steps replayed from HIP graphs give the eagerly launched results bit for bit, over
+    repeated replays with other GPU work and synchronisations in between, and when steps that ask
+    for logits (launched eagerly) are interleaved with replayed ones."""
+    torch = require_gpu()
+    import hierarchical_global_local_amd as hg
+    cfg = SMALL_BF16.with_(**kw)
+    W = wl.make_weights(cfg, seed=7, ln_jitter=True)
+    prompt = torch.from_numpy(wl.make_prompt(cfg, seed=7)).cuda()
+    G = 23
+    eager = hg.BlockTransformer(cfg, W, max_batch=5, max_tokens=128, graphs=False)
+    ref_ids, ref_lg = eager.generate(prompt, G, logits_steps=range(G))
+    torch.cuda.synchronize()
+    graph = hg.BlockTransformer(cfg, W, max_batch=5, max_tokens=128, graphs=True)
+    for rep in range(3):
+        ids, lg = graph.generate(prompt, G, logits_steps=[3, 9] if rep == 1 else [])
+        junk = torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(ids, ref_ids), f"replay {rep}"
+        for g, v in lg.items():
+            assert torch.equal(v, ref_lg[g])
+        del junk
