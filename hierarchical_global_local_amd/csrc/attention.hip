@@ -86,7 +86,10 @@ hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, 
 }
 
 // ---------------------------------------------------------------- MFMA flash prefill (fp16)
-// grid (ceil(n/64), H, B), 4 waves x 16 queries.  MFMA 16x16x32 layouts (lane l, g = l / 16):
+// grid (ceil(n/64), H, B), 4 waves x 16 queries.  Each 64-key tile of K ([key][dh]) and V^T
+// ([dh][key]) is loaded once per workgroup with coalesced 16-byte loads into a double-buffered
+// LDS stage (the next tile's loads are in flight while the current one is used) and read by all
+// four waves.  MFMA 16x16x32 layouts (lane l, g = l / 16):
 //   A operand: row l % 16, k = 8g..8g+7;  B operand: column l % 16, same k;
 //   result:    column l % 16, rows 4g..4g+3.
 template <int DH>
@@ -96,11 +99,17 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
                                                        int ld_act, float scale_log2) {
   constexpr int KS = DH / 32;   // 32-wide dh slices of q and k
   constexpr int MT = DH / 16;   // 16-row dh tiles of O^T
+  constexpr int KLD = DH + 8;   // LDS row strides (+16 B: conflict-free fragment reads)
+  constexpr int VLD = 64 + 8;
+  constexpr int CK = 64 * DH / 8 / 256;  // 16-byte chunks per thread of a K tile
+  constexpr int CV = DH * 64 / 8 / 256;  // ... and of a V^T tile
+  __shared__ __attribute__((aligned(16))) f16 Ks[2][64 * KLD];
+  __shared__ __attribute__((aligned(16))) f16 Vs[2][DH * VLD];
+
   const int qt = gridDim.x - 1 - blockIdx.x;  // longest (latest) query tiles first
   const int h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int q0 = qt * 64 + wave * 16;
-  if (q0 >= n) return;
   const int qi = q0 + c16;
   const int qrow = min(qi, n - 1);
   const size_t bh = (size_t)b * H + h;
@@ -127,25 +136,56 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
       }
   }
 
+  // cooperative tile loads (keys beyond the cache capacity never occur: cap is a multiple of 64)
+  half8 rk[CK], rv[CV];
+  auto gload = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      const int c = tid + i * 256, r = c / (DH / 8), cc = c % (DH / 8);
+      rk[i] = *(const half8*)(K + (size_t)(kb + r) * DH + cc * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < CV; ++i) {
+      const int c = tid + i * 256, r = c / 8, cc = c % 8;
+      rv[i] = *(const half8*)(VT + (size_t)r * cap + kb + cc * 8);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      const int c = tid + i * 256, r = c / (DH / 8), cc = c % (DH / 8);
+      *(half8*)&Ks[buf][r * KLD + cc * 8] = rk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < CV; ++i) {
+      const int c = tid + i * 256, r = c / 8, cc = c % 8;
+      *(half8*)&Vs[buf][r * VLD + cc * 8] = rv[i];
+    }
+  };
+
   float4_ o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = float4_{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
-  const int klast = min(q0 + 15, n - 1);
+  const int ntiles = qt + 1;  // key tiles 0..qt (causal)
 
-  for (int kb = 0; kb <= klast; kb += 64) {
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1, kb = t * 64;
+    if (t + 1 < ntiles) gload(kb + 64);
     float4_ s[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       s[nt] = float4_{0.f, 0.f, 0.f, 0.f};
-      const f16* kp = K + (size_t)(kb + nt * 16 + c16) * DH + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        half8 kf = *(const half8*)(kp + 32 * ks);
+        const half8 kf = *(const half8*)&Ks[buf][(nt * 16 + c16) * KLD + 32 * ks + 8 * g];
         s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], s[nt], 0, 0, 0);
       }
     }
-    // causal mask and tile maximum for this lane's query column
+    // causal mask (only the diagonal tile has masked keys) and the tile maximum of this lane's query
     float mx = -INFINITY;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -188,7 +228,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const f16* vp = VT + (size_t)(mt * 16 + c16) * cap + kb + 32 * sl + 4 * g;
+        const f16* vp = &Vs[buf][(mt * 16 + c16) * VLD + 32 * sl + 4 * g];
         const half4 v0 = *(const half4*)vp;
         const half4 v1 = *(const half4*)(vp + 16);
         half8 vf;
@@ -200,6 +240,8 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
         o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[mt], 0, 0, 0);
       }
     }
+    if (t + 1 < ntiles) sstore(buf ^ 1);
+    __syncthreads();
   }
   if (qi < n) {
     const float inv = 1.0f / lrun;

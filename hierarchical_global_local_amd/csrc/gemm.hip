@@ -48,9 +48,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
   constexpr int CA = BM * BK / 8 / 256, CB = BN * BK / 8 / 256;
   static_assert(WM * WN == 4 && FM >= 1 && FN >= 1 && CA >= 1 && CB >= 1, "tile");
-  static_assert(STAGES >= 2 && STAGES % 2 == 0, "register stages alternate the two LDS buffers");
-  __shared__ __attribute__((aligned(16))) f16 As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) f16 Bs[2][BN * LDK];
+  static_assert(STAGES == 1 || STAGES % 2 == 0, "register stages alternate the two LDS buffers");
+  __shared__ __attribute__((aligned(16))) f16 smem[2 * (BM + BN) * LDK];
+  f16(*As)[BM * LDK] = reinterpret_cast<f16(*)[BM * LDK]>(smem);
+  f16(*Bs)[BN * LDK] = reinterpret_cast<f16(*)[BN * LDK]>(smem + 2 * BM * LDK);
 
   const int ntm = (M + BM - 1) / BM, ntn = N / BN;
   const int lt = xcd_contiguous_tile(blockIdx.x, gridDim.x);
@@ -103,39 +104,119 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
 
   const int nk_all = K / BK, per = (nk_all + ep.splits - 1) / ep.splits;
   const int kt0 = split * per, nk = min(nk_all, kt0 + per);  // this workgroup's K tiles [kt0, nk)
+  auto mma = [&](int buf) {
 #pragma unroll
-  for (int st = 0; st < STAGES; ++st)
-    if (kt0 + st < nk) gload(st, (kt0 + st) * BK);
-  for (int kb = kt0; kb < nk; kb += STAGES) {
+    for (int kk = 0; kk < BK / 32; ++kk) {
+      half8 af[FM], bw[FN];
 #pragma unroll
-    for (int st = 0; st < STAGES; ++st) {
-      const int kt = kb + st;
-      if (kt < nk) {
-        const int buf = st & 1;
-        sstore(st, buf);
-        if (kt + STAGES < nk) gload(st, (kt + STAGES) * BK);
-        __syncthreads();
+      for (int fm = 0; fm < FM; ++fm)
+        af[fm] = *(const half8*)&As[buf][(wm * TM + fm * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-          half8 af[FM], bw[FN];
+      for (int fn = 0; fn < FN; ++fn)
+        bw[fn] = *(const half8*)&Bs[buf][(wn * TN + fn * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
 #pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-            af[fm] = *(const half8*)&As[buf][(wm * TM + fm * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            bw[fn] = *(const half8*)&Bs[buf][(wn * TN + fn * 16 + (lane & 15)) * LDK + kk * 32 + (lane >> 4) * 8];
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+    }
+  };
+  if constexpr (STAGES == 1) {
+    // one register stage (large tiles, where registers bound the occupancy): the next K step is
+    // loaded while the current one is multiplied, then stored to the other LDS buffer
+    gload(0, kt0 * BK);
+    sstore(0, 0);
+    __syncthreads();
+    for (int kt = kt0; kt < nk; ++kt) {
+      const int buf = (kt - kt0) & 1;
+      if (kt + 1 < nk) gload(0, (kt + 1) * BK);
+      mma(buf);
+      if (kt + 1 < nk) sstore(0, buf ^ 1);
+      __syncthreads();
+    }
+  } else {
 #pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
+    for (int st = 0; st < STAGES; ++st)
+      if (kt0 + st < nk) gload(st, (kt0 + st) * BK);
+    for (int kb = kt0; kb < nk; kb += STAGES) {
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-              acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+      for (int st = 0; st < STAGES; ++st) {
+        const int kt = kb + st;
+        if (kt < nk) {
+          const int buf = st & 1;
+          sstore(st, buf);
+          if (kt + STAGES < nk) gload(st, (kt + STAGES) * BK);
+          __syncthreads();
+          mma(buf);
         }
       }
     }
   }
 
   // epilogue: lane holds C[4*(lane/16) + i][lane % 16] of each 16 x 16 tile
-  if constexpr (MODE == EPI_ARGMAX) {
+  constexpr bool kStaged = BM >= 128 && (MODE == EPI_QKV_GELU || MODE == EPI_RESID) &&
+                           BM * (BN + 4) * 4 <= 2 * (BM + BN) * LDK * 2;
+  if constexpr (kStaged) {
+    // Large tiles: the finished tile goes through LDS so that global stores are whole 16-byte
+    // row segments.  (Split-K never uses this tile size.)
+    constexpr int CLD = BN + 4;
+    float* Cs = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every wave is done reading the operand tiles
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int cl = wn * TN + fn * 16 + (lane & 15);
+      const float bias = ep.bias[n0 + cl] + (MODE == EPI_RESID ? ep.bias2[n0 + cl] : 0.f);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+          float v = acc[fm][fn][i] * ep.wscale + bias;
+          if constexpr (MODE == EPI_QKV_GELU)
+            if (n0 >= ep.n_split) v = gelu_erf(v);
+          Cs[rl * CLD + cl] = v;
+        }
+    }
+    __syncthreads();
+    if constexpr (MODE == EPI_QKV_GELU) {
+      f16* dst;
+      int ld, c0;
+      if (n0 < ep.n_split) {
+        dst = (f16*)ep.out0, ld = ep.ld0, c0 = n0;
+      } else {
+        dst = (f16*)ep.out1, ld = ep.ld1, c0 = ep.act_col0 + (n0 - ep.n_split);
+      }
+      constexpr int CH = BM * BN / 8 / 256;  // 8-wide chunks per thread
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        const int c = tid + q * 256, rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+        if (m0 + rl < M) {
+          half8 w;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = to_f16(Cs[rl * CLD + cl + e]);
+          *(half8*)(dst + (size_t)(m0 + rl) * ld + c0 + cl) = w;
+        }
+      }
+    } else {
+      constexpr int CH = BM * BN / 4 / 256;  // 4-wide chunks per thread
+      float* X = (float*)ep.out0;
+      float4 xo[CH];
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        const int c = tid + q * 256, rl = c / (BN / 4), cl = (c % (BN / 4)) * 4;
+        xo[q] = *(const float4*)(X + (size_t)min(m0 + rl, M - 1) * ep.ld0 + n0 + cl);
+      }
+#pragma unroll
+      for (int q = 0; q < CH; ++q) {
+        const int c = tid + q * 256, rl = c / (BN / 4), cl = (c % (BN / 4)) * 4;
+        if (m0 + rl < M) {
+          const float* cs = &Cs[rl * CLD + cl];
+          *(float4*)(X + (size_t)(m0 + rl) * ep.ld0 + n0 + cl) =
+              make_float4(xo[q].x + cs[0], xo[q].y + cs[1], xo[q].z + cs[2], xo[q].w + cs[3]);
+        }
+      }
+    }
+  } else if constexpr (MODE == EPI_ARGMAX) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -370,11 +451,12 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
   // fp16 MFMA path: K % 64 == 0, N % 32 == 0 and n_split on a tile boundary (checked at plan time)
   const bool split_ok128 = (mode != EPI_QKV_GELU) || (ep.n_split % 128 == 0);
   if (M > 1024 && N % 128 == 0 && split_ok128 && ep.splits == 1)
-    return launch_mfma_cfg<128, 128, 2, 2, 2>(A1, A2, lda, W, M, N, K, mode, ep, st);
+    return launch_mfma_cfg<128, 128, 2, 2, 1>(A1, A2, lda, W, M, N, K, mode, ep, st);
   if (ep.splits > 1) return launch_mfma_cfg<64, 64, 2, 2, 4>(A1, A2, lda, W, M, N, K, mode, ep, st);
   const long tiles64 = (long)((M + 63) / 64) * (N / 64);
   if (N % 64 == 0 && tiles64 >= 512) return launch_mfma_cfg<64, 64, 2, 2, 4>(A1, A2, lda, W, M, N, K, mode, ep, st);
   const long tiles6432 = (long)((M + 63) / 64) * (N / 32);
+  // decode shapes: small tiles keep several K steps in flight per workgroup
   if (tiles6432 >= 512) return launch_mfma_cfg<64, 32, 4, 1, 6>(A1, A2, lda, W, M, N, K, mode, ep, st);
   return launch_mfma_cfg<32, 32, 2, 2, 6>(A1, A2, lda, W, M, N, K, mode, ep, st);
 }
