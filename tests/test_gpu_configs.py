@@ -1,7 +1,8 @@
 """Parity at the full workload sizes (C1-C4): the GPU runs the whole configuration in the launch
 configuration the benchmark times; the oracle recomputes rows 0 and B-1 teacher-forced on the GPU's
-ids at sampled steps (logits <= 2e-2 max-abs, ids within the tolerance band), and the cache lengths
-follow the closed forms."""
+ids at every generation step: logits <= 2e-2 max-abs at the sampled steps where the GPU returned
+them, and every GPU id within the tolerance band of the oracle's argmax; the cache lengths follow
+the closed forms."""
 import time
 
 import numpy as np
@@ -34,11 +35,12 @@ def test_full_config_sampled_parity(name):
     del model
     worst = 0.0
     for r in (0, cfg.batch - 1):
-        ref = teacher_forced_logits(cfg, W, prompt[r], ids[r], steps)      # [S, V]
+        ref = teacher_forced_logits(cfg, W, prompt[r], ids[r], range(G))    # [G, V]
         got = np.stack([lg[g][r] for g in steps])
-        err = float(np.abs(got - ref).max())
+        err = float(np.abs(got - ref[steps]).max())
         worst = max(worst, err)
-        exact = check_ids_against(ref, ids[r, steps], BF16_TOL)
-        log(f"  row {r}: max-abs logit error {err:.3e}, exact argmax {exact:.3f}")
+        exact = check_ids_against(ref, ids[r], BF16_TOL)
+        log(f"  row {r}: max-abs logit error {err:.3e} ({len(steps)} steps), "
+            f"exact argmax {exact:.4f} over all {G} steps")
     log(f"  gpu {t1 - t0:.1f}s, oracle {time.time() - t1:.1f}s")
     assert worst <= BF16_TOL
