@@ -247,12 +247,13 @@ float wscale(const Layout& lo) { return lo.f32 ? 1.0f : kWeightUnscale; }
 
 const ResidPending* pending(bt_handle* h) { return h->pending.nsplit > 0 ? &h->pending : nullptr; }
 
-// LN1/LN2 -> [q|k|v|up] GEMM with bias (+GELU on the up part)
-int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows) {
+// LN1/LN2 -> [q|k|v|up] GEMM with bias (+GELU on the up part).  With ln_done the LayerNorm
+// outputs were already written (by the previous step's finalisation).
+int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows, bool ln_done = false) {
   const Layout& lo = h->lo;
   const float* lnp = (const float*)P_(h, w.ln);
   const double E = (double)lo.elem, D = lo.D, N1 = 3.0 * lo.D + lo.F;
-  {
+  if (!ln_done) {
     Prof p(h, PK_LN, rows * D * (4.0 + 2.0 * E), 8.0 * rows * D);
     BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), rows, lo.D, 1, 0, lnp, ln_buf(h, 0), lnp + 2 * lo.D,
                                  ln_buf(h, 1), lo.f32, h->cfg.ln_eps, pending(h), h->st),
@@ -303,11 +304,11 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
 }
 
 // token decoder over new local slots [s0, s0 + m) of every row (rows = B * m in X)
-int run_token_decoder(bt_handle* h, int m, int s0) {
+int run_token_decoder(bt_handle* h, int m, int s0, bool first_ln_done = false) {
   const Layout& lo = h->lo;
   const int rows = h->B * m;
   for (int l = 0; l < lo.Nt; ++l) {
-    int r = run_ln_qkv(h, lo.tok[l], rows);
+    int r = run_ln_qkv(h, lo.tok[l], rows, l == 0 && first_ln_done);
     if (r) return r;
     {
       const double E = (double)lo.elem, D = lo.D, Bd = h->B;
@@ -352,13 +353,28 @@ int run_head(bt_handle* h, int m, int slot, float* d_logits) {
   return BT_OK;
 }
 
-// greedy ids of in-block offset j into d_next and the current-block buffer; a block step also
-// advances the device block-KV length
+// Greedy ids of in-block offset j into d_next and the current-block buffer; a block step also
+// advances the device block-KV length.  The same kernel prepares the input of decode step g + 1
+// (g = the index of the token just chosen): its embedding row and first-layer LayerNorms.
 int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
   const Layout& lo = h->lo;
-  Prof p(h, PK_FINALIZE, (double)h->B * 16.0, 0.0);
+  NextStepArgs nx;
+  const bool next_is_block = (h->g + 1) % lo.L == 0;
+  nx.mode = next_is_block ? 2 : 1;
+  nx.E = next_is_block ? P_(h, lo.emb_block) : P_(h, lo.emb_tok);
+  nx.width = next_is_block ? lo.De : lo.D;
+  nx.tab_bf16 = !lo.f32;
+  nx.out_f32 = lo.f32;
+  nx.X = (float*)P_(h, lo.X);
+  nx.lnp = (const float*)P_(h, next_is_block ? lo.blk[0].ln : lo.tok[0].ln);
+  nx.ln1 = ln_buf(h, 0);
+  nx.ln2 = ln_buf(h, 1);
+  nx.D = lo.D;
+  nx.V = lo.V;
+  nx.eps = h->cfg.ln_eps;
+  Prof p(h, PK_FINALIZE, (double)h->B * (16.0 + lo.D * (lo.tab_elem + 4.0 + 2.0 * lo.elem)), 0.0);
   BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->head_nparts, h->B, h->B, d_next,
-                              (int32_t*)P_(h, lo.cur), lo.L, j, (int*)P_(h, lo.dstate), n_inc, h->st),
+                              (int32_t*)P_(h, lo.cur), lo.L, j, (int*)P_(h, lo.dstate), n_inc, nx, h->st),
            "finalize");
   return BT_OK;
 }
@@ -414,16 +430,11 @@ int enqueue_decode(bt_handle* h, int j, float* d_logits) {
   const double E = (double)lo.elem, Dd = lo.D, Bd = h->B;
   int r;
   if (j == 0) {
-    // the previous L_B emitted tokens complete a block: one block-decoder step
-    {
-      Prof p(h, PK_EMBED, Bd * Dd * (lo.tab_elem + 4.0) + Bd * L * 4.0, 0.0);
-      BT_CHECK(h, launch_embed_block((const int32_t*)P_(h, lo.cur), h->B, L, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De,
-                                     (float*)P_(h, lo.X), h->st),
-               "embed block");
-    }
+    // the previous L_B emitted tokens complete a block: one block-decoder step (its input block
+    // embedding and first LayerNorms were written by the previous finalisation)
     const int n = h->n_blocks;  // host mirror, for the profiler's byte count only
     for (int l = 0; l < lo.Nb; ++l) {
-      if ((r = run_ln_qkv(h, lo.blk[l], h->B))) return r;
+      if ((r = run_ln_qkv(h, lo.blk[l], h->B, l == 0))) return r;
       {
         // keys and values of entries [0, n) read once, the new entry written, q read, output written
         Prof p(h, PK_ATTN_DECODE, Bd * lo.H * (double)n * lo.dh * 2.0 * E + Bd * Dd * E * 6.0,
@@ -440,14 +451,9 @@ int enqueue_decode(bt_handle* h, int j, float* d_logits) {
     if ((r = run_token_decoder(h, P, 0))) return r;
     if ((r = run_head(h, P, P - 1, d_logits))) return r;
   } else {
-    // one token-decoder position at local slot P + j - 1
-    {
-      Prof p(h, PK_EMBED, Bd * Dd * (lo.tab_elem + 4.0) + Bd * 4.0, 0.0);
-      BT_CHECK(h, launch_embed_token((const int32_t*)P_(h, lo.cur), h->B, L, j - 1, P_(h, lo.emb_tok), !lo.f32, lo.V,
-                                     lo.D, (float*)P_(h, lo.X), h->st),
-               "embed token");
-    }
-    if ((r = run_token_decoder(h, 1, P + j - 1))) return r;
+    // one token-decoder position at local slot P + j - 1 (input row and first LayerNorms written
+    // by the previous finalisation)
+    if ((r = run_token_decoder(h, 1, P + j - 1, true))) return r;
     if ((r = run_head(h, 1, 0, d_logits))) return r;
   }
   advance_host_state(h, j);
@@ -582,6 +588,7 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
   const int Tp = std::max(L, (T + L - 1) / L * L);
   if ((int64_t)Tp + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "padded prompt + 1 exceeds max_tokens");
   h->ready = false;
+  h->g = 0;  // index of the token the prefill emits
   if (B != h->graph_B) drop_graphs(h);
   h->B = B;
   h->Tp = Tp;

@@ -88,13 +88,6 @@ hipError_t launch_rope_table(float2* tab, int npos, int dh, float base, hipStrea
 // Also sets the device block-KV length *n_state = Tp / L.
 hipError_t launch_embed_prompt(const int32_t* prompt, int B, int T, int Tp, int pad, const void* E,
                                bool tab_bf16, int V, int De, int L, float* X, int* n_state, hipStream_t st);
-// one completed block per row: X[b][o*De + d] = E[cur[b*L + o]][d]
-hipError_t launch_embed_block(const int32_t* cur, int B, int L, const void* E, bool tab_bf16, int V,
-                              int De, float* X, hipStream_t st);
-// one token per row: X[b][:] = E_tok[cur[b*L + j]]
-hipError_t launch_embed_token(const int32_t* cur, int B, int L, int j, const void* E, bool tab_bf16,
-                              int V, int D, float* X, hipStream_t st);
-
 // ---- LayerNorm over rows r < rows of X[(r*stride + off)][:] -> out1 (params p1), out2 (p2, optional).
 // With `resid` (split-K residual update pending), the row is first completed as
 //   x = X + sum_{s < nsplit} part[s][row][:] + bias_a + bias_b   (fixed summation order)
@@ -156,9 +149,23 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
                                   hipStream_t st);
 
-// ---- greedy ids from the classifier's partial maxima [nparts][ld]: next[b] = id, cur[b*L + j] = id
+// ---- greedy ids from the classifier's partial maxima [nparts][ld]: next[b] = id, cur[b*L + j] = id.
 // The step that completes a block also advances the device block-KV length (*n_state += n_inc).
+// With next.mode != 0 the same kernel writes the next decode step's input row into X and that
+// step's first-layer LN1/LN2 outputs (the next step then starts at its first GEMM).
+struct NextStepArgs {
+  int mode = 0;          // 0: none, 1: next step is a token step, 2: a block step
+  const void* E = nullptr;
+  int width = 0;         // table row width (D for the token table, D / L for the block embedder)
+  bool tab_bf16 = false, out_f32 = false;
+  float* X = nullptr;
+  const float* lnp = nullptr;
+  void* ln1 = nullptr;
+  void* ln2 = nullptr;
+  int D = 0, V = 0;
+  float eps = 1e-5f;
+};
 hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, int B, int32_t* next, int32_t* cur,
-                           int L, int j, int* n_state, int n_inc, hipStream_t st);
+                           int L, int j, int* n_state, int n_inc, const NextStepArgs& nxt, hipStream_t st);
 
 }  // namespace bt

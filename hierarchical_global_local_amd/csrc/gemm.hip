@@ -6,6 +6,8 @@
 // XCDs walks a contiguous range of output tiles, grouped 8 M-tiles at a time, so that A and W
 // tiles are re-read from that XCD's L2 rather than from HBM.
 // fp32 operands (BT_FP32): a plain LDS-tiled VALU kernel with the same epilogues.
+#include <cstdlib>
+
 #include "bt_internal.h"
 #include "device_common.h"
 
@@ -154,11 +156,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
   }
 
   // epilogue: lane holds C[4*(lane/16) + i][lane % 16] of each 16 x 16 tile
-  constexpr bool kStaged = BM >= 128 && (MODE == EPI_QKV_GELU || MODE == EPI_RESID) &&
-                           BM * (BN + 4) * 4 <= 2 * (BM + BN) * LDK * 2;
-  if constexpr (kStaged) {
-    // Large tiles: the finished tile goes through LDS so that global stores are whole 16-byte
-    // row segments.  (Split-K never uses this tile size.)
+  constexpr bool kStaged = (MODE == EPI_QKV_GELU || MODE == EPI_RESID) && BM * (BN + 4) * 4 <= 2 * (BM + BN) * LDK * 2;
+  if (kStaged && !(MODE == EPI_RESID && ep.splits > 1)) {
+    // The finished tile goes through LDS so that global stores are whole 16-byte row segments
+    // (split-K partials take the direct path below).
     constexpr int CLD = BN + 4;
     float* Cs = reinterpret_cast<float*>(smem);
     __syncthreads();  // every wave is done reading the operand tiles
@@ -186,10 +187,11 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
       } else {
         dst = (f16*)ep.out1, ld = ep.ld1, c0 = ep.act_col0 + (n0 - ep.n_split);
       }
-      constexpr int CH = BM * BN / 8 / 256;  // 8-wide chunks per thread
+      constexpr int CH = (BM * BN / 8 + 255) / 256;  // 8-wide chunks per thread
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
         const int c = tid + q * 256, rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+        if (c >= BM * BN / 8) break;
         if (m0 + rl < M) {
           half8 w;
 #pragma unroll
@@ -198,18 +200,18 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
         }
       }
     } else {
-      constexpr int CH = BM * BN / 4 / 256;  // 4-wide chunks per thread
+      constexpr int CH = (BM * BN / 4 + 255) / 256;  // 4-wide chunks per thread
       float* X = (float*)ep.out0;
       float4 xo[CH];
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
-        const int c = tid + q * 256, rl = c / (BN / 4), cl = (c % (BN / 4)) * 4;
+        const int c = min(tid + q * 256, BM * BN / 4 - 1), rl = c / (BN / 4), cl = (c % (BN / 4)) * 4;
         xo[q] = *(const float4*)(X + (size_t)min(m0 + rl, M - 1) * ep.ld0 + n0 + cl);
       }
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
         const int c = tid + q * 256, rl = c / (BN / 4), cl = (c % (BN / 4)) * 4;
-        if (m0 + rl < M) {
+        if (c < BM * BN / 4 && m0 + rl < M) {
           const float* cs = &Cs[rl * CLD + cl];
           *(float4*)(X + (size_t)(m0 + rl) * ep.ld0 + n0 + cl) =
               make_float4(xo[q].x + cs[0], xo[q].y + cs[1], xo[q].z + cs[2], xo[q].w + cs[3]);
@@ -426,7 +428,7 @@ int resid_splits(int M, int N, int K) {
   const int nk = K / 64 > 0 ? K / 64 : 1;
   int s = std::min(std::min(16, nk), std::max(1, (512 + tiles - 1) / tiles));  // <= 16: the LayerNorm folds at most 16
   const int per = (nk + s - 1) / s;
-  return (nk + per - 1) / per;  // every split gets at least one K tile
+  return (nk + per - 1) / per;  // every split gets at least one K tile of 64
 }
 
 hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N, int K,
@@ -450,7 +452,7 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
   }
   // fp16 MFMA path: K % 64 == 0, N % 32 == 0 and n_split on a tile boundary (checked at plan time)
   const bool split_ok128 = (mode != EPI_QKV_GELU) || (ep.n_split % 128 == 0);
-  if (M > 1024 && N % 128 == 0 && split_ok128 && ep.splits == 1)
+  if ((M > 1024 || (M >= 256 && mode == EPI_ARGMAX)) && N % 128 == 0 && split_ok128 && ep.splits == 1)
     return launch_mfma_cfg<128, 128, 2, 2, 1>(A1, A2, lda, W, M, N, K, mode, ep, st);
   if (ep.splits > 1) return launch_mfma_cfg<64, 64, 2, 2, 4>(A1, A2, lda, W, M, N, K, mode, ep, st);
   const long tiles64 = (long)((M + 63) / 64) * (N / 64);

@@ -144,38 +144,6 @@ hipError_t launch_embed_prompt(const int32_t* prompt, int B, int T, int Tp, int 
   return hipGetLastError();
 }
 
-template <typename Tt>
-__global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ cur, int L, int j0, int nt,
-                                                    const Tt* __restrict__ E, int V, int W,
-                                                    float* __restrict__ X) {
-  // row b: X[b][o*W + d] = E[cur[b*L + j0 + o]][d] for o < nt
-  const int b = blockIdx.x;
-  const int D = W * nt;
-  for (int c = threadIdx.x; c < D; c += 256) {
-    int o = c / W, d = c % W;
-    int tok = clamp_id(cur[b * L + j0 + o], V);
-    X[(size_t)b * D + c] = load_f32(E + (size_t)tok * W + d);
-  }
-}
-
-hipError_t launch_embed_block(const int32_t* cur, int B, int L, const void* E, bool tab_bf16, int V, int De,
-                              float* X, hipStream_t st) {
-  if (tab_bf16)
-    hipLaunchKernelGGL(k_embed_rows<bf16_t>, dim3(B), dim3(256), 0, st, cur, L, 0, L, (const bf16_t*)E, V, De, X);
-  else
-    hipLaunchKernelGGL(k_embed_rows<float>, dim3(B), dim3(256), 0, st, cur, L, 0, L, (const float*)E, V, De, X);
-  return hipGetLastError();
-}
-
-hipError_t launch_embed_token(const int32_t* cur, int B, int L, int j, const void* E, bool tab_bf16, int V, int D,
-                              float* X, hipStream_t st) {
-  if (tab_bf16)
-    hipLaunchKernelGGL(k_embed_rows<bf16_t>, dim3(B), dim3(256), 0, st, cur, L, j, 1, (const bf16_t*)E, V, D, X);
-  else
-    hipLaunchKernelGGL(k_embed_rows<float>, dim3(B), dim3(256), 0, st, cur, L, j, 1, (const float*)E, V, D, X);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------- LayerNorm
 // TPR threads per row (one wave for the many-row prefill case, a whole workgroup for the few-row
 // decode case), PER values per thread held in registers (D <= TPR * PER); biased variance from the
@@ -326,39 +294,138 @@ hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, cons
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- greedy ids
+// ---------------------------------------------------------------- greedy ids (+ next step's input)
 // One workgroup per row reduces the classifier's partial maxima (packed value/id keys) in a fixed
-// order; the largest key is the largest logit with the lowest id among equals.
+// order; the largest key is the largest logit with the lowest id among equals.  The same workgroup
+// then prepares the next decode step's input row: the embedding of the token just chosen (token
+// step) or of the block it completes (block step), and the first layer's LN1/LN2 of that row.
+struct NextStep {
+  int mode;              // 0: nothing, 1: token step (E_tok row), 2: block step (concat of E_emb rows)
+  const void* E;         // table of the next step's embedder
+  int width;             // row width of that table (D for E_tok, D / L for E_emb)
+  float* X;              // residual stream [B][D]
+  const float* lnp;      // first layer's LayerNorm parameters [4][D]
+  void* ln1;
+  void* ln2;
+  int D, V;
+  float eps;
+};
+
+template <int PER, typename Tt, typename To>
 __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __restrict__ keys, int nparts, int ld,
                                                   int32_t* __restrict__ next, int32_t* __restrict__ cur, int L,
-                                                  int j, int* __restrict__ n_state, int n_inc) {
+                                                  int j, int* __restrict__ n_state, int n_inc, NextStep ns) {
   __shared__ unsigned long long red[256];
-  const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x == 0 && n_inc) *n_state += n_inc;
+  __shared__ float redf[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (b == 0 && tid == 0 && n_inc) *n_state += n_inc;
   unsigned long long best = 0ull;
-  for (int p = threadIdx.x; p < nparts; p += 256) {
+  for (int p = tid; p < nparts; p += 256) {
     const unsigned long long k = keys[(size_t)p * ld + b];
     best = k > best ? k : best;
   }
-  red[threadIdx.x] = best;
+  red[tid] = best;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) {
-      const unsigned long long k = red[threadIdx.x + o];
-      if (k > red[threadIdx.x]) red[threadIdx.x] = k;
+    if (tid < o) {
+      const unsigned long long k = red[tid + o];
+      if (k > red[tid]) red[tid] = k;
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    const int id = (int)(0xFFFFFFFFu - (unsigned)(red[0] & 0xFFFFFFFFull));
+  const int id = (int)(0xFFFFFFFFu - (unsigned)(red[0] & 0xFFFFFFFFull));
+  if (tid == 0) {
     next[b] = id;
     cur[b * L + j] = id;
   }
+  if (ns.mode == 0) return;
+  const int D = ns.D;
+  const Tt* __restrict__ E = (const Tt*)ns.E;
+  float v[PER], g1[PER], b1[PER], g2[PER], b2[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = tid + 256 * q;
+    const int cc = min(c, D - 1);
+    int tok, col;
+    if (ns.mode == 1) {
+      tok = id, col = cc;
+    } else {
+      const int o = cc / ns.width;
+      tok = o == j ? id : cur[b * L + o];
+      col = cc - o * ns.width;
+    }
+    tok = tok < 0 ? 0 : (tok >= ns.V ? ns.V - 1 : tok);
+    const float e = load_f32(E + (size_t)tok * ns.width + col);
+    v[q] = c < D ? e : 0.f;
+    g1[q] = ns.lnp[cc];
+    b1[q] = ns.lnp[D + cc];
+    g2[q] = ns.lnp[2 * D + cc];
+    b2[q] = ns.lnp[3 * D + cc];
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) s += v[q];
+  s = row_sum<256>(s, redf);
+  const float mean = s / (float)D;
+  float var = 0.f;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = tid + 256 * q;
+    const float d = c < D ? v[q] - mean : 0.f;
+    var += d * d;
+  }
+  var = row_sum<256>(var, redf);
+  const float rstd = 1.0f / sqrtf(var / (float)D + ns.eps);
+  To* o1 = (To*)ns.ln1 + (size_t)b * D;
+  To* o2 = (To*)ns.ln2 + (size_t)b * D;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = tid + 256 * q;
+    if (c < D) {
+      ns.X[(size_t)b * D + c] = v[q];
+      const float y = (v[q] - mean) * rstd;
+      store_from_f32(o1 + c, y * g1[q] + b1[q]);
+      store_from_f32(o2 + c, y * g2[q] + b2[q]);
+    }
+  }
 }
+
+template <int PER>
+static void launch_fin_cfg(bool tab_bf16, bool out_f32, int B, const unsigned long long* keys, int nparts, int ld,
+                           int32_t* next, int32_t* cur, int L, int j, int* n_state, int n_inc, const NextStep& ns,
+                           hipStream_t st) {
+  if (tab_bf16) {
+    if (out_f32)
+      hipLaunchKernelGGL((k_finalize<PER, bf16_t, float>), dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j,
+                         n_state, n_inc, ns);
+    else
+      hipLaunchKernelGGL((k_finalize<PER, bf16_t, f16>), dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j,
+                         n_state, n_inc, ns);
+  } else {
+    if (out_f32)
+      hipLaunchKernelGGL((k_finalize<PER, float, float>), dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j,
+                         n_state, n_inc, ns);
+    else
+      hipLaunchKernelGGL((k_finalize<PER, float, f16>), dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j,
+                         n_state, n_inc, ns);
+  }
+}
+
 hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, int B, int32_t* next, int32_t* cur,
-                           int L, int j, int* n_state, int n_inc, hipStream_t st) {
+                           int L, int j, int* n_state, int n_inc, const NextStepArgs& a, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_finalize, dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j, n_state, n_inc);
+  NextStep ns{a.mode, a.E, a.width, a.X, a.lnp, a.ln1, a.ln2, a.D, a.V, a.eps};
+  const int per = (a.D + 255) / 256;
+  if (per <= 1)
+    launch_fin_cfg<1>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);
+  else if (per <= 3)
+    launch_fin_cfg<3>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);
+  else if (per <= 8)
+    launch_fin_cfg<8>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);
+  else if (per <= 16)
+    launch_fin_cfg<16>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
