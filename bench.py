@@ -125,6 +125,85 @@ def roofline_of(name, rec):
             "algorithmic_per_launch": per_launch}
 
 
+COPY_BYTES = 1 << 30
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_JSON = os.path.join(PROFILES, "traffic_decode_gemm_qkv_up.json")
+GEMM_SOURCE = os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", "gemm.hip")
+
+
+def _rocprof_db(d):
+    import glob
+    found = glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)
+    if not found:
+        raise FileNotFoundError(f"no rocprofv3 results database under {d}")
+    return found[0]
+
+
+def summarize_rocprof(d, top=25):
+    """Per-kernel totals of a rocprofv3 --kernel-trace run (the same figures --stats reports)."""
+    import sqlite3
+    cur = sqlite3.connect(_rocprof_db(d)).cursor()
+    rows = list(cur.execute("select name, count(*), sum(end-start), avg(end-start), min(end-start), max(end-start) "
+                            "from kernels group by name order by sum(end-start) desc"))
+    total = sum(r[2] for r in rows)
+    out = [f"{'total_ms':>10} {'pct':>6} {'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel"]
+    for name, n, tot, avg, mn, mx in rows[:top]:
+        out.append(f"{tot / 1e6:10.3f} {100 * tot / total:6.2f} {n:7d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f}  {name[:140]}")
+    return "\n".join(out)
+
+
+def _counter_per_dispatch(d, counter):
+    import sqlite3
+    cur = sqlite3.connect(_rocprof_db(d)).cursor()
+    rows = cur.execute("select kernel_name, counter_name, value from counters_collection")
+    per = {}
+    for kname, cname, value in rows:
+        if cname.startswith(counter):
+            per.setdefault(kname, []).append(float(value))
+    return per
+
+
+def source_hash(path=GEMM_SOURCE):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_counters(fetch_dir, write_dir, kernel_pattern):
+    """Average HBM bytes per dispatch of the kernel matching kernel_pattern, from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for the 1 GiB
+    reference copy (--copy-calibration).  Written to profiles/ with the GEMM source hash."""
+    fetch, write = _counter_per_dispatch(fetch_dir, "FETCH_SIZE"), _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    copy_f = next(v for k, v in fetch.items() if "copy" in k.lower() or "elementwise" in k.lower())
+    copy_w = next(v for k, v in write.items() if "copy" in k.lower() or "elementwise" in k.lower())
+    f_scale = COPY_BYTES / (max(copy_f) * 1024.0)
+    w_scale = COPY_BYTES / (max(copy_w) * 1024.0)
+    names = [k for k in fetch if kernel_pattern in k]
+    if not names:
+        raise KeyError(f"no kernel matches {kernel_pattern}")
+    name = names[0]
+    fb = sum(fetch[name]) / len(fetch[name]) * 1024.0 * f_scale
+    wb = sum(write[name]) / len(write[name]) * 1024.0 * w_scale
+    res = {"kernel": name, "dispatches": len(fetch[name]), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+           "traffic_bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
+           "gemm_source_sha256_16": source_hash()}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
+def stored_traffic():
+    """Counter-measured bytes per launch of the decode [q|k|v|up] GEMM, or None if absent or if the
+    GEMM source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t if t.get("gemm_source_sha256_16") == source_hash() else None
+
+
 def cpu_baseline(cfg, rows, tokens):
     """The oracle (numpy fp32, incremental prefill + decode) on a bounded sample of the workload."""
     import numpy as np
@@ -159,7 +238,21 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB device-to-device twice (reference kernel for HBM counter scaling)")
+    ap.add_argument("--summarize", metavar="ROCPROF_DIR", help="print a kernel summary of a rocprofv3 run and exit")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="HBM traffic of the dominant kernel from two rocprofv3 --pmc runs; writes profiles/")
+    ap.add_argument("--kernel", default=None, help="kernel-name pattern for --traffic")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="skip the event-profiled repeat (roofline null); for hardware-counter runs")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize_rocprof(args.summarize))
+        return
+    if args.traffic:
+        print(json.dumps(traffic_from_counters(args.traffic[0], args.traffic[1], args.kernel), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the Block Transformer path shards by batch rows with no "
               "exchange (each GPU would run this same step on its own rows); run with --gpus 1", file=sys.stderr)
@@ -168,24 +261,21 @@ def main():
     import torch
 
     import bt_workloads as wl
+    if args.copy_calibration:
+        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(2):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     cfg = wl.get_config(args.config)
     log(f"[bench] {describe(cfg)}")
     r = Runner(cfg)
     t = r.timed(args.steps, args.warmup)
     log(f"[bench] timed {args.steps} steps: {t['ms_per_step']:.2f} ms/step "
         f"(prefill {t['prefill_ms']:.2f} ms, decode {t['decode_ms']:.2f} ms)")
-    prof, prof_ms = r.profiled(args.steps)
     B, G = cfg.batch, cfg.gen_len
     value = B * G / (t["ms_per_step"] * 1e-3)
-    dec_bytes = sum(v["bytes"] for k, v in prof.items() if k.startswith("decode/"))
-    pre_flops = sum(v["flops"] for k, v in prof.items() if k.startswith("prefill/"))
-    active = {k: v for k, v in prof.items() if v["launches"]}
-    dominant = max(active, key=lambda k: active[k]["ms"])
-    classes = {k: {"ms_per_step": round(v["ms"], 3), "launches": v["launches"],
-                   "rate": roofline_of(k, v)["achieved"], "unit": roofline_of(k, v)["unit"]}
-               for k, v in sorted(active.items(), key=lambda kv: -kv[1]["ms"])}
-    for k, v in classes.items():
-        log(f"[bench]   {k:28s} {v['ms_per_step']:9.3f} ms/step  {v['launches']:8.1f} launches  {v['rate']:9.1f} {v['unit']}")
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(t["ms_per_step"], 3), "higher_is_better": True,
@@ -195,14 +285,30 @@ def main():
         "data": "synthetic (random-init N(0,0.02^2) weights, uniform random prompt ids)",
         "config": {"workload": describe(cfg), "global_batch": B, "seq_len": cfg.prompt_len, "gen_len": G},
         "prefill_ms": round(t["prefill_ms"], 3), "decode_ms": round(t["decode_ms"], 3),
-        "prefill_tflops": round(pre_flops / (t["prefill_ms"] * 1e-3) / 1e12, 2),
-        "decode_hbm_gbps": round(dec_bytes / (t["decode_ms"] * 1e-3) / 1e9, 1),
-        "roofline": roofline_of(dominant, prof[dominant]),
-        "profiled_ms_per_step": round(prof_ms, 3),
-        "kernel_classes": classes,
+        "roofline": None,
     }
-    result["roofline"]["measured"] = ("HIP events on the library's stream around every launch of the class, "
-                                      f"over a profiled repeat of the {args.steps} timed steps")
+    if not args.no_profile:
+        prof, prof_ms = r.profiled(args.steps)
+        dec_bytes = sum(v["bytes"] for k, v in prof.items() if k.startswith("decode/"))
+        pre_flops = sum(v["flops"] for k, v in prof.items() if k.startswith("prefill/"))
+        active = {k: v for k, v in prof.items() if v["launches"]}
+        dominant = max(active, key=lambda k: active[k]["ms"])
+        classes = {k: {"ms_per_step": round(v["ms"], 3), "launches": v["launches"],
+                       "rate": roofline_of(k, v)["achieved"], "unit": roofline_of(k, v)["unit"]}
+                   for k, v in sorted(active.items(), key=lambda kv: -kv[1]["ms"])}
+        for k, v in classes.items():
+            log(f"[bench]   {k:28s} {v['ms_per_step']:9.3f} ms/step  {v['launches']:8.1f} launches  {v['rate']:9.1f} {v['unit']}")
+        result["prefill_tflops"] = round(pre_flops / (t["prefill_ms"] * 1e-3) / 1e12, 2)
+        result["decode_hbm_gbps"] = round(dec_bytes / (t["decode_ms"] * 1e-3) / 1e9, 1)
+        result["roofline"] = roofline_of(dominant, prof[dominant])
+        result["roofline"]["measured"] = ("HIP events on the library's stream around every launch of the class, "
+                                          f"over a profiled repeat of the {args.steps} timed steps")
+        tr = stored_traffic()
+        if tr is not None and dominant == "decode/gemm_qkv_up":
+            result["roofline"]["traffic"] = round(tr["traffic_bytes_per_launch"], 1)
+            result["roofline"]["traffic_source"] = "profiles/traffic_decode_gemm_qkv_up.json (FETCH_SIZE + WRITE_SIZE)"
+        result["profiled_ms_per_step"] = round(prof_ms, 3)
+        result["kernel_classes"] = classes
     del r
     torch.cuda.empty_cache()
     if args.decode_config != "none":
@@ -213,6 +319,7 @@ def main():
         prof2, _ = r2.profiled(1)
         d_bytes = sum(v["bytes"] for k, v in prof2.items() if k.startswith("decode/"))
         att = prof2["decode/attn_block_decode"]
+        dom2 = max((k for k in prof2 if prof2[k]["launches"]), key=lambda k: prof2[k]["ms"])
         result["decode_heavy"] = {
             "workload": describe(c2), "value": round(c2.batch * c2.gen_len / (t2["ms_per_step"] * 1e-3), 1),
             "unit": "tokens/s", "ms_per_step": round(t2["ms_per_step"], 3),
@@ -220,6 +327,7 @@ def main():
             "decode_tokens_per_s": round(c2.batch * (c2.gen_len - 1) / (t2["decode_ms"] * 1e-3), 1),
             "decode_hbm_gbps": round(d_bytes / (t2["decode_ms"] * 1e-3) / 1e9, 1),
             "block_attn_decode": roofline_of("decode/attn_block_decode", att),
+            "dominant": roofline_of(dom2, prof2[dom2]),
         }
         log(f"[bench] decode-heavy: {result['decode_heavy']['value']:.0f} tokens/s, "
             f"decode {result['decode_heavy']['decode_hbm_gbps']} GB/s")
