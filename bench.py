@@ -234,8 +234,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c1_prefill_heavy")
     ap.add_argument("--decode-config", default="c2_decode_heavy", help="second workload reported alongside, or 'none'")
-    ap.add_argument("--cpu-rows", type=int, default=8)
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -244,6 +244,8 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="HBM traffic of the dominant kernel from two rocprofv3 --pmc runs; writes profiles/")
     ap.add_argument("--kernel", default=None, help="kernel-name pattern for --traffic")
+    ap.add_argument("--compare-vanilla", action="store_true",
+                    help="also time token-level transformers of the same width and depth on the same kernels")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip the event-profiled repeat (roofline null); for hardware-counter runs")
     args = ap.parse_args()
@@ -333,6 +335,23 @@ def main():
             f"decode {result['decode_heavy']['decode_hbm_gbps']} GB/s")
         del r2
         torch.cuda.empty_cache()
+    if args.compare_vanilla:
+        cmp = {}
+        for block_name, van_name in (("c1_prefill_heavy", "v1_vanilla_prefill_heavy"),
+                                     ("c2_decode_heavy", "v2_vanilla_decode_heavy")):
+            row = {}
+            for name in (block_name, van_name):
+                c = wl.get_config(name)
+                rr = Runner(c)
+                tt = rr.timed(1, 1)
+                row[name] = {"tokens_per_s": round(c.batch * c.gen_len / (tt["ms_per_step"] * 1e-3), 1),
+                             "prefill_ms": round(tt["prefill_ms"], 3), "decode_ms": round(tt["decode_ms"], 3)}
+                log(f"[bench] {name}: {row[name]}")
+                del rr
+                torch.cuda.empty_cache()
+            row["block_over_vanilla"] = round(row[block_name]["tokens_per_s"] / row[van_name]["tokens_per_s"], 2)
+            cmp[block_name] = row
+        result["vanilla_comparison"] = cmp
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_rows, cfg.batch), min(args.cpu_tokens, cfg.gen_len))

@@ -97,6 +97,14 @@ CONFIGS: Dict[str, Config] = {
                      batch=32, prompt_len=8192, gen_len=512),
     "c4_lb8": Config("c4_lb8", "bf16", **_D768, block_len=8, prefix_len=2,
                      batch=32, prompt_len=8192, gen_len=512),
+    # token-level (vanilla) transformers on the same kernels, at the d=768 width and the same total
+    # depth (12 layers) as the Block Transformers above: n_token_layers = 0 with L_B = 1
+    "v1_vanilla_prefill_heavy": Config("v1_vanilla_prefill_heavy", "bf16", vocab=50304, d_model=768, n_heads=12,
+                                       d_mlp=3072, n_block_layers=12, n_token_layers=0, block_len=1,
+                                       prefix_len=1, batch=64, prompt_len=2048, gen_len=128),
+    "v2_vanilla_decode_heavy": Config("v2_vanilla_decode_heavy", "bf16", vocab=50304, d_model=768, n_heads=12,
+                                      d_mlp=3072, n_block_layers=12, n_token_layers=0, block_len=1,
+                                      prefix_len=1, batch=256, prompt_len=128, gen_len=2048),
 }
 
 
@@ -132,8 +140,11 @@ def weight_specs(cfg: Config) -> List[Tuple[str, Tuple[int, ...], str]]:
     specs: List[Tuple[str, Tuple[int, ...], str]] = [("emb_block", (V, cfg.d_emb), "normal")]
     for l in range(cfg.n_block_layers):
         specs += _layer_specs(f"blk.{l}", D, F)
-    specs += [("blk.lnf.g", (D,), "ln_gain"), ("blk.lnf.b", (D,), "ln_bias"),
-              ("prefix.w", (D, P * D), "normal"), ("prefix.b", (P * D,), "normal"),
+    specs += [("blk.lnf.g", (D,), "ln_gain"), ("blk.lnf.b", (D,), "ln_bias")]
+    if cfg.n_token_layers == 0:
+        # token-level (vanilla) transformer: no prefix, no token decoder
+        return specs + [("head.w", (V, D), "normal")]
+    specs += [("prefix.w", (D, P * D), "normal"), ("prefix.b", (P * D,), "normal"),
               ("emb_token", (V, D), "normal")]
     for l in range(cfg.n_token_layers):
         specs += _layer_specs(f"tok.{l}", D, F)

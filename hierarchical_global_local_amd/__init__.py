@@ -92,7 +92,10 @@ def weight_names(model) -> List[str]:
              "mlp.up.w", "mlp.up.b", "mlp.down.w", "mlp.down.b"]
     names = ["emb_block"]
     names += [f"blk.{l}.{n}" for l in range(model.n_block_layers) for n in layer]
-    names += ["blk.lnf.g", "blk.lnf.b", "prefix.w", "prefix.b", "emb_token"]
+    names += ["blk.lnf.g", "blk.lnf.b"]
+    if model.n_token_layers == 0:  # token-level transformer
+        return names + ["head.w"]
+    names += ["prefix.w", "prefix.b", "emb_token"]
     names += [f"tok.{l}.{n}" for l in range(model.n_token_layers) for n in layer]
     names += ["tok.lnf.g", "tok.lnf.b", "head.w"]
     return names

@@ -42,7 +42,9 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   if (c.block_len < 1 || c.prefix_len < 1) return "block_len and prefix_len must be >= 1";
   if (c.d_model % c.block_len) return "d_model must be a multiple of block_len";
   if (c.prefix_len + c.block_len > 32) return "prefix_len + block_len must be <= 32";
-  if (c.n_block_layers < 1 || c.n_token_layers < 1) return "n_block_layers and n_token_layers must be >= 1";
+  if (c.n_block_layers < 1 || c.n_token_layers < 0) return "n_block_layers must be >= 1, n_token_layers >= 0";
+  if (c.n_token_layers == 0 && c.block_len != 1)
+    return "n_token_layers = 0 (token-level transformer) needs block_len = 1";
   if (c.d_model > 4096) return "d_model must be <= 4096";
   if (!f32 && (c.d_model % 64 || c.d_mlp % 64)) return "BT_BF16 needs d_model and d_mlp multiples of 64";
   if (c.max_batch < 1) return "max_batch must be >= 1";
@@ -64,6 +66,7 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.Bmax = c.max_batch;
   lo.max_tokens = c.max_tokens;
   lo.f32 = f32;
+  lo.vanilla = c.n_token_layers == 0;
   lo.elem = f32 ? 4 : 2;
   lo.tab_elem = f32 ? 4 : 2;
   lo.ncap = (int)align_up((size_t)nblk, 64);
@@ -89,25 +92,28 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   for (int l = 0; l < lo.Nb; ++l) lo.bl_blk.push_back(blob_layer());
   lo.bl_lnf_blk_g = take(D);
   lo.bl_lnf_blk_b = take(D);
-  lo.bl_prefix_w = take(D * P * D);
-  lo.bl_prefix_b = take(P * D);
-  lo.bl_emb_tok = take(V * D);
-  for (int l = 0; l < lo.Nt; ++l) lo.bl_tok.push_back(blob_layer());
-  lo.bl_lnf_tok_g = take(D);
-  lo.bl_lnf_tok_b = take(D);
+  if (!lo.vanilla) {  // a token-level transformer has no prefix projection and no token decoder
+    lo.bl_prefix_w = take(D * P * D);
+    lo.bl_prefix_b = take(P * D);
+    lo.bl_emb_tok = take(V * D);
+    for (int l = 0; l < lo.Nt; ++l) lo.bl_tok.push_back(blob_layer());
+    lo.bl_lnf_tok_g = take(D);
+    lo.bl_lnf_tok_b = take(D);
+  }
   lo.bl_head = take(V * D);
   lo.bl_total = o;
 
   // ---- workspace
   size_t w = 0;
   auto region = [&](size_t bytes) { size_t r = w; w = align_up(w + bytes, 256); return r; };
+  const size_t tokw = lo.vanilla ? 0 : 1;  // token-decoder side present
   lo.emb_block = region(V * lo.De * TE);
-  lo.emb_tok = region(V * D * TE);
+  lo.emb_tok = region(tokw * V * D * TE);
   lo.head = region((size_t)lo.Vpad * D * E);
   lo.lnf_blk = region(2 * D * 4);
-  lo.lnf_tok = region(2 * D * 4);
-  lo.prefix_w = region(P * D * D * E);
-  lo.prefix_b = region(P * D * 4);
+  lo.lnf_tok = region(tokw * 2 * D * 4);
+  lo.prefix_w = region(tokw * P * D * D * E);
+  lo.prefix_b = region(tokw * P * D * 4);
   lo.rope = region((size_t)lo.npos * (lo.dh / 2) * sizeof(float2));
   auto layer = [&]() {
     LayerOff L;
@@ -123,7 +129,7 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   for (int l = 0; l < lo.Nb; ++l) lo.blk.push_back(layer());
   for (int l = 0; l < lo.Nt; ++l) lo.tok.push_back(layer());
   lo.block_kv_bytes = (size_t)lo.Nb * 2 * lo.Bmax * lo.H * lo.ncap * lo.dh * E;
-  lo.local_kv_bytes = (size_t)lo.Nt * 2 * lo.Bmax * lo.H * lo.lcap * lo.dh * E;
+  lo.local_kv_bytes = (size_t)lo.Nt * 2 * lo.Bmax * lo.H * lo.lcap * lo.dh * E;  // 0 for Nt = 0
   lo.block_kv = region(lo.block_kv_bytes);
   lo.local_kv = region(lo.local_kv_bytes);
   const size_t M = (size_t)lo.Mmax;
@@ -332,8 +338,10 @@ int run_head(bt_handle* h, int m, int slot, float* d_logits) {
   const Layout& lo = h->lo;
   const double E = (double)lo.elem, D = lo.D, Bd = h->B, V = lo.V;
   {
+    // a token-level transformer classifies the block decoder's (token-level) output directly
+    const float* lnf = (const float*)P_(h, lo.vanilla ? lo.lnf_blk : lo.lnf_tok);
     Prof p(h, PK_LN, Bd * D * (4.0 + E), 8.0 * Bd * D);
-    BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_tok),
+    BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), h->B, lo.D, m, slot, lnf,
                                  ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps, pending(h), h->st),
              "final layernorm");
     h->pending.nsplit = 0;
@@ -366,7 +374,7 @@ int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
   nx.tab_bf16 = !lo.f32;
   nx.out_f32 = lo.f32;
   nx.X = (float*)P_(h, lo.X);
-  nx.lnp = (const float*)P_(h, next_is_block ? lo.blk[0].ln : lo.tok[0].ln);
+  nx.lnp = (const float*)P_(h, next_is_block ? lo.blk[0].ln : lo.tok[0].ln);  // (vanilla: always a block step)
   nx.ln1 = ln_buf(h, 0);
   nx.ln2 = ln_buf(h, 1);
   nx.D = lo.D;
@@ -414,7 +422,7 @@ void drop_graphs(bt_handle* h) {
 void advance_host_state(bt_handle* h, int j) {
   if (j == 0) {
     h->n_blocks += 1;
-    h->local_len = h->lo.P;
+    h->local_len = h->lo.vanilla ? 0 : h->lo.P;
   } else {
     h->local_len = h->lo.P + j;
   }
@@ -447,9 +455,13 @@ int enqueue_decode(bt_handle* h, int j, float* d_logits) {
       }
       if ((r = run_out(h, lo.blk[l], h->B))) return r;
     }
-    if ((r = run_prefix(h, 1, 0))) return r;
-    if ((r = run_token_decoder(h, P, 0))) return r;
-    if ((r = run_head(h, P, P - 1, d_logits))) return r;
+    if (lo.vanilla) {
+      if ((r = run_head(h, 1, 0, d_logits))) return r;
+    } else {
+      if ((r = run_prefix(h, 1, 0))) return r;
+      if ((r = run_token_decoder(h, P, 0))) return r;
+      if ((r = run_head(h, P, P - 1, d_logits))) return r;
+    }
   } else {
     // one token-decoder position at local slot P + j - 1 (input row and first LayerNorms written
     // by the previous finalisation)
@@ -536,9 +548,10 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
   INIT_CHECK(hipMemcpyAsync(h->ws + lo.emb_block, wb + lo.bl_emb_block, (size_t)lo.V * lo.De * lo.tab_elem,
                             hipMemcpyDeviceToDevice, h->st),
              "copy");
-  INIT_CHECK(hipMemcpyAsync(h->ws + lo.emb_tok, wb + lo.bl_emb_tok, (size_t)lo.V * D * lo.tab_elem,
-                            hipMemcpyDeviceToDevice, h->st),
-             "copy");
+  if (!lo.vanilla)
+    INIT_CHECK(hipMemcpyAsync(h->ws + lo.emb_tok, wb + lo.bl_emb_tok, (size_t)lo.V * D * lo.tab_elem,
+                              hipMemcpyDeviceToDevice, h->st),
+               "copy");
   auto repack_layer = [&](const Layout::BlobLayer& s, const LayerOff& d) -> hipError_t {
     hipError_t err;
     float* ln = (float*)(h->ws + d.ln);
@@ -563,13 +576,15 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
   float* lnf = (float*)(h->ws + lo.lnf_blk);
   INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_blk_g, bf, D, lnf, h->st), "repack");
   INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_blk_b, bf, D, lnf + D, h->st), "repack");
-  lnf = (float*)(h->ws + lo.lnf_tok);
-  INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_g, bf, D, lnf, h->st), "repack");
-  INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_b, bf, D, lnf + D, h->st), "repack");
-  INIT_CHECK(launch_transpose_convert(wb + lo.bl_prefix_w, bf, D, lo.P * D, h->ws + lo.prefix_w, f32, D, 0, 0, sc,
-                                      h->st),
-             "repack prefix");
-  INIT_CHECK(launch_to_f32(wb + lo.bl_prefix_b, bf, lo.P * D, (float*)(h->ws + lo.prefix_b), h->st), "repack");
+  if (!lo.vanilla) {
+    lnf = (float*)(h->ws + lo.lnf_tok);
+    INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_g, bf, D, lnf, h->st), "repack");
+    INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_b, bf, D, lnf + D, h->st), "repack");
+    INIT_CHECK(launch_transpose_convert(wb + lo.bl_prefix_w, bf, D, lo.P * D, h->ws + lo.prefix_w, f32, D, 0, 0, sc,
+                                        h->st),
+               "repack prefix");
+    INIT_CHECK(launch_to_f32(wb + lo.bl_prefix_b, bf, lo.P * D, (float*)(h->ws + lo.prefix_b), h->st), "repack");
+  }
   INIT_CHECK(launch_convert_rows(wb + lo.bl_head, bf, lo.V, D, lo.Vpad, h->ws + lo.head, f32, sc, h->st),
              "repack head");
   INIT_CHECK(launch_rope_table((float2*)(h->ws + lo.rope), lo.npos, lo.dh, cfg->rope_base, h->st), "rope table");
@@ -624,16 +639,18 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
     r = run_out(h, lo.blk[l], M);
     if (r) return r;
   }
-  int r = run_prefix(h, n0, n0 - 1);
-  if (r) return r;
-  r = run_token_decoder(h, lo.P, 0);
-  if (r) return r;
-  r = run_head(h, lo.P, lo.P - 1, d_logits);
-  if (r) return r;
+  int r;
+  if (lo.vanilla) {
+    if ((r = run_head(h, n0, n0 - 1, d_logits))) return r;
+  } else {
+    if ((r = run_prefix(h, n0, n0 - 1))) return r;
+    if ((r = run_token_decoder(h, lo.P, 0))) return r;
+    if ((r = run_head(h, lo.P, lo.P - 1, d_logits))) return r;
+  }
   r = run_finalize(h, 0, d_next, 0);
   if (r) return r;
   h->n_blocks = n0;
-  h->local_len = lo.P;
+  h->local_len = lo.vanilla ? 0 : lo.P;
   h->g = 1;
   h->ready = true;
   return BT_OK;

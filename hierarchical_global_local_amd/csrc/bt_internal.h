@@ -42,6 +42,7 @@ struct Layout {
   int Vpad;     // classifier rows padded to a multiple of 128
   int64_t Mmax; // activation rows
   bool f32;     // BT_FP32 mode (fp32 everywhere) vs fp16 operands
+  bool vanilla; // n_token_layers == 0: token-level transformer (block decoder + classifier)
   size_t elem;  // bytes per matrix / cache element (4 or 2)
   size_t tab_elem;  // bytes per embedding-table element (blob dtype)
   // workspace regions (byte offsets)

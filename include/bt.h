@@ -56,7 +56,10 @@ typedef enum {
 /* Model and capacity.  Constraints (checked by bt_init and the sizing calls):
  *   d_model % n_heads == 0, d_head = d_model / n_heads in {32, 64, 128};
  *   d_model % block_len == 0 (embedder width d_model / block_len, even);
- *   n_block_layers >= 1, n_token_layers >= 1, block_len >= 1, prefix_len >= 1;
+ *   n_block_layers >= 1, n_token_layers >= 0, block_len >= 1, prefix_len >= 1;
+ *   n_token_layers = 0 selects a token-level ("vanilla") transformer on the same kernels: it
+ *   needs block_len = 1, and the classifier reads the block decoder's final LayerNorm output
+ *   directly (no prefix projection, no token decoder, no local KV);
  *   BT_BF16 also needs d_model % 64 == 0 and d_mlp % 64 == 0;
  *   max_batch >= 1; max_tokens >= block_len (padded prompt + generated). */
 typedef struct {
@@ -84,6 +87,8 @@ typedef struct {
  *   per token layer: same twelve tensors as a block layer
  *   tok.lnf.g [D], tok.lnf.b [D]
  *   head.w [V, D]                      (output classifier, no bias)
+ * With n_token_layers = 0 the blob ends blk.lnf.g, blk.lnf.b, head.w (no prefix, token table,
+ * token layers or tok.lnf).
  * Linear maps are y = x W + b with W stored [in, out].  Returns 0 for an
  * invalid config (see bt_last_error). */
 size_t bt_weights_bytes(const bt_config* cfg);

@@ -36,6 +36,12 @@ listed, with reasons, in the design notes of this repository):
     tables (embedder, token embedding, classifier);
   - greedy decoding, ties to the lowest id.
 
+With n_token_layers = 0 (and L_B = 1) the same definitions describe a token-level
+("vanilla") transformer: the block decoder runs over tokens and its final LayerNorm
+output at position t-1 goes straight to the classifier to predict token t.  The pages
+compare Block Transformers against such Pythia-style models (§5 Evaluation Methodology,
+baselines).
+
 Computation runs in the dtype of the weights handed in (float64 for the exact
 checks, float32 for the large shapes).  No blocking, fusion or reordering
 beyond the definitions: matmuls are numpy's.
@@ -239,6 +245,11 @@ def context_embeddings(W: Weights, cfg, tokens: np.ndarray, n_blocks: int) -> np
     return block_decoder(W, cfg, embed_blocks(W, cfg, tokens[:, : n_blocks * L]))
 
 
+def is_vanilla(cfg) -> bool:
+    """Token-level transformer: no token decoder, one token per block."""
+    return cfg.n_token_layers == 0
+
+
 def logits_at(W: Weights, cfg, tokens: np.ndarray, positions: Sequence[int]) -> np.ndarray:
     """Logits predicting token t from tokens[:, :t], for each t in positions.
 
@@ -251,6 +262,9 @@ def logits_at(W: Weights, cfg, tokens: np.ndarray, positions: Sequence[int]) -> 
     assert all(L <= t <= tokens.shape[1] for t in positions)
     k_max = max(t // L for t in positions)
     c = context_embeddings(W, cfg, tokens, k_max)
+    if is_vanilla(cfg):
+        assert L == 1
+        return np.stack([output_logits(W, c[:, t - 1]) for t in positions], axis=1)
     out = np.empty((tokens.shape[0], len(positions), W["head.w"].shape[0]), dtype=c.dtype)
     by_block: Dict[int, List[int]] = {}
     for idx, t in enumerate(positions):
@@ -291,7 +305,10 @@ class State:
 
 
 def _new_prefix_pass(W: Weights, cfg, st: State, c_last: np.ndarray) -> np.ndarray:
-    """Reset the local caches, run the token decoder on the P prefix slots, return logits of slot P-1."""
+    """Reset the local caches, run the token decoder on the P prefix slots, return logits of slot P-1.
+    (Token-level transformer: the context embedding goes straight to the classifier.)"""
+    if is_vanilla(cfg):
+        return output_logits(W, c_last)
     P = cfg.prefix_len
     st.local_caches = [LayerCache() for _ in range(cfg.n_token_layers)]
     prefix = prefix_from_context(W, cfg, c_last)

@@ -175,3 +175,19 @@ def test_graph_replay_matches_eager(kw):
         for g, v in lg.items():
             assert torch.equal(v, ref_lg[g])
         del junk
+
+
+def test_vanilla_mode_fp32_and_bf16_every_step():
+    """n_token_layers = 0: a token-level transformer on the same kernels (the pages' baselines)."""
+    cfg = wl.get_config("c0_tiny", n_token_layers=0, block_len=1, n_block_layers=3)
+    _fp32_case(cfg, 2, 11, 9, seed=8)
+    cfg = SMALL_BF16.with_(n_token_layers=0, block_len=1, n_block_layers=3)
+    W = wl.make_weights(cfg, seed=8, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=8)
+    G = 15
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G))
+    _, ref_lg, st = om.generate(om.weights_as(W, np.float64), cfg, prompt, G, keep_logits=True, forced=ids)
+    gl = np.stack([lg[g] for g in range(G)], axis=1)
+    assert np.abs(gl - ref_lg).max() <= BF16_TOL
+    check_ids_against(ref_lg, ids, BF16_TOL)
+    assert model.cache_lengths() == (st.block_kv_len, 0)

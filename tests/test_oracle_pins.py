@@ -275,3 +275,19 @@ def test_float32_oracle_stays_float32():
     ids, lg, st = om.generate(W, cfg, wl.make_prompt(cfg, batch=1, T=8), 6, keep_logits=True)
     assert lg.dtype == np.float32 and st.block_caches[0].k.dtype == np.float32
     assert om.gelu(np.ones(3, np.float32)).dtype == np.float32
+
+
+def test_vanilla_mode_matches_library_and_incremental():
+    """n_token_layers = 0, L_B = 1: a standard token-level decoder (the pages' Pythia baselines)."""
+    cfg = tiny(n_token_layers=0, block_len=1, n_block_layers=3)
+    W = w64(cfg)
+    assert "emb_token" not in W and "prefix.w" not in W
+    x = np.random.default_rng(11).integers(0, cfg.vocab, (2, 12))
+    for t in (1, 5, 12):
+        np.testing.assert_allclose(om.logits_at(W, cfg, x, [t])[:, 0], tc.vanilla_logits(W, cfg, x, t), atol=1e-11)
+    prompt = wl.make_prompt(cfg, batch=2, T=7)
+    ids, lg, st = om.generate(W, cfg, prompt, 9, keep_logits=True)
+    seq = np.concatenate([prompt.astype(np.int64), ids], axis=1)
+    full = om.logits_at(W, cfg, seq, range(7, 16))
+    assert np.abs(full - lg).max() <= 1e-10
+    assert st.block_kv_len == 7 + 8 and st.local_kv_len == 0

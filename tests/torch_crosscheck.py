@@ -64,3 +64,10 @@ def block_logits(W, cfg, tokens, k):
     z = torch.cat([prefix, _t(W["emb_token"])[x[:, k * L: k * L + L - 1]]], dim=1)
     y = stack(W, "tok", cfg.n_token_layers, z, cfg)[:, P - 1:]
     return (y @ _t(W["head.w"]).T).numpy()
+
+
+def vanilla_logits(W, cfg, tokens, t):
+    """Token-level transformer: logits [B, V] predicting token t from tokens[:, :t]."""
+    x = torch.as_tensor(tokens[:, :t], dtype=torch.long)
+    h = stack(W, "blk", cfg.n_block_layers, _t(W["emb_block"])[x], cfg)
+    return (h[:, -1] @ _t(W["head.w"]).T).numpy()
