@@ -246,12 +246,15 @@ class BlockTransformer:
         return out
 
 
-def gemm(a, w, scale: float = 1.0, stream=None):
-    """C = scale * a @ w.T in fp32 through the library's GEMM kernels (a, w: fp32 or fp16 device tensors)."""
+def gemm(a, w, M: int, N: int, K: int, scale: float = 1.0, stream=None):
+    """C [M, N] = scale * A @ W.T in fp32 through the library's GEMM kernels.  a, w: fp32 row-major
+    [M, K] / [N, K] device tensors, or fp16 device tensors already in the library's operand order
+    (see bt_test_gemm in include/bt_test.h)."""
     import torch
     assert a.dtype == w.dtype and a.dtype in (torch.float32, torch.float16)
-    M, K = a.shape
-    N = w.shape[0]
+    assert a.is_contiguous() and w.is_contiguous()
+    rows_a = M if a.dtype == torch.float32 else (M + 15) // 16 * 16
+    assert a.numel() == rows_a * K and w.numel() == N * K
     c = torch.empty((M, N), dtype=torch.float32, device=a.device)
     st = stream if stream is not None else torch.cuda.current_stream(a.device)
     check(lib().bt_test_gemm(BT_FP32 if a.dtype == torch.float32 else BT_BF16, a.data_ptr(), w.data_ptr(),

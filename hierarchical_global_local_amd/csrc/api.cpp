@@ -74,6 +74,7 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.npos = std::max(lo.ncap, lo.lcap);
   lo.Vpad = (int)align_up((size_t)lo.V, 128);
   lo.Mmax = std::max<int64_t>((int64_t)lo.Bmax * nblk, (int64_t)lo.Bmax * lo.P);
+  lo.Mpad = (int64_t)align_up((size_t)lo.Mmax, 16);
 
   const size_t D = lo.D, F = lo.F, V = lo.V, P = lo.P, E = lo.elem, TE = lo.tab_elem;
   // ---- canonical blob
@@ -134,9 +135,9 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.local_kv = region(lo.local_kv_bytes);
   const size_t M = (size_t)lo.Mmax;
   lo.X = region(M * D * 4);
-  lo.LN = region(2 * M * D * E);
+  lo.LN = region(2 * (size_t)lo.Mpad * D * E);
   lo.QKV = region(M * 3 * D * E);
-  lo.ACT = region(M * (D + F) * E);
+  lo.ACT = region((size_t)lo.Mpad * (D + F) * E);
   lo.part_bytes = (size_t)lo.Bmax * lo.H * 32 * (lo.dh + 2) * 4;
   lo.part = region(lo.part_bytes);
   lo.keys = region((size_t)lo.Bmax * (lo.Vpad / 4 + 64) * 8);
@@ -246,7 +247,7 @@ void* local_v(bt_handle* h, int l) {
 }
 void* ln_buf(bt_handle* h, int which) {
   const Layout& lo = h->lo;
-  return P_(h, lo.LN + (size_t)which * lo.Mmax * lo.D * lo.elem);
+  return P_(h, lo.LN + (size_t)which * lo.Mpad * lo.D * lo.elem);
 }
 
 float wscale(const Layout& lo) { return lo.f32 ? 1.0f : kWeightUnscale; }
@@ -352,7 +353,7 @@ int run_head(bt_handle* h, int m, int slot, float* d_logits) {
   ep.ld0 = lo.V;
   ep.n_valid = lo.V;
   ep.keys = (unsigned long long*)P_(h, lo.keys);
-  ep.keys_ld = h->B;
+  ep.keys_ld = lo.Vpad / 4 + 64;
   ep.nparts_out = &h->head_nparts;
   Prof p(h, PK_GEMM_HEAD, V * D * E + Bd * D * E + (d_logits ? Bd * V * 4.0 : 0.0) + Bd * 8.0, 2.0 * Bd * V * D);
   BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.head), h->B, lo.f32 ? lo.V : lo.Vpad, lo.D,
@@ -381,7 +382,7 @@ int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
   nx.V = lo.V;
   nx.eps = h->cfg.ln_eps;
   Prof p(h, PK_FINALIZE, (double)h->B * (16.0 + lo.D * (lo.tab_elem + 4.0 + 2.0 * lo.elem)), 0.0);
-  BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->head_nparts, h->B, h->B, d_next,
+  BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->head_nparts, lo.Vpad / 4 + 64, h->B, d_next,
                               (int32_t*)P_(h, lo.cur), lo.L, j, (int*)P_(h, lo.dstate), n_inc, nx, h->st),
            "finalize");
   return BT_OK;
@@ -559,14 +560,27 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     if ((err = launch_to_f32(wb + s.ln1b, bf, D, ln + D, h->st))) return err;
     if ((err = launch_to_f32(wb + s.ln2g, bf, D, ln + 2 * D, h->st))) return err;
     if ((err = launch_to_f32(wb + s.ln2b, bf, D, ln + 3 * D, h->st))) return err;
-    if ((err = launch_transpose_convert(wb + s.qkvw, bf, D, 3 * D, h->ws + d.w1, f32, D, 0, 0, sc, h->st))) return err;
-    if ((err = launch_transpose_convert(wb + s.upw, bf, D, F, h->ws + d.w1, f32, D, 3 * D, 0, sc, h->st))) return err;
+    // canonical [in, out] matrices: element (n = out, k = in) at src[k * out + n]
+    if (f32) {
+      if ((err = launch_transpose_convert(wb + s.qkvw, bf, D, 3 * D, h->ws + d.w1, f32, D, 0, 0, sc, h->st))) return err;
+      if ((err = launch_transpose_convert(wb + s.upw, bf, D, F, h->ws + d.w1, f32, D, 3 * D, 0, sc, h->st))) return err;
+    } else {
+      if ((err = launch_pack_frag(wb + s.qkvw, bf, 1, 3 * D, 3 * D, 3 * D, D, h->ws + d.w1, D, 0, 0, sc, h->st)))
+        return err;
+      if ((err = launch_pack_frag(wb + s.upw, bf, 1, F, F, F, D, h->ws + d.w1, D, 3 * D, 0, sc, h->st))) return err;
+    }
     float* b1 = (float*)(h->ws + d.b1);
     if ((err = launch_to_f32(wb + s.qkvb, bf, 3 * D, b1, h->st))) return err;
     if ((err = launch_to_f32(wb + s.upb, bf, F, b1 + 3 * D, h->st))) return err;
-    if ((err = launch_transpose_convert(wb + s.outw, bf, D, D, h->ws + d.w2, f32, D + F, 0, 0, sc, h->st))) return err;
-    if ((err = launch_transpose_convert(wb + s.downw, bf, F, D, h->ws + d.w2, f32, D + F, 0, D, sc, h->st)))
-      return err;
+    if (f32) {
+      if ((err = launch_transpose_convert(wb + s.outw, bf, D, D, h->ws + d.w2, f32, D + F, 0, 0, sc, h->st)))
+        return err;
+      if ((err = launch_transpose_convert(wb + s.downw, bf, F, D, h->ws + d.w2, f32, D + F, 0, D, sc, h->st)))
+        return err;
+    } else {
+      if ((err = launch_pack_frag(wb + s.outw, bf, 1, D, D, D, D, h->ws + d.w2, D + F, 0, 0, sc, h->st))) return err;
+      if ((err = launch_pack_frag(wb + s.downw, bf, 1, D, D, D, F, h->ws + d.w2, D + F, 0, D, sc, h->st))) return err;
+    }
     float* b2 = (float*)(h->ws + d.b2);
     if ((err = launch_to_f32(wb + s.outb, bf, D, b2, h->st))) return err;
     return launch_to_f32(wb + s.downb, bf, D, b2 + D, h->st);
@@ -580,13 +594,25 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     lnf = (float*)(h->ws + lo.lnf_tok);
     INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_g, bf, D, lnf, h->st), "repack");
     INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_b, bf, D, lnf + D, h->st), "repack");
-    INIT_CHECK(launch_transpose_convert(wb + lo.bl_prefix_w, bf, D, lo.P * D, h->ws + lo.prefix_w, f32, D, 0, 0, sc,
-                                        h->st),
-               "repack prefix");
+    if (f32) {
+      INIT_CHECK(launch_transpose_convert(wb + lo.bl_prefix_w, bf, D, lo.P * D, h->ws + lo.prefix_w, f32, D, 0, 0, sc,
+                                          h->st),
+                 "repack prefix");
+    } else {
+      INIT_CHECK(launch_pack_frag(wb + lo.bl_prefix_w, bf, 1, (size_t)lo.P * D, lo.P * D, lo.P * D, D,
+                                  h->ws + lo.prefix_w, D, 0, 0, sc, h->st),
+                 "repack prefix");
+    }
     INIT_CHECK(launch_to_f32(wb + lo.bl_prefix_b, bf, lo.P * D, (float*)(h->ws + lo.prefix_b), h->st), "repack");
   }
-  INIT_CHECK(launch_convert_rows(wb + lo.bl_head, bf, lo.V, D, lo.Vpad, h->ws + lo.head, f32, sc, h->st),
-             "repack head");
+  // classifier table [V, D]: element (n = id, k) at src[n * D + k]; rows up to Vpad are zero
+  if (f32) {
+    INIT_CHECK(launch_convert_rows(wb + lo.bl_head, bf, lo.V, D, lo.Vpad, h->ws + lo.head, f32, sc, h->st),
+               "repack head");
+  } else {
+    INIT_CHECK(launch_pack_frag(wb + lo.bl_head, bf, D, 1, lo.V, lo.Vpad, D, h->ws + lo.head, D, 0, 0, sc, h->st),
+               "repack head");
+  }
   INIT_CHECK(launch_rope_table((float2*)(h->ws + lo.rope), lo.npos, lo.dh, cfg->rope_base, h->st), "rope table");
 #undef INIT_CHECK
   *out = h;

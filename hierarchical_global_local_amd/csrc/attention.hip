@@ -9,8 +9,9 @@
 //  * k_attn_decode: memory-bound block-attention decode: one workgroup per (row, head, key split)
 //    streams K then V^T with 16-byte loads, wave-shuffle dot products, online softmax through LDS,
 //    split-KV partials merged by k_attn_combine with log-sum-exp weights.
-//  * k_local_attn: the token decoder's local attention over at most prefix + block entries, held
-//    in LDS by one wave per (row, head).
+//  * k_local_attn_step: the token decoder's local attention for one new slot (decode), one wave
+//    per (row, head) with keys spread over lane groups, everything in registers;
+//    k_local_attn: the same over several new slots (prefill tail), entries held in LDS.
 //  * k_attn_naive: plain prefill attention for fp32 mode.
 #include "bt_internal.h"
 #include "device_common.h"
@@ -245,14 +246,11 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
   }
   if (qi < n) {
     const float inv = 1.0f / lrun;
-    f16* out = ACT + ((size_t)b * n + qi) * ld_act + h * DH;
+    const int row = b * n + qi;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      half4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = to_f16(o[mt][i] * inv);
-      *(half4*)(out + mt * 16 + 4 * g) = w;
-    }
+    for (int mt = 0; mt < MT; ++mt)
+      store4(ACT, frag_off(row, h * DH + mt * 16 + 4 * g, ld_act), o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv,
+             o[mt][3] * inv);
   }
 }
 
@@ -298,7 +296,7 @@ __global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, in
     const T* vp = VTc + (bh * dh + d) * cap;
     float o = 0.f;
     for (int j = 0; j <= qi; ++j) o = fmaf(sc[j], (float)vp[j], o);
-    ACT[((size_t)b * n + qi) * ld_act + h * dh + d] = round_t<T>(o / l);
+    ACT[opnd_idx(ACT, b * n + qi, h * dh + d, ld_act)] = round_t<T>(o / l);
   }
 }
 
@@ -459,7 +457,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
       const int d = r * 32 + wave * 8 + rl;
       const float o = acc[r] + pn * vn[d];
       if (nsplit == 1) {
-        ACT[(size_t)b * ld_act + h * DH + d] = round_t<T>(o / ls);
+        ACT[opnd_idx(ACT, b, h * DH + d, ld_act)] = round_t<T>(o / ls);
       } else {
         float* pp_ = part + ((bh * nsplit) + s) * (DH + 2);
         pp_[2 + d] = o;
@@ -486,7 +484,7 @@ __global__ void k_attn_combine(const float* __restrict__ part, int H, int nsplit
     l += w * p[s * (DH + 2) + 1];
     o += w * p[s * (DH + 2) + 2 + d];
   }
-  ACT[(size_t)b * ld_act + h * DH + d] = round_t<T>(o / l);
+  ACT[opnd_idx(ACT, b, h * DH + d, ld_act)] = round_t<T>(o / l);
 }
 
 template <typename T, int DH>
@@ -589,9 +587,113 @@ __global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, in
     for (int d = lane; d < DH; d += 64) {
       float o = 0.f;
       for (int j = 0; j < nkeys; ++j) o = fmaf(ps[j], vs[j][d], o);
-      ACT[((size_t)b * m + i) * ld_act + h * DH + d] = round_t<T>(o / l);
+      ACT[opnd_idx(ACT, b * m + i, h * DH + d, ld_act)] = round_t<T>(o / l);
     }
     __syncthreads();
+  }
+}
+
+// 8 consecutive elements from floats
+__device__ __forceinline__ void store8(f16* p, const float* v) {
+  half8 w;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = to_f16(v[e]);
+  *(half8*)p = w;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+  *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// Token-decoder attention for ONE new slot s0 per row (a decode step).  One wave per (row, head);
+// LPK = DH / 8 lanes per key hold 8 dimensions each, so a wave scores 64 / LPK keys per pass.  The
+// new key (rotary applied, rounded to the cache type) and value are written to local slot s0 and
+// used from registers; the s0 cached entries are read with 16-byte loads.  Each key group keeps an
+// online softmax (base 2) over its keys; the groups are merged with shuffles in a fixed order.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ QKV, int B, int s0, int D, int H,
+                                                         const float2* __restrict__ rope, T* __restrict__ Kc,
+                                                         T* __restrict__ Vc, int cap, T* __restrict__ ACT, int ld_act,
+                                                         float scale_log2) {
+  constexpr int LPK = DH / 8, KPP = 64 / LPK, HALF = DH / 2;
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= B * H) return;  // whole wave
+  const int b = pair / H, h = pair % H;
+  const int g = lane % LPK, kg = lane / LPK;  // dimensions [8g, 8g + 8), key group
+  const size_t bh = (size_t)b * H + h;
+  T* __restrict__ K = Kc + bh * cap * DH;
+  T* __restrict__ V = Vc + bh * cap * DH;
+  const T* row = QKV + (size_t)b * 3 * D + h * DH + 8 * g;
+  float q[8], kn[8], vn[8], kc[8], vc[8];
+  load8(row, q);
+  load8(row + D, kn);
+  load8(row + 2 * D, vn);
+  const int nkeys = s0 + 1;
+  // first pass's cached entry of this key group (clamped; masked below)
+  const int jc0 = min(kg, max(s0 - 1, 0));
+  load8(K + (size_t)jc0 * DH + 8 * g, kc);
+  load8(V + (size_t)jc0 * DH + 8 * g, vc);
+  // rotary embedding at position s0: dimension d pairs with d +- DH/2, held by lane ^ (LPK / 2)
+  const bool first = 8 * g < HALF;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float qp = __shfl_xor(q[e], LPK / 2, 64), kp = __shfl_xor(kn[e], LPK / 2, 64);
+    const float2 cs = rope[(size_t)s0 * HALF + (8 * g + e) % HALF];
+    if (first) {
+      q[e] = q[e] * cs.x - qp * cs.y;
+      kn[e] = (float)round_t<T>(kn[e] * cs.x - kp * cs.y);
+    } else {
+      q[e] = q[e] * cs.x + qp * cs.y;
+      kn[e] = (float)round_t<T>(kn[e] * cs.x + kp * cs.y);
+    }
+  }
+  if (kg == 0) {
+    store8(K + (size_t)s0 * DH + 8 * g, kn);
+    store8(V + (size_t)s0 * DH + 8 * g, vn);
+  }
+  float mrun = -INFINITY, lrun = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int j0 = 0; j0 < nkeys; j0 += KPP) {
+    const int j = j0 + kg;
+    if (j0 > 0) {  // later passes (long local windows)
+      const int jc = min(j, max(s0 - 1, 0));
+      load8(K + (size_t)jc * DH + 8 * g, kc);
+      load8(V + (size_t)jc * DH + 8 * g, vc);
+    }
+    const bool isnew = j == s0;
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf(q[e], isnew ? kn[e] : kc[e], dot);
+#pragma unroll
+    for (int w = 1; w < LPK; w <<= 1) dot += __shfl_xor(dot, w, 64);
+    const float sc = j < nkeys ? dot * scale_log2 : -INFINITY;
+    const float mn = fmaxf(mrun, sc);
+    const float corr = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
+    const float p = sc == -INFINITY ? 0.f : exp2f(sc - mn);
+    lrun = lrun * corr + p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * corr + p * (isnew ? vn[e] : (j < nkeys ? vc[e] : 0.f));
+    mrun = mn;
+  }
+  // merge the key groups
+#pragma unroll
+  for (int w = LPK; w < 64; w <<= 1) {
+    const float mo = __shfl_xor(mrun, w, 64), lo = __shfl_xor(lrun, w, 64);
+    const float mn = fmaxf(mrun, mo);
+    const float c1 = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
+    const float c2 = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+    lrun = lrun * c1 + lo * c2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * c1 + __shfl_xor(o[e], w, 64) * c2;
+    mrun = mn;
+  }
+  if (kg == 0) {
+    const float inv = 1.0f / lrun;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv;
+    store8(ACT + opnd_idx(ACT, b, h * DH + 8 * g, ld_act), o);
   }
 }
 
@@ -601,6 +703,23 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s
   if (B <= 0 || m <= 0) return hipSuccess;
   if (s0 + m > kMaxLocal || s0 + m > cap) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)dh);
+  if (m == 1) {
+    // decode step: register-resident kernel, 4 (row, head) pairs per workgroup
+    const dim3 g1((B * H + 3) / 4);
+#define BT_STEP(T, DHV)                                                                                         \
+  if (dh == DHV) {                                                                                              \
+    hipLaunchKernelGGL((k_local_attn_step<T, DHV>), g1, dim3(256), 0, st, (const T*)QKV, B, s0, D, H, rope,     \
+                       (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale * kLog2e);                                    \
+    return hipGetLastError();                                                                                   \
+  }
+    if (f32) {
+      BT_STEP(float, 32) BT_STEP(float, 64) BT_STEP(float, 128)
+    } else {
+      BT_STEP(f16, 64) BT_STEP(f16, 128)
+    }
+#undef BT_STEP
+    return hipErrorInvalidValue;
+  }
   dim3 grid(H, B);
 #define BT_LOC(T, DHV)                                                                                          \
   if (dh == DHV) {                                                                                              \

@@ -26,9 +26,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct LayerOff {
   size_t ln;  // fp32 [4][D]: ln1.g, ln1.b, ln2.g, ln2.b
-  size_t w1;  // T [N1 = 3D + F][D]: rows = output features of q | k | v | up (K-contiguous)
+  size_t w1;  // T [N1 = 3D + F][D]: rows = output features of q | k | v | up (fp32: K-contiguous;
+              //   fp16: fragment order, see frag_off)
   size_t b1;  // fp32 [3D + F]
-  size_t w2;  // T [D][D + F]: row n = output feature n of attn.out (k < D) and mlp.down (k >= D)
+  size_t w2;  // T [D][D + F]: row n = output feature n of attn.out (k < D) and mlp.down (k >= D),
+              //   same layout as w1
   size_t b2;  // fp32 [2][D]: attn.out.b, mlp.down.b
 };
 
@@ -41,6 +43,7 @@ struct Layout {
   int npos;     // rows of the rotary table
   int Vpad;     // classifier rows padded to a multiple of 128
   int64_t Mmax; // activation rows
+  int64_t Mpad; // activation rows rounded up to 16 (fragment-order operands)
   bool f32;     // BT_FP32 mode (fp32 everywhere) vs fp16 operands
   bool vanilla; // n_token_layers == 0: token-level transformer (block decoder + classifier)
   size_t elem;  // bytes per matrix / cache element (4 or 2)
@@ -50,9 +53,9 @@ struct Layout {
   std::vector<LayerOff> blk, tok;
   size_t block_kv, local_kv;
   size_t X;     // fp32 [Mmax][D] residual stream
-  size_t LN;    // T [2][Mmax][D] LayerNorm outputs (ln1, ln2)
+  size_t LN;    // T [2][Mpad][D] LayerNorm outputs (ln1, ln2); fp16: fragment order
   size_t QKV;   // T [Mmax][3D]
-  size_t ACT;   // T [Mmax][D + F]: attention output | GELU(up)
+  size_t ACT;   // T [Mpad][D + F]: attention output | GELU(up); fp16: fragment order
   size_t part;  // fp32 split-KV partials of block-attention decode
   size_t part_bytes;
   size_t keys;  // u64 [nparts][Bmax] partial argmax keys of the classifier
@@ -80,6 +83,10 @@ hipError_t launch_transpose_convert(const void* src, bool src_bf16, int K, int N
                                     int ld_dst, int row0, int col0, float scale, hipStream_t st);
 hipError_t launch_convert_rows(const void* src, bool src_bf16, int rows, int cols, int rows_pad, void* dst,
                                bool dst_f32, float scale, hipStream_t st);
+// fp16 weights in fragment order: destination rows [row0, row0 + N), columns [col0, col0 + K) of a
+// matrix of width Ktot take scale * src[n * sn + k * sk] (zero for rows n >= n_valid).
+hipError_t launch_pack_frag(const void* src, bool src_bf16, size_t sn, size_t sk, int n_valid, int N, int K,
+                            void* dst, int Ktot, int row0, int col0, float scale, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool src_bf16, int n, float* dst, hipStream_t st);
 hipError_t launch_add_f32(float* dst, const float* a, int n, hipStream_t st);
 hipError_t launch_rope_table(float2* tab, int npos, int dh, float base, hipStream_t st);
@@ -103,21 +110,23 @@ hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, cons
                             const float* p2, void* out2, bool out_f32, float eps, const ResidPending* resid,
                             hipStream_t st);
 
-// ---- GEMM: C[M][N] = A[M][K] * W[N][K]^T with an epilogue
+// ---- GEMM: C[M][N] = A[M][K] * W[N][K]^T with an epilogue.  fp32: row-major operands (A with
+// leading dimension lda).  fp16: both operands in fragment order with width K (lda unused); the
+// GELU columns of EPI_QKV_GELU are written to out1 in fragment order (width ld1).
 enum EpiMode { EPI_QKV_GELU = 0, EPI_RESID = 1, EPI_STORE = 2, EPI_ARGMAX = 3 };
 struct Epi {
   float wscale;             // multiplies the accumulator
   const float* bias;        // [N] (QKV|up, STORE), attn.out.b (RESID); unused for ARGMAX
   const float* bias2;       // mlp.down.b (RESID)
   void* out0;               // QKV (T, ld0) | X (fp32, ld0) | Y (fp32, ld0) | logits (fp32, ld0, may be null)
-  void* out1;               // ACT (T, ld1) for the GELU columns
+  void* out1;               // ACT (T, width ld1; fp16: fragment order) for the GELU columns
   int ld0, ld1;
   int n_split;              // QKV_GELU: columns >= n_split take A2 and go through GELU into out1
   int act_col0;             // QKV_GELU: first ACT column of the GELU part
   int n_valid;              // ARGMAX: columns >= n_valid are padding
-  unsigned long long* keys; // ARGMAX: packed (value, id) maxima, [nparts][keys_ld]: one entry per row
-                            // for every column group (written in full by each launch)
-  int keys_ld;
+  unsigned long long* keys; // ARGMAX: packed (value, id) maxima, [M][keys_ld]: per row, one entry
+                            // for every column group (entries [0, nparts) written by each launch)
+  int keys_ld;              //   >= the number of column groups of any kernel (N / 4 + 64 suffices)
   int* nparts_out;          // ARGMAX: receives the number of column groups
   int splits;               // RESID: K is split over `splits` workgroups per tile (1 = no split)
   float* part;              // RESID with splits > 1: [splits][M][N] fp32 partial products (no bias)
@@ -150,7 +159,8 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
                                   hipStream_t st);
 
-// ---- greedy ids from the classifier's partial maxima [nparts][ld]: next[b] = id, cur[b*L + j] = id.
+// ---- greedy ids from the classifier's partial maxima [B][ld] (nparts per row): next[b] = id,
+// cur[b*L + j] = id.
 // The step that completes a block also advances the device block-KV length (*n_state += n_inc).
 // With next.mode != 0 the same kernel writes the next decode step's input row into X and that
 // step's first-layer LN1/LN2 outputs (the next step then starts at its first GEMM).

@@ -44,6 +44,40 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Operand layout of the fp16 GEMMs ("fragment order").  An M x K operand (weights: N x K) is cut
+// into tiles of 16 rows x 32 columns; tile (g, s) holds 512 contiguous elements starting at
+// (g * K/32 + s) * 512, and inside it the 8 elements k = 8q .. 8q+7 of row r (q < 4, r < 16) are
+// the 16 bytes at element (16 q + r) * 8.  Those 16 bytes are exactly what lane 16 q + r of a wave
+// holds as an operand of v_mfma_f32_16x16x32_f16, so one wave reads a whole operand tile with one
+// fully contiguous 1 KB load, from HBM, L2 or LDS alike.  Rows are padded to a multiple of 16.
+__device__ __forceinline__ size_t frag_off(int m, int k, int K) {
+  return ((((size_t)(m >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (m & 15)) << 3) + (k & 7);
+}
+// Element index of (row m, column k) of an activation operand of width K: fragment order for the
+// fp16 path, row-major for the fp32 path.
+__device__ __forceinline__ size_t opnd_idx(const f16*, int m, int k, int K) { return frag_off(m, k, K); }
+__device__ __forceinline__ size_t opnd_idx(const float*, int m, int k, int K) { return (size_t)m * K + k; }
+
+// Stores 4 consecutive columns (k % 4 == 0) of an activation operand.
+__device__ __forceinline__ void store4(float* base, size_t idx, float a, float b, float c, float d) {
+  *(float4*)(base + idx) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(f16* base, size_t idx, float a, float b, float c, float d) {
+  half4 w;
+  w[0] = to_f16(a);
+  w[1] = to_f16(b);
+  w[2] = to_f16(c);
+  w[3] = to_f16(d);
+  *(half4*)(base + idx) = w;
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m, 64);
+  hi = __shfl_xor(hi, m, 64);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
 // exact-erf GELU
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 

@@ -47,6 +47,38 @@ hipError_t launch_transpose_convert(const void* src, bool src_bf16, int K, int N
   return hipGetLastError();
 }
 
+// fp16 weights in fragment order (frag_off): rows [row0, row0 + N) and columns [col0, col0 + K)
+// of a destination of width Ktot receive scale * (element (n, k) of the source, at
+// src[n * sn + k * sk]); rows n >= n_valid are zero.  One thread writes 8 consecutive columns.
+template <typename Tin>
+__global__ __launch_bounds__(256) void k_pack_frag(const Tin* __restrict__ src, size_t sn, size_t sk, int n_valid,
+                                                   int N, int K, f16* __restrict__ dst, int Ktot, int row0, int col0,
+                                                   float scale) {
+  const size_t total = (size_t)N * (K / 8);
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+    const int n = (int)(i % N), kc = (int)(i / N);
+    half8 w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      w[e] = n < n_valid ? to_f16(load_f32(src + (size_t)n * sn + (size_t)(kc * 8 + e) * sk) * scale) : (f16)0.f;
+    *(half8*)(dst + frag_off(row0 + n, col0 + kc * 8, Ktot)) = w;
+  }
+}
+
+hipError_t launch_pack_frag(const void* src, bool src_bf16, size_t sn, size_t sk, int n_valid, int N, int K,
+                            void* dst, int Ktot, int row0, int col0, float scale, hipStream_t st) {
+  if (K % 8 || col0 % 8 || Ktot % 32 || row0 % 16) return hipErrorInvalidValue;
+  const size_t total = (size_t)N * (K / 8);
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  if (src_bf16)
+    hipLaunchKernelGGL(k_pack_frag<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)src, sn, sk, n_valid, N, K,
+                       (f16*)dst, Ktot, row0, col0, scale);
+  else
+    hipLaunchKernelGGL(k_pack_frag<float>, dim3(blocks), dim3(256), 0, st, (const float*)src, sn, sk, n_valid, N, K,
+                       (f16*)dst, Ktot, row0, col0, scale);
+  return hipGetLastError();
+}
+
 // dst[r][c] = scale * src[r][c] for r < rows, 0 for rows <= r < rows_pad
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void k_convert_rows(const Tin* __restrict__ src, int rows, int cols,
@@ -165,129 +197,158 @@ __device__ __forceinline__ float row_sum(float v, float* red) {
   }
 }
 
-template <int TPR, int PER, typename To>
+__device__ __forceinline__ float4 f4add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+
+// TPR threads per row (64: one wave, 256: the whole workgroup); thread t of a row holds the
+// 4-column chunks t, t + TPR, ... (CPT of them).  MAXS > 0: fold up to MAXS split-K partials.
+template <int TPR, int CPT, int MAXS, typename To>
 __global__ __launch_bounds__(256) void k_layernorm(float* __restrict__ X, int rows, int D, int stride, int off,
                                                    const float* __restrict__ p1, To* __restrict__ o1,
                                                    const float* __restrict__ p2, To* __restrict__ o2, float eps,
                                                    ResidPending rp) {
   __shared__ float red[4];
   constexpr int RPB = 256 / TPR;  // rows per block
-  constexpr int MAXS = 16;        // split-K partials folded in (at most)
   const int t = threadIdx.x % TPR;
   const int r = blockIdx.x * RPB + threadIdx.x / TPR;
   if (TPR == 64 && r >= rows) return;  // (TPR == 256: one row per block, always valid)
+  const int nch = D >> 2;
   const size_t xr = (size_t)r * stride + off;
   float* __restrict__ x = X + xr * D;
-  const float* __restrict__ part = rp.part;
   // Every load is issued before any arithmetic and none sits behind a divergent branch (indices
   // are clamped and out-of-range values masked afterwards), so the row costs one memory round trip.
-  float v[PER], g1[PER], b1[PER], g2[PER], b2[PER];
+  float4 v[CPT], g1[CPT], b1[CPT], g2[CPT], b2[CPT];
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int c = t + TPR * j;
-    const int cc = min(c, D - 1);
-    const float xv = x[cc];
-    v[j] = c < D ? xv : 0.f;
-    g1[j] = p1[cc];
-    b1[j] = p1[D + cc];
+  for (int j = 0; j < CPT; ++j) {
+    const int c = t + TPR * j, cc = 4 * min(c, nch - 1);
+    const float4 xv = *(const float4*)(x + cc);
+    v[j] = c < nch ? xv : zero;
+    g1[j] = *(const float4*)(p1 + cc);
+    b1[j] = *(const float4*)(p1 + D + cc);
     if (o2) {
-      g2[j] = p2[cc];
-      b2[j] = p2[D + cc];
+      g2[j] = *(const float4*)(p2 + cc);
+      b2[j] = *(const float4*)(p2 + D + cc);
     }
   }
-  if (rp.nsplit > 0) {
-    float add[PER];
+  if constexpr (MAXS > 0) {
+    if (rp.nsplit > 0) {
+      float4 add[CPT];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int cc = min(t + TPR * j, D - 1);
-      add[j] = rp.bias_a[cc] + rp.bias_b[cc];
-    }
-#pragma unroll
-    for (int q = 0; q < MAXS; ++q) {
-      const int qq = min(q, rp.nsplit - 1);
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int cc = min(t + TPR * j, D - 1);
-        const float pv = part[((size_t)qq * rp.part_rows + xr) * D + cc];
-        add[j] += q < rp.nsplit ? pv : 0.f;
+      for (int j = 0; j < CPT; ++j) {
+        const int cc = 4 * min(t + TPR * j, nch - 1);
+        add[j] = f4add(*(const float4*)(rp.bias_a + cc), *(const float4*)(rp.bias_b + cc));
       }
-    }
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int c = t + TPR * j;
-      if (c < D) {
-        v[j] += add[j];
-        x[c] = v[j];
+      for (int q = 0; q < MAXS; ++q) {
+        const int qq = min(q, rp.nsplit - 1);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          const int cc = 4 * min(t + TPR * j, nch - 1);
+          const float4 pv = *(const float4*)(rp.part + ((size_t)qq * rp.part_rows + xr) * D + cc);
+          add[j] = f4add(add[j], q < rp.nsplit ? pv : zero);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int c = t + TPR * j;
+        if (c < nch) {
+          v[j] = f4add(v[j], add[j]);
+          *(float4*)(x + 4 * c) = v[j];
+        }
       }
     }
   }
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) s += v[j];
+  for (int j = 0; j < CPT; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
   s = row_sum<TPR>(s, red);
   const float mean = s / (float)D;
   float q = 0.f;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int c = t + TPR * j;
-    const float d = c < D ? v[j] - mean : 0.f;
-    q += d * d;
+  for (int j = 0; j < CPT; ++j) {
+    if (t + TPR * j < nch) {
+      const float d0 = v[j].x - mean, d1 = v[j].y - mean, d2 = v[j].z - mean, d3 = v[j].w - mean;
+      q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+    }
   }
   q = row_sum<TPR>(q, red);
   const float rstd = 1.0f / sqrtf(q / (float)D + eps);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
+  for (int j = 0; j < CPT; ++j) {
     const int c = t + TPR * j;
-    if (c < D) {
-      const float y = (v[j] - mean) * rstd;
-      store_from_f32(o1 + (size_t)r * D + c, y * g1[j] + b1[j]);
-      if (o2) store_from_f32(o2 + (size_t)r * D + c, y * g2[j] + b2[j]);
+    if (c < nch) {
+      const float y0 = (v[j].x - mean) * rstd, y1 = (v[j].y - mean) * rstd;
+      const float y2 = (v[j].z - mean) * rstd, y3 = (v[j].w - mean) * rstd;
+      store4(o1, opnd_idx(o1, r, 4 * c, D), y0 * g1[j].x + b1[j].x, y1 * g1[j].y + b1[j].y, y2 * g1[j].z + b1[j].z,
+             y3 * g1[j].w + b1[j].w);
+      if (o2)
+        store4(o2, opnd_idx(o2, r, 4 * c, D), y0 * g2[j].x + b2[j].x, y1 * g2[j].y + b2[j].y,
+               y2 * g2[j].z + b2[j].z, y3 * g2[j].w + b2[j].w);
     }
   }
 }
 
-template <int TPR, int PER>
+template <int TPR, int CPT, int MAXS>
 static void launch_ln_cfg(int rows, float* X, int D, int stride, int off, const float* p1, void* out1,
                           const float* p2, void* out2, bool out_f32, float eps, const ResidPending& rp,
                           hipStream_t st) {
   const int blocks = (rows + 256 / TPR - 1) / (256 / TPR);
   if (out_f32)
-    hipLaunchKernelGGL((k_layernorm<TPR, PER, float>), dim3(blocks), dim3(256), 0, st, X, rows, D, stride, off, p1,
-                       (float*)out1, p2, (float*)out2, eps, rp);
+    hipLaunchKernelGGL((k_layernorm<TPR, CPT, MAXS, float>), dim3(blocks), dim3(256), 0, st, X, rows, D, stride, off,
+                       p1, (float*)out1, p2, (float*)out2, eps, rp);
   else
-    hipLaunchKernelGGL((k_layernorm<TPR, PER, f16>), dim3(blocks), dim3(256), 0, st, X, rows, D, stride, off, p1,
-                       (f16*)out1, p2, (f16*)out2, eps, rp);
+    hipLaunchKernelGGL((k_layernorm<TPR, CPT, MAXS, f16>), dim3(blocks), dim3(256), 0, st, X, rows, D, stride, off,
+                       p1, (f16*)out1, p2, (f16*)out2, eps, rp);
+}
+
+template <int CPT>
+static void launch_ln_small(int rows, float* X, int D, int stride, int off, const float* p1, void* out1,
+                            const float* p2, void* out2, bool out_f32, float eps, const ResidPending& rp,
+                            hipStream_t st) {
+  if (rp.nsplit <= 0)
+    launch_ln_cfg<256, CPT, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+  else if (rp.nsplit <= 8)
+    launch_ln_cfg<256, CPT, 8>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+  else
+    launch_ln_cfg<256, CPT, 16>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
 }
 
 hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, const float* p1, void* out1,
                             const float* p2, void* out2, bool out_f32, float eps, const ResidPending* resid,
                             hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (D % 4) return hipErrorInvalidValue;
   ResidPending rp{};
   if (resid) rp = *resid;
+  if (rp.nsplit > 16) return hipErrorInvalidValue;
+  const int nch = D / 4;
   if (rows <= 1024) {
-    // few rows: one workgroup per row
-    const int per = (D + 255) / 256;
+    // few rows (decode): one workgroup per row
+    const int per = (nch + 255) / 256;
     if (per <= 1)
-      launch_ln_cfg<256, 1>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
-    else if (per <= 3)
-      launch_ln_cfg<256, 3>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
-    else if (per <= 8)
-      launch_ln_cfg<256, 8>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
-    else if (per <= 16)
-      launch_ln_cfg<256, 16>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+      launch_ln_small<1>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 2)
+      launch_ln_small<2>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 4)
+      launch_ln_small<4>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
     else
       return hipErrorInvalidValue;
   } else {
-    const int per = (D + 63) / 64;
-    if (per <= 2)
-      launch_ln_cfg<64, 2>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
-    else if (per <= 12)
-      launch_ln_cfg<64, 12>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
-    else if (per <= 32)
-      launch_ln_cfg<64, 32>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
-    else if (per <= 64)
-      launch_ln_cfg<64, 64>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    // one wave per row; split-K partials are only produced for at most 1024 rows
+    if (rp.nsplit > 0) return hipErrorInvalidValue;
+    const int per = (nch + 63) / 64;
+    if (per <= 1)
+      launch_ln_cfg<64, 1, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 2)
+      launch_ln_cfg<64, 2, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 3)
+      launch_ln_cfg<64, 3, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 4)
+      launch_ln_cfg<64, 4, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 8)
+      launch_ln_cfg<64, 8, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+    else if (per <= 16)
+      launch_ln_cfg<64, 16, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
     else
       return hipErrorInvalidValue;
   }
@@ -315,25 +376,28 @@ template <int PER, typename Tt, typename To>
 __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __restrict__ keys, int nparts, int ld,
                                                   int32_t* __restrict__ next, int32_t* __restrict__ cur, int L,
                                                   int j, int* __restrict__ n_state, int n_inc, NextStep ns) {
-  __shared__ unsigned long long red[256];
+  __shared__ unsigned long long red[4];
   __shared__ float redf[4];
   const int b = blockIdx.x, tid = threadIdx.x;
   if (b == 0 && tid == 0 && n_inc) *n_state += n_inc;
+  // the row's keys are contiguous: 256 threads read 2 KB per pass (max is order-independent)
+  const unsigned long long* kr = keys + (size_t)b * ld;
   unsigned long long best = 0ull;
   for (int p = tid; p < nparts; p += 256) {
-    const unsigned long long k = keys[(size_t)p * ld + b];
+    const unsigned long long k = kr[p];
     best = k > best ? k : best;
   }
-  red[tid] = best;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) {
-      const unsigned long long k = red[tid + o];
-      if (k > red[tid]) red[tid] = k;
-    }
-    __syncthreads();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long k = shfl_xor_u64(best, o);
+    best = k > best ? k : best;
   }
-  const int id = (int)(0xFFFFFFFFu - (unsigned)(red[0] & 0xFFFFFFFFull));
+  if ((tid & 63) == 0) red[tid >> 6] = best;
+  __syncthreads();
+  best = red[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) best = red[w] > best ? red[w] : best;
+  const int id = (int)(0xFFFFFFFFu - (unsigned)(best & 0xFFFFFFFFull));
   if (tid == 0) {
     next[b] = id;
     cur[b * L + j] = id;
@@ -376,16 +440,16 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
   }
   var = row_sum<256>(var, redf);
   const float rstd = 1.0f / sqrtf(var / (float)D + ns.eps);
-  To* o1 = (To*)ns.ln1 + (size_t)b * D;
-  To* o2 = (To*)ns.ln2 + (size_t)b * D;
+  To* o1 = (To*)ns.ln1;
+  To* o2 = (To*)ns.ln2;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int c = tid + 256 * q;
     if (c < D) {
       ns.X[(size_t)b * D + c] = v[q];
       const float y = (v[q] - mean) * rstd;
-      store_from_f32(o1 + c, y * g1[q] + b1[q]);
-      store_from_f32(o2 + c, y * g2[q] + b2[q]);
+      store_from_f32(o1 + opnd_idx(o1, b, c, D), y * g1[q] + b1[q]);
+      store_from_f32(o2 + opnd_idx(o2, b, c, D), y * g2[q] + b2[q]);
     }
   }
 }

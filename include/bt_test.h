@@ -32,9 +32,13 @@ int bt_profile_enable(bt_handle* h, int32_t on);
 int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* launches, double* bytes,
                     double* flops);
 
-/* C[M][N] = scale * A[M][K] * W[N][K]^T in fp32, on `stream` (a hipStream_t).  dtype BT_FP32:
- * A and W fp32; BT_BF16: A and W fp16 (the library's matrix-operand type), K % 64 == 0,
- * N % 32 == 0.  Device pointers; synchronous errors only. */
+/* C[M][N] = scale * A[M][K] * W[N][K]^T in fp32 (C row-major), on `stream` (a hipStream_t).
+ * dtype BT_FP32: A and W fp32, row-major.  BT_BF16: A and W fp16 (the library's matrix-operand
+ * type) in the library's operand order, K % 64 == 0, N % 32 == 0: a matrix with R rows (R rounded up
+ * to a multiple of 16; A holds ceil(M / 16) * 16 * K elements) is stored as the 16 x 32 tiles
+ * (g, s) = (rows 16g.., columns 32s..) in the order g-major, s-minor, 512 elements each; inside a
+ * tile, the 8 elements (row 16g + r, columns 32s + 8q .. 32s + 8q + 7) sit at element 8 * (16q + r).
+ * Device pointers; synchronous errors only. */
 int bt_test_gemm(int32_t dtype, const void* d_a, const void* d_w, float* d_c, int32_t M, int32_t N, int32_t K,
                  float scale, void* stream);
 
