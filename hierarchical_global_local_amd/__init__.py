@@ -74,8 +74,9 @@ def lib() -> ctypes.CDLL:
     L.bt_profile_read.argtypes = [c_p, c_i32, dp, ctypes.POINTER(ctypes.c_int64), dp, dp]
     L.bt_test_gemm.argtypes = [c_i32, c_p, c_p, c_p, c_i32, c_i32, c_i32, ctypes.c_float, c_p]
     L.bt_set_graphs.argtypes = [c_p, c_i32]
+    L.bt_test_replay.argtypes = [c_p, c_i32, c_i32]
     for f in ("bt_init", "bt_prefill", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
-              "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs"):
+              "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs", "bt_test_replay"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -231,6 +232,11 @@ class BlockTransformer:
 
     def profile(self, on: bool) -> None:
         check(lib().bt_profile_enable(self.h, 1 if on else 0))
+
+    def replay(self, kind: str, reps: int) -> None:
+        """Launch the decode kernel of class `kind` ("gemm_qkv_up" or "attn_block_decode") `reps` times
+        back to back on the model's stream (see bt_test_replay in include/bt_test.h)."""
+        check(lib().bt_test_replay(self.h, PROFILE_KINDS.index(kind), reps))
 
     def profile_read(self) -> Dict[str, dict]:
         """{phase/kind: {"ms", "launches", "bytes", "flops"}} since profile(True); phase is prefill or decode."""

@@ -254,6 +254,21 @@ float wscale(const Layout& lo) { return lo.f32 ? 1.0f : kWeightUnscale; }
 
 const ResidPending* pending(bt_handle* h) { return h->pending.nsplit > 0 ? &h->pending : nullptr; }
 
+// Epilogue of the [q|k|v|up] GEMM: bias, q|k|v to the QKV buffer, GELU(up) to ACT.
+Epi qkv_epi(bt_handle* h, const LayerOff& w) {
+  const Layout& lo = h->lo;
+  Epi ep{};
+  ep.wscale = wscale(lo);
+  ep.bias = (const float*)P_(h, w.b1);
+  ep.out0 = P_(h, lo.QKV);
+  ep.ld0 = 3 * lo.D;
+  ep.out1 = P_(h, lo.ACT);
+  ep.ld1 = lo.D + lo.F;
+  ep.n_split = 3 * lo.D;
+  ep.act_col0 = lo.D;
+  return ep;
+}
+
 // LN1/LN2 -> [q|k|v|up] GEMM with bias (+GELU on the up part).  With ln_done the LayerNorm
 // outputs were already written (by the previous step's finalisation).
 int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows, bool ln_done = false) {
@@ -267,15 +282,7 @@ int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows, bool ln_done = false) 
              "layernorm");
     h->pending.nsplit = 0;
   }
-  Epi ep{};
-  ep.wscale = wscale(lo);
-  ep.bias = (const float*)P_(h, w.b1);
-  ep.out0 = P_(h, lo.QKV);
-  ep.ld0 = 3 * lo.D;
-  ep.out1 = P_(h, lo.ACT);
-  ep.ld1 = lo.D + lo.F;
-  ep.n_split = 3 * lo.D;
-  ep.act_col0 = lo.D;
+  const Epi ep = qkv_epi(h, w);
   Prof p(h, PK_GEMM_QKV, N1 * D * E + 2.0 * rows * D * E + rows * N1 * E + N1 * 4.0, 2.0 * rows * N1 * D);
   BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), rows, 3 * lo.D + lo.F, lo.D,
                           EPI_QKV_GELU, ep, h->st),
@@ -782,6 +789,38 @@ int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* la
   h->ev_used.clear();
   h->ev_next = 0;
   return BT_OK;
+}
+
+int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
+  if (!h || reps < 1) return fail(BT_ERR_INVALID_ARG, "bad argument");
+  if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
+  if (h->B <= 0) return fail(BT_ERR_STATE, "bt_test_replay before bt_prefill");
+  const Layout& lo = h->lo;
+  // the attention appends at slot n (the device length, equal to the host mirror between calls)
+  if (kind == PK_ATTN_DECODE && h->n_blocks >= lo.ncap) return fail(BT_ERR_CAPACITY, "block-KV cache full");
+  int r = BT_OK;
+  for (int i = 0; i < reps && r == BT_OK; ++i) {
+    if (kind == PK_GEMM_QKV) {
+      // the decode step's [q|k|v|up] GEMM, cycling over the layers of both decoders (as many
+      // distinct weights as a decode step streams between two uses of one layer)
+      const int nl = lo.Nb + lo.Nt, l = i % nl;
+      const LayerOff& w = l < lo.Nt ? lo.tok[l] : lo.blk[l - lo.Nt];
+      const Epi ep = qkv_epi(h, w);
+      hipError_t e = launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), h->B, 3 * lo.D + lo.F, lo.D,
+                                 EPI_QKV_GELU, ep, h->st);
+      if (e != hipSuccess) r = hip_fail(h, e, "replay gemm");
+    } else if (kind == PK_ATTN_DECODE) {
+      const int l = i % lo.Nb;
+      hipError_t e = launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.D, lo.H,
+                                              lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l),
+                                              lo.ncap, P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part),
+                                              lo.part_bytes, h->dec_nsplit, h->st);
+      if (e != hipSuccess) r = hip_fail(h, e, "replay attention");
+    } else {
+      r = fail(BT_ERR_INVALID_ARG, "kind not replayable");
+    }
+  }
+  return r;
 }
 
 int bt_test_gemm(int32_t dtype, const void* d_a, const void* d_w, float* d_c, int32_t M, int32_t N, int32_t K,

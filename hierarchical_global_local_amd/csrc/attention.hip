@@ -32,6 +32,18 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
   o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
+// the same with non-temporal loads (block-KV streams: they must not evict cached weights)
+__device__ __forceinline__ void load8_nt(const f16* p, float* o) {
+  half8 v = __builtin_nontemporal_load((const half8*)p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8_nt(const float* p, float* o) {
+  const float4_ a = __builtin_nontemporal_load((const float4_*)p), b = __builtin_nontemporal_load((const float4_*)(p + 4));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = a[e], o[4 + e] = b[e];
+}
+
 template <typename T>
 __device__ __forceinline__ T round_t(float v) { return from_f32<T>(v); }
 
@@ -338,7 +350,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   constexpr int LPK = DH / 8;      // lanes per key in the score pass (8 values each)
   constexpr int KPW = 64 / LPK;    // keys per wave per step
   constexpr int RPL = DH / 32;     // value rows per lane in the value pass
-  constexpr int U = 4;             // loads in flight per lane
+  constexpr int U = 8;             // key loads in flight per lane (score pass)
+  constexpr int UV = 4;            // value-chunk loads in flight per lane and row (value pass)
   __shared__ float qs[DH], kn[DH], vn[DH];
   __shared__ __attribute__((aligned(16))) float sc[kMaxChunk + 8];
   __shared__ float red[8];
@@ -386,7 +399,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
     for (int u = 0; u < U; ++u) {
       // clamped rather than guarded, so that the U loads are in flight together
       const int j = min(jb + u * 4 * KPW + kl, jc_end - 1);
-      load8(K + (size_t)j * DH + 8 * pp, kv[u]);
+      load8_nt(K + (size_t)j * DH + 8 * pp, kv[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -432,17 +445,26 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   float acc[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) acc[r] = 0.f;
-  for (int jc = j0 + cl * 8; jc < jc_end; jc += 64) {
-    float p[8];
+  for (int jb = j0 + cl * 8; jb < jc_end; jb += 64 * UV) {
+    // UV chunks of 8 keys per row in flight; chunks past the cached keys are clamped to a valid
+    // address and weighted by zero
+    float v[UV][RPL][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = (jc + e < jc_end) ? sc[jc - j0 + e] : 0.f;
+    for (int u = 0; u < UV; ++u) {
+      const int jc = jb + 64 * u < jc_end ? jb + 64 * u : jb;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const int d = r * 32 + wave * 8 + rl;
-      float v[8];
-      load8(VT + (size_t)d * cap + jc, v);
+      for (int r = 0; r < RPL; ++r) load8_nt(VT + (size_t)(r * 32 + wave * 8 + rl) * cap + jc, v[u][r]);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[r] = fmaf(p[e], v[e], acc[r]);
+    for (int u = 0; u < UV; ++u) {
+      const int jc = jb + 64 * u;
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = (jc + e < jc_end) ? sc[min(jc + e, jc_end - 1) - j0] : 0.f;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r] = fmaf(p[e], v[u][r][e], acc[r]);
     }
   }
 #pragma unroll

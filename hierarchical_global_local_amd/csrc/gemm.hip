@@ -269,13 +269,13 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
 // workgroup owns a slab of 16*NG output columns for ALL rows: MW waves along M (MG 16-row groups
 // each) times KW waves along K.  Both operands are in fragment order and go straight from memory
 // into MFMA operand registers (one contiguous 1 KB load per 16 x 32 tile, no LDS on the operand
-// path), two K steps in flight per wave.  The KW partial tiles are summed once through LDS, in a
+// path), DEPTH K steps in flight per wave.  The KW partial tiles are summed once through LDS, in a
 // fixed order, and the epilogue writes 8 consecutive columns per thread.  gridDim.y > 1 splits K
 // over workgroups (EPI_RESID only): the partial products go to ep.part and the consumer adds them.
-template <int MG, int MW, int NG, int KW, int MODE>
+template <int MG, int MW, int NG, int KW, int MODE, int DEPTH = 2>
 __global__ __launch_bounds__(64 * MW * KW) void k_gemm_skinny(const f16* __restrict__ A1, const f16* __restrict__ A2,
                                                               const f16* __restrict__ W, int M, int N, int K, Epi ep) {
-  constexpr int R = 16 * MG * MW, C = 16 * NG, CLD = C + 4, NT = 64 * MW * KW, DEPTH = 2;
+  constexpr int R = 16 * MG * MW, C = 16 * NG, CLD = C + 4, NT = 64 * MW * KW;
   __shared__ __attribute__((aligned(16))) float red[KW * R * CLD];
   const int KS = K / 32, mgs = (M + 15) / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -32,6 +32,16 @@ int bt_profile_enable(bt_handle* h, int32_t on);
 int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* launches, double* bytes,
                     double* flops);
 
+/* Launch again, `reps` times back to back on the handle's stream, the kernel of one decode launch
+ * class at the batch of the last prefill, for timing it without per-launch events.  kind (profile
+ * class index): 2 = the decode [q|k|v|up] GEMM, cycling over the weights of all token- and
+ * block-decoder layers; 8 = block-attention
+ * decode at the current block-KV length, cycling over the block-decoder layers.  Only activations
+ * are overwritten, plus for kind 8 the block-KV entry at the current length (not yet valid; the
+ * next block step writes it again), so decoding can continue afterwards.  BT_ERR_STATE before a
+ * prefill; BT_ERR_INVALID_ARG for other kinds. */
+int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps);
+
 /* C[M][N] = scale * A[M][K] * W[N][K]^T in fp32 (C row-major), on `stream` (a hipStream_t).
  * dtype BT_FP32: A and W fp32, row-major.  BT_BF16: A and W fp16 (the library's matrix-operand
  * type) in the library's operand order, K % 64 == 0, N % 32 == 0: a matrix with R rows (R rounded up

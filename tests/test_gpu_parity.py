@@ -191,3 +191,29 @@ def test_vanilla_mode_fp32_and_bf16_every_step():
     assert np.abs(gl - ref_lg).max() <= BF16_TOL
     check_ids_against(ref_lg, ids, BF16_TOL)
     assert model.cache_lengths() == (st.block_kv_len, 0)
+
+
+def test_kernel_replay_leaves_decoding_unchanged():
+    """bt_test_replay (used by the benchmark to time one kernel class) may only overwrite
+    activations and the not-yet-valid block-KV slot: decoding after it is bit-identical."""
+    torch = require_gpu()
+    import hierarchical_global_local_amd as hg
+    cfg = SMALL_BF16
+    W = wl.make_weights(cfg, seed=11, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=11)
+    G = 14
+    ref, _, _ = run_gpu(cfg, W, prompt, G)
+    model = hg.BlockTransformer(cfg, W, max_batch=prompt.shape[0], max_tokens=wl.padded_len(cfg, prompt.shape[1]) + G)
+    d_prompt = torch.from_numpy(np.ascontiguousarray(prompt, dtype=np.int32)).cuda()
+    ids = torch.empty((G, prompt.shape[0]), dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(model.stream):
+        model.prefill(d_prompt, ids[0])
+        for g in range(1, G):
+            if g in (3, 4, 7):  # after token steps and after a block step
+                model.replay("gemm_qkv_up", 5)
+                model.replay("attn_block_decode", 5)
+            model.decode_step(ids[g])
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy().T, ref)
+    with pytest.raises(hg.BtError):
+        model.replay("layernorm", 1)
