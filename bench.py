@@ -36,7 +36,9 @@ def describe(cfg):
 
 
 class Runner:
-    def __init__(self, cfg):
+    def __init__(self, cfg, prompt_sized=False):
+        """prompt_sized: size the prefill activations for this prompt only (max_prompt_tokens), as a
+        server that knows its longest prompt would; the caches are sized for prompt + generation."""
         import torch
 
         import bt_workloads as wl
@@ -45,8 +47,9 @@ class Runner:
         self.G = cfg.gen_len
         W = wl.make_weights(cfg)
         prompt = wl.make_prompt(cfg)
-        self.model = hg.BlockTransformer(cfg, W, max_batch=cfg.batch,
-                                         max_tokens=wl.padded_len(cfg, cfg.prompt_len) + self.G)
+        Tp = wl.padded_len(cfg, cfg.prompt_len)
+        self.model = hg.BlockTransformer(cfg, W, max_batch=cfg.batch, max_tokens=Tp + self.G,
+                                         max_prompt_tokens=Tp if prompt_sized else 0)
         del W
         self.stream = self.model.stream
         self.prompt = torch.from_numpy(prompt).cuda()
@@ -257,6 +260,46 @@ def cpu_baseline(cfg, rows, tokens):
             "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
 
 
+def batch_sweep(args):
+    """Throughput against batch size at one prompt / generation shape (the pages measure both
+    models at their largest batch and report batch sensitivity).  Workspaces are sized for the
+    prompt (max_prompt_tokens) so the batch is bounded by the caches; points that do not fit in HBM
+    are reported as such."""
+    import torch
+
+    import bt_workloads as wl
+    base = wl.get_config(args.sweep_config)
+    todo = [(base, int(b)) for b in args.batch_sweep.split(",")]
+    if args.sweep_vanilla:
+        van = wl.get_config({"c2_decode_heavy": "v2_vanilla_decode_heavy",
+                             "c1_prefill_heavy": "v1_vanilla_prefill_heavy"}[args.sweep_config])
+        todo += [(van, int(b)) for b in args.sweep_vanilla.split(",")]
+    rows = []
+    for cfg0, B in todo:
+        cfg = cfg0.with_(batch=B)
+        rec = {"model": cfg0.name, "batch": B}
+        try:
+            r = Runner(cfg, prompt_sized=True)
+            t = r.timed(1, 1)
+            rec.update(tokens_per_s=round(B * cfg.gen_len / (t["ms_per_step"] * 1e-3), 1),
+                       decode_tokens_per_s=round(B * (cfg.gen_len - 1) / (t["decode_ms"] * 1e-3), 1),
+                       ms_per_step=round(t["ms_per_step"], 2), prefill_ms=round(t["prefill_ms"], 2),
+                       decode_ms=round(t["decode_ms"], 2),
+                       workspace_gib=round(r.model.workspace.numel() / 2 ** 30, 2))
+            del r
+        except torch.cuda.OutOfMemoryError:
+            rec["result"] = "does not fit in HBM"
+        torch.cuda.empty_cache()
+        log(f"[sweep] {rec}")
+        rows.append(rec)
+    line = json.dumps({"batch_sweep": describe(base), "gen_len": base.gen_len, "prompt_len": base.prompt_len,
+                       "points": rows})
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,6 +319,12 @@ def main():
     ap.add_argument("--kernel", default=None, help="kernel-name pattern for --traffic")
     ap.add_argument("--compare-vanilla", action="store_true",
                     help="also time token-level transformers of the same width and depth on the same kernels")
+    ap.add_argument("--batch-sweep", default=None, metavar="B1,B2,...",
+                    help="only sweep the batch size of --sweep-config (one untimed + one timed generation each) "
+                         "and print one JSON line; with --sweep-vanilla also the token-level model")
+    ap.add_argument("--sweep-config", default="c2_decode_heavy")
+    ap.add_argument("--sweep-vanilla", default=None, metavar="B1,B2,...",
+                    help="batch sizes of the token-level model of the same shape for --batch-sweep")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip the event-profiled repeat (roofline null); for hardware-counter runs")
     args = ap.parse_args()
@@ -284,6 +333,9 @@ def main():
         return
     if args.traffic:
         print(json.dumps(traffic_from_counters(args.traffic[0], args.traffic[1], args.kernel), indent=1))
+        return
+    if args.batch_sweep:
+        batch_sweep(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the Block Transformer path shards by batch rows with no "

@@ -36,14 +36,15 @@ class BtConfig(ctypes.Structure):
                 ("d_mlp", ctypes.c_int32), ("n_block_layers", ctypes.c_int32), ("n_token_layers", ctypes.c_int32),
                 ("block_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32), ("pad_id", ctypes.c_int32),
-                ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+                ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("max_prompt_tokens", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, model, max_batch: int, max_tokens: int) -> "BtConfig":
+    def make(cls, model, max_batch: int, max_tokens: int, max_prompt_tokens: int = 0) -> "BtConfig":
         """From any object with the model fields (vocab, d_model, ..., dtype "fp32"/"bf16")."""
         return cls(model.vocab, model.d_model, model.n_heads, model.d_mlp, model.n_block_layers,
                    model.n_token_layers, model.block_len, model.prefix_len, max_batch, max_tokens,
-                   BT_FP32 if model.dtype == "fp32" else BT_BF16, model.pad_id, model.ln_eps, model.rope_base)
+                   BT_FP32 if model.dtype == "fp32" else BT_BF16, model.pad_id, model.ln_eps, model.rope_base,
+                   max_prompt_tokens)
 
 
 _lib = None
@@ -122,12 +123,12 @@ class BlockTransformer:
     """One model instance bound to a CUDA/HIP stream.  Device memory is owned by torch tensors."""
 
     def __init__(self, model, weights: Mapping[str, np.ndarray], max_batch: int, max_tokens: int,
-                 device: str = "cuda:0", stream=None, graphs: bool = True):
+                 device: str = "cuda:0", stream=None, graphs: bool = True, max_prompt_tokens: int = 0):
         import torch
         self.torch = torch
         L = lib()
         self.model = model
-        self.cfg = BtConfig.make(model, max_batch, max_tokens)
+        self.cfg = BtConfig.make(model, max_batch, max_tokens, max_prompt_tokens)
         self.device = torch.device(device)
         # a stream of its own: decode steps are captured into HIP graphs, which the NULL stream forbids
         self.stream = stream if stream is not None else torch.cuda.Stream(self.device)

@@ -52,6 +52,10 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   if (!(c.ln_eps > 0.f) || !(c.rope_base > 0.f)) return "ln_eps and rope_base must be > 0";
   const int nblk = (c.max_tokens + c.block_len - 1) / c.block_len;
   if (nblk > 131072) return "max_tokens / block_len must be <= 131072";
+  if (c.max_prompt_tokens < 0 || c.max_prompt_tokens > c.max_tokens)
+    return "max_prompt_tokens must be in [0, max_tokens]";
+  const int max_prompt = c.max_prompt_tokens > 0 ? c.max_prompt_tokens : c.max_tokens;
+  const int nblk_prompt = std::max(1, (max_prompt + c.block_len - 1) / c.block_len);
 
   lo.V = c.vocab;
   lo.D = c.d_model;
@@ -73,7 +77,8 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.lcap = lo.P + lo.L;
   lo.npos = std::max(lo.ncap, lo.lcap);
   lo.Vpad = (int)align_up((size_t)lo.V, 128);
-  lo.Mmax = std::max<int64_t>((int64_t)lo.Bmax * nblk, (int64_t)lo.Bmax * lo.P);
+  lo.max_prompt = nblk_prompt * lo.L;  // prompts up to this padded length fit the activations
+  lo.Mmax = std::max<int64_t>((int64_t)lo.Bmax * nblk_prompt, (int64_t)lo.Bmax * lo.P);
   lo.Mpad = (int64_t)align_up((size_t)lo.Mmax, 16);
 
   const size_t D = lo.D, F = lo.F, V = lo.V, P = lo.P, E = lo.elem, TE = lo.tab_elem;
@@ -635,6 +640,7 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
   const int L = lo.L;
   const int Tp = std::max(L, (T + L - 1) / L * L);
   if ((int64_t)Tp + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "padded prompt + 1 exceeds max_tokens");
+  if (Tp > lo.max_prompt) return fail(BT_ERR_CAPACITY, "padded prompt exceeds max_prompt_tokens");
   h->ready = false;
   h->g = 0;  // index of the token the prefill emits
   if (B != h->graph_B) drop_graphs(h);

@@ -38,6 +38,7 @@ struct Layout {
   // model dimensions
   int V, D, H, dh, F, L, P, Nb, Nt, De;
   int Bmax, max_tokens;
+  int max_prompt;  // longest padded prompt the activations hold (a multiple of L)
   int ncap;     // block-KV entries per (layer, row, head), multiple of 64
   int lcap;     // local-KV entries per (layer, row, head) = P + L
   int npos;     // rows of the rotary table

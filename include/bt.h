@@ -61,7 +61,8 @@ typedef enum {
  *   needs block_len = 1, and the classifier reads the block decoder's final LayerNorm output
  *   directly (no prefix projection, no token decoder, no local KV);
  *   BT_BF16 also needs d_model % 64 == 0 and d_mlp % 64 == 0;
- *   max_batch >= 1; max_tokens >= block_len (padded prompt + generated). */
+ *   max_batch >= 1; max_tokens >= block_len (padded prompt + generated);
+ *   0 <= max_prompt_tokens <= max_tokens. */
 typedef struct {
   int32_t vocab, d_model, n_heads, d_mlp;
   int32_t n_block_layers, n_token_layers;
@@ -72,6 +73,9 @@ typedef struct {
   int32_t pad_id;     /* token used to left-pad prompts to whole blocks     */
   float ln_eps;       /* LayerNorm epsilon (1e-5)                           */
   float rope_base;    /* rotary frequency base (10000)                      */
+  int32_t max_prompt_tokens; /* longest prompt bt_prefill accepts, after left padding; sizes the
+                                prefill activations (one row per prompt block and batch row).
+                                0 = max_tokens.  Must be <= max_tokens when set. */
 } bt_config;
 
 /* Size in bytes of the canonical weights blob for this config.  The blob is
@@ -114,8 +118,8 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
  * over the P prefix slots of the last context embedding (resetting the local
  * KV), and writes the first generated token of every row to d_next (device
  * int32 [B]).  If d_logits is not NULL, the fp32 logits [B, V] of that token
- * are written there too.  Requires 1 <= B <= max_batch, T >= 1 and
- * T' + 1 <= max_tokens (else BT_ERR_CAPACITY). */
+ * are written there too.  Requires 1 <= B <= max_batch, T >= 1, T' + 1 <= max_tokens and
+ * T' <= max_prompt_tokens when that is set (else BT_ERR_CAPACITY). */
 int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int32_t* d_next,
                float* d_logits);
 

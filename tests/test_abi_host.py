@@ -70,7 +70,9 @@ def test_block_kv_footprint_ratio_is_block_len():
 
 @pytest.mark.parametrize("field,value,msg", [("n_heads", 5, "multiple of n_heads"), ("block_len", 0, "block_len"),
                                              ("dtype", 7, "dtype"), ("max_batch", 0, "max_batch"),
-                                             ("d_model", 96, "d_head"), ("prefix_len", 40, "prefix_len")])
+                                             ("d_model", 96, "d_head"), ("prefix_len", 40, "prefix_len"),
+                                             ("max_prompt_tokens", -4, "max_prompt_tokens"),
+                                             ("max_prompt_tokens", 1 << 20, "max_prompt_tokens")])
 def test_invalid_config_rejected_on_host(field, value, msg):
     import hierarchical_global_local_amd as hg
     _, cfg = _cfg("c1_prefill_heavy")
@@ -87,3 +89,24 @@ def test_null_arguments_rejected():
     assert L.bt_prefill(None, None, 1, 1, None, None) == -1
     assert L.bt_decode_step(None, None, None) == -1
     assert L.bt_destroy(None) == -1
+
+
+def test_prompt_capacity_sizes_the_activations():
+    """max_prompt_tokens bounds the prefill activations (one row per prompt block and batch row);
+    the caches still follow max_tokens."""
+    import hierarchical_global_local_amd as hg
+    c = wl.get_config("c2_decode_heavy")
+    Tp = wl.padded_len(c, c.prompt_len)
+    full = hg.BtConfig.make(c, 1024, Tp + c.gen_len)
+    short = hg.BtConfig.make(c, 1024, Tp + c.gen_len, Tp)
+    L = hg.lib()
+    nb_full, nb_short = L.bt_workspace_bytes(ctypes.byref(full)), L.bt_workspace_bytes(ctypes.byref(short))
+    assert 0 < nb_short < nb_full
+    for which in (0, 1):
+        got = []
+        for cfg in (full, short):
+            off, nb, cap = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+            assert L.bt_workspace_region(ctypes.byref(cfg), which, ctypes.byref(off), ctypes.byref(nb),
+                                         ctypes.byref(cap)) == 0
+            got.append((nb.value, cap.value))
+        assert got[0] == got[1]

@@ -143,6 +143,11 @@ def test_host_side_errors():
     with pytest.raises(hg.BtError) as e:
         model.prefill(torch.zeros((1, 16), dtype=torch.int32, device="cuda"))
     assert e.value.code == -2
+    short = hg.BlockTransformer(cfg, W, max_batch=2, max_tokens=16, max_prompt_tokens=8)
+    with pytest.raises(hg.BtError) as e:
+        short.prefill(torch.zeros((2, 9), dtype=torch.int32, device="cuda"))   # padded to 12 > 8
+    assert e.value.code == -2
+    short.prefill(torch.zeros((2, 8), dtype=torch.int32, device="cuda"))
     model.prefill(torch.zeros((2, 11), dtype=torch.int32, device="cuda"))   # padded to 12, room for 4 tokens
     for _ in range(3):
         model.decode_step()
