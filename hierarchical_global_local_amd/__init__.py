@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
     L.bt_workspace_bytes.argtypes, L.bt_workspace_bytes.restype = [cfgp], c_sz
     L.bt_init.argtypes = [cfgp, c_p, c_p, c_sz, c_p, ctypes.POINTER(c_p)]
     L.bt_prefill.argtypes = [c_p, c_p, c_i32, c_i32, c_p, c_p]
+    L.bt_prefill_lengths.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
     L.bt_decode_step.argtypes = [c_p, c_p, c_p]
     L.bt_cache_lengths.argtypes = [c_p, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
     L.bt_workspace_region.argtypes = [cfgp, c_i32, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz), ctypes.POINTER(c_i32)]
@@ -76,7 +77,7 @@ def lib() -> ctypes.CDLL:
     L.bt_test_gemm.argtypes = [c_i32, c_p, c_p, c_p, c_i32, c_i32, c_i32, ctypes.c_float, c_p]
     L.bt_set_graphs.argtypes = [c_p, c_i32]
     L.bt_test_replay.argtypes = [c_p, c_i32, c_i32]
-    for f in ("bt_init", "bt_prefill", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
+    for f in ("bt_init", "bt_prefill", "bt_prefill_lengths", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
               "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs", "bt_test_replay"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -173,15 +174,22 @@ class BlockTransformer:
                 if t is not None:
                     t.record_stream(self.stream)
 
-    def prefill(self, prompt, out=None, logits=None):
-        """prompt: int32 device tensor [B, T]; writes the first generated ids into ``out`` [B]."""
+    def prefill(self, prompt, out=None, logits=None, lengths=None):
+        """prompt: int32 device tensor [B, T]; writes the first generated ids into ``out`` [B].
+        lengths: optional int32 device tensor [B]: row b's prompt is prompt[b, :lengths[b]]."""
         torch = self.torch
         assert prompt.dtype == torch.int32 and prompt.is_contiguous() and prompt.dim() == 2
         B, T = prompt.shape
         if out is None:
             out = torch.empty(B, dtype=torch.int32, device=self.device)
-        self._order(prompt, out, logits)
-        check(lib().bt_prefill(self.h, prompt.data_ptr(), B, T, out.data_ptr(), _ptr(logits)))
+        if lengths is None:
+            self._order(prompt, out, logits)
+            check(lib().bt_prefill(self.h, prompt.data_ptr(), B, T, out.data_ptr(), _ptr(logits)))
+        else:
+            assert lengths.dtype == torch.int32 and lengths.is_contiguous() and lengths.shape == (B,)
+            self._order(prompt, lengths, out, logits)
+            check(lib().bt_prefill_lengths(self.h, prompt.data_ptr(), lengths.data_ptr(), B, T, out.data_ptr(),
+                                           _ptr(logits)))
         self.batch = B
         return out
 

@@ -631,7 +631,21 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
   return BT_OK;
 }
 
+static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
+                        int32_t* d_next, float* d_logits);
+
 int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int32_t* d_next, float* d_logits) {
+  return prefill_impl(h, d_prompt, nullptr, B, T, d_next, d_logits);
+}
+
+int bt_prefill_lengths(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
+                       int32_t* d_next, float* d_logits) {
+  if (!d_lengths) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  return prefill_impl(h, d_prompt, d_lengths, B, T, d_next, d_logits);
+}
+
+static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
+                        int32_t* d_next, float* d_logits) {
   if (!h || !d_prompt || !d_next) return fail(BT_ERR_INVALID_ARG, "NULL argument");
   if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
   const Layout& lo = h->lo;
@@ -654,8 +668,8 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
   const double E = (double)lo.elem, Dd = lo.D, Md = M;
   {
     Prof p(h, PK_EMBED, Md * Dd * (lo.tab_elem + 4.0) + (double)B * T * 4.0, 0.0);
-    BT_CHECK(h, launch_embed_prompt(d_prompt, B, T, Tp, h->cfg.pad_id, P_(h, lo.emb_block), !lo.f32, lo.V, lo.De, L,
-                                    (float*)P_(h, lo.X), (int*)P_(h, lo.dstate), h->st),
+    BT_CHECK(h, launch_embed_prompt(d_prompt, d_lengths, B, T, Tp, h->cfg.pad_id, P_(h, lo.emb_block), !lo.f32, lo.V,
+                                    lo.De, L, (float*)P_(h, lo.X), (int*)P_(h, lo.dstate), h->st),
              "embed prompt");
   }
   for (int l = 0; l < lo.Nb; ++l) {

@@ -93,9 +93,10 @@ hipError_t launch_add_f32(float* dst, const float* a, int n, hipStream_t st);
 hipError_t launch_rope_table(float2* tab, int npos, int dh, float base, hipStream_t st);
 
 // ---- embedders
-// prompt blocks: X[b*n + i][o*De + d] = E[tok(b, i*L + o)][d], tok from the left-padded prompt
-// Also sets the device block-KV length *n_state = Tp / L.
-hipError_t launch_embed_prompt(const int32_t* prompt, int B, int T, int Tp, int pad, const void* E,
+// prompt blocks: X[b*n + i][o*De + d] = E[tok(b, i*L + o)][d], tok from the left-padded prompt: row b
+// holds len_b tokens at positions [0, len_b) (len_b = T without `lengths`, else lengths[b] clamped to
+// [1, T]) and is padded on the left to Tp.  Also sets the device block-KV length *n_state = Tp / L.
+hipError_t launch_embed_prompt(const int32_t* prompt, const int32_t* lengths, int B, int T, int Tp, int pad, const void* E,
                                bool tab_bf16, int V, int De, int L, float* X, int* n_state, hipStream_t st);
 // ---- LayerNorm over rows r < rows of X[(r*stride + off)][:] -> out1 (params p1), out2 (p2, optional).
 // With `resid` (split-K residual update pending), the row is first completed as

@@ -148,7 +148,8 @@ hipError_t launch_rope_table(float2* tab, int npos, int dh, float base, hipStrea
 __device__ __forceinline__ int clamp_id(int t, int V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
 
 template <typename Tt>
-__global__ __launch_bounds__(256) void k_embed_prompt(const int32_t* __restrict__ prompt, int T, int Tp, int pad,
+__global__ __launch_bounds__(256) void k_embed_prompt(const int32_t* __restrict__ prompt,
+                                                      const int32_t* __restrict__ lengths, int T, int Tp, int pad,
                                                       const Tt* __restrict__ E, int V, int De, int L,
                                                       float* __restrict__ X, int* __restrict__ n_state) {
   const int n = Tp / L;
@@ -156,23 +157,25 @@ __global__ __launch_bounds__(256) void k_embed_prompt(const int32_t* __restrict_
   const int row = blockIdx.x;  // b * n + i
   const int b = row / n, i = row % n;
   const int D = De * L;
+  const int len = lengths ? min(max(lengths[b], 1), T) : T;
   for (int c = threadIdx.x; c < D; c += 256) {
     int o = c / De, d = c % De;
-    int p = i * L + o - (Tp - T);  // position in the unpadded prompt
+    int p = i * L + o - (Tp - len);  // position in the row's unpadded prompt
     int tok = p < 0 ? pad : prompt[(size_t)b * T + p];
     X[(size_t)row * D + c] = load_f32(E + (size_t)clamp_id(tok, V) * De + d);
   }
 }
 
-hipError_t launch_embed_prompt(const int32_t* prompt, int B, int T, int Tp, int pad, const void* E,
-                               bool tab_bf16, int V, int De, int L, float* X, int* n_state, hipStream_t st) {
+hipError_t launch_embed_prompt(const int32_t* prompt, const int32_t* lengths, int B, int T, int Tp, int pad,
+                               const void* E, bool tab_bf16, int V, int De, int L, float* X, int* n_state,
+                               hipStream_t st) {
   dim3 grid(B * (Tp / L));
   if (tab_bf16)
-    hipLaunchKernelGGL(k_embed_prompt<bf16_t>, grid, dim3(256), 0, st, prompt, T, Tp, pad, (const bf16_t*)E, V,
-                       De, L, X, n_state);
+    hipLaunchKernelGGL(k_embed_prompt<bf16_t>, grid, dim3(256), 0, st, prompt, lengths, T, Tp, pad, (const bf16_t*)E,
+                       V, De, L, X, n_state);
   else
-    hipLaunchKernelGGL(k_embed_prompt<float>, grid, dim3(256), 0, st, prompt, T, Tp, pad, (const float*)E, V, De,
-                       L, X, n_state);
+    hipLaunchKernelGGL(k_embed_prompt<float>, grid, dim3(256), 0, st, prompt, lengths, T, Tp, pad, (const float*)E, V,
+                       De, L, X, n_state);
   return hipGetLastError();
 }
 

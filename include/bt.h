@@ -123,6 +123,16 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
 int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int32_t* d_next,
                float* d_logits);
 
+/* Prefill with a prompt length per row (summary page §3.4 "The Embedder": sequences are left
+ * padded so that every row is whole blocks).  Row b of d_prompt (device int32 [B, T]) holds its
+ * lengths[b] tokens in columns [0, lengths[b]); the rest of the row is ignored.  Every row is left
+ * padded with pad_id to the same T' as bt_prefill computes from T, so a row of length len gets
+ * T' - len pad tokens; the result equals bt_prefill on that host-padded prompt.  d_lengths: device
+ * int32 [B]; values outside [1, T] are clamped to it (they are not read on the host).  Other
+ * arguments, capacities and errors as bt_prefill. */
+int bt_prefill_lengths(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
+                       int32_t* d_next, float* d_logits);
+
 /* One decode step (summary page §3.4, decode stage): feeds back the token the
  * previous call emitted and writes the next token of every row to d_next
  * (device int32 [B]; B is the prefill's batch), plus its fp32 logits [B, V] if

@@ -222,3 +222,37 @@ def test_kernel_replay_leaves_decoding_unchanged():
     assert np.array_equal(ids.cpu().numpy().T, ref)
     with pytest.raises(hg.BtError):
         model.replay("layernorm", 1)
+
+
+@pytest.mark.parametrize("name", ["c0_tiny", "small_bf16"])
+def test_per_row_prompt_lengths(name):
+    """bt_prefill_lengths: each row left-padded to the common length equals bt_prefill on the
+    host-padded prompt (bit for bit) and the oracle on it (pad tokens are ordinary tokens)."""
+    torch = require_gpu()
+    import hierarchical_global_local_amd as hg
+    cfg = SMALL_BF16 if name == "small_bf16" else wl.get_config("c0_tiny")
+    W = wl.make_weights(cfg, seed=12, ln_jitter=True)
+    B, T, G = 5, 23, 10
+    rng = np.random.default_rng(12)
+    lengths = np.array([23, 1, 9, 16, 4], dtype=np.int32)
+    prompt = rng.integers(0, cfg.vocab, (B, T)).astype(np.int32)          # tokens past a row's length are junk
+    Tp = wl.padded_len(cfg, T)
+    padded = np.full((B, Tp), cfg.pad_id, dtype=np.int32)
+    for b in range(B):
+        padded[b, Tp - lengths[b]:] = prompt[b, :lengths[b]]
+    ref_ids, ref_lg, _ = run_gpu(cfg, W, padded, G, logits_steps=range(G))
+    model = hg.BlockTransformer(cfg, W, max_batch=B, max_tokens=Tp + G)
+    ids = torch.empty((G, B), dtype=torch.int32, device="cuda")
+    lg = torch.empty((G, B, cfg.vocab), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(model.stream):
+        model.prefill(torch.from_numpy(prompt).cuda(), ids[0], lg[0], lengths=torch.from_numpy(lengths).cuda())
+        for g in range(1, G):
+            model.decode_step(ids[g], lg[g])
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy().T
+    assert np.array_equal(got, ref_ids)
+    for g in range(G):
+        np.testing.assert_array_equal(lg[g].cpu().numpy(), ref_lg[g])
+    _, oracle_lg, _ = om.generate(om.weights_as(W, np.float64), cfg, padded, G, keep_logits=True, forced=got)
+    tol = FP32_TOL if cfg.dtype == "fp32" else BF16_TOL
+    assert np.abs(np.stack([lg[g].cpu().numpy() for g in range(G)], axis=1) - oracle_lg).max() <= tol
