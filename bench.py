@@ -161,7 +161,7 @@ def roofline_of(name, rec):
 COPY_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_JSON = os.path.join(PROFILES, "traffic_decode_gemm_qkv_up.json")
-GEMM_SOURCE = os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", "gemm.hip")
+GEMM_SOURCE = os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", "gemm_decode.hip")
 
 
 def _rocprof_db(d):
@@ -223,6 +223,24 @@ def traffic_from_counters(fetch_dir, write_dir, kernel_pattern):
     os.makedirs(PROFILES, exist_ok=True)
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(res, f, indent=1)
+    # readable summary of the two counter runs next to it
+    lines = [f"# HBM traffic of the decode [q|k|v|up] GEMM ({name[:60]}...) in c1_prefill_heavy",
+             "# commands (two passes, one counter each; the 1 GiB reference copy precedes the workload):",
+             "#   cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT"]
+    for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        lines.append(f"#   rocprofv3 --pmc {c} -d {d} -o run -- python3 bench.py --steps 1 --warmup 0 "
+                     "--decode-config none --no-cpu-baseline --no-profile --copy-calibration")
+    lines.append(f"#   python bench.py --traffic {fetch_dir} {write_dir} --kernel {kernel_pattern}")
+    lines.append(f"# scaling: FETCH_SIZE of the 1 GiB copy reads {max(copy_f):.0f} KiB (x{f_scale:.3f}), "
+                 f"WRITE_SIZE {max(copy_w):.0f} KiB (x{w_scale:.3f})")
+    lines.append("# per-kernel averages (KiB per dispatch, unscaled), the 10 most frequent kernels:")
+    for cname, d in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        for k, vs in sorted(d.items(), key=lambda kv: -len(kv[1]))[:10]:
+            lines.append(f"{cname}  {len(vs):6d}  {sum(vs) / len(vs):10.1f}  {k[:110]}")
+    lines.append(f"# result ({os.path.relpath(TRAFFIC_JSON, ROOT)}): fetch {fb / 1e6:.2f} MB + write {wb / 1e6:.2f} MB "
+                 f"per launch = {(fb + wb) / 1e6:.2f} MB")
+    with open(os.path.join(PROFILES, "counters_decode_gemm_qkv_up_c1.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
     return res
 
 

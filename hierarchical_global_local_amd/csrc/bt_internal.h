@@ -136,6 +136,15 @@ struct Epi {
 // Number of K splits the [out|down] GEMM uses for M rows (1 for large M); also the partial count
 // the next LayerNorm must reduce.
 int resid_splits(int M, int N, int K);
+// Decode-shape (M <= 256) fp16 GEMM (gemm_decode.hip): the configuration a shape runs, and its launch.
+struct SkinnyPlan {
+  bool ok;             // the shape runs on the skinny kernel
+  int mg, mw, ng, kw;  // row groups per wave, waves along M, column groups per wave, waves along K
+  int splits;          // K splits over workgroups (EPI_RESID)
+};
+SkinnyPlan skinny_plan(int M, int N, int K, EpiMode mode);
+hipError_t launch_gemm_skinny(const SkinnyPlan& p, const void* A1, const void* A2, const void* W, int M, int N, int K,
+                              EpiMode mode, const Epi& ep, hipStream_t st);
 hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N,
                        int K, EpiMode mode, const Epi& ep, hipStream_t st);
 

@@ -8,7 +8,8 @@
 //    conflict-free 16-byte reads, no swizzle or padding.  Workgroup ids are remapped so that each
 //    of the 8 XCDs walks a contiguous range of output tiles, grouped 8 M-tiles at a time, so that A
 //    and W tiles are re-read from that XCD's L2 rather than from HBM.
-//  - skinny kernel (decode, M <= 256): operands go straight from memory into registers.
+//  - large-tile kernel (prefill with a long K): 256 x 256 tiles fed by direct global -> LDS copies;
+//  - the skinny kernel for decode shapes (M <= 256) is in gemm_decode.hip.
 // fp32 operands (BT_FP32): a plain LDS-tiled VALU kernel with the same epilogues, row-major.
 #include <cstdlib>
 
@@ -264,165 +265,180 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
   }
 }
 
-// ---------------------------------------------------------------- skinny GEMM (decode shapes)
-// For M <= 256 rows (the batch of a decode step) the GEMM is a stream over the weights.  One
-// workgroup owns a slab of 16*NG output columns for ALL rows: MW waves along M (MG 16-row groups
-// each) times KW waves along K.  Both operands are in fragment order and go straight from memory
-// into MFMA operand registers (one contiguous 1 KB load per 16 x 32 tile, no LDS on the operand
-// path), DEPTH K steps in flight per wave.  The KW partial tiles are summed once through LDS, in a
-// fixed order, and the epilogue writes 8 consecutive columns per thread.  gridDim.y > 1 splits K
-// over workgroups (EPI_RESID only): the partial products go to ep.part and the consumer adds them.
-template <int MG, int MW, int NG, int KW, int MODE, int DEPTH = 2>
-__global__ __launch_bounds__(64 * MW * KW) void k_gemm_skinny(const f16* __restrict__ A1, const f16* __restrict__ A2,
-                                                              const f16* __restrict__ W, int M, int N, int K, Epi ep) {
-  constexpr int R = 16 * MG * MW, C = 16 * NG, CLD = C + 4, NT = 64 * MW * KW;
-  __shared__ __attribute__((aligned(16))) float red[KW * R * CLD];
-  const int KS = K / 32, mgs = (M + 15) / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int mw = wave % MW, kw = wave / MW;
-  const int ng0 = blockIdx.x * NG, n0 = ng0 * 16;
+// ---------------------------------------------------------------- large-tile GEMM (prefill)
+// With many rows (prefill: M = batch x prompt blocks) the GEMM is MFMA-bound, and what limits the
+// 128 x 128 kernel is LDS read bandwidth (a 64 x 64 wave tile reads 8 KB of fragments per 16
+// MFMAs) and global latency (one register stage of prefetch).  Here each of the 4 waves owns a
+// 128 x TN tile (accumulators in AGPRs), which halves the LDS bytes per MFMA, and the operand tiles
+// travel global -> LDS directly (global_load_lds_dwordx4: a wave moves one 1 KB fragment-order tile
+// per instruction, no registers) through a ring of NS = 4 stages, 3 K steps in flight.
+// Each wave waits for its own copies of a stage with an explicit vmcnt and the workgroup barrier
+// publishes them; a slot is refilled only after the barrier that follows every wave's last use of
+// it.  EPI_QKV_GELU and EPI_RESID (no split) only; the epilogue goes through LDS 128 rows at a time
+// so that every global store is a whole 16-byte segment.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {  // s_waitcnt vmcnt(N), other counters untouched
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+// workgroup barrier without a memory fence (which would wait for every copy in flight); the empty
+// asm statements keep the compiler from moving LDS accesses across it
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BN, int NS, int MODE>
+__global__ __launch_bounds__(256) void k_gemm_big(const f16* __restrict__ A1, const f16* __restrict__ A2,
+                                                  const f16* __restrict__ W, int M, int N, int K, Epi ep) {
+  constexpr int BM = 256, WN = 2;
+  constexpr int TM = 128, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+  constexpr int CHA = BM / 16, CHB = BN / 16;  // 1 KB operand tiles per 32-wide K step
+  constexpr int CA = CHA / 4, CB = CHB / 4;    // copies per wave per stage
+  constexpr int PER = CA + CB;
+  constexpr int STG = (CHA + CHB) * 512;       // f16 elements per stage
+  constexpr int SR = TM, CLD = BN + 4;         // epilogue slab: one wave row of fp32
+  constexpr int EPIL = SR * CLD * 2;
+  static_assert(MODE == EPI_QKV_GELU || MODE == EPI_RESID, "epilogue");
+  static_assert(NS == 4 && 2 * PER < 64, "ring: three stages in flight");
+  __shared__ __attribute__((aligned(16))) f16 smem[NS * STG > EPIL ? NS * STG : EPIL];
+
+  const int ntm = (M + BM - 1) / BM, ntn = N / BN;
+  const int t = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  constexpr int GM = 8;
+  const int group = t / (GM * ntn), first_m = group * GM;
+  const int gm = min(GM, ntm - first_m);
+  const int r_in = t - group * GM * ntn;
+  const int tm = first_m + r_in % gm, tn = r_in / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
   const f16* __restrict__ A = (MODE == EPI_QKV_GELU && n0 >= ep.n_split) ? A2 : A1;
-  // K steps of this workgroup (split blockIdx.y of gridDim.y), then of this wave
-  const int S = gridDim.y, sper = (KS + S - 1) / S;
-  const int sb = blockIdx.y * sper, se = min(KS, sb + sper);
-  const int wper = (se - sb + KW - 1) / KW;
-  const int kb = min(se, sb + kw * wper), ke = min(se, kb + wper);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int KS = K / 32, mgs = (M + 15) / 16, mg0 = m0 / 16, ng0 = n0 / 16;
 
-  const f16* ap[MG];
+  // K step ks -> ring slot ks % NS: A tiles (16-row groups of the tile) then W tiles
+  auto issue = [&](int ks) {
+    f16* st = smem + (ks % NS) * STG;
 #pragma unroll
-  for (int i = 0; i < MG; ++i) ap[i] = A + ((size_t)min(mw * MG + i, mgs - 1) * KS * 64 + lane) * 8;
-  const f16* wp[NG];
+    for (int i = 0; i < CA; ++i) {
+      const int c = wave + 4 * i, mg = min(mg0 + c, mgs - 1);
+      __builtin_amdgcn_global_load_lds(A + ((size_t)(mg * KS + ks) * 64 + lane) * 8,
+                                       (__attribute__((address_space(3))) void*)(st + c * 512), 16, 0, 0);
+    }
 #pragma unroll
-  for (int j = 0; j < NG; ++j) wp[j] = W + ((size_t)(ng0 + j) * KS * 64 + lane) * 8;
-
-  float4_ acc[MG][NG];
-#pragma unroll
-  for (int i = 0; i < MG; ++i)
-#pragma unroll
-    for (int j = 0; j < NG; ++j) acc[i][j] = float4_{0.f, 0.f, 0.f, 0.f};
-  half8 ra[DEPTH][MG], rw[DEPTH][NG];
-  auto load = [&](int s, int ks) {
-#pragma unroll
-    for (int i = 0; i < MG; ++i) ra[s][i] = *(const half8*)(ap[i] + (size_t)ks * 512);
-#pragma unroll
-    for (int j = 0; j < NG; ++j) rw[s][j] = *(const half8*)(wp[j] + (size_t)ks * 512);
+    for (int i = 0; i < CB; ++i) {
+      const int c = wave + 4 * i;
+      __builtin_amdgcn_global_load_lds(W + ((size_t)((ng0 + c) * KS + ks) * 64 + lane) * 8,
+                                       (__attribute__((address_space(3))) void*)(st + (CHA + c) * 512), 16, 0, 0);
+    }
   };
-#pragma unroll
-  for (int s = 0; s < DEPTH; ++s)
-    if (kb + s < ke) load(s, kb + s);
-  for (int k0 = kb; k0 < ke; k0 += DEPTH) {
-#pragma unroll
-    for (int s = 0; s < DEPTH; ++s) {
-      if (k0 + s < ke) {
-#pragma unroll
-        for (int i = 0; i < MG; ++i)
-#pragma unroll
-          for (int j = 0; j < NG; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ra[s][i], rw[s][j], acc[i][j], 0, 0, 0);
-        if (k0 + s + DEPTH < ke) load(s, k0 + s + DEPTH);
-      }
-    }
-  }
-  // partial tiles of the KW waves -> LDS [kw][row][col]
-#pragma unroll
-  for (int i = 0; i < MG; ++i)
-#pragma unroll
-    for (int j = 0; j < NG; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        red[(kw * R + (mw * MG + i) * 16 + 4 * (lane >> 4) + e) * CLD + j * 16 + (lane & 15)] = acc[i][j][e];
-  __syncthreads();
 
-  // epilogue: item = (row, 8 consecutive columns); every thread runs the same number of items so
-  // that the row-wise shuffles of EPI_ARGMAX see whole groups
-  constexpr int CPR = C / 8, ITEMS = R * CPR, ITER = (ITEMS + NT - 1) / NT;
-  static_assert(64 % CPR == 0 && NT % 64 == 0, "a row's items sit in one wave");
-  const int tid = threadIdx.x;
-#pragma unroll 1
-  for (int it = 0; it < ITER; ++it) {
-    const int item = tid + it * NT;
-    const int rl = min(item, ITEMS - 1) / CPR, cl = (min(item, ITEMS - 1) % CPR) * 8;
-    const int row = rl, col = n0 + cl;
-    const bool live = item < ITEMS && row < M;
-    float v[8];
-    {
-      float4 a0 = *(const float4*)&red[rl * CLD + cl], a1 = *(const float4*)&red[rl * CLD + cl + 4];
+  float4_ acc[FM][FN];
 #pragma unroll
-      for (int q = 1; q < KW; ++q) {
-        const float4 b0 = *(const float4*)&red[(q * R + rl) * CLD + cl];
-        const float4 b1 = *(const float4*)&red[(q * R + rl) * CLD + cl + 4];
-        a0.x += b0.x, a0.y += b0.y, a0.z += b0.z, a0.w += b0.w;
-        a1.x += b1.x, a1.y += b1.y, a1.z += b1.z, a1.w += b1.w;
-      }
-      v[0] = a0.x, v[1] = a0.y, v[2] = a0.z, v[3] = a0.w, v[4] = a1.x, v[5] = a1.y, v[6] = a1.z, v[7] = a1.w;
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = float4_{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q)
+    if (q < KS) issue(q);
+  for (int ks = 0; ks < KS; ++ks) {
+    // stage ks is complete once at most (stages issued after it) x PER copies are outstanding
+    const int later = min(NS - 2, KS - 1 - ks);
+    if (later >= 2) wait_vmcnt<2 * PER>();
+    else if (later == 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+    // after this barrier every wave has consumed (waited for and multiplied) its reads of step
+    // ks - 1, so that step's slot can be refilled
+    barrier_nofence();
+    if (ks + NS - 1 < KS) issue(ks + NS - 1);
+    const f16* st = smem + (ks % NS) * STG;
+    // all fragments of the step are read before the first MFMA (the scheduling barrier keeps the
+    // compiler from sinking the reads between MFMA groups, which would expose the LDS latency)
+    half8 af[FM], bw[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) bw[fn] = *(const half8*)&st[(CHA + wn * FN + fn) * 512 + lane * 8];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) af[fm] = *(const half8*)&st[(wm * FM + fm) * 512 + lane * 8];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with the ring before it becomes the epilogue's staging area
+
+  // epilogue, one wave row (128 rows) of the tile at a time: the two waves owning it stage
+  // acc * scale + bias in LDS, then all threads apply GELU (the up columns) and write whole 16-byte
+  // segments, so that the transcendental work is spread over the whole workgroup
+  float bias[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+    bias[fn] = ep.bias[col] + (MODE == EPI_RESID ? ep.bias2[col] : 0.f);
+  }
+  float* Cs = reinterpret_cast<float*>(smem);
+  const bool gelu = MODE == EPI_QKV_GELU && n0 >= ep.n_split;
+#pragma unroll
+  for (int s = 0; s < BM / SR; ++s) {
+    if (wm == s) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int cl = wn * TN + fn * 16 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Cs[(fm * 16 + (lane >> 4) * 4 + i) * CLD + cl] = acc[fm][fn][i] * ep.wscale + bias[fn];
+        }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= ep.wscale;
+    __syncthreads();
+    const int r0 = m0 + s * SR;
     if constexpr (MODE == EPI_QKV_GELU) {
-      const float4 c0 = *(const float4*)(ep.bias + col), c1 = *(const float4*)(ep.bias + col + 4);
-      v[0] += c0.x, v[1] += c0.y, v[2] += c0.z, v[3] += c0.w, v[4] += c1.x, v[5] += c1.y, v[6] += c1.z, v[7] += c1.w;
-      if (live) {
-        half8 w;
-        if (n0 >= ep.n_split) {
+      constexpr int CH = SR * BN / 8 / 256;
+#pragma unroll 4
+      for (int q = 0; q < CH; ++q) {
+        const int c = tid + q * 256, rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+        const int row = r0 + rl;
+        if (row < M) {
+          half8 w;
+          if (gelu) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) w[e] = to_f16(gelu_erf(v[e]));
-          *(half8*)((f16*)ep.out1 + frag_off(row, ep.act_col0 + (col - ep.n_split), ep.ld1)) = w;
-        } else {
+            for (int e = 0; e < 8; ++e) w[e] = to_f16(gelu_erf(Cs[rl * CLD + cl + e]));
+            *(half8*)((f16*)ep.out1 + frag_off(row, ep.act_col0 + (n0 - ep.n_split) + cl, ep.ld1)) = w;
+          } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) w[e] = to_f16(v[e]);
-          *(half8*)((f16*)ep.out0 + (size_t)row * ep.ld0 + col) = w;
+            for (int e = 0; e < 8; ++e) w[e] = to_f16(Cs[rl * CLD + cl + e]);
+            *(half8*)((f16*)ep.out0 + (size_t)row * ep.ld0 + n0 + cl) = w;
+          }
         }
       }
-    } else if constexpr (MODE == EPI_RESID) {
-      if (S > 1) {
-        float* p = ep.part + ((size_t)blockIdx.y * M + row) * N + col;
-        if (live) {
-          *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
-          *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      // residual rows in groups of 8 float4 per thread: all loads of a group before its stores
+      constexpr int CH = SR * BN / 4 / 256, G = 8;
+      float* X = (float*)ep.out0;
+#pragma unroll
+      for (int q0 = 0; q0 < CH; q0 += G) {
+        float4 xo[G];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          const int c = tid + (q0 + q) * 256, rl = c / (BN / 4), cl = (c % (BN / 4)) * 4;
+          xo[q] = *(const float4*)(X + (size_t)min(r0 + rl, M - 1) * ep.ld0 + n0 + cl);
         }
-      } else {
-        float* x = (float*)ep.out0 + (size_t)min(row, M - 1) * ep.ld0 + col;
-        const float4 x0 = *(const float4*)x, x1 = *(const float4*)(x + 4);
-        const float4 c0 = *(const float4*)(ep.bias + col), c1 = *(const float4*)(ep.bias + col + 4);
-        const float4 d0 = *(const float4*)(ep.bias2 + col), d1 = *(const float4*)(ep.bias2 + col + 4);
-        if (live) {
-          *(float4*)x = make_float4(x0.x + (v[0] + c0.x + d0.x), x0.y + (v[1] + c0.y + d0.y),
-                                    x0.z + (v[2] + c0.z + d0.z), x0.w + (v[3] + c0.w + d0.w));
-          *(float4*)(x + 4) = make_float4(x1.x + (v[4] + c1.x + d1.x), x1.y + (v[5] + c1.y + d1.y),
-                                          x1.z + (v[6] + c1.z + d1.z), x1.w + (v[7] + c1.w + d1.w));
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          const int c = tid + (q0 + q) * 256, rl = c / (BN / 4), cl = (c % (BN / 4)) * 4;
+          if (r0 + rl < M) {
+            const float* cs = &Cs[rl * CLD + cl];
+            *(float4*)(X + (size_t)(r0 + rl) * ep.ld0 + n0 + cl) =
+                make_float4(xo[q].x + cs[0], xo[q].y + cs[1], xo[q].z + cs[2], xo[q].w + cs[3]);
+          }
         }
       }
-    } else if constexpr (MODE == EPI_STORE) {
-      float b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (ep.bias) {
-        const float4 c0 = *(const float4*)(ep.bias + col), c1 = *(const float4*)(ep.bias + col + 4);
-        b[0] = c0.x, b[1] = c0.y, b[2] = c0.z, b[3] = c0.w, b[4] = c1.x, b[5] = c1.y, b[6] = c1.z, b[7] = c1.w;
-      }
-      if (live) {
-        float* o = (float*)ep.out0 + (size_t)row * ep.ld0 + col;
-        *(float4*)o = make_float4(v[0] + b[0], v[1] + b[1], v[2] + b[2], v[3] + b[3]);
-        *(float4*)(o + 4) = make_float4(v[4] + b[4], v[5] + b[5], v[6] + b[6], v[7] + b[7]);
-      }
-    } else {  // EPI_ARGMAX
-      unsigned long long best = 0ull;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const unsigned long long k = argmax_key(v[e], col + e);
-        if (col + e < ep.n_valid && k > best) best = k;
-      }
-      if (live && ep.out0) {
-        float* o = (float*)ep.out0 + (size_t)row * ep.ld0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (col + e < ep.n_valid) o[col + e] = v[e];
-      }
-#pragma unroll
-      for (int o = 1; o < CPR; o <<= 1) {
-        const unsigned long long other = shfl_xor_u64(best, o);
-        best = other > best ? other : best;
-      }
-      if (live && cl == 0) ep.keys[(size_t)row * ep.keys_ld + blockIdx.x] = best;
     }
+    __syncthreads();
   }
 }
 
@@ -510,26 +526,15 @@ static hipError_t launch_mfma_cfg(const void* A1, const void* A2, const void* W,
   return hipGetLastError();
 }
 
-template <int MG, int MW, int NG, int KW>
-static hipError_t launch_skinny_cfg(const void* A1, const void* A2, const void* W, int M, int N, int K, EpiMode mode,
-                                    const Epi& ep, int S, hipStream_t st) {
-  if (mode == EPI_ARGMAX && ep.nparts_out) *ep.nparts_out = N / (16 * NG);
-  dim3 grid(N / (16 * NG), S), block(64 * MW * KW);
+template <int BN, int NS>
+static hipError_t launch_big_cfg(const void* A1, const void* A2, const void* W, int M, int N, int K, EpiMode mode,
+                                 const Epi& ep, hipStream_t st) {
+  dim3 grid(((M + 255) / 256) * (N / BN)), block(256);
   const f16 *a1 = (const f16*)A1, *a2 = (const f16*)A2, *w = (const f16*)W;
-  switch (mode) {
-    case EPI_QKV_GELU:
-      hipLaunchKernelGGL((k_gemm_skinny<MG, MW, NG, KW, EPI_QKV_GELU>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
-      break;
-    case EPI_RESID:
-      hipLaunchKernelGGL((k_gemm_skinny<MG, MW, NG, KW, EPI_RESID>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
-      break;
-    case EPI_STORE:
-      hipLaunchKernelGGL((k_gemm_skinny<MG, MW, NG, KW, EPI_STORE>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
-      break;
-    case EPI_ARGMAX:
-      hipLaunchKernelGGL((k_gemm_skinny<MG, MW, NG, KW, EPI_ARGMAX>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
-      break;
-  }
+  if (mode == EPI_QKV_GELU)
+    hipLaunchKernelGGL((k_gemm_big<BN, NS, EPI_QKV_GELU>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
+  else
+    hipLaunchKernelGGL((k_gemm_big<BN, NS, EPI_RESID>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
   return hipGetLastError();
 }
 
@@ -554,50 +559,21 @@ static hipError_t launch_f32(const float* A, int lda, const float* W, int M, int
   return hipGetLastError();
 }
 
-// Which fp16 kernel a GEMM of this shape runs (shared by launch_gemm and resid_splits, so that the
-// split count the consumer folds is the one the kernel used).
-struct GemmPlan {
-  bool skinny;
-  int mg, mw, ng, kw;  // skinny: waves and fragments
-  int splits;          // K splits over workgroups (EPI_RESID only)
-};
-
-static GemmPlan plan_gemm(int M, int N, int K, EpiMode mode) {
-  GemmPlan p{};
-  p.splits = 1;
-  // The skinny kernel streams the weights once for all M <= 256 rows.  The classifier of a batch
-  // above 128 rows has enough MFMA work to prefer the LDS-tiled kernel.
-  p.skinny = M <= 256 && N % 32 == 0 && K % 32 == 0 && !(mode == EPI_ARGMAX && M > 128);
-  if (p.skinny) {
-    const int mgt = (M + 15) / 16;
-    if (mgt <= 1) p.mg = 1, p.mw = 1;
-    else if (mgt <= 2) p.mg = 2, p.mw = 1;
-    else if (mgt <= 4) p.mg = 4, p.mw = 1;
-    else if (mgt <= 8) p.mg = 4, p.mw = 2;
-    else p.mg = 4, p.mw = 4;
-    p.kw = p.mw == 1 ? 8 : 4;
-    p.ng = (p.mw == 2 && N % 64 == 0 && N / 64 >= 224) ? 4 : 2;
-    const int slabs = N / (16 * p.ng), ks = K / 32;
-    if (mode == EPI_RESID && slabs < 128) {
-      // narrow outputs ([out|down]: N = d_model) split K so that ~192 workgroups stream the weights
-      int s = std::min(16, (192 + slabs - 1) / slabs);
-      s = std::max(1, std::min(s, ks / p.kw));
-      const int per = (ks + s - 1) / s;
-      p.splits = (ks + per - 1) / per;  // every split owns at least one K step
-    }
-    return p;
-  }
-  if (mode == EPI_RESID && M <= 1024) {
-    const int tiles = ((M + 63) / 64) * std::max(1, N / 64);
-    const int nk = std::max(1, K / 64);
-    int s = std::min(std::min(16, nk), std::max(1, (512 + tiles - 1) / tiles));
-    const int per = (nk + s - 1) / s;
-    p.splits = (nk + per - 1) / per;
-  }
-  return p;
+// Split count of a tiled-kernel GEMM (decode-size M above the skinny range): K is split over
+// workgroups for EPI_RESID with at most 1024 rows until ~512 workgroups run.
+static int tiled_resid_splits(int M, int N, int K) {
+  if (M > 1024) return 1;
+  const int tiles = ((M + 63) / 64) * std::max(1, N / 64);
+  const int nk = std::max(1, K / 64);
+  int s = std::min(std::min(16, nk), std::max(1, (512 + tiles - 1) / tiles));
+  const int per = (nk + s - 1) / s;
+  return (nk + per - 1) / per;
 }
 
-int resid_splits(int M, int N, int K) { return plan_gemm(M, N, K, EPI_RESID).splits; }
+int resid_splits(int M, int N, int K) {
+  const SkinnyPlan p = skinny_plan(M, N, K, EPI_RESID);
+  return p.ok ? p.splits : tiled_resid_splits(M, N, K);
+}
 
 hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N, int K,
                        EpiMode mode, const Epi& ep_in, hipStream_t st) {
@@ -619,22 +595,17 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
     return launch_f32((const float*)A1, lda, (const float*)W, M, N, K, mode, ep, st);
   }
   // fp16 path: both operands in fragment order (their width is K)
-  const GemmPlan p = plan_gemm(M, N, K, mode);
-  if (mode == EPI_RESID && ep.splits != p.splits) ep.splits = p.splits;
+  const SkinnyPlan sp = skinny_plan(M, N, K, mode);
+  if (mode == EPI_RESID) ep.splits = sp.ok ? sp.splits : tiled_resid_splits(M, N, K);
   if (ep.splits > 1 && !ep.part) return hipErrorInvalidValue;
-  if (p.skinny) {
-    const int S = ep.splits;
-#define BT_SKINNY(MG, MW, NG, KW) \
-  if (p.mg == MG && p.mw == MW && p.ng == NG && p.kw == KW) return launch_skinny_cfg<MG, MW, NG, KW>(A1, A2, W, M, N, K, mode, ep, S, st);
-    BT_SKINNY(1, 1, 2, 8)
-    BT_SKINNY(2, 1, 2, 8)
-    BT_SKINNY(4, 1, 2, 8)
-    BT_SKINNY(4, 2, 2, 4)
-    BT_SKINNY(4, 2, 4, 4)
-    BT_SKINNY(4, 4, 2, 4)
-#undef BT_SKINNY
-    return hipErrorInvalidValue;
-  }
+  if (sp.ok) return launch_gemm_skinny(sp, A1, A2, W, M, N, K, mode, ep, st);
+  // 256 x 256 tiles for many rows and a long K (prefill [out|down], wide models): measured faster
+  // than the 128 x 128 kernel from K = 2048 up (+5 % at K = 3840, +17 % at K = 10240) once there
+  // are >= 256 tiles; at K = 768 its prologue and GELU epilogue, which nothing overlaps at one
+  // workgroup per CU, cost more than the LDS traffic it saves
+  if (M > 1024 && ep.splits == 1 && (mode == EPI_QKV_GELU || mode == EPI_RESID) && K % 64 == 0 && K >= 2048 &&
+      N % 256 == 0 && (mode != EPI_QKV_GELU || ep.n_split % 256 == 0) && (long)((M + 255) / 256) * (N / 256) >= 256)
+    return launch_big_cfg<256, 4>(A1, A2, W, M, N, K, mode, ep, st);
   // LDS-tiled kernel: K % 64 == 0, N % 32 == 0 and n_split on a tile boundary (checked at plan time)
   const bool split_ok128 = (mode != EPI_QKV_GELU) || (ep.n_split % 128 == 0);
   if ((M > 1024 || (M >= 256 && mode == EPI_ARGMAX)) && N % 128 == 0 && split_ok128 && ep.splits == 1)
