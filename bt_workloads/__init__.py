@@ -45,10 +45,15 @@ class Config:
     pad_id: int = 0
     ln_eps: float = 1e-5
     rope_base: float = 10000.0
+    n_kv_heads: int = 0   # key/value heads of every attention layer (grouped-query); 0 = n_heads
 
     @property
     def d_head(self) -> int:
         return self.d_model // self.n_heads
+
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_heads or self.n_heads
 
     @property
     def d_emb(self) -> int:
@@ -113,12 +118,14 @@ def get_config(name: str, **overrides) -> Config:
     return cfg.with_(**overrides) if overrides else cfg
 
 
-def _layer_specs(prefix: str, D: int, F: int) -> List[Tuple[str, Tuple[int, ...], str]]:
+def _layer_specs(prefix: str, D: int, F: int, QKV: int) -> List[Tuple[str, Tuple[int, ...], str]]:
+    """QKV = output width of attn.qkv: D query columns, then the key and the value columns of the
+    key/value heads (D each without grouped-query attention)."""
     return [
         (f"{prefix}.ln1.g", (D,), "ln_gain"),
         (f"{prefix}.ln1.b", (D,), "ln_bias"),
-        (f"{prefix}.attn.qkv.w", (D, 3 * D), "normal"),
-        (f"{prefix}.attn.qkv.b", (3 * D,), "normal"),
+        (f"{prefix}.attn.qkv.w", (D, QKV), "normal"),
+        (f"{prefix}.attn.qkv.b", (QKV,), "normal"),
         (f"{prefix}.attn.out.w", (D, D), "normal"),
         (f"{prefix}.attn.out.b", (D,), "normal"),
         (f"{prefix}.ln2.g", (D,), "ln_gain"),
@@ -137,9 +144,10 @@ def weight_specs(cfg: Config) -> List[Tuple[str, Tuple[int, ...], str]]:
     the canonical weight-blob order of the C-ABI (include/bt.h).
     """
     V, D, F, P = cfg.vocab, cfg.d_model, cfg.d_mlp, cfg.prefix_len
+    QKV = D + 2 * cfg.kv_heads * cfg.d_head
     specs: List[Tuple[str, Tuple[int, ...], str]] = [("emb_block", (V, cfg.d_emb), "normal")]
     for l in range(cfg.n_block_layers):
-        specs += _layer_specs(f"blk.{l}", D, F)
+        specs += _layer_specs(f"blk.{l}", D, F, QKV)
     specs += [("blk.lnf.g", (D,), "ln_gain"), ("blk.lnf.b", (D,), "ln_bias")]
     if cfg.n_token_layers == 0:
         # token-level (vanilla) transformer: no prefix, no token decoder
@@ -147,7 +155,7 @@ def weight_specs(cfg: Config) -> List[Tuple[str, Tuple[int, ...], str]]:
     specs += [("prefix.w", (D, P * D), "normal"), ("prefix.b", (P * D,), "normal"),
               ("emb_token", (V, D), "normal")]
     for l in range(cfg.n_token_layers):
-        specs += _layer_specs(f"tok.{l}", D, F)
+        specs += _layer_specs(f"tok.{l}", D, F, QKV)
     specs += [("tok.lnf.g", (D,), "ln_gain"), ("tok.lnf.b", (D,), "ln_bias"),
               ("head.w", (V, D), "normal")]
     return specs

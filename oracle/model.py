@@ -138,21 +138,26 @@ class LayerCache:
 
 
 def layer_forward(W: Weights, name: str, h: np.ndarray, pos: np.ndarray, n_heads: int,
-                  eps: float, base: float, cache: Optional[LayerCache] = None) -> np.ndarray:
+                  eps: float, base: float, cache: Optional[LayerCache] = None,
+                  n_kv_heads: int = 0) -> np.ndarray:
     """h + Attn(LN1 h) + MLP(LN2 h) for h [B, n, D] at positions pos [n].
 
     With a cache, the new keys/values are appended first and the queries attend
     over everything cached (earlier positions plus the causal part of the new ones).
+    With n_kv_heads < n_heads (grouped-query attention) the projection has n_kv_heads key and
+    value heads, and query head i uses key/value head i // (n_heads / n_kv_heads); the cache
+    holds the n_kv_heads heads.
     """
     B, n, D = h.shape
     dh = D // n_heads
+    hkv = n_kv_heads or n_heads
     a = layer_norm(h, W[f"{name}.ln1.g"], W[f"{name}.ln1.b"], eps)
     m = layer_norm(h, W[f"{name}.ln2.g"], W[f"{name}.ln2.b"], eps)
 
     qkv = a @ W[f"{name}.attn.qkv.w"] + W[f"{name}.attn.qkv.b"]
-    q = qkv[..., 0 * D:1 * D].reshape(B, n, n_heads, dh)
-    k = qkv[..., 1 * D:2 * D].reshape(B, n, n_heads, dh)
-    v = qkv[..., 2 * D:3 * D].reshape(B, n, n_heads, dh)
+    q = qkv[..., :D].reshape(B, n, n_heads, dh)
+    k = qkv[..., D:D + hkv * dh].reshape(B, n, hkv, dh)
+    v = qkv[..., D + hkv * dh:D + 2 * hkv * dh].reshape(B, n, hkv, dh)
     q = apply_rope(q, pos, base)
     k = apply_rope(k, pos, base)
     if cache is not None:
@@ -160,6 +165,9 @@ def layer_forward(W: Weights, name: str, h: np.ndarray, pos: np.ndarray, n_heads
         k_all, v_all, k_pos = cache.k, cache.v, cache.pos
     else:
         k_all, v_all, k_pos = k, v, np.asarray(pos)
+    group = n_heads // hkv
+    k_all = np.repeat(k_all, group, axis=2)   # head i -> key/value head i // group
+    v_all = np.repeat(v_all, group, axis=2)
     o = causal_attention(q, k_all, v_all, np.asarray(pos), k_pos).reshape(B, n, D)
     attn = o @ W[f"{name}.attn.out.w"] + W[f"{name}.attn.out.b"]
 
@@ -170,11 +178,11 @@ def layer_forward(W: Weights, name: str, h: np.ndarray, pos: np.ndarray, n_heads
 
 def stack_forward(W: Weights, prefix: str, n_layers: int, h: np.ndarray, pos: np.ndarray,
                   n_heads: int, eps: float, base: float,
-                  caches: Optional[List[LayerCache]] = None) -> np.ndarray:
+                  caches: Optional[List[LayerCache]] = None, n_kv_heads: int = 0) -> np.ndarray:
     """Run n_layers layers named ``{prefix}.{l}`` and the final LayerNorm ``{prefix}.lnf``."""
     for l in range(n_layers):
         h = layer_forward(W, f"{prefix}.{l}", h, pos, n_heads, eps, base,
-                          None if caches is None else caches[l])
+                          None if caches is None else caches[l], n_kv_heads)
     return layer_norm(h, W[f"{prefix}.lnf.g"], W[f"{prefix}.lnf.b"], eps)
 
 
@@ -207,7 +215,7 @@ def block_decoder(W: Weights, cfg, e: np.ndarray, first_pos: int = 0,
     """Block decoder: causal transformer over block embeddings -> context embeddings c."""
     pos = np.arange(first_pos, first_pos + e.shape[1])
     return stack_forward(W, "blk", cfg.n_block_layers, e, pos, cfg.n_heads,
-                         cfg.ln_eps, cfg.rope_base, caches)
+                         cfg.ln_eps, cfg.rope_base, caches, getattr(cfg, "n_kv_heads", 0))
 
 
 def prefix_from_context(W: Weights, cfg, c: np.ndarray) -> np.ndarray:
@@ -221,7 +229,7 @@ def token_decoder(W: Weights, cfg, z: np.ndarray, first_pos: int = 0,
     """Token decoder over the local sequence z [B, m, D] at local slots first_pos.. -> LN_f output."""
     pos = np.arange(first_pos, first_pos + z.shape[1])
     return stack_forward(W, "tok", cfg.n_token_layers, z, pos, cfg.n_heads,
-                         cfg.ln_eps, cfg.rope_base, caches)
+                         cfg.ln_eps, cfg.rope_base, caches, getattr(cfg, "n_kv_heads", 0))
 
 
 def output_logits(W: Weights, y: np.ndarray) -> np.ndarray:

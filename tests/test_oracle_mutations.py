@@ -51,18 +51,43 @@ def attn_scale_slip(q, k, v, q_pos, k_pos):
     return _orig["causal_attention"](q / np.sqrt(q.shape[-1]), k, v, q_pos, k_pos)
 
 
-def layer_sequential(W, name, h, pos, n_heads, eps, base, cache=None):
+def layer_sequential(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0):
     # sequential residual: the MLP sees h + attn instead of h
     zero = {k: (np.zeros_like(v) if k.startswith(name + ".mlp") else v) for k, v in W.items()}
-    h1 = _orig["layer_forward"](zero, name, h, pos, n_heads, eps, base, cache)
+    h1 = _orig["layer_forward"](zero, name, h, pos, n_heads, eps, base, cache, n_kv_heads)
     zero_attn = {k: (np.zeros_like(v) if k.startswith(name + ".attn") else v) for k, v in W.items()}
-    return _orig["layer_forward"](zero_attn, name, h1, pos, n_heads, eps, base, None)
+    return _orig["layer_forward"](zero_attn, name, h1, pos, n_heads, eps, base, None, n_kv_heads)
 
 
-def layer_no_qkv_bias(W, name, h, pos, n_heads, eps, base, cache=None):
+def layer_no_qkv_bias(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0):
     W2 = dict(W)
     W2[f"{name}.attn.qkv.b"] = np.zeros_like(W[f"{name}.attn.qkv.b"])
-    return _orig["layer_forward"](W2, name, h, pos, n_heads, eps, base, cache)
+    return _orig["layer_forward"](W2, name, h, pos, n_heads, eps, base, cache, n_kv_heads)
+
+
+def layer_gqa_interleaved(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0):
+    # grouped-query slip: query head i uses key/value head i mod n_kv_heads instead of i // group
+    hkv = n_kv_heads or n_heads
+    if hkv == n_heads:
+        return _orig["layer_forward"](W, name, h, pos, n_heads, eps, base, cache, n_kv_heads)
+    B, n, D = h.shape
+    dh = D // n_heads
+    a = om.layer_norm(h, W[f"{name}.ln1.g"], W[f"{name}.ln1.b"], eps)
+    m = om.layer_norm(h, W[f"{name}.ln2.g"], W[f"{name}.ln2.b"], eps)
+    qkv = a @ W[f"{name}.attn.qkv.w"] + W[f"{name}.attn.qkv.b"]
+    q = om.apply_rope(qkv[..., :D].reshape(B, n, n_heads, dh), pos, base)
+    k = om.apply_rope(qkv[..., D:D + hkv * dh].reshape(B, n, hkv, dh), pos, base)
+    v = qkv[..., D + hkv * dh:].reshape(B, n, hkv, dh)
+    if cache is not None:
+        cache.append(k, v, pos)
+        k, v, k_pos = cache.k, cache.v, cache.pos
+    else:
+        k_pos = np.asarray(pos)
+    g = n_heads // hkv
+    o = om.causal_attention(q, np.tile(k, (1, 1, g, 1)), np.tile(v, (1, 1, g, 1)), np.asarray(pos), k_pos)
+    attn = o.reshape(B, n, D) @ W[f"{name}.attn.out.w"] + W[f"{name}.attn.out.b"]
+    mlp = om.gelu(m @ W[f"{name}.mlp.up.w"] + W[f"{name}.mlp.up.b"]) @ W[f"{name}.mlp.down.w"] + W[f"{name}.mlp.down.b"]
+    return h + attn + mlp
 
 
 def embed_reversed(W, cfg, tokens):
@@ -77,13 +102,13 @@ def prefix_transposed(W, cfg, c):
     return u.reshape(c.shape[0], cfg.d_model, cfg.prefix_len).transpose(0, 2, 1)
 
 
-def stack_no_final_ln(W, prefix, n_layers, h, pos, n_heads, eps, base, caches=None):
+def stack_no_final_ln(W, prefix, n_layers, h, pos, n_heads, eps, base, caches=None, n_kv_heads=0):
     # the token decoder's output skips its final LayerNorm
     if prefix != "tok":
-        return _orig["stack_forward"](W, prefix, n_layers, h, pos, n_heads, eps, base, caches)
+        return _orig["stack_forward"](W, prefix, n_layers, h, pos, n_heads, eps, base, caches, n_kv_heads)
     for l in range(n_layers):
         h = om.layer_forward(W, f"{prefix}.{l}", h, pos, n_heads, eps, base,
-                             None if caches is None else caches[l])
+                             None if caches is None else caches[l], n_kv_heads)
     return h
 
 
@@ -129,6 +154,7 @@ MUTATIONS = {
     "token_decoder_final_ln_dropped": ("stack_forward", stack_no_final_ln),
     "context_of_own_block": ("logits_at", logits_own_context),
     "logit_slot_off_by_one": ("logits_at", logits_slot_slip),
+    "gqa_heads_interleaved": ("layer_forward", layer_gqa_interleaved),
 }
 
 PIN_CALLS = [
@@ -143,6 +169,7 @@ PIN_CALLS = [
     lambda: pins.test_matches_library_crosscheck(dict(block_len=2, prefix_len=2)),
     lambda: pins.test_incremental_equals_full_recompute(dict(), 30, 13),
     pins.test_causality_bitwise,
+    lambda: pins.test_grouped_query_attention_matches_library_and_incremental(2),
 ]
 
 

@@ -277,6 +277,37 @@ def test_float32_oracle_stays_float32():
     assert om.gelu(np.ones(3, np.float32)).dtype == np.float32
 
 
+@pytest.mark.parametrize("kv", [1, 2])
+def test_grouped_query_attention_matches_library_and_incremental(kv):
+    """n_kv_heads < n_heads: query head i attends with key/value head i // (H / n_kv_heads) (torch's
+    grouped-query option of scaled_dot_product_attention); n_kv_heads = 1 is multi-query attention.
+    Also pinned: the caches hold n_kv_heads heads, and the incremental path equals full recompute."""
+    cfg = tiny(n_heads=4, n_kv_heads=kv, d_model=64)
+    W = w64(cfg)
+    assert W["blk.0.attn.qkv.w"].shape == (64, 64 + 2 * kv * 16)
+    x = np.random.default_rng(12).integers(0, cfg.vocab, (2, 4 * cfg.block_len))
+    for k in (1, 2, 3):
+        np.testing.assert_allclose(om.logits_at(W, cfg, x, range(k * cfg.block_len, (k + 1) * cfg.block_len)),
+                                   tc.block_logits(W, cfg, x, k), atol=1e-11)
+    prompt = wl.make_prompt(cfg, batch=2, T=9)
+    ids, lg, st = om.generate(W, cfg, prompt, 9, keep_logits=True)
+    Tp = wl.padded_len(cfg, 9)
+    seq = np.concatenate([om.pad_prompt(cfg, prompt), ids], axis=1)
+    full = om.logits_at(W, cfg, seq, range(Tp, Tp + 9))
+    assert np.abs(full - lg).max() <= 1e-10
+    assert st.block_caches[0].k.shape[2] == kv and st.local_caches[0].k.shape[2] == kv
+
+
+def test_grouped_query_with_full_groups_is_multi_head():
+    """n_kv_heads = n_heads is ordinary multi-head attention: same weights, same logits."""
+    cfg = tiny()
+    W = w64(cfg)
+    x = np.random.default_rng(13).integers(0, cfg.vocab, (2, 3 * cfg.block_len))
+    a = om.logits_at(W, cfg, x, range(cfg.block_len, 3 * cfg.block_len))
+    b = om.logits_at(W, cfg.with_(n_kv_heads=cfg.n_heads), x, range(cfg.block_len, 3 * cfg.block_len))
+    assert np.array_equal(a, b)
+
+
 def test_vanilla_mode_matches_library_and_incremental():
     """n_token_layers = 0, L_B = 1: a standard token-level decoder (the pages' Pythia baselines)."""
     cfg = tiny(n_token_layers=0, block_len=1, n_block_layers=3)

@@ -28,17 +28,19 @@ def rope_complex(x: torch.Tensor, pos: torch.Tensor, base: float) -> torch.Tenso
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def layer(W, name, h, pos, n_heads, eps, base):
+def layer(W, name, h, pos, n_heads, eps, base, n_kv_heads=0):
     B, n, D = h.shape
     dh = D // n_heads
+    hkv = n_kv_heads or n_heads
     a = F.layer_norm(h, (D,), _t(W[f"{name}.ln1.g"]), _t(W[f"{name}.ln1.b"]), eps)
     m = F.layer_norm(h, (D,), _t(W[f"{name}.ln2.g"]), _t(W[f"{name}.ln2.b"]), eps)
     qkv = F.linear(a, _t(W[f"{name}.attn.qkv.w"]).T, _t(W[f"{name}.attn.qkv.b"]))
-    q, k, v = qkv.split(D, dim=-1)
-    heads = lambda t: t.reshape(B, n, n_heads, dh).transpose(1, 2)   # noqa: E731
-    q, k, v = heads(q), heads(k), heads(v)
+    q, k, v = qkv.split([D, hkv * dh, hkv * dh], dim=-1)
+    heads = lambda t, nh: t.reshape(B, n, nh, dh).transpose(1, 2)   # noqa: E731
+    q, k, v = heads(q, n_heads), heads(k, hkv), heads(v, hkv)
     q, k = rope_complex(q, pos, base), rope_complex(k, pos, base)
-    o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+    # grouped-query attention through the library's own option (query heads share key/value heads)
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=hkv != n_heads)
     o = o.transpose(1, 2).reshape(B, n, D)
     attn = F.linear(o, _t(W[f"{name}.attn.out.w"]).T, _t(W[f"{name}.attn.out.b"]))
     u = F.gelu(F.linear(m, _t(W[f"{name}.mlp.up.w"]).T, _t(W[f"{name}.mlp.up.b"])), approximate="none")
@@ -49,7 +51,7 @@ def layer(W, name, h, pos, n_heads, eps, base):
 def stack(W, pre, n_layers, h, cfg):
     pos = torch.arange(h.shape[1])
     for l in range(n_layers):
-        h = layer(W, f"{pre}.{l}", h, pos, cfg.n_heads, cfg.ln_eps, cfg.rope_base)
+        h = layer(W, f"{pre}.{l}", h, pos, cfg.n_heads, cfg.ln_eps, cfg.rope_base, getattr(cfg, "n_kv_heads", 0))
     return F.layer_norm(h, (cfg.d_model,), _t(W[f"{pre}.lnf.g"]), _t(W[f"{pre}.lnf.b"]), cfg.ln_eps)
 
 
