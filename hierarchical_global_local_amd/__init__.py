@@ -36,7 +36,8 @@ class BtConfig(ctypes.Structure):
                 ("d_mlp", ctypes.c_int32), ("n_block_layers", ctypes.c_int32), ("n_token_layers", ctypes.c_int32),
                 ("block_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32), ("pad_id", ctypes.c_int32),
-                ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("max_prompt_tokens", ctypes.c_int32)]
+                ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("max_prompt_tokens", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32)]
 
     @classmethod
     def make(cls, model, max_batch: int, max_tokens: int, max_prompt_tokens: int = 0) -> "BtConfig":
@@ -44,7 +45,7 @@ class BtConfig(ctypes.Structure):
         return cls(model.vocab, model.d_model, model.n_heads, model.d_mlp, model.n_block_layers,
                    model.n_token_layers, model.block_len, model.prefix_len, max_batch, max_tokens,
                    BT_FP32 if model.dtype == "fp32" else BT_BF16, model.pad_id, model.ln_eps, model.rope_base,
-                   max_prompt_tokens)
+                   max_prompt_tokens, getattr(model, "n_kv_heads", 0))
 
 
 _lib = None

@@ -54,13 +54,17 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   if (nblk > 131072) return "max_tokens / block_len must be <= 131072";
   if (c.max_prompt_tokens < 0 || c.max_prompt_tokens > c.max_tokens)
     return "max_prompt_tokens must be in [0, max_tokens]";
+  if (c.n_kv_heads < 0 || c.n_kv_heads > c.n_heads || (c.n_kv_heads > 0 && c.n_heads % c.n_kv_heads))
+    return "n_kv_heads must be 0 or a divisor of n_heads";
   const int max_prompt = c.max_prompt_tokens > 0 ? c.max_prompt_tokens : c.max_tokens;
   const int nblk_prompt = std::max(1, (max_prompt + c.block_len - 1) / c.block_len);
 
   lo.V = c.vocab;
   lo.D = c.d_model;
   lo.H = c.n_heads;
+  lo.Hkv = c.n_kv_heads > 0 ? c.n_kv_heads : c.n_heads;
   lo.dh = dh;
+  lo.QW = lo.D + 2 * lo.Hkv * dh;
   lo.F = c.d_mlp;
   lo.L = c.block_len;
   lo.P = c.prefix_len;
@@ -81,14 +85,14 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.Mmax = std::max<int64_t>((int64_t)lo.Bmax * nblk_prompt, (int64_t)lo.Bmax * lo.P);
   lo.Mpad = (int64_t)align_up((size_t)lo.Mmax, 16);
 
-  const size_t D = lo.D, F = lo.F, V = lo.V, P = lo.P, E = lo.elem, TE = lo.tab_elem;
+  const size_t D = lo.D, F = lo.F, V = lo.V, P = lo.P, E = lo.elem, TE = lo.tab_elem, QW = lo.QW;
   // ---- canonical blob
   size_t o = 0;
   auto take = [&](size_t n) { size_t r = o; o += n * TE; return r; };
   lo.bl_emb_block = take(V * lo.De);
   auto blob_layer = [&]() {
     Layout::BlobLayer b;
-    b.ln1g = take(D); b.ln1b = take(D); b.qkvw = take(D * 3 * D); b.qkvb = take(3 * D);
+    b.ln1g = take(D); b.ln1b = take(D); b.qkvw = take(D * QW); b.qkvb = take(QW);
     b.outw = take(D * D); b.outb = take(D); b.ln2g = take(D); b.ln2b = take(D);
     b.upw = take(D * F); b.upb = take(F); b.downw = take(F * D); b.downb = take(D);
     return b;
@@ -124,8 +128,8 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   auto layer = [&]() {
     LayerOff L;
     L.ln = region(4 * D * 4);
-    L.w1 = region((3 * D + F) * D * E);
-    L.b1 = region((3 * D + F) * 4);
+    L.w1 = region((QW + F) * D * E);
+    L.b1 = region((QW + F) * 4);
     L.w2 = region(D * (D + F) * E);
     L.b2 = region(2 * D * 4);
     return L;
@@ -134,14 +138,14 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.tok.clear();
   for (int l = 0; l < lo.Nb; ++l) lo.blk.push_back(layer());
   for (int l = 0; l < lo.Nt; ++l) lo.tok.push_back(layer());
-  lo.block_kv_bytes = (size_t)lo.Nb * 2 * lo.Bmax * lo.H * lo.ncap * lo.dh * E;
-  lo.local_kv_bytes = (size_t)lo.Nt * 2 * lo.Bmax * lo.H * lo.lcap * lo.dh * E;  // 0 for Nt = 0
+  lo.block_kv_bytes = (size_t)lo.Nb * 2 * lo.Bmax * lo.Hkv * lo.ncap * lo.dh * E;
+  lo.local_kv_bytes = (size_t)lo.Nt * 2 * lo.Bmax * lo.Hkv * lo.lcap * lo.dh * E;  // 0 for Nt = 0
   lo.block_kv = region(lo.block_kv_bytes);
   lo.local_kv = region(lo.local_kv_bytes);
   const size_t M = (size_t)lo.Mmax;
   lo.X = region(M * D * 4);
   lo.LN = region(2 * (size_t)lo.Mpad * D * E);
-  lo.QKV = region(M * 3 * D * E);
+  lo.QKV = region(M * QW * E);
   lo.ACT = region((size_t)lo.Mpad * (D + F) * E);
   lo.part_bytes = (size_t)lo.Bmax * lo.H * 32 * (lo.dh + 2) * 4;
   lo.part = region(lo.part_bytes);
@@ -232,22 +236,22 @@ int hip_fail(bt_handle* h, hipError_t e, const char* what) {
 
 void* block_k(bt_handle* h, int l) {
   const Layout& lo = h->lo;
-  size_t per = (size_t)lo.Bmax * lo.H * lo.ncap * lo.dh * lo.elem;
+  size_t per = (size_t)lo.Bmax * lo.Hkv * lo.ncap * lo.dh * lo.elem;
   return P_(h, lo.block_kv + (size_t)(2 * l) * per);
 }
 void* block_v(bt_handle* h, int l) {
   const Layout& lo = h->lo;
-  size_t per = (size_t)lo.Bmax * lo.H * lo.ncap * lo.dh * lo.elem;
+  size_t per = (size_t)lo.Bmax * lo.Hkv * lo.ncap * lo.dh * lo.elem;
   return P_(h, lo.block_kv + (size_t)(2 * l + 1) * per);
 }
 void* local_k(bt_handle* h, int l) {
   const Layout& lo = h->lo;
-  size_t per = (size_t)lo.Bmax * lo.H * lo.lcap * lo.dh * lo.elem;
+  size_t per = (size_t)lo.Bmax * lo.Hkv * lo.lcap * lo.dh * lo.elem;
   return P_(h, lo.local_kv + (size_t)(2 * l) * per);
 }
 void* local_v(bt_handle* h, int l) {
   const Layout& lo = h->lo;
-  size_t per = (size_t)lo.Bmax * lo.H * lo.lcap * lo.dh * lo.elem;
+  size_t per = (size_t)lo.Bmax * lo.Hkv * lo.lcap * lo.dh * lo.elem;
   return P_(h, lo.local_kv + (size_t)(2 * l + 1) * per);
 }
 void* ln_buf(bt_handle* h, int which) {
@@ -266,10 +270,10 @@ Epi qkv_epi(bt_handle* h, const LayerOff& w) {
   ep.wscale = wscale(lo);
   ep.bias = (const float*)P_(h, w.b1);
   ep.out0 = P_(h, lo.QKV);
-  ep.ld0 = 3 * lo.D;
+  ep.ld0 = lo.QW;
   ep.out1 = P_(h, lo.ACT);
   ep.ld1 = lo.D + lo.F;
-  ep.n_split = 3 * lo.D;
+  ep.n_split = lo.QW;
   ep.act_col0 = lo.D;
   return ep;
 }
@@ -279,7 +283,7 @@ Epi qkv_epi(bt_handle* h, const LayerOff& w) {
 int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows, bool ln_done = false) {
   const Layout& lo = h->lo;
   const float* lnp = (const float*)P_(h, w.ln);
-  const double E = (double)lo.elem, D = lo.D, N1 = 3.0 * lo.D + lo.F;
+  const double E = (double)lo.elem, D = lo.D, N1 = (double)lo.QW + lo.F;
   if (!ln_done) {
     Prof p(h, PK_LN, rows * D * (4.0 + 2.0 * E), 8.0 * rows * D);
     BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), rows, lo.D, 1, 0, lnp, ln_buf(h, 0), lnp + 2 * lo.D,
@@ -289,7 +293,7 @@ int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows, bool ln_done = false) 
   }
   const Epi ep = qkv_epi(h, w);
   Prof p(h, PK_GEMM_QKV, N1 * D * E + 2.0 * rows * D * E + rows * N1 * E + N1 * 4.0, 2.0 * rows * N1 * D);
-  BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), rows, 3 * lo.D + lo.F, lo.D,
+  BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), rows, lo.QW + lo.F, lo.D,
                           EPI_QKV_GELU, ep, h->st),
            "gemm qkv|up");
   return BT_OK;
@@ -330,12 +334,13 @@ int run_token_decoder(bt_handle* h, int m, int s0, bool first_ln_done = false) {
     int r = run_ln_qkv(h, lo.tok[l], rows, l == 0 && first_ln_done);
     if (r) return r;
     {
-      const double E = (double)lo.elem, D = lo.D, Bd = h->B;
+      const double E = (double)lo.elem, D = lo.D, Bd = h->B, KVW = (double)lo.Hkv * lo.dh;
       double pairs = 0;
       for (int i = 0; i < m; ++i) pairs += s0 + i + 1;
-      Prof p(h, PK_ATTN_LOCAL, Bd * s0 * 2.0 * D * E + rows * 3.0 * D * E + rows * 3.0 * D * E,
+      // cached K/V read, q|k|v read, new K/V and the output written
+      Prof p(h, PK_ATTN_LOCAL, (Bd * s0 * 2.0 * KVW + 2.0 * rows * (D + 2.0 * KVW)) * E,
              4.0 * Bd * lo.H * lo.dh * pairs);
-      BT_CHECK(h, launch_local_attention(lo.f32, P_(h, lo.QKV), h->B, m, s0, lo.D, lo.H, lo.dh,
+      BT_CHECK(h, launch_local_attention(lo.f32, P_(h, lo.QKV), h->B, m, s0, lo.H, lo.Hkv, lo.dh,
                                          (const float2*)P_(h, lo.rope), local_k(h, l), local_v(h, l), lo.lcap,
                                          P_(h, lo.ACT), lo.D + lo.F, h->st),
                "local attention");
@@ -448,7 +453,7 @@ void advance_host_state(bt_handle* h, int j) {
 int enqueue_decode(bt_handle* h, int j, float* d_logits) {
   const Layout& lo = h->lo;
   const int L = lo.L, P = lo.P;
-  const double E = (double)lo.elem, Dd = lo.D, Bd = h->B;
+  const double E = (double)lo.elem, Dd = lo.D, Bd = h->B, KVW = (double)lo.Hkv * lo.dh;
   int r;
   if (j == 0) {
     // the previous L_B emitted tokens complete a block: one block-decoder step (its input block
@@ -457,11 +462,12 @@ int enqueue_decode(bt_handle* h, int j, float* d_logits) {
     for (int l = 0; l < lo.Nb; ++l) {
       if ((r = run_ln_qkv(h, lo.blk[l], h->B, l == 0))) return r;
       {
-        // keys and values of entries [0, n) read once, the new entry written, q read, output written
-        Prof p(h, PK_ATTN_DECODE, Bd * lo.H * (double)n * lo.dh * 2.0 * E + Bd * Dd * E * 6.0,
+        // keys and values of entries [0, n) read once per KV head, q|k|v read, the new entry and
+        // the output written
+        Prof p(h, PK_ATTN_DECODE, Bd * (double)n * KVW * 2.0 * E + Bd * (2.0 * Dd + 4.0 * KVW) * E,
                4.0 * Bd * lo.H * lo.dh * (double)(n + 1));
-        BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.D, lo.H,
-                                             lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l),
+        BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,
+                                             lo.Hkv, lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l),
                                              lo.ncap, P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part),
                                              lo.part_bytes, h->dec_nsplit, h->st),
                  "block attention decode");
@@ -546,7 +552,7 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
   const bool bf = !lo.f32;
   const bool f32 = lo.f32;
   const float sc = f32 ? 1.0f : kWeightScale;
-  const int D = lo.D, F = lo.F;
+  const int D = lo.D, F = lo.F, QW = lo.QW;
   auto fin = [&](hipError_t err, const char* what) -> int {
     if (err == hipSuccess) return 0;
     delete h;
@@ -574,16 +580,15 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     if ((err = launch_to_f32(wb + s.ln2b, bf, D, ln + 3 * D, h->st))) return err;
     // canonical [in, out] matrices: element (n = out, k = in) at src[k * out + n]
     if (f32) {
-      if ((err = launch_transpose_convert(wb + s.qkvw, bf, D, 3 * D, h->ws + d.w1, f32, D, 0, 0, sc, h->st))) return err;
-      if ((err = launch_transpose_convert(wb + s.upw, bf, D, F, h->ws + d.w1, f32, D, 3 * D, 0, sc, h->st))) return err;
+      if ((err = launch_transpose_convert(wb + s.qkvw, bf, D, QW, h->ws + d.w1, f32, D, 0, 0, sc, h->st))) return err;
+      if ((err = launch_transpose_convert(wb + s.upw, bf, D, F, h->ws + d.w1, f32, D, QW, 0, sc, h->st))) return err;
     } else {
-      if ((err = launch_pack_frag(wb + s.qkvw, bf, 1, 3 * D, 3 * D, 3 * D, D, h->ws + d.w1, D, 0, 0, sc, h->st)))
-        return err;
-      if ((err = launch_pack_frag(wb + s.upw, bf, 1, F, F, F, D, h->ws + d.w1, D, 3 * D, 0, sc, h->st))) return err;
+      if ((err = launch_pack_frag(wb + s.qkvw, bf, 1, QW, QW, QW, D, h->ws + d.w1, D, 0, 0, sc, h->st))) return err;
+      if ((err = launch_pack_frag(wb + s.upw, bf, 1, F, F, F, D, h->ws + d.w1, D, QW, 0, sc, h->st))) return err;
     }
     float* b1 = (float*)(h->ws + d.b1);
-    if ((err = launch_to_f32(wb + s.qkvb, bf, 3 * D, b1, h->st))) return err;
-    if ((err = launch_to_f32(wb + s.upb, bf, F, b1 + 3 * D, h->st))) return err;
+    if ((err = launch_to_f32(wb + s.qkvb, bf, QW, b1, h->st))) return err;
+    if ((err = launch_to_f32(wb + s.upb, bf, F, b1 + QW, h->st))) return err;
     if (f32) {
       if ((err = launch_transpose_convert(wb + s.outw, bf, D, D, h->ws + d.w2, f32, D + F, 0, 0, sc, h->st)))
         return err;
@@ -661,11 +666,11 @@ static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_
   h->B = B;
   h->Tp = Tp;
   h->pending.nsplit = 0;
-  h->dec_nsplit = decode_splits(B, lo.H, lo.ncap);
+  h->dec_nsplit = decode_splits(B, lo.H, lo.Hkv, lo.ncap);
   const int n0 = Tp / L;
   const int M = B * n0;
   h->decode_phase = false;
-  const double E = (double)lo.elem, Dd = lo.D, Md = M;
+  const double E = (double)lo.elem, Dd = lo.D, Md = M, KVW = (double)lo.Hkv * lo.dh;
   {
     Prof p(h, PK_EMBED, Md * Dd * (lo.tab_elem + 4.0) + (double)B * T * 4.0, 0.0);
     BT_CHECK(h, launch_embed_prompt(d_prompt, d_lengths, B, T, Tp, h->cfg.pad_id, P_(h, lo.emb_block), !lo.f32, lo.V,
@@ -676,15 +681,16 @@ static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_
     int r = run_ln_qkv(h, lo.blk[l], M);
     if (r) return r;
     {
-      Prof p(h, PK_ROPE_SCATTER, Md * 4.0 * Dd * E, 6.0 * Md * Dd);
-      BT_CHECK(h, launch_rope_scatter(lo.f32, P_(h, lo.QKV), B, n0, 0, lo.D, lo.H, lo.dh, (const float2*)P_(h, lo.rope),
-                                      block_k(h, l), block_v(h, l), lo.ncap, true, h->st),
+      Prof p(h, PK_ROPE_SCATTER, Md * 4.0 * KVW * E, 3.0 * Md * KVW);
+      BT_CHECK(h, launch_rope_scatter(lo.f32, P_(h, lo.QKV), B, n0, 0, lo.H, lo.Hkv, lo.dh,
+                                      (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap, true,
+                                      h->st),
                "rope scatter");
     }
     {
-      Prof p(h, PK_ATTN_PREFILL, Md * Dd * E * 4.0,
+      Prof p(h, PK_ATTN_PREFILL, Md * (2.0 * Dd + 2.0 * KVW) * E,
              4.0 * B * lo.H * lo.dh * (double)n0 * (n0 + 1) / 2.0);
-      BT_CHECK(h, launch_prefill_attention(lo.f32, P_(h, lo.QKV), B, n0, lo.D, lo.H, lo.dh,
+      BT_CHECK(h, launch_prefill_attention(lo.f32, P_(h, lo.QKV), B, n0, lo.H, lo.Hkv, lo.dh,
                                            (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
                                            P_(h, lo.ACT), lo.D + lo.F, h->st),
                "prefill attention");
@@ -826,14 +832,14 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
       const int nl = lo.Nb + lo.Nt, l = i % nl;
       const LayerOff& w = l < lo.Nt ? lo.tok[l] : lo.blk[l - lo.Nt];
       const Epi ep = qkv_epi(h, w);
-      hipError_t e = launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), h->B, 3 * lo.D + lo.F, lo.D,
+      hipError_t e = launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), h->B, lo.QW + lo.F, lo.D,
                                  EPI_QKV_GELU, ep, h->st);
       if (e != hipSuccess) r = hip_fail(h, e, "replay gemm");
     } else if (kind == PK_ATTN_DECODE) {
       const int l = i % lo.Nb;
-      hipError_t e = launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.D, lo.H,
-                                              lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l),
-                                              lo.ncap, P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part),
+      hipError_t e = launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,
+                                              lo.Hkv, lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l),
+                                              block_v(h, l), lo.ncap, P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part),
                                               lo.part_bytes, h->dec_nsplit, h->st);
       if (e != hipSuccess) r = hip_fail(h, e, "replay attention");
     } else {

@@ -48,19 +48,20 @@ template <typename T>
 __device__ __forceinline__ T round_t(float v) { return from_f32<T>(v); }
 
 // ---------------------------------------------------------------- rotary + scatter (prefill)
-// grid (ceil(m/64), H, B); rows (b, i) of QKV [B*m][3D] go to cache slot s0 + i.
+// grid (ceil(m/64), Hkv, B); KV head hk of rows (b, i) of QKV [B*m][QW] goes to cache slot s0 + i.
 template <typename T>
-__global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV, int m, int s0, int D, int H, int dh,
+__global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV, int m, int s0, int H, int Hkv, int dh,
                                                       const float2* __restrict__ rope, T* __restrict__ Kc,
                                                       T* __restrict__ Vc, int cap, int vt) {
   __shared__ T vtile[64][129];
-  const int h = blockIdx.y, b = blockIdx.z, i0 = blockIdx.x * 64;
+  const int hk = blockIdx.y, b = blockIdx.z, i0 = blockIdx.x * 64;
   const int half = dh / 2, tid = threadIdx.x;
-  const size_t bh = (size_t)b * H + h;
+  const size_t qw = (size_t)(H + 2 * Hkv) * dh, koff = (size_t)(H + hk) * dh, voff = (size_t)(H + Hkv + hk) * dh;
+  const size_t bh = (size_t)b * Hkv + hk;
   const int cnt = min(64, m - i0);
   for (int e = tid; e < cnt * half; e += 256) {
     const int si = e / half, c = e % half, i = i0 + si, slot = s0 + i;
-    const T* kr = QKV + ((size_t)b * m + i) * 3 * D + D + h * dh;
+    const T* kr = QKV + ((size_t)b * m + i) * qw + koff;
     const float2 cs = rope[(size_t)slot * half + c];
     const float x1 = (float)kr[c], x2 = (float)kr[c + half];
     T* kd = Kc + (bh * cap + slot) * dh;
@@ -70,13 +71,13 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV,
   if (!vt) {
     for (int e = tid; e < cnt * dh; e += 256) {
       const int si = e / dh, d = e % dh, i = i0 + si;
-      Vc[(bh * cap + s0 + i) * dh + d] = QKV[((size_t)b * m + i) * 3 * D + 2 * D + h * dh + d];
+      Vc[(bh * cap + s0 + i) * dh + d] = QKV[((size_t)b * m + i) * qw + voff + d];
     }
     return;
   }
   for (int e = tid; e < cnt * dh; e += 256) {
     const int si = e / dh, d = e % dh;
-    vtile[si][d] = QKV[((size_t)b * m + i0 + si) * 3 * D + 2 * D + h * dh + d];
+    vtile[si][d] = QKV[((size_t)b * m + i0 + si) * qw + voff + d];
   }
   __syncthreads();
   for (int e = tid; e < cnt * dh; e += 256) {
@@ -85,28 +86,29 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV,
   }
 }
 
-hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
+hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed, hipStream_t st) {
   if (B <= 0 || m <= 0) return hipSuccess;
-  dim3 grid((m + 63) / 64, H, B);
+  if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  dim3 grid((m + 63) / 64, Hkv, B);
   if (f32)
-    hipLaunchKernelGGL(k_rope_scatter<float>, grid, dim3(256), 0, st, (const float*)QKV, m, s0, D, H, dh, rope,
+    hipLaunchKernelGGL(k_rope_scatter<float>, grid, dim3(256), 0, st, (const float*)QKV, m, s0, H, Hkv, dh, rope,
                        (float*)Kc, (float*)Vc, cap, (int)v_transposed);
   else
-    hipLaunchKernelGGL(k_rope_scatter<f16>, grid, dim3(256), 0, st, (const f16*)QKV, m, s0, D, H, dh, rope, (f16*)Kc,
-                       (f16*)Vc, cap, (int)v_transposed);
+    hipLaunchKernelGGL(k_rope_scatter<f16>, grid, dim3(256), 0, st, (const f16*)QKV, m, s0, H, Hkv, dh, rope,
+                       (f16*)Kc, (f16*)Vc, cap, (int)v_transposed);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- MFMA flash prefill (fp16)
-// grid (ceil(n/64), H, B), 4 waves x 16 queries.  Each 64-key tile of K ([key][dh]) and V^T
-// ([dh][key]) is loaded once per workgroup with coalesced 16-byte loads into a double-buffered
-// LDS stage (the next tile's loads are in flight while the current one is used) and read by all
-// four waves.  MFMA 16x16x32 layouts (lane l, g = l / 16):
+// grid (ceil(n/64), H, B), 4 waves x 16 queries; query head h reads KV head h / (H / Hkv).  Each
+// 64-key tile of K ([key][dh]) and V^T ([dh][key]) is loaded once per workgroup with coalesced
+// 16-byte loads into a double-buffered LDS stage (the next tile's loads are in flight while the
+// current one is used) and read by all four waves.  MFMA 16x16x32 layouts (lane l, g = l / 16):
 //   A operand: row l % 16, k = 8g..8g+7;  B operand: column l % 16, same k;
 //   result:    column l % 16, rows 4g..4g+3.
 template <int DH>
-__global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ QKV, int n, int D, int H,
+__global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ QKV, int n, int H, int Hkv,
                                                        const float2* __restrict__ rope, const f16* __restrict__ Kc,
                                                        const f16* __restrict__ VTc, int cap, f16* __restrict__ ACT,
                                                        int ld_act, float scale_log2) {
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
   const int q0 = qt * 64 + wave * 16;
   const int qi = q0 + c16;
   const int qrow = min(qi, n - 1);
-  const size_t bh = (size_t)b * H + h;
+  const size_t bh = (size_t)b * Hkv + h / (H / Hkv);
   const f16* __restrict__ K = Kc + bh * cap * DH;
   const f16* __restrict__ VT = VTc + bh * DH * cap;
 
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
   half8 qf[KS];
   {
     float x[KS][8];
-    const f16* qp = QKV + ((size_t)b * n + qrow) * 3 * D + h * DH;
+    const f16* qp = QKV + ((size_t)b * n + qrow) * (H + 2 * Hkv) * DH + h * DH;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) load8(qp + 32 * ks + 8 * g, x[ks]);
     const float2* rp = rope + (size_t)qrow * (DH / 2);
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
 // ---------------------------------------------------------------- plain prefill attention (fp32)
 // grid (n, H, B), one wave per query; scores staged in dynamic LDS.
 template <typename T>
-__global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, int n, int D, int H, int dh,
+__global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, int n, int H, int Hkv, int dh,
                                                    const float2* __restrict__ rope, const T* __restrict__ Kc,
                                                    const T* __restrict__ VTc, int cap, T* __restrict__ ACT,
                                                    int ld_act, float scale) {
@@ -277,8 +279,8 @@ __global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, in
   float* q = sm;          // [dh]
   float* sc = sm + 128;   // [n]
   const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  const size_t bh = (size_t)b * H + h;
-  const T* qp = QKV + ((size_t)b * n + qi) * 3 * D + h * dh;
+  const size_t bh = (size_t)b * Hkv + h / (H / Hkv);
+  const T* qp = QKV + ((size_t)b * n + qi) * (H + 2 * Hkv) * dh + h * dh;
   const int half = dh / 2;
   for (int c = lane; c < half; c += 64) {
     const float2 cs = rope[(size_t)qi * half + c];
@@ -312,23 +314,24 @@ __global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, in
   }
 }
 
-hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int D, int H, int dh,
+hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int H, int Hkv, int dh,
                                     const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
                                     int ld_act, hipStream_t st) {
   if (B <= 0 || n <= 0) return hipSuccess;
+  if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)dh);
   if (f32) {
     size_t lds = (128 + (size_t)n) * sizeof(float);
-    hipLaunchKernelGGL(k_attn_naive<float>, dim3(n, H, B), dim3(64), lds, st, (const float*)QKV, n, D, H, dh, rope,
+    hipLaunchKernelGGL(k_attn_naive<float>, dim3(n, H, B), dim3(64), lds, st, (const float*)QKV, n, H, Hkv, dh, rope,
                        (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale);
     return hipGetLastError();
   }
   dim3 grid((n + 63) / 64, H, B);
   if (dh == 64)
-    hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, (const f16*)QKV, n, D, H, rope, (const f16*)Kc,
+    hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
                        (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e);
   else if (dh == 128)
-    hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, (const f16*)QKV, n, D, H, rope, (const f16*)Kc,
+    hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
                        (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e);
   else
     return hipErrorInvalidValue;
@@ -336,63 +339,79 @@ hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int
 }
 
 // ---------------------------------------------------------------- block-attention decode
-// grid (nsplit, H, B), 256 threads.  Keys [0, n) come from the cache, key n is the new one
-// (rotated here, appended to the cache by split 0 and used from LDS by the split that owns it).
-constexpr int kMaxChunk = 4096;
+// grid (nsplit, Hkv * nsub, B), 256 threads.  A workgroup serves gsz <= GM query heads of one KV
+// head (the group of G = H / Hkv heads is cut into nsub runs of gsz), so that the KV head's keys
+// and values are streamed from HBM once for all of them.  Keys [0, n) come from the cache, key n
+// is the new one (rotated here, appended to the cache by split 0 of the group's first run, and
+// used from LDS by the split that owns it).
+constexpr int kMaxChunk = 4096;  // scores held in LDS per workgroup, over all its query heads
 constexpr int kMaxSplit = 32;
 
-template <typename T, int DH>
-__global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, const int* __restrict__ n_ptr, int D,
-                                                     int H, const float2* __restrict__ rope, T* __restrict__ Kc,
-                                                     T* __restrict__ VTc, int cap, T* __restrict__ ACT, int ld_act,
-                                                     float* __restrict__ part, int nsplit, int chunk,
-                                                     float scale_log2) {
+template <typename T, int DH, int GM>
+__global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, const int* __restrict__ n_ptr, int H,
+                                                     int Hkv, int gsz, const float2* __restrict__ rope,
+                                                     T* __restrict__ Kc, T* __restrict__ VTc, int cap,
+                                                     T* __restrict__ ACT, int ld_act, float* __restrict__ part,
+                                                     int nsplit, int chunk, float scale_log2) {
+  static_assert(GM >= 1 && GM <= 4, "one wave scores each head's new key");
   constexpr int LPK = DH / 8;      // lanes per key in the score pass (8 values each)
   constexpr int KPW = 64 / LPK;    // keys per wave per step
   constexpr int RPL = DH / 32;     // value rows per lane in the value pass
   constexpr int U = 8;             // key loads in flight per lane (score pass)
-  constexpr int UV = 4;            // value-chunk loads in flight per lane and row (value pass)
-  __shared__ float qs[DH], kn[DH], vn[DH];
-  __shared__ __attribute__((aligned(16))) float sc[kMaxChunk + 8];
-  __shared__ float red[8];
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  constexpr int UV = (GM > 1 && DH == 128) ? 2 : 4;  // value-chunk loads in flight per lane and row
+  __shared__ float qs[GM][DH], kn[DH], vn[DH];
+  __shared__ __attribute__((aligned(16))) float sc[kMaxChunk + 8];  // [GM][chunk]
+  __shared__ float red[GM][8];
+  const int s = blockIdx.x, b = blockIdx.z;
+  const int G = H / Hkv, nsub = (G + gsz - 1) / gsz;
+  const int hk = blockIdx.y / nsub, run = blockIdx.y % nsub;
+  const int h0 = hk * G + run * gsz, gcnt = min(gsz, G - run * gsz);  // query heads [h0, h0 + gcnt)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = *n_ptr;  // entries already cached; the new one goes to slot n
-  const size_t bh = (size_t)b * H + h;
-  T* __restrict__ K = Kc + bh * cap * DH;
-  T* __restrict__ VT = VTc + bh * DH * cap;
+  const size_t bk = (size_t)b * Hkv + hk;
+  T* __restrict__ K = Kc + bk * cap * DH;
+  T* __restrict__ VT = VTc + bk * DH * cap;
   const int j0 = s * chunk, j1 = min(n + 1, j0 + chunk);  // this split's keys [j0, j1)
   const int jc_end = min(j1, n);                           // of which cached: [j0, jc_end)
   const bool owns_new = (n >= j0 && n < j1);
+  const bool appends = s == 0 && run == 0;
 
-  const T* row = QKV + (size_t)b * 3 * D;
+  const T* row = QKV + (size_t)b * (H + 2 * Hkv) * DH;
+  for (int e = tid; e < GM * (DH / 2); e += 256) {
+    // slots g >= gcnt repeat the last head; their results are never stored
+    const int g = e / (DH / 2), c = e % (DH / 2), hq = h0 + min(g, gcnt - 1);
+    const float2 cs = rope[(size_t)n * (DH / 2) + c];
+    const float q1 = (float)row[hq * DH + c], q2 = (float)row[hq * DH + c + DH / 2];
+    qs[g][c] = q1 * cs.x - q2 * cs.y;
+    qs[g][c + DH / 2] = q2 * cs.x + q1 * cs.y;
+  }
   if (tid < DH / 2) {
     const int c = tid;
     const float2 cs = rope[(size_t)n * (DH / 2) + c];
-    const float q1 = (float)row[h * DH + c], q2 = (float)row[h * DH + c + DH / 2];
-    qs[c] = q1 * cs.x - q2 * cs.y;
-    qs[c + DH / 2] = q2 * cs.x + q1 * cs.y;
-    const float k1 = (float)row[D + h * DH + c], k2 = (float)row[D + h * DH + c + DH / 2];
+    const T* kr = row + (size_t)(H + hk) * DH;
+    const float k1 = (float)kr[c], k2 = (float)kr[c + DH / 2];
     const T ka = round_t<T>(k1 * cs.x - k2 * cs.y), kb = round_t<T>(k2 * cs.x + k1 * cs.y);
     kn[c] = (float)ka;
     kn[c + DH / 2] = (float)kb;
-    if (s == 0) {
+    if (appends) {
       K[(size_t)n * DH + c] = ka;
       K[(size_t)n * DH + c + DH / 2] = kb;
     }
   } else if (tid >= 64 && tid < 64 + DH) {
     const int d = tid - 64;
-    const T v = row[2 * D + h * DH + d];
+    const T v = row[(size_t)(H + Hkv + hk) * DH + d];
     vn[d] = (float)v;
-    if (s == 0) VT[(size_t)d * cap + n] = v;
+    if (appends) VT[(size_t)d * cap + n] = v;
   }
   __syncthreads();
 
-  // ---- scores of the cached keys
+  // ---- scores of the cached keys: each key is loaded once and scored against every head
   const int kl = lane / LPK, pp = lane % LPK;
-  float qr[8];
+  float qr[GM][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qr[e] = qs[8 * pp + e];
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qr[g][e] = qs[g][8 * pp + e];
   for (int jb = j0 + wave * KPW; jb < jc_end; jb += 4 * KPW * U) {
     float kv[U][8];
 #pragma unroll
@@ -403,48 +422,74 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float d = 0.f;
+      float d[GM];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qr[e], kv[u][e], d);
+      for (int g = 0; g < GM; ++g) {
+        d[g] = 0.f;
 #pragma unroll
-      for (int o = 1; o < LPK; o <<= 1) d += __shfl_xor(d, o, 64);
+        for (int e = 0; e < 8; ++e) d[g] = fmaf(qr[g][e], kv[u][e], d[g]);
+      }
+#pragma unroll
+      for (int o = 1; o < LPK; o <<= 1)
+#pragma unroll
+        for (int g = 0; g < GM; ++g) d[g] += __shfl_xor(d[g], o, 64);
       const int j = jb + u * 4 * KPW + kl;
-      if (pp == 0 && j < jc_end) sc[j - j0] = d * scale_log2;
+      if (pp == 0 && j < jc_end)
+#pragma unroll
+        for (int g = 0; g < GM; ++g) sc[g * chunk + j - j0] = d[g] * scale_log2;
     }
   }
-  if (owns_new && wave == 0) {
+  if (owns_new && wave < GM) {  // wave g scores the new key for head slot g
     float d = 0.f;
-    for (int e = lane; e < DH; e += 64) d = fmaf(qs[e], kn[e], d);
+    for (int e = lane; e < DH; e += 64) d = fmaf(qs[wave][e], kn[e], d);
     d = wave_sum(d);
-    if (lane == 0) sc[n - j0] = d * scale_log2;
+    if (lane == 0) sc[wave * chunk + n - j0] = d * scale_log2;
   }
   __syncthreads();
 
-  // ---- softmax over [j0, j1)
+  // ---- softmax over [j0, j1), per head
   const int cnt = j1 - j0;
-  float mx = -INFINITY;
-  for (int j = tid; j < cnt; j += 256) mx = fmaxf(mx, sc[j]);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float ls = 0.f;
-  for (int j = tid; j < cnt; j += 256) {
-    const float p = exp2f(sc[j] - mx);
-    sc[j] = p;
-    ls += p;
+  float mx[GM], ls[GM];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) mx[g] = -INFINITY;
+  for (int j = tid; j < cnt; j += 256)
+#pragma unroll
+    for (int g = 0; g < GM; ++g) mx[g] = fmaxf(mx[g], sc[g * chunk + j]);
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    mx[g] = wave_max(mx[g]);
+    if (lane == 0) red[g][wave] = mx[g];
   }
-  ls = wave_sum(ls);
-  __syncthreads();  // everyone has read red[] (max) before it is reused
-  if (lane == 0) red[4 + wave] = ls;
   __syncthreads();
-  ls = red[4] + red[5] + red[6] + red[7];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    mx[g] = fmaxf(fmaxf(red[g][0], red[g][1]), fmaxf(red[g][2], red[g][3]));
+    ls[g] = 0.f;
+  }
+  for (int j = tid; j < cnt; j += 256)
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      const float p = exp2f(sc[g * chunk + j] - mx[g]);
+      sc[g * chunk + j] = p;
+      ls[g] += p;
+    }
+#pragma unroll
+  for (int g = 0; g < GM; ++g) ls[g] = wave_sum(ls[g]);
+  __syncthreads();  // everyone has read red[] (max) before it is reused
+  if (lane == 0)
+#pragma unroll
+    for (int g = 0; g < GM; ++g) red[g][4 + wave] = ls[g];
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < GM; ++g) ls[g] = red[g][4] + red[g][5] + red[g][6] + red[g][7];
 
   // ---- values: lane (row lane rl, chunk lane cl) owns rows r*32 + wave*8 + rl, keys cl*8 + 64t
   const int cl = lane & 7, rl = lane >> 3;
-  float acc[RPL];
+  float acc[GM][RPL];
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) acc[r] = 0.f;
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) acc[g][r] = 0.f;
   for (int jb = j0 + cl * 8; jb < jc_end; jb += 64 * UV) {
     // UV chunks of 8 keys per row in flight; chunks past the cached keys are clamped to a valid
     // address and weighted by zero
@@ -458,34 +503,46 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       const int jc = jb + 64 * u;
-      float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = (jc + e < jc_end) ? sc[min(jc + e, jc_end - 1) - j0] : 0.f;
+      for (int g = 0; g < GM; ++g) {
+        // jc - j0 is a multiple of 8 and the row's 8 scores end within sc (chunk + 8 padding)
+        const float4 s0 = *(const float4*)&sc[g * chunk + jc - j0];
+        const float4 s1 = *(const float4*)&sc[g * chunk + jc - j0 + 4];
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-      for (int r = 0; r < RPL; ++r)
+        for (int e = 0; e < 8; ++e) {
+          const float p = (jc + e < jc_end) ? sv[e] : 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r] = fmaf(p[e], v[u][r][e], acc[r]);
+          for (int r = 0; r < RPL; ++r) acc[g][r] = fmaf(p, v[u][r][e], acc[g][r]);
+        }
+      }
     }
   }
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) {
+  for (int g = 0; g < GM; ++g)
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) acc[r] += __shfl_xor(acc[r], o, 64);
-  }
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) acc[g][r] += __shfl_xor(acc[g][r], o, 64);
   if (cl == 0) {
-    const float pn = owns_new ? sc[n - j0] : 0.f;
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      const int d = r * 32 + wave * 8 + rl;
-      const float o = acc[r] + pn * vn[d];
-      if (nsplit == 1) {
-        ACT[opnd_idx(ACT, b, h * DH + d, ld_act)] = round_t<T>(o / ls);
-      } else {
-        float* pp_ = part + ((bh * nsplit) + s) * (DH + 2);
-        pp_[2 + d] = o;
-        if (d == 0) {
-          pp_[0] = mx;
-          pp_[1] = ls;
+    for (int g = 0; g < GM; ++g) {
+      if (g >= gcnt) break;
+      const int h = h0 + g;
+      const float pn = owns_new ? sc[g * chunk + n - j0] : 0.f;
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        const int d = r * 32 + wave * 8 + rl;
+        const float o = acc[g][r] + pn * vn[d];
+        if (nsplit == 1) {
+          ACT[opnd_idx(ACT, b, h * DH + d, ld_act)] = round_t<T>(o / ls[g]);
+        } else {
+          float* pp_ = part + (((size_t)b * H + h) * nsplit + s) * (DH + 2);
+          pp_[2 + d] = o;
+          if (d == 0) {
+            pp_[0] = mx[g];
+            pp_[1] = ls[g];
+          }
         }
       }
     }
@@ -509,61 +566,75 @@ __global__ void k_attn_combine(const float* __restrict__ part, int H, int nsplit
   ACT[opnd_idx(ACT, b, h * DH + d, ld_act)] = round_t<T>(o / l);
 }
 
-template <typename T, int DH>
-static hipError_t launch_decode_t(const void* QKV, int B, const int* n_ptr, int D, int H, const float2* rope, void* Kc,
-                                  void* Vc, int cap, void* ACT, int ld_act, float* part, size_t part_bytes, int nsplit,
-                                  hipStream_t st) {
+// query heads per decode workgroup: all of a group up to 4 (runs of <= 4 for larger groups)
+static int decode_group_max(int H, int Hkv) { return H == Hkv ? 1 : (H / Hkv == 2 ? 2 : 4); }
+
+template <typename T, int DH, int GM>
+static hipError_t launch_decode_t(const void* QKV, int B, const int* n_ptr, int H, int Hkv, const float2* rope,
+                                  void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part, size_t part_bytes,
+                                  int nsplit, hipStream_t st) {
   // the split layout covers the whole capacity, so it does not depend on the current length n
   // (which is read on the device); splits past n + 1 produce empty partials
   int chunk = (cap + nsplit - 1) / nsplit;
   chunk = (chunk + 63) / 64 * 64;
-  if (chunk > kMaxChunk) return hipErrorInvalidValue;
+  if (chunk * GM > kMaxChunk) return hipErrorInvalidValue;
   if (nsplit > 1 && (size_t)B * H * nsplit * (DH + 2) * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  const int G = H / Hkv, nsub = (G + GM - 1) / GM, gsz = (G + nsub - 1) / nsub;
   const float sl2 = kLog2e / sqrtf((float)DH);
-  hipLaunchKernelGGL((k_attn_decode<T, DH>), dim3(nsplit, H, B), dim3(256), 0, st, (const T*)QKV, n_ptr, D, H, rope,
-                     (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, part, nsplit, chunk, sl2);
+  hipLaunchKernelGGL((k_attn_decode<T, DH, GM>), dim3(nsplit, Hkv * nsub, B), dim3(256), 0, st, (const T*)QKV, n_ptr,
+                     H, Hkv, gsz, rope, (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, part, nsplit, chunk, sl2);
   if (nsplit > 1)
     hipLaunchKernelGGL((k_attn_combine<T, DH>), dim3(H, B), dim3(DH), 0, st, (const float*)part, H, nsplit, (T*)ACT,
                        ld_act);
   return hipGetLastError();
 }
 
-int decode_splits(int B, int H, int cap) {
-  int s = (cap + kMaxChunk - 1) / kMaxChunk;                       // LDS holds at most kMaxChunk scores
-  if (B * H < 512) s = std::max(s, std::min((1024 + B * H - 1) / (B * H), (cap + 255) / 256));
+int decode_splits(int B, int H, int Hkv, int cap) {
+  const int gm = decode_group_max(H, Hkv);
+  const int wgs = B * Hkv * ((H / Hkv + gm - 1) / gm);              // workgroups per split
+  int s = (cap + kMaxChunk / gm - 1) / (kMaxChunk / gm);            // LDS holds at most kMaxChunk scores
+  if (wgs < 512) s = std::max(s, std::min((1024 + wgs - 1) / wgs, (cap + 255) / 256));
   return std::max(1, std::min(s, kMaxSplit));
 }
 
-hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int D, int H, int dh,
+hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int H, int Hkv, int dh,
                                     const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part,
                                     size_t part_bytes, int nsplit, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-#define BT_DEC(T, DHV)                                                                                            \
-  if (dh == DHV)                                                                                                  \
-    return launch_decode_t<T, DHV>(QKV, B, n_ptr, D, H, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, nsplit, \
-                                   st);
+  if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  const int gm = decode_group_max(H, Hkv);
+#define BT_DEC(T, DHV, GMV)                                                                                        \
+  if (dh == DHV && gm == GMV)                                                                                      \
+    return launch_decode_t<T, DHV, GMV>(QKV, B, n_ptr, H, Hkv, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes,   \
+                                        nsplit, st);
+#define BT_DEC_G(T, DHV) BT_DEC(T, DHV, 1) BT_DEC(T, DHV, 2) BT_DEC(T, DHV, 4)
   if (f32) {
-    BT_DEC(float, 32) BT_DEC(float, 64) BT_DEC(float, 128)
+    BT_DEC_G(float, 32) BT_DEC_G(float, 64) BT_DEC_G(float, 128)
   } else {
-    BT_DEC(f16, 64) BT_DEC(f16, 128)
+    BT_DEC_G(f16, 64) BT_DEC_G(f16, 128)
   }
+#undef BT_DEC_G
 #undef BT_DEC
   return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- local attention (token decoder)
-// grid (H, B), one wave.  New slots [s0, s0 + m) of row b come from QKV rows b*m + i.
+// grid (H, B), one wave.  New slots [s0, s0 + m) of row b come from QKV rows b*m + i; the first
+// query head of each KV group writes them to the cache (the others read only slots < s0).
 constexpr int kMaxLocal = 32;
 
 template <typename T, int DH>
-__global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, int m, int s0, int D, int H,
+__global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, int m, int s0, int H, int Hkv,
                                                    const float2* __restrict__ rope, T* __restrict__ Kc,
                                                    T* __restrict__ Vc, int cap, T* __restrict__ ACT, int ld_act,
                                                    float scale) {
   __shared__ float ks[kMaxLocal][DH + 1], vs[kMaxLocal][DH + 1], qs[kMaxLocal][DH + 1];
   __shared__ float ps[64];
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const size_t bh = (size_t)b * H + h;
+  const int G = H / Hkv, hk = h / G;
+  const bool writes = h % G == 0;
+  const size_t qw = (size_t)(H + 2 * Hkv) * DH, koff = (size_t)(H + hk) * DH, voff = (size_t)(H + Hkv + hk) * DH;
+  const size_t bh = (size_t)b * Hkv + hk;
   T* __restrict__ K = Kc + bh * cap * DH;
   T* __restrict__ V = Vc + bh * cap * DH;
   constexpr int HALF = DH / 2;
@@ -573,23 +644,25 @@ __global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, in
   }
   for (int e = lane; e < m * HALF; e += 64) {
     const int i = e / HALF, c = e % HALF, slot = s0 + i;
-    const T* r = QKV + ((size_t)b * m + i) * 3 * D + h * DH;
+    const T* r = QKV + ((size_t)b * m + i) * qw;
     const float2 cs = rope[(size_t)slot * HALF + c];
-    const float q1 = (float)r[c], q2 = (float)r[c + HALF];
+    const float q1 = (float)r[h * DH + c], q2 = (float)r[h * DH + c + HALF];
     qs[i][c] = q1 * cs.x - q2 * cs.y;
     qs[i][c + HALF] = q2 * cs.x + q1 * cs.y;
-    const float k1 = (float)r[D + c], k2 = (float)r[D + c + HALF];
+    const float k1 = (float)r[koff + c], k2 = (float)r[koff + c + HALF];
     const T ka = round_t<T>(k1 * cs.x - k2 * cs.y), kb = round_t<T>(k2 * cs.x + k1 * cs.y);
     ks[slot][c] = (float)ka;
     ks[slot][c + HALF] = (float)kb;
-    K[(size_t)slot * DH + c] = ka;
-    K[(size_t)slot * DH + c + HALF] = kb;
+    if (writes) {
+      K[(size_t)slot * DH + c] = ka;
+      K[(size_t)slot * DH + c + HALF] = kb;
+    }
   }
   for (int e = lane; e < m * DH; e += 64) {
     const int i = e / DH, d = e % DH, slot = s0 + i;
-    const T v = QKV[((size_t)b * m + i) * 3 * D + 2 * D + h * DH + d];
+    const T v = QKV[((size_t)b * m + i) * qw + voff + d];
     vs[slot][d] = (float)v;
-    V[(size_t)slot * DH + d] = v;
+    if (writes) V[(size_t)slot * DH + d] = v;
   }
   __syncthreads();
   for (int i = 0; i < m; ++i) {
@@ -630,10 +703,11 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 // Token-decoder attention for ONE new slot s0 per row (a decode step).  One wave per (row, head);
 // LPK = DH / 8 lanes per key hold 8 dimensions each, so a wave scores 64 / LPK keys per pass.  The
 // new key (rotary applied, rounded to the cache type) and value are written to local slot s0 and
-// used from registers; the s0 cached entries are read with 16-byte loads.  Each key group keeps an
+// used from registers (the first query head of each KV group writes them); the s0 cached entries
+// are read with 16-byte loads.  Each key group keeps an
 // online softmax (base 2) over its keys; the groups are merged with shuffles in a fixed order.
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ QKV, int B, int s0, int D, int H,
+__global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ QKV, int B, int s0, int H, int Hkv,
                                                          const float2* __restrict__ rope, T* __restrict__ Kc,
                                                          T* __restrict__ Vc, int cap, T* __restrict__ ACT, int ld_act,
                                                          float scale_log2) {
@@ -643,14 +717,15 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
   if (pair >= B * H) return;  // whole wave
   const int b = pair / H, h = pair % H;
   const int g = lane % LPK, kg = lane / LPK;  // dimensions [8g, 8g + 8), key group
-  const size_t bh = (size_t)b * H + h;
+  const int G = H / Hkv, hk = h / G;
+  const size_t bh = (size_t)b * Hkv + hk;
   T* __restrict__ K = Kc + bh * cap * DH;
   T* __restrict__ V = Vc + bh * cap * DH;
-  const T* row = QKV + (size_t)b * 3 * D + h * DH + 8 * g;
+  const T* row = QKV + (size_t)b * (H + 2 * Hkv) * DH + 8 * g;
   float q[8], kn[8], vn[8], kc[8], vc[8];
-  load8(row, q);
-  load8(row + D, kn);
-  load8(row + 2 * D, vn);
+  load8(row + h * DH, q);
+  load8(row + (H + hk) * DH, kn);
+  load8(row + (H + Hkv + hk) * DH, vn);
   const int nkeys = s0 + 1;
   // first pass's cached entry of this key group (clamped; masked below)
   const int jc0 = min(kg, max(s0 - 1, 0));
@@ -670,7 +745,7 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
       kn[e] = (float)round_t<T>(kn[e] * cs.x + kp * cs.y);
     }
   }
-  if (kg == 0) {
+  if (kg == 0 && h % G == 0) {
     store8(K + (size_t)s0 * DH + 8 * g, kn);
     store8(V + (size_t)s0 * DH + 8 * g, vn);
   }
@@ -719,10 +794,11 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
   }
 }
 
-hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
+hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
                                   hipStream_t st) {
   if (B <= 0 || m <= 0) return hipSuccess;
+  if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
   if (s0 + m > kMaxLocal || s0 + m > cap) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)dh);
   if (m == 1) {
@@ -730,7 +806,7 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s
     const dim3 g1((B * H + 3) / 4);
 #define BT_STEP(T, DHV)                                                                                         \
   if (dh == DHV) {                                                                                              \
-    hipLaunchKernelGGL((k_local_attn_step<T, DHV>), g1, dim3(256), 0, st, (const T*)QKV, B, s0, D, H, rope,     \
+    hipLaunchKernelGGL((k_local_attn_step<T, DHV>), g1, dim3(256), 0, st, (const T*)QKV, B, s0, H, Hkv, rope,   \
                        (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale * kLog2e);                                    \
     return hipGetLastError();                                                                                   \
   }
@@ -745,8 +821,8 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s
   dim3 grid(H, B);
 #define BT_LOC(T, DHV)                                                                                          \
   if (dh == DHV) {                                                                                              \
-    hipLaunchKernelGGL((k_local_attn<T, DHV>), grid, dim3(64), 0, st, (const T*)QKV, m, s0, D, H, rope, (T*)Kc, \
-                       (T*)Vc, cap, (T*)ACT, ld_act, scale);                                                     \
+    hipLaunchKernelGGL((k_local_attn<T, DHV>), grid, dim3(64), 0, st, (const T*)QKV, m, s0, H, Hkv, rope,       \
+                       (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale);                                             \
     return hipGetLastError();                                                                                   \
   }
   if (f32) {

@@ -26,9 +26,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct LayerOff {
   size_t ln;  // fp32 [4][D]: ln1.g, ln1.b, ln2.g, ln2.b
-  size_t w1;  // T [N1 = 3D + F][D]: rows = output features of q | k | v | up (fp32: K-contiguous;
+  size_t w1;  // T [N1 = QW + F][D]: rows = output features of q | k | v | up (fp32: K-contiguous;
               //   fp16: fragment order, see frag_off)
-  size_t b1;  // fp32 [3D + F]
+  size_t b1;  // fp32 [QW + F]
   size_t w2;  // T [D][D + F]: row n = output feature n of attn.out (k < D) and mlp.down (k >= D),
               //   same layout as w1
   size_t b2;  // fp32 [2][D]: attn.out.b, mlp.down.b
@@ -37,10 +37,12 @@ struct LayerOff {
 struct Layout {
   // model dimensions
   int V, D, H, dh, F, L, P, Nb, Nt, De;
+  int Hkv;      // key/value heads (grouped-query attention: H / Hkv query heads per KV head)
+  int QW;       // width of the fused q | k | v projection: D + 2 Hkv dh
   int Bmax, max_tokens;
   int max_prompt;  // longest padded prompt the activations hold (a multiple of L)
-  int ncap;     // block-KV entries per (layer, row, head), multiple of 64
-  int lcap;     // local-KV entries per (layer, row, head) = P + L
+  int ncap;     // block-KV entries per (layer, row, KV head), multiple of 64
+  int lcap;     // local-KV entries per (layer, row, KV head) = P + L
   int npos;     // rows of the rotary table
   int Vpad;     // classifier rows padded to a multiple of 128
   int64_t Mmax; // activation rows
@@ -55,7 +57,7 @@ struct Layout {
   size_t block_kv, local_kv;
   size_t X;     // fp32 [Mmax][D] residual stream
   size_t LN;    // T [2][Mpad][D] LayerNorm outputs (ln1, ln2); fp16: fragment order
-  size_t QKV;   // T [Mmax][3D]
+  size_t QKV;   // T [Mmax][QW]
   size_t ACT;   // T [Mpad][D + F]: attention output | GELU(up); fp16: fragment order
   size_t part;  // fp32 split-KV partials of block-attention decode
   size_t part_bytes;
@@ -149,24 +151,28 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
                        int K, EpiMode mode, const Epi& ep, hipStream_t st);
 
 // ---- attention
+// Attention launchers take H query heads and Hkv key/value heads of width dh (H % Hkv == 0); a
+// QKV row is [q: H dh | k: Hkv dh | v: Hkv dh] and query head h reads KV head h / (H / Hkv).
+// Caches are [row][KV head][...].
+//
 // rotary + scatter of K (row-major [slot][dh]) and V (block cache: transposed [dh][slot]) for rows
-// (b, i) of QKV [B*m][3D] into cache slots s0 + i, at rotary positions s0 + i.
-hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
+// (b, i) of QKV [B*m][QW] into cache slots s0 + i, at rotary positions s0 + i.
+hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed,
                                hipStream_t st);
 // causal prefill attention of rows (b, i < n) at positions i over cache entries [0, i]
-hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int D, int H, int dh,
+hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int H, int Hkv, int dh,
                                     const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
                                     int ld_act, hipStream_t st);
 // one new block-decoder position per row: n = *n_ptr (device state) entries are cached; rotary at
-// position n, append K/V at slot n, attend over [0, n].  nsplit = decode_splits(B, H, cap) splits of
-// the capacity (fixed for a batch size, so the launch does not depend on n).
-int decode_splits(int B, int H, int cap);
-hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int D, int H, int dh,
+// position n, append K/V at slot n, attend over [0, n].  nsplit = decode_splits(B, H, Hkv, cap)
+// splits of the capacity (fixed for a batch size, so the launch does not depend on n).
+int decode_splits(int B, int H, int Hkv, int cap);
+hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int H, int Hkv, int dh,
                                     const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
                                     float* part, size_t part_bytes, int nsplit, hipStream_t st);
 // local attention: new slots [s0, s0 + m) per row; rotary at slot, write to local cache, attend over [0, slot]
-hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int D, int H, int dh,
+hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
                                   hipStream_t st);
 

@@ -62,7 +62,8 @@ typedef enum {
  *   directly (no prefix projection, no token decoder, no local KV);
  *   BT_BF16 also needs d_model % 64 == 0 and d_mlp % 64 == 0;
  *   max_batch >= 1; max_tokens >= block_len (padded prompt + generated);
- *   0 <= max_prompt_tokens <= max_tokens. */
+ *   0 <= max_prompt_tokens <= max_tokens;
+ *   n_kv_heads = 0 (multi-head) or a divisor of n_heads (grouped-query; 1 = multi-query). */
 typedef struct {
   int32_t vocab, d_model, n_heads, d_mlp;
   int32_t n_block_layers, n_token_layers;
@@ -76,14 +77,20 @@ typedef struct {
   int32_t max_prompt_tokens; /* longest prompt bt_prefill accepts, after left padding; sizes the
                                 prefill activations (one row per prompt block and batch row).
                                 0 = max_tokens.  Must be <= max_tokens when set. */
+  int32_t n_kv_heads; /* key/value heads of every attention layer (block and token decoder).
+                         0 = n_heads.  With H_kv < n_heads, query heads are grouped in runs of
+                         G = n_heads / H_kv consecutive heads and head i attends with key/value
+                         head i / G (grouped-query attention; summary page §3.4 "The Block
+                         Decoder" names it as compatible); the KV caches then hold H_kv heads. */
 } bt_config;
 
 /* Size in bytes of the canonical weights blob for this config.  The blob is
  * the concatenation, without padding, of these tensors in this order, each
  * row-major, elements of the config's dtype (bf16 or fp32):
  *   emb_block [V, D/L_B]
- *   per block layer l: ln1.g [D], ln1.b [D], attn.qkv.w [D, 3D] (columns: q | k | v,
- *     head-major inside each), attn.qkv.b [3D], attn.out.w [D, D], attn.out.b [D],
+ *   per block layer l: ln1.g [D], ln1.b [D], attn.qkv.w [D, Q] (columns: q | k | v,
+ *     head-major inside each; Q = D + 2 H_kv d_head, = 3D for multi-head attention),
+ *     attn.qkv.b [Q], attn.out.w [D, D], attn.out.b [D],
  *     ln2.g [D], ln2.b [D], mlp.up.w [D, F], mlp.up.b [F], mlp.down.w [F, D], mlp.down.b [D]
  *   blk.lnf.g [D], blk.lnf.b [D]
  *   prefix.w [D, P*D], prefix.b [P*D]
@@ -155,14 +162,15 @@ int bt_set_graphs(bt_handle* h, int32_t enable);
 int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_kv_len);
 
 /* Read-only introspection of the workspace layout, for tests and tools.
- * which = 0: block-KV cache [N_blk][2 (K, V)][max_batch][n_heads][cap * d_head] with
+ * which = 0: block-KV cache [N_blk][2 (K, V)][max_batch][H_kv][cap * d_head] with
  *            cap = ceil(max_tokens / L_B) rounded up to a multiple of 64; per (layer,
- *            row, head) the keys are [cap][d_head] (after the rotary embedding) and the
+ *            row, KV head) the keys are [cap][d_head] (after the rotary embedding) and the
  *            values are transposed, [d_head][cap];
- * which = 1: local-KV cache [N_tok][2][max_batch][n_heads][P + L_B][d_head] (keys after
+ * which = 1: local-KV cache [N_tok][2][max_batch][H_kv][P + L_B][d_head] (keys after
  *            the rotary embedding, values not transposed).
  * Elements are fp16 for BT_BF16 and fp32 for BT_FP32.  Writes the byte
- * offset from the workspace start, the byte size and the per-head capacity. */
+ * offset from the workspace start, the byte size and the per-head capacity.  H_kv is
+ * n_kv_heads, or n_heads when that is 0. */
 int bt_workspace_region(const bt_config* cfg, int32_t which, size_t* offset, size_t* bytes,
                         int32_t* capacity);
 

@@ -46,6 +46,27 @@ def test_blob_size_matches_packer(name):
     assert hg.weight_names(c) == [s[0] for s in wl.weight_specs(c)]
 
 
+@pytest.mark.parametrize("kv", [1, 3, 4])
+def test_grouped_query_blob_and_cache_sizes(kv):
+    """With n_kv_heads the q|k|v projection is D + 2 H_kv d_head wide and both KV caches hold H_kv
+    heads: H / H_kv times smaller than with multi-head attention."""
+    import hierarchical_global_local_amd as hg
+    L = hg.lib()
+    c, cfg = _cfg("c2_decode_heavy", n_kv_heads=kv)
+    n = sum(int(np.prod(s)) for _, s, _ in wl.weight_specs(c))
+    assert L.bt_weights_bytes(ctypes.byref(cfg)) == n * 2
+    assert dict((k, s) for k, s, _ in wl.weight_specs(c))["blk.0.attn.qkv.w"] == (768, 768 + 2 * kv * 64)
+    _, mha = _cfg("c2_decode_heavy")
+    for which in (0, 1):
+        got = []
+        for x in (cfg, mha):
+            off, nb, cap = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+            assert L.bt_workspace_region(ctypes.byref(x), which, ctypes.byref(off), ctypes.byref(nb),
+                                         ctypes.byref(cap)) == 0
+            got.append((nb.value, cap.value))
+        assert got[0][1] == got[1][1] and got[0][0] * (12 // kv) == got[1][0]
+
+
 def test_packed_blob_matches_declared_size():
     import hierarchical_global_local_amd as hg
     c, cfg = _cfg("c0_tiny")
@@ -72,7 +93,9 @@ def test_block_kv_footprint_ratio_is_block_len():
                                              ("dtype", 7, "dtype"), ("max_batch", 0, "max_batch"),
                                              ("d_model", 96, "d_head"), ("prefix_len", 40, "prefix_len"),
                                              ("max_prompt_tokens", -4, "max_prompt_tokens"),
-                                             ("max_prompt_tokens", 1 << 20, "max_prompt_tokens")])
+                                             ("max_prompt_tokens", 1 << 20, "max_prompt_tokens"),
+                                             ("n_kv_heads", 5, "n_kv_heads"), ("n_kv_heads", -1, "n_kv_heads"),
+                                             ("n_kv_heads", 24, "n_kv_heads")])
 def test_invalid_config_rejected_on_host(field, value, msg):
     import hierarchical_global_local_amd as hg
     _, cfg = _cfg("c1_prefill_heavy")

@@ -46,6 +46,40 @@ def test_fp32_variants(kw, B, T, G):
     _fp32_case(wl.get_config("c0_tiny", **kw), B, T, G, seed=1)
 
 
+# grouped-query attention: groups of 2 (one decode workgroup per KV head), 3 (a workgroup with an
+# idle head slot), 8 (a group cut into two runs of 4) and multi-query with L_B = 2
+GQA_FP32 = [(dict(d_model=128, n_heads=4, n_kv_heads=2), 2, 10, 9),
+            (dict(d_model=192, n_heads=6, n_kv_heads=2, d_mlp=320), 3, 13, 8),
+            (dict(d_model=256, n_heads=8, n_kv_heads=1), 2, 9, 7),
+            (dict(d_model=128, n_heads=4, n_kv_heads=1, block_len=2, prefix_len=2), 2, 11, 10)]
+
+
+@pytest.mark.parametrize("kw,B,T,G", GQA_FP32)
+def test_fp32_grouped_query_attention(kw, B, T, G):
+    _fp32_case(wl.get_config("c0_tiny", **kw), B, T, G, seed=13)
+
+
+@pytest.mark.parametrize("kw,max_tokens", [(dict(d_model=256, n_heads=4, n_kv_heads=2), None),
+                                           (dict(d_model=384, n_heads=6, n_kv_heads=2, d_mlp=768), None),
+                                           (dict(d_model=256, n_heads=4, n_kv_heads=1), 4096),
+                                           (dict(d_model=512, n_heads=4, n_kv_heads=2), None)])
+def test_bf16_grouped_query_attention(kw, max_tokens):
+    """bf16 GQA / MQA every step; max_tokens=4096 adds key splits, d_model=512 gives d_head=128."""
+    cfg = SMALL_BF16.with_(**kw)
+    log(f"bf16 GQA case {kw} max_tokens={max_tokens}")
+    W = wl.make_weights(cfg, seed=14, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=14)
+    G = cfg.gen_len
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G), max_tokens=max_tokens)
+    _, ref_lg, st = om.generate(om.weights_as(W, np.float64), cfg, prompt, G, keep_logits=True, forced=ids)
+    gl = np.stack([lg[g] for g in range(G)], axis=1)
+    err = np.abs(gl - ref_lg).max()
+    exact = check_ids_against(ref_lg, ids, BF16_TOL)
+    log(f"  max-abs logit error {err:.3e}, exact argmax {exact:.3f}")
+    assert err <= BF16_TOL
+    assert model.cache_lengths() == (st.block_kv_len, st.local_kv_len)
+
+
 @pytest.mark.parametrize("kw,max_tokens", [(dict(), None), (dict(d_model=256, n_heads=2), None),
                                            (dict(block_len=1, prefix_len=1), None), (dict(block_len=8, prefix_len=2), None),
                                            (dict(), 4096)])
@@ -67,16 +101,18 @@ def test_bf16_small_every_step(kw, max_tokens):
     assert model.cache_lengths() == (st.block_kv_len, st.local_kv_len)
 
 
-def test_kv_caches_hold_rotated_keys_and_values():
-    """Block-KV (keys [slot][d], values transposed) and local-KV contents equal the oracle's caches."""
+@pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=4, n_kv_heads=2)])
+def test_kv_caches_hold_rotated_keys_and_values(kw):
+    """Block-KV (keys [slot][d], values transposed) and local-KV contents equal the oracle's caches
+    (H_kv heads per row under grouped-query attention)."""
     torch = require_gpu()
-    cfg = SMALL_BF16
+    cfg = SMALL_BF16.with_(**kw)
     W = wl.make_weights(cfg, seed=3, ln_jitter=True)
     prompt = wl.make_prompt(cfg, seed=3)
     G = 7   # ends inside a block: local KV holds P + 2 entries
     ids, _, model = run_gpu(cfg, W, prompt, G, max_tokens=64)
     _, _, st = om.generate(om.weights_as(W, np.float64), cfg, prompt, G, forced=ids)
-    B, H, dh = prompt.shape[0], cfg.n_heads, cfg.d_head
+    B, H, dh = prompt.shape[0], cfg.kv_heads, cfg.d_head
     blk, cap = model.cache_view(0)
     blk = blk.cpu().float().numpy().reshape(cfg.n_block_layers, 2, B, H, cap, dh)
     n = st.block_kv_len
