@@ -110,6 +110,15 @@ CONFIGS: Dict[str, Config] = {
     "v2_vanilla_decode_heavy": Config("v2_vanilla_decode_heavy", "bf16", vocab=50304, d_model=768, n_heads=12,
                                       d_mlp=3072, n_block_layers=12, n_token_layers=0, block_len=1,
                                       prefix_len=1, batch=256, prompt_len=128, gen_len=2048),
+    # variants the pages name as compatible: grouped-query (4 KV heads) and multi-query attention
+    # in every layer, at the decode-heavy shapes
+    "f4_gqa4_decode_heavy": Config("f4_gqa4_decode_heavy", "bf16", **_D768, block_len=4, prefix_len=1,
+                                   batch=256, prompt_len=128, gen_len=2048, n_kv_heads=4),
+    "f4_mqa_decode_heavy": Config("f4_mqa_decode_heavy", "bf16", **_D768, block_len=4, prefix_len=1,
+                                  batch=256, prompt_len=128, gen_len=2048, n_kv_heads=1),
+    # a context beyond 8K: 32768-token prompts (8192 prompt blocks at L_B = 4)
+    "f4_long32k_lb4": Config("f4_long32k_lb4", "bf16", **_D768, block_len=4, prefix_len=2,
+                             batch=8, prompt_len=32768, gen_len=256),
 }
 
 

@@ -47,7 +47,7 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
     return "n_token_layers = 0 (token-level transformer) needs block_len = 1";
   if (c.d_model > 4096) return "d_model must be <= 4096";
   if (!f32 && (c.d_model % 64 || c.d_mlp % 64)) return "BT_BF16 needs d_model and d_mlp multiples of 64";
-  if (c.max_batch < 1) return "max_batch must be >= 1";
+  if (c.max_batch < 1 || c.max_batch > (1 << 20)) return "max_batch must be in [1, 1048576]";
   if (c.max_tokens < c.block_len + 1) return "max_tokens must be > block_len";
   if (!(c.ln_eps > 0.f) || !(c.rope_base > 0.f)) return "ln_eps and rope_base must be > 0";
   const int nblk = (c.max_tokens + c.block_len - 1) / c.block_len;
@@ -147,7 +147,12 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.LN = region(2 * (size_t)lo.Mpad * D * E);
   lo.QKV = region(M * QW * E);
   lo.ACT = region((size_t)lo.Mpad * (D + F) * E);
-  lo.part_bytes = (size_t)lo.Bmax * lo.H * 32 * (lo.dh + 2) * 4;
+  // split-KV partials [B][H][nsplit][dh + 2] for the largest B * nsplit any batch size uses
+  lo.part_bytes = 0;
+  for (int b = 1; b <= lo.Bmax; ++b) {
+    const int ns = decode_splits(b, lo.H, lo.Hkv, lo.ncap);
+    if (ns > 1) lo.part_bytes = std::max(lo.part_bytes, (size_t)b * lo.H * ns * (lo.dh + 2) * 4);
+  }
   lo.part = region(lo.part_bytes);
   lo.keys = region((size_t)lo.Bmax * (lo.Vpad / 4 + 64) * 8);
   lo.rpart_rows = (int)std::min<int64_t>(lo.Mmax, 1024);

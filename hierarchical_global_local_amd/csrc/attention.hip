@@ -345,7 +345,7 @@ hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int
 // is the new one (rotated here, appended to the cache by split 0 of the group's first run, and
 // used from LDS by the split that owns it).
 constexpr int kMaxChunk = 4096;  // scores held in LDS per workgroup, over all its query heads
-constexpr int kMaxSplit = 32;
+constexpr int kMaxSplit = 128;   // with GM = 4 (chunks of 1024 keys): the 131072-entry capacity limit
 
 template <typename T, int DH, int GM>
 __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, const int* __restrict__ n_ptr, int H,

@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name", ["c1_prefill_heavy", "c2_decode_heavy", "c4_lb1", "c4_lb2", "c4_lb8", "c3_1p2b",
-                                  "v1_vanilla_prefill_heavy", "v2_vanilla_decode_heavy"])
+                                  "v1_vanilla_prefill_heavy", "v2_vanilla_decode_heavy", "f4_gqa4_decode_heavy",
+                                  "f4_mqa_decode_heavy", "f4_long32k_lb4"])
 def test_full_config_sampled_parity(name):
     require_gpu()
     cfg = wl.get_config(name)

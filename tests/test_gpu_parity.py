@@ -8,7 +8,8 @@ import pytest
 
 import bt_workloads as wl
 from oracle import model as om
-from tests.gpu_harness import (BF16_TOL, FP32_TOL, check_ids_against, log, require_gpu, run_gpu)
+from tests.gpu_harness import (BF16_TOL, FP32_TOL, check_ids_against, log, require_gpu, run_gpu,
+                               teacher_forced_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +100,28 @@ def test_bf16_small_every_step(kw, max_tokens):
     log(f"  max-abs logit error {err:.3e}, exact argmax {exact:.3f}")
     assert err <= BF16_TOL
     assert model.cache_lengths() == (st.block_kv_len, st.local_kv_len)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=4, n_kv_heads=1)])
+def test_deep_split_kv_long_context(kw):
+    """12000 prompt blocks (L_B = 1) in the largest block-KV capacity, 131072 entries: the block
+    attention runs its deepest split (32 splits of 4096 keys; 128 splits of 1024 keys when a
+    workgroup serves a group of 4 query heads) and merges several non-empty splits every step."""
+    cfg = SMALL_BF16.with_(block_len=1, prefix_len=2, **kw)
+    B, T, G = 2, 12000, 5
+    log(f"deep split-KV case {kw} B={B} T={T} G={G}")
+    W = wl.make_weights(cfg, seed=15, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, batch=B, T=T, seed=15)
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G), max_tokens=131072)
+    assert model.cache_lengths()[0] == T + G - 1
+    model.close()
+    del model
+    for r in range(B):
+        ref = teacher_forced_logits(cfg, W, prompt[r], ids[r], range(G))
+        err = float(np.abs(np.stack([lg[g][r] for g in range(G)]) - ref).max())
+        log(f"  row {r}: max-abs logit error {err:.3e}")
+        assert err <= BF16_TOL
+        check_ids_against(ref, ids[r], BF16_TOL)
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=4, n_kv_heads=2)])
