@@ -31,7 +31,8 @@ def log(msg):
 
 def describe(cfg):
     return (f"{cfg.name}: Block Transformer d={cfg.d_model} {cfg.n_block_layers}+{cfg.n_token_layers} layers "
-            f"H={cfg.n_heads} MLP={cfg.d_mlp} L_B={cfg.block_len} P={cfg.prefix_len} V={cfg.vocab}, "
+            f"H={cfg.n_heads}{'' if cfg.kv_heads == cfg.n_heads else f' H_kv={cfg.kv_heads}'} MLP={cfg.d_mlp} "
+            f"L_B={cfg.block_len} P={cfg.prefix_len} V={cfg.vocab}, "
             f"batch {cfg.batch}, {cfg.prompt_len}-token prompt, {cfg.gen_len} generated")
 
 
@@ -129,12 +130,12 @@ REPLAYABLE = {"decode/gemm_qkv_up": "gemm_qkv_up", "decode/attn_block_decode": "
 
 def attn_replay_roofline(runner, cfg):
     """Block-attention decode at the block-KV length reached at the end of the generation: K and V of
-    n entries read once per (row, head), q/k/v read and the output written (fp16)."""
+    n entries read once per (row, KV head), q|k|v read, the new entry and the output written (fp16)."""
     n, _ = runner.model.cache_lengths()
     reps = 20 * cfg.n_block_layers
     us = runner.replay_us("attn_block_decode", reps)
-    D, H, B = cfg.d_model, cfg.n_heads, cfg.batch
-    per_launch = B * H * n * (D // H) * 2 * 2 + B * D * 2 * 6
+    D, B, kvw = cfg.d_model, cfg.batch, cfg.kv_heads * cfg.d_head
+    per_launch = B * n * kvw * 2 * 2 + B * (2 * D + 4 * kvw) * 2
     achieved = per_launch / (us * 1e-6) / 1e9
     return {"kernel_class": "decode/attn_block_decode", "bound": "hbm", "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
