@@ -46,6 +46,10 @@ class Config:
     ln_eps: float = 1e-5
     rope_base: float = 10000.0
     n_kv_heads: int = 0   # key/value heads of every attention layer (grouped-query); 0 = n_heads
+    # how the context embedding reaches the token decoder: "prefix" (P prefix vectors in the local
+    # sequence), "sum" (L_B vectors added to the token inputs) or "xattn" (P vectors as encoder
+    # states of a cross-attention branch in every token-decoder layer)
+    context_mode: str = "prefix"
 
     @property
     def d_head(self) -> int:
@@ -58,6 +62,16 @@ class Config:
     @property
     def d_emb(self) -> int:
         return self.d_model // self.block_len
+
+    @property
+    def n_ctx(self) -> int:
+        """Vectors the context projection produces."""
+        return self.block_len if self.context_mode == "sum" else self.prefix_len
+
+    @property
+    def lead(self) -> int:
+        """Local slots before the block's first token: the P prefix vectors, or one start slot."""
+        return self.prefix_len if self.context_mode == "prefix" else 1
 
     def with_(self, **kw) -> "Config":
         return replace(self, **kw)
@@ -152,8 +166,9 @@ def weight_specs(cfg: Config) -> List[Tuple[str, Tuple[int, ...], str]]:
     Matrices are [in, out]; the three tables are [vocab, width].  The order is
     the canonical weight-blob order of the C-ABI (include/bt.h).
     """
-    V, D, F, P = cfg.vocab, cfg.d_model, cfg.d_mlp, cfg.prefix_len
-    QKV = D + 2 * cfg.kv_heads * cfg.d_head
+    V, D, F, NC = cfg.vocab, cfg.d_model, cfg.d_mlp, cfg.n_ctx
+    KVW = cfg.kv_heads * cfg.d_head
+    QKV = D + 2 * KVW
     specs: List[Tuple[str, Tuple[int, ...], str]] = [("emb_block", (V, cfg.d_emb), "normal")]
     for l in range(cfg.n_block_layers):
         specs += _layer_specs(f"blk.{l}", D, F, QKV)
@@ -161,10 +176,15 @@ def weight_specs(cfg: Config) -> List[Tuple[str, Tuple[int, ...], str]]:
     if cfg.n_token_layers == 0:
         # token-level (vanilla) transformer: no prefix, no token decoder
         return specs + [("head.w", (V, D), "normal")]
-    specs += [("prefix.w", (D, P * D), "normal"), ("prefix.b", (P * D,), "normal"),
+    specs += [("prefix.w", (D, NC * D), "normal"), ("prefix.b", (NC * D,), "normal"),
               ("emb_token", (V, D), "normal")]
     for l in range(cfg.n_token_layers):
         specs += _layer_specs(f"tok.{l}", D, F, QKV)
+        if cfg.context_mode == "xattn":
+            specs += [(f"tok.{l}.xattn.q.w", (D, D), "normal"), (f"tok.{l}.xattn.q.b", (D,), "normal"),
+                      (f"tok.{l}.xattn.kv.w", (D, 2 * KVW), "normal"),
+                      (f"tok.{l}.xattn.kv.b", (2 * KVW,), "normal"),
+                      (f"tok.{l}.xattn.out.w", (D, D), "normal"), (f"tok.{l}.xattn.out.b", (D,), "normal")]
     specs += [("tok.lnf.g", (D,), "ln_gain"), ("tok.lnf.b", (D,), "ln_bias"),
               ("head.w", (V, D), "normal")]
     return specs

@@ -36,6 +36,17 @@ listed, with reasons, in the design notes of this repository):
     tables (embedder, token embedding, classifier);
   - greedy decoding, ties to the lowest id.
 
+Context injection variants (§3.4 "The Token Decoder", alternatives to prefix tokens: summation,
+as in MEGABYTE, and cross-attention), selected by cfg.context_mode:
+  - "prefix" (default): as above;
+  - "sum": Proj maps c to L_B vectors u_0..u_{L-1}; the local sequence has no prefix slots; slot
+    0 holds a start token (the embedding of pad_id) and slot i >= 1 the token x_{kL+i-1}, and
+    u_i is added to slot i; slot i predicts x_{kL+i};
+  - "xattn": the same start-token local sequence without u; Proj maps c to P vectors used as
+    encoder states: every token-decoder layer gets a third parallel branch
+    h + Attn(LN1 h) + XAttn(LN1 h, enc) + MLP(LN2 h), multi-head attention from the layer's
+    queries to all P states, without rotary embedding or mask.
+
 With n_token_layers = 0 (and L_B = 1) the same definitions describe a token-level
 ("vanilla") transformer: the block decoder runs over tokens and its final LayerNorm
 output at position t-1 goes straight to the classifier to predict token t.  The pages
@@ -112,6 +123,11 @@ def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return np.transpose(o, (0, 2, 1, 3))
 
 
+def cross_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """softmax(q k^T / sqrt(d)) v per head with every key visible (no positions, no mask)."""
+    return causal_attention(q, k, v, np.zeros(q.shape[1], np.int64), np.zeros(k.shape[1], np.int64))
+
+
 # ----------------------------------------------------------------------------
 # one transformer layer (shared form of block decoder and token decoder layers)
 # ----------------------------------------------------------------------------
@@ -139,7 +155,7 @@ class LayerCache:
 
 def layer_forward(W: Weights, name: str, h: np.ndarray, pos: np.ndarray, n_heads: int,
                   eps: float, base: float, cache: Optional[LayerCache] = None,
-                  n_kv_heads: int = 0) -> np.ndarray:
+                  n_kv_heads: int = 0, enc: Optional[np.ndarray] = None) -> np.ndarray:
     """h + Attn(LN1 h) + MLP(LN2 h) for h [B, n, D] at positions pos [n].
 
     With a cache, the new keys/values are appended first and the queries attend
@@ -147,6 +163,8 @@ def layer_forward(W: Weights, name: str, h: np.ndarray, pos: np.ndarray, n_heads
     With n_kv_heads < n_heads (grouped-query attention) the projection has n_kv_heads key and
     value heads, and query head i uses key/value head i // (n_heads / n_kv_heads); the cache
     holds the n_kv_heads heads.
+    With encoder states enc [B, P, D] the layer adds a cross-attention branch: queries from LN1 h,
+    keys and values from enc (n_kv_heads heads, grouped the same way), output projection.
     """
     B, n, D = h.shape
     dh = D // n_heads
@@ -173,16 +191,26 @@ def layer_forward(W: Weights, name: str, h: np.ndarray, pos: np.ndarray, n_heads
 
     u = gelu(m @ W[f"{name}.mlp.up.w"] + W[f"{name}.mlp.up.b"])
     mlp = u @ W[f"{name}.mlp.down.w"] + W[f"{name}.mlp.down.b"]
-    return h + attn + mlp
+    out = h + attn + mlp
+    if enc is not None:
+        P = enc.shape[1]
+        xq = (a @ W[f"{name}.xattn.q.w"] + W[f"{name}.xattn.q.b"]).reshape(B, n, n_heads, dh)
+        xkv = enc @ W[f"{name}.xattn.kv.w"] + W[f"{name}.xattn.kv.b"]
+        xk = xkv[..., :hkv * dh].reshape(B, P, hkv, dh)
+        xv = xkv[..., hkv * dh:].reshape(B, P, hkv, dh)
+        xo = cross_attention(xq, np.repeat(xk, group, axis=2), np.repeat(xv, group, axis=2)).reshape(B, n, D)
+        out = out + xo @ W[f"{name}.xattn.out.w"] + W[f"{name}.xattn.out.b"]
+    return out
 
 
 def stack_forward(W: Weights, prefix: str, n_layers: int, h: np.ndarray, pos: np.ndarray,
                   n_heads: int, eps: float, base: float,
-                  caches: Optional[List[LayerCache]] = None, n_kv_heads: int = 0) -> np.ndarray:
+                  caches: Optional[List[LayerCache]] = None, n_kv_heads: int = 0,
+                  enc: Optional[np.ndarray] = None) -> np.ndarray:
     """Run n_layers layers named ``{prefix}.{l}`` and the final LayerNorm ``{prefix}.lnf``."""
     for l in range(n_layers):
         h = layer_forward(W, f"{prefix}.{l}", h, pos, n_heads, eps, base,
-                          None if caches is None else caches[l], n_kv_heads)
+                          None if caches is None else caches[l], n_kv_heads, enc)
     return layer_norm(h, W[f"{prefix}.lnf.g"], W[f"{prefix}.lnf.b"], eps)
 
 
@@ -219,17 +247,34 @@ def block_decoder(W: Weights, cfg, e: np.ndarray, first_pos: int = 0,
 
 
 def prefix_from_context(W: Weights, cfg, c: np.ndarray) -> np.ndarray:
-    """Proj: c [B, D] -> P prefix vectors [B, P, D]; prefix j is slice [jD, (j+1)D)."""
+    """Proj: c [B, D] -> n_ctx vectors [B, n_ctx, D] (P prefix vectors, L_B summands with
+    summation); vector j is slice [jD, (j+1)D)."""
     u = c @ W["prefix.w"] + W["prefix.b"]
-    return u.reshape(c.shape[0], cfg.prefix_len, cfg.d_model)
+    return u.reshape(c.shape[0], cfg.n_ctx, cfg.d_model)
+
+
+def local_inputs(W: Weights, cfg, c: np.ndarray, toks: np.ndarray):
+    """Token-decoder input of one block from the previous block's context embedding c [B, D] and
+    the block's tokens toks [B, o] before the predicted one: (z [B, lead + o, D], encoder states
+    or None).  Slot lead - 1 + o predicts the block's token o."""
+    ctx = prefix_from_context(W, cfg, c)
+    emb = W["emb_token"][toks]
+    if cfg.context_mode == "prefix":
+        return np.concatenate([ctx, emb], axis=1), None
+    start = np.broadcast_to(W["emb_token"][cfg.pad_id], (c.shape[0], 1, cfg.d_model))
+    z = np.concatenate([start, emb], axis=1)
+    if cfg.context_mode == "sum":
+        return z + ctx[:, : z.shape[1]], None
+    assert cfg.context_mode == "xattn"
+    return z, ctx
 
 
 def token_decoder(W: Weights, cfg, z: np.ndarray, first_pos: int = 0,
-                  caches: Optional[List[LayerCache]] = None) -> np.ndarray:
+                  caches: Optional[List[LayerCache]] = None, enc: Optional[np.ndarray] = None) -> np.ndarray:
     """Token decoder over the local sequence z [B, m, D] at local slots first_pos.. -> LN_f output."""
     pos = np.arange(first_pos, first_pos + z.shape[1])
     return stack_forward(W, "tok", cfg.n_token_layers, z, pos, cfg.n_heads,
-                         cfg.ln_eps, cfg.rope_base, caches, getattr(cfg, "n_kv_heads", 0))
+                         cfg.ln_eps, cfg.rope_base, caches, getattr(cfg, "n_kv_heads", 0), enc)
 
 
 def output_logits(W: Weights, y: np.ndarray) -> np.ndarray:
@@ -265,7 +310,7 @@ def logits_at(W: Weights, cfg, tokens: np.ndarray, positions: Sequence[int]) -> 
     generated ids); t ranges over [L_B, S].  Block k = t // L_B is decoded from
     c_{k-1} and the tokens of block k before t.  Returns [B, len(positions), V].
     """
-    L, P = cfg.block_len, cfg.prefix_len
+    L, lead = cfg.block_len, cfg.lead
     positions = [int(t) for t in positions]
     assert all(L <= t <= tokens.shape[1] for t in positions)
     k_max = max(t // L for t in positions)
@@ -279,12 +324,10 @@ def logits_at(W: Weights, cfg, tokens: np.ndarray, positions: Sequence[int]) -> 
         by_block.setdefault(t // L, []).append(idx)
     for k, idxs in by_block.items():
         o_max = max(positions[i] % L for i in idxs)
-        prefix = prefix_from_context(W, cfg, c[:, k - 1])
-        toks = tokens[:, k * L: k * L + o_max]
-        z = np.concatenate([prefix, W["emb_token"][toks]], axis=1)
-        y = token_decoder(W, cfg, z)
+        z, enc = local_inputs(W, cfg, c[:, k - 1], tokens[:, k * L: k * L + o_max])
+        y = token_decoder(W, cfg, z, enc=enc)
         for i in idxs:
-            out[:, i] = output_logits(W, y[:, P - 1 + positions[i] % L])
+            out[:, i] = output_logits(W, y[:, lead - 1 + positions[i] % L])
     return out
 
 
@@ -302,6 +345,8 @@ class State:
     generated: List[np.ndarray]   # ids emitted so far, each [B]
     kv_reads_block: int = 0       # block-KV entries read by attention (per row, per layer)
     kv_reads_local: int = 0       # local-KV entries read by attention (per row, per layer)
+    summands: Optional[np.ndarray] = None   # "sum": u_0..u_{L-1} of the current block [B, L, D]
+    enc: Optional[np.ndarray] = None        # "xattn": encoder states of the current block [B, P, D]
 
     @property
     def block_kv_len(self) -> int:
@@ -313,16 +358,18 @@ class State:
 
 
 def _new_prefix_pass(W: Weights, cfg, st: State, c_last: np.ndarray) -> np.ndarray:
-    """Reset the local caches, run the token decoder on the P prefix slots, return logits of slot P-1.
+    """Reset the local caches, run the token decoder on the lead slots (P prefix vectors, or the
+    start slot), return the logits of the last one.
     (Token-level transformer: the context embedding goes straight to the classifier.)"""
     if is_vanilla(cfg):
         return output_logits(W, c_last)
-    P = cfg.prefix_len
+    lead = cfg.lead
     st.local_caches = [LayerCache() for _ in range(cfg.n_token_layers)]
-    prefix = prefix_from_context(W, cfg, c_last)
-    y = token_decoder(W, cfg, prefix, 0, st.local_caches)
-    st.kv_reads_local += P * (P + 1) // 2
-    return output_logits(W, y[:, P - 1])
+    z, st.enc = local_inputs(W, cfg, c_last, np.zeros((c_last.shape[0], 0), np.int64))
+    st.summands = prefix_from_context(W, cfg, c_last) if cfg.context_mode == "sum" else None
+    y = token_decoder(W, cfg, z, 0, st.local_caches, st.enc)
+    st.kv_reads_local += lead * (lead + 1) // 2
+    return output_logits(W, y[:, lead - 1])
 
 
 def prefill(W: Weights, cfg, prompt: np.ndarray):
@@ -338,7 +385,7 @@ def prefill(W: Weights, cfg, prompt: np.ndarray):
 
 def decode_step(W: Weights, cfg, st: State, prev: np.ndarray) -> np.ndarray:
     """Feed back the previous id and return the logits of the next token."""
-    L, P = cfg.block_len, cfg.prefix_len
+    L, lead = cfg.block_len, cfg.lead
     st.generated.append(np.asarray(prev, dtype=np.int64))
     g = len(st.generated)                 # index of the token being predicted
     j = g % L                             # its offset within its block
@@ -351,10 +398,12 @@ def decode_step(W: Weights, cfg, st: State, prev: np.ndarray) -> np.ndarray:
         st.kv_reads_block += n + 1
         st.n_blocks += 1
         return _new_prefix_pass(W, cfg, st, c[:, -1])
-    # token step at local slot P + j - 1
+    # token step at local slot lead + j - 1
     z = W["emb_token"][st.generated[-1]][:, None, :]
-    y = token_decoder(W, cfg, z, P + j - 1, st.local_caches)
-    st.kv_reads_local += P + j
+    if cfg.context_mode == "sum":
+        z = z + st.summands[:, j: j + 1]
+    y = token_decoder(W, cfg, z, lead + j - 1, st.local_caches, st.enc)
+    st.kv_reads_local += lead + j
     return output_logits(W, y[:, -1])
 
 

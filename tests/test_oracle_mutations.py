@@ -12,7 +12,8 @@ from tests import test_oracle_pins as pins
 
 _orig = {name: getattr(om, name) for name in
          ["layer_norm", "gelu", "apply_rope", "rope_cos_sin", "causal_attention", "layer_forward",
-          "embed_blocks", "prefix_from_context", "stack_forward", "output_logits", "logits_at"]}
+          "embed_blocks", "prefix_from_context", "stack_forward", "output_logits", "logits_at",
+          "local_inputs"]}
 
 
 def ln_unbiased(x, g, b, eps):
@@ -51,25 +52,26 @@ def attn_scale_slip(q, k, v, q_pos, k_pos):
     return _orig["causal_attention"](q / np.sqrt(q.shape[-1]), k, v, q_pos, k_pos)
 
 
-def layer_sequential(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0):
+def layer_sequential(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0, enc=None):
     # sequential residual: the MLP sees h + attn instead of h
     zero = {k: (np.zeros_like(v) if k.startswith(name + ".mlp") else v) for k, v in W.items()}
-    h1 = _orig["layer_forward"](zero, name, h, pos, n_heads, eps, base, cache, n_kv_heads)
-    zero_attn = {k: (np.zeros_like(v) if k.startswith(name + ".attn") else v) for k, v in W.items()}
-    return _orig["layer_forward"](zero_attn, name, h1, pos, n_heads, eps, base, None, n_kv_heads)
+    h1 = _orig["layer_forward"](zero, name, h, pos, n_heads, eps, base, cache, n_kv_heads, enc)
+    zero_attn = {k: (np.zeros_like(v) if k.startswith((name + ".attn", name + ".xattn")) else v)
+                 for k, v in W.items()}
+    return _orig["layer_forward"](zero_attn, name, h1, pos, n_heads, eps, base, None, n_kv_heads, enc)
 
 
-def layer_no_qkv_bias(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0):
+def layer_no_qkv_bias(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0, enc=None):
     W2 = dict(W)
     W2[f"{name}.attn.qkv.b"] = np.zeros_like(W[f"{name}.attn.qkv.b"])
-    return _orig["layer_forward"](W2, name, h, pos, n_heads, eps, base, cache, n_kv_heads)
+    return _orig["layer_forward"](W2, name, h, pos, n_heads, eps, base, cache, n_kv_heads, enc)
 
 
-def layer_gqa_interleaved(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0):
+def layer_gqa_interleaved(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0, enc=None):
     # grouped-query slip: query head i uses key/value head i mod n_kv_heads instead of i // group
     hkv = n_kv_heads or n_heads
-    if hkv == n_heads:
-        return _orig["layer_forward"](W, name, h, pos, n_heads, eps, base, cache, n_kv_heads)
+    if hkv == n_heads or enc is not None:
+        return _orig["layer_forward"](W, name, h, pos, n_heads, eps, base, cache, n_kv_heads, enc)
     B, n, D = h.shape
     dh = D // n_heads
     a = om.layer_norm(h, W[f"{name}.ln1.g"], W[f"{name}.ln1.b"], eps)
@@ -90,6 +92,42 @@ def layer_gqa_interleaved(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_
     return h + attn + mlp
 
 
+def layer_xattn_query_from_ln2(W, name, h, pos, n_heads, eps, base, cache=None, n_kv_heads=0, enc=None):
+    # cross-attention queries normalised by LN2 (the MLP's LayerNorm) instead of LN1
+    if enc is None:
+        return _orig["layer_forward"](W, name, h, pos, n_heads, eps, base, cache, n_kv_heads, enc)
+    base_out = _orig["layer_forward"](W, name, h, pos, n_heads, eps, base, cache, n_kv_heads, None)
+    B, n, D = h.shape
+    dh = D // n_heads
+    hkv = n_kv_heads or n_heads
+    m = om.layer_norm(h, W[f"{name}.ln2.g"], W[f"{name}.ln2.b"], eps)
+    xq = (m @ W[f"{name}.xattn.q.w"] + W[f"{name}.xattn.q.b"]).reshape(B, n, n_heads, dh)
+    xkv = enc @ W[f"{name}.xattn.kv.w"] + W[f"{name}.xattn.kv.b"]
+    xk = np.repeat(xkv[..., :hkv * dh].reshape(B, -1, hkv, dh), n_heads // hkv, axis=2)
+    xv = np.repeat(xkv[..., hkv * dh:].reshape(B, -1, hkv, dh), n_heads // hkv, axis=2)
+    xo = om.cross_attention(xq, xk, xv).reshape(B, n, D)
+    return base_out + xo @ W[f"{name}.xattn.out.w"] + W[f"{name}.xattn.out.b"]
+
+
+def local_inputs_summand_shift(W, cfg, c, toks):
+    # summation slip: slot i gets u_{i+1} (cyclically) instead of u_i
+    z, enc = _orig["local_inputs"](W, cfg, c, toks)
+    if cfg.context_mode != "sum":
+        return z, enc
+    u = om.prefix_from_context(W, cfg, c)
+    return z - u[:, : z.shape[1]] + np.roll(u, -1, axis=1)[:, : z.shape[1]], enc
+
+
+def local_inputs_zero_start(W, cfg, c, toks):
+    # start slot left empty (zero vector) instead of the pad token's embedding
+    z, enc = _orig["local_inputs"](W, cfg, c, toks)
+    if cfg.context_mode == "prefix":
+        return z, enc
+    z = z.copy()
+    z[:, 0] -= W["emb_token"][cfg.pad_id]
+    return z, enc
+
+
 def embed_reversed(W, cfg, tokens):
     B, S = tokens.shape
     L = cfg.block_len
@@ -102,13 +140,13 @@ def prefix_transposed(W, cfg, c):
     return u.reshape(c.shape[0], cfg.d_model, cfg.prefix_len).transpose(0, 2, 1)
 
 
-def stack_no_final_ln(W, prefix, n_layers, h, pos, n_heads, eps, base, caches=None, n_kv_heads=0):
+def stack_no_final_ln(W, prefix, n_layers, h, pos, n_heads, eps, base, caches=None, n_kv_heads=0, enc=None):
     # the token decoder's output skips its final LayerNorm
     if prefix != "tok":
-        return _orig["stack_forward"](W, prefix, n_layers, h, pos, n_heads, eps, base, caches, n_kv_heads)
+        return _orig["stack_forward"](W, prefix, n_layers, h, pos, n_heads, eps, base, caches, n_kv_heads, enc)
     for l in range(n_layers):
         h = om.layer_forward(W, f"{prefix}.{l}", h, pos, n_heads, eps, base,
-                             None if caches is None else caches[l], n_kv_heads)
+                             None if caches is None else caches[l], n_kv_heads, enc)
     return h
 
 
@@ -155,6 +193,9 @@ MUTATIONS = {
     "context_of_own_block": ("logits_at", logits_own_context),
     "logit_slot_off_by_one": ("logits_at", logits_slot_slip),
     "gqa_heads_interleaved": ("layer_forward", layer_gqa_interleaved),
+    "xattn_query_from_ln2": ("layer_forward", layer_xattn_query_from_ln2),
+    "summand_index_shifted": ("local_inputs", local_inputs_summand_shift),
+    "start_slot_zero": ("local_inputs", local_inputs_zero_start),
 }
 
 PIN_CALLS = [
@@ -170,6 +211,8 @@ PIN_CALLS = [
     lambda: pins.test_incremental_equals_full_recompute(dict(), 30, 13),
     pins.test_causality_bitwise,
     lambda: pins.test_grouped_query_attention_matches_library_and_incremental(2),
+    lambda: pins.test_context_variants_match_library_crosscheck(dict(context_mode="sum", block_len=2)),
+    lambda: pins.test_context_variants_match_library_crosscheck(dict(context_mode="xattn", prefix_len=2)),
 ]
 
 

@@ -322,3 +322,101 @@ def test_vanilla_mode_matches_library_and_incremental():
     full = om.logits_at(W, cfg, seq, range(7, 16))
     assert np.abs(full - lg).max() <= 1e-10
     assert st.block_kv_len == 7 + 8 and st.local_kv_len == 0
+
+
+# ------------------------------------------------------------------ context injection variants
+# §3.4 "The Token Decoder" compares prefix tokens with two alternatives: summation (MEGABYTE) and
+# cross-attention.  Both run a local sequence led by one start slot (the pad token's embedding).
+
+CONTEXT_VARIANTS = [dict(context_mode="sum"), dict(context_mode="sum", block_len=2),
+                    dict(context_mode="xattn", prefix_len=2),
+                    dict(context_mode="xattn", prefix_len=3, n_heads=4, n_kv_heads=2)]
+
+
+@pytest.mark.parametrize("kw", CONTEXT_VARIANTS)
+def test_context_variants_match_library_crosscheck(kw):
+    """Summation and cross-attention injection vs the torch-library formulation, block by block."""
+    cfg = tiny(**kw)
+    W = w64(cfg)
+    L = cfg.block_len
+    x = np.random.default_rng(21).integers(0, cfg.vocab, (2, 4 * L))
+    for k in (1, 2, 3):
+        np.testing.assert_allclose(om.logits_at(W, cfg, x, [k * L + o for o in range(L)]),
+                                   tc.block_logits(W, cfg, x, k), atol=1e-11, rtol=0)
+
+
+@pytest.mark.parametrize("kw", CONTEXT_VARIANTS)
+def test_context_variants_incremental_and_causal(kw):
+    """Incremental decoding == full recompute; the local cache holds the start slot plus the
+    block's tokens; perturbing later tokens leaves earlier logits bit-identical."""
+    cfg = tiny(**kw)
+    W = w64(cfg)
+    prompt = wl.make_prompt(cfg, batch=2, T=11)
+    G = 10
+    ids, lg, st = om.generate(W, cfg, prompt, G, keep_logits=True)
+    seq = np.concatenate([om.pad_prompt(cfg, prompt), ids], axis=1)
+    Tp = seq.shape[1] - G
+    full = om.logits_at(W, cfg, seq, range(Tp, Tp + G))
+    assert np.abs(full - lg).max() <= 1e-10
+    assert cfg.lead == 1 and st.local_kv_len == 1 + (G - 1) % cfg.block_len
+    x = np.random.default_rng(22).integers(0, cfg.vocab, (2, 24))
+    s = 13
+    y = x.copy()
+    y[:, s:] = (y[:, s:] + 57) % cfg.vocab
+    t = np.arange(cfg.block_len, 25)
+    a, b = om.logits_at(W, cfg, x, t), om.logits_at(W, cfg, y, t)
+    np.testing.assert_array_equal(a[:, t <= s], b[:, t <= s])
+    assert np.abs(a[:, t > s] - b[:, t > s]).max() > 1e-6
+
+
+def test_summation_with_one_token_blocks_is_one_prefix_vector():
+    """With L_B = 1 the summation design has one local slot, start + u_0; with a zero pad-token
+    embedding that is u_0 = Proj(c), the single prefix vector of the P = 1 prefix design."""
+    cfg_p = tiny(block_len=1, prefix_len=1)
+    cfg_s = cfg_p.with_(context_mode="sum")
+    W = w64(cfg_p)
+    assert [s for s in wl.weight_specs(cfg_p)] == [s for s in wl.weight_specs(cfg_s)]
+    x = np.random.default_rng(23).integers(1, cfg_p.vocab, (2, 8))
+    t = range(1, 9)
+    assert np.abs(om.logits_at(W, cfg_p, x, t) - om.logits_at(W, cfg_s, x, t)).max() > 1e-6
+    W["emb_token"][cfg_p.pad_id] = 0.0
+    np.testing.assert_array_equal(om.logits_at(W, cfg_p, x, t), om.logits_at(W, cfg_s, x, t))
+
+
+def test_cross_attention_over_one_state_ignores_the_query():
+    """With P = 1 the cross-attention softmax has a single term of weight exactly 1, so the branch
+    adds the projected value whatever the queries: new query weights leave the logits bit-identical,
+    new value biases do not."""
+    cfg = tiny(context_mode="xattn", prefix_len=1)
+    W = w64(cfg)
+    rng = np.random.default_rng(24)
+    x = rng.integers(0, cfg.vocab, (2, 16))
+    t = range(4, 17)
+    ref = om.logits_at(W, cfg, x, t)
+    Wq, Wv = dict(W), dict(W)
+    kvw = cfg.kv_heads * cfg.d_head
+    for l in range(cfg.n_token_layers):
+        Wq[f"tok.{l}.xattn.q.w"] = rng.standard_normal(W[f"tok.{l}.xattn.q.w"].shape)
+        Wq[f"tok.{l}.xattn.q.b"] = rng.standard_normal(W[f"tok.{l}.xattn.q.b"].shape)
+        Wv[f"tok.{l}.xattn.kv.b"] = W[f"tok.{l}.xattn.kv.b"] + np.r_[np.zeros(kvw), np.full(kvw, 0.5)]
+    np.testing.assert_array_equal(om.logits_at(Wq, cfg, x, t), ref)
+    assert np.abs(om.logits_at(Wv, cfg, x, t) - ref).max() > 1e-6
+
+
+def test_cross_attention_with_equal_scores_averages_the_values():
+    """A zero query projection gives every encoder state the same score, so the cross-attention
+    branch of a layer is the mean of the P projected values through the output projection."""
+    cfg = tiny(context_mode="xattn", prefix_len=3)
+    W = w64(cfg)
+    rng = np.random.default_rng(25)
+    name, D = "tok.0", cfg.d_model
+    W[f"{name}.xattn.q.w"] = np.zeros_like(W[f"{name}.xattn.q.w"])
+    W[f"{name}.xattn.q.b"] = np.zeros_like(W[f"{name}.xattn.q.b"])
+    h = rng.standard_normal((2, 5, D))
+    enc = rng.standard_normal((2, 3, D))
+    pos = np.arange(5)
+    args = (W, name, h, pos, cfg.n_heads, cfg.ln_eps, cfg.rope_base)
+    branch = om.layer_forward(*args, None, 0, enc) - om.layer_forward(*args)
+    v = enc @ W[f"{name}.xattn.kv.w"][:, D:] + W[f"{name}.xattn.kv.b"][D:]     # [2, P, D] values
+    want = v.mean(axis=1) @ W[f"{name}.xattn.out.w"] + W[f"{name}.xattn.out.b"]
+    np.testing.assert_allclose(branch, np.broadcast_to(want[:, None], branch.shape), atol=1e-12, rtol=0)
