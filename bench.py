@@ -32,7 +32,8 @@ def log(msg):
 def describe(cfg):
     return (f"{cfg.name}: Block Transformer d={cfg.d_model} {cfg.n_block_layers}+{cfg.n_token_layers} layers "
             f"H={cfg.n_heads}{'' if cfg.kv_heads == cfg.n_heads else f' H_kv={cfg.kv_heads}'} MLP={cfg.d_mlp} "
-            f"L_B={cfg.block_len} P={cfg.prefix_len} V={cfg.vocab}, "
+            f"L_B={cfg.block_len} P={cfg.prefix_len} V={cfg.vocab}"
+            f"{'' if cfg.context_mode == 'prefix' else f' context={cfg.context_mode}'}, "
             f"batch {cfg.batch}, {cfg.prompt_len}-token prompt, {cfg.gen_len} generated")
 
 

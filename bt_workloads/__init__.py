@@ -130,6 +130,11 @@ CONFIGS: Dict[str, Config] = {
                                    batch=256, prompt_len=128, gen_len=2048, n_kv_heads=4),
     "f4_mqa_decode_heavy": Config("f4_mqa_decode_heavy", "bf16", **_D768, block_len=4, prefix_len=1,
                                   batch=256, prompt_len=128, gen_len=2048, n_kv_heads=1),
+    # context injection by summation (L_B = 4 summands) and by cross-attention (2 encoder states)
+    "f4_sum_decode_heavy": Config("f4_sum_decode_heavy", "bf16", **_D768, block_len=4, prefix_len=1,
+                                  batch=256, prompt_len=128, gen_len=2048, context_mode="sum"),
+    "f4_xattn_decode_heavy": Config("f4_xattn_decode_heavy", "bf16", **_D768, block_len=4, prefix_len=2,
+                                    batch=256, prompt_len=128, gen_len=2048, context_mode="xattn"),
     # a context beyond 8K: 32768-token prompts (8192 prompt blocks at L_B = 4)
     "f4_long32k_lb4": Config("f4_long32k_lb4", "bf16", **_D768, block_len=4, prefix_len=2,
                              batch=8, prompt_len=32768, gen_len=256),

@@ -21,8 +21,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libbt.so")
 
 BT_FP32, BT_BF16 = 0, 1
+# bt_context_mode values of the workload names
+CONTEXT_MODES = {"prefix": 0, "sum": 1, "xattn": 2}
+
 PROFILE_KINDS = ["embed", "layernorm", "gemm_qkv_up", "gemm_out_down", "gemm_prefix", "gemm_head",
-                 "attn_prefill", "rope_scatter", "attn_block_decode", "attn_local", "finalize"]
+                 "attn_prefill", "rope_scatter", "attn_block_decode", "attn_local", "finalize", "attn_cross"]
 
 
 class BtError(RuntimeError):
@@ -37,7 +40,7 @@ class BtConfig(ctypes.Structure):
                 ("block_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32), ("pad_id", ctypes.c_int32),
                 ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("max_prompt_tokens", ctypes.c_int32),
-                ("n_kv_heads", ctypes.c_int32)]
+                ("n_kv_heads", ctypes.c_int32), ("context_mode", ctypes.c_int32)]
 
     @classmethod
     def make(cls, model, max_batch: int, max_tokens: int, max_prompt_tokens: int = 0) -> "BtConfig":
@@ -45,7 +48,8 @@ class BtConfig(ctypes.Structure):
         return cls(model.vocab, model.d_model, model.n_heads, model.d_mlp, model.n_block_layers,
                    model.n_token_layers, model.block_len, model.prefix_len, max_batch, max_tokens,
                    BT_FP32 if model.dtype == "fp32" else BT_BF16, model.pad_id, model.ln_eps, model.rope_base,
-                   max_prompt_tokens, getattr(model, "n_kv_heads", 0))
+                   max_prompt_tokens, getattr(model, "n_kv_heads", 0),
+                   CONTEXT_MODES[getattr(model, "context_mode", "prefix")])
 
 
 _lib = None
@@ -100,7 +104,9 @@ def weight_names(model) -> List[str]:
     if model.n_token_layers == 0:  # token-level transformer
         return names + ["head.w"]
     names += ["prefix.w", "prefix.b", "emb_token"]
-    names += [f"tok.{l}.{n}" for l in range(model.n_token_layers) for n in layer]
+    xattn = ["xattn.q.w", "xattn.q.b", "xattn.kv.w", "xattn.kv.b", "xattn.out.w", "xattn.out.b"]
+    tok_layer = layer + (xattn if getattr(model, "context_mode", "prefix") == "xattn" else [])
+    names += [f"tok.{l}.{n}" for l in range(model.n_token_layers) for n in tok_layer]
     names += ["tok.lnf.g", "tok.lnf.b", "head.w"]
     return names
 

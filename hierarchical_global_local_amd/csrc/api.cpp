@@ -56,6 +56,11 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
     return "max_prompt_tokens must be in [0, max_tokens]";
   if (c.n_kv_heads < 0 || c.n_kv_heads > c.n_heads || (c.n_kv_heads > 0 && c.n_heads % c.n_kv_heads))
     return "n_kv_heads must be 0 or a divisor of n_heads";
+  if (c.pad_id < 0 || c.pad_id >= c.vocab) return "pad_id must be in [0, vocab)";
+  if (c.context_mode < BT_CTX_PREFIX || c.context_mode > BT_CTX_XATTN)
+    return "context_mode must be BT_CTX_PREFIX, BT_CTX_SUM or BT_CTX_XATTN";
+  if (c.n_token_layers == 0 && c.context_mode != BT_CTX_PREFIX)
+    return "context_mode needs a token decoder (n_token_layers >= 1)";
   const int max_prompt = c.max_prompt_tokens > 0 ? c.max_prompt_tokens : c.max_tokens;
   const int nblk_prompt = std::max(1, (max_prompt + c.block_len - 1) / c.block_len);
 
@@ -68,6 +73,9 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.F = c.d_mlp;
   lo.L = c.block_len;
   lo.P = c.prefix_len;
+  lo.mode = c.context_mode;
+  lo.lead = lo.mode == BT_CTX_PREFIX ? lo.P : 1;
+  lo.NC = lo.mode == BT_CTX_SUM ? lo.L : lo.P;
   lo.Nb = c.n_block_layers;
   lo.Nt = c.n_token_layers;
   lo.De = c.d_model / c.block_len;
@@ -78,7 +86,7 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.elem = f32 ? 4 : 2;
   lo.tab_elem = f32 ? 4 : 2;
   lo.ncap = (int)align_up((size_t)nblk, 64);
-  lo.lcap = lo.P + lo.L;
+  lo.lcap = lo.lead + lo.L;
   lo.npos = std::max(lo.ncap, lo.lcap);
   lo.Vpad = (int)align_up((size_t)lo.V, 128);
   lo.max_prompt = nblk_prompt * lo.L;  // prompts up to this padded length fit the activations
@@ -90,23 +98,29 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   size_t o = 0;
   auto take = [&](size_t n) { size_t r = o; o += n * TE; return r; };
   lo.bl_emb_block = take(V * lo.De);
-  auto blob_layer = [&]() {
+  const bool xattn = lo.mode == BT_CTX_XATTN;
+  const size_t KVW = (size_t)lo.Hkv * dh, NC = lo.NC;
+  auto blob_layer = [&](bool with_xattn) {
     Layout::BlobLayer b;
     b.ln1g = take(D); b.ln1b = take(D); b.qkvw = take(D * QW); b.qkvb = take(QW);
     b.outw = take(D * D); b.outb = take(D); b.ln2g = take(D); b.ln2b = take(D);
     b.upw = take(D * F); b.upb = take(F); b.downw = take(F * D); b.downb = take(D);
+    if (with_xattn) {
+      b.xqw = take(D * D); b.xqb = take(D); b.xkvw = take(D * 2 * KVW); b.xkvb = take(2 * KVW);
+      b.xow = take(D * D); b.xob = take(D);
+    }
     return b;
   };
   lo.bl_blk.clear();
   lo.bl_tok.clear();
-  for (int l = 0; l < lo.Nb; ++l) lo.bl_blk.push_back(blob_layer());
+  for (int l = 0; l < lo.Nb; ++l) lo.bl_blk.push_back(blob_layer(false));
   lo.bl_lnf_blk_g = take(D);
   lo.bl_lnf_blk_b = take(D);
   if (!lo.vanilla) {  // a token-level transformer has no prefix projection and no token decoder
-    lo.bl_prefix_w = take(D * P * D);
-    lo.bl_prefix_b = take(P * D);
+    lo.bl_prefix_w = take(D * NC * D);
+    lo.bl_prefix_b = take(NC * D);
     lo.bl_emb_tok = take(V * D);
-    for (int l = 0; l < lo.Nt; ++l) lo.bl_tok.push_back(blob_layer());
+    for (int l = 0; l < lo.Nt; ++l) lo.bl_tok.push_back(blob_layer(xattn));
     lo.bl_lnf_tok_g = take(D);
     lo.bl_lnf_tok_b = take(D);
   }
@@ -122,22 +136,26 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.head = region((size_t)lo.Vpad * D * E);
   lo.lnf_blk = region(2 * D * 4);
   lo.lnf_tok = region(tokw * 2 * D * 4);
-  lo.prefix_w = region(tokw * P * D * D * E);
-  lo.prefix_b = region(tokw * P * D * 4);
+  lo.prefix_w = region(tokw * NC * D * D * E);
+  lo.prefix_b = region(tokw * NC * D * 4);
   lo.rope = region((size_t)lo.npos * (lo.dh / 2) * sizeof(float2));
-  auto layer = [&]() {
+  auto layer = [&](bool with_xattn) {
     LayerOff L;
+    L.n1 = (int)(QW + (with_xattn ? D : 0));
+    L.k2 = (int)(D + F + (with_xattn ? D : 0));
     L.ln = region(4 * D * 4);
-    L.w1 = region((QW + F) * D * E);
-    L.b1 = region((QW + F) * 4);
-    L.w2 = region(D * (D + F) * E);
-    L.b2 = region(2 * D * 4);
+    L.w1 = region((L.n1 + F) * D * E);
+    L.b1 = region((L.n1 + F) * 4);
+    L.w2 = region(D * L.k2 * E);
+    L.b2 = region(3 * D * 4);
     return L;
   };
   lo.blk.clear();
   lo.tok.clear();
-  for (int l = 0; l < lo.Nb; ++l) lo.blk.push_back(layer());
-  for (int l = 0; l < lo.Nt; ++l) lo.tok.push_back(layer());
+  for (int l = 0; l < lo.Nb; ++l) lo.blk.push_back(layer(false));
+  for (int l = 0; l < lo.Nt; ++l) lo.tok.push_back(layer(xattn));
+  lo.maxN1 = (int)QW + (xattn ? lo.D : 0);
+  lo.maxK2 = lo.D + lo.F + (xattn ? lo.D : 0);
   lo.block_kv_bytes = (size_t)lo.Nb * 2 * lo.Bmax * lo.Hkv * lo.ncap * lo.dh * E;
   lo.local_kv_bytes = (size_t)lo.Nt * 2 * lo.Bmax * lo.Hkv * lo.lcap * lo.dh * E;  // 0 for Nt = 0
   lo.block_kv = region(lo.block_kv_bytes);
@@ -145,8 +163,8 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   const size_t M = (size_t)lo.Mmax;
   lo.X = region(M * D * 4);
   lo.LN = region(2 * (size_t)lo.Mpad * D * E);
-  lo.QKV = region(M * QW * E);
-  lo.ACT = region((size_t)lo.Mpad * (D + F) * E);
+  lo.QKV = region(M * lo.maxN1 * E);
+  lo.ACT = region((size_t)lo.Mpad * lo.maxK2 * E);
   // split-KV partials [B][H][nsplit][dh + 2] for the largest B * nsplit any batch size uses
   lo.part_bytes = 0;
   for (int b = 1; b <= lo.Bmax; ++b) {
@@ -155,6 +173,16 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   }
   lo.part = region(lo.part_bytes);
   lo.keys = region((size_t)lo.Bmax * (lo.Vpad / 4 + 64) * 8);
+  const bool start_slot = !lo.vanilla && lo.mode != BT_CTX_PREFIX;
+  const size_t encr = xattn ? (size_t)lo.Bmax * P : 0;  // encoder-state rows
+  lo.xkv_ld = xattn ? (int)(lo.Nt * 2 * KVW) : 0;
+  lo.pad_emb = region(start_slot ? D * 4 : 0);
+  lo.ctx = region(lo.mode == BT_CTX_SUM ? (size_t)lo.Bmax * lo.L * D * 4 : 0);
+  lo.enc = region(encr * D * 4);
+  lo.enc16 = region(f32 ? 0 : align_up(encr, 16) * D * E);
+  lo.xkv_w = region((size_t)lo.xkv_ld * D * E);
+  lo.xkv_b = region((size_t)lo.xkv_ld * 4);
+  lo.xkv = region(encr * lo.xkv_ld * 4);
   lo.rpart_rows = (int)std::min<int64_t>(lo.Mmax, 1024);
   lo.rpart = region((size_t)16 * lo.rpart_rows * D * 4);
   lo.cur = region((size_t)lo.Bmax * lo.L * 4);
@@ -196,7 +224,8 @@ struct bt_handle {
 namespace {
 
 enum ProfKind { PK_EMBED = 0, PK_LN, PK_GEMM_QKV, PK_GEMM_OUT, PK_GEMM_PREFIX, PK_GEMM_HEAD, PK_ATTN_PREFILL,
-                PK_ROPE_SCATTER, PK_ATTN_DECODE, PK_ATTN_LOCAL, PK_FINALIZE, PK_COUNT };
+                PK_ROPE_SCATTER, PK_ATTN_DECODE, PK_ATTN_LOCAL, PK_FINALIZE, PK_ATTN_CROSS, PK_COUNT };
+static_assert(PK_COUNT == BT_PROFILE_KINDS, "profiler classes");
 
 // Records a pair of events around one launch with its algorithmic bytes and flops (the minimal
 // traffic and arithmetic of the operation, independent of how the kernel achieves it).
@@ -275,10 +304,10 @@ Epi qkv_epi(bt_handle* h, const LayerOff& w) {
   ep.wscale = wscale(lo);
   ep.bias = (const float*)P_(h, w.b1);
   ep.out0 = P_(h, lo.QKV);
-  ep.ld0 = lo.QW;
+  ep.ld0 = w.n1;
   ep.out1 = P_(h, lo.ACT);
-  ep.ld1 = lo.D + lo.F;
-  ep.n_split = lo.QW;
+  ep.ld1 = w.k2;
+  ep.n_split = w.n1;
   ep.act_col0 = lo.D;
   return ep;
 }
@@ -288,7 +317,7 @@ Epi qkv_epi(bt_handle* h, const LayerOff& w) {
 int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows, bool ln_done = false) {
   const Layout& lo = h->lo;
   const float* lnp = (const float*)P_(h, w.ln);
-  const double E = (double)lo.elem, D = lo.D, N1 = (double)lo.QW + lo.F;
+  const double E = (double)lo.elem, D = lo.D, N1 = (double)w.n1 + lo.F;
   if (!ln_done) {
     Prof p(h, PK_LN, rows * D * (4.0 + 2.0 * E), 8.0 * rows * D);
     BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), rows, lo.D, 1, 0, lnp, ln_buf(h, 0), lnp + 2 * lo.D,
@@ -298,13 +327,13 @@ int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows, bool ln_done = false) 
   }
   const Epi ep = qkv_epi(h, w);
   Prof p(h, PK_GEMM_QKV, N1 * D * E + 2.0 * rows * D * E + rows * N1 * E + N1 * 4.0, 2.0 * rows * N1 * D);
-  BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), rows, lo.QW + lo.F, lo.D,
+  BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), rows, w.n1 + lo.F, lo.D,
                           EPI_QKV_GELU, ep, h->st),
            "gemm qkv|up");
   return BT_OK;
 }
 
-// [attn | gelu(up)] x [W_o ; W_down] + b_o + b_down added into the residual stream
+// [attn | gelu(up) (| cross-attention)] x [W_o ; W_down (; W_xo)] + biases added into the residual stream
 int run_out(bt_handle* h, const LayerOff& w, int rows) {
   const Layout& lo = h->lo;
   Epi ep{};
@@ -313,7 +342,7 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
   ep.bias2 = (const float*)P_(h, w.b2) + lo.D;
   ep.out0 = P_(h, lo.X);
   ep.ld0 = lo.D;
-  ep.splits = rows <= lo.rpart_rows ? resid_splits(rows, lo.D, lo.D + lo.F) : 1;
+  ep.splits = rows <= lo.rpart_rows ? resid_splits(rows, lo.D, w.k2) : 1;
   ep.part = (float*)P_(h, lo.rpart);
   if (ep.splits > 1) {
     // the partial products are summed (with both biases) by the next LayerNorm
@@ -323,9 +352,9 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
     h->pending.bias_a = ep.bias;
     h->pending.bias_b = ep.bias2;
   }
-  const double E = (double)lo.elem, D = lo.D, K2 = (double)lo.D + lo.F;
+  const double E = (double)lo.elem, D = lo.D, K2 = w.k2;
   Prof p(h, PK_GEMM_OUT, D * K2 * E + rows * K2 * E + 8.0 * rows * D + 8.0 * D, 2.0 * rows * D * K2);
-  BT_CHECK(h, launch_gemm(lo.f32, P_(h, lo.ACT), nullptr, lo.D + lo.F, P_(h, w.w2), rows, lo.D, lo.D + lo.F,
+  BT_CHECK(h, launch_gemm(lo.f32, P_(h, lo.ACT), nullptr, w.k2, P_(h, w.w2), rows, lo.D, w.k2,
                           EPI_RESID, ep, h->st),
            "gemm out|down");
   return BT_OK;
@@ -345,10 +374,20 @@ int run_token_decoder(bt_handle* h, int m, int s0, bool first_ln_done = false) {
       // cached K/V read, q|k|v read, new K/V and the output written
       Prof p(h, PK_ATTN_LOCAL, (Bd * s0 * 2.0 * KVW + 2.0 * rows * (D + 2.0 * KVW)) * E,
              4.0 * Bd * lo.H * lo.dh * pairs);
-      BT_CHECK(h, launch_local_attention(lo.f32, P_(h, lo.QKV), h->B, m, s0, lo.H, lo.Hkv, lo.dh,
+      BT_CHECK(h, launch_local_attention(lo.f32, P_(h, lo.QKV), lo.tok[l].n1, h->B, m, s0, lo.H, lo.Hkv, lo.dh,
                                          (const float2*)P_(h, lo.rope), local_k(h, l), local_v(h, l), lo.lcap,
-                                         P_(h, lo.ACT), lo.D + lo.F, h->st),
+                                         P_(h, lo.ACT), lo.tok[l].k2, h->st),
                "local attention");
+    }
+    if (lo.mode == BT_CTX_XATTN) {
+      // one local slot per row (the local sequence starts with a single start slot)
+      if (m != 1) return fail(BT_ERR_INVALID_ARG, "cross-attention runs one local slot per row");
+      const double E = (double)lo.elem, D = lo.D, Bd = h->B, KVW = (double)lo.Hkv * lo.dh;
+      Prof p(h, PK_ATTN_CROSS, Bd * (lo.P * 2.0 * KVW * 4.0 + 2.0 * D * E), 4.0 * Bd * lo.H * lo.dh * lo.P);
+      BT_CHECK(h, launch_cross_attention(lo.f32, P_(h, lo.QKV), lo.tok[l].n1, lo.QW, h->B, lo.H, lo.Hkv, lo.dh,
+                                         (const float*)P_(h, lo.xkv), lo.xkv_ld, l * 2 * lo.Hkv * lo.dh, lo.P,
+                                         P_(h, lo.ACT), lo.tok[l].k2, lo.D + lo.F, h->st),
+               "cross attention");
     }
     r = run_out(h, lo.tok[l], rows);
     if (r) return r;
@@ -403,6 +442,11 @@ int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
   nx.D = lo.D;
   nx.V = lo.V;
   nx.eps = h->cfg.ln_eps;
+  if (lo.mode == BT_CTX_SUM && !next_is_block) {
+    // summation: the next slot, (g + 1) % L, also takes its projected summand
+    nx.add = (const float*)P_(h, lo.ctx) + (size_t)((h->g + 1) % lo.L) * lo.D;
+    nx.add_ld = lo.L * lo.D;
+  }
   Prof p(h, PK_FINALIZE, (double)h->B * (16.0 + lo.D * (lo.tab_elem + 4.0 + 2.0 * lo.elem)), 0.0);
   BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->head_nparts, lo.Vpad / 4 + 64, h->B, d_next,
                               (int32_t*)P_(h, lo.cur), lo.L, j, (int*)P_(h, lo.dstate), n_inc, nx, h->st),
@@ -410,10 +454,14 @@ int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
   return BT_OK;
 }
 
-// context embedding of rows (b, slot) of X [B][m][D] -> prefix rows X [B][P][D]
+// Context embedding of rows (b, slot) of X [B][m][D] -> the token decoder's lead slots:
+//   prefix: the P projected vectors become rows X [B][P][D];
+//   summation: the L_B projected vectors go to CTX [B][L][D], and X [B][D] = pad embedding + u_0;
+//   cross-attention: the P projected vectors go to ENC [B*P][D], their keys and values for every
+//   token layer to XKV [B*P][Nt * 2 Hkv dh], and X [B][D] = pad embedding.
 int run_prefix(bt_handle* h, int m, int slot) {
   const Layout& lo = h->lo;
-  const double E = (double)lo.elem, D = lo.D, Bd = h->B, PD = (double)lo.P * lo.D;
+  const double E = (double)lo.elem, D = lo.D, Bd = h->B, PD = (double)lo.NC * lo.D;
   {
     Prof p(h, PK_LN, Bd * D * (4.0 + E), 8.0 * Bd * D);
     BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), h->B, lo.D, m, slot, (const float*)P_(h, lo.lnf_blk),
@@ -424,12 +472,40 @@ int run_prefix(bt_handle* h, int m, int slot) {
   Epi ep{};
   ep.wscale = wscale(lo);
   ep.bias = (const float*)P_(h, lo.prefix_b);
-  ep.out0 = P_(h, lo.X);
-  ep.ld0 = lo.P * lo.D;
-  Prof p(h, PK_GEMM_PREFIX, PD * D * E + Bd * D * E + Bd * PD * 4.0 + PD * 4.0, 2.0 * Bd * PD * D);
-  BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.prefix_w), h->B, lo.P * lo.D, lo.D, EPI_STORE,
-                          ep, h->st),
-           "prefix projection");
+  ep.out0 = P_(h, lo.mode == BT_CTX_PREFIX ? lo.X : lo.mode == BT_CTX_SUM ? lo.ctx : lo.enc);
+  ep.ld0 = lo.NC * lo.D;
+  {
+    Prof p(h, PK_GEMM_PREFIX, PD * D * E + Bd * D * E + Bd * PD * 4.0 + PD * 4.0, 2.0 * Bd * PD * D);
+    BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.prefix_w), h->B, lo.NC * lo.D, lo.D,
+                            EPI_STORE, ep, h->st),
+             "context projection");
+  }
+  if (lo.mode == BT_CTX_XATTN) {
+    const int rows = h->B * lo.P;
+    const double R = rows, N = lo.xkv_ld;
+    Prof p(h, PK_GEMM_PREFIX, N * D * E + R * D * (4.0 + E) + R * N * 4.0 + N * 4.0, 2.0 * R * N * D);
+    const void* A = P_(h, lo.enc);
+    if (!lo.f32) {
+      // encoder states as an fp16 operand in fragment order (rows padded to 16 with zeros)
+      BT_CHECK(h, launch_pack_frag(P_(h, lo.enc), false, lo.D, 1, rows, (int)align_up(rows, 16), lo.D,
+                                   P_(h, lo.enc16), lo.D, 0, 0, 1.0f, h->st),
+               "encoder states");
+      A = P_(h, lo.enc16);
+    }
+    Epi ex{};
+    ex.wscale = wscale(lo);
+    ex.bias = (const float*)P_(h, lo.xkv_b);
+    ex.out0 = P_(h, lo.xkv);
+    ex.ld0 = lo.xkv_ld;
+    BT_CHECK(h, launch_gemm(lo.f32, A, nullptr, lo.D, P_(h, lo.xkv_w), rows, lo.xkv_ld, lo.D, EPI_STORE, ex, h->st),
+             "cross-attention keys and values");
+  }
+  if (lo.mode != BT_CTX_PREFIX) {
+    Prof p(h, PK_EMBED, Bd * D * (lo.mode == BT_CTX_SUM ? 12.0 : 8.0), 0.0);
+    BT_CHECK(h, launch_rows_init((float*)P_(h, lo.X), h->B, lo.D, (const float*)P_(h, lo.pad_emb),
+                                 lo.mode == BT_CTX_SUM ? (const float*)P_(h, lo.ctx) : nullptr, lo.L * lo.D, h->st),
+             "start slot");
+  }
   return BT_OK;
 }
 
@@ -445,9 +521,9 @@ void drop_graphs(bt_handle* h) {
 void advance_host_state(bt_handle* h, int j) {
   if (j == 0) {
     h->n_blocks += 1;
-    h->local_len = h->lo.vanilla ? 0 : h->lo.P;
+    h->local_len = h->lo.vanilla ? 0 : h->lo.lead;
   } else {
-    h->local_len = h->lo.P + j;
+    h->local_len = h->lo.lead + j;
   }
   h->pending.nsplit = 0;
 }
@@ -457,7 +533,7 @@ void advance_host_state(bt_handle* h, int j) {
 // device, so the same launch sequence is valid for every step with this j.
 int enqueue_decode(bt_handle* h, int j, float* d_logits) {
   const Layout& lo = h->lo;
-  const int L = lo.L, P = lo.P;
+  const int lead = lo.lead;
   const double E = (double)lo.elem, Dd = lo.D, Bd = h->B, KVW = (double)lo.Hkv * lo.dh;
   int r;
   if (j == 0) {
@@ -473,7 +549,7 @@ int enqueue_decode(bt_handle* h, int j, float* d_logits) {
                4.0 * Bd * lo.H * lo.dh * (double)(n + 1));
         BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,
                                              lo.Hkv, lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l),
-                                             lo.ncap, P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part),
+                                             lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, (float*)P_(h, lo.part),
                                              lo.part_bytes, h->dec_nsplit, h->st),
                  "block attention decode");
       }
@@ -483,13 +559,13 @@ int enqueue_decode(bt_handle* h, int j, float* d_logits) {
       if ((r = run_head(h, 1, 0, d_logits))) return r;
     } else {
       if ((r = run_prefix(h, 1, 0))) return r;
-      if ((r = run_token_decoder(h, P, 0))) return r;
-      if ((r = run_head(h, P, P - 1, d_logits))) return r;
+      if ((r = run_token_decoder(h, lead, 0))) return r;
+      if ((r = run_head(h, lead, lead - 1, d_logits))) return r;
     }
   } else {
-    // one token-decoder position at local slot P + j - 1 (input row and first LayerNorms written
+    // one token-decoder position at local slot lead + j - 1 (input row and first LayerNorms written
     // by the previous finalisation)
-    if ((r = run_token_decoder(h, 1, P + j - 1, true))) return r;
+    if ((r = run_token_decoder(h, 1, lead + j - 1, true))) return r;
     if ((r = run_head(h, 1, 0, d_logits))) return r;
   }
   advance_host_state(h, j);
@@ -576,39 +652,50 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     INIT_CHECK(hipMemcpyAsync(h->ws + lo.emb_tok, wb + lo.bl_emb_tok, (size_t)lo.V * D * lo.tab_elem,
                               hipMemcpyDeviceToDevice, h->st),
                "copy");
-  auto repack_layer = [&](const Layout::BlobLayer& s, const LayerOff& d) -> hipError_t {
+  // one [in, out] canonical matrix into rows [row0, row0 + N) and columns [col0, col0 + K) of a
+  // repacked [rows][Ktot] weight (element (n = out, k = in) at src[k * N + n])
+  auto put = [&](size_t src, int K, int N, size_t dst, int Ktot, int row0, int col0) -> hipError_t {
+    if (f32) return launch_transpose_convert(wb + src, bf, K, N, h->ws + dst, f32, Ktot, row0, col0, sc, h->st);
+    return launch_pack_frag(wb + src, bf, 1, N, N, N, K, h->ws + dst, Ktot, row0, col0, sc, h->st);
+  };
+  // xl: index of a token layer with a cross-attention branch, else -1
+  auto repack_layer = [&](const Layout::BlobLayer& s, const LayerOff& d, int xl) -> hipError_t {
     hipError_t err;
     float* ln = (float*)(h->ws + d.ln);
     if ((err = launch_to_f32(wb + s.ln1g, bf, D, ln, h->st))) return err;
     if ((err = launch_to_f32(wb + s.ln1b, bf, D, ln + D, h->st))) return err;
     if ((err = launch_to_f32(wb + s.ln2g, bf, D, ln + 2 * D, h->st))) return err;
     if ((err = launch_to_f32(wb + s.ln2b, bf, D, ln + 3 * D, h->st))) return err;
-    // canonical [in, out] matrices: element (n = out, k = in) at src[k * out + n]
-    if (f32) {
-      if ((err = launch_transpose_convert(wb + s.qkvw, bf, D, QW, h->ws + d.w1, f32, D, 0, 0, sc, h->st))) return err;
-      if ((err = launch_transpose_convert(wb + s.upw, bf, D, F, h->ws + d.w1, f32, D, QW, 0, sc, h->st))) return err;
-    } else {
-      if ((err = launch_pack_frag(wb + s.qkvw, bf, 1, QW, QW, QW, D, h->ws + d.w1, D, 0, 0, sc, h->st))) return err;
-      if ((err = launch_pack_frag(wb + s.upw, bf, 1, F, F, F, D, h->ws + d.w1, D, QW, 0, sc, h->st))) return err;
-    }
+    // w1 rows: q | k | v (| cross-attention q) | up
+    if ((err = put(s.qkvw, D, QW, d.w1, D, 0, 0))) return err;
+    if (xl >= 0 && (err = put(s.xqw, D, D, d.w1, D, QW, 0))) return err;
+    if ((err = put(s.upw, D, F, d.w1, D, d.n1, 0))) return err;
     float* b1 = (float*)(h->ws + d.b1);
     if ((err = launch_to_f32(wb + s.qkvb, bf, QW, b1, h->st))) return err;
-    if ((err = launch_to_f32(wb + s.upb, bf, F, b1 + QW, h->st))) return err;
-    if (f32) {
-      if ((err = launch_transpose_convert(wb + s.outw, bf, D, D, h->ws + d.w2, f32, D + F, 0, 0, sc, h->st)))
-        return err;
-      if ((err = launch_transpose_convert(wb + s.downw, bf, F, D, h->ws + d.w2, f32, D + F, 0, D, sc, h->st)))
-        return err;
-    } else {
-      if ((err = launch_pack_frag(wb + s.outw, bf, 1, D, D, D, D, h->ws + d.w2, D + F, 0, 0, sc, h->st))) return err;
-      if ((err = launch_pack_frag(wb + s.downw, bf, 1, D, D, D, F, h->ws + d.w2, D + F, 0, D, sc, h->st))) return err;
-    }
+    if (xl >= 0 && (err = launch_to_f32(wb + s.xqb, bf, D, b1 + QW, h->st))) return err;
+    if ((err = launch_to_f32(wb + s.upb, bf, F, b1 + d.n1, h->st))) return err;
+    // w2 columns: attn.out | mlp.down (| cross-attention out)
+    if ((err = put(s.outw, D, D, d.w2, d.k2, 0, 0))) return err;
+    if ((err = put(s.downw, F, D, d.w2, d.k2, 0, D))) return err;
+    if (xl >= 0 && (err = put(s.xow, D, D, d.w2, d.k2, 0, D + F))) return err;
     float* b2 = (float*)(h->ws + d.b2);
     if ((err = launch_to_f32(wb + s.outb, bf, D, b2, h->st))) return err;
-    return launch_to_f32(wb + s.downb, bf, D, b2 + D, h->st);
+    if ((err = launch_to_f32(wb + s.downb, bf, D, b2 + D, h->st))) return err;
+    if (xl < 0) return hipSuccess;
+    // the branch's output bias joins attn.out.b; its key|value projection joins those of all layers
+    if ((err = launch_to_f32(wb + s.xob, bf, D, b2 + 2 * D, h->st))) return err;
+    if ((err = launch_add_f32(b2, b2 + 2 * D, D, h->st))) return err;
+    const int xw = 2 * lo.Hkv * lo.dh;
+    if ((err = put(s.xkvw, D, xw, lo.xkv_w, D, xl * xw, 0))) return err;
+    return launch_to_f32(wb + s.xkvb, bf, xw, (float*)(h->ws + lo.xkv_b) + (size_t)xl * xw, h->st);
   };
-  for (int l = 0; l < lo.Nb; ++l) INIT_CHECK(repack_layer(lo.bl_blk[l], lo.blk[l]), "repack block layer");
-  for (int l = 0; l < lo.Nt; ++l) INIT_CHECK(repack_layer(lo.bl_tok[l], lo.tok[l]), "repack token layer");
+  for (int l = 0; l < lo.Nb; ++l) INIT_CHECK(repack_layer(lo.bl_blk[l], lo.blk[l], -1), "repack block layer");
+  for (int l = 0; l < lo.Nt; ++l)
+    INIT_CHECK(repack_layer(lo.bl_tok[l], lo.tok[l], lo.mode == BT_CTX_XATTN ? l : -1), "repack token layer");
+  if (!lo.vanilla && lo.mode != BT_CTX_PREFIX)
+    INIT_CHECK(launch_to_f32(wb + lo.bl_emb_tok + (size_t)cfg->pad_id * D * lo.tab_elem, bf, D,
+                             (float*)(h->ws + lo.pad_emb), h->st),
+               "pad embedding");
   float* lnf = (float*)(h->ws + lo.lnf_blk);
   INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_blk_g, bf, D, lnf, h->st), "repack");
   INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_blk_b, bf, D, lnf + D, h->st), "repack");
@@ -617,15 +704,15 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_g, bf, D, lnf, h->st), "repack");
     INIT_CHECK(launch_to_f32(wb + lo.bl_lnf_tok_b, bf, D, lnf + D, h->st), "repack");
     if (f32) {
-      INIT_CHECK(launch_transpose_convert(wb + lo.bl_prefix_w, bf, D, lo.P * D, h->ws + lo.prefix_w, f32, D, 0, 0, sc,
+      INIT_CHECK(launch_transpose_convert(wb + lo.bl_prefix_w, bf, D, lo.NC * D, h->ws + lo.prefix_w, f32, D, 0, 0, sc,
                                           h->st),
                  "repack prefix");
     } else {
-      INIT_CHECK(launch_pack_frag(wb + lo.bl_prefix_w, bf, 1, (size_t)lo.P * D, lo.P * D, lo.P * D, D,
+      INIT_CHECK(launch_pack_frag(wb + lo.bl_prefix_w, bf, 1, (size_t)lo.NC * D, lo.NC * D, lo.NC * D, D,
                                   h->ws + lo.prefix_w, D, 0, 0, sc, h->st),
                  "repack prefix");
     }
-    INIT_CHECK(launch_to_f32(wb + lo.bl_prefix_b, bf, lo.P * D, (float*)(h->ws + lo.prefix_b), h->st), "repack");
+    INIT_CHECK(launch_to_f32(wb + lo.bl_prefix_b, bf, lo.NC * D, (float*)(h->ws + lo.prefix_b), h->st), "repack");
   }
   // classifier table [V, D]: element (n = id, k) at src[n * D + k]; rows up to Vpad are zero
   if (f32) {
@@ -697,7 +784,7 @@ static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_
              4.0 * B * lo.H * lo.dh * (double)n0 * (n0 + 1) / 2.0);
       BT_CHECK(h, launch_prefill_attention(lo.f32, P_(h, lo.QKV), B, n0, lo.H, lo.Hkv, lo.dh,
                                            (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
-                                           P_(h, lo.ACT), lo.D + lo.F, h->st),
+                                           P_(h, lo.ACT), lo.blk[l].k2, h->st),
                "prefill attention");
     }
     r = run_out(h, lo.blk[l], M);
@@ -708,13 +795,13 @@ static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_
     if ((r = run_head(h, n0, n0 - 1, d_logits))) return r;
   } else {
     if ((r = run_prefix(h, n0, n0 - 1))) return r;
-    if ((r = run_token_decoder(h, lo.P, 0))) return r;
-    if ((r = run_head(h, lo.P, lo.P - 1, d_logits))) return r;
+    if ((r = run_token_decoder(h, lo.lead, 0))) return r;
+    if ((r = run_head(h, lo.lead, lo.lead - 1, d_logits))) return r;
   }
   r = run_finalize(h, 0, d_next, 0);
   if (r) return r;
   h->n_blocks = n0;
-  h->local_len = lo.vanilla ? 0 : lo.P;
+  h->local_len = lo.vanilla ? 0 : lo.lead;
   h->g = 1;
   h->ready = true;
   return BT_OK;
@@ -837,14 +924,14 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
       const int nl = lo.Nb + lo.Nt, l = i % nl;
       const LayerOff& w = l < lo.Nt ? lo.tok[l] : lo.blk[l - lo.Nt];
       const Epi ep = qkv_epi(h, w);
-      hipError_t e = launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), h->B, lo.QW + lo.F, lo.D,
+      hipError_t e = launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), h->B, w.n1 + lo.F, lo.D,
                                  EPI_QKV_GELU, ep, h->st);
       if (e != hipSuccess) r = hip_fail(h, e, "replay gemm");
     } else if (kind == PK_ATTN_DECODE) {
       const int l = i % lo.Nb;
       hipError_t e = launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,
                                               lo.Hkv, lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l),
-                                              block_v(h, l), lo.ncap, P_(h, lo.ACT), lo.D + lo.F, (float*)P_(h, lo.part),
+                                              block_v(h, l), lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, (float*)P_(h, lo.part),
                                               lo.part_bytes, h->dec_nsplit, h->st);
       if (e != hipSuccess) r = hip_fail(h, e, "replay attention");
     } else {

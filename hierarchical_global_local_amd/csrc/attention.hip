@@ -624,7 +624,7 @@ hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int*
 constexpr int kMaxLocal = 32;
 
 template <typename T, int DH>
-__global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, int m, int s0, int H, int Hkv,
+__global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, int ldq, int m, int s0, int H, int Hkv,
                                                    const float2* __restrict__ rope, T* __restrict__ Kc,
                                                    T* __restrict__ Vc, int cap, T* __restrict__ ACT, int ld_act,
                                                    float scale) {
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, in
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int G = H / Hkv, hk = h / G;
   const bool writes = h % G == 0;
-  const size_t qw = (size_t)(H + 2 * Hkv) * DH, koff = (size_t)(H + hk) * DH, voff = (size_t)(H + Hkv + hk) * DH;
+  const size_t qw = (size_t)ldq, koff = (size_t)(H + hk) * DH, voff = (size_t)(H + Hkv + hk) * DH;
   const size_t bh = (size_t)b * Hkv + hk;
   T* __restrict__ K = Kc + bh * cap * DH;
   T* __restrict__ V = Vc + bh * cap * DH;
@@ -707,7 +707,8 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 // are read with 16-byte loads.  Each key group keeps an
 // online softmax (base 2) over its keys; the groups are merged with shuffles in a fixed order.
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ QKV, int B, int s0, int H, int Hkv,
+__global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ QKV, int ldq, int B, int s0, int H,
+                                                         int Hkv,
                                                          const float2* __restrict__ rope, T* __restrict__ Kc,
                                                          T* __restrict__ Vc, int cap, T* __restrict__ ACT, int ld_act,
                                                          float scale_log2) {
@@ -721,7 +722,7 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
   const size_t bh = (size_t)b * Hkv + hk;
   T* __restrict__ K = Kc + bh * cap * DH;
   T* __restrict__ V = Vc + bh * cap * DH;
-  const T* row = QKV + (size_t)b * (H + 2 * Hkv) * DH + 8 * g;
+  const T* row = QKV + (size_t)b * ldq + 8 * g;
   float q[8], kn[8], vn[8], kc[8], vc[8];
   load8(row + h * DH, q);
   load8(row + (H + hk) * DH, kn);
@@ -794,11 +795,11 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
   }
 }
 
-hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
+hipError_t launch_local_attention(bool f32, const void* QKV, int ldq, int B, int m, int s0, int H, int Hkv, int dh,
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
                                   hipStream_t st) {
   if (B <= 0 || m <= 0) return hipSuccess;
-  if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  if (Hkv < 1 || H % Hkv || ldq < (H + 2 * Hkv) * dh || ldq % 8) return hipErrorInvalidValue;
   if (s0 + m > kMaxLocal || s0 + m > cap) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)dh);
   if (m == 1) {
@@ -806,7 +807,8 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s
     const dim3 g1((B * H + 3) / 4);
 #define BT_STEP(T, DHV)                                                                                         \
   if (dh == DHV) {                                                                                              \
-    hipLaunchKernelGGL((k_local_attn_step<T, DHV>), g1, dim3(256), 0, st, (const T*)QKV, B, s0, H, Hkv, rope,   \
+    hipLaunchKernelGGL((k_local_attn_step<T, DHV>), g1, dim3(256), 0, st, (const T*)QKV, ldq, B, s0, H, Hkv,     \
+                       rope,                                                                                    \
                        (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale * kLog2e);                                    \
     return hipGetLastError();                                                                                   \
   }
@@ -821,7 +823,7 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s
   dim3 grid(H, B);
 #define BT_LOC(T, DHV)                                                                                          \
   if (dh == DHV) {                                                                                              \
-    hipLaunchKernelGGL((k_local_attn<T, DHV>), grid, dim3(64), 0, st, (const T*)QKV, m, s0, H, Hkv, rope,       \
+    hipLaunchKernelGGL((k_local_attn<T, DHV>), grid, dim3(64), 0, st, (const T*)QKV, ldq, m, s0, H, Hkv, rope,  \
                        (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale);                                             \
     return hipGetLastError();                                                                                   \
   }
@@ -831,6 +833,91 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s
     BT_LOC(f16, 64) BT_LOC(f16, 128)
   }
 #undef BT_LOC
+  return hipErrorInvalidValue;
+}
+
+
+// ---------------------------------------------------------------- cross-attention (token decoder)
+// Context injection by cross-attention: query head h of row b (QKV row b, columns qoff + h*DH, no
+// rotary embedding) attends to the P encoder states of row b, whose keys and values (fp32) sit in
+// XKV rows b*P + p at columns koff + hk*DH and koff + Hkv*DH + hk*DH, hk = h / (H / Hkv).  One
+// wave per (row, head) with the layout of the local-attention step: DH / 8 lanes per key holding 8
+// dimensions each, an online softmax (base 2) per key group, groups merged with shuffles.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_cross_attn(const T* __restrict__ QKV, int ldq, int qoff, int B, int H,
+                                                    int Hkv, const float* __restrict__ XKV, int ldx, int koff, int P,
+                                                    T* __restrict__ ACT, int ld_act, int act_col, float scale_log2) {
+  constexpr int LPK = DH / 8, KPP = 64 / LPK;
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= B * H) return;  // whole wave
+  const int b = pair / H, h = pair % H, hk = h / (H / Hkv);
+  const int g = lane % LPK, kg = lane / LPK;  // dimensions [8g, 8g + 8), key group
+  float q[8];
+  load8(QKV + (size_t)b * ldq + qoff + h * DH + 8 * g, q);
+  const float* kb = XKV + (size_t)b * P * ldx + koff + hk * DH + 8 * g;
+  const float* vb = kb + Hkv * DH;
+  float mrun = -INFINITY, lrun = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int p0 = 0; p0 < P; p0 += KPP) {
+    const int p = p0 + kg, pc = min(p, P - 1);
+    float kc[8], vc[8];
+    load8(kb + (size_t)pc * ldx, kc);
+    load8(vb + (size_t)pc * ldx, vc);
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kc[e], dot);
+#pragma unroll
+    for (int w = 1; w < LPK; w <<= 1) dot += __shfl_xor(dot, w, 64);
+    const float sc = p < P ? dot * scale_log2 : -INFINITY;
+    const float mn = fmaxf(mrun, sc);
+    const float corr = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
+    const float pr = sc == -INFINITY ? 0.f : exp2f(sc - mn);
+    lrun = lrun * corr + pr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * corr + pr * vc[e];
+    mrun = mn;
+  }
+#pragma unroll
+  for (int w = LPK; w < 64; w <<= 1) {
+    const float mo = __shfl_xor(mrun, w, 64), lo = __shfl_xor(lrun, w, 64);
+    const float mn = fmaxf(mrun, mo);
+    const float c1 = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
+    const float c2 = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+    lrun = lrun * c1 + lo * c2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * c1 + __shfl_xor(o[e], w, 64) * c2;
+    mrun = mn;
+  }
+  if (kg == 0) {
+    const float inv = 1.0f / lrun;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= inv;
+    store8(ACT + opnd_idx(ACT, b, act_col + h * DH + 8 * g, ld_act), o);
+  }
+}
+
+hipError_t launch_cross_attention(bool f32, const void* QKV, int ldq, int qoff, int B, int H, int Hkv, int dh,
+                                  const float* XKV, int ldx, int koff, int P, void* ACT, int ld_act, int act_col,
+                                  hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  if (P < 1 || Hkv < 1 || H % Hkv || ldq % 8 || qoff % 8 || ldx % 8 || koff % 8 || act_col % 8)
+    return hipErrorInvalidValue;
+  const float sl2 = kLog2e / sqrtf((float)dh);
+  const dim3 grid((B * H + 3) / 4);
+#define BT_XA(T, DHV)                                                                                          \
+  if (dh == DHV) {                                                                                             \
+    hipLaunchKernelGGL((k_cross_attn<T, DHV>), grid, dim3(256), 0, st, (const T*)QKV, ldq, qoff, B, H, Hkv, XKV, \
+                       ldx, koff, P, (T*)ACT, ld_act, act_col, sl2);                                            \
+    return hipGetLastError();                                                                                  \
+  }
+  if (f32) {
+    BT_XA(float, 32) BT_XA(float, 64) BT_XA(float, 128)
+  } else {
+    BT_XA(f16, 64) BT_XA(f16, 128)
+  }
+#undef BT_XA
   return hipErrorInvalidValue;
 }
 

@@ -31,7 +31,10 @@ struct LayerOff {
   size_t b1;  // fp32 [QW + F]
   size_t w2;  // T [D][D + F]: row n = output feature n of attn.out (k < D) and mlp.down (k >= D),
               //   same layout as w1
-  size_t b2;  // fp32 [2][D]: attn.out.b, mlp.down.b
+  size_t b2;  // fp32 [3][D]: attn.out.b (+ xattn.out.b), mlp.down.b, (xattn.out.b at init)
+  int n1;     // q | k | v (| cross-attention q) columns of w1: QW, or QW + D in a token layer with
+              //   cross-attention; the up rows follow
+  int k2;     // width of the [attn | gelu(up) (| cross-attention)] operand of w2: D + F (+ D)
 };
 
 struct Layout {
@@ -39,6 +42,10 @@ struct Layout {
   int V, D, H, dh, F, L, P, Nb, Nt, De;
   int Hkv;      // key/value heads (grouped-query attention: H / Hkv query heads per KV head)
   int QW;       // width of the fused q | k | v projection: D + 2 Hkv dh
+  int mode;     // bt_context_mode
+  int lead;     // local slots before a block's first token: P (prefix) or 1 (start slot)
+  int NC;       // vectors of the context projection: P, or L_B for summation
+  int maxN1, maxK2;  // largest LayerOff::n1 and ::k2 (QKV and ACT widths)
   int Bmax, max_tokens;
   int max_prompt;  // longest padded prompt the activations hold (a multiple of L)
   int ncap;     // block-KV entries per (layer, row, KV head), multiple of 64
@@ -62,6 +69,14 @@ struct Layout {
   size_t part;  // fp32 split-KV partials of block-attention decode
   size_t part_bytes;
   size_t keys;  // u64 [nparts][Bmax] partial argmax keys of the classifier
+  size_t pad_emb;  // fp32 [D] token embedding of pad_id (start slot of summation / cross-attention)
+  size_t ctx;      // summation: fp32 [Bmax][L][D] projected summands of the current block
+  size_t enc;      // cross-attention: fp32 [Bmax * P][D] encoder states of the current block
+  size_t enc16;    // ... the same as an fp16 operand in fragment order (BT_BF16)
+  size_t xkv_w;    // cross-attention: T [Nt * 2 Hkv dh][D] key|value projections of all token layers
+  size_t xkv_b;    // fp32 [Nt * 2 Hkv dh]
+  size_t xkv;      // fp32 [Bmax * P][Nt * 2 Hkv dh] keys and values of the encoder states
+  int xkv_ld;      // Nt * 2 Hkv dh
   size_t rpart; // fp32 [16][rpart_rows][D] split-K partials of the [out|down] GEMM (decode)
   int rpart_rows;
   size_t cur;   // int32 [Bmax][L] ids of the block being generated
@@ -69,7 +84,10 @@ struct Layout {
   size_t total;
   size_t block_kv_bytes, local_kv_bytes;
   // canonical blob offsets (bytes)
-  struct BlobLayer { size_t ln1g, ln1b, qkvw, qkvb, outw, outb, ln2g, ln2b, upw, upb, downw, downb; };
+  struct BlobLayer {
+    size_t ln1g, ln1b, qkvw, qkvb, outw, outb, ln2g, ln2b, upw, upb, downw, downb;
+    size_t xqw = 0, xqb = 0, xkvw = 0, xkvb = 0, xow = 0, xob = 0;  // cross-attention (token layers)
+  };
   size_t bl_emb_block, bl_lnf_blk_g, bl_lnf_blk_b, bl_prefix_w, bl_prefix_b, bl_emb_tok, bl_lnf_tok_g,
       bl_lnf_tok_b, bl_head, bl_total;
   std::vector<BlobLayer> bl_blk, bl_tok;
@@ -92,6 +110,9 @@ hipError_t launch_pack_frag(const void* src, bool src_bf16, size_t sn, size_t sk
                             void* dst, int Ktot, int row0, int col0, float scale, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool src_bf16, int n, float* dst, hipStream_t st);
 hipError_t launch_add_f32(float* dst, const float* a, int n, hipStream_t st);
+// X[b][:] = base[:] (+ add[b * add_ld + :] when add is not null), rows b < B of width D
+hipError_t launch_rows_init(float* X, int B, int D, const float* base, const float* add, int add_ld,
+                            hipStream_t st);
 hipError_t launch_rope_table(float2* tab, int npos, int dh, float base, hipStream_t st);
 
 // ---- embedders
@@ -172,8 +193,15 @@ hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int*
                                     const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
                                     float* part, size_t part_bytes, int nsplit, hipStream_t st);
 // local attention: new slots [s0, s0 + m) per row; rotary at slot, write to local cache, attend over [0, slot]
-hipError_t launch_local_attention(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
+// (ldq = QKV row stride, >= (H + 2 Hkv) dh: token layers with cross-attention carry its queries too)
+hipError_t launch_local_attention(bool f32, const void* QKV, int ldq, int B, int m, int s0, int H, int Hkv, int dh,
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
+                                  hipStream_t st);
+// cross-attention of one slot per row: query head h of row b (QKV[b * ldq + qoff + h dh ..], no rotary)
+// over the P encoder states of row b, keys and values (fp32) at XKV[(b P + p) * ldx + koff + ..]
+// (keys of KV head hk at hk dh, values at Hkv dh + hk dh); output to ACT columns act_col + h dh.
+hipError_t launch_cross_attention(bool f32, const void* QKV, int ldq, int qoff, int B, int H, int Hkv, int dh,
+                                  const float* XKV, int ldx, int koff, int P, void* ACT, int ld_act, int act_col,
                                   hipStream_t st);
 
 // ---- greedy ids from the classifier's partial maxima [B][ld] (nparts per row): next[b] = id,
@@ -192,6 +220,8 @@ struct NextStepArgs {
   void* ln2 = nullptr;
   int D = 0, V = 0;
   float eps = 1e-5f;
+  const float* add = nullptr;  // token step: fp32 [B][add_ld] added to the embedding (summation)
+  int add_ld = 0;
 };
 hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, int B, int32_t* next, int32_t* cur,
                            int L, int j, int* n_state, int n_inc, const NextStepArgs& nxt, hipStream_t st);

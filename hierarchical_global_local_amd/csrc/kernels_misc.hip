@@ -126,6 +126,19 @@ hipError_t launch_add_f32(float* dst, const float* a, int n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// X[b][:] = base[:] + add[b][:] (add optional): the start slot of a local sequence
+__global__ void k_rows_init(float* __restrict__ X, int D, const float* __restrict__ base,
+                            const float* __restrict__ add, int add_ld) {
+  const int b = blockIdx.y, d = blockIdx.x * 256 + threadIdx.x;
+  if (d < D) X[(size_t)b * D + d] = base[d] + (add ? add[(size_t)b * add_ld + d] : 0.f);
+}
+hipError_t launch_rows_init(float* X, int B, int D, const float* base, const float* add, int add_ld,
+                            hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rows_init, dim3((D + 255) / 256, B), dim3(256), 0, st, X, D, base, add, add_ld);
+  return hipGetLastError();
+}
+
 // Rotary table: tab[p][i] = (cos, sin)(p * base^(-2i/dh)), angles in double precision.
 __global__ void k_rope_table(float2* tab, int npos, int dh, double base) {
   int half = dh / 2;
@@ -373,6 +386,8 @@ struct NextStep {
   void* ln2;
   int D, V;
   float eps;
+  const float* add;      // token step: fp32 [B][add_ld] added to the embedding row (or null)
+  int add_ld;
 };
 
 template <int PER, typename Tt, typename To>
@@ -422,7 +437,8 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
       col = cc - o * ns.width;
     }
     tok = tok < 0 ? 0 : (tok >= ns.V ? ns.V - 1 : tok);
-    const float e = load_f32(E + (size_t)tok * ns.width + col);
+    float e = load_f32(E + (size_t)tok * ns.width + col);
+    if (ns.add) e += ns.add[(size_t)b * ns.add_ld + cc];
     v[q] = c < D ? e : 0.f;
     g1[q] = ns.lnp[cc];
     b1[q] = ns.lnp[D + cc];
@@ -481,7 +497,7 @@ static void launch_fin_cfg(bool tab_bf16, bool out_f32, int B, const unsigned lo
 hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, int B, int32_t* next, int32_t* cur,
                            int L, int j, int* n_state, int n_inc, const NextStepArgs& a, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  NextStep ns{a.mode, a.E, a.width, a.X, a.lnp, a.ln1, a.ln2, a.D, a.V, a.eps};
+  NextStep ns{a.mode, a.E, a.width, a.X, a.lnp, a.ln1, a.ln2, a.D, a.V, a.eps, a.add, a.add_ld};
   const int per = (a.D + 255) / 256;
   if (per <= 1)
     launch_fin_cfg<1>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);

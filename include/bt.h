@@ -53,6 +53,18 @@ typedef enum {
                   accumulation, fp32 residual stream                           */
 } bt_dtype;
 
+/* How the context embedding of the previous block reaches the token decoder (summary page §3.4
+ * "The Token Decoder" and its comparison of prefix tokens with summation and cross-attention). */
+typedef enum {
+  BT_CTX_PREFIX = 0, /* P prefix vectors lead the local sequence (the method's own design)      */
+  BT_CTX_SUM = 1,    /* the projection gives L_B vectors; u_i is added to local slot i, which
+                        holds a start token (the pad token's embedding) at i = 0 and the block's
+                        token i-1 after it; slot i predicts the block's token i                 */
+  BT_CTX_XATTN = 2   /* the projection gives P encoder states; the same start-token local
+                        sequence; every token-decoder layer adds a cross-attention branch
+                        h + Attn(LN1 h) + XAttn(LN1 h) + MLP(LN2 h) (no rotary, no mask)        */
+} bt_context_mode;
+
 /* Model and capacity.  Constraints (checked by bt_init and the sizing calls):
  *   d_model % n_heads == 0, d_head = d_model / n_heads in {32, 64, 128};
  *   d_model % block_len == 0 (embedder width d_model / block_len, even);
@@ -63,7 +75,8 @@ typedef enum {
  *   BT_BF16 also needs d_model % 64 == 0 and d_mlp % 64 == 0;
  *   max_batch >= 1; max_tokens >= block_len (padded prompt + generated);
  *   0 <= max_prompt_tokens <= max_tokens;
- *   n_kv_heads = 0 (multi-head) or a divisor of n_heads (grouped-query; 1 = multi-query). */
+ *   n_kv_heads = 0 (multi-head) or a divisor of n_heads (grouped-query; 1 = multi-query);
+ *   context_mode a bt_context_mode, BT_CTX_PREFIX when n_token_layers = 0. */
 typedef struct {
   int32_t vocab, d_model, n_heads, d_mlp;
   int32_t n_block_layers, n_token_layers;
@@ -82,6 +95,7 @@ typedef struct {
                          G = n_heads / H_kv consecutive heads and head i attends with key/value
                          head i / G (grouped-query attention; summary page §3.4 "The Block
                          Decoder" names it as compatible); the KV caches then hold H_kv heads. */
+  int32_t context_mode; /* bt_context_mode (0 = prefix) */
 } bt_config;
 
 /* Size in bytes of the canonical weights blob for this config.  The blob is
@@ -93,9 +107,11 @@ typedef struct {
  *     attn.qkv.b [Q], attn.out.w [D, D], attn.out.b [D],
  *     ln2.g [D], ln2.b [D], mlp.up.w [D, F], mlp.up.b [F], mlp.down.w [F, D], mlp.down.b [D]
  *   blk.lnf.g [D], blk.lnf.b [D]
- *   prefix.w [D, P*D], prefix.b [P*D]
+ *   prefix.w [D, C*D], prefix.b [C*D]     (context projection; C = L_B for BT_CTX_SUM, else P)
  *   emb_token [V, D]
- *   per token layer: same twelve tensors as a block layer
+ *   per token layer: same twelve tensors as a block layer; with BT_CTX_XATTN followed by
+ *     xattn.q.w [D, D], xattn.q.b [D], xattn.kv.w [D, 2 H_kv d_head] (columns: k | v),
+ *     xattn.kv.b [2 H_kv d_head], xattn.out.w [D, D], xattn.out.b [D]
  *   tok.lnf.g [D], tok.lnf.b [D]
  *   head.w [V, D]                      (output classifier, no bias)
  * With n_token_layers = 0 the blob ends blk.lnf.g, blk.lnf.b, head.w (no prefix, token table,
@@ -166,11 +182,11 @@ int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_k
  *            cap = ceil(max_tokens / L_B) rounded up to a multiple of 64; per (layer,
  *            row, KV head) the keys are [cap][d_head] (after the rotary embedding) and the
  *            values are transposed, [d_head][cap];
- * which = 1: local-KV cache [N_tok][2][max_batch][H_kv][P + L_B][d_head] (keys after
+ * which = 1: local-KV cache [N_tok][2][max_batch][H_kv][S + L_B][d_head] (keys after
  *            the rotary embedding, values not transposed).
  * Elements are fp16 for BT_BF16 and fp32 for BT_FP32.  Writes the byte
  * offset from the workspace start, the byte size and the per-head capacity.  H_kv is
- * n_kv_heads, or n_heads when that is 0. */
+ * n_kv_heads, or n_heads when that is 0; S is P for BT_CTX_PREFIX, else 1 (the start slot). */
 int bt_workspace_region(const bt_config* cfg, int32_t which, size_t* offset, size_t* bytes,
                         int32_t* capacity);
 

@@ -14,12 +14,13 @@
 extern "C" {
 #endif
 
-/* Kernel classes timed by the profiler (BT_PROFILE_KINDS of them): 0 embedder gathers,
- * 1 LayerNorms, 2 [q|k|v|up] GEMMs (with GELU), 3 [out|down] GEMMs (residual add), 4 prefix
- * projection, 5 classifier + argmax, 6 prefill attention, 7 prefill rotary/KV scatter, 8 block-
- * attention decode (incl. split merge), 9 local attention, 10 greedy-id finalisation.  Each class is
- * counted separately for launches made by bt_prefill (index k) and by bt_decode_step (index 11 + k). */
-#define BT_PROFILE_KINDS 11
+/* Kernel classes timed by the profiler (BT_PROFILE_KINDS of them): 0 embedder gathers and
+ * start-slot rows, 1 LayerNorms, 2 [q|k|v|up] GEMMs (with GELU), 3 [out|down] GEMMs (residual
+ * add), 4 context projection (and the cross-attention key/value projection), 5 classifier +
+ * argmax, 6 prefill attention, 7 prefill rotary/KV scatter, 8 block-attention decode (incl. split
+ * merge), 9 local attention, 10 greedy-id finalisation, 11 cross-attention.  Each class is counted
+ * separately for launches made by bt_prefill (index k) and by bt_decode_step (index 12 + k). */
+#define BT_PROFILE_KINDS 12
 
 /* Start (on != 0) or stop recording a pair of HIP events around every kernel launch of the
  * handle, on the handle's stream.  Clears what was recorded before. */

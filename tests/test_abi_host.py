@@ -67,6 +67,29 @@ def test_grouped_query_blob_and_cache_sizes(kv):
         assert got[0][1] == got[1][1] and got[0][0] * (12 // kv) == got[1][0]
 
 
+@pytest.mark.parametrize("mode,kw", [("sum", dict()), ("sum", dict(block_len=2)), ("xattn", dict(prefix_len=3)),
+                                     ("xattn", dict(n_kv_heads=2))])
+def test_context_variant_blob_and_local_cache(mode, kw):
+    """Summation projects to L_B vectors and cross-attention adds six tensors per token layer; both
+    local caches hold one start slot plus the block's tokens."""
+    import hierarchical_global_local_amd as hg
+    L = hg.lib()
+    c, cfg = _cfg("c2_decode_heavy", context_mode=mode, **kw)
+    n = sum(int(np.prod(s)) for _, s, _ in wl.weight_specs(c))
+    assert L.bt_weights_bytes(ctypes.byref(cfg)) == n * 2
+    assert hg.weight_names(c) == [s[0] for s in wl.weight_specs(c)]
+    off, nb, cap = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+    assert L.bt_workspace_region(ctypes.byref(cfg), 1, ctypes.byref(off), ctypes.byref(nb), ctypes.byref(cap)) == 0
+    assert cap.value == 1 + c.block_len
+
+
+def test_context_mode_needs_a_token_decoder():
+    import hierarchical_global_local_amd as hg
+    _, cfg = _cfg("v2_vanilla_decode_heavy", context_mode="sum")
+    assert hg.lib().bt_weights_bytes(ctypes.byref(cfg)) == 0
+    assert "token decoder" in hg.lib().bt_last_error().decode()
+
+
 def test_packed_blob_matches_declared_size():
     import hierarchical_global_local_amd as hg
     c, cfg = _cfg("c0_tiny")
@@ -95,7 +118,8 @@ def test_block_kv_footprint_ratio_is_block_len():
                                              ("max_prompt_tokens", -4, "max_prompt_tokens"),
                                              ("max_prompt_tokens", 1 << 20, "max_prompt_tokens"),
                                              ("n_kv_heads", 5, "n_kv_heads"), ("n_kv_heads", -1, "n_kv_heads"),
-                                             ("n_kv_heads", 24, "n_kv_heads")])
+                                             ("n_kv_heads", 24, "n_kv_heads"), ("context_mode", 3, "context_mode"),
+                                             ("pad_id", 50304, "pad_id"), ("pad_id", -1, "pad_id")])
 def test_invalid_config_rejected_on_host(field, value, msg):
     import hierarchical_global_local_amd as hg
     _, cfg = _cfg("c1_prefill_heavy")

@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("name", ["c1_prefill_heavy", "c2_decode_heavy", "c4_lb1", "c4_lb2", "c4_lb8", "c3_1p2b",
                                   "v1_vanilla_prefill_heavy", "v2_vanilla_decode_heavy", "f4_gqa4_decode_heavy",
-                                  "f4_mqa_decode_heavy", "f4_long32k_lb4"])
+                                  "f4_mqa_decode_heavy", "f4_long32k_lb4", "f4_sum_decode_heavy",
+                                  "f4_xattn_decode_heavy"])
 def test_full_config_sampled_parity(name):
     require_gpu()
     cfg = wl.get_config(name)
@@ -31,7 +32,7 @@ def test_full_config_sampled_parity(name):
     ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=steps)
     t1 = time.time()
     Tp = wl.padded_len(cfg, cfg.prompt_len)
-    local = 0 if cfg.n_token_layers == 0 else cfg.prefix_len + (G - 1) % cfg.block_len
+    local = 0 if cfg.n_token_layers == 0 else cfg.lead + (G - 1) % cfg.block_len
     assert model.cache_lengths() == (Tp // cfg.block_len + (G - 1) // cfg.block_len, local)
     model.close()
     del model

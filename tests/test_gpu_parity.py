@@ -60,6 +60,40 @@ def test_fp32_grouped_query_attention(kw, B, T, G):
     _fp32_case(wl.get_config("c0_tiny", **kw), B, T, G, seed=13)
 
 
+# context injection by summation (L_B summands; L_B = 1 is a single slot) and by cross-attention
+# (P encoder states; P = 1 is a single state), with grouped-query heads in one case
+CONTEXT_FP32 = [(dict(context_mode="sum"), 3, 13, 11), (dict(context_mode="sum", block_len=2), 2, 9, 8),
+                (dict(context_mode="sum", block_len=1), 2, 7, 6),
+                (dict(context_mode="xattn", prefix_len=2), 3, 13, 11),
+                (dict(context_mode="xattn", prefix_len=1, block_len=2), 2, 9, 8),
+                (dict(context_mode="xattn", prefix_len=3, d_model=128, n_heads=4, n_kv_heads=2), 2, 10, 9)]
+
+
+@pytest.mark.parametrize("kw,B,T,G", CONTEXT_FP32)
+def test_fp32_context_injection_variants(kw, B, T, G):
+    _fp32_case(wl.get_config("c0_tiny", **kw), B, T, G, seed=16)
+
+
+@pytest.mark.parametrize("kw", [dict(context_mode="sum"), dict(context_mode="xattn", prefix_len=3),
+                                dict(context_mode="xattn", prefix_len=2, d_model=512, n_heads=4, n_kv_heads=2),
+                                dict(context_mode="sum", block_len=8)])
+def test_bf16_context_injection_variants(kw):
+    """bf16 every step for both variants (d_head 64, and 128 with grouped-query heads)."""
+    cfg = SMALL_BF16.with_(**kw)
+    log(f"bf16 context-variant case {kw}")
+    W = wl.make_weights(cfg, seed=17, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=17)
+    G = cfg.gen_len
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G))
+    _, ref_lg, st = om.generate(om.weights_as(W, np.float64), cfg, prompt, G, keep_logits=True, forced=ids)
+    gl = np.stack([lg[g] for g in range(G)], axis=1)
+    err = np.abs(gl - ref_lg).max()
+    exact = check_ids_against(ref_lg, ids, BF16_TOL)
+    log(f"  max-abs logit error {err:.3e}, exact argmax {exact:.3f}")
+    assert err <= BF16_TOL
+    assert model.cache_lengths() == (st.block_kv_len, st.local_kv_len)
+
+
 @pytest.mark.parametrize("kw,max_tokens", [(dict(d_model=256, n_heads=4, n_kv_heads=2), None),
                                            (dict(d_model=384, n_heads=6, n_kv_heads=2, d_mlp=768), None),
                                            (dict(d_model=256, n_heads=4, n_kv_heads=1), 4096),
@@ -216,7 +250,8 @@ def test_host_side_errors():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(block_len=1, prefix_len=2)])
+@pytest.mark.parametrize("kw", [dict(), dict(block_len=1, prefix_len=2), dict(context_mode="sum"),
+                                dict(context_mode="xattn", prefix_len=3)])
 def test_graph_replay_matches_eager(kw):
     """Decode steps replayed from HIP graphs give the eagerly launched results bit for bit, over
     repeated replays with other GPU work and synchronisations in between, and when steps that ask
