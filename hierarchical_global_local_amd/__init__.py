@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.bt_init.argtypes = [cfgp, c_p, c_p, c_sz, c_p, ctypes.POINTER(c_p)]
     L.bt_prefill.argtypes = [c_p, c_p, c_i32, c_i32, c_p, c_p]
     L.bt_prefill_lengths.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
+    L.bt_prefill_ragged.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
+    L.bt_prefill_rows.argtypes = [c_p, ctypes.POINTER(c_i32), c_i32, c_p, c_p, c_i32, c_p, c_p]
+    L.bt_block_lengths.argtypes = [c_p, ctypes.POINTER(c_i32)]
     L.bt_decode_step.argtypes = [c_p, c_p, c_p]
     L.bt_cache_lengths.argtypes = [c_p, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
     L.bt_workspace_region.argtypes = [cfgp, c_i32, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz), ctypes.POINTER(c_i32)]
@@ -82,7 +85,8 @@ def lib() -> ctypes.CDLL:
     L.bt_test_gemm.argtypes = [c_i32, c_p, c_p, c_p, c_i32, c_i32, c_i32, ctypes.c_float, c_p]
     L.bt_set_graphs.argtypes = [c_p, c_i32]
     L.bt_test_replay.argtypes = [c_p, c_i32, c_i32]
-    for f in ("bt_init", "bt_prefill", "bt_prefill_lengths", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
+    for f in ("bt_init", "bt_prefill", "bt_prefill_lengths", "bt_prefill_ragged", "bt_prefill_rows",
+              "bt_block_lengths", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
               "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs", "bt_test_replay"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -181,9 +185,11 @@ class BlockTransformer:
                 if t is not None:
                     t.record_stream(self.stream)
 
-    def prefill(self, prompt, out=None, logits=None, lengths=None):
+    def prefill(self, prompt, out=None, logits=None, lengths=None, ragged=False):
         """prompt: int32 device tensor [B, T]; writes the first generated ids into ``out`` [B].
-        lengths: optional int32 device tensor [B]: row b's prompt is prompt[b, :lengths[b]]."""
+        lengths: optional int32 device tensor [B]: row b's prompt is prompt[b, :lengths[b]], left
+        padded to the common length (bt_prefill_lengths) or, with ragged=True, only to its own
+        whole blocks (bt_prefill_ragged)."""
         torch = self.torch
         assert prompt.dtype == torch.int32 and prompt.is_contiguous() and prompt.dim() == 2
         B, T = prompt.shape
@@ -195,10 +201,32 @@ class BlockTransformer:
         else:
             assert lengths.dtype == torch.int32 and lengths.is_contiguous() and lengths.shape == (B,)
             self._order(prompt, lengths, out, logits)
-            check(lib().bt_prefill_lengths(self.h, prompt.data_ptr(), lengths.data_ptr(), B, T, out.data_ptr(),
-                                           _ptr(logits)))
+            fn = lib().bt_prefill_ragged if ragged else lib().bt_prefill_lengths
+            check(fn(self.h, prompt.data_ptr(), lengths.data_ptr(), B, T, out.data_ptr(), _ptr(logits)))
         self.batch = B
         return out
+
+    def join(self, rows, prompt, lengths, out=None, logits=None):
+        """Continuous batching (bt_prefill_rows): the prompts of ``prompt`` [B_new, T] / ``lengths``
+        [B_new] (int32 device tensors) take over rows ``rows`` (host ints) of the running batch.
+        Returns their first generated ids [B_new]."""
+        torch = self.torch
+        assert prompt.dtype == torch.int32 and prompt.is_contiguous() and prompt.dim() == 2
+        Bn, T = prompt.shape
+        assert lengths.dtype == torch.int32 and lengths.is_contiguous() and lengths.shape == (Bn,)
+        if out is None:
+            out = torch.empty(Bn, dtype=torch.int32, device=self.device)
+        self._order(prompt, lengths, out, logits)
+        r = (ctypes.c_int32 * Bn)(*[int(x) for x in rows])
+        check(lib().bt_prefill_rows(self.h, r, Bn, prompt.data_ptr(), lengths.data_ptr(), T, out.data_ptr(),
+                                    _ptr(logits)))
+        return out
+
+    def block_lengths(self):
+        """Block-KV entries of every row of the running batch (synchronises)."""
+        a = (ctypes.c_int32 * self.batch)()
+        check(lib().bt_block_lengths(self.h, a))
+        return np.array(a, dtype=np.int64)
 
     def decode_step(self, out=None, logits=None):
         torch = self.torch

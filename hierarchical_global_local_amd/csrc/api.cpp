@@ -186,7 +186,9 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.rpart_rows = (int)std::min<int64_t>(lo.Mmax, 1024);
   lo.rpart = region((size_t)16 * lo.rpart_rows * D * 4);
   lo.cur = region((size_t)lo.Bmax * lo.L * 4);
-  lo.dstate = region(64);
+  lo.dstate = region(std::max<size_t>(64, (size_t)lo.Bmax * 4));
+  lo.rowmap = region((size_t)lo.Bmax * 4);
+  lo.lastblk = region((size_t)lo.Bmax * 4);
   lo.total = w;
   return "";
 }
@@ -201,9 +203,11 @@ struct bt_handle {
   char* ws = nullptr;
   hipStream_t st = nullptr;
   int B = 0, Tp = 0;
-  int n_blocks = 0;   // block-KV entries per layer
+  int n_blocks = 0;   // block-KV entries per layer (the largest over the rows)
   int local_len = 0;  // local-KV entries per layer
   int g = 0;          // tokens emitted since the prefill
+  std::vector<int64_t> row_tok;  // per row: padded prompt + emitted tokens, an upper bound
+  const int* rmap = nullptr;     // during a join: device cache row of each prefilled row
   bool ready = false, broken = false;
   // optional per-kernel-class event timing
   bool prof = false;
@@ -376,7 +380,7 @@ int run_token_decoder(bt_handle* h, int m, int s0, bool first_ln_done = false) {
              4.0 * Bd * lo.H * lo.dh * pairs);
       BT_CHECK(h, launch_local_attention(lo.f32, P_(h, lo.QKV), lo.tok[l].n1, h->B, m, s0, lo.H, lo.Hkv, lo.dh,
                                          (const float2*)P_(h, lo.rope), local_k(h, l), local_v(h, l), lo.lcap,
-                                         P_(h, lo.ACT), lo.tok[l].k2, h->st),
+                                         P_(h, lo.ACT), lo.tok[l].k2, h->st, h->rmap),
                "local attention");
     }
     if (lo.mode == BT_CTX_XATTN) {
@@ -423,13 +427,12 @@ int run_head(bt_handle* h, int m, int slot, float* d_logits) {
   return BT_OK;
 }
 
-// Greedy ids of in-block offset j into d_next and the current-block buffer; a block step also
-// advances the device block-KV length.  The same kernel prepares the input of decode step g + 1
-// (g = the index of the token just chosen): its embedding row and first-layer LayerNorms.
-int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
+// Input of the decode step that predicts token gn: the embedding row of the id just emitted (token
+// step) or of the block it completes (block step), and the first layer's LN1/LN2 of that row.
+NextStepArgs next_step_args(bt_handle* h, int gn) {
   const Layout& lo = h->lo;
   NextStepArgs nx;
-  const bool next_is_block = (h->g + 1) % lo.L == 0;
+  const bool next_is_block = gn % lo.L == 0;
   nx.mode = next_is_block ? 2 : 1;
   nx.E = next_is_block ? P_(h, lo.emb_block) : P_(h, lo.emb_tok);
   nx.width = next_is_block ? lo.De : lo.D;
@@ -443,14 +446,37 @@ int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
   nx.V = lo.V;
   nx.eps = h->cfg.ln_eps;
   if (lo.mode == BT_CTX_SUM && !next_is_block) {
-    // summation: the next slot, (g + 1) % L, also takes its projected summand
-    nx.add = (const float*)P_(h, lo.ctx) + (size_t)((h->g + 1) % lo.L) * lo.D;
+    // summation: that slot, gn % L, also takes its projected summand
+    nx.add = (const float*)P_(h, lo.ctx) + (size_t)(gn % lo.L) * lo.D;
     nx.add_ld = lo.L * lo.D;
   }
+  return nx;
+}
+
+// Greedy ids of in-block offset j into d_next and the current-block buffer; a block step also
+// advances the device block-KV lengths.  The same kernel prepares the input of decode step g + 1
+// (g = the index of the token just chosen), except in a join (rows prefilled into a running batch:
+// their inputs are prepared afterwards, with everyone else's).
+int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
+  const Layout& lo = h->lo;
+  NextStepArgs nx = next_step_args(h, h->g + 1);
+  if (h->rmap) nx.mode = 0;
   Prof p(h, PK_FINALIZE, (double)h->B * (16.0 + lo.D * (lo.tab_elem + 4.0 + 2.0 * lo.elem)), 0.0);
   BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->head_nparts, lo.Vpad / 4 + 64, h->B, d_next,
-                              (int32_t*)P_(h, lo.cur), lo.L, j, (int*)P_(h, lo.dstate), n_inc, nx, h->st),
+                              (int32_t*)P_(h, lo.cur), lo.L, j, (int*)P_(h, lo.dstate), n_inc, nx, h->st, h->rmap),
            "finalize");
+  return BT_OK;
+}
+
+// After a join: the input of the next decode step (which predicts token g) of every row, from the
+// id each row emitted last (offset (g - 1) % L of its current block)
+int run_prepare_inputs(bt_handle* h) {
+  const Layout& lo = h->lo;
+  NextStepArgs nx = next_step_args(h, h->g);
+  Prof p(h, PK_FINALIZE, (double)h->B * (4.0 + lo.D * (lo.tab_elem + 4.0 + 2.0 * lo.elem)), 0.0);
+  BT_CHECK(h, launch_finalize(nullptr, 0, 0, h->B, nullptr, (int32_t*)P_(h, lo.cur), lo.L, (h->g - 1) % lo.L,
+                              (int*)P_(h, lo.dstate), 0, nx, h->st, nullptr, true),
+           "next-step inputs");
   return BT_OK;
 }
 
@@ -728,21 +754,75 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
   return BT_OK;
 }
 
-static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
-                        int32_t* d_next, float* d_logits);
-
-int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int32_t* d_next, float* d_logits) {
-  return prefill_impl(h, d_prompt, nullptr, B, T, d_next, d_logits);
+// Prefill of h->B rows (a join: into the cache rows h->rmap of a running batch): the block decoder
+// over their Tp / L prompt blocks, the prefill tail and the first generated token.  ragged: every
+// row padded only to its own multiple of L (its blocks left-aligned; the rest of the Tp / L rows
+// are pad blocks whose results nothing reads).
+static int prefill_core(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t T, int Tp,
+                        bool ragged, int32_t* d_next, float* d_logits) {
+  const Layout& lo = h->lo;
+  const int L = lo.L, B = h->B;
+  const int n0 = Tp / L;
+  const int M = B * n0;
+  h->pending.nsplit = 0;
+  h->decode_phase = false;
+  const double E = (double)lo.elem, Dd = lo.D, Md = M, KVW = (double)lo.Hkv * lo.dh;
+  {
+    Prof p(h, PK_EMBED, Md * Dd * (lo.tab_elem + 4.0) + (double)B * T * 4.0, 0.0);
+    BT_CHECK(h, launch_embed_prompt(d_prompt, d_lengths, B, T, Tp, h->cfg.pad_id, P_(h, lo.emb_block), !lo.f32, lo.V,
+                                    lo.De, L, (float*)P_(h, lo.X), (int*)P_(h, lo.dstate), ragged, h->rmap,
+                                    ragged ? (int*)P_(h, lo.lastblk) : nullptr, h->st),
+             "embed prompt");
+  }
+  for (int l = 0; l < lo.Nb; ++l) {
+    int r = run_ln_qkv(h, lo.blk[l], M);
+    if (r) return r;
+    {
+      Prof p(h, PK_ROPE_SCATTER, Md * 4.0 * KVW * E, 3.0 * Md * KVW);
+      BT_CHECK(h, launch_rope_scatter(lo.f32, P_(h, lo.QKV), B, n0, 0, lo.H, lo.Hkv, lo.dh,
+                                      (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap, true,
+                                      h->st, h->rmap),
+               "rope scatter");
+    }
+    {
+      Prof p(h, PK_ATTN_PREFILL, Md * (2.0 * Dd + 2.0 * KVW) * E,
+             4.0 * B * lo.H * lo.dh * (double)n0 * (n0 + 1) / 2.0);
+      BT_CHECK(h, launch_prefill_attention(lo.f32, P_(h, lo.QKV), B, n0, lo.H, lo.Hkv, lo.dh,
+                                           (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
+                                           P_(h, lo.ACT), lo.blk[l].k2, h->st, h->rmap),
+               "prefill attention");
+    }
+    r = run_out(h, lo.blk[l], M);
+    if (r) return r;
+  }
+  int r;
+  if (ragged && n0 > 1) {
+    // the context of each row is its last real block: move it to the row's last activation slot
+    if (h->pending.nsplit) {
+      // the last layer's split-K residual is normally folded in by the LayerNorm that reads the
+      // context row, after this move: fold it into every row first (its outputs are scratch)
+      Prof p(h, PK_LN, Md * Dd * (4.0 + E), 8.0 * Md * Dd);
+      BT_CHECK(h, launch_layernorm((float*)P_(h, lo.X), M, lo.D, 1, 0, (const float*)P_(h, lo.lnf_blk),
+                                   ln_buf(h, 0), nullptr, nullptr, lo.f32, h->cfg.ln_eps, pending(h), h->st),
+               "fold residual");
+      h->pending.nsplit = 0;
+    }
+    Prof p(h, PK_EMBED, (double)B * Dd * 8.0, 0.0);
+    BT_CHECK(h, launch_gather_last((float*)P_(h, lo.X), B, n0, lo.D, (const int*)P_(h, lo.lastblk), h->st),
+             "last prompt blocks");
+  }
+  if (lo.vanilla) {
+    if ((r = run_head(h, n0, n0 - 1, d_logits))) return r;
+  } else {
+    if ((r = run_prefix(h, n0, n0 - 1))) return r;
+    if ((r = run_token_decoder(h, lo.lead, 0))) return r;
+    if ((r = run_head(h, lo.lead, lo.lead - 1, d_logits))) return r;
+  }
+  return run_finalize(h, 0, d_next, 0);
 }
 
-int bt_prefill_lengths(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
-                       int32_t* d_next, float* d_logits) {
-  if (!d_lengths) return fail(BT_ERR_INVALID_ARG, "NULL argument");
-  return prefill_impl(h, d_prompt, d_lengths, B, T, d_next, d_logits);
-}
-
 static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
-                        int32_t* d_next, float* d_logits) {
+                        int32_t* d_next, float* d_logits, bool ragged) {
   if (!h || !d_prompt || !d_next) return fail(BT_ERR_INVALID_ARG, "NULL argument");
   if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
   const Layout& lo = h->lo;
@@ -757,53 +837,75 @@ static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_
   if (B != h->graph_B) drop_graphs(h);
   h->B = B;
   h->Tp = Tp;
-  h->pending.nsplit = 0;
+  h->rmap = nullptr;
   h->dec_nsplit = decode_splits(B, lo.H, lo.Hkv, lo.ncap);
-  const int n0 = Tp / L;
-  const int M = B * n0;
-  h->decode_phase = false;
-  const double E = (double)lo.elem, Dd = lo.D, Md = M, KVW = (double)lo.Hkv * lo.dh;
-  {
-    Prof p(h, PK_EMBED, Md * Dd * (lo.tab_elem + 4.0) + (double)B * T * 4.0, 0.0);
-    BT_CHECK(h, launch_embed_prompt(d_prompt, d_lengths, B, T, Tp, h->cfg.pad_id, P_(h, lo.emb_block), !lo.f32, lo.V,
-                                    lo.De, L, (float*)P_(h, lo.X), (int*)P_(h, lo.dstate), h->st),
-             "embed prompt");
-  }
-  for (int l = 0; l < lo.Nb; ++l) {
-    int r = run_ln_qkv(h, lo.blk[l], M);
-    if (r) return r;
-    {
-      Prof p(h, PK_ROPE_SCATTER, Md * 4.0 * KVW * E, 3.0 * Md * KVW);
-      BT_CHECK(h, launch_rope_scatter(lo.f32, P_(h, lo.QKV), B, n0, 0, lo.H, lo.Hkv, lo.dh,
-                                      (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap, true,
-                                      h->st),
-               "rope scatter");
-    }
-    {
-      Prof p(h, PK_ATTN_PREFILL, Md * (2.0 * Dd + 2.0 * KVW) * E,
-             4.0 * B * lo.H * lo.dh * (double)n0 * (n0 + 1) / 2.0);
-      BT_CHECK(h, launch_prefill_attention(lo.f32, P_(h, lo.QKV), B, n0, lo.H, lo.Hkv, lo.dh,
-                                           (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
-                                           P_(h, lo.ACT), lo.blk[l].k2, h->st),
-               "prefill attention");
-    }
-    r = run_out(h, lo.blk[l], M);
-    if (r) return r;
-  }
-  int r;
-  if (lo.vanilla) {
-    if ((r = run_head(h, n0, n0 - 1, d_logits))) return r;
-  } else {
-    if ((r = run_prefix(h, n0, n0 - 1))) return r;
-    if ((r = run_token_decoder(h, lo.lead, 0))) return r;
-    if ((r = run_head(h, lo.lead, lo.lead - 1, d_logits))) return r;
-  }
-  r = run_finalize(h, 0, d_next, 0);
+  int r = prefill_core(h, d_prompt, d_lengths, T, Tp, ragged, d_next, d_logits);
   if (r) return r;
-  h->n_blocks = n0;
+  h->n_blocks = Tp / L;
   h->local_len = lo.vanilla ? 0 : lo.lead;
+  h->row_tok.assign(B, (int64_t)Tp + 1);
   h->g = 1;
   h->ready = true;
+  return BT_OK;
+}
+
+int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int32_t* d_next, float* d_logits) {
+  return prefill_impl(h, d_prompt, nullptr, B, T, d_next, d_logits, false);
+}
+
+int bt_prefill_lengths(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
+                       int32_t* d_next, float* d_logits) {
+  if (!d_lengths) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  return prefill_impl(h, d_prompt, d_lengths, B, T, d_next, d_logits, false);
+}
+
+int bt_prefill_ragged(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
+                      int32_t* d_next, float* d_logits) {
+  if (!d_lengths) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  return prefill_impl(h, d_prompt, d_lengths, B, T, d_next, d_logits, true);
+}
+
+int bt_prefill_rows(bt_handle* h, const int32_t* rows, int32_t B_new, const int32_t* d_prompt,
+                    const int32_t* d_lengths, int32_t T, int32_t* d_next, float* d_logits) {
+  if (!h || !rows || !d_prompt || !d_lengths || !d_next) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
+  if (!h->ready) return fail(BT_ERR_STATE, "bt_prefill_rows before bt_prefill");
+  const Layout& lo = h->lo;
+  if (lo.mode != BT_CTX_PREFIX) return fail(BT_ERR_UNSUPPORTED, "rows join only with BT_CTX_PREFIX");
+  if (B_new < 1 || B_new > h->B || T < 1) return fail(BT_ERR_INVALID_ARG, "B_new must be in [1, B], T >= 1");
+  std::vector<char> seen(h->B, 0);
+  for (int i = 0; i < B_new; ++i) {
+    if (rows[i] < 0 || rows[i] >= h->B || seen[rows[i]]) return fail(BT_ERR_INVALID_ARG, "rows must be distinct, in [0, B)");
+    seen[rows[i]] = 1;
+  }
+  const int L = lo.L;
+  if (h->g % L != 1 % L)
+    return fail(BT_ERR_STATE, "rows join only where a block starts (after a step that emitted a block's first token)");
+  const int Tp = std::max(L, (T + L - 1) / L * L);
+  if ((int64_t)Tp + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "padded prompt + 1 exceeds max_tokens");
+  if (Tp > lo.max_prompt) return fail(BT_ERR_CAPACITY, "padded prompt exceeds max_prompt_tokens");
+  BT_CHECK(h, hipMemcpyAsync(P_(h, lo.rowmap), rows, (size_t)B_new * 4, hipMemcpyHostToDevice, h->st), "row map");
+  // the join runs its own classifier at B_new rows; the running batch's (possibly replayed from a
+  // graph, which does not record it) column-group count must survive for its finalisations
+  const int running_B = h->B, running_nparts = h->head_nparts;
+  h->B = B_new;
+  h->rmap = (const int*)P_(h, lo.rowmap);
+  int r = prefill_core(h, d_prompt, d_lengths, T, Tp, true, d_next, d_logits);
+  h->B = running_B;
+  h->head_nparts = running_nparts;
+  h->rmap = nullptr;
+  h->pending.nsplit = 0;
+  if (r) {
+    h->ready = false;  // some rows may be half written
+    return r;
+  }
+  // the prefill used the activation rows that held every row's next-step input: rebuild them
+  if ((r = run_prepare_inputs(h))) {
+    h->ready = false;
+    return r;
+  }
+  for (int i = 0; i < B_new; ++i) h->row_tok[rows[i]] = (int64_t)Tp + 1;
+  h->n_blocks = std::max(h->n_blocks, Tp / L);
   return BT_OK;
 }
 
@@ -812,7 +914,9 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
   if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
   if (!h->ready) return fail(BT_ERR_STATE, "bt_decode_step before bt_prefill");
   const Layout& lo = h->lo;
-  if ((int64_t)h->Tp + h->g + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "max_tokens reached");
+  int64_t most = 0;
+  for (int64_t t : h->row_tok) most = std::max(most, t);
+  if (most + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "max_tokens reached");
   const int j = h->g % lo.L;
   h->decode_phase = true;
   int r;
@@ -850,6 +954,15 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
   r = run_finalize(h, j, d_next, j == 0 ? 1 : 0);
   if (r) return r;
   h->g += 1;
+  for (int64_t& t : h->row_tok) t += 1;
+  return BT_OK;
+}
+
+int bt_block_lengths(bt_handle* h, int32_t* lengths) {
+  if (!h || !lengths) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  if (!h->ready) return fail(BT_ERR_STATE, "bt_block_lengths before bt_prefill");
+  BT_CHECK(h, hipStreamSynchronize(h->st), "synchronize");
+  BT_CHECK(h, hipMemcpy(lengths, P_(h, h->lo.dstate), (size_t)h->B * 4, hipMemcpyDeviceToHost), "copy");
   return BT_OK;
 }
 

@@ -52,12 +52,12 @@ __device__ __forceinline__ T round_t(float v) { return from_f32<T>(v); }
 template <typename T>
 __global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV, int m, int s0, int H, int Hkv, int dh,
                                                       const float2* __restrict__ rope, T* __restrict__ Kc,
-                                                      T* __restrict__ Vc, int cap, int vt) {
+                                                      T* __restrict__ Vc, int cap, int vt, const int* __restrict__ rmap) {
   __shared__ T vtile[64][129];
   const int hk = blockIdx.y, b = blockIdx.z, i0 = blockIdx.x * 64;
   const int half = dh / 2, tid = threadIdx.x;
   const size_t qw = (size_t)(H + 2 * Hkv) * dh, koff = (size_t)(H + hk) * dh, voff = (size_t)(H + Hkv + hk) * dh;
-  const size_t bh = (size_t)b * Hkv + hk;
+  const size_t bh = (size_t)(rmap ? rmap[b] : b) * Hkv + hk;
   const int cnt = min(64, m - i0);
   for (int e = tid; e < cnt * half; e += 256) {
     const int si = e / half, c = e % half, i = i0 + si, slot = s0 + i;
@@ -87,16 +87,17 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV,
 }
 
 hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
-                               const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed, hipStream_t st) {
+                               const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed, hipStream_t st,
+                               const int* rmap) {
   if (B <= 0 || m <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
   dim3 grid((m + 63) / 64, Hkv, B);
   if (f32)
     hipLaunchKernelGGL(k_rope_scatter<float>, grid, dim3(256), 0, st, (const float*)QKV, m, s0, H, Hkv, dh, rope,
-                       (float*)Kc, (float*)Vc, cap, (int)v_transposed);
+                       (float*)Kc, (float*)Vc, cap, (int)v_transposed, rmap);
   else
     hipLaunchKernelGGL(k_rope_scatter<f16>, grid, dim3(256), 0, st, (const f16*)QKV, m, s0, H, Hkv, dh, rope,
-                       (f16*)Kc, (f16*)Vc, cap, (int)v_transposed);
+                       (f16*)Kc, (f16*)Vc, cap, (int)v_transposed, rmap);
   return hipGetLastError();
 }
 
@@ -111,7 +112,7 @@ template <int DH>
 __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ QKV, int n, int H, int Hkv,
                                                        const float2* __restrict__ rope, const f16* __restrict__ Kc,
                                                        const f16* __restrict__ VTc, int cap, f16* __restrict__ ACT,
-                                                       int ld_act, float scale_log2) {
+                                                       int ld_act, float scale_log2, const int* __restrict__ rmap) {
   constexpr int KS = DH / 32;   // 32-wide dh slices of q and k
   constexpr int MT = DH / 16;   // 16-row dh tiles of O^T
   constexpr int KLD = DH + 8;   // LDS row strides (+16 B: conflict-free fragment reads)
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
   const int q0 = qt * 64 + wave * 16;
   const int qi = q0 + c16;
   const int qrow = min(qi, n - 1);
-  const size_t bh = (size_t)b * Hkv + h / (H / Hkv);
+  const size_t bh = (size_t)(rmap ? rmap[b] : b) * Hkv + h / (H / Hkv);
   const f16* __restrict__ K = Kc + bh * cap * DH;
   const f16* __restrict__ VT = VTc + bh * DH * cap;
 
@@ -274,12 +275,12 @@ template <typename T>
 __global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, int n, int H, int Hkv, int dh,
                                                    const float2* __restrict__ rope, const T* __restrict__ Kc,
                                                    const T* __restrict__ VTc, int cap, T* __restrict__ ACT,
-                                                   int ld_act, float scale) {
+                                                   int ld_act, float scale, const int* __restrict__ rmap) {
   extern __shared__ float sm[];
   float* q = sm;          // [dh]
   float* sc = sm + 128;   // [n]
   const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  const size_t bh = (size_t)b * Hkv + h / (H / Hkv);
+  const size_t bh = (size_t)(rmap ? rmap[b] : b) * Hkv + h / (H / Hkv);
   const T* qp = QKV + ((size_t)b * n + qi) * (H + 2 * Hkv) * dh + h * dh;
   const int half = dh / 2;
   for (int c = lane; c < half; c += 64) {
@@ -316,23 +317,23 @@ __global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, in
 
 hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int H, int Hkv, int dh,
                                     const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
-                                    int ld_act, hipStream_t st) {
+                                    int ld_act, hipStream_t st, const int* rmap) {
   if (B <= 0 || n <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
   const float scale = 1.0f / sqrtf((float)dh);
   if (f32) {
     size_t lds = (128 + (size_t)n) * sizeof(float);
     hipLaunchKernelGGL(k_attn_naive<float>, dim3(n, H, B), dim3(64), lds, st, (const float*)QKV, n, H, Hkv, dh, rope,
-                       (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale);
+                       (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale, rmap);
     return hipGetLastError();
   }
   dim3 grid((n + 63) / 64, H, B);
   if (dh == 64)
     hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
-                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e);
+                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap);
   else if (dh == 128)
     hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
-                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e);
+                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -367,7 +368,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   const int hk = blockIdx.y / nsub, run = blockIdx.y % nsub;
   const int h0 = hk * G + run * gsz, gcnt = min(gsz, G - run * gsz);  // query heads [h0, h0 + gcnt)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = *n_ptr;  // entries already cached; the new one goes to slot n
+  // entries already cached in this row; the new one goes to slot n (the host keeps every row below
+  // the capacity; the clamp only keeps a misused row inside its own cache)
+  const int n = min(n_ptr[b], cap - 1);
   const size_t bk = (size_t)b * Hkv + hk;
   T* __restrict__ K = Kc + bk * cap * DH;
   T* __restrict__ VT = VTc + bk * DH * cap;
@@ -627,14 +630,14 @@ template <typename T, int DH>
 __global__ __launch_bounds__(64) void k_local_attn(const T* __restrict__ QKV, int ldq, int m, int s0, int H, int Hkv,
                                                    const float2* __restrict__ rope, T* __restrict__ Kc,
                                                    T* __restrict__ Vc, int cap, T* __restrict__ ACT, int ld_act,
-                                                   float scale) {
+                                                   float scale, const int* __restrict__ rmap) {
   __shared__ float ks[kMaxLocal][DH + 1], vs[kMaxLocal][DH + 1], qs[kMaxLocal][DH + 1];
   __shared__ float ps[64];
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int G = H / Hkv, hk = h / G;
   const bool writes = h % G == 0;
   const size_t qw = (size_t)ldq, koff = (size_t)(H + hk) * DH, voff = (size_t)(H + Hkv + hk) * DH;
-  const size_t bh = (size_t)b * Hkv + hk;
+  const size_t bh = (size_t)(rmap ? rmap[b] : b) * Hkv + hk;
   T* __restrict__ K = Kc + bh * cap * DH;
   T* __restrict__ V = Vc + bh * cap * DH;
   constexpr int HALF = DH / 2;
@@ -711,7 +714,7 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
                                                          int Hkv,
                                                          const float2* __restrict__ rope, T* __restrict__ Kc,
                                                          T* __restrict__ Vc, int cap, T* __restrict__ ACT, int ld_act,
-                                                         float scale_log2) {
+                                                         float scale_log2, const int* __restrict__ rmap) {
   constexpr int LPK = DH / 8, KPP = 64 / LPK, HALF = DH / 2;
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -719,7 +722,7 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
   const int b = pair / H, h = pair % H;
   const int g = lane % LPK, kg = lane / LPK;  // dimensions [8g, 8g + 8), key group
   const int G = H / Hkv, hk = h / G;
-  const size_t bh = (size_t)b * Hkv + hk;
+  const size_t bh = (size_t)(rmap ? rmap[b] : b) * Hkv + hk;
   T* __restrict__ K = Kc + bh * cap * DH;
   T* __restrict__ V = Vc + bh * cap * DH;
   const T* row = QKV + (size_t)b * ldq + 8 * g;
@@ -797,7 +800,7 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
 
 hipError_t launch_local_attention(bool f32, const void* QKV, int ldq, int B, int m, int s0, int H, int Hkv, int dh,
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
-                                  hipStream_t st) {
+                                  hipStream_t st, const int* rmap) {
   if (B <= 0 || m <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv || ldq < (H + 2 * Hkv) * dh || ldq % 8) return hipErrorInvalidValue;
   if (s0 + m > kMaxLocal || s0 + m > cap) return hipErrorInvalidValue;
@@ -809,7 +812,7 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int ldq, int B, int
   if (dh == DHV) {                                                                                              \
     hipLaunchKernelGGL((k_local_attn_step<T, DHV>), g1, dim3(256), 0, st, (const T*)QKV, ldq, B, s0, H, Hkv,     \
                        rope,                                                                                    \
-                       (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale * kLog2e);                                    \
+                       (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale * kLog2e, rmap);                              \
     return hipGetLastError();                                                                                   \
   }
     if (f32) {
@@ -824,7 +827,7 @@ hipError_t launch_local_attention(bool f32, const void* QKV, int ldq, int B, int
 #define BT_LOC(T, DHV)                                                                                          \
   if (dh == DHV) {                                                                                              \
     hipLaunchKernelGGL((k_local_attn<T, DHV>), grid, dim3(64), 0, st, (const T*)QKV, ldq, m, s0, H, Hkv, rope,  \
-                       (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale);                                             \
+                       (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, scale, rmap);                                       \
     return hipGetLastError();                                                                                   \
   }
   if (f32) {

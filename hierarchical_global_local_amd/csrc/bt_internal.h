@@ -80,7 +80,9 @@ struct Layout {
   size_t rpart; // fp32 [16][rpart_rows][D] split-K partials of the [out|down] GEMM (decode)
   int rpart_rows;
   size_t cur;   // int32 [Bmax][L] ids of the block being generated
-  size_t dstate;  // int32 device state: [0] = block-KV entries per layer
+  size_t dstate;  // int32 [Bmax] device state: block-KV entries of each row (per layer)
+  size_t rowmap;  // int32 [Bmax]: cache rows of the rows a join prefills
+  size_t lastblk; // int32 [Bmax]: last real prompt block of each prefilled row
   size_t total;
   size_t block_kv_bytes, local_kv_bytes;
   // canonical blob offsets (bytes)
@@ -116,11 +118,16 @@ hipError_t launch_rows_init(float* X, int B, int D, const float* base, const flo
 hipError_t launch_rope_table(float2* tab, int npos, int dh, float base, hipStream_t st);
 
 // ---- embedders
-// prompt blocks: X[b*n + i][o*De + d] = E[tok(b, i*L + o)][d], tok from the left-padded prompt: row b
-// holds len_b tokens at positions [0, len_b) (len_b = T without `lengths`, else lengths[b] clamped to
-// [1, T]) and is padded on the left to Tp.  Also sets the device block-KV length *n_state = Tp / L.
+// prompt blocks: X[b*n + i][o*De + d] = E[tok(b, i*L + o)][d], n = Tp / L, tok from the left-padded
+// prompt: row b holds len_b tokens at positions [0, len_b) (len_b = T without `lengths`, else
+// lengths[b] clamped to [1, T]) and is padded on the left to Tp, or with `ragged` to its own
+// n_b = ceil(len_b / L) blocks, left-aligned (blocks i >= n_b hold pad tokens).  Sets the row's
+// block-KV length n_state[rmap ? rmap[b] : b] = n_b and, if `last` is given, last[b] = n_b - 1.
 hipError_t launch_embed_prompt(const int32_t* prompt, const int32_t* lengths, int B, int T, int Tp, int pad, const void* E,
-                               bool tab_bf16, int V, int De, int L, float* X, int* n_state, hipStream_t st);
+                               bool tab_bf16, int V, int De, int L, float* X, int* n_state, bool ragged,
+                               const int* rmap, int* last, hipStream_t st);
+// X row (b, n - 1) = X row (b, last[b]) for rows b < B of an activation laid out [B][n][D]
+hipError_t launch_gather_last(float* X, int B, int n, int D, const int* last, hipStream_t st);
 // ---- LayerNorm over rows r < rows of X[(r*stride + off)][:] -> out1 (params p1), out2 (p2, optional).
 // With `resid` (split-K residual update pending), the row is first completed as
 //   x = X + sum_{s < nsplit} part[s][row][:] + bias_a + bias_b   (fixed summation order)
@@ -178,15 +185,17 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
 //
 // rotary + scatter of K (row-major [slot][dh]) and V (block cache: transposed [dh][slot]) for rows
 // (b, i) of QKV [B*m][QW] into cache slots s0 + i, at rotary positions s0 + i.
+// (rmap: optional cache row of each activation row b, for a prefill into rows of a running batch;
+// the same argument of the prefill and local attention launchers)
 hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed,
-                               hipStream_t st);
+                               hipStream_t st, const int* rmap = nullptr);
 // causal prefill attention of rows (b, i < n) at positions i over cache entries [0, i]
 hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int H, int Hkv, int dh,
                                     const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
-                                    int ld_act, hipStream_t st);
-// one new block-decoder position per row: n = *n_ptr (device state) entries are cached; rotary at
-// position n, append K/V at slot n, attend over [0, n].  nsplit = decode_splits(B, H, Hkv, cap)
+                                    int ld_act, hipStream_t st, const int* rmap = nullptr);
+// one new block-decoder position per row: n = n_ptr[b] (device state of row b) entries are cached;
+// rotary at position n, append K/V at slot n, attend over [0, n].  nsplit = decode_splits(B, H, Hkv, cap)
 // splits of the capacity (fixed for a batch size, so the launch does not depend on n).
 int decode_splits(int B, int H, int Hkv, int cap);
 hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int H, int Hkv, int dh,
@@ -196,7 +205,7 @@ hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int*
 // (ldq = QKV row stride, >= (H + 2 Hkv) dh: token layers with cross-attention carry its queries too)
 hipError_t launch_local_attention(bool f32, const void* QKV, int ldq, int B, int m, int s0, int H, int Hkv, int dh,
                                   const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
-                                  hipStream_t st);
+                                  hipStream_t st, const int* rmap = nullptr);
 // cross-attention of one slot per row: query head h of row b (QKV[b * ldq + qoff + h dh ..], no rotary)
 // over the P encoder states of row b, keys and values (fp32) at XKV[(b P + p) * ldx + koff + ..]
 // (keys of KV head hk at hk dh, values at Hkv dh + hk dh); output to ACT columns act_col + h dh.
@@ -223,7 +232,10 @@ struct NextStepArgs {
   const float* add = nullptr;  // token step: fp32 [B][add_ld] added to the embedding (summation)
   int add_ld = 0;
 };
+// rmap: cache/state row of each row b (cur, n_state); from_cur: no argmax, the next step's input is
+// prepared from the id already at cur[b][j] (next, cur and n_state untouched)
 hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, int B, int32_t* next, int32_t* cur,
-                           int L, int j, int* n_state, int n_inc, const NextStepArgs& nxt, hipStream_t st);
+                           int L, int j, int* n_state, int n_inc, const NextStepArgs& nxt, hipStream_t st,
+                           const int* rmap = nullptr, bool from_cur = false);
 
 }  // namespace bt

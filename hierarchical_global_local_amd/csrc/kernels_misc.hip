@@ -164,31 +164,49 @@ template <typename Tt>
 __global__ __launch_bounds__(256) void k_embed_prompt(const int32_t* __restrict__ prompt,
                                                       const int32_t* __restrict__ lengths, int T, int Tp, int pad,
                                                       const Tt* __restrict__ E, int V, int De, int L,
-                                                      float* __restrict__ X, int* __restrict__ n_state) {
-  const int n = Tp / L;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *n_state = n;
+                                                      float* __restrict__ X, int* __restrict__ n_state, int ragged,
+                                                      const int* __restrict__ rmap, int* __restrict__ last) {
+  const int n = Tp / L;        // blocks per row in the activation layout
   const int row = blockIdx.x;  // b * n + i
   const int b = row / n, i = row % n;
   const int D = De * L;
   const int len = lengths ? min(max(lengths[b], 1), T) : T;
+  // blocks of this row: every row padded to Tp, or (ragged) to its own multiple of L, left-aligned
+  const int nb = ragged ? (len + L - 1) / L : n;
+  if (i == 0 && threadIdx.x == 0) {
+    n_state[rmap ? rmap[b] : b] = nb;
+    if (last) last[b] = nb - 1;
+  }
   for (int c = threadIdx.x; c < D; c += 256) {
     int o = c / De, d = c % De;
-    int p = i * L + o - (Tp - len);  // position in the row's unpadded prompt
-    int tok = p < 0 ? pad : prompt[(size_t)b * T + p];
+    int p = i * L + o - (nb * L - len);  // position in the row's unpadded prompt
+    int tok = (p < 0 || i >= nb) ? pad : prompt[(size_t)b * T + p];
     X[(size_t)row * D + c] = load_f32(E + (size_t)clamp_id(tok, V) * De + d);
   }
 }
 
 hipError_t launch_embed_prompt(const int32_t* prompt, const int32_t* lengths, int B, int T, int Tp, int pad,
                                const void* E, bool tab_bf16, int V, int De, int L, float* X, int* n_state,
-                               hipStream_t st) {
+                               bool ragged, const int* rmap, int* last, hipStream_t st) {
   dim3 grid(B * (Tp / L));
   if (tab_bf16)
     hipLaunchKernelGGL(k_embed_prompt<bf16_t>, grid, dim3(256), 0, st, prompt, lengths, T, Tp, pad, (const bf16_t*)E,
-                       V, De, L, X, n_state);
+                       V, De, L, X, n_state, (int)ragged, rmap, last);
   else
     hipLaunchKernelGGL(k_embed_prompt<float>, grid, dim3(256), 0, st, prompt, lengths, T, Tp, pad, (const float*)E, V,
-                       De, L, X, n_state);
+                       De, L, X, n_state, (int)ragged, rmap, last);
+  return hipGetLastError();
+}
+
+// X row (b, n - 1) = X row (b, last[b]): the last real block of a ragged row where the prefill
+// tail reads its context embedding
+__global__ void k_gather_last(float* __restrict__ X, int n, int D, const int* __restrict__ last) {
+  const int b = blockIdx.y, d = blockIdx.x * 256 + threadIdx.x;
+  const int src = last[b];
+  if (d < D && src != n - 1) X[((size_t)b * n + n - 1) * D + d] = X[((size_t)b * n + src) * D + d];
+}
+hipError_t launch_gather_last(float* X, int B, int n, int D, const int* last, hipStream_t st) {
+  hipLaunchKernelGGL(k_gather_last, dim3((D + 255) / 256, B), dim3(256), 0, st, X, n, D, last);
   return hipGetLastError();
 }
 
@@ -393,32 +411,40 @@ struct NextStep {
 template <int PER, typename Tt, typename To>
 __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __restrict__ keys, int nparts, int ld,
                                                   int32_t* __restrict__ next, int32_t* __restrict__ cur, int L,
-                                                  int j, int* __restrict__ n_state, int n_inc, NextStep ns) {
+                                                  int j, int* __restrict__ n_state, int n_inc, NextStep ns,
+                                                  const int* __restrict__ rmap, int from_cur) {
   __shared__ unsigned long long red[4];
   __shared__ float redf[4];
   const int b = blockIdx.x, tid = threadIdx.x;
-  if (b == 0 && tid == 0 && n_inc) *n_state += n_inc;
-  // the row's keys are contiguous: 256 threads read 2 KB per pass (max is order-independent)
-  const unsigned long long* kr = keys + (size_t)b * ld;
-  unsigned long long best = 0ull;
-  for (int p = tid; p < nparts; p += 256) {
-    const unsigned long long k = kr[p];
-    best = k > best ? k : best;
-  }
+  const int cb = rmap ? rmap[b] : b;  // the row's index in the caches and step state
+  if (tid == 0 && n_inc) n_state[cb] += n_inc;
+  int id;
+  if (from_cur) {
+    // only the next step's input, from the id already at offset j of the current block
+    id = cur[(size_t)b * L + j];
+  } else {
+    // the row's keys are contiguous: 256 threads read 2 KB per pass (max is order-independent)
+    const unsigned long long* kr = keys + (size_t)b * ld;
+    unsigned long long best = 0ull;
+    for (int p = tid; p < nparts; p += 256) {
+      const unsigned long long k = kr[p];
+      best = k > best ? k : best;
+    }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long k = shfl_xor_u64(best, o);
-    best = k > best ? k : best;
-  }
-  if ((tid & 63) == 0) red[tid >> 6] = best;
-  __syncthreads();
-  best = red[0];
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long k = shfl_xor_u64(best, o);
+      best = k > best ? k : best;
+    }
+    if ((tid & 63) == 0) red[tid >> 6] = best;
+    __syncthreads();
+    best = red[0];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) best = red[w] > best ? red[w] : best;
-  const int id = (int)(0xFFFFFFFFu - (unsigned)(best & 0xFFFFFFFFull));
-  if (tid == 0) {
-    next[b] = id;
-    cur[b * L + j] = id;
+    for (int w = 1; w < 4; ++w) best = red[w] > best ? red[w] : best;
+    id = (int)(0xFFFFFFFFu - (unsigned)(best & 0xFFFFFFFFull));
+    if (tid == 0) {
+      next[b] = id;
+      cur[(size_t)cb * L + j] = id;
+    }
   }
   if (ns.mode == 0) return;
   const int D = ns.D;
@@ -433,7 +459,7 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
       tok = id, col = cc;
     } else {
       const int o = cc / ns.width;
-      tok = o == j ? id : cur[b * L + o];
+      tok = o == j ? id : cur[(size_t)cb * L + o];
       col = cc - o * ns.width;
     }
     tok = tok < 0 ? 0 : (tok >= ns.V ? ns.V - 1 : tok);
@@ -476,37 +502,38 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
 template <int PER>
 static void launch_fin_cfg(bool tab_bf16, bool out_f32, int B, const unsigned long long* keys, int nparts, int ld,
                            int32_t* next, int32_t* cur, int L, int j, int* n_state, int n_inc, const NextStep& ns,
-                           hipStream_t st) {
+                           const int* rmap, int from_cur, hipStream_t st) {
   if (tab_bf16) {
     if (out_f32)
       hipLaunchKernelGGL((k_finalize<PER, bf16_t, float>), dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j,
-                         n_state, n_inc, ns);
+                         n_state, n_inc, ns, rmap, from_cur);
     else
       hipLaunchKernelGGL((k_finalize<PER, bf16_t, f16>), dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j,
-                         n_state, n_inc, ns);
+                         n_state, n_inc, ns, rmap, from_cur);
   } else {
     if (out_f32)
       hipLaunchKernelGGL((k_finalize<PER, float, float>), dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j,
-                         n_state, n_inc, ns);
+                         n_state, n_inc, ns, rmap, from_cur);
     else
       hipLaunchKernelGGL((k_finalize<PER, float, f16>), dim3(B), dim3(256), 0, st, keys, nparts, ld, next, cur, L, j,
-                         n_state, n_inc, ns);
+                         n_state, n_inc, ns, rmap, from_cur);
   }
 }
 
 hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, int B, int32_t* next, int32_t* cur,
-                           int L, int j, int* n_state, int n_inc, const NextStepArgs& a, hipStream_t st) {
+                           int L, int j, int* n_state, int n_inc, const NextStepArgs& a, hipStream_t st,
+                           const int* rmap, bool from_cur) {
   if (B <= 0) return hipSuccess;
   NextStep ns{a.mode, a.E, a.width, a.X, a.lnp, a.ln1, a.ln2, a.D, a.V, a.eps, a.add, a.add_ld};
   const int per = (a.D + 255) / 256;
   if (per <= 1)
-    launch_fin_cfg<1>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);
+    launch_fin_cfg<1>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, rmap, (int)from_cur, st);
   else if (per <= 3)
-    launch_fin_cfg<3>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);
+    launch_fin_cfg<3>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, rmap, (int)from_cur, st);
   else if (per <= 8)
-    launch_fin_cfg<8>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);
+    launch_fin_cfg<8>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, rmap, (int)from_cur, st);
   else if (per <= 16)
-    launch_fin_cfg<16>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, st);
+    launch_fin_cfg<16>(a.tab_bf16, a.out_f32, B, keys, nparts, ld, next, cur, L, j, n_state, n_inc, ns, rmap, (int)from_cur, st);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -156,6 +156,33 @@ int bt_prefill(bt_handle* h, const int32_t* d_prompt, int32_t B, int32_t T, int3
 int bt_prefill_lengths(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
                        int32_t* d_next, float* d_logits);
 
+/* Prefill in which every row is padded only to its own whole number of blocks (summary page §3.4
+ * "The Embedder": left padding to a multiple of L_B): row b (device int32 [B, T], its lengths[b]
+ * tokens in columns [0, lengths[b])) gets ceil(len_b / L_B) blocks, so rows keep block-KV lengths of
+ * their own and each row's result equals a prefill of that row alone.  The activations are sized
+ * for ceil(T / L_B) blocks per row (shorter rows leave the rest unused).  d_lengths: device int32
+ * [B], clamped to [1, T].  Other arguments, capacities and errors as bt_prefill. */
+int bt_prefill_ragged(bt_handle* h, const int32_t* d_prompt, const int32_t* d_lengths, int32_t B, int32_t T,
+                      int32_t* d_next, float* d_logits);
+
+/* Continuous batching: new sequences take over rows of the running batch while the other rows keep
+ * decoding.  Rows rows[0..B_new) (host int32, distinct, each in [0, B) of the running batch) are
+ * prefilled with the prompts of d_prompt / d_lengths exactly as bt_prefill_ragged would (each row
+ * padded to its own whole blocks, block-KV length of its own); their first token goes to d_next
+ * (device int32 [B_new]) and, if d_logits is not NULL, its logits to d_logits (fp32 [B_new, V]).
+ * The other rows are untouched, and the next bt_decode_step advances every row by one token.
+ * Rows join where a block starts, that is right after a call that emitted the first token of a
+ * block (bt_prefill, or a decode step at in-block offset 0; any step when L_B = 1), so that every
+ * row is at the same in-block offset: else BT_ERR_STATE.  BT_CTX_PREFIX only
+ * (BT_ERR_UNSUPPORTED otherwise).  Capacities as bt_prefill for the new prompts; every row's
+ * tokens stay bounded by max_tokens (bt_decode_step returns BT_ERR_CAPACITY before any row would
+ * exceed it). */
+int bt_prefill_rows(bt_handle* h, const int32_t* rows, int32_t B_new, const int32_t* d_prompt,
+                    const int32_t* d_lengths, int32_t T, int32_t* d_next, float* d_logits);
+
+/* Block-KV entries of each row of the running batch (host int32 [B]); synchronises the stream. */
+int bt_block_lengths(bt_handle* h, int32_t* lengths);
+
 /* One decode step (summary page §3.4, decode stage): feeds back the token the
  * previous call emitted and writes the next token of every row to d_next
  * (device int32 [B]; B is the prefill's batch), plus its fp32 logits [B, V] if
@@ -174,7 +201,8 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits);
 int bt_set_graphs(bt_handle* h, int32_t enable);
 
 /* Host mirror of the cache lengths after the last call: block-KV entries per
- * block-decoder layer and local-KV entries per token-decoder layer. */
+ * block-decoder layer (the largest over the rows after a ragged prefill or a join; see
+ * bt_block_lengths) and local-KV entries per token-decoder layer. */
 int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_kv_len);
 
 /* Read-only introspection of the workspace layout, for tests and tools.
