@@ -40,16 +40,17 @@ class BtConfig(ctypes.Structure):
                 ("block_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32), ("pad_id", ctypes.c_int32),
                 ("ln_eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("max_prompt_tokens", ctypes.c_int32),
-                ("n_kv_heads", ctypes.c_int32), ("context_mode", ctypes.c_int32)]
+                ("n_kv_heads", ctypes.c_int32), ("context_mode", ctypes.c_int32), ("kv_pages", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, model, max_batch: int, max_tokens: int, max_prompt_tokens: int = 0) -> "BtConfig":
+    def make(cls, model, max_batch: int, max_tokens: int, max_prompt_tokens: int = 0,
+             kv_pages: int = 0) -> "BtConfig":
         """From any object with the model fields (vocab, d_model, ..., dtype "fp32"/"bf16")."""
         return cls(model.vocab, model.d_model, model.n_heads, model.d_mlp, model.n_block_layers,
                    model.n_token_layers, model.block_len, model.prefix_len, max_batch, max_tokens,
                    BT_FP32 if model.dtype == "fp32" else BT_BF16, model.pad_id, model.ln_eps, model.rope_base,
                    max_prompt_tokens, getattr(model, "n_kv_heads", 0),
-                   CONTEXT_MODES[getattr(model, "context_mode", "prefix")])
+                   CONTEXT_MODES[getattr(model, "context_mode", "prefix")], kv_pages)
 
 
 _lib = None
@@ -74,6 +75,7 @@ def lib() -> ctypes.CDLL:
     L.bt_prefill_ragged.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_p, c_p]
     L.bt_prefill_rows.argtypes = [c_p, ctypes.POINTER(c_i32), c_i32, c_p, c_p, c_i32, c_p, c_p]
     L.bt_block_lengths.argtypes = [c_p, ctypes.POINTER(c_i32)]
+    L.bt_page_table.argtypes = [c_p, ctypes.POINTER(c_i32)]
     L.bt_decode_step.argtypes = [c_p, c_p, c_p]
     L.bt_cache_lengths.argtypes = [c_p, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
     L.bt_workspace_region.argtypes = [cfgp, c_i32, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz), ctypes.POINTER(c_i32)]
@@ -86,7 +88,7 @@ def lib() -> ctypes.CDLL:
     L.bt_set_graphs.argtypes = [c_p, c_i32]
     L.bt_test_replay.argtypes = [c_p, c_i32, c_i32]
     for f in ("bt_init", "bt_prefill", "bt_prefill_lengths", "bt_prefill_ragged", "bt_prefill_rows",
-              "bt_block_lengths", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
+              "bt_block_lengths", "bt_page_table", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
               "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs", "bt_test_replay"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -135,12 +137,13 @@ class BlockTransformer:
     """One model instance bound to a CUDA/HIP stream.  Device memory is owned by torch tensors."""
 
     def __init__(self, model, weights: Mapping[str, np.ndarray], max_batch: int, max_tokens: int,
-                 device: str = "cuda:0", stream=None, graphs: bool = True, max_prompt_tokens: int = 0):
+                 device: str = "cuda:0", stream=None, graphs: bool = True, max_prompt_tokens: int = 0,
+                 kv_pages: int = 0):
         import torch
         self.torch = torch
         L = lib()
         self.model = model
-        self.cfg = BtConfig.make(model, max_batch, max_tokens, max_prompt_tokens)
+        self.cfg = BtConfig.make(model, max_batch, max_tokens, max_prompt_tokens, kv_pages)
         self.device = torch.device(device)
         # a stream of its own: decode steps are captured into HIP graphs, which the NULL stream forbids
         self.stream = stream if stream is not None else torch.cuda.Stream(self.device)
@@ -221,6 +224,13 @@ class BlockTransformer:
         check(lib().bt_prefill_rows(self.h, r, Bn, prompt.data_ptr(), lengths.data_ptr(), T, out.data_ptr(),
                                     _ptr(logits)))
         return out
+
+    def page_table(self):
+        """Paged block KV: the page table [max_batch][cap / 64] (synchronises)."""
+        blocks = -(-self.cfg.max_tokens // self.model.block_len)
+        a = (ctypes.c_int32 * (self.cfg.max_batch * -(-blocks // 64)))()
+        check(lib().bt_page_table(self.h, a))
+        return np.array(a, dtype=np.int64).reshape(self.cfg.max_batch, -1)
 
     def block_lengths(self):
         """Block-KV entries of every row of the running batch (synchronises)."""

@@ -57,6 +57,8 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   if (c.n_kv_heads < 0 || c.n_kv_heads > c.n_heads || (c.n_kv_heads > 0 && c.n_heads % c.n_kv_heads))
     return "n_kv_heads must be 0 or a divisor of n_heads";
   if (c.pad_id < 0 || c.pad_id >= c.vocab) return "pad_id must be in [0, vocab)";
+  if (c.kv_pages < 0 || (int64_t)c.kv_pages > (int64_t)c.max_batch * ((nblk + 63) / 64))
+    return "kv_pages must be in [0, max_batch * cap / 64]";
   if (c.context_mode < BT_CTX_PREFIX || c.context_mode > BT_CTX_XATTN)
     return "context_mode must be BT_CTX_PREFIX, BT_CTX_SUM or BT_CTX_XATTN";
   if (c.n_token_layers == 0 && c.context_mode != BT_CTX_PREFIX)
@@ -156,7 +158,10 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   for (int l = 0; l < lo.Nt; ++l) lo.tok.push_back(layer(xattn));
   lo.maxN1 = (int)QW + (xattn ? lo.D : 0);
   lo.maxK2 = lo.D + lo.F + (xattn ? lo.D : 0);
-  lo.block_kv_bytes = (size_t)lo.Nb * 2 * lo.Bmax * lo.Hkv * lo.ncap * lo.dh * E;
+  lo.pages = c.kv_pages;
+  // flat: per layer and K/V, [Bmax][Hkv][ncap][dh]; paged: [pages][Hkv][64][dh] (the same bytes per entry)
+  lo.block_kv_bytes = (size_t)lo.Nb * 2 * (lo.pages ? (size_t)lo.pages * 64 : (size_t)lo.Bmax * lo.ncap) * lo.Hkv *
+                      lo.dh * E;
   lo.local_kv_bytes = (size_t)lo.Nt * 2 * lo.Bmax * lo.Hkv * lo.lcap * lo.dh * E;  // 0 for Nt = 0
   lo.block_kv = region(lo.block_kv_bytes);
   lo.local_kv = region(lo.local_kv_bytes);
@@ -188,6 +193,7 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.cur = region((size_t)lo.Bmax * lo.L * 4);
   lo.dstate = region(std::max<size_t>(64, (size_t)lo.Bmax * 4));
   lo.rowmap = region((size_t)lo.Bmax * 4);
+  lo.ptab = region(lo.pages ? (size_t)lo.Bmax * (lo.ncap / 64) * 4 : 0);
   lo.lastblk = region((size_t)lo.Bmax * 4);
   lo.total = w;
   return "";
@@ -208,6 +214,12 @@ struct bt_handle {
   int g = 0;          // tokens emitted since the prefill
   std::vector<int64_t> row_tok;  // per row: padded prompt + emitted tokens, an upper bound
   const int* rmap = nullptr;     // during a join: device cache row of each prefilled row
+  // paged block KV: the host allocates pages (a row's entries are known here exactly)
+  std::vector<int> free_pages;              // stack of free page ids
+  std::vector<std::vector<int>> row_pages;  // pages of each row, in entry order
+  std::vector<int> row_n;                   // block-KV entries of each row
+  int32_t* ptab_host = nullptr;             // pinned mirror of the page table [Bmax][ncap / 64]
+  hipEvent_t ptab_ev = nullptr;             // completion of its last upload
   bool ready = false, broken = false;
   // optional per-kernel-class event timing
   bool prof = false;
@@ -272,16 +284,12 @@ int hip_fail(bt_handle* h, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(h, e_, what); \
   } while (0)
 
-void* block_k(bt_handle* h, int l) {
-  const Layout& lo = h->lo;
-  size_t per = (size_t)lo.Bmax * lo.Hkv * lo.ncap * lo.dh * lo.elem;
-  return P_(h, lo.block_kv + (size_t)(2 * l) * per);
+// bytes of one layer's keys (or values) in the block-KV region
+size_t block_kv_per(const Layout& lo) {
+  return (lo.pages ? (size_t)lo.pages * 64 : (size_t)lo.Bmax * lo.ncap) * lo.Hkv * lo.dh * lo.elem;
 }
-void* block_v(bt_handle* h, int l) {
-  const Layout& lo = h->lo;
-  size_t per = (size_t)lo.Bmax * lo.Hkv * lo.ncap * lo.dh * lo.elem;
-  return P_(h, lo.block_kv + (size_t)(2 * l + 1) * per);
-}
+void* block_k(bt_handle* h, int l) { return P_(h, h->lo.block_kv + (size_t)(2 * l) * block_kv_per(h->lo)); }
+void* block_v(bt_handle* h, int l) { return P_(h, h->lo.block_kv + (size_t)(2 * l + 1) * block_kv_per(h->lo)); }
 void* local_k(bt_handle* h, int l) {
   const Layout& lo = h->lo;
   size_t per = (size_t)lo.Bmax * lo.Hkv * lo.lcap * lo.dh * lo.elem;
@@ -300,6 +308,80 @@ void* ln_buf(bt_handle* h, int which) {
 float wscale(const Layout& lo) { return lo.f32 ? 1.0f : kWeightUnscale; }
 
 const ResidPending* pending(bt_handle* h) { return h->pending.nsplit > 0 ? &h->pending : nullptr; }
+
+// ---- paged block KV
+const int* page_table(bt_handle* h) { return h->lo.pages ? (const int*)P_(h, h->lo.ptab) : nullptr; }
+// per-row entry counts (the device lengths) bound what a paged prefill writes and reads
+const int* page_limits(bt_handle* h) { return h->lo.pages ? (const int*)P_(h, h->lo.dstate) : nullptr; }
+
+// Waits until the previous upload of the pinned mirror has been consumed, so it may change.
+int pages_wait(bt_handle* h) {
+  BT_CHECK(h, hipEventSynchronize(h->ptab_ev), "page table");
+  return BT_OK;
+}
+int pages_upload(bt_handle* h) {
+  const Layout& lo = h->lo;
+  BT_CHECK(h, hipMemcpyAsync(P_(h, lo.ptab), h->ptab_host, (size_t)lo.Bmax * (lo.ncap / 64) * 4,
+                             hipMemcpyHostToDevice, h->st),
+           "page table");
+  BT_CHECK(h, hipEventRecord(h->ptab_ev, h->st), "page table");
+  return BT_OK;
+}
+// Gives rows[i] pages for entries [0, entries[i]), releasing what they held first; nothing changes
+// (BT_ERR_CAPACITY) if the pool is short.  Uploads the table.
+int pages_assign(bt_handle* h, const std::vector<int>& rows, const std::vector<int>& entries) {
+  const Layout& lo = h->lo;
+  size_t held = 0, want = 0;
+  for (size_t i = 0; i < rows.size(); ++i) {
+    held += h->row_pages[rows[i]].size();
+    want += (size_t)(entries[i] + 63) / 64;
+  }
+  if (h->free_pages.size() + held < want) return fail(BT_ERR_CAPACITY, "kv_pages exhausted");
+  int r = pages_wait(h);
+  if (r) return r;
+  for (int row : rows) {
+    for (int pg : h->row_pages[row]) h->free_pages.push_back(pg);
+    h->row_pages[row].clear();
+  }
+  const int pld = lo.ncap / 64;
+  for (size_t i = 0; i < rows.size(); ++i) {
+    auto& mine = h->row_pages[rows[i]];
+    for (int k = 0; k < (entries[i] + 63) / 64; ++k) {
+      mine.push_back(h->free_pages.back());
+      h->free_pages.pop_back();
+      h->ptab_host[(size_t)rows[i] * pld + k] = mine.back();
+    }
+    h->row_n[rows[i]] = entries[i];
+  }
+  return pages_upload(h);
+}
+// Before a block step: a page for every row whose append slot starts one.
+int pages_grow(bt_handle* h) {
+  const Layout& lo = h->lo;
+  size_t need = 0;
+  for (int b = 0; b < h->B; ++b) need += h->row_n[b] % 64 == 0;
+  if (!need) return BT_OK;
+  if (h->free_pages.size() < need) return fail(BT_ERR_CAPACITY, "kv_pages exhausted");
+  int r = pages_wait(h);
+  if (r) return r;
+  const int pld = lo.ncap / 64;
+  for (int b = 0; b < h->B; ++b)
+    if (h->row_n[b] % 64 == 0) {
+      h->row_pages[b].push_back(h->free_pages.back());
+      h->free_pages.pop_back();
+      h->ptab_host[(size_t)b * pld + h->row_n[b] / 64] = h->row_pages[b].back();
+    }
+  return pages_upload(h);
+}
+// Exact entries of each row after a ragged prefill of B rows (reads the lengths back).
+int ragged_entries(bt_handle* h, const int32_t* d_lengths, int B, int T, std::vector<int>& out) {
+  std::vector<int32_t> len(B);
+  BT_CHECK(h, hipMemcpyAsync(len.data(), d_lengths, (size_t)B * 4, hipMemcpyDeviceToHost, h->st), "lengths");
+  BT_CHECK(h, hipStreamSynchronize(h->st), "lengths");
+  out.resize(B);
+  for (int b = 0; b < B; ++b) out[b] = (std::min(std::max(len[b], 1), T) + h->lo.L - 1) / h->lo.L;
+  return BT_OK;
+}
 
 // Epilogue of the [q|k|v|up] GEMM: bias, q|k|v to the QKV buffer, GELU(up) to ACT.
 Epi qkv_epi(bt_handle* h, const LayerOff& w) {
@@ -576,7 +658,7 @@ int enqueue_decode(bt_handle* h, int j, float* d_logits) {
         BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,
                                              lo.Hkv, lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l),
                                              lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, (float*)P_(h, lo.part),
-                                             lo.part_bytes, h->dec_nsplit, h->st),
+                                             lo.part_bytes, h->dec_nsplit, h->st, page_table(h), lo.ncap / 64),
                  "block attention decode");
       }
       if ((r = run_out(h, lo.blk[l], h->B))) return r;
@@ -628,7 +710,7 @@ int bt_workspace_region(const bt_config* cfg, int32_t which, size_t* offset, siz
   if (which == 0) {
     *offset = lo.block_kv;
     *bytes = lo.block_kv_bytes;
-    *capacity = lo.ncap;
+    *capacity = lo.pages ? 64 : lo.ncap;
   } else if (which == 1) {
     *offset = lo.local_kv;
     *bytes = lo.local_kv_bytes;
@@ -749,6 +831,15 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
                "repack head");
   }
   INIT_CHECK(launch_rope_table((float2*)(h->ws + lo.rope), lo.npos, lo.dh, cfg->rope_base, h->st), "rope table");
+  if (lo.pages) {
+    // every table entry starts at page 0, so no entry ever names memory outside the pool
+    const size_t tab = (size_t)lo.Bmax * (lo.ncap / 64) * 4;
+    INIT_CHECK(hipHostMalloc((void**)&h->ptab_host, tab), "page table");
+    memset(h->ptab_host, 0, tab);
+    INIT_CHECK(hipEventCreateWithFlags(&h->ptab_ev, hipEventDisableTiming), "page table");
+    INIT_CHECK(hipMemcpyAsync(h->ws + lo.ptab, h->ptab_host, tab, hipMemcpyHostToDevice, h->st), "page table");
+    INIT_CHECK(hipEventRecord(h->ptab_ev, h->st), "page table");
+  }
 #undef INIT_CHECK
   *out = h;
   return BT_OK;
@@ -781,7 +872,7 @@ static int prefill_core(bt_handle* h, const int32_t* d_prompt, const int32_t* d_
       Prof p(h, PK_ROPE_SCATTER, Md * 4.0 * KVW * E, 3.0 * Md * KVW);
       BT_CHECK(h, launch_rope_scatter(lo.f32, P_(h, lo.QKV), B, n0, 0, lo.H, lo.Hkv, lo.dh,
                                       (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap, true,
-                                      h->st, h->rmap),
+                                      h->st, h->rmap, page_table(h), lo.ncap / 64, page_limits(h)),
                "rope scatter");
     }
     {
@@ -789,7 +880,8 @@ static int prefill_core(bt_handle* h, const int32_t* d_prompt, const int32_t* d_
              4.0 * B * lo.H * lo.dh * (double)n0 * (n0 + 1) / 2.0);
       BT_CHECK(h, launch_prefill_attention(lo.f32, P_(h, lo.QKV), B, n0, lo.H, lo.Hkv, lo.dh,
                                            (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l), lo.ncap,
-                                           P_(h, lo.ACT), lo.blk[l].k2, h->st, h->rmap),
+                                           P_(h, lo.ACT), lo.blk[l].k2, h->st, h->rmap, page_table(h), lo.ncap / 64,
+                                           page_limits(h)),
                "prefill attention");
     }
     r = run_out(h, lo.blk[l], M);
@@ -839,6 +931,24 @@ static int prefill_impl(bt_handle* h, const int32_t* d_prompt, const int32_t* d_
   h->Tp = Tp;
   h->rmap = nullptr;
   h->dec_nsplit = decode_splits(B, lo.H, lo.Hkv, lo.ncap);
+  if (lo.pages) {
+    // a new batch: every page back in the pool, then each row's prompt blocks
+    std::vector<int> rows(B), entries(B, Tp / L);
+    for (int b = 0; b < B; ++b) rows[b] = b;
+    if (ragged) {
+      int e = ragged_entries(h, d_lengths, B, T, entries);
+      if (e) return e;
+    }
+    size_t want = 0;
+    for (int n : entries) want += (size_t)(n + 63) / 64;
+    if (want > (size_t)lo.pages) return fail(BT_ERR_CAPACITY, "kv_pages exhausted");
+    h->free_pages.clear();
+    for (int pg = lo.pages - 1; pg >= 0; --pg) h->free_pages.push_back(pg);
+    h->row_pages.assign(lo.Bmax, {});
+    h->row_n.assign(lo.Bmax, 0);
+    int e = pages_assign(h, rows, entries);
+    if (e) return e;
+  }
   int r = prefill_core(h, d_prompt, d_lengths, T, Tp, ragged, d_next, d_logits);
   if (r) return r;
   h->n_blocks = Tp / L;
@@ -884,6 +994,13 @@ int bt_prefill_rows(bt_handle* h, const int32_t* rows, int32_t B_new, const int3
   const int Tp = std::max(L, (T + L - 1) / L * L);
   if ((int64_t)Tp + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "padded prompt + 1 exceeds max_tokens");
   if (Tp > lo.max_prompt) return fail(BT_ERR_CAPACITY, "padded prompt exceeds max_prompt_tokens");
+  if (lo.pages) {
+    // the joining rows give back their pages and take what their prompts need
+    std::vector<int> rv(rows, rows + B_new), entries;
+    int e = ragged_entries(h, d_lengths, B_new, T, entries);
+    if (!e) e = pages_assign(h, rv, entries);
+    if (e) return e;
+  }
   BT_CHECK(h, hipMemcpyAsync(P_(h, lo.rowmap), rows, (size_t)B_new * 4, hipMemcpyHostToDevice, h->st), "row map");
   // the join runs its own classifier at B_new rows; the running batch's (possibly replayed from a
   // graph, which does not record it) column-group count must survive for its finalisations
@@ -920,6 +1037,7 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
   const int j = h->g % lo.L;
   h->decode_phase = true;
   int r;
+  if (lo.pages && j == 0 && (r = pages_grow(h))) return r;
   // graphs replay everything up to the classifier; the logits variant and profiling run eagerly
   if (h->use_graphs && !d_logits && !h->prof && h->st != nullptr) {
     if (h->graph_B != h->B) {
@@ -955,6 +1073,18 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
   if (r) return r;
   h->g += 1;
   for (int64_t& t : h->row_tok) t += 1;
+  if (lo.pages && j == 0)
+    for (int b = 0; b < h->B; ++b) h->row_n[b] += 1;
+  return BT_OK;
+}
+
+int bt_page_table(bt_handle* h, int32_t* table) {
+  if (!h || !table) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  if (!h->lo.pages) return fail(BT_ERR_UNSUPPORTED, "the block KV is not paged (kv_pages = 0)");
+  BT_CHECK(h, hipStreamSynchronize(h->st), "synchronize");
+  BT_CHECK(h, hipMemcpy(table, P_(h, h->lo.ptab), (size_t)h->lo.Bmax * (h->lo.ncap / 64) * 4,
+                        hipMemcpyDeviceToHost),
+           "copy");
   return BT_OK;
 }
 
@@ -984,6 +1114,8 @@ int bt_destroy(bt_handle* h) {
   if (!h) return fail(BT_ERR_INVALID_ARG, "NULL handle");
   drop_graphs(h);
   for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
+  if (h->ptab_ev) (void)hipEventDestroy(h->ptab_ev);
+  if (h->ptab_host) (void)hipHostFree(h->ptab_host);
   delete h;
   return BT_OK;
 }
@@ -1029,6 +1161,8 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
   const Layout& lo = h->lo;
   // the attention appends at slot n (the device length, equal to the host mirror between calls)
   if (kind == PK_ATTN_DECODE && h->n_blocks >= lo.ncap) return fail(BT_ERR_CAPACITY, "block-KV cache full");
+  if (kind == PK_ATTN_DECODE && lo.pages)
+    return fail(BT_ERR_UNSUPPORTED, "no replay of the block attention on a paged cache (its append slot may have no page)");
   int r = BT_OK;
   for (int i = 0; i < reps && r == BT_OK; ++i) {
     if (kind == PK_GEMM_QKV) {
@@ -1045,7 +1179,7 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
       hipError_t e = launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,
                                               lo.Hkv, lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l),
                                               block_v(h, l), lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, (float*)P_(h, lo.part),
-                                              lo.part_bytes, h->dec_nsplit, h->st);
+                                              lo.part_bytes, h->dec_nsplit, h->st, page_table(h), lo.ncap / 64);
       if (e != hipSuccess) r = hip_fail(h, e, "replay attention");
     } else {
       r = fail(BT_ERR_INVALID_ARG, "kind not replayable");

@@ -47,24 +47,48 @@ __device__ __forceinline__ void load8_nt(const float* p, float* o) {
 template <typename T>
 __device__ __forceinline__ T round_t(float v) { return from_f32<T>(v); }
 
+// ---------------------------------------------------------------- block-KV addressing
+// Entry j of cache row r, KV head hk: flat caches hold keys [row][head][cap][dh] and values
+// transposed [row][head][dh][cap]; paged caches (ptab set) hold pages of 64 entries, keys
+// [page][head][64][dh] and values [page][head][dh][64], entry j of row r in page ptab[r*pld + j/64].
+// nlim (paged prefill): entries at or past nlim[r] are not written or read (their pages may not
+// exist).
+struct KvPages {
+  const int* ptab;
+  int pld;
+  const int* nlim;
+};
+__device__ __forceinline__ size_t kv_key(const KvPages& pg, int r, int hk, int j, int Hkv, int cap, int dh) {
+  return pg.ptab ? (((size_t)pg.ptab[(size_t)r * pg.pld + (j >> 6)] * Hkv + hk) * 64 + (j & 63)) * dh
+                 : (((size_t)r * Hkv + hk) * cap + j) * dh;
+}
+__device__ __forceinline__ size_t kv_val(const KvPages& pg, int r, int hk, int d, int j, int Hkv, int cap, int dh) {
+  return pg.ptab ? (((size_t)pg.ptab[(size_t)r * pg.pld + (j >> 6)] * Hkv + hk) * dh + d) * 64 + (j & 63)
+                 : (((size_t)r * Hkv + hk) * dh + d) * cap + j;
+}
+
 // ---------------------------------------------------------------- rotary + scatter (prefill)
 // grid (ceil(m/64), Hkv, B); KV head hk of rows (b, i) of QKV [B*m][QW] goes to cache slot s0 + i.
 template <typename T>
 __global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV, int m, int s0, int H, int Hkv, int dh,
                                                       const float2* __restrict__ rope, T* __restrict__ Kc,
-                                                      T* __restrict__ Vc, int cap, int vt, const int* __restrict__ rmap) {
+                                                      T* __restrict__ Vc, int cap, int vt, const int* __restrict__ rmap,
+                                                      KvPages pg) {
   __shared__ T vtile[64][129];
   const int hk = blockIdx.y, b = blockIdx.z, i0 = blockIdx.x * 64;
   const int half = dh / 2, tid = threadIdx.x;
   const size_t qw = (size_t)(H + 2 * Hkv) * dh, koff = (size_t)(H + hk) * dh, voff = (size_t)(H + Hkv + hk) * dh;
-  const size_t bh = (size_t)(rmap ? rmap[b] : b) * Hkv + hk;
-  const int cnt = min(64, m - i0);
+  const int cb = rmap ? rmap[b] : b;
+  const size_t bh = (size_t)cb * Hkv + hk;
+  // slots past the row's length (paged ragged prefill) are skipped
+  const int cnt = min(64, min(m, pg.nlim ? pg.nlim[cb] - s0 : m) - i0);
+  if (cnt <= 0) return;
   for (int e = tid; e < cnt * half; e += 256) {
     const int si = e / half, c = e % half, i = i0 + si, slot = s0 + i;
     const T* kr = QKV + ((size_t)b * m + i) * qw + koff;
     const float2 cs = rope[(size_t)slot * half + c];
     const float x1 = (float)kr[c], x2 = (float)kr[c + half];
-    T* kd = Kc + (bh * cap + slot) * dh;
+    T* kd = Kc + kv_key(pg, cb, hk, slot, Hkv, cap, dh);
     kd[c] = round_t<T>(x1 * cs.x - x2 * cs.y);
     kd[c + half] = round_t<T>(x2 * cs.x + x1 * cs.y);
   }
@@ -82,22 +106,23 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV,
   __syncthreads();
   for (int e = tid; e < cnt * dh; e += 256) {
     const int d = e / cnt, si = e % cnt;
-    Vc[(bh * dh + d) * cap + s0 + i0 + si] = vtile[si][d];
+    Vc[kv_val(pg, cb, hk, d, s0 + i0 + si, Hkv, cap, dh)] = vtile[si][d];
   }
 }
 
 hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed, hipStream_t st,
-                               const int* rmap) {
+                               const int* rmap, const int* ptab, int pld, const int* nlim) {
   if (B <= 0 || m <= 0) return hipSuccess;
-  if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  if (Hkv < 1 || H % Hkv || (ptab && !v_transposed)) return hipErrorInvalidValue;
+  const KvPages pg{ptab, pld, nlim};
   dim3 grid((m + 63) / 64, Hkv, B);
   if (f32)
     hipLaunchKernelGGL(k_rope_scatter<float>, grid, dim3(256), 0, st, (const float*)QKV, m, s0, H, Hkv, dh, rope,
-                       (float*)Kc, (float*)Vc, cap, (int)v_transposed, rmap);
+                       (float*)Kc, (float*)Vc, cap, (int)v_transposed, rmap, pg);
   else
     hipLaunchKernelGGL(k_rope_scatter<f16>, grid, dim3(256), 0, st, (const f16*)QKV, m, s0, H, Hkv, dh, rope,
-                       (f16*)Kc, (f16*)Vc, cap, (int)v_transposed, rmap);
+                       (f16*)Kc, (f16*)Vc, cap, (int)v_transposed, rmap, pg);
   return hipGetLastError();
 }
 
@@ -112,7 +137,8 @@ template <int DH>
 __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ QKV, int n, int H, int Hkv,
                                                        const float2* __restrict__ rope, const f16* __restrict__ Kc,
                                                        const f16* __restrict__ VTc, int cap, f16* __restrict__ ACT,
-                                                       int ld_act, float scale_log2, const int* __restrict__ rmap) {
+                                                       int ld_act, float scale_log2, const int* __restrict__ rmap,
+                                                       KvPages pg) {
   constexpr int KS = DH / 32;   // 32-wide dh slices of q and k
   constexpr int MT = DH / 16;   // 16-row dh tiles of O^T
   constexpr int KLD = DH + 8;   // LDS row strides (+16 B: conflict-free fragment reads)
@@ -128,9 +154,8 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
   const int q0 = qt * 64 + wave * 16;
   const int qi = q0 + c16;
   const int qrow = min(qi, n - 1);
-  const size_t bh = (size_t)(rmap ? rmap[b] : b) * Hkv + h / (H / Hkv);
-  const f16* __restrict__ K = Kc + bh * cap * DH;
-  const f16* __restrict__ VT = VTc + bh * DH * cap;
+  const int cb = rmap ? rmap[b] : b, hk = h / (H / Hkv);
+  if (pg.nlim && qt * 64 >= pg.nlim[cb]) return;  // queries past the row's length: nothing reads them
 
   // q^T fragments with the rotary embedding: lane holds dh indices 32*ks + 8g + e; the rotation
   // partner (index +- DH/2) sits in slice ks +- KS/2 of the same lane.
@@ -154,16 +179,20 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
 
   // cooperative tile loads (keys beyond the cache capacity never occur: cap is a multiple of 64)
   half8 rk[CK], rv[CV];
+  // a 64-key tile is one page of a paged cache: keys [64][DH] and values [DH][64] (row stride 64)
+  const int vstride = pg.ptab ? 64 : cap;
   auto gload = [&](int kb) {
+    const f16* __restrict__ Kt = Kc + kv_key(pg, cb, hk, kb, Hkv, cap, DH);
+    const f16* __restrict__ Vt = VTc + kv_val(pg, cb, hk, 0, kb, Hkv, cap, DH);
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
       const int c = tid + i * 256, r = c / (DH / 8), cc = c % (DH / 8);
-      rk[i] = *(const half8*)(K + (size_t)(kb + r) * DH + cc * 8);
+      rk[i] = *(const half8*)(Kt + (size_t)r * DH + cc * 8);
     }
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
       const int c = tid + i * 256, r = c / 8, cc = c % 8;
-      rv[i] = *(const half8*)(VT + (size_t)r * cap + kb + cc * 8);
+      rv[i] = *(const half8*)(Vt + (size_t)r * vstride + cc * 8);
     }
   };
   auto sstore = [&](int buf) {
@@ -275,12 +304,14 @@ template <typename T>
 __global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, int n, int H, int Hkv, int dh,
                                                    const float2* __restrict__ rope, const T* __restrict__ Kc,
                                                    const T* __restrict__ VTc, int cap, T* __restrict__ ACT,
-                                                   int ld_act, float scale, const int* __restrict__ rmap) {
+                                                   int ld_act, float scale, const int* __restrict__ rmap,
+                                                   KvPages pg) {
   extern __shared__ float sm[];
   float* q = sm;          // [dh]
   float* sc = sm + 128;   // [n]
   const int qi = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  const size_t bh = (size_t)(rmap ? rmap[b] : b) * Hkv + h / (H / Hkv);
+  const int cb = rmap ? rmap[b] : b, hk = h / (H / Hkv);
+  if (pg.nlim && qi >= pg.nlim[cb]) return;
   const T* qp = QKV + ((size_t)b * n + qi) * (H + 2 * Hkv) * dh + h * dh;
   const int half = dh / 2;
   for (int c = lane; c < half; c += 64) {
@@ -292,7 +323,7 @@ __global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, in
   __syncthreads();
   float mx = -INFINITY;
   for (int j = lane; j <= qi; j += 64) {
-    const T* kp = Kc + (bh * cap + j) * dh;
+    const T* kp = Kc + kv_key(pg, cb, hk, j, Hkv, cap, dh);
     float d = 0.f;
     for (int e = 0; e < dh; ++e) d = fmaf(q[e], (float)kp[e], d);
     sc[j] = d * scale;
@@ -308,32 +339,33 @@ __global__ __launch_bounds__(64) void k_attn_naive(const T* __restrict__ QKV, in
   l = wave_sum(l);
   __syncthreads();
   for (int d = lane; d < dh; d += 64) {
-    const T* vp = VTc + (bh * dh + d) * cap;
     float o = 0.f;
-    for (int j = 0; j <= qi; ++j) o = fmaf(sc[j], (float)vp[j], o);
+    for (int j = 0; j <= qi; ++j) o = fmaf(sc[j], (float)VTc[kv_val(pg, cb, hk, d, j, Hkv, cap, dh)], o);
     ACT[opnd_idx(ACT, b * n + qi, h * dh + d, ld_act)] = round_t<T>(o / l);
   }
 }
 
 hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int H, int Hkv, int dh,
                                     const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
-                                    int ld_act, hipStream_t st, const int* rmap) {
+                                    int ld_act, hipStream_t st, const int* rmap, const int* ptab, int pld,
+                                    const int* nlim) {
   if (B <= 0 || n <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  const KvPages pg{ptab, pld, nlim};
   const float scale = 1.0f / sqrtf((float)dh);
   if (f32) {
     size_t lds = (128 + (size_t)n) * sizeof(float);
     hipLaunchKernelGGL(k_attn_naive<float>, dim3(n, H, B), dim3(64), lds, st, (const float*)QKV, n, H, Hkv, dh, rope,
-                       (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale, rmap);
+                       (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale, rmap, pg);
     return hipGetLastError();
   }
   dim3 grid((n + 63) / 64, H, B);
   if (dh == 64)
     hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
-                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap);
+                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
   else if (dh == 128)
     hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
-                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap);
+                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -348,12 +380,13 @@ hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int
 constexpr int kMaxChunk = 4096;  // scores held in LDS per workgroup, over all its query heads
 constexpr int kMaxSplit = 128;   // with GM = 4 (chunks of 1024 keys): the 131072-entry capacity limit
 
-template <typename T, int DH, int GM>
+template <typename T, int DH, int GM, bool PAGED>
 __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, const int* __restrict__ n_ptr, int H,
                                                      int Hkv, int gsz, const float2* __restrict__ rope,
                                                      T* __restrict__ Kc, T* __restrict__ VTc, int cap,
                                                      T* __restrict__ ACT, int ld_act, float* __restrict__ part,
-                                                     int nsplit, int chunk, float scale_log2) {
+                                                     int nsplit, int chunk, float scale_log2,
+                                                     const int* __restrict__ ptab, int pld) {
   static_assert(GM >= 1 && GM <= 4, "one wave scores each head's new key");
   constexpr int LPK = DH / 8;      // lanes per key in the score pass (8 values each)
   constexpr int KPW = 64 / LPK;    // keys per wave per step
@@ -363,6 +396,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   __shared__ float qs[GM][DH], kn[DH], vn[DH];
   __shared__ __attribute__((aligned(16))) float sc[kMaxChunk + 8];  // [GM][chunk]
   __shared__ float red[GM][8];
+  __shared__ int pgs[PAGED ? kMaxChunk / 64 : 1];  // pages of this split's keys (paged cache)
   const int s = blockIdx.x, b = blockIdx.z;
   const int G = H / Hkv, nsub = (G + gsz - 1) / gsz;
   const int hk = blockIdx.y / nsub, run = blockIdx.y % nsub;
@@ -372,12 +406,34 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   // the capacity; the clamp only keeps a misused row inside its own cache)
   const int n = min(n_ptr[b], cap - 1);
   const size_t bk = (size_t)b * Hkv + hk;
-  T* __restrict__ K = Kc + bk * cap * DH;
+  T* __restrict__ K = Kc + bk * cap * DH;  // (flat cache)
   T* __restrict__ VT = VTc + bk * DH * cap;
   const int j0 = s * chunk, j1 = min(n + 1, j0 + chunk);  // this split's keys [j0, j1)
   const int jc_end = min(j1, n);                           // of which cached: [j0, jc_end)
   const bool owns_new = (n >= j0 && n < j1);
   const bool appends = s == 0 && run == 0;
+  // paged: key j at Kc[((page * Hkv + hk) * 64 + j % 64) * DH], value (d, j) at
+  // VTc[((page * Hkv + hk) * DH + d) * 64 + j % 64], page = pgs[(j - j0) / 64] (j0 % 64 == 0)
+  if (PAGED)
+    for (int k = threadIdx.x; k < chunk / 64 && j0 / 64 + k < pld; k += 256) pgs[k] = ptab[(size_t)b * pld + j0 / 64 + k];
+  auto kaddr = [&](int j) -> const T* {
+    if (!PAGED) return K + (size_t)j * DH;
+    return Kc + (((size_t)pgs[(j - j0) >> 6] * Hkv + hk) * 64 + (j & 63)) * DH;
+  };
+  auto vaddr = [&](int row, int j) -> const T* {
+    if (!PAGED) return VT + (size_t)row * cap + j;
+    return VTc + (((size_t)pgs[(j - j0) >> 6] * Hkv + hk) * DH + row) * 64 + (j & 63);
+  };
+  // the appended entry's place (its page comes from the table directly: LDS is not ready yet)
+  size_t kn_off = (size_t)n * DH, vn_off = n, vn_stride = cap;
+  if (PAGED) {
+    const size_t pn = (size_t)ptab[(size_t)b * pld + (n >> 6)] * Hkv + hk;
+    kn_off = (pn * 64 + (n & 63)) * DH;
+    vn_off = pn * DH * 64 + (n & 63);
+    vn_stride = 64;
+  }
+  T* __restrict__ Kn = PAGED ? Kc + kn_off : K + kn_off;
+  T* __restrict__ Vn = PAGED ? VTc + vn_off : VT + vn_off;
 
   const T* row = QKV + (size_t)b * (H + 2 * Hkv) * DH;
   for (int e = tid; e < GM * (DH / 2); e += 256) {
@@ -397,14 +453,14 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
     kn[c] = (float)ka;
     kn[c + DH / 2] = (float)kb;
     if (appends) {
-      K[(size_t)n * DH + c] = ka;
-      K[(size_t)n * DH + c + DH / 2] = kb;
+      Kn[c] = ka;
+      Kn[c + DH / 2] = kb;
     }
   } else if (tid >= 64 && tid < 64 + DH) {
     const int d = tid - 64;
     const T v = row[(size_t)(H + Hkv + hk) * DH + d];
     vn[d] = (float)v;
-    if (appends) VT[(size_t)d * cap + n] = v;
+    if (appends) Vn[(size_t)d * vn_stride] = v;
   }
   __syncthreads();
 
@@ -421,7 +477,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
     for (int u = 0; u < U; ++u) {
       // clamped rather than guarded, so that the U loads are in flight together
       const int j = min(jb + u * 4 * KPW + kl, jc_end - 1);
-      load8_nt(K + (size_t)j * DH + 8 * pp, kv[u]);
+      load8_nt(kaddr(j) + 8 * pp, kv[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -501,7 +557,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
     for (int u = 0; u < UV; ++u) {
       const int jc = jb + 64 * u < jc_end ? jb + 64 * u : jb;
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) load8_nt(VT + (size_t)(r * 32 + wave * 8 + rl) * cap + jc, v[u][r]);
+      for (int r = 0; r < RPL; ++r) load8_nt(vaddr(r * 32 + wave * 8 + rl, jc), v[u][r]);
     }
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
@@ -575,7 +631,7 @@ static int decode_group_max(int H, int Hkv) { return H == Hkv ? 1 : (H / Hkv == 
 template <typename T, int DH, int GM>
 static hipError_t launch_decode_t(const void* QKV, int B, const int* n_ptr, int H, int Hkv, const float2* rope,
                                   void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part, size_t part_bytes,
-                                  int nsplit, hipStream_t st) {
+                                  int nsplit, hipStream_t st, const int* ptab, int pld) {
   // the split layout covers the whole capacity, so it does not depend on the current length n
   // (which is read on the device); splits past n + 1 produce empty partials
   int chunk = (cap + nsplit - 1) / nsplit;
@@ -584,8 +640,14 @@ static hipError_t launch_decode_t(const void* QKV, int B, const int* n_ptr, int 
   if (nsplit > 1 && (size_t)B * H * nsplit * (DH + 2) * sizeof(float) > part_bytes) return hipErrorInvalidValue;
   const int G = H / Hkv, nsub = (G + GM - 1) / GM, gsz = (G + nsub - 1) / nsub;
   const float sl2 = kLog2e / sqrtf((float)DH);
-  hipLaunchKernelGGL((k_attn_decode<T, DH, GM>), dim3(nsplit, Hkv * nsub, B), dim3(256), 0, st, (const T*)QKV, n_ptr,
-                     H, Hkv, gsz, rope, (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, part, nsplit, chunk, sl2);
+  if (ptab)
+    hipLaunchKernelGGL((k_attn_decode<T, DH, GM, true>), dim3(nsplit, Hkv * nsub, B), dim3(256), 0, st, (const T*)QKV,
+                       n_ptr, H, Hkv, gsz, rope, (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, part, nsplit, chunk, sl2, ptab,
+                       pld);
+  else
+    hipLaunchKernelGGL((k_attn_decode<T, DH, GM, false>), dim3(nsplit, Hkv * nsub, B), dim3(256), 0, st, (const T*)QKV,
+                       n_ptr, H, Hkv, gsz, rope, (T*)Kc, (T*)Vc, cap, (T*)ACT, ld_act, part, nsplit, chunk, sl2, ptab,
+                       pld);
   if (nsplit > 1)
     hipLaunchKernelGGL((k_attn_combine<T, DH>), dim3(H, B), dim3(DH), 0, st, (const float*)part, H, nsplit, (T*)ACT,
                        ld_act);
@@ -602,14 +664,14 @@ int decode_splits(int B, int H, int Hkv, int cap) {
 
 hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int H, int Hkv, int dh,
                                     const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part,
-                                    size_t part_bytes, int nsplit, hipStream_t st) {
+                                    size_t part_bytes, int nsplit, hipStream_t st, const int* ptab, int pld) {
   if (B <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
   const int gm = decode_group_max(H, Hkv);
 #define BT_DEC(T, DHV, GMV)                                                                                        \
   if (dh == DHV && gm == GMV)                                                                                      \
     return launch_decode_t<T, DHV, GMV>(QKV, B, n_ptr, H, Hkv, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes,   \
-                                        nsplit, st);
+                                        nsplit, st, ptab, pld);
 #define BT_DEC_G(T, DHV) BT_DEC(T, DHV, 1) BT_DEC(T, DHV, 2) BT_DEC(T, DHV, 4)
   if (f32) {
     BT_DEC_G(float, 32) BT_DEC_G(float, 64) BT_DEC_G(float, 128)

@@ -49,6 +49,8 @@ struct Layout {
   int Bmax, max_tokens;
   int max_prompt;  // longest padded prompt the activations hold (a multiple of L)
   int ncap;     // block-KV entries per (layer, row, KV head), multiple of 64
+  int pages;    // paged block KV: pages of 64 entries in the pool (0: one flat cache per row)
+  size_t ptab;  // int32 [Bmax][ncap / 64] page table (paged)
   int lcap;     // local-KV entries per (layer, row, KV head) = P + L
   int npos;     // rows of the rotary table
   int Vpad;     // classifier rows padded to a multiple of 128
@@ -186,21 +188,26 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
 // rotary + scatter of K (row-major [slot][dh]) and V (block cache: transposed [dh][slot]) for rows
 // (b, i) of QKV [B*m][QW] into cache slots s0 + i, at rotary positions s0 + i.
 // (rmap: optional cache row of each activation row b, for a prefill into rows of a running batch;
-// the same argument of the prefill and local attention launchers)
+// the same argument of the prefill and local attention launchers.  ptab / pld: page table of a
+// paged block KV (pages of 64 entries, [page][Hkv][64][dh] keys, [page][Hkv][dh][64] values),
+// nlim: with it, entries past each cache row's length nlim[row] are neither written nor read.)
 hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed,
-                               hipStream_t st, const int* rmap = nullptr);
+                               hipStream_t st, const int* rmap = nullptr, const int* ptab = nullptr, int pld = 0,
+                               const int* nlim = nullptr);
 // causal prefill attention of rows (b, i < n) at positions i over cache entries [0, i]
 hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int H, int Hkv, int dh,
                                     const float2* rope, const void* Kc, const void* Vc, int cap, void* ACT,
-                                    int ld_act, hipStream_t st, const int* rmap = nullptr);
+                                    int ld_act, hipStream_t st, const int* rmap = nullptr, const int* ptab = nullptr,
+                                    int pld = 0, const int* nlim = nullptr);
 // one new block-decoder position per row: n = n_ptr[b] (device state of row b) entries are cached;
 // rotary at position n, append K/V at slot n, attend over [0, n].  nsplit = decode_splits(B, H, Hkv, cap)
 // splits of the capacity (fixed for a batch size, so the launch does not depend on n).
 int decode_splits(int B, int H, int Hkv, int cap);
 hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int H, int Hkv, int dh,
                                     const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act,
-                                    float* part, size_t part_bytes, int nsplit, hipStream_t st);
+                                    float* part, size_t part_bytes, int nsplit, hipStream_t st,
+                                    const int* ptab = nullptr, int pld = 0);
 // local attention: new slots [s0, s0 + m) per row; rotary at slot, write to local cache, attend over [0, slot]
 // (ldq = QKV row stride, >= (H + 2 Hkv) dh: token layers with cross-attention carry its queries too)
 hipError_t launch_local_attention(bool f32, const void* QKV, int ldq, int B, int m, int s0, int H, int Hkv, int dh,

@@ -76,7 +76,8 @@ typedef enum {
  *   max_batch >= 1; max_tokens >= block_len (padded prompt + generated);
  *   0 <= max_prompt_tokens <= max_tokens;
  *   n_kv_heads = 0 (multi-head) or a divisor of n_heads (grouped-query; 1 = multi-query);
- *   context_mode a bt_context_mode, BT_CTX_PREFIX when n_token_layers = 0. */
+ *   context_mode a bt_context_mode, BT_CTX_PREFIX when n_token_layers = 0;
+ *   0 <= kv_pages <= max_batch * cap / 64 (cap below, bt_workspace_region). */
 typedef struct {
   int32_t vocab, d_model, n_heads, d_mlp;
   int32_t n_block_layers, n_token_layers;
@@ -96,6 +97,11 @@ typedef struct {
                          head i / G (grouped-query attention; summary page §3.4 "The Block
                          Decoder" names it as compatible); the KV caches then hold H_kv heads. */
   int32_t context_mode; /* bt_context_mode (0 = prefix) */
+  int32_t kv_pages;     /* 0: every row owns a block-KV cache of the full capacity.  > 0: paged
+                           block KV (the PagedAttention idea): a pool of kv_pages pages of 64
+                           entries (all block layers), given to rows as their caches grow, so
+                           rows of different lengths share the pool.  Running out of pages is
+                           BT_ERR_CAPACITY, reported before any work is queued. */
 } bt_config;
 
 /* Size in bytes of the canonical weights blob for this config.  The blob is
@@ -183,6 +189,11 @@ int bt_prefill_rows(bt_handle* h, const int32_t* rows, int32_t B_new, const int3
 /* Block-KV entries of each row of the running batch (host int32 [B]); synchronises the stream. */
 int bt_block_lengths(bt_handle* h, int32_t* lengths);
 
+/* Paged block KV: the page table, host int32 [max_batch][cap / 64] (page of each row's entries
+ * 64 i .. 64 i + 63; entries past a row's length are unspecified).  BT_ERR_UNSUPPORTED without
+ * kv_pages. */
+int bt_page_table(bt_handle* h, int32_t* table);
+
 /* One decode step (summary page §3.4, decode stage): feeds back the token the
  * previous call emitted and writes the next token of every row to d_next
  * (device int32 [B]; B is the prefill's batch), plus its fp32 logits [B, V] if
@@ -210,6 +221,9 @@ int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_k
  *            cap = ceil(max_tokens / L_B) rounded up to a multiple of 64; per (layer,
  *            row, KV head) the keys are [cap][d_head] (after the rotary embedding) and the
  *            values are transposed, [d_head][cap];
+ *            with kv_pages > 0 the cache is a pool [N_blk][2][kv_pages][H_kv][64 * d_head]
+ *            (keys [64][d_head], values [d_head][64] per page and head; capacity = 64), and
+ *            entry j of row b is in page bt_page_table(h)[b][j / 64] at j % 64;
  * which = 1: local-KV cache [N_tok][2][max_batch][H_kv][S + L_B][d_head] (keys after
  *            the rotary embedding, values not transposed).
  * Elements are fp16 for BT_BF16 and fp32 for BT_FP32.  Writes the byte

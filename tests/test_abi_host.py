@@ -83,6 +83,24 @@ def test_context_variant_blob_and_local_cache(mode, kw):
     assert cap.value == 1 + c.block_len
 
 
+def test_paged_pool_sizes_the_block_kv():
+    """kv_pages pages of 64 entries (all block layers) replace the per-row caches of full capacity."""
+    import hierarchical_global_local_amd as hg
+    L = hg.lib()
+    c = wl.get_config("c2_decode_heavy")
+    flat = hg.BtConfig.make(c, 256, 2180)
+    paged = hg.BtConfig.make(c, 256, 2180, kv_pages=1000)
+    regions = []
+    for cfg in (flat, paged):
+        off, nb, cap = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int32()
+        assert L.bt_workspace_region(ctypes.byref(cfg), 0, ctypes.byref(off), ctypes.byref(nb), ctypes.byref(cap)) == 0
+        regions.append((nb.value, cap.value))
+    (flat_b, flat_cap), (paged_b, paged_cap) = regions
+    assert flat_cap == 576 and paged_cap == 64
+    assert paged_b * 256 * 576 == flat_b * 1000 * 64
+    assert L.bt_workspace_bytes(ctypes.byref(paged)) < L.bt_workspace_bytes(ctypes.byref(flat))
+
+
 def test_context_mode_needs_a_token_decoder():
     import hierarchical_global_local_amd as hg
     _, cfg = _cfg("v2_vanilla_decode_heavy", context_mode="sum")
@@ -119,7 +137,8 @@ def test_block_kv_footprint_ratio_is_block_len():
                                              ("max_prompt_tokens", 1 << 20, "max_prompt_tokens"),
                                              ("n_kv_heads", 5, "n_kv_heads"), ("n_kv_heads", -1, "n_kv_heads"),
                                              ("n_kv_heads", 24, "n_kv_heads"), ("context_mode", 3, "context_mode"),
-                                             ("pad_id", 50304, "pad_id"), ("pad_id", -1, "pad_id")])
+                                             ("pad_id", 50304, "pad_id"), ("pad_id", -1, "pad_id"),
+                                             ("kv_pages", -1, "kv_pages"), ("kv_pages", 1 << 30, "kv_pages")])
 def test_invalid_config_rejected_on_host(field, value, msg):
     import hierarchical_global_local_amd as hg
     _, cfg = _cfg("c1_prefill_heavy")

@@ -150,3 +150,75 @@ def test_join_errors_are_reported_on_the_host():
     with pytest.raises(hg.BtError, match="BT_CTX_PREFIX"):
         m2.join([0], p[:1], l[:1])
     torch.cuda.synchronize()
+
+
+def _paged_run(cfg, W, kv_pages, B, T, steps, prompt, lengths, join, with_logits=True):
+    """Ragged prefill, decode steps (with logits: launched eagerly; without: replayed from graphs),
+    one join at `join[0]`; returns ids, logits, model."""
+    torch = require_gpu()
+    import hierarchical_global_local_amd as hg
+    model = hg.BlockTransformer(cfg, W, max_batch=B, max_tokens=wl.padded_len(cfg, T) + steps + 1,
+                                kv_pages=kv_pages)
+    ids, lgs = [], []
+    with torch.cuda.stream(model.stream):
+        lg = torch.empty((B, cfg.vocab), dtype=torch.float32, device="cuda")
+        ids.append(model.prefill(torch.from_numpy(prompt).cuda(), logits=lg,
+                                 lengths=torch.from_numpy(lengths).cuda(), ragged=True).clone())
+        lgs.append(lg.clone())
+        for g in range(1, steps):
+            if g == join[0]:
+                rows, p, l = join[1:]
+                ids.append(model.join(rows, torch.from_numpy(p).cuda(), torch.from_numpy(l).cuda()).clone())
+            lg = torch.empty((B, cfg.vocab), dtype=torch.float32, device="cuda") if with_logits else None
+            ids.append(model.decode_step(logits=lg).clone())
+            if with_logits:
+                lgs.append(lg.clone())
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in ids], [t.cpu().numpy() for t in lgs], model
+
+
+@pytest.mark.parametrize("name", ["fp32", "bf16"])
+def test_paged_block_kv_is_bit_identical_to_flat(name):
+    """Pages of 64 entries from a shared pool instead of one cache per row: rows spanning several
+    pages, decode steps that open new pages, and a join that hands pages back and takes new
+    ones give exactly the flat cache's ids and logits."""
+    cfg = (wl.get_config("c0_tiny") if name == "fp32" else SMALL_BF16).with_(block_len=1, prefix_len=2)
+    W = wl.make_weights(cfg, seed=36, ln_jitter=True)
+    B, T, steps = 4, 150, 90
+    prompt, lengths = _prompts(cfg, B, T, 36)
+    lengths[1], lengths[2] = 64, 63                       # a row ending exactly at a page boundary
+    join = (40, [2], *_prompts(cfg, 1, 100, 37))
+    flat = _paged_run(cfg, W, 0, B, T, steps, prompt, lengths, join)
+    paged = _paged_run(cfg, W, 14, B, T, steps, prompt, lengths, join)   # flat: 4 rows x 4 pages
+    for a, b in zip(flat[0], paged[0]):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(flat[1], paged[1]):
+        np.testing.assert_array_equal(a, b)
+    replayed = _paged_run(cfg, W, 14, B, T, steps, prompt, lengths, join, with_logits=False)
+    for a, b in zip(flat[0], replayed[0]):
+        np.testing.assert_array_equal(a, b)
+    n = paged[2].block_lengths()
+    np.testing.assert_array_equal(n, flat[2].block_lengths())
+    tab = paged[2].page_table()
+    held = [tab[b, : -(-int(n[b]) // 64)].tolist() for b in range(B)]
+    allp = sum(held, [])
+    assert len(allp) == len(set(allp)), "a page is held by two rows"
+    log(f"paged {name}: block lengths {n.tolist()}, pages {held}")
+
+
+def test_paged_pool_exhaustion_is_a_host_error():
+    torch = require_gpu()
+    import hierarchical_global_local_amd as hg
+    cfg = SMALL_BF16.with_(block_len=1, prefix_len=2)
+    W = wl.make_weights(cfg, seed=38)
+    model = hg.BlockTransformer(cfg, W, max_batch=2, max_tokens=400, kv_pages=4)
+    p = torch.zeros((2, 130), dtype=torch.int32, device="cuda")
+    l = torch.tensor([130, 60], dtype=torch.int32, device="cuda")
+    model.prefill(p, lengths=l, ragged=True)            # 3 + 1 pages: the pool is full
+    with pytest.raises(hg.BtError, match="kv_pages exhausted"):
+        for _ in range(10):                             # row 1 needs a new page at 64 entries
+            model.decode_step()
+    torch.cuda.synchronize()
+    with pytest.raises(hg.BtError, match="kv_pages exhausted"):
+        model.prefill(torch.zeros((2, 300), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
