@@ -608,6 +608,255 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   }
 }
 
+// ---------------------------------------------------------------- block-attention decode, MFMA (fp16)
+// A unit is one (row b, KV head hk, key split s) with all G = H / Hkv query heads of that KV head
+// (G <= 16: grouped-query heads share the unit, so their keys and values stream once).  WPU waves
+// serve a unit: with WPU = 4 they take its TK-key steps round-robin and merge through LDS at the
+// end (few units); with WPU = 1 a wave serves a unit alone, four units per workgroup, no barrier.
+// Per step a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_f16 (A = cached keys, B = Q^T with
+// one column per query head), an online softmax per column in registers, and O^T += V^T P^T.  The
+// keys are assigned to the rows of the S^T tiles so that lane group g ends up holding the
+// probabilities of 8 consecutive keys of each 32-key slice -- exactly its B operand of the P V
+// product -- and its V^T operand is one 16-byte load of the same 8 keys: nothing passes through
+// LDS.  Keys past the cached range get score -inf and value 0; the new entry (slot n, appended by
+// split 0) joins the softmax at the end, from registers.  MFMA layouts as in k_flash_prefill.
+template <int DH, int WPU, bool PAGED>
+__global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict__ QKV, const int* __restrict__ n_ptr,
+                                                          int B, int H, int Hkv, const float2* __restrict__ rope,
+                                                          f16* __restrict__ Kc, f16* __restrict__ VTc, int cap,
+                                                          f16* __restrict__ ACT, int ld_act, float* __restrict__ part,
+                                                          int nsplit, int chunk, float scale_log2,
+                                                          const int* __restrict__ ptab, int pld) {
+  constexpr int KS = DH / 32, MT = DH / 16;
+  constexpr int KT = DH == 64 ? 4 : 2;  // 16-key S^T tiles per step
+  constexpr int SL = KT / 2;            // 32-key slices per step
+  constexpr int TK = 16 * KT;           // keys per step (a step never straddles a 64-entry page)
+  __shared__ float so[WPU == 1 ? 1 : WPU][16][WPU == 1 ? 1 : DH + 1];
+  __shared__ float sm[WPU][16], sl_[WPU][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;  // query column (head of the group), lane group
+  const int G = H / Hkv;
+  const int unit = WPU == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
+  if (unit >= B * Hkv * nsplit) return;  // whole wave (WPU = 1) or whole workgroup (WPU = 4)
+  const int s = unit % nsplit, bk = unit / nsplit, hk = bk % Hkv, b = bk / Hkv;
+  const int n = min(n_ptr[b], cap - 1);
+  const int j0 = s * chunk, j1 = min(n + 1, j0 + chunk), jc_end = min(j1, n);
+  const bool owns_new = n >= j0 && n < j1;
+  const bool colv = c < G;
+  const int hq = hk * G + min(c, G - 1);  // columns past the group repeat its last head (never stored)
+  const f16* row = QKV + (size_t)b * (H + 2 * Hkv) * DH;
+
+  // q^T operand with the rotary embedding at position n; the new key (rotated, rounded as cached)
+  // for the new entry's score; the lane's new values; the append by split 0
+  half8 qf[KS];
+  float sc_new, vn[MT][4];
+  {
+    float q[KS][8], k[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      load8(row + hq * DH + 32 * ks + 8 * g, q[ks]);
+      load8(row + (size_t)(H + hk) * DH + 32 * ks + 8 * g, k[ks]);
+    }
+    const float2* rp = rope + (size_t)n * (DH / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 cs = rp[32 * ks + 8 * g + e];
+        const float q1 = q[ks][e], q2 = q[ks + KS / 2][e], k1 = k[ks][e], k2 = k[ks + KS / 2][e];
+        q[ks][e] = q1 * cs.x - q2 * cs.y;
+        q[ks + KS / 2][e] = q2 * cs.x + q1 * cs.y;
+        k[ks][e] = (float)to_f16(k1 * cs.x - k2 * cs.y);
+        k[ks + KS / 2][e] = (float)to_f16(k2 * cs.x + k1 * cs.y);
+      }
+    float dot = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qf[ks][e] = colv ? to_f16(q[ks][e]) : (f16)0.f;
+        dot = fmaf(q[ks][e], k[ks][e], dot);
+      }
+    dot += __shfl_xor(dot, 16, 64);
+    dot += __shfl_xor(dot, 32, 64);
+    sc_new = dot * scale_log2;
+    const f16* vr = row + (size_t)(H + Hkv + hk) * DH;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const half4 v4 = *(const half4*)(vr + 16 * mt + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vn[mt][i] = (float)v4[i];
+    }
+    if (s == 0 && c == 0 && (WPU == 1 || wave == 0)) {
+      // lanes 0, 16, 32, 48 hold dims 8g.. of every 32-dim slice of k and rows 4g.. of each v tile
+      size_t kofs, vofs, vstr;
+      if (PAGED) {
+        const size_t pg = (size_t)ptab[(size_t)b * pld + (n >> 6)] * Hkv + hk;
+        kofs = (pg * 64 + (n & 63)) * DH, vofs = pg * DH * 64 + (n & 63), vstr = 64;
+      } else {
+        kofs = (((size_t)b * Hkv + hk) * cap + n) * DH, vofs = ((size_t)b * Hkv + hk) * DH * cap + n, vstr = cap;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        half8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = to_f16(k[ks][e]);
+        *(half8*)(Kc + kofs + 32 * ks + 8 * g) = w;
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) VTc[vofs + (size_t)(16 * mt + 4 * g + i) * vstr] = to_f16(vn[mt][i]);
+    }
+  }
+
+  float4_ o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) o[mt] = float4_{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  const int w0 = WPU == 1 ? 0 : wave;
+  for (int t = j0 + w0 * TK; t < jc_end; t += WPU * TK) {
+    const f16 *kb, *vb;
+    int vstr;
+    if (PAGED) {
+      const size_t pg = (size_t)ptab[(size_t)b * pld + (t >> 6)] * Hkv + hk;
+      kb = Kc + (pg * 64 + (t & 63)) * DH, vb = VTc + pg * DH * 64 + (t & 63), vstr = 64;
+    } else {
+      kb = Kc + (((size_t)b * Hkv + hk) * cap + t) * DH, vb = VTc + ((size_t)b * Hkv + hk) * DH * cap + t, vstr = cap;
+    }
+    const int lim = jc_end - t;  // keys of this step that are cached: [0, lim)
+    // K rows: tile nt, row c holds key 32 (nt / 2) + 8 (c / 4) + 4 (nt % 2) + c % 4 (clamped: masked)
+    half8 kf[KT][KS], vf[SL][MT];
+#pragma unroll
+    for (int nt = 0; nt < KT; ++nt) {
+      const int kk = min(32 * (nt / 2) + 8 * (c / 4) + 4 * (nt % 2) + (c % 4), lim - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[nt][ks] = *(const half8*)(kb + (size_t)kk * DH + 32 * ks + 8 * g);
+    }
+    // V^T rows 16 mt + c at the 8 keys 32 sl + 8 g .. (a chunk past the cached keys reads chunk 0)
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) {
+      const int kc = 32 * sl + 8 * g < lim ? 32 * sl + 8 * g : 0;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        vf[sl][mt] = *(const half8*)(vb + (size_t)(16 * mt + c) * vstr + kc);
+    }
+    float4_ sv[KT];
+#pragma unroll
+    for (int nt = 0; nt < KT; ++nt) {
+      sv[nt] = float4_{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[nt][ks], qf[ks], sv[nt], 0, 0, 0);
+    }
+    // lane (c, g) holds the scores of keys 32 (nt / 2) + 8 g + 4 (nt % 2) + i for column c
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nt = 0; nt < KT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = 32 * (nt / 2) + 8 * g + 4 * (nt % 2) + i;
+        const float x = kk < lim ? sv[nt][i] * scale_log2 : -INFINITY;
+        sv[nt][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m, mx);  // finite: every step has a cached key
+    const float corr = exp2f(m - mnew);
+    float ls = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < KT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(sv[nt][i] - mnew);
+        sv[nt][i] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l = l * corr + ls;
+    m = mnew;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] *= corr;
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) {
+      half8 pf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = to_f16(sv[2 * sl][e]);
+        pf[4 + e] = to_f16(sv[2 * sl + 1][e]);
+      }
+      const bool tail = 32 * sl + 8 * g + 8 > lim;  // values past the cached keys must be 0, not junk
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        half8 v = vf[sl][mt];
+        if (tail) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = 32 * sl + 8 * g + e < lim ? v[e] : (f16)0.f;
+        }
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v, pf, o[mt], 0, 0, 0);
+      }
+    }
+  }
+  if (owns_new && (WPU == 1 || wave == 0)) {
+    const float mnew = fmaxf(m, sc_new);
+    const float corr = exp2f(m - mnew), pn = exp2f(sc_new - mnew);
+    l = l * corr + pn;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[mt][i] = o[mt][i] * corr + pn * vn[mt][i];
+    m = mnew;
+  }
+  if (WPU > 1) {
+    // merge the waves' partial softmaxes of each column (fixed order)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) so[wave][c][16 * mt + 4 * g + i] = o[mt][i];
+    if (g == 0) sm[wave][c] = m, sl_[wave][c] = l;
+    __syncthreads();
+    for (int it = threadIdx.x; it < G * DH; it += 256) {
+      const int cc = it / DH, d = it % DH, h = hk * G + cc;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WPU; ++w) M = fmaxf(M, sm[w][cc]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY)
+#pragma unroll
+        for (int w = 0; w < WPU; ++w) {
+          const float f = exp2f(sm[w][cc] - M);
+          L += f * sl_[w][cc];
+          O += f * so[w][cc][d];
+        }
+      if (nsplit == 1) {
+        ACT[frag_off(b, h * DH + d, ld_act)] = to_f16(O / L);
+      } else {
+        float* pp = part + (((size_t)b * H + h) * nsplit + s) * (DH + 2);
+        pp[2 + d] = O;
+        if (d == 0) pp[0] = M, pp[1] = L;
+      }
+    }
+    return;
+  }
+  if (!colv) return;
+  if (nsplit == 1) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      store4(ACT, frag_off(b, hq * DH + 16 * mt + 4 * g, ld_act), o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv,
+             o[mt][3] * inv);
+  } else {
+    float* pp = part + (((size_t)b * H + hq) * nsplit + s) * (DH + 2);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pp[2 + 16 * mt + 4 * g + i] = o[mt][i];
+    if (g == 0) pp[0] = m, pp[1] = l;
+  }
+}
+
 // merge split partials: o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
 template <typename T, int DH>
 __global__ void k_attn_combine(const float* __restrict__ part, int H, int nsplit, T* __restrict__ ACT, int ld_act) {
@@ -662,11 +911,52 @@ int decode_splits(int B, int H, int Hkv, int cap) {
   return std::max(1, std::min(s, kMaxSplit));
 }
 
+// fp16, groups of <= 16 query heads: the MFMA kernel, 4 waves per unit while units are few
+template <int DH>
+static hipError_t launch_decode_mfma(const void* QKV, int B, const int* n_ptr, int H, int Hkv, const float2* rope,
+                                     void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part, size_t part_bytes,
+                                     int nsplit, hipStream_t st, const int* ptab, int pld) {
+  int chunk = (cap + nsplit - 1) / nsplit;
+  chunk = (chunk + 63) / 64 * 64;
+  if (nsplit > 1 && (size_t)B * H * nsplit * (DH + 2) * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  const float sl2 = kLog2e / sqrtf((float)DH);
+  const long units = (long)B * Hkv * nsplit;
+#define BT_DM(WPUV, GRID)                                                                                        \
+  {                                                                                                              \
+    if (ptab)                                                                                                    \
+      hipLaunchKernelGGL((k_attn_decode_mfma<DH, WPUV, true>), dim3(GRID), dim3(256), 0, st, (const f16*)QKV,    \
+                         n_ptr, B, H, Hkv, rope, (f16*)Kc, (f16*)Vc, cap, (f16*)ACT, ld_act, part, nsplit, chunk, \
+                         sl2, ptab, pld);                                                                        \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_attn_decode_mfma<DH, WPUV, false>), dim3(GRID), dim3(256), 0, st, (const f16*)QKV,   \
+                         n_ptr, B, H, Hkv, rope, (f16*)Kc, (f16*)Vc, cap, (f16*)ACT, ld_act, part, nsplit, chunk, \
+                         sl2, ptab, pld);                                                                        \
+  }
+  if (units < 1024) BT_DM(4, units) else BT_DM(1, (units + 3) / 4)
+#undef BT_DM
+  if (nsplit > 1)
+    hipLaunchKernelGGL((k_attn_combine<f16, DH>), dim3(H, B), dim3(DH), 0, st, (const float*)part, H, nsplit,
+                       (f16*)ACT, ld_act);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int H, int Hkv, int dh,
                                     const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part,
                                     size_t part_bytes, int nsplit, hipStream_t st, const int* ptab, int pld) {
   if (B <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  // grouped-query heads (2..16 per KV head): one MFMA wave reads a KV head's keys and values once
+  // for all of them.  Multi-head attention stays on the streaming kernel below, whose 8-lanes-per-
+  // key loads cover whole cache lines per instruction (the MFMA operand loads cover half lines:
+  // 112 us vs 90 us for the decode-heavy shape)
+  if (!f32 && H / Hkv > 1 && H / Hkv <= 16) {
+    if (dh == 64)
+      return launch_decode_mfma<64>(QKV, B, n_ptr, H, Hkv, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, nsplit,
+                                    st, ptab, pld);
+    if (dh == 128)
+      return launch_decode_mfma<128>(QKV, B, n_ptr, H, Hkv, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, nsplit,
+                                     st, ptab, pld);
+  }
   const int gm = decode_group_max(H, Hkv);
 #define BT_DEC(T, DHV, GMV)                                                                                        \
   if (dh == DHV && gm == GMV)                                                                                      \
