@@ -8,7 +8,8 @@
 //    conflict-free 16-byte reads, no swizzle or padding.  Workgroup ids are remapped so that each
 //    of the 8 XCDs walks a contiguous range of output tiles, grouped 8 M-tiles at a time, so that A
 //    and W tiles are re-read from that XCD's L2 rather than from HBM.
-//  - large-tile kernel (prefill with a long K): 256 x 256 tiles fed by direct global -> LDS copies;
+//  - large-tile kernel (prefill [q|k|v|up] and [out|down]): 256 x 128 tiles fed by direct
+//    global -> LDS copies, two workgroups per CU;
 //  - the skinny kernel for decode shapes (M <= 256) is in gemm_decode.hip.
 // fp32 operands (BT_FP32): a plain LDS-tiled VALU kernel with the same epilogues, row-major.
 #include <cstdlib>
@@ -269,9 +270,12 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
 // With many rows (prefill: M = batch x prompt blocks) the GEMM is MFMA-bound, and what limits the
 // 128 x 128 kernel is LDS read bandwidth (a 64 x 64 wave tile reads 8 KB of fragments per 16
 // MFMAs) and global latency (one register stage of prefetch).  Here each of the 4 waves owns a
-// 128 x TN tile (accumulators in AGPRs), which halves the LDS bytes per MFMA, and the operand tiles
-// travel global -> LDS directly (global_load_lds_dwordx4: a wave moves one 1 KB fragment-order tile
-// per instruction, no registers) through a ring of NS = 4 stages, 3 K steps in flight.
+// 128 x TN tile (BN = 2 TN), which cuts the LDS bytes per MFMA, and the operand tiles travel
+// global -> LDS directly (global_load_lds_dwordx4: a wave moves one 1 KB fragment-order tile per
+// instruction, no registers) through a ring of NS stages, NS - 1 K steps in flight.  Used with
+// BN = 128, NS = 3: 72 KB of LDS and <= 256 registers per lane, so two workgroups share a CU and
+// one's epilogue overlaps the other's main loop (BN = 256, NS = 4 -- 128 x 128 per wave, one
+// workgroup per CU -- measured slower on every prefill shape once that variant existed).
 // Each wave waits for its own copies of a stage with an explicit vmcnt and the workgroup barrier
 // publishes them; a slot is refilled only after the barrier that follows every wave's last use of
 // it.  EPI_QKV_GELU and EPI_RESID (no split) only; the epilogue goes through LDS 128 rows at a time
@@ -290,7 +294,7 @@ __device__ __forceinline__ void barrier_nofence() {
 }
 
 template <int BN, int NS, int MODE>
-__global__ __launch_bounds__(256) void k_gemm_big(const f16* __restrict__ A1, const f16* __restrict__ A2,
+__global__ __launch_bounds__(256, BN == 128 ? 2 : 1) void k_gemm_big(const f16* __restrict__ A1, const f16* __restrict__ A2,
                                                   const f16* __restrict__ W, int M, int N, int K, Epi ep) {
   constexpr int BM = 256, WN = 2;
   constexpr int TM = 128, TN = BN / WN, FM = TM / 16, FN = TN / 16;
@@ -301,7 +305,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const f16* __restrict__ A1, co
   constexpr int SR = TM, CLD = BN + 4;         // epilogue slab: one wave row of fp32
   constexpr int EPIL = SR * CLD * 2;
   static_assert(MODE == EPI_QKV_GELU || MODE == EPI_RESID, "epilogue");
-  static_assert(NS == 4 && 2 * PER < 64, "ring: three stages in flight");
+  static_assert((NS == 4 || NS == 3) && 2 * PER < 64, "ring: NS - 1 stages in flight");
   __shared__ __attribute__((aligned(16))) f16 smem[NS * STG > EPIL ? NS * STG : EPIL];
 
   const int ntm = (M + BM - 1) / BM, ntn = N / BN;
@@ -599,13 +603,15 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
   if (mode == EPI_RESID) ep.splits = sp.ok ? sp.splits : tiled_resid_splits(M, N, K);
   if (ep.splits > 1 && !ep.part) return hipErrorInvalidValue;
   if (sp.ok) return launch_gemm_skinny(sp, A1, A2, W, M, N, K, mode, ep, st);
-  // 256 x 256 tiles for many rows and a long K (prefill [out|down], wide models): measured faster
-  // than the 128 x 128 kernel from K = 2048 up (+5 % at K = 3840, +17 % at K = 10240) once there
-  // are >= 256 tiles; at K = 768 its prologue and GELU epilogue, which nothing overlaps at one
-  // workgroup per CU, cost more than the LDS traffic it saves
-  if (M > 1024 && ep.splits == 1 && (mode == EPI_QKV_GELU || mode == EPI_RESID) && K % 64 == 0 && K >= 2048 &&
-      N % 256 == 0 && (mode != EPI_QKV_GELU || ep.n_split % 256 == 0) && (long)((M + 255) / 256) * (N / 256) >= 256)
-    return launch_big_cfg<256, 4>(A1, A2, W, M, N, K, mode, ep, st);
+  // Prefill [q|k|v|up] and [out|down] (fused epilogues): 256 x 128 tiles, 128 x 64 per wave, operand
+  // tiles copied global -> LDS through a 3-stage ring (72 KB), two workgroups per CU so that one's
+  // epilogue (GELU, staged stores) overlaps the other's main loop.  Measured against the 128 x 128
+  // kernel: 573 -> 701 TFLOP/s on the prefill-heavy [q|k|v|up] (K = 768), 637 -> 801 on its
+  // [out|down] (K = 3840, where the 256 x 256 variant at one workgroup per CU had been used); the
+  // 1.2B prefill drops from 105 to 96 ms.
+  if (M > 1024 && ep.splits == 1 && (mode == EPI_QKV_GELU || mode == EPI_RESID) && K % 64 == 0 && N % 128 == 0 &&
+      (mode != EPI_QKV_GELU || ep.n_split % 128 == 0) && (long)((M + 255) / 256) * (N / 128) >= 512)
+    return launch_big_cfg<128, 3>(A1, A2, W, M, N, K, mode, ep, st);
   // LDS-tiled kernel: K % 64 == 0, N % 32 == 0 and n_split on a tile boundary (checked at plan time)
   const bool split_ok128 = (mode != EPI_QKV_GELU) || (ep.n_split % 128 == 0);
   if ((M > 1024 || (M >= 256 && mode == EPI_ARGMAX)) && N % 128 == 0 && split_ok128 && ep.splits == 1)
