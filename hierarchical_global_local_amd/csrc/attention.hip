@@ -127,7 +127,9 @@ hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, 
 }
 
 // ---------------------------------------------------------------- MFMA flash prefill (fp16)
-// grid (ceil(n/64), H, B), 4 waves x 16 queries; query head h reads KV head h / (H / Hkv).  Each
+// grid ceil(n/64) * H * B, 4 waves x 16 queries; query head h reads KV head h / (H / Hkv).  The
+// query tiles of one (row, head) run on one XCD, consecutively and longest first, so that the
+// row's keys and values come from that XCD's L2 after the first tile instead of from HBM.  Each
 // 64-key tile of K ([key][dh]) and V^T ([dh][key]) is loaded once per workgroup with coalesced
 // 16-byte loads into a double-buffered LDS stage (the next tile's loads are in flight while the
 // current one is used) and read by all four waves.  MFMA 16x16x32 layouts (lane l, g = l / 16):
@@ -148,8 +150,9 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
   __shared__ __attribute__((aligned(16))) f16 Ks[2][64 * KLD];
   __shared__ __attribute__((aligned(16))) f16 Vs[2][DH * VLD];
 
-  const int qt = gridDim.x - 1 - blockIdx.x;  // longest (latest) query tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int nq = (n + 63) / 64, lt = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int pair = lt / nq, qt = nq - 1 - lt % nq;  // longest (latest) query tiles first
+  const int h = pair % H, b = pair / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int q0 = qt * 64 + wave * 16;
   const int qi = q0 + c16;
@@ -359,7 +362,7 @@ hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int
                        (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale, rmap, pg);
     return hipGetLastError();
   }
-  dim3 grid((n + 63) / 64, H, B);
+  dim3 grid((n + 63) / 64 * H * B);
   if (dh == 64)
     hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
                        (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);

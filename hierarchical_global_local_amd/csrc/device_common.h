@@ -71,6 +71,13 @@ __device__ __forceinline__ void store4(f16* base, size_t idx, float a, float b, 
   *(half4*)(base + idx) = w;
 }
 
+// Maps the hardware workgroup id to a logical tile index so that the workgroups one XCD
+// receives (ids x, x+8, x+16, ... go to XCD x) form one contiguous range of tiles.
+__device__ __forceinline__ int xcd_contiguous_tile(int bid, int nb) {
+  int per = nb >> 3, rem = nb & 7, x = bid & 7, i = bid >> 3;
+  return x * per + min(x, rem) + i;
+}
+
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
   uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
   lo = __shfl_xor(lo, m, 64);

@@ -35,13 +35,6 @@ __device__ __forceinline__ void epi_store(const Epi& ep, int row, int col, float
   }
 }
 
-// Maps the hardware workgroup id to a logical tile index so that the workgroups one XCD
-// receives (ids x, x+8, x+16, ... go to XCD x) form one contiguous range of tiles.
-__device__ __forceinline__ int xcd_contiguous_tile(int bid, int nb) {
-  int per = nb >> 3, rem = nb & 7, x = bid & 7, i = bid >> 3;
-  return x * per + min(x, rem) + i;
-}
-
 template <int BM, int BN, int WM, int WN, int MODE, int STAGES>
 __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, const f16* __restrict__ A2,
                                                    const f16* __restrict__ W, int M, int N, int K, Epi ep) {
