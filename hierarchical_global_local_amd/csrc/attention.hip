@@ -616,12 +616,13 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
 // (G <= 16: grouped-query heads share the unit, so their keys and values stream once).  WPU waves
 // serve a unit: with WPU = 4 they take its TK-key steps round-robin and merge through LDS at the
 // end (few units); with WPU = 1 a wave serves a unit alone, four units per workgroup, no barrier.
-// Per step a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_f16 (A = cached keys, B = Q^T with
-// one column per query head), an online softmax per column in registers, and O^T += V^T P^T.  The
-// keys are assigned to the rows of the S^T tiles so that lane group g ends up holding the
-// probabilities of 8 consecutive keys of each 32-key slice -- exactly its B operand of the P V
-// product -- and its V^T operand is one 16-byte load of the same 8 keys: nothing passes through
-// LDS.  Keys past the cached range get score -inf and value 0; the new entry (slot n, appended by
+// Per step a wave stages the step's keys and values in its own LDS region (whole 128-byte rows,
+// 1 KB per load instruction, non-temporal), then computes S^T = K Q^T with
+// v_mfma_f32_16x16x32_f16 (A = keys, B = Q^T with one column per query head), an online softmax
+// per column in registers, and O^T += V^T P^T.  The keys are assigned to the rows of the S^T tiles
+// so that lane group g ends up holding the probabilities of 8 consecutive keys of each 32-key
+// slice -- exactly its B operand of the P V product -- and its V^T operand is one 16-byte read of
+// the same 8 keys; the probabilities never leave registers.  Keys past the cached range get score -inf and value 0; the new entry (slot n, appended by
 // split 0) joins the softmax at the end, from registers.  MFMA layouts as in k_flash_prefill.
 template <int DH, int WPU, bool PAGED>
 __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict__ QKV, const int* __restrict__ n_ptr,
@@ -636,7 +637,13 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
   constexpr int TK = 16 * KT;           // keys per step (a step never straddles a 64-entry page)
   __shared__ float so[WPU == 1 ? 1 : WPU][16][WPU == 1 ? 1 : DH + 1];
   __shared__ float sm[WPU][16], sl_[WPU][16];
+  // per-wave staging of a step's keys [TK][DH] and values [DH][TK] (padded rows: conflict-free
+  // fragment reads), so that the global loads are whole 128-byte rows, 1 KB per instruction
+  constexpr int KLD = DH + 8, VLD = TK + 8;
+  __shared__ __attribute__((aligned(16))) f16 stage[4][TK * KLD + DH * VLD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f16* const Ks = stage[wave];
+  f16* const Vs = stage[wave] + TK * KLD;
   const int c = lane & 15, g = lane >> 4;  // query column (head of the group), lane group
   const int G = H / Hkv;
   const int unit = WPU == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
@@ -728,23 +735,39 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
       kb = Kc + (((size_t)b * Hkv + hk) * cap + t) * DH, vb = VTc + ((size_t)b * Hkv + hk) * DH * cap + t, vstr = cap;
     }
     const int lim = jc_end - t;  // keys of this step that are cached: [0, lim)
-    // K rows: tile nt, row c holds key 32 (nt / 2) + 8 (c / 4) + 4 (nt % 2) + c % 4 (clamped: masked)
+    // stage the step: key rows (clamped to cached keys, masked below) and value rows, 8 lanes per
+    // 128-byte row segment
+    {
+      constexpr int LPR = DH / 8, RK = 64 / LPR;  // lanes per key row, key rows per instruction
+      half8 rk[TK / RK], rv[DH * TK / 8 / 64];
+#pragma unroll
+      for (int i = 0; i < TK / RK; ++i) {
+        const int kr = min(i * RK + lane / LPR, lim - 1);
+        rk[i] = __builtin_nontemporal_load((const half8*)(kb + (size_t)kr * DH + 8 * (lane % LPR)));
+      }
+      constexpr int LPV = TK / 8, RV = 64 / LPV;  // lanes per value row segment, rows per instruction
+#pragma unroll
+      for (int i = 0; i < DH / RV; ++i)
+        rv[i] = __builtin_nontemporal_load((const half8*)(vb + (size_t)(i * RV + lane / LPV) * vstr + 8 * (lane % LPV)));
+#pragma unroll
+      for (int i = 0; i < TK / RK; ++i) *(half8*)&Ks[(i * RK + lane / LPR) * KLD + 8 * (lane % LPR)] = rk[i];
+#pragma unroll
+      for (int i = 0; i < DH / RV; ++i) *(half8*)&Vs[(i * RV + lane / LPV) * VLD + 8 * (lane % LPV)] = rv[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    // K rows: tile nt, row c holds key 32 (nt / 2) + 8 (c / 4) + 4 (nt % 2) + c % 4
     half8 kf[KT][KS], vf[SL][MT];
 #pragma unroll
     for (int nt = 0; nt < KT; ++nt) {
-      const int kk = min(32 * (nt / 2) + 8 * (c / 4) + 4 * (nt % 2) + (c % 4), lim - 1);
+      const int kk = 32 * (nt / 2) + 8 * (c / 4) + 4 * (nt % 2) + (c % 4);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[nt][ks] = *(const half8*)(kb + (size_t)kk * DH + 32 * ks + 8 * g);
+      for (int ks = 0; ks < KS; ++ks) kf[nt][ks] = *(const half8*)&Ks[kk * KLD + 32 * ks + 8 * g];
     }
-    // V^T rows 16 mt + c at the 8 keys 32 sl + 8 g .. (a chunk past the cached keys reads chunk 0)
+    // V^T rows 16 mt + c at the 8 keys 32 sl + 8 g ..
 #pragma unroll
-    for (int sl = 0; sl < SL; ++sl) {
-      const int kc = 32 * sl + 8 * g < lim ? 32 * sl + 8 * g : 0;
+    for (int sl = 0; sl < SL; ++sl)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        vf[sl][mt] = *(const half8*)(vb + (size_t)(16 * mt + c) * vstr + kc);
-    }
+      for (int mt = 0; mt < MT; ++mt) vf[sl][mt] = *(const half8*)&Vs[(16 * mt + c) * VLD + 32 * sl + 8 * g];
     float4_ sv[KT];
 #pragma unroll
     for (int nt = 0; nt < KT; ++nt) {
@@ -949,9 +972,9 @@ hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int*
   if (B <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
   // grouped-query heads (2..16 per KV head): one MFMA wave reads a KV head's keys and values once
-  // for all of them.  Multi-head attention stays on the streaming kernel below, whose 8-lanes-per-
-  // key loads cover whole cache lines per instruction (the MFMA operand loads cover half lines:
-  // 112 us vs 90 us for the decode-heavy shape)
+  // for all of them.  Multi-head attention stays on the streaming kernel below (decode-heavy shape
+  // at 543 entries: 90 us; the MFMA kernel 95 us with its LDS staging, 113 us loading fragments
+  // straight from memory, where an instruction covers half cache lines)
   if (!f32 && H / Hkv > 1 && H / Hkv <= 16) {
     if (dh == 64)
       return launch_decode_mfma<64>(QKV, B, n_ptr, H, Hkv, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, nsplit,
