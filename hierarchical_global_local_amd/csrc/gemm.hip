@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256, BN == 128 ? 2 : 1) void k_gemm_big(const f16* 
   constexpr int STG = (CHA + CHB) * 512;       // f16 elements per stage
   constexpr int SR = TM, CLD = BN + 4;         // epilogue slab: one wave row of fp32
   constexpr int EPIL = SR * CLD * 2;
-  static_assert(MODE == EPI_QKV_GELU || MODE == EPI_RESID, "epilogue");
+  static_assert(MODE == EPI_QKV_GELU || MODE == EPI_RESID || MODE == EPI_ARGMAX, "epilogue");
   static_assert((NS == 4 || NS == 3) && 2 * PER < 64, "ring: NS - 1 stages in flight");
   __shared__ __attribute__((aligned(16))) f16 smem[NS * STG > EPIL ? NS * STG : EPIL];
 
@@ -366,6 +366,34 @@ __global__ __launch_bounds__(256, BN == 128 ? 2 : 1) void k_gemm_big(const f16* 
         acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[fm], bw[fn], acc[fm][fn], 0, 0, 0);
   }
   wait_vmcnt<0>();
+  if constexpr (MODE == EPI_ARGMAX) {
+    // classifier: per row, the largest (value, id) key of this wave's TN columns (ids >= n_valid
+    // are padding), and the logits if requested
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = n0 + wn * TN + fn * 16 + (lane & 15);
+          const float v = acc[fm][fn][i] * ep.wscale;
+          if (col < ep.n_valid) {
+            if (ep.out0 && row < M) ((float*)ep.out0)[(size_t)row * ep.ld0 + col] = v;
+            const unsigned long long k = argmax_key(v, col);
+            best = k > best ? k : best;
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const unsigned long long other = shfl_xor_u64(best, o);
+          best = other > best ? other : best;
+        }
+        if ((lane & 15) == 0 && row < M) ep.keys[(size_t)row * ep.keys_ld + tn * WN + wn] = best;
+      }
+    return;
+  }
   __syncthreads();  // every wave is done with the ring before it becomes the epilogue's staging area
 
   // epilogue, one wave row (128 rows) of the tile at a time: the two waves owning it stage
@@ -375,7 +403,7 @@ __global__ __launch_bounds__(256, BN == 128 ? 2 : 1) void k_gemm_big(const f16* 
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     const int col = n0 + wn * TN + fn * 16 + (lane & 15);
-    bias[fn] = ep.bias[col] + (MODE == EPI_RESID ? ep.bias2[col] : 0.f);
+    if constexpr (MODE != EPI_ARGMAX) bias[fn] = ep.bias[col] + (MODE == EPI_RESID ? ep.bias2[col] : 0.f);
   }
   float* Cs = reinterpret_cast<float*>(smem);
   const bool gelu = MODE == EPI_QKV_GELU && n0 >= ep.n_split;
@@ -528,10 +556,14 @@ static hipError_t launch_big_cfg(const void* A1, const void* A2, const void* W, 
                                  const Epi& ep, hipStream_t st) {
   dim3 grid(((M + 255) / 256) * (N / BN)), block(256);
   const f16 *a1 = (const f16*)A1, *a2 = (const f16*)A2, *w = (const f16*)W;
-  if (mode == EPI_QKV_GELU)
+  if (mode == EPI_QKV_GELU) {
     hipLaunchKernelGGL((k_gemm_big<BN, NS, EPI_QKV_GELU>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
-  else
+  } else if (mode == EPI_RESID) {
     hipLaunchKernelGGL((k_gemm_big<BN, NS, EPI_RESID>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
+  } else {
+    if (ep.nparts_out) *ep.nparts_out = N / (BN / 2);  // one key per row and wave column half
+    hipLaunchKernelGGL((k_gemm_big<BN, NS, EPI_ARGMAX>), grid, block, 0, st, a1, a2, w, M, N, K, ep);
+  }
   return hipGetLastError();
 }
 
@@ -604,6 +636,9 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
   // 1.2B prefill drops from 105 to 96 ms.
   if (M > 1024 && ep.splits == 1 && (mode == EPI_QKV_GELU || mode == EPI_RESID) && K % 64 == 0 && N % 128 == 0 &&
       (mode != EPI_QKV_GELU || ep.n_split % 128 == 0) && (long)((M + 255) / 256) * (N / 128) >= 512)
+    return launch_big_cfg<128, 3>(A1, A2, W, M, N, K, mode, ep, st);
+  // the classifier of a batch above the skinny kernel's 128 rows: the weights stream once
+  if (mode == EPI_ARGMAX && M > 128 && K % 64 == 0 && N % 128 == 0)
     return launch_big_cfg<128, 3>(A1, A2, W, M, N, K, mode, ep, st);
   // LDS-tiled kernel: K % 64 == 0, N % 32 == 0 and n_split on a tile boundary (checked at plan time)
   const bool split_ok128 = (mode != EPI_QKV_GELU) || (ep.n_split % 128 == 0);
