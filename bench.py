@@ -126,7 +126,8 @@ def classify(name):
     return "hbm"
 
 
-REPLAYABLE = {"decode/gemm_qkv_up": "gemm_qkv_up", "decode/attn_block_decode": "attn_block_decode"}
+REPLAYABLE = {"decode/gemm_qkv_up": "gemm_qkv_up", "decode/local_attn_out": "local_attn_out",
+              "decode/attn_block_decode": "attn_block_decode"}
 
 
 def attn_replay_roofline(runner, cfg):
@@ -162,7 +163,9 @@ def roofline_of(name, rec):
 
 COPY_BYTES = 1 << 30
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_JSON = os.path.join(PROFILES, "traffic_decode_gemm_qkv_up.json")
+def traffic_json(kernel_class):
+    """Counter-measured traffic of a decode kernel class, e.g. profiles/traffic_decode_gemm_qkv_up.json."""
+    return os.path.join(PROFILES, "traffic_" + kernel_class.replace("/", "_") + ".json")
 GEMM_SOURCE = os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", "gemm_decode.hip")
 
 
@@ -204,10 +207,11 @@ def source_hash(path=GEMM_SOURCE):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_counters(fetch_dir, write_dir, kernel_pattern):
-    """Average HBM bytes per dispatch of the kernel matching kernel_pattern, from FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads for the 1 GiB
-    reference copy (--copy-calibration).  Written to profiles/ with the GEMM source hash."""
+def traffic_from_counters(fetch_dir, write_dir, kernel_pattern, kernel_class):
+    """Average HBM bytes per dispatch of the kernel matching kernel_pattern (of class kernel_class),
+    from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for the 1 GiB reference copy (--copy-calibration).  Written to profiles/ with the hash of the
+    decode GEMM source (which holds both decode GEMM kernels and their configuration tables)."""
     fetch, write = _counter_per_dispatch(fetch_dir, "FETCH_SIZE"), _counter_per_dispatch(write_dir, "WRITE_SIZE")
     copy_f = next(v for k, v in fetch.items() if "copy" in k.lower() or "elementwise" in k.lower())
     copy_w = next(v for k, v in write.items() if "copy" in k.lower() or "elementwise" in k.lower())
@@ -221,36 +225,37 @@ def traffic_from_counters(fetch_dir, write_dir, kernel_pattern):
     wb = sum(write[name]) / len(write[name]) * 1024.0 * w_scale
     res = {"kernel": name, "dispatches": len(fetch[name]), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
            "traffic_bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
-           "gemm_source_sha256_16": source_hash()}
+           "kernel_class": kernel_class, "gemm_source_sha256_16": source_hash()}
     os.makedirs(PROFILES, exist_ok=True)
-    with open(TRAFFIC_JSON, "w") as f:
+    out_json = traffic_json(kernel_class)
+    with open(out_json, "w") as f:
         json.dump(res, f, indent=1)
     # readable summary of the two counter runs next to it
-    lines = [f"# HBM traffic of the decode [q|k|v|up] GEMM ({name[:60]}...) in c1_prefill_heavy",
+    lines = [f"# HBM traffic of the {kernel_class} kernel ({name[:60]}...) in c1_prefill_heavy",
              "# commands (two passes, one counter each; the 1 GiB reference copy precedes the workload):",
              "#   cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT"]
     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         lines.append(f"#   rocprofv3 --pmc {c} -d {d} -o run -- python3 bench.py --steps 1 --warmup 0 "
                      "--decode-config none --no-cpu-baseline --no-profile --copy-calibration")
-    lines.append(f"#   python bench.py --traffic {fetch_dir} {write_dir} --kernel {kernel_pattern}")
+    lines.append(f"#   python bench.py --traffic {fetch_dir} {write_dir} --kernel {kernel_pattern} --kernel-class {kernel_class}")
     lines.append(f"# scaling: FETCH_SIZE of the 1 GiB copy reads {max(copy_f):.0f} KiB (x{f_scale:.3f}), "
                  f"WRITE_SIZE {max(copy_w):.0f} KiB (x{w_scale:.3f})")
     lines.append("# per-kernel averages (KiB per dispatch, unscaled), the 10 most frequent kernels:")
     for cname, d in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
         for k, vs in sorted(d.items(), key=lambda kv: -len(kv[1]))[:10]:
             lines.append(f"{cname}  {len(vs):6d}  {sum(vs) / len(vs):10.1f}  {k[:110]}")
-    lines.append(f"# result ({os.path.relpath(TRAFFIC_JSON, ROOT)}): fetch {fb / 1e6:.2f} MB + write {wb / 1e6:.2f} MB "
+    lines.append(f"# result ({os.path.relpath(out_json, ROOT)}): fetch {fb / 1e6:.2f} MB + write {wb / 1e6:.2f} MB "
                  f"per launch = {(fb + wb) / 1e6:.2f} MB")
-    with open(os.path.join(PROFILES, "counters_decode_gemm_qkv_up_c1.txt"), "w") as f:
+    with open(os.path.join(PROFILES, "counters_" + kernel_class.replace("/", "_") + "_c1.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     return res
 
 
-def stored_traffic():
-    """Counter-measured bytes per launch of the decode [q|k|v|up] GEMM, or None if absent or if the
+def stored_traffic(kernel_class):
+    """Counter-measured bytes per launch of a decode kernel class, or None if absent or if the decode
     GEMM source changed since the counters were taken."""
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(traffic_json(kernel_class)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -337,6 +342,7 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="HBM traffic of the dominant kernel from two rocprofv3 --pmc runs; writes profiles/")
     ap.add_argument("--kernel", default=None, help="kernel-name pattern for --traffic")
+    ap.add_argument("--kernel-class", default="decode/gemm_qkv_up", help="kernel class of --kernel")
     ap.add_argument("--compare-vanilla", action="store_true",
                     help="also time token-level transformers of the same width and depth on the same kernels")
     ap.add_argument("--batch-sweep", default=None, metavar="B1,B2,...",
@@ -352,7 +358,8 @@ def main():
         print(summarize_rocprof(args.summarize))
         return
     if args.traffic:
-        print(json.dumps(traffic_from_counters(args.traffic[0], args.traffic[1], args.kernel), indent=1))
+        print(json.dumps(traffic_from_counters(args.traffic[0], args.traffic[1], args.kernel, args.kernel_class),
+                         indent=1))
         return
     if args.batch_sweep:
         batch_sweep(args)
@@ -422,10 +429,11 @@ def main():
                                 f"class's kernel at the decode shape (bt_test_replay, weights cycled over all "
                                 f"layers of both decoders), after the timed steps; algorithmic bytes per launch from the profiled "
                                 f"repeat of the timed steps")
-        tr = stored_traffic()
-        if tr is not None and dominant == "decode/gemm_qkv_up":
+        tr = stored_traffic(dominant)
+        if tr is not None:
             result["roofline"]["traffic"] = round(tr["traffic_bytes_per_launch"], 1)
-            result["roofline"]["traffic_source"] = "profiles/traffic_decode_gemm_qkv_up.json (FETCH_SIZE + WRITE_SIZE)"
+            result["roofline"]["traffic_source"] = (os.path.relpath(traffic_json(dominant), ROOT) +
+                                                    " (FETCH_SIZE + WRITE_SIZE)")
         result["profiled_ms_per_step"] = round(prof_ms, 3)
         result["kernel_classes"] = classes
     del r

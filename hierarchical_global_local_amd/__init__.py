@@ -25,7 +25,8 @@ BT_FP32, BT_BF16 = 0, 1
 CONTEXT_MODES = {"prefix": 0, "sum": 1, "xattn": 2}
 
 PROFILE_KINDS = ["embed", "layernorm", "gemm_qkv_up", "gemm_out_down", "gemm_prefix", "gemm_head",
-                 "attn_prefill", "rope_scatter", "attn_block_decode", "attn_local", "finalize", "attn_cross"]
+                 "attn_prefill", "rope_scatter", "attn_block_decode", "attn_local", "finalize", "attn_cross",
+                 "local_attn_out"]
 
 
 class BtError(RuntimeError):
@@ -87,9 +88,11 @@ def lib() -> ctypes.CDLL:
     L.bt_test_gemm.argtypes = [c_i32, c_p, c_p, c_p, c_i32, c_i32, c_i32, ctypes.c_float, c_p]
     L.bt_set_graphs.argtypes = [c_p, c_i32]
     L.bt_test_replay.argtypes = [c_p, c_i32, c_i32]
+    L.bt_test_fuse_local.argtypes = [c_p, c_i32]
     for f in ("bt_init", "bt_prefill", "bt_prefill_lengths", "bt_prefill_ragged", "bt_prefill_rows",
               "bt_block_lengths", "bt_page_table", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
-              "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs", "bt_test_replay"):
+              "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs", "bt_test_replay",
+              "bt_test_fuse_local"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -248,6 +251,11 @@ class BlockTransformer:
 
     def set_graphs(self, enable: bool) -> None:
         check(lib().bt_set_graphs(self.h, 1 if enable else 0))
+
+    def set_fuse_local(self, enable: bool) -> None:
+        """Decode steps with the token decoder's local attention inside its [out|down] GEMM (default)
+        or as a launch of its own (see bt_test_fuse_local in include/bt_test.h)."""
+        check(lib().bt_test_fuse_local(self.h, 1 if enable else 0))
 
     def generate(self, prompt, G: int, logits_steps: Iterable[int] = ()):
         """Greedy generation of G tokens: ids [G, B] (device int32) and {step: logits [B, V] fp32}."""

@@ -233,6 +233,9 @@ struct bt_handle {
   int dec_nsplit = 1;         // key splits of block-attention decode for this batch size
   // decode steps replayed from HIP graphs, one per in-block offset j (0 = block step)
   bool use_graphs = true;
+  // decode steps run the token decoder's local attention inside its [out|down] GEMM where the
+  // shape allows (attn_out_splits); off: separate launches (test hook)
+  bool fuse_local = true;
   int graph_B = -1;
   std::vector<hipGraphExec_t> graphs;
 };
@@ -240,7 +243,7 @@ struct bt_handle {
 namespace {
 
 enum ProfKind { PK_EMBED = 0, PK_LN, PK_GEMM_QKV, PK_GEMM_OUT, PK_GEMM_PREFIX, PK_GEMM_HEAD, PK_ATTN_PREFILL,
-                PK_ROPE_SCATTER, PK_ATTN_DECODE, PK_ATTN_LOCAL, PK_FINALIZE, PK_ATTN_CROSS, PK_COUNT };
+                PK_ROPE_SCATTER, PK_ATTN_DECODE, PK_ATTN_LOCAL, PK_FINALIZE, PK_ATTN_CROSS, PK_LOCAL_OUT, PK_COUNT };
 static_assert(PK_COUNT == BT_PROFILE_KINDS, "profiler classes");
 
 // Records a pair of events around one launch with its algorithmic bytes and flops (the minimal
@@ -419,8 +422,9 @@ int run_ln_qkv(bt_handle* h, const LayerOff& w, int rows, bool ln_done = false) 
   return BT_OK;
 }
 
-// [attn | gelu(up) (| cross-attention)] x [W_o ; W_down (; W_xo)] + biases added into the residual stream
-int run_out(bt_handle* h, const LayerOff& w, int rows) {
+// Epilogue of the [out|down] GEMM with `splits` K splits; with more than one the partial products
+// are summed (with both biases) by the next LayerNorm.
+Epi resid_epi(bt_handle* h, const LayerOff& w, int rows, int splits) {
   const Layout& lo = h->lo;
   Epi ep{};
   ep.wscale = wscale(lo);
@@ -428,16 +432,22 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
   ep.bias2 = (const float*)P_(h, w.b2) + lo.D;
   ep.out0 = P_(h, lo.X);
   ep.ld0 = lo.D;
-  ep.splits = rows <= lo.rpart_rows ? resid_splits(rows, lo.D, w.k2) : 1;
+  ep.splits = splits;
   ep.part = (float*)P_(h, lo.rpart);
   if (ep.splits > 1) {
-    // the partial products are summed (with both biases) by the next LayerNorm
     h->pending.part = ep.part;
     h->pending.nsplit = ep.splits;
     h->pending.part_rows = rows;
     h->pending.bias_a = ep.bias;
     h->pending.bias_b = ep.bias2;
   }
+  return ep;
+}
+
+// [attn | gelu(up) (| cross-attention)] x [W_o ; W_down (; W_xo)] + biases added into the residual stream
+int run_out(bt_handle* h, const LayerOff& w, int rows) {
+  const Layout& lo = h->lo;
+  const Epi ep = resid_epi(h, w, rows, rows <= lo.rpart_rows ? resid_splits(rows, lo.D, w.k2) : 1);
   const double E = (double)lo.elem, D = lo.D, K2 = w.k2;
   Prof p(h, PK_GEMM_OUT, D * K2 * E + rows * K2 * E + 8.0 * rows * D + 8.0 * D, 2.0 * rows * D * K2);
   BT_CHECK(h, launch_gemm(lo.f32, P_(h, lo.ACT), nullptr, w.k2, P_(h, w.w2), rows, lo.D, w.k2,
@@ -446,13 +456,61 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
   return BT_OK;
 }
 
+// Partial count of the token decoder's fused local attention + [out|down] launch for one new
+// slot per row (attn_out_splits), 0 where it runs as two launches: fp32, head width other than
+// 64, cross-attention, or more rows than the partial buffer or the fused kernel take.
+int fused_local_splits(bt_handle* h, int m) {
+  const Layout& lo = h->lo;
+  const int rows = h->B * m;
+  if (m != 1 || !h->fuse_local || lo.f32 || lo.dh != 64 || lo.mode == BT_CTX_XATTN || rows > lo.rpart_rows ||
+      lo.Nt == 0)
+    return 0;
+  return attn_out_splits(rows, lo.D, lo.tok[0].k2, lo.H);
+}
+
+// Token layer l, one new slot s0 per row: local attention inside the [out|down] GEMM; its
+// `splits` partial products are folded by the next LayerNorm.
+int run_fused_local_out(bt_handle* h, int l, int s0, int splits) {
+  const Layout& lo = h->lo;
+  const LayerOff& w = lo.tok[l];
+  const int rows = h->B;
+  LocalStep ls{};
+  ls.qkv = (const f16*)P_(h, lo.QKV);
+  ls.ldq = w.n1;
+  ls.H = lo.H;
+  ls.Hkv = lo.Hkv;
+  ls.s0 = s0;
+  ls.rope = (const float2*)P_(h, lo.rope);
+  ls.kc = (f16*)local_k(h, l);
+  ls.vc = (f16*)local_v(h, l);
+  ls.cap = lo.lcap;
+  ls.rmap = h->rmap;
+  ls.scale_log2 = 1.4426950408889634f / sqrtf((float)lo.dh);
+  const Epi ep = resid_epi(h, w, rows, splits);
+  const double E = (double)lo.elem, D = lo.D, Bd = h->B, KVW = (double)lo.Hkv * lo.dh, F = lo.F;
+  // weights, the GELU columns, q|k|v, cached K/V read and the new K/V written, the residual
+  // stream read and written (fp32) and both biases
+  Prof p(h, PK_LOCAL_OUT,
+         D * w.k2 * E + rows * F * E + (Bd * s0 * 2.0 * KVW + rows * (D + 4.0 * KVW)) * E + 8.0 * rows * D + 8.0 * D,
+         2.0 * rows * D * w.k2 + 4.0 * Bd * lo.H * lo.dh * (s0 + 1));
+  BT_CHECK(h, launch_attn_out_decode(P_(h, lo.ACT), P_(h, w.w2), rows, lo.D, w.k2, ep, ls, h->st),
+           "local attention + out|down");
+  return BT_OK;
+}
+
 // token decoder over new local slots [s0, s0 + m) of every row (rows = B * m in X)
 int run_token_decoder(bt_handle* h, int m, int s0, bool first_ln_done = false) {
   const Layout& lo = h->lo;
   const int rows = h->B * m;
+  const int fused_splits = fused_local_splits(h, m);
   for (int l = 0; l < lo.Nt; ++l) {
     int r = run_ln_qkv(h, lo.tok[l], rows, l == 0 && first_ln_done);
     if (r) return r;
+    if (fused_splits > 0) {
+      r = run_fused_local_out(h, l, s0, fused_splits);
+      if (r) return r;
+      continue;
+    }
     {
       const double E = (double)lo.elem, D = lo.D, Bd = h->B, KVW = (double)lo.Hkv * lo.dh;
       double pairs = 0;
@@ -1096,6 +1154,13 @@ int bt_block_lengths(bt_handle* h, int32_t* lengths) {
   return BT_OK;
 }
 
+int bt_test_fuse_local(bt_handle* h, int32_t enable) {
+  if (!h) return fail(BT_ERR_INVALID_ARG, "NULL handle");
+  if (h->fuse_local != (enable != 0)) drop_graphs(h);
+  h->fuse_local = enable != 0;
+  return BT_OK;
+}
+
 int bt_set_graphs(bt_handle* h, int32_t enable) {
   if (!h) return fail(BT_ERR_INVALID_ARG, "NULL handle");
   h->use_graphs = enable != 0;
@@ -1174,6 +1239,15 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
       hipError_t e = launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), h->B, w.n1 + lo.F, lo.D,
                                  EPI_QKV_GELU, ep, h->st);
       if (e != hipSuccess) r = hip_fail(h, e, "replay gemm");
+    } else if (kind == PK_LOCAL_OUT) {
+      // the token decoder's fused local attention + [out|down] launch at the next local slot (not
+      // yet valid; the next token step writes it again), cycling over the token layers; its
+      // products only go to the split-K partials, which nothing folds
+      const int fs = fused_local_splits(h, 1);
+      if (fs == 0) return fail(BT_ERR_UNSUPPORTED, "no fused [out|down] launch at this shape to replay");
+      const ResidPending keep = h->pending;
+      r = run_fused_local_out(h, i % lo.Nt, std::min(h->local_len, lo.lcap - 1), fs);
+      h->pending = keep;
     } else if (kind == PK_ATTN_DECODE) {
       const int l = i % lo.Nb;
       hipError_t e = launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,

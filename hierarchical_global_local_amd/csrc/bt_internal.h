@@ -180,6 +180,25 @@ hipError_t launch_gemm_skinny(const SkinnyPlan& p, const void* A1, const void* A
 hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N,
                        int K, EpiMode mode, const Epi& ep, hipStream_t st);
 
+// Decode step of a token-decoder layer with head width 64 (fp16): the local attention of the new
+// slot fused into the [out|down] GEMM that consumes it (gemm_decode.hip).  ACT holds the GELU
+// columns [D, D + F) of the operand (width K = D + F, fragment order); W is that GEMM's weight.
+// Every product goes to ep.part as a split-K partial: attn_out_splits(M, N = D, K, H) of them
+// (0: the shape does not run fused), folded with both biases by the next LayerNorm.
+struct LocalStep {
+  const f16* qkv;  // [M][ldq]: q (H x 64) | k (Hkv x 64) | v (Hkv x 64) of the new slot
+  int ldq, H, Hkv, s0;  // s0: local slot of the new entry (= entries already cached)
+  const float2* rope;   // [slot][32] (cos, sin)
+  f16* kc;              // local keys [cache row][Hkv][cap][64]; the new key is written at slot s0
+  f16* vc;              // local values, same layout
+  int cap;
+  const int* rmap;  // cache row of activation row b (null: b)
+  float scale_log2;  // log2(e) / sqrt(64)
+};
+int attn_out_splits(int M, int N, int K, int H);
+hipError_t launch_attn_out_decode(const void* ACT, const void* W, int M, int N, int K, const Epi& ep,
+                                  const LocalStep& ls, hipStream_t st);
+
 // ---- attention
 // Attention launchers take H query heads and Hkv key/value heads of width dh (H % Hkv == 0); a
 // QKV row is [q: H dh | k: Hkv dh | v: Hkv dh] and query head h reads KV head h / (H / Hkv).

@@ -15,19 +15,26 @@ namespace bt {
 // path), DEPTH K steps in flight per wave.  The KW partial tiles are summed once through LDS, in a
 // fixed order, and the epilogue writes 8 consecutive columns per thread.  gridDim.y > 1 splits K
 // over workgroups (EPI_RESID only): the partial products go to ep.part and the consumer adds them.
-template <int MG, int MW, int NG, int KW, int MODE, int DEPTH = 2>
-__global__ __launch_bounds__(64 * MW * KW) void k_gemm_skinny(const f16* __restrict__ A1, const f16* __restrict__ A2,
-                                                              const f16* __restrict__ W, int M, int N, int K, Epi ep) {
+// One workgroup's tile: all rows x the 16 * NG columns of column slab `slab`, over the K steps
+// [ks_lo, ks_hi) cut into `nsplit` equal ranges of which this is range `split`.  EPI_RESID with
+// to_part writes the partial products to ep.part slot `pslot`.  red: KW * R * (16 NG + 4) floats of LDS.
+template <int MG, int MW, int NG, int KW>
+constexpr int skinny_lds_floats() { return KW * (16 * MG * MW) * (16 * NG + 4); }
+
+template <int MG, int MW, int NG, int KW, int MODE, int DEPTH>
+__device__ __forceinline__ void skinny_tile(const f16* __restrict__ A1, const f16* __restrict__ A2,
+                                            const f16* __restrict__ W, int M, int N, int K, const Epi& ep, int slab,
+                                            int ks_lo, int ks_hi, int split, int nsplit, bool to_part, int pslot,
+                                            float* __restrict__ red) {
   constexpr int R = 16 * MG * MW, C = 16 * NG, CLD = C + 4, NT = 64 * MW * KW;
-  __shared__ __attribute__((aligned(16))) float red[KW * R * CLD];
   const int KS = K / 32, mgs = (M + 15) / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int mw = wave % MW, kw = wave / MW;
-  const int ng0 = blockIdx.x * NG, n0 = ng0 * 16;
+  const int ng0 = slab * NG, n0 = ng0 * 16;
   const f16* __restrict__ A = (MODE == EPI_QKV_GELU && n0 >= ep.n_split) ? A2 : A1;
-  // K steps of this workgroup (split blockIdx.y of gridDim.y), then of this wave
-  const int S = gridDim.y, sper = (KS + S - 1) / S;
-  const int sb = blockIdx.y * sper, se = min(KS, sb + sper);
+  // K steps of this workgroup, then of this wave
+  const int sper = (ks_hi - ks_lo + nsplit - 1) / nsplit;
+  const int sb = min(ks_hi, ks_lo + split * sper), se = min(ks_hi, sb + sper);
   const int wper = (se - sb + KW - 1) / KW;
   const int kb = min(se, sb + kw * wper), ke = min(se, kb + wper);
 
@@ -117,8 +124,8 @@ __global__ __launch_bounds__(64 * MW * KW) void k_gemm_skinny(const f16* __restr
         }
       }
     } else if constexpr (MODE == EPI_RESID) {
-      if (S > 1) {
-        float* p = ep.part + ((size_t)blockIdx.y * M + row) * N + col;
+      if (to_part) {
+        float* p = ep.part + ((size_t)pslot * M + row) * N + col;
         if (live) {
           *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
           *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -164,9 +171,257 @@ __global__ __launch_bounds__(64 * MW * KW) void k_gemm_skinny(const f16* __restr
         const unsigned long long other = shfl_xor_u64(best, o);
         best = other > best ? other : best;
       }
-      if (live && cl == 0) ep.keys[(size_t)row * ep.keys_ld + blockIdx.x] = best;
+      if (live && cl == 0) ep.keys[(size_t)row * ep.keys_ld + slab] = best;
     }
   }
+}
+
+// grid (N / (16 NG), splits): gridDim.y > 1 splits K over workgroups (EPI_RESID only), whose
+// partial products go to ep.part for the consumer to add.
+template <int MG, int MW, int NG, int KW, int MODE, int DEPTH = 2>
+__global__ __launch_bounds__(64 * MW * KW) void k_gemm_skinny(const f16* __restrict__ A1, const f16* __restrict__ A2,
+                                                              const f16* __restrict__ W, int M, int N, int K, Epi ep) {
+  __shared__ __attribute__((aligned(16))) float red[skinny_lds_floats<MG, MW, NG, KW>()];
+  skinny_tile<MG, MW, NG, KW, MODE, DEPTH>(A1, A2, W, M, N, K, ep, blockIdx.x, 0, K / 32, blockIdx.y, gridDim.y,
+                                           gridDim.y > 1, blockIdx.y, red);
+}
+
+// ---------------------------------------------------------------- local attention + [out|down]
+// Decode step of a token-decoder layer (one new local slot per row, head width 64): the token
+// decoder's attention over its local window (prefix + the current block's tokens, summary page
+// §3.4, The Token Decoder) is computed inside the [out|down] GEMM that consumes it, so that its
+// latency overlaps the weight stream of the same launch instead of costing a launch of its own.
+//  * attention workgroups (rb, hp, cp): rows [RB rb, RB rb + RB) (RB = 4 x waves: 32 or 64),
+//    query heads 2hp and 2hp + 1, output columns [128 cp, 128 cp + 128).  Half the waves take
+//    each head, 8 rows per wave: lane = (row, 8 dimensions), rotary at the new slot, the new key
+//    and value from the q | k | v row and the s0 cached ones from the local cache, softmax in base
+//    2.  The outputs go to LDS in fragment order and feed 8 MFMAs per wave (column group
+//    8 cp + wave % 8, the heads' four K steps); the products are partial sums (split hp) of the
+//    residual update.  The workgroups with cp = 0 also write the new key (rotary applied,
+//    rounded) and value to local slot s0 (first query head of a KV group).  A workgroup issues
+//    its loads in the order it consumes them and the weight tiles last, so that waiting for the
+//    attention's operands never waits for the weight stream.
+//  * GEMM workgroups: the skinny tiles over the GELU columns [D, D + F) of the K range, K split
+//    mlp_splits ways, partial slots H / 2 + split.
+// All partials (H / 2 + mlp_splits of them) are folded, with both biases, by the next LayerNorm.
+
+__device__ __forceinline__ void h8_to_f(const half8& v, float* o) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
+}
+
+template <int MG, int MW, int NG, int KW>
+__global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict__ ACT, const f16* __restrict__ W,
+                                                           int M, int N, int K, Epi ep, LocalStep ls, int n_attn,
+                                                           int n_cp, int mlp_splits, int spread) {
+  // attention tiles of RB rows: WPI waves per head (8 rows each), two heads
+  constexpr int NWAVE = MW * KW, RB = 4 * NWAVE, RG = RB / 16, WPI = NWAVE / 2;
+  static_assert(NWAVE == 8 || NWAVE == 16, "8 or 16 waves");
+  constexpr int LDS_GEMM = skinny_lds_floats<MG, MW, NG, KW>(), LDS_A = RG * 4 * 256, LDS_ATT = LDS_A + 64;
+  __shared__ __attribute__((aligned(16))) float lds[LDS_GEMM > LDS_ATT ? LDS_GEMM : LDS_ATT];
+  const int n_hp = ls.H / 2;
+  // Workgroup id -> tile.  Workgroup ids x, x + 8, ... run on XCD x.  Attention group a = (rb, hp)
+  // goes to XCD a % 8 with all n_cp of its column parts (the copies of its attention then share
+  // that XCD's L2), and the GEMM tiles fill each XCD's remaining workgroups in order (consecutive
+  // slabs of one K split share their operand rows).  spread = 0 (an XCD would hold more attention
+  // tiles than workgroups): tiles in id order.
+  const int nb = gridDim.x, n_grp = n_attn / n_cp;
+  int t = blockIdx.x;
+  if (spread) {
+    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    const int na = (n_grp / 8 + (x < n_grp % 8)) * n_cp;
+    if (i < na) {
+      t = ((i / n_cp) * 8 + x) * n_cp + i % n_cp;
+    } else {
+      const int before = x * (nb / 8) + min(x, nb % 8) - n_cp * (x * (n_grp / 8) + min(x, n_grp % 8));
+      t = n_attn + before + (i - na);
+    }
+  }
+  if (t >= n_attn) {
+    const int u = t - n_attn, slabs = N / (16 * NG);
+    skinny_tile<MG, MW, NG, KW, EPI_RESID, 2>(ACT, nullptr, W, M, N, K, ep, u % slabs, ls.H * 2, K / 32,
+                                              u / slabs, mlp_splits, true, n_hp + u / slabs, lds);
+    return;
+  }
+  const int cp = t % n_cp, hp = (t / n_cp) % n_hp, rb = t / (n_cp * n_hp);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int KS = K / 32, ng = cp * 8 + (wave & 7);
+  const int g = lane & 7, it = wave / WPI, lr = 8 * (wave % WPI) + (lane >> 3);
+  const int r = rb * RB + lr, rc = min(r, M - 1);
+  const int G = ls.H / ls.Hkv, s0 = ls.s0, h = 2 * hp + it, hk = h / G;
+  const int crow = ls.rmap ? ls.rmap[rc] : rc;
+  // Loads in the order they are consumed (a wait for one load is a wait for every earlier one):
+  // q | k | v, the cached entries, the rotary row (one float per thread of the first wave), then
+  // the weight tiles, which only the MFMAs at the end need.
+  const f16* __restrict__ qrow = ls.qkv + (size_t)rc * ls.ldq + 8 * g;
+  const half8 qh = *(const half8*)(qrow + h * 64);
+  const half8 kh = *(const half8*)(qrow + (ls.H + hk) * 64);
+  const half8 vh = *(const half8*)(qrow + (ls.H + ls.Hkv + hk) * 64);
+  // element offset of (cache row, KV head, entry 0, dimension 8g) in the local caches
+  const size_t base = ((size_t)crow * ls.Hkv + hk) * ls.cap * 64 + 8 * g;
+  half8 ch[8];  // cached keys 0..3, values 0..3 of the first group of four entries
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = min(u, max(s0 - 1, 0));  // clamped into the cached entries (masked below)
+    ch[u] = *(const half8*)(ls.kc + base + (size_t)j * 64);
+    ch[4 + u] = *(const half8*)(ls.vc + base + (size_t)j * 64);
+  }
+  float rv = 0.f;
+  if (threadIdx.x < 64) rv = ((const float*)(ls.rope + (size_t)s0 * 32))[threadIdx.x];
+  half8 rw[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) rw[ks] = *(const half8*)(W + (((size_t)ng * KS + 4 * hp + ks) * 64 + lane) * 8);
+  __builtin_amdgcn_sched_barrier(0);
+  float* __restrict__ rope_s = lds + LDS_A;
+  if (threadIdx.x < 64) rope_s[threadIdx.x] = rv;
+  __syncthreads();
+  float cs[8], sn[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float4 c = *(const float4*)(rope_s + 2 * ((8 * g) % 32) + 4 * e);
+    cs[2 * e] = c.x, sn[2 * e] = c.y, cs[2 * e + 1] = c.z, sn[2 * e + 1] = c.w;
+  }
+  const bool first = g < 4;  // dimensions [0, 32): rotated with -sin
+  const bool live = r < M;
+  f16* __restrict__ at = (f16*)lds;  // A tiles [RG][4 K steps][512]
+  float q[8], kn[8], vn[8];
+  h8_to_f(qh, q);
+  h8_to_f(kh, kn);
+  h8_to_f(vh, vn);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float qp = __shfl_xor(q[e], 4, 64), kp = __shfl_xor(kn[e], 4, 64);
+    q[e] = first ? q[e] * cs[e] - qp * sn[e] : q[e] * cs[e] + qp * sn[e];
+    kn[e] = (float)to_f16(first ? kn[e] * cs[e] - kp * sn[e] : kn[e] * cs[e] + kp * sn[e]);
+  }
+  if (cp == 0 && live && h % G == 0) {
+    half8 kw8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kw8[e] = (f16)kn[e];
+    *(half8*)(ls.kc + base + (size_t)s0 * 64) = kw8;
+    *(half8*)(ls.vc + base + (size_t)s0 * 64) = vh;
+  }
+  // online softmax over the s0 cached keys (groups of four) and the new one
+  float mrun = -INFINITY, lrun = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int j0 = 0; j0 < s0; j0 += 4) {
+    if (j0 > 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = min(j0 + u, s0 - 1);
+        ch[u] = *(const half8*)(ls.kc + base + (size_t)j * 64);
+        ch[4 + u] = *(const half8*)(ls.vc + base + (size_t)j * 64);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float kv[8];
+      h8_to_f(ch[u], kv);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kv[e], dot);
+      dot += __shfl_xor(dot, 1, 64);
+      dot += __shfl_xor(dot, 2, 64);
+      dot += __shfl_xor(dot, 4, 64);
+      if (j0 + u < s0) {
+        const float sc = dot * ls.scale_log2, mn = fmaxf(mrun, sc);
+        const float corr = exp2f(mrun - mn), p = exp2f(sc - mn);
+        h8_to_f(ch[4 + u], kv);
+        lrun = lrun * corr + p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = o[e] * corr + p * kv[e];
+        mrun = mn;
+      }
+    }
+  }
+  {
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kn[e], dot);
+    dot += __shfl_xor(dot, 1, 64);
+    dot += __shfl_xor(dot, 2, 64);
+    dot += __shfl_xor(dot, 4, 64);
+    const float sc = dot * ls.scale_log2, mn = fmaxf(mrun, sc);
+    const float corr = exp2f(mrun - mn), p = exp2f(sc - mn);
+    lrun = lrun * corr + p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = o[e] * corr + p * vn[e];
+  }
+  const float inv = live ? 1.0f / lrun : 0.f;
+  half8 ov;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ov[e] = to_f16(o[e] * inv);
+  // A tile (row group lr / 16, K step 2 it + g / 4): element (row lr % 16, column 8 (g % 4) + e)
+  *(half8*)(at + ((lr >> 4) * 4 + 2 * it + (g >> 2)) * 512 + ((g & 3) * 16 + (lr & 15)) * 8) = ov;
+  __syncthreads();
+  // the 16 x 16 output tiles (row groups rg0, rg0 + 1; column group ng) over the heads' 4 K steps
+  const int rg0 = (wave >> 3) * 2;
+  float4_ acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    acc[i] = float4_{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)(at + ((rg0 + i) * 4 + ks) * 512 + lane * 8),
+                                                      rw[ks], acc[i], 0, 0, 0);
+  }
+  const int col = ng * 16 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = rb * RB + (rg0 + i) * 16 + 4 * (lane >> 4) + e;
+      if (row < M) ep.part[((size_t)hp * M + row) * N + col] = acc[i][e] * ep.wscale;
+    }
+}
+
+template <int MG, int MW, int NG, int KW>
+static hipError_t launch_attn_out_cfg(const void* ACT, const void* W, int M, int N, int K, const Epi& ep,
+                                      const LocalStep& ls, int mlp_splits, hipStream_t st) {
+  constexpr int RB = 4 * MW * KW;
+  const int n_cp = N / 128, n_attn = (M + RB - 1) / RB * (ls.H / 2) * n_cp;
+  const int n_gemm = N / (16 * NG) * mlp_splits, nb = n_attn + n_gemm, n_grp = n_attn / n_cp;
+  const int spread = (n_grp + 7) / 8 * n_cp <= nb / 8;
+  hipLaunchKernelGGL((k_attn_out<MG, MW, NG, KW>), dim3(nb), dim3(64 * MW * KW), 0, st, (const f16*)ACT,
+                     (const f16*)W, M, N, K, ep, ls, n_attn, n_cp, mlp_splits, spread);
+  return hipGetLastError();
+}
+
+// Partial count of the fused launch (0: the shape does not run fused): H / 2 attention splits, and
+// the GELU columns' K split so that attention and GEMM tiles together take about one workgroup per
+// CU (every split owning at least one K step, at most 16 partials).
+int attn_out_splits(int M, int N, int K, int H) {
+  if (M < 1 || M > 256 || H < 2 || H % 2 || H > 30 || N != 64 * H || K <= N || (K - N) % 32) return 0;
+  const SkinnyPlan p = skinny_plan(M, N, K, EPI_RESID);
+  if (!p.ok) return 0;
+  const int rb = 4 * p.mw * p.kw, n_attn = (M + rb - 1) / rb * (H / 2) * (N / 128);
+  const int slabs = N / (16 * p.ng), ks = (K - N) / 32;
+  int s = std::min(16 - H / 2, std::max(1, (256 - n_attn) / slabs));
+  s = std::max(1, std::min(s, ks / p.kw));
+  const int per = (ks + s - 1) / s;
+  s = (ks + per - 1) / per;  // every split owns at least one K step
+  return H / 2 + s;
+}
+
+
+hipError_t launch_attn_out_decode(const void* ACT, const void* W, int M, int N, int K, const Epi& ep,
+                                  const LocalStep& ls, hipStream_t st) {
+  const int total = attn_out_splits(M, N, K, ls.H);
+  if (total <= ls.H / 2 || total > 16 || !ep.part || ls.Hkv < 1 || ls.H % ls.Hkv || ls.s0 < 0 ||
+      ls.s0 >= ls.cap || ls.ldq < (ls.H + 2 * ls.Hkv) * 64 || ls.ldq % 8)
+    return hipErrorInvalidValue;
+  const int mlp_splits = total - ls.H / 2;
+  const SkinnyPlan p = skinny_plan(M, N, K, EPI_RESID);
+#define BT_AO(MG, MW, NG, KW) \
+  if (p.mg == MG && p.mw == MW && p.ng == NG && p.kw == KW) return launch_attn_out_cfg<MG, MW, NG, KW>(ACT, W, M, N, K, ep, ls, mlp_splits, st);
+  BT_AO(1, 1, 2, 8)
+  BT_AO(2, 1, 2, 8)
+  BT_AO(4, 1, 2, 8)
+  BT_AO(4, 2, 2, 4)
+  BT_AO(4, 4, 2, 4)
+#undef BT_AO
+  return hipErrorInvalidValue;
 }
 
 template <int MG, int MW, int NG, int KW>

@@ -18,9 +18,10 @@ extern "C" {
  * start-slot rows, 1 LayerNorms, 2 [q|k|v|up] GEMMs (with GELU), 3 [out|down] GEMMs (residual
  * add), 4 context projection (and the cross-attention key/value projection), 5 classifier +
  * argmax, 6 prefill attention, 7 prefill rotary/KV scatter, 8 block-attention decode (incl. split
- * merge), 9 local attention, 10 greedy-id finalisation, 11 cross-attention.  Each class is counted
- * separately for launches made by bt_prefill (index k) and by bt_decode_step (index 12 + k). */
-#define BT_PROFILE_KINDS 12
+ * merge), 9 local attention, 10 greedy-id finalisation, 11 cross-attention, 12 local attention
+ * inside the [out|down] GEMM (token decoder, one new slot per row).  Each class is counted
+ * separately for launches made by bt_prefill (index k) and by bt_decode_step (index 13 + k). */
+#define BT_PROFILE_KINDS 13
 
 /* Start (on != 0) or stop recording a pair of HIP events around every kernel launch of the
  * handle, on the handle's stream.  Clears what was recorded before. */
@@ -36,12 +37,21 @@ int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* la
 /* Launch again, `reps` times back to back on the handle's stream, the kernel of one decode launch
  * class at the batch of the last prefill, for timing it without per-launch events.  kind (profile
  * class index): 2 = the decode [q|k|v|up] GEMM, cycling over the weights of all token- and
- * block-decoder layers; 8 = block-attention
- * decode at the current block-KV length, cycling over the block-decoder layers.  Only activations
- * are overwritten, plus for kind 8 the block-KV entry at the current length (not yet valid; the
- * next block step writes it again), so decoding can continue afterwards.  BT_ERR_STATE before a
- * prefill; BT_ERR_INVALID_ARG for other kinds. */
+ * block-decoder layers; 8 = block-attention decode at the current block-KV length, cycling over
+ * the block-decoder layers; 12 = the token decoder's local attention inside its [out|down] GEMM
+ * (see bt_test_fuse_local) at the next local slot, cycling over the token-decoder layers
+ * (BT_ERR_UNSUPPORTED where decode steps do not run it).  Only activations and split-K partials
+ * are overwritten, plus the cache entry each kind appends (kind 8: the block-KV entry at the
+ * current length; kind 12: the local-KV entry at the next local slot), which is not yet valid and is
+ * written again by the next step that uses it, so decoding can continue afterwards.
+ * BT_ERR_STATE before a prefill; BT_ERR_INVALID_ARG for other kinds. */
 int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps);
+
+/* enable = 0: decode steps launch the token decoder's local attention separately from its
+ * [out|down] GEMM instead of inside it (the default where the shape allows: fp16, head width 64,
+ * prefix or summation context, at most 256 rows).  Same results up to the summation order of the
+ * residual update.  Drops captured decode graphs when the setting changes. */
+int bt_test_fuse_local(bt_handle* h, int32_t enable);
 
 /* C[M][N] = scale * A[M][K] * W[N][K]^T in fp32 (C row-major), on `stream` (a hipStream_t).
  * dtype BT_FP32: A and W fp32, row-major.  BT_BF16: A and W fp16 (the library's matrix-operand

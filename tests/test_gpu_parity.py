@@ -136,6 +136,48 @@ def test_bf16_small_every_step(kw, max_tokens):
     assert model.cache_lengths() == (st.block_kv_len, st.local_kv_len)
 
 
+@pytest.mark.parametrize("kw,B", [(dict(), 1), (dict(), 5), (dict(d_model=256, n_heads=4), 40),
+                                  (dict(d_model=256, n_heads=4, n_kv_heads=2), 100),
+                                  (dict(d_model=384, n_heads=6, n_kv_heads=1, d_mlp=768), 200),
+                                  (dict(context_mode="sum"), 70), (dict(block_len=8, prefix_len=3), 130)])
+def test_fused_local_attention_out_gemm(kw, B):
+    """The token decoder's local attention computed inside its [out|down] GEMM (the default decode
+    path for fp16 with head width 64) against the oracle at every step, and against the separate
+    launches: batches of 1 to 200 rows cover every workgroup shape of the fused kernel (8 and 16
+    waves, one to four 64-row attention blocks), local windows up to 11 entries take the loop over
+    cached keys past its first group of four."""
+    torch = require_gpu()
+    import hierarchical_global_local_amd as hg
+    cfg = SMALL_BF16.with_(batch=B, **kw)
+    log(f"fused local attention case {kw} B={B}")
+    W = wl.make_weights(cfg, seed=21, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=21)
+    G = cfg.gen_len
+    d_prompt = torch.from_numpy(np.ascontiguousarray(prompt, dtype=np.int32)).cuda()
+    mt = wl.padded_len(cfg, prompt.shape[1]) + G
+    runs = {}
+    for fused in (True, False):
+        model = hg.BlockTransformer(cfg, W, max_batch=B, max_tokens=mt)
+        model.set_fuse_local(fused)
+        ids, lg = model.generate(d_prompt, G, logits_steps=range(G))
+        torch.cuda.synchronize()
+        runs[fused] = (ids.cpu().numpy().T.copy(), np.stack([lg[g].cpu().numpy() for g in range(G)], axis=1))
+        del model
+    ids, gl = runs[True]
+    _, ref_lg, _ = om.generate(om.weights_as(W, np.float64), cfg, prompt, G, keep_logits=True, forced=ids)
+    err = np.abs(gl - ref_lg).max()
+    exact = check_ids_against(ref_lg, ids, BF16_TOL)
+    ids_s, gl_s = runs[False]
+    same = ids == ids_s
+    log(f"  fused: max-abs logit error {err:.3e}, exact argmax {exact:.3f}; ids equal to the separate "
+        f"launches {same.mean():.3f}")
+    assert err <= BF16_TOL
+    # up to the first step where the two id streams part, the logits agree within the tolerance
+    first = int(np.argmin(same.all(axis=0))) if not same.all() else G
+    if first > 0:
+        assert np.abs(gl[:, :first] - gl_s[:, :first]).max() <= BF16_TOL
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=4, n_kv_heads=1)])
 def test_deep_split_kv_long_context(kw):
     """12000 prompt blocks (L_B = 1) in the largest block-KV capacity, 131072 entries: the block
@@ -294,7 +336,8 @@ def test_vanilla_mode_fp32_and_bf16_every_step():
 
 def test_kernel_replay_leaves_decoding_unchanged():
     """bt_test_replay (used by the benchmark to time one kernel class) may only overwrite
-    activations and the not-yet-valid block-KV slot: decoding after it is bit-identical."""
+    activations, split-K partials and the not-yet-valid block-KV and local-KV slots: decoding
+    after it is bit-identical."""
     torch = require_gpu()
     import hierarchical_global_local_amd as hg
     cfg = SMALL_BF16
@@ -310,6 +353,7 @@ def test_kernel_replay_leaves_decoding_unchanged():
         for g in range(1, G):
             if g in (3, 4, 7):  # after token steps and after a block step
                 model.replay("gemm_qkv_up", 5)
+                model.replay("local_attn_out", 5)
                 model.replay("attn_block_decode", 5)
             model.decode_step(ids[g])
     torch.cuda.synchronize()
