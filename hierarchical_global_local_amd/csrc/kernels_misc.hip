@@ -423,12 +423,16 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
     // only the next step's input, from the id already at offset j of the current block
     id = cur[(size_t)b * L + j];
   } else {
-    // the row's keys are contiguous: 256 threads read 2 KB per pass (max is order-independent)
+    // the row's keys are contiguous: 256 threads read 8 keys each per pass, all loads in flight
+    // together (indices clamped into the row: a repeated key leaves the maximum unchanged)
     const unsigned long long* kr = keys + (size_t)b * ld;
     unsigned long long best = 0ull;
-    for (int p = tid; p < nparts; p += 256) {
-      const unsigned long long k = kr[p];
-      best = k > best ? k : best;
+    for (int p0 = 0; p0 < nparts; p0 += 8 * 256) {
+      unsigned long long k[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) k[u] = kr[min(p0 + tid + 256 * u, nparts - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) best = k[u] > best ? k[u] : best;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -449,27 +453,39 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
   if (ns.mode == 0) return;
   const int D = ns.D;
   const Tt* __restrict__ E = (const Tt*)ns.E;
-  float v[PER], g1[PER], b1[PER], g2[PER], b2[PER];
+  // token of each of this thread's columns (the block's ids for a block step), then every table
+  // load at once: no load waits behind another
+  int tok[PER], col[PER];
+  if (ns.mode == 1) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) tok[q] = id, col[q] = min(tid + 256 * q, D - 1);
+  } else {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int cc = min(tid + 256 * q, D - 1), o = cc / ns.width;
+      const int cv = cur[(size_t)cb * L + o];
+      tok[q] = o == j ? id : cv;
+      col[q] = cc - o * ns.width;
+    }
+  }
+  // every load first, through valid (clamped) addresses and behind no branch (the summand of a
+  // summation context is read from the parameters when there is none), then the arithmetic
+  float v[PER], ad[PER], g1[PER], b1[PER], g2[PER], b2[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    const int c = tid + 256 * q;
-    const int cc = min(c, D - 1);
-    int tok, col;
-    if (ns.mode == 1) {
-      tok = id, col = cc;
-    } else {
-      const int o = cc / ns.width;
-      tok = o == j ? id : cur[(size_t)cb * L + o];
-      col = cc - o * ns.width;
-    }
-    tok = tok < 0 ? 0 : (tok >= ns.V ? ns.V - 1 : tok);
-    float e = load_f32(E + (size_t)tok * ns.width + col);
-    if (ns.add) e += ns.add[(size_t)b * ns.add_ld + cc];
-    v[q] = c < D ? e : 0.f;
+    const int cc = min(tid + 256 * q, D - 1);
+    const int t = tok[q] < 0 ? 0 : (tok[q] >= ns.V ? ns.V - 1 : tok[q]);
+    v[q] = load_f32(E + (size_t)t * ns.width + col[q]);
+    ad[q] = *(ns.add ? ns.add + (size_t)b * ns.add_ld + cc : ns.lnp + cc);
     g1[q] = ns.lnp[cc];
     b1[q] = ns.lnp[D + cc];
     g2[q] = ns.lnp[2 * D + cc];
     b2[q] = ns.lnp[3 * D + cc];
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const float e = ns.add ? v[q] + ad[q] : v[q];
+    v[q] = tid + 256 * q < D ? e : 0.f;
   }
   float s = 0.f;
 #pragma unroll
