@@ -272,16 +272,22 @@ __global__ __launch_bounds__(256) void k_layernorm(float* __restrict__ X, int ro
         const int cc = 4 * min(t + TPR * j, nch - 1);
         add[j] = f4add(*(const float4*)(rp.bias_a + cc), *(const float4*)(rp.bias_b + cc));
       }
+      // every partial in flight at once, then the sums (in split order)
+      float4 pv[MAXS][CPT];
 #pragma unroll
       for (int q = 0; q < MAXS; ++q) {
         const int qq = min(q, rp.nsplit - 1);
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
           const int cc = 4 * min(t + TPR * j, nch - 1);
-          const float4 pv = *(const float4*)(rp.part + ((size_t)qq * rp.part_rows + xr) * D + cc);
-          add[j] = f4add(add[j], q < rp.nsplit ? pv : zero);
+          pv[q][j] = *(const float4*)(rp.part + ((size_t)qq * rp.part_rows + xr) * D + cc);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < MAXS; ++q)
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) add[j] = f4add(add[j], q < rp.nsplit ? pv[q][j] : zero);
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int c = t + TPR * j;
