@@ -389,15 +389,19 @@ static hipError_t launch_attn_out_cfg(const void* ACT, const void* W, int M, int
 }
 
 // Partial count of the fused launch (0: the shape does not run fused): H / 2 attention splits, and
-// the GELU columns' K split so that attention and GEMM tiles together take about one workgroup per
-// CU (every split owning at least one K step, at most 16 partials).
+// the GELU columns' K split so that attention and GEMM tiles together take at most about one
+// workgroup per CU and each wave about 3 K steps (every split owning at least one K step, at most
+// 16 partials).
 int attn_out_splits(int M, int N, int K, int H) {
   if (M < 1 || M > 256 || H < 2 || H % 2 || H > 30 || N != 64 * H || K <= N || (K - N) % 32) return 0;
   const SkinnyPlan p = skinny_plan(M, N, K, EPI_RESID);
   if (!p.ok) return 0;
   const int rb = 4 * p.mw * p.kw, n_attn = (M + rb - 1) / rb * (H / 2) * (N / 128);
   const int slabs = N / (16 * p.ng), ks = (K - N) / 32;
+  // (measured: fewer, longer splits win once each wave has about 3 K steps -- C1 decode 23.27 ->
+  // 23.10 ms at 4 splits instead of 7 -- the next LayerNorm then folds fewer partials)
   int s = std::min(16 - H / 2, std::max(1, (256 - n_attn) / slabs));
+  s = std::min(s, std::max(1, ks / (3 * p.kw)));
   s = std::max(1, std::min(s, ks / p.kw));
   const int per = (ks + s - 1) / s;
   s = (ks + per - 1) / per;  // every split owns at least one K step
