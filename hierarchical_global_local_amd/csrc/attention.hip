@@ -110,6 +110,66 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV,
   }
 }
 
+// fp16 block cache (values transposed), slot offset s0 % 8 == 0: the same with 16-byte accesses.
+// Keys: a thread takes 8 dimensions and their rotary partners (8 further by DH / 2) of one slot,
+// with the 8 (cos, sin) pairs as 4 16-byte loads.  Values: the 64 x DH tile goes through LDS and
+// leaves as 16-byte runs of 8 slots per dimension (element stores for a ragged last run).
+template <int DH>
+__global__ __launch_bounds__(256) void k_rope_scatter_v(const f16* __restrict__ QKV, int m, int s0, int H, int Hkv,
+                                                        const float2* __restrict__ rope, f16* __restrict__ Kc,
+                                                        f16* __restrict__ Vc, int cap, const int* __restrict__ rmap,
+                                                        KvPages pg) {
+  constexpr int NC = DH / 8, HALF = DH / 2, VLD = DH + 8;
+  __shared__ __attribute__((aligned(16))) f16 vtile[64 * VLD];
+  const int hk = blockIdx.y, b = blockIdx.z, i0 = blockIdx.x * 64, tid = threadIdx.x;
+  const size_t qw = (size_t)(H + 2 * Hkv) * DH, koff = (size_t)(H + hk) * DH, voff = (size_t)(H + Hkv + hk) * DH;
+  const int cb = rmap ? rmap[b] : b;
+  const int cnt = min(64, min(m, pg.nlim ? pg.nlim[cb] - s0 : m) - i0);
+  if (cnt <= 0) return;
+  // keys: items (slot si, chunk pair p < NC / 2)
+  for (int e = tid; e < cnt * (NC / 2); e += 256) {
+    const int si = e / (NC / 2), p = e % (NC / 2), slot = s0 + i0 + si;
+    const f16* kr = QKV + ((size_t)b * m + i0 + si) * qw + koff + 8 * p;
+    const half8 a = *(const half8*)kr, c = *(const half8*)(kr + HALF);
+    const float4* rp = (const float4*)(rope + (size_t)slot * HALF + 8 * p);
+    half8 oa, oc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 r = rp[q];  // (cos, sin) of dimensions 8p + 2q and 8p + 2q + 1
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e2 = 2 * q + u;
+        const float cs = u ? r.z : r.x, sn = u ? r.w : r.y;
+        const float x1 = (float)a[e2], x2 = (float)c[e2];
+        oa[e2] = to_f16(x1 * cs - x2 * sn);
+        oc[e2] = to_f16(x2 * cs + x1 * sn);
+      }
+    }
+    f16* kd = Kc + kv_key(pg, cb, hk, slot, Hkv, cap, DH) + 8 * p;
+    *(half8*)kd = oa;
+    *(half8*)(kd + HALF) = oc;
+  }
+  // values: rows of the tile into LDS (16 bytes per item), then 8-slot runs per dimension
+  for (int e = tid; e < cnt * NC; e += 256) {
+    const int si = e / NC, c = e % NC;
+    *(half8*)(vtile + si * VLD + 8 * c) = *(const half8*)(QKV + ((size_t)b * m + i0 + si) * qw + voff + 8 * c);
+  }
+  __syncthreads();
+  const int runs = (cnt + 7) / 8;
+  for (int e = tid; e < DH * runs; e += 256) {
+    const int d = e / runs, q = e % runs, n8 = min(8, cnt - 8 * q);
+    f16* vd = Vc + kv_val(pg, cb, hk, d, s0 + i0 + 8 * q, Hkv, cap, DH);
+    if (n8 == 8) {
+      half8 w;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = vtile[(8 * q + u) * VLD + d];
+      *(half8*)vd = w;
+    } else {
+      for (int u = 0; u < n8; ++u) vd[u] = vtile[(8 * q + u) * VLD + d];
+    }
+  }
+}
+
 hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed, hipStream_t st,
                                const int* rmap, const int* ptab, int pld, const int* nlim) {
@@ -117,6 +177,15 @@ hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, 
   if (Hkv < 1 || H % Hkv || (ptab && !v_transposed)) return hipErrorInvalidValue;
   const KvPages pg{ptab, pld, nlim};
   dim3 grid((m + 63) / 64, Hkv, B);
+  if (!f32 && v_transposed && s0 % 8 == 0 && cap % 8 == 0 && (dh == 64 || dh == 128)) {
+    if (dh == 64)
+      hipLaunchKernelGGL(k_rope_scatter_v<64>, grid, dim3(256), 0, st, (const f16*)QKV, m, s0, H, Hkv, rope, (f16*)Kc,
+                         (f16*)Vc, cap, rmap, pg);
+    else
+      hipLaunchKernelGGL(k_rope_scatter_v<128>, grid, dim3(256), 0, st, (const f16*)QKV, m, s0, H, Hkv, rope, (f16*)Kc,
+                         (f16*)Vc, cap, rmap, pg);
+    return hipGetLastError();
+  }
   if (f32)
     hipLaunchKernelGGL(k_rope_scatter<float>, grid, dim3(256), 0, st, (const float*)QKV, m, s0, H, Hkv, dh, rope,
                        (float*)Kc, (float*)Vc, cap, (int)v_transposed, rmap, pg);
