@@ -302,28 +302,34 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
         s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], s[nt], 0, 0, 0);
       }
     }
-    // causal mask (only the diagonal tile has masked keys) and the tile maximum of this lane's query
+    // causal mask (only the diagonal tile, the last one, has masked keys) and the tile maximum of
+    // this lane's query
     float mx = -INFINITY;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + nt * 16 + 4 * g + i;
-        float v = s[nt][i] * scale_log2;
-        v = key <= qi ? v : -INFINITY;
-        s[nt][i] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int i = 0; i < 4; ++i) s[nt][i] *= scale_log2;
+    if (t == ntiles - 1) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[nt][i] = kb + nt * 16 + 4 * g + i <= qi ? s[nt][i] : -INFINITY;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[nt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(mrun, mx);
-    const float corr = exp2f(mrun - mnew);
+    // hardware exp2 (arguments <= 0; results below 2^-126 flush to zero, a negligible weight)
+    const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
     float ls = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[nt][i] - mnew);
+        const float p = __builtin_amdgcn_exp2f(s[nt][i] - mnew);
         s[nt][i] = p;
         ls += p;
       }
