@@ -19,6 +19,10 @@
 namespace bt {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Softmax weights use the hardware exp2 (__builtin_amdgcn_exp2f, v_exp_f32) directly: every
+// argument is a difference from a running or final maximum (<= 0, or -inf giving 0), where the
+// library exp2f only adds a denormal-range fix-up (compare, select, ldexp); a weight below 2^-126
+// of the largest one is negligible.
 
 // 8 consecutive elements as floats
 __device__ __forceinline__ void load8(const f16* p, float* o) {
@@ -322,7 +326,6 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(mrun, mx);
-    // hardware exp2 (arguments <= 0; results below 2^-126 flush to zero, a negligible weight)
     const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
     float ls = 0.f;
 #pragma unroll
@@ -606,7 +609,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   for (int j = tid; j < cnt; j += 256)
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-      const float p = exp2f(sc[g * chunk + j] - mx[g]);
+      const float p = __builtin_amdgcn_exp2f(sc[g * chunk + j] - mx[g]);
       sc[g * chunk + j] = p;
       ls[g] += p;
     }
@@ -864,13 +867,13 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(m, mx);  // finite: every step has a cached key
-    const float corr = exp2f(m - mnew);
+    const float corr = __builtin_amdgcn_exp2f(m - mnew);
     float ls = 0.f;
 #pragma unroll
     for (int nt = 0; nt < KT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sv[nt][i] - mnew);
+        const float p = __builtin_amdgcn_exp2f(sv[nt][i] - mnew);
         sv[nt][i] = p;
         ls += p;
       }
@@ -902,7 +905,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
   }
   if (owns_new && (WPU == 1 || wave == 0)) {
     const float mnew = fmaxf(m, sc_new);
-    const float corr = exp2f(m - mnew), pn = exp2f(sc_new - mnew);
+    const float corr = __builtin_amdgcn_exp2f(m - mnew), pn = __builtin_amdgcn_exp2f(sc_new - mnew);
     l = l * corr + pn;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -927,7 +930,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
       if (M != -INFINITY)
 #pragma unroll
         for (int w = 0; w < WPU; ++w) {
-          const float f = exp2f(sm[w][cc] - M);
+          const float f = __builtin_amdgcn_exp2f(sm[w][cc] - M);
           L += f * sl_[w][cc];
           O += f * so[w][cc][d];
         }
@@ -968,7 +971,7 @@ __global__ void k_attn_combine(const float* __restrict__ part, int H, int nsplit
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * (DH + 2)]);
   float l = 0.f, o = 0.f;
   for (int s = 0; s < nsplit; ++s) {
-    const float w = exp2f(p[s * (DH + 2)] - M);
+    const float w = __builtin_amdgcn_exp2f(p[s * (DH + 2)] - M);
     l += w * p[s * (DH + 2) + 1];
     o += w * p[s * (DH + 2) + 2 + d];
   }
@@ -1224,8 +1227,8 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
     for (int w = 1; w < LPK; w <<= 1) dot += __shfl_xor(dot, w, 64);
     const float sc = j < nkeys ? dot * scale_log2 : -INFINITY;
     const float mn = fmaxf(mrun, sc);
-    const float corr = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
-    const float p = sc == -INFINITY ? 0.f : exp2f(sc - mn);
+    const float corr = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+    const float p = sc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc - mn);
     lrun = lrun * corr + p;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = o[e] * corr + p * (isnew ? vn[e] : (j < nkeys ? vc[e] : 0.f));
@@ -1236,8 +1239,8 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
   for (int w = LPK; w < 64; w <<= 1) {
     const float mo = __shfl_xor(mrun, w, 64), lo = __shfl_xor(lrun, w, 64);
     const float mn = fmaxf(mrun, mo);
-    const float c1 = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
-    const float c2 = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+    const float c1 = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+    const float c2 = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
     lrun = lrun * c1 + lo * c2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = o[e] * c1 + __shfl_xor(o[e], w, 64) * c2;
@@ -1328,8 +1331,8 @@ __global__ __launch_bounds__(256) void k_cross_attn(const T* __restrict__ QKV, i
     for (int w = 1; w < LPK; w <<= 1) dot += __shfl_xor(dot, w, 64);
     const float sc = p < P ? dot * scale_log2 : -INFINITY;
     const float mn = fmaxf(mrun, sc);
-    const float corr = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
-    const float pr = sc == -INFINITY ? 0.f : exp2f(sc - mn);
+    const float corr = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+    const float pr = sc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc - mn);
     lrun = lrun * corr + pr;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = o[e] * corr + pr * vc[e];
@@ -1339,8 +1342,8 @@ __global__ __launch_bounds__(256) void k_cross_attn(const T* __restrict__ QKV, i
   for (int w = LPK; w < 64; w <<= 1) {
     const float mo = __shfl_xor(mrun, w, 64), lo = __shfl_xor(lrun, w, 64);
     const float mn = fmaxf(mrun, mo);
-    const float c1 = mrun == -INFINITY ? 0.f : exp2f(mrun - mn);
-    const float c2 = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+    const float c1 = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+    const float c2 = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
     lrun = lrun * c1 + lo * c2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = o[e] * c1 + __shfl_xor(o[e], w, 64) * c2;

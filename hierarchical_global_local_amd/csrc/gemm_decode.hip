@@ -301,7 +301,8 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
     *(half8*)(ls.kc + base + (size_t)s0 * 64) = kw8;
     *(half8*)(ls.vc + base + (size_t)s0 * 64) = vh;
   }
-  // online softmax over the s0 cached keys (groups of four) and the new one
+  // online softmax over the s0 cached keys (groups of four) and the new one (hardware exp2 of
+  // differences from the running maximum, <= 0)
   float mrun = -INFINITY, lrun = 0.f, o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
       dot += __shfl_xor(dot, 4, 64);
       if (j0 + u < s0) {
         const float sc = dot * ls.scale_log2, mn = fmaxf(mrun, sc);
-        const float corr = exp2f(mrun - mn), p = exp2f(sc - mn);
+        const float corr = __builtin_amdgcn_exp2f(mrun - mn), p = __builtin_amdgcn_exp2f(sc - mn);
         h8_to_f(ch[4 + u], kv);
         lrun = lrun * corr + p;
 #pragma unroll
@@ -343,7 +344,7 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
     dot += __shfl_xor(dot, 2, 64);
     dot += __shfl_xor(dot, 4, 64);
     const float sc = dot * ls.scale_log2, mn = fmaxf(mrun, sc);
-    const float corr = exp2f(mrun - mn), p = exp2f(sc - mn);
+    const float corr = __builtin_amdgcn_exp2f(mrun - mn), p = __builtin_amdgcn_exp2f(sc - mn);
     lrun = lrun * corr + p;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = o[e] * corr + p * vn[e];
