@@ -353,6 +353,79 @@ static void launch_ln_small(int rows, float* X, int D, int stride, int off, cons
     launch_ln_cfg<256, CPT, 16>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
 }
 
+// Many rows (prefill), fp16 outputs in fragment order: a workgroup normalises one 16-row group,
+// each wave 4 rows with all their loads in flight (one wave per row, as above: the same sums in
+// the same order), assembles the group's fragment tiles in LDS and writes them out as one
+// contiguous range with 16-byte stores (the tiles of a 16-row group are contiguous in fragment
+// order; per-row stores would scatter 8-byte pieces 256 bytes apart).  D <= 256 CPT, D % 32 == 0.
+// Rows of the last group past `rows` repeat the last row (padding rows no consumer reads).
+template <int CPT>
+__global__ __launch_bounds__(256) void k_layernorm_g16(const float* __restrict__ X, int rows, int D,
+                                                       const float* __restrict__ p1, f16* __restrict__ o1,
+                                                       const float* __restrict__ p2, f16* __restrict__ o2,
+                                                       float eps) {
+  __shared__ __attribute__((aligned(16))) f16 tiles[2][16 * 256 * CPT];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = blockIdx.x;
+  const int nch = D >> 2;
+  float4 g1[CPT], b1[CPT], g2[CPT], b2[CPT], v[4][CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int cc = 4 * min(lane + 64 * j, nch - 1);
+    g1[j] = *(const float4*)(p1 + cc);
+    b1[j] = *(const float4*)(p1 + D + cc);
+    if (o2) {
+      g2[j] = *(const float4*)(p2 + cc);
+      b2[j] = *(const float4*)(p2 + D + cc);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = min(16 * grp + 4 * wave + rr, rows - 1);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) v[rr][j] = *(const float4*)(X + (size_t)row * D + 4 * min(lane + 64 * j, nch - 1));
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = 4 * wave + rr;
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+      if (lane + 64 * j < nch) s += (v[rr][j].x + v[rr][j].y) + (v[rr][j].z + v[rr][j].w);
+    s = wave_sum(s);
+    const float mean = s / (float)D;
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      if (lane + 64 * j < nch) {
+        const float d0 = v[rr][j].x - mean, d1 = v[rr][j].y - mean, d2 = v[rr][j].z - mean, d3 = v[rr][j].w - mean;
+        q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+      }
+    }
+    q = wave_sum(q);
+    const float rstd = 1.0f / sqrtf(q / (float)D + eps);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nch) {
+        const float y0 = (v[rr][j].x - mean) * rstd, y1 = (v[rr][j].y - mean) * rstd;
+        const float y2 = (v[rr][j].z - mean) * rstd, y3 = (v[rr][j].w - mean) * rstd;
+        const size_t o = frag_off(r, 4 * c, D);
+        store4(tiles[0], o, y0 * g1[j].x + b1[j].x, y1 * g1[j].y + b1[j].y, y2 * g1[j].z + b1[j].z,
+               y3 * g1[j].w + b1[j].w);
+        if (o2)
+          store4(tiles[1], o, y0 * g2[j].x + b2[j].x, y1 * g2[j].y + b2[j].y, y2 * g2[j].z + b2[j].z,
+                 y3 * g2[j].w + b2[j].w);
+      }
+    }
+  }
+  __syncthreads();
+  const size_t base = (size_t)grp * 16 * D;
+  for (int i = threadIdx.x; i < 2 * D; i += 256) {  // 16 D halves = 2 D chunks of 16 bytes
+    *(half8*)(o1 + base + 8 * i) = *(const half8*)(tiles[0] + 8 * i);
+    if (o2) *(half8*)(o2 + base + 8 * i) = *(const half8*)(tiles[1] + 8 * i);
+  }
+}
+
 hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, const float* p1, void* out1,
                             const float* p2, void* out2, bool out_f32, float eps, const ResidPending* resid,
                             hipStream_t st) {
@@ -377,6 +450,16 @@ hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, cons
     // one wave per row; split-K partials are only produced for at most 1024 rows
     if (rp.nsplit > 0) return hipErrorInvalidValue;
     const int per = (nch + 63) / 64;
+    if (!out_f32 && stride == 1 && off == 0 && D % 32 == 0 && per <= 3) {
+      const dim3 grid((rows + 15) / 16);
+      if (per == 1)
+        hipLaunchKernelGGL(k_layernorm_g16<1>, grid, dim3(256), 0, st, X, rows, D, p1, (f16*)out1, p2, (f16*)out2, eps);
+      else if (per == 2)
+        hipLaunchKernelGGL(k_layernorm_g16<2>, grid, dim3(256), 0, st, X, rows, D, p1, (f16*)out1, p2, (f16*)out2, eps);
+      else
+        hipLaunchKernelGGL(k_layernorm_g16<3>, grid, dim3(256), 0, st, X, rows, D, p1, (f16*)out1, p2, (f16*)out2, eps);
+      return hipGetLastError();
+    }
     if (per <= 1)
       launch_ln_cfg<64, 1, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
     else if (per <= 2)
