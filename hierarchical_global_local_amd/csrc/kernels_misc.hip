@@ -349,6 +349,10 @@ static void launch_ln_small(int rows, float* X, int D, int stride, int off, cons
     launch_ln_cfg<256, CPT, 0>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
   else if (rp.nsplit <= 8)
     launch_ln_cfg<256, CPT, 8>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+  else if (rp.nsplit <= 10)  // (the fused local attention + [out|down] launch of a 12-head model)
+    launch_ln_cfg<256, CPT, 10>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
+  else if (rp.nsplit <= 12)
+    launch_ln_cfg<256, CPT, 12>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
   else
     launch_ln_cfg<256, CPT, 16>(rows, X, D, stride, off, p1, out1, p2, out2, out_f32, eps, rp, st);
 }
