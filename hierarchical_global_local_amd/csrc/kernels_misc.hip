@@ -216,12 +216,13 @@ hipError_t launch_gather_last(float* X, int B, int n, int D, const int* last, hi
 // centred values.  Optionally completes a pending split-K residual update first (see ResidPending).
 template <int TPR>
 __device__ __forceinline__ float row_sum(float v, float* red) {
+  // red[4] is written once per call: a caller reducing twice passes two arrays, so no barrier is
+  // needed before the writes
   v = wave_sum(v);
   if constexpr (TPR == 64) {
     return v;
   } else {
     const int w = (threadIdx.x >> 6) & (TPR / 64 - 1);
-    __syncthreads();
     if ((threadIdx.x & 63) == 0) red[w] = v;
     __syncthreads();
     float t = 0.f;
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(256) void k_layernorm(float* __restrict__ X, int ro
                                                    const float* __restrict__ p1, To* __restrict__ o1,
                                                    const float* __restrict__ p2, To* __restrict__ o2, float eps,
                                                    ResidPending rp) {
-  __shared__ float red[4];
+  __shared__ float red[2][4];
   constexpr int RPB = 256 / TPR;  // rows per block
   const int t = threadIdx.x % TPR;
   const int r = blockIdx.x * RPB + threadIdx.x / TPR;
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(256) void k_layernorm(float* __restrict__ X, int ro
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < CPT; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
-  s = row_sum<TPR>(s, red);
+  s = row_sum<TPR>(s, red[0]);
   const float mean = s / (float)D;
   float q = 0.f;
 #pragma unroll
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(256) void k_layernorm(float* __restrict__ X, int ro
       q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
     }
   }
-  q = row_sum<TPR>(q, red);
+  q = row_sum<TPR>(q, red[1]);
   const float rstd = 1.0f / sqrtf(q / (float)D + eps);
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
                                                   int j, int* __restrict__ n_state, int n_inc, NextStep ns,
                                                   const int* __restrict__ rmap, int from_cur) {
   __shared__ unsigned long long red[4];
-  __shared__ float redf[4];
+  __shared__ float redf[2][4];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int cb = rmap ? rmap[b] : b;  // the row's index in the caches and step state
   if (tid == 0 && n_inc) n_state[cb] += n_inc;
@@ -583,7 +584,7 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
   float s = 0.f;
 #pragma unroll
   for (int q = 0; q < PER; ++q) s += v[q];
-  s = row_sum<256>(s, redf);
+  s = row_sum<256>(s, redf[0]);
   const float mean = s / (float)D;
   float var = 0.f;
 #pragma unroll
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
     const float d = c < D ? v[q] - mean : 0.f;
     var += d * d;
   }
-  var = row_sum<256>(var, redf);
+  var = row_sum<256>(var, redf[1]);
   const float rstd = 1.0f / sqrtf(var / (float)D + ns.eps);
   To* o1 = (To*)ns.ln1;
   To* o2 = (To*)ns.ln2;
