@@ -6,9 +6,11 @@
 //  * k_flash_prefill: causal flash attention over block positions with MFMA (fp16 operands, fp32
 //    softmax); computes S^T = K Q^T so that the probabilities come out of the MFMA already in the
 //    operand layout of O^T = V^T P^T, with no LDS round trip.
-//  * k_attn_decode: memory-bound block-attention decode: one workgroup per (row, head, key split)
-//    streams K then V^T with 16-byte loads, wave-shuffle dot products, online softmax through LDS,
-//    split-KV partials merged by k_attn_combine with log-sum-exp weights.
+//  * k_attn_decode_wave: memory-bound block-attention decode, fp16 multi-head: one wave per (row,
+//    head, key split) streams a step's K and V^T together with 16-byte loads, wave-shuffle dot
+//    products, online softmax in registers; split-KV partials merged by k_attn_combine with
+//    log-sum-exp weights.  k_attn_decode (fp32, groups above 16 heads): one workgroup per unit,
+//    K then V^T, softmax through LDS; k_attn_decode_mfma: grouped-query heads on MFMA.
 //  * k_local_attn_step: the token decoder's local attention for one new slot (decode), one wave
 //    per (row, head) with keys spread over lane groups, everything in registers;
 //    k_local_attn: the same over several new slots (prefill tail), entries held in LDS.
@@ -689,6 +691,215 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   }
 }
 
+// ---------------------------------------------------------------- block-attention decode, one wave per unit (fp16)
+// Multi-head attention (one query head per KV head).  A unit is one (row b, head h, key split s);
+// its cached keys [j0, jc_end) are taken in steps of KS = 8 NG keys (64 at d_h = 64, 32 at
+// d_h = 128).  Lane (group kl, part pp) loads dims 8 pp .. 8 pp + 7 of keys kl*8 + u (u < 8) and
+// value rows 8 pp .. 8 pp + 7 of the same 8 keys (one 16-byte load per row from V^T), so the
+// probabilities a lane weighs its values with are the 8 scores its own lane group has just reduced:
+// a step's keys and values are in flight together, and nothing passes through LDS.  Online softmax
+// in registers across steps; the new entry (slot n: rotated here, appended by split 0 after its
+// output is stored) joins at the end.  WPU = 4: the unit's steps are dealt round-robin to the 4 waves of a workgroup, merged
+// through LDS (few units); WPU = 1: four units per workgroup, one per wave, no barrier.  Compared
+// with the workgroup-per-unit kernel above, a short cache costs one round trip for the length and
+// one for everything else, instead of five separated by barriers.
+template <int DH, int WPU, bool PAGED>
+__global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict__ QKV, const int* __restrict__ n_ptr,
+                                                          int B, int H, const float2* __restrict__ rope,
+                                                          f16* __restrict__ Kc, f16* __restrict__ VTc, int cap,
+                                                          f16* __restrict__ ACT, int ld_act, float* __restrict__ part,
+                                                          int nsplit, int chunk, float scale_log2,
+                                                          const int* __restrict__ ptab, int pld) {
+  static_assert(DH == 64 || DH == 128, "head width");
+  static_assert(WPU == 1 || WPU == 4, "waves per unit");
+  constexpr int LPK = DH / 8, NG = 64 / LPK, KS = 8 * NG, HALF = DH / 2;
+  __shared__ float mrg[WPU][DH + 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int unit = WPU == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
+  if (WPU == 1 && unit >= B * H * nsplit) return;  // idle waves of the last workgroup (no barrier in this mode)
+  const int s = unit % nsplit, bh = unit / nsplit, h = bh % H, b = bh / H;
+  const int w = WPU == 1 ? 0 : wave;  // this wave takes steps w, w + WPU, ...
+  const int kl = lane / LPK, pp = lane % LPK;
+  // entries already cached in this row; the new one goes to slot n (the host keeps every row below
+  // the capacity; the clamp only keeps a misused row inside its own cache)
+  const int n = min(n_ptr[b], cap - 1);
+  const int j0 = s * chunk, j1 = min(n + 1, j0 + chunk), jc_end = min(j1, n);
+  const bool owns_new = n >= j0 && n < j1;
+  const int nsteps = jc_end > j0 ? (jc_end - j0 + KS - 1) / KS : 0;
+  // 8-key group holding the last cached key: value loads of groups past the cached keys are
+  // clamped into it (their weights are zero; every slot below the capacity is finite).  Loads of a
+  // step past the unit's keys (the first step of a unit or wave without any) stay inside the
+  // capacity, on page 0 for a paged cache, and their values are never used.
+  const int jlast = min(max(j0, (jc_end - 1) & ~7), cap - 8);
+  // paged: lane i holds the page of keys j0 + 64 i .. (chunk <= 4096 keys: at most 64 pages); a
+  // step's keys lie in one page
+  int pg = 0;
+  if (PAGED && j0 / 64 + lane < pld && lane * 64 < chunk) pg = ptab[(size_t)b * pld + j0 / 64 + lane];
+  const int pg_new = PAGED && s == 0 ? ptab[(size_t)b * pld + (n >> 6)] : 0;  // page of the appended entry
+
+  // ---- query, new key and value of this head: lane pp holds dims 8 pp .. 8 pp + 7 and their
+  // rotary partners (dims +- d_h / 2)
+  const f16* row = QKV + (size_t)b * 3 * H * DH;
+  const int dp = (8 * pp + HALF) % DH, c0 = (8 * pp) % HALF;
+  const half8 q_own = *(const half8*)(row + h * DH + 8 * pp), q_par = *(const half8*)(row + h * DH + dp);
+  const half8 k_own = *(const half8*)(row + (H + h) * DH + 8 * pp), k_par = *(const half8*)(row + (H + h) * DH + dp);
+  const half8 v_new = *(const half8*)(row + (2 * H + h) * DH + 8 * pp);
+  float4 cs4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cs4[i] = *(const float4*)(rope + (size_t)n * HALF + c0 + 2 * i);
+
+  // ---- the first step's keys and values, issued before the query is rotated
+  auto load_step = [&](int t, half8 (&kr)[8], half8 (&vr)[8]) {
+    const int jb = j0 + t * KS;
+    const int page = PAGED && t < nsteps ? __builtin_amdgcn_readlane(pg, (jb - j0) >> 6) : 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = max(0, min(jb + kl * 8 + u, jc_end - 1));
+      const f16* p = PAGED ? Kc + (((size_t)page * H + h) * 64 + (j & 63)) * DH : Kc + ((size_t)bh * cap + j) * DH;
+      kr[u] = __builtin_nontemporal_load((const half8*)(p + 8 * pp));
+    }
+    const int jg = min(jb + kl * 8, jlast);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const f16* p = PAGED ? VTc + (((size_t)page * H + h) * DH + 8 * pp + r) * 64 + (jg & 63)
+                           : VTc + ((size_t)bh * DH + 8 * pp + r) * cap + jg;
+      vr[r] = __builtin_nontemporal_load((const half8*)p);
+    }
+  };
+  half8 kr[8], vr[8];
+  load_step(w, kr, vr);
+
+  const bool lo = 8 * pp < HALF;
+  float qr[8], kn[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float c = e & 1 ? cs4[e >> 1].z : cs4[e >> 1].x, sn = e & 1 ? cs4[e >> 1].w : cs4[e >> 1].y;
+    const float qa = (float)q_own[e], qb = (float)q_par[e], ka = (float)k_own[e], kb = (float)k_par[e];
+    qr[e] = lo ? qa * c - qb * sn : qa * c + qb * sn;
+    kn[e] = (float)to_f16(lo ? ka * c - kb * sn : ka * c + kb * sn);
+  }
+  float sn_new = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sn_new = fmaf(qr[e], kn[e], sn_new);
+#pragma unroll
+  for (int o = 1; o < LPK; o <<= 1) sn_new += __shfl_xor(sn_new, o, 64);
+  sn_new *= scale_log2;
+
+  // ---- cached keys, online softmax: m (running maximum, log2 units), l (this lane group's sum of
+  // weights), acc[r] (value row 8 pp + r weighted by this lane group's keys)
+  float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+  // (the next step's loads follow the exit test, so that they reuse the registers of this one)
+  for (int t = w; t < nsteps;) {
+    const int jb = j0 + t * KS;
+    float sv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qr[e], (float)kr[u][e], d);
+#pragma unroll
+      for (int o = 1; o < LPK; o <<= 1) d += __shfl_xor(d, o, 64);
+      sv[u] = jb + kl * 8 + u < jc_end ? d * scale_log2 : -INFINITY;
+    }
+    float cm = sv[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) cm = fmaxf(cm, sv[u]);
+#pragma unroll
+    for (int o = LPK; o < 64; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
+    const float mn = fmaxf(m, cm);  // finite: every step holds a cached key
+    const float al = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    l *= al;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] *= al;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float p = __builtin_amdgcn_exp2f(sv[u] - mn);
+      l += p;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r] = fmaf(p, (float)vr[r][u], acc[r]);
+    }
+    // the weighting is finished here, before the next loads (left to itself the compiler sinks it
+    // below them, which needs a second set of value registers)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(acc[r]));
+    asm volatile("" : "+v"(l));
+    t += WPU;
+    if (t >= nsteps) break;
+    load_step(t, kr, vr);
+  }
+  // sum over the lane groups (the lanes of one group hold the same l)
+#pragma unroll
+  for (int o = LPK; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o, 64);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] += __shfl_xor(acc[r], o, 64);
+  }
+  if constexpr (WPU > 1) {
+    if (kl == 0) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) mrg[wave][2 + 8 * pp + r] = acc[r];
+      if (pp == 0) mrg[wave][0] = m, mrg[wave][1] = l;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float M = mrg[0][0];
+#pragma unroll
+    for (int i = 1; i < WPU; ++i) M = fmaxf(M, mrg[i][0]);
+    l = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < WPU; ++i) {
+      const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrg[i][0] - M);
+      l = fmaf(f, mrg[i][1], l);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r] = fmaf(f, mrg[i][2 + 8 * pp + r], acc[r]);
+    }
+    m = M;
+  }
+  if (owns_new) {
+    const float mn = fmaxf(m, sn_new);
+    const float al = __builtin_amdgcn_exp2f(m - mn), pn = __builtin_amdgcn_exp2f(sn_new - mn);
+    l = fmaf(l, al, pn);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = fmaf(acc[r], al, pn * (float)v_new[r]);
+    m = mn;
+  }
+  if (kl != 0) return;
+  if (nsplit == 1) {
+    half8 o;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) o[r] = to_f16(acc[r] / l);
+    *(half8*)(ACT + frag_off(b, h * DH + 8 * pp, ld_act)) = o;
+  } else {
+    float* q = part + ((size_t)bh * nsplit + s) * (DH + 2);
+#pragma unroll
+    for (int r = 0; r < 8; r += 2) *(float2*)(q + 2 + 8 * pp + r) = make_float2(acc[r], acc[r + 1]);
+    if (pp == 0) *(float2*)q = make_float2(m, l);
+  }
+  // split 0 appends the new entry (wave 0 of the unit, lane group 0).  Last: stores count in the
+  // same in-order counter as loads, so an earlier append would hold up every later wait for data
+  // until its scattered value-column writes are acknowledged.
+  if (s == 0 && w == 0) {
+    size_t koff = ((size_t)bh * cap + n) * DH, voff = (size_t)bh * DH * cap + n, vstr = cap;
+    if (PAGED) {
+      const size_t pn = (size_t)pg_new * H + h;
+      koff = (pn * 64 + (n & 63)) * DH;
+      voff = pn * DH * 64 + (n & 63);
+      vstr = 64;
+    }
+    half8 kh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kh[e] = to_f16(kn[e]);
+    *(half8*)(Kc + koff + 8 * pp) = kh;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) VTc[voff + (size_t)(8 * pp + r) * vstr] = v_new[r];
+  }
+}
+
 // ---------------------------------------------------------------- block-attention decode, MFMA (fp16)
 // A unit is one (row b, KV head hk, key split s) with all G = H / Hkv query heads of that KV head
 // (G <= 16: grouped-query heads share the unit, so their keys and values stream once).  WPU waves
@@ -1044,15 +1255,57 @@ static hipError_t launch_decode_mfma(const void* QKV, int B, const int* n_ptr, i
   return hipGetLastError();
 }
 
+// fp16 multi-head attention: one wave per (row, head, split); four waves share a unit while units
+// are few
+template <int DH>
+static hipError_t launch_decode_wave(const void* QKV, int B, const int* n_ptr, int H, const float2* rope, void* Kc,
+                                     void* Vc, int cap, void* ACT, int ld_act, float* part, size_t part_bytes,
+                                     int nsplit, hipStream_t st, const int* ptab, int pld) {
+  int chunk = (cap + nsplit - 1) / nsplit;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk > 4096) return hipErrorInvalidValue;  // a paged split's pages are held one per lane
+  if (nsplit > 1 && (size_t)B * H * nsplit * (DH + 2) * sizeof(float) > part_bytes) return hipErrorInvalidValue;
+  const float sl2 = kLog2e / sqrtf((float)DH);
+  const long units = (long)B * H * nsplit;
+#define BT_DW(WPUV, GRID)                                                                                        \
+  {                                                                                                              \
+    if (ptab)                                                                                                    \
+      hipLaunchKernelGGL((k_attn_decode_wave<DH, WPUV, true>), dim3(GRID), dim3(256), 0, st, (const f16*)QKV,    \
+                         n_ptr, B, H, rope, (f16*)Kc, (f16*)Vc, cap, (f16*)ACT, ld_act, part, nsplit, chunk, sl2, \
+                         ptab, pld);                                                                             \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_attn_decode_wave<DH, WPUV, false>), dim3(GRID), dim3(256), 0, st, (const f16*)QKV,   \
+                         n_ptr, B, H, rope, (f16*)Kc, (f16*)Vc, cap, (f16*)ACT, ld_act, part, nsplit, chunk, sl2, \
+                         ptab, pld);                                                                             \
+  }
+  if (units < 2048) BT_DW(4, units) else BT_DW(1, (units + 3) / 4)
+#undef BT_DW
+  if (nsplit > 1)
+    hipLaunchKernelGGL((k_attn_combine<f16, DH>), dim3(H, B), dim3(DH), 0, st, (const float*)part, H, nsplit,
+                       (f16*)ACT, ld_act);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_attn_decode(bool f32, const void* QKV, int B, const int* n_ptr, int H, int Hkv, int dh,
                                     const float2* rope, void* Kc, void* Vc, int cap, void* ACT, int ld_act, float* part,
                                     size_t part_bytes, int nsplit, hipStream_t st, const int* ptab, int pld) {
   if (B <= 0) return hipSuccess;
   if (Hkv < 1 || H % Hkv) return hipErrorInvalidValue;
+  // the kernels read whole 8-key value chunks and clamp loads into [0, cap)
+  if (cap < 64 || cap % 64) return hipErrorInvalidValue;
+  // fp16 multi-head attention: one wave per (row, head, split), VALU dot products (with one query
+  // head per KV head an MFMA column would be 1/16 used; the MFMA kernel measured 95 us at the
+  // decode-heavy shape and 543 entries against 90 us for the workgroup kernel, which this one
+  // replaces: 75 us there, and 17 us instead of 22 us at 32-64 entries)
+  if (!f32 && H == Hkv && (dh == 64 || dh == 128)) {
+    if (dh == 64)
+      return launch_decode_wave<64>(QKV, B, n_ptr, H, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, nsplit, st,
+                                    ptab, pld);
+    return launch_decode_wave<128>(QKV, B, n_ptr, H, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, nsplit, st,
+                                   ptab, pld);
+  }
   // grouped-query heads (2..16 per KV head): one MFMA wave reads a KV head's keys and values once
-  // for all of them.  Multi-head attention stays on the streaming kernel below (decode-heavy shape
-  // at 543 entries: 90 us; the MFMA kernel 95 us with its LDS staging, 113 us loading fragments
-  // straight from memory, where an instruction covers half cache lines)
+  // for all of them
   if (!f32 && H / Hkv > 1 && H / Hkv <= 16) {
     if (dh == 64)
       return launch_decode_mfma<64>(QKV, B, n_ptr, H, Hkv, rope, Kc, Vc, cap, ACT, ld_act, part, part_bytes, nsplit,

@@ -200,6 +200,27 @@ def test_deep_split_kv_long_context(kw):
         check_ids_against(ref, ids[r], BF16_TOL)
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=2)])
+def test_block_attention_one_wave_per_unit(kw):
+    """1024 rows x 2 heads = 2048 (row, head) units: the multi-head block attention runs one wave
+    per unit (with fewer units four waves share one); head widths 64 and 128.  Rows 0, 511 and 1023
+    are teacher-forced through the oracle at every step."""
+    cfg = SMALL_BF16.with_(**kw)
+    B, T, G = 1024, 37, 12
+    log(f"one-wave block attention case {kw} B={B} T={T} G={G}")
+    W = wl.make_weights(cfg, seed=16, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, batch=B, T=T, seed=16)
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G))
+    model.close()
+    del model
+    for r in (0, 511, B - 1):
+        ref = teacher_forced_logits(cfg, W, prompt[r], ids[r], range(G))
+        err = float(np.abs(np.stack([lg[g][r] for g in range(G)]) - ref).max())
+        log(f"  row {r}: max-abs logit error {err:.3e}")
+        assert err <= BF16_TOL
+        check_ids_against(ref, ids[r], BF16_TOL)
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=4, n_kv_heads=2)])
 def test_kv_caches_hold_rotated_keys_and_values(kw):
     """Block-KV (keys [slot][d], values transposed) and local-KV contents equal the oracle's caches
