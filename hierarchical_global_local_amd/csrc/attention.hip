@@ -1,8 +1,8 @@
 // Attention kernels of libbt.
 //
 //  * k_rope_scatter: rotary embedding of prompt keys and scatter of K / V into the block-KV cache
-//    (keys [slot][dh]; values transposed [dh][slot] so that the prefill P*V product and the decode
-//    value pass read 8 consecutive keys per 16-byte load).
+//    (keys [slot][dh]; values in groups of 8 slots, each group transposed [dh][8], so that the
+//    prefill P*V product and the decode value passes read 8 consecutive keys per 16-byte load).
 //  * k_flash_prefill: causal flash attention over block positions with MFMA (fp16 operands, fp32
 //    softmax); computes S^T = K Q^T so that the probabilities come out of the MFMA already in the
 //    operand layout of O^T = V^T P^T, with no LDS round trip.
@@ -54,9 +54,12 @@ template <typename T>
 __device__ __forceinline__ T round_t(float v) { return from_f32<T>(v); }
 
 // ---------------------------------------------------------------- block-KV addressing
-// Entry j of cache row r, KV head hk: flat caches hold keys [row][head][cap][dh] and values
-// transposed [row][head][dh][cap]; paged caches (ptab set) hold pages of 64 entries, keys
-// [page][head][64][dh] and values [page][head][dh][64], entry j of row r in page ptab[r*pld + j/64].
+// Entry j of cache row r, KV head hk: flat caches hold keys [row][head][cap][dh] and values in
+// groups of 8 entries, each group transposed: [row][head][cap / 8][dh][8]; paged caches (ptab set)
+// hold pages of 64 entries, keys [page][head][64][dh] and values [page][head][8][dh][8], entry j of
+// row r in page ptab[r*pld + j/64].  A 16-byte load (fp16) takes 8 consecutive entries of one value
+// dimension -- the operand shape of the P*V products -- while appending one entry touches the
+// group's dh * 16 contiguous bytes instead of one cache line per dimension.
 // nlim (paged prefill): entries at or past nlim[r] are not written or read (their pages may not
 // exist).
 struct KvPages {
@@ -69,8 +72,9 @@ __device__ __forceinline__ size_t kv_key(const KvPages& pg, int r, int hk, int j
                  : (((size_t)r * Hkv + hk) * cap + j) * dh;
 }
 __device__ __forceinline__ size_t kv_val(const KvPages& pg, int r, int hk, int d, int j, int Hkv, int cap, int dh) {
-  return pg.ptab ? (((size_t)pg.ptab[(size_t)r * pg.pld + (j >> 6)] * Hkv + hk) * dh + d) * 64 + (j & 63)
-                 : (((size_t)r * Hkv + hk) * dh + d) * cap + j;
+  return pg.ptab ? ((((size_t)pg.ptab[(size_t)r * pg.pld + (j >> 6)] * Hkv + hk) * 8 + ((j & 63) >> 3)) * dh + d) * 8 +
+                       (j & 7)
+                 : ((((size_t)r * Hkv + hk) * (cap >> 3) + (j >> 3)) * dh + d) * 8 + (j & 7);
 }
 
 // ---------------------------------------------------------------- rotary + scatter (prefill)
@@ -116,10 +120,11 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const T* __restrict__ QKV,
   }
 }
 
-// fp16 block cache (values transposed), slot offset s0 % 8 == 0: the same with 16-byte accesses.
+// fp16 block cache, slot offset s0 % 8 == 0: the same with 16-byte accesses.
 // Keys: a thread takes 8 dimensions and their rotary partners (8 further by DH / 2) of one slot,
 // with the 8 (cos, sin) pairs as 4 16-byte loads.  Values: the 64 x DH tile goes through LDS and
-// leaves as 16-byte runs of 8 slots per dimension (element stores for a ragged last run).
+// leaves as 16-byte runs of 8 slots per dimension, one value group at a time (element stores for a
+// ragged last run).
 template <int DH>
 __global__ __launch_bounds__(256) void k_rope_scatter_v(const f16* __restrict__ QKV, int m, int s0, int H, int Hkv,
                                                         const float2* __restrict__ rope, f16* __restrict__ Kc,
@@ -162,8 +167,8 @@ __global__ __launch_bounds__(256) void k_rope_scatter_v(const f16* __restrict__ 
   }
   __syncthreads();
   const int runs = (cnt + 7) / 8;
-  for (int e = tid; e < DH * runs; e += 256) {
-    const int d = e / runs, q = e % runs, n8 = min(8, cnt - 8 * q);
+  for (int e = tid; e < DH * runs; e += 256) {  // consecutive threads: consecutive dimensions of a group
+    const int d = e % DH, q = e / DH, n8 = min(8, cnt - 8 * q);
     f16* vd = Vc + kv_val(pg, cb, hk, d, s0 + i0 + 8 * q, Hkv, cap, DH);
     if (n8 == 8) {
       half8 w;
@@ -257,8 +262,9 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
 
   // cooperative tile loads (keys beyond the cache capacity never occur: cap is a multiple of 64)
   half8 rk[CK], rv[CV];
-  // a 64-key tile is one page of a paged cache: keys [64][DH] and values [DH][64] (row stride 64)
-  const int vstride = pg.ptab ? 64 : cap;
+  // a 64-key tile is 8 value groups ([8][DH][8], contiguous; one page of a paged cache): item
+  // (group cc, dimension r) is 16 bytes at (cc * DH + r) * 8, consecutive lanes taking consecutive
+  // dimensions
   auto gload = [&](int kb) {
     const f16* __restrict__ Kt = Kc + kv_key(pg, cb, hk, kb, Hkv, cap, DH);
     const f16* __restrict__ Vt = VTc + kv_val(pg, cb, hk, 0, kb, Hkv, cap, DH);
@@ -269,8 +275,8 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
     }
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
-      const int c = tid + i * 256, r = c / 8, cc = c % 8;
-      rv[i] = *(const half8*)(Vt + (size_t)r * vstride + cc * 8);
+      const int c = tid + i * 256, r = c % DH, cc = c / DH;
+      rv[i] = *(const half8*)(Vt + ((size_t)cc * DH + r) * 8);
     }
   };
   auto sstore = [&](int buf) {
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
     }
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
-      const int c = tid + i * 256, r = c / 8, cc = c % 8;
+      const int c = tid + i * 256, r = c % DH, cc = c / DH;
       *(half8*)&Vs[buf][r * VLD + cc * 8] = rv[i];
     }
   };
@@ -496,24 +502,26 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
   const bool owns_new = (n >= j0 && n < j1);
   const bool appends = s == 0 && run == 0;
   // paged: key j at Kc[((page * Hkv + hk) * 64 + j % 64) * DH], value (d, j) at
-  // VTc[((page * Hkv + hk) * DH + d) * 64 + j % 64], page = pgs[(j - j0) / 64] (j0 % 64 == 0)
+  // VTc[(((page * Hkv + hk) * 8 + j % 64 / 8) * DH + d) * 8 + j % 8], page = pgs[(j - j0) / 64]
+  // (j0 % 64 == 0)
   if (PAGED)
     for (int k = threadIdx.x; k < chunk / 64 && j0 / 64 + k < pld; k += 256) pgs[k] = ptab[(size_t)b * pld + j0 / 64 + k];
   auto kaddr = [&](int j) -> const T* {
     if (!PAGED) return K + (size_t)j * DH;
     return Kc + (((size_t)pgs[(j - j0) >> 6] * Hkv + hk) * 64 + (j & 63)) * DH;
   };
-  auto vaddr = [&](int row, int j) -> const T* {
-    if (!PAGED) return VT + (size_t)row * cap + j;
-    return VTc + (((size_t)pgs[(j - j0) >> 6] * Hkv + hk) * DH + row) * 64 + (j & 63);
+  auto vaddr = [&](int row, int j) -> const T* {  // 8 entries from j (j % 8 == 0)
+    if (!PAGED) return VT + ((size_t)(j >> 3) * DH + row) * 8;
+    return VTc + ((((size_t)pgs[(j - j0) >> 6] * Hkv + hk) * 8 + ((j & 63) >> 3)) * DH + row) * 8;
   };
-  // the appended entry's place (its page comes from the table directly: LDS is not ready yet)
-  size_t kn_off = (size_t)n * DH, vn_off = n, vn_stride = cap;
+  // the appended entry's place (its page comes from the table directly: LDS is not ready yet);
+  // value dimension d at Vn[d * 8]
+  size_t kn_off = (size_t)n * DH, vn_off = (size_t)(n >> 3) * DH * 8 + (n & 7);
+  constexpr size_t vn_stride = 8;
   if (PAGED) {
     const size_t pn = (size_t)ptab[(size_t)b * pld + (n >> 6)] * Hkv + hk;
     kn_off = (pn * 64 + (n & 63)) * DH;
-    vn_off = pn * DH * 64 + (n & 63);
-    vn_stride = 64;
+    vn_off = ((pn * 8 + ((n & 63) >> 3)) * DH) * 8 + (n & 7);
   }
   T* __restrict__ Kn = PAGED ? Kc + kn_off : K + kn_off;
   T* __restrict__ Vn = PAGED ? VTc + vn_off : VT + vn_off;
@@ -695,8 +703,9 @@ __global__ __launch_bounds__(256) void k_attn_decode(const T* __restrict__ QKV, 
 // Multi-head attention (one query head per KV head).  A unit is one (row b, head h, key split s);
 // its cached keys [j0, jc_end) are taken in steps of KS = 8 NG keys (64 at d_h = 64, 32 at
 // d_h = 128).  Lane (group kl, part pp) loads dims 8 pp .. 8 pp + 7 of keys kl*8 + u (u < 8) and
-// value rows 8 pp .. 8 pp + 7 of the same 8 keys (one 16-byte load per row from V^T), so the
-// probabilities a lane weighs its values with are the 8 scores its own lane group has just reduced:
+// value rows r * LPK + pp (r < 8) of the same 8 keys (one 16-byte load per row from their value
+// group), so the probabilities a lane weighs its values with are the 8 scores its own lane group has
+// just reduced:
 // a step's keys and values are in flight together, and nothing passes through LDS.  Online softmax
 // in registers across steps; the new entry (slot n: rotated here, appended by split 0 after its
 // output is stored) joins at the end.  WPU = 4: the unit's steps are dealt round-robin to the 4 waves of a workgroup, merged
@@ -713,7 +722,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
   static_assert(DH == 64 || DH == 128, "head width");
   static_assert(WPU == 1 || WPU == 4, "waves per unit");
   constexpr int LPK = DH / 8, NG = 64 / LPK, KS = 8 * NG, HALF = DH / 2;
-  __shared__ float mrg[WPU][DH + 2];
+  __shared__ float mrg[4][DH + 2];  // per wave: (m, l, value rows)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int unit = WPU == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
   if (WPU == 1 && unit >= B * H * nsplit) return;  // idle waves of the last workgroup (no barrier in this mode)
@@ -758,13 +767,13 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
       const f16* p = PAGED ? Kc + (((size_t)page * H + h) * 64 + (j & 63)) * DH : Kc + ((size_t)bh * cap + j) * DH;
       kr[u] = __builtin_nontemporal_load((const half8*)(p + 8 * pp));
     }
+    // value rows r * LPK + pp of the group at jg: the LPK lanes of a lane group read one whole
+    // 16 * LPK-byte run of the group per instruction
     const int jg = min(jb + kl * 8, jlast);
+    const f16* vg = PAGED ? VTc + ((((size_t)page * H + h) * 8 + ((jg & 63) >> 3)) * DH) * 8
+                          : VTc + (((size_t)bh * (cap >> 3) + (jg >> 3)) * DH) * 8;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const f16* p = PAGED ? VTc + (((size_t)page * H + h) * DH + 8 * pp + r) * 64 + (jg & 63)
-                           : VTc + ((size_t)bh * DH + 8 * pp + r) * cap + jg;
-      vr[r] = __builtin_nontemporal_load((const half8*)p);
-    }
+    for (int r = 0; r < 8; ++r) vr[r] = __builtin_nontemporal_load((const half8*)(vg + (size_t)(r * LPK + pp) * 8));
   };
   half8 kr[8], vr[8];
   load_step(w, kr, vr);
@@ -837,12 +846,16 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[r] += __shfl_xor(acc[r], o, 64);
   }
-  if constexpr (WPU > 1) {
-    if (kl == 0) {
+  // lane pp of group 0 holds value rows r * LPK + pp; through LDS it takes rows 8 pp .. 8 pp + 7
+  if (kl == 0) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) mrg[wave][2 + 8 * pp + r] = acc[r];
-      if (pp == 0) mrg[wave][0] = m, mrg[wave][1] = l;
-    }
+    for (int r = 0; r < 8; ++r) mrg[wave][2 + r * LPK + pp] = acc[r];
+    if (pp == 0) mrg[wave][0] = m, mrg[wave][1] = l;
+  }
+  if constexpr (WPU == 1) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = mrg[wave][2 + 8 * pp + r];  // same wave: LDS keeps its order
+  } else {
     __syncthreads();
     if (wave != 0) return;
     float M = mrg[0][0];
@@ -884,19 +897,19 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
   // same in-order counter as loads, so an earlier append would hold up every later wait for data
   // until its scattered value-column writes are acknowledged.
   if (s == 0 && w == 0) {
-    size_t koff = ((size_t)bh * cap + n) * DH, voff = (size_t)bh * DH * cap + n, vstr = cap;
+    // value dimension d of the entry at voff + d * 8 (within its group of 8 entries)
+    size_t koff = ((size_t)bh * cap + n) * DH, voff = ((size_t)bh * (cap >> 3) + (n >> 3)) * DH * 8 + (n & 7);
     if (PAGED) {
       const size_t pn = (size_t)pg_new * H + h;
       koff = (pn * 64 + (n & 63)) * DH;
-      voff = pn * DH * 64 + (n & 63);
-      vstr = 64;
+      voff = ((pn * 8 + ((n & 63) >> 3)) * DH) * 8 + (n & 7);
     }
     half8 kh;
 #pragma unroll
     for (int e = 0; e < 8; ++e) kh[e] = to_f16(kn[e]);
     *(half8*)(Kc + koff + 8 * pp) = kh;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) VTc[voff + (size_t)(8 * pp + r) * vstr] = v_new[r];
+    for (int r = 0; r < 8; ++r) VTc[voff + (size_t)(8 * pp + r) * 8] = v_new[r];
   }
 }
 
@@ -988,12 +1001,15 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
     }
     if (s == 0 && c == 0 && (WPU == 1 || wave == 0)) {
       // lanes 0, 16, 32, 48 hold dims 8g.. of every 32-dim slice of k and rows 4g.. of each v tile
-      size_t kofs, vofs, vstr;
+      // value dimension d of the entry at vofs + d * 8 (its group of 8 entries, transposed)
+      size_t kofs, vofs;
+      constexpr size_t vstr = 8;
       if (PAGED) {
         const size_t pg = (size_t)ptab[(size_t)b * pld + (n >> 6)] * Hkv + hk;
-        kofs = (pg * 64 + (n & 63)) * DH, vofs = pg * DH * 64 + (n & 63), vstr = 64;
+        kofs = (pg * 64 + (n & 63)) * DH, vofs = ((pg * 8 + ((n & 63) >> 3)) * DH) * 8 + (n & 7);
       } else {
-        kofs = (((size_t)b * Hkv + hk) * cap + n) * DH, vofs = ((size_t)b * Hkv + hk) * DH * cap + n, vstr = cap;
+        kofs = (((size_t)b * Hkv + hk) * cap + n) * DH;
+        vofs = (((size_t)b * Hkv + hk) * (cap >> 3) + (n >> 3)) * DH * 8 + (n & 7);
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -1015,13 +1031,14 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
   float m = -INFINITY, l = 0.f;
   const int w0 = WPU == 1 ? 0 : wave;
   for (int t = j0 + w0 * TK; t < jc_end; t += WPU * TK) {
+    // vb: the step's first value group ([TK / 8][DH][8], contiguous; t % 8 == 0)
     const f16 *kb, *vb;
-    int vstr;
     if (PAGED) {
       const size_t pg = (size_t)ptab[(size_t)b * pld + (t >> 6)] * Hkv + hk;
-      kb = Kc + (pg * 64 + (t & 63)) * DH, vb = VTc + pg * DH * 64 + (t & 63), vstr = 64;
+      kb = Kc + (pg * 64 + (t & 63)) * DH, vb = VTc + ((pg * 8 + ((t & 63) >> 3)) * DH) * 8;
     } else {
-      kb = Kc + (((size_t)b * Hkv + hk) * cap + t) * DH, vb = VTc + ((size_t)b * Hkv + hk) * DH * cap + t, vstr = cap;
+      kb = Kc + (((size_t)b * Hkv + hk) * cap + t) * DH;
+      vb = VTc + (((size_t)b * Hkv + hk) * (cap >> 3) + (t >> 3)) * DH * 8;
     }
     const int lim = jc_end - t;  // keys of this step that are cached: [0, lim)
     // stage the step: key rows (clamped to cached keys, masked below) and value rows, 8 lanes per
@@ -1034,14 +1051,16 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
         const int kr = min(i * RK + lane / LPR, lim - 1);
         rk[i] = __builtin_nontemporal_load((const half8*)(kb + (size_t)kr * DH + 8 * (lane % LPR)));
       }
-      constexpr int LPV = TK / 8, RV = 64 / LPV;  // lanes per value row segment, rows per instruction
+      // value item (row, group q): 16 bytes at vb + (q * DH + row) * 8; an instruction takes RV
+      // consecutive rows of LPV groups
+      constexpr int LPV = TK / 8, RV = 64 / LPV;  // groups per step, rows per instruction
 #pragma unroll
       for (int i = 0; i < DH / RV; ++i)
-        rv[i] = __builtin_nontemporal_load((const half8*)(vb + (size_t)(i * RV + lane / LPV) * vstr + 8 * (lane % LPV)));
+        rv[i] = __builtin_nontemporal_load((const half8*)(vb + ((size_t)(lane / RV) * DH + i * RV + lane % RV) * 8));
 #pragma unroll
       for (int i = 0; i < TK / RK; ++i) *(half8*)&Ks[(i * RK + lane / LPR) * KLD + 8 * (lane % LPR)] = rk[i];
 #pragma unroll
-      for (int i = 0; i < DH / RV; ++i) *(half8*)&Vs[(i * RV + lane / LPV) * VLD + 8 * (lane % LPV)] = rv[i];
+      for (int i = 0; i < DH / RV; ++i) *(half8*)&Vs[(i * RV + lane % RV) * VLD + 8 * (lane / RV)] = rv[i];
     }
     __builtin_amdgcn_wave_barrier();
     // K rows: tile nt, row c holds key 32 (nt / 2) + 8 (c / 4) + 4 (nt % 2) + c % 4

@@ -204,11 +204,12 @@ hipError_t launch_attn_out_decode(const void* ACT, const void* W, int M, int N, 
 // QKV row is [q: H dh | k: Hkv dh | v: Hkv dh] and query head h reads KV head h / (H / Hkv).
 // Caches are [row][KV head][...].
 //
-// rotary + scatter of K (row-major [slot][dh]) and V (block cache: transposed [dh][slot]) for rows
-// (b, i) of QKV [B*m][QW] into cache slots s0 + i, at rotary positions s0 + i.
+// rotary + scatter of K (row-major [slot][dh]) and V (block cache, v_transposed: groups of 8 slots,
+// each transposed, [slot / 8][dh][8]; local cache: row-major) for rows (b, i) of QKV [B*m][QW] into
+// cache slots s0 + i, at rotary positions s0 + i.
 // (rmap: optional cache row of each activation row b, for a prefill into rows of a running batch;
 // the same argument of the prefill and local attention launchers.  ptab / pld: page table of a
-// paged block KV (pages of 64 entries, [page][Hkv][64][dh] keys, [page][Hkv][dh][64] values),
+// paged block KV (pages of 64 entries, [page][Hkv][64][dh] keys, [page][Hkv][8][dh][8] values),
 // nlim: with it, entries past each cache row's length nlim[row] are neither written nor read.)
 hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, int H, int Hkv, int dh,
                                const float2* rope, void* Kc, void* Vc, int cap, bool v_transposed,

@@ -220,9 +220,9 @@ int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_k
  * which = 0: block-KV cache [N_blk][2 (K, V)][max_batch][H_kv][cap * d_head] with
  *            cap = ceil(max_tokens / L_B) rounded up to a multiple of 64; per (layer,
  *            row, KV head) the keys are [cap][d_head] (after the rotary embedding) and the
- *            values are transposed, [d_head][cap];
+ *            values are in groups of 8 entries, each group transposed: [cap / 8][d_head][8];
  *            with kv_pages > 0 the cache is a pool [N_blk][2][kv_pages][H_kv][64 * d_head]
- *            (keys [64][d_head], values [d_head][64] per page and head; capacity = 64), and
+ *            (keys [64][d_head], values [8][d_head][8] per page and head; capacity = 64), and
  *            entry j of row b is in page bt_page_table(h)[b][j / 64] at j % 64;
  * which = 1: local-KV cache [N_tok][2][max_batch][H_kv][S + L_B][d_head] (keys after
  *            the rotary embedding, values not transposed).

@@ -223,8 +223,8 @@ def test_block_attention_one_wave_per_unit(kw):
 
 @pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=4, n_kv_heads=2)])
 def test_kv_caches_hold_rotated_keys_and_values(kw):
-    """Block-KV (keys [slot][d], values transposed) and local-KV contents equal the oracle's caches
-    (H_kv heads per row under grouped-query attention)."""
+    """Block-KV (keys [slot][d], values in transposed groups of 8 slots [slot / 8][d][8]) and
+    local-KV contents equal the oracle's caches (H_kv heads per row under grouped-query attention)."""
     torch = require_gpu()
     cfg = SMALL_BF16.with_(**kw)
     W = wl.make_weights(cfg, seed=3, ln_jitter=True)
@@ -240,7 +240,7 @@ def test_kv_caches_hold_rotated_keys_and_values(kw):
         k_ref = st.block_caches[l].k.transpose(0, 2, 1, 3)            # [B, H, n, dh]
         v_ref = st.block_caches[l].v.transpose(0, 2, 3, 1)            # [B, H, dh, n]
         k_gpu = blk[l, 0, :, :, :n, :]
-        v_gpu = blk[l, 1].reshape(B, H, dh, cap)[:, :, :, :n]
+        v_gpu = blk[l, 1].reshape(B, H, cap // 8, dh, 8).transpose(0, 1, 3, 2, 4).reshape(B, H, dh, cap)[:, :, :, :n]
         assert np.abs(k_gpu - k_ref).max() <= 2e-2 * max(1.0, np.abs(k_ref).max())
         assert np.abs(v_gpu - v_ref).max() <= 2e-2 * max(1.0, np.abs(v_ref).max())
     loc, lcap = model.cache_view(1)
