@@ -206,6 +206,24 @@ def test_paged_block_kv_is_bit_identical_to_flat(name):
     log(f"paged {name}: block lengths {n.tolist()}, pages {held}")
 
 
+def test_paged_block_kv_one_wave_per_unit_is_bit_identical_to_flat():
+    """1024 ragged rows x 2 heads (2048 units): the block attention's one-wave-per-unit mode reads and
+    appends through the page table and gives exactly the flat cache's ids and logits."""
+    cfg = SMALL_BF16.with_(block_len=1, prefix_len=2)
+    W = wl.make_weights(cfg, seed=38, ln_jitter=True)
+    B, T, steps = 1024, 70, 60
+    prompt, lengths = _prompts(cfg, B, T, 38)
+    flat = _paged_run(cfg, W, 0, B, T, steps, prompt, lengths, (-1,))
+    paged = _paged_run(cfg, W, 3 * B, B, T, steps, prompt, lengths, (-1,))   # capacity: 3 pages a row
+    for a, b in zip(flat[0], paged[0]):
+        np.testing.assert_array_equal(a, b)
+    for a, b in zip(flat[1], paged[1]):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(paged[2].block_lengths(), flat[2].block_lengths())
+    log(f"paged one-wave mode: block lengths {int(paged[2].block_lengths().min())}.."
+        f"{int(paged[2].block_lengths().max())}")
+
+
 def test_paged_pool_exhaustion_is_a_host_error():
     torch = require_gpu()
     import hierarchical_global_local_amd as hg
