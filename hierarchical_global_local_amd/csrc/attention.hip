@@ -240,8 +240,9 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
   const int cb = rmap ? rmap[b] : b, hk = h / (H / Hkv);
   if (pg.nlim && qt * 64 >= pg.nlim[cb]) return;  // queries past the row's length: nothing reads them
 
-  // q^T fragments with the rotary embedding: lane holds dh indices 32*ks + 8g + e; the rotation
-  // partner (index +- DH/2) sits in slice ks +- KS/2 of the same lane.
+  // q^T fragments with the rotary embedding and the softmax scale (log2 units) folded in: lane
+  // holds dh indices 32*ks + 8g + e; the rotation partner (index +- DH/2) sits in slice ks +- KS/2
+  // of the same lane.
   half8 qf[KS];
   {
     float x[KS][8];
@@ -255,8 +256,8 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
       for (int e = 0; e < 8; ++e) {
         const float2 cs = rp[32 * ks + 8 * g + e];
         const float x1 = x[ks][e], x2 = x[ks + KS / 2][e];
-        qf[ks][e] = to_f16(x1 * cs.x - x2 * cs.y);
-        qf[ks + KS / 2][e] = to_f16(x2 * cs.x + x1 * cs.y);
+        qf[ks][e] = to_f16((x1 * cs.x - x2 * cs.y) * scale_log2);
+        qf[ks + KS / 2][e] = to_f16((x2 * cs.x + x1 * cs.y) * scale_log2);
       }
   }
 
@@ -315,12 +316,8 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
       }
     }
     // causal mask (only the diagonal tile, the last one, has masked keys) and the tile maximum of
-    // this lane's query
+    // this lane's query (the scores are already scaled, through q)
     float mx = -INFINITY;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[nt][i] *= scale_log2;
     if (t == ntiles - 1) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
