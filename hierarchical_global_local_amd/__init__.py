@@ -89,10 +89,11 @@ def lib() -> ctypes.CDLL:
     L.bt_set_graphs.argtypes = [c_p, c_i32]
     L.bt_test_replay.argtypes = [c_p, c_i32, c_i32]
     L.bt_test_fuse_local.argtypes = [c_p, c_i32]
+    L.bt_numerics_status.argtypes = [c_p, c_i32, ctypes.POINTER(ctypes.c_int64)]
     for f in ("bt_init", "bt_prefill", "bt_prefill_lengths", "bt_prefill_ragged", "bt_prefill_rows",
               "bt_block_lengths", "bt_page_table", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
               "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs", "bt_test_replay",
-              "bt_test_fuse_local"):
+              "bt_test_fuse_local", "bt_numerics_status"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -291,6 +292,13 @@ class BlockTransformer:
         dt = torch.float32 if self.model.dtype == "fp32" else torch.float16
         raw = self.workspace[off.value: off.value + nb.value]
         return raw.view(dt), cap.value
+
+    def numerics_status(self, reset: bool = False) -> dict:
+        """bt_numerics_status: weight elements rounded at init, and whether an activation or cache
+        value was clamped to fp16's range since the flag was last cleared (synchronises)."""
+        a = (ctypes.c_int64 * 2)()
+        check(lib().bt_numerics_status(self.h, 1 if reset else 0, a))
+        return {"weights_rounded": int(a[0]), "values_clamped": bool(a[1])}
 
     def profile(self, on: bool) -> None:
         check(lib().bt_profile_enable(self.h, 1 if on else 0))

@@ -195,6 +195,7 @@ std::string plan_layout(const bt_config& c, Layout& lo) {
   lo.rowmap = region((size_t)lo.Bmax * 4);
   lo.ptab = region(lo.pages ? (size_t)lo.Bmax * (lo.ncap / 64) * 4 : 0);
   lo.lastblk = region((size_t)lo.Bmax * 4);
+  lo.wflags = region(2 * 4);
   lo.total = w;
   return "";
 }
@@ -231,6 +232,7 @@ struct bt_handle {
   ResidPending pending{};     // split-K residual update not yet folded into X (nsplit = 0: none)
   int head_nparts = 0;        // column groups of the last classifier launch
   int dec_nsplit = 1;         // key splits of block-attention decode for this batch size
+  int64_t weights_rounded = 0;  // weight elements bt_init could not convert to fp16 exactly
   // decode steps replayed from HIP graphs, one per in-block offset j (0 = block step)
   bool use_graphs = true;
   // decode steps run the token decoder's local attention inside its [out|down] GEMM where the
@@ -275,6 +277,13 @@ struct Prof {
 };
 
 inline char* P_(bt_handle* h, size_t off) { return h->ws + off; }
+
+// Partial-result buffers of the workspace (split-K, split-KV, classifier keys).
+float* rpart_buf(bt_handle* h) { return (float*)P_(h, h->lo.rpart); }
+float* part_buf(bt_handle* h) { return (float*)P_(h, h->lo.part); }
+size_t part_cap(bt_handle* h) { return h->lo.part_bytes; }
+unsigned long long* keys_buf(bt_handle* h) { return (unsigned long long*)P_(h, h->lo.keys); }
+int keys_ld(const Layout& lo) { return lo.Vpad / 4 + 64; }
 
 int hip_fail(bt_handle* h, hipError_t e, const char* what) {
   if (h) h->broken = true;
@@ -433,7 +442,7 @@ Epi resid_epi(bt_handle* h, const LayerOff& w, int rows, int splits) {
   ep.out0 = P_(h, lo.X);
   ep.ld0 = lo.D;
   ep.splits = splits;
-  ep.part = (float*)P_(h, lo.rpart);
+  ep.part = rpart_buf(h);
   if (ep.splits > 1) {
     h->pending.part = ep.part;
     h->pending.nsplit = ep.splits;
@@ -557,8 +566,8 @@ int run_head(bt_handle* h, int m, int slot, float* d_logits) {
   ep.out0 = d_logits;
   ep.ld0 = lo.V;
   ep.n_valid = lo.V;
-  ep.keys = (unsigned long long*)P_(h, lo.keys);
-  ep.keys_ld = lo.Vpad / 4 + 64;
+  ep.keys = keys_buf(h);
+  ep.keys_ld = keys_ld(lo);
   ep.nparts_out = &h->head_nparts;
   Prof p(h, PK_GEMM_HEAD, V * D * E + Bd * D * E + (d_logits ? Bd * V * 4.0 : 0.0) + Bd * 8.0, 2.0 * Bd * V * D);
   BT_CHECK(h, launch_gemm(lo.f32, ln_buf(h, 0), nullptr, lo.D, P_(h, lo.head), h->B, lo.f32 ? lo.V : lo.Vpad, lo.D,
@@ -602,7 +611,7 @@ int run_finalize(bt_handle* h, int j, int32_t* d_next, int n_inc) {
   NextStepArgs nx = next_step_args(h, h->g + 1);
   if (h->rmap) nx.mode = 0;
   Prof p(h, PK_FINALIZE, (double)h->B * (16.0 + lo.D * (lo.tab_elem + 4.0 + 2.0 * lo.elem)), 0.0);
-  BT_CHECK(h, launch_finalize((const unsigned long long*)P_(h, lo.keys), h->head_nparts, lo.Vpad / 4 + 64, h->B, d_next,
+  BT_CHECK(h, launch_finalize(keys_buf(h), h->head_nparts, keys_ld(lo), h->B, d_next,
                               (int32_t*)P_(h, lo.cur), lo.L, j, (int*)P_(h, lo.dstate), n_inc, nx, h->st, h->rmap),
            "finalize");
   return BT_OK;
@@ -715,8 +724,8 @@ int enqueue_decode(bt_handle* h, int j, float* d_logits) {
                4.0 * Bd * lo.H * lo.dh * (double)(n + 1));
         BT_CHECK(h, launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,
                                              lo.Hkv, lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l), block_v(h, l),
-                                             lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, (float*)P_(h, lo.part),
-                                             lo.part_bytes, h->dec_nsplit, h->st, page_table(h), lo.ncap / 64),
+                                             lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, part_buf(h),
+                                             part_cap(h), h->dec_nsplit, h->st, page_table(h), lo.ncap / 64),
                  "block attention decode");
       }
       if ((r = run_out(h, lo.blk[l], h->B))) return r;
@@ -802,7 +811,7 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
   const int D = lo.D, F = lo.F, QW = lo.QW;
   auto fin = [&](hipError_t err, const char* what) -> int {
     if (err == hipSuccess) return 0;
-    delete h;
+    bt_destroy(h);
     return fail(BT_ERR_HIP, std::string("bt_init ") + what + ": " + hipGetErrorString(err));
   };
 #define INIT_CHECK(expr, what) \
@@ -811,6 +820,11 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
   INIT_CHECK(hipMemsetAsync(h->ws + lo.block_kv, 0, lo.block_kv_bytes, h->st), "memset");
   INIT_CHECK(hipMemsetAsync(h->ws + lo.local_kv, 0, lo.local_kv_bytes, h->st), "memset");
   INIT_CHECK(hipMemsetAsync(h->ws + lo.cur, 0, (size_t)lo.Bmax * lo.L * 4, h->st), "memset");
+  // weight-conversion flags: [0] = first out-of-range tensor (none: 0x7f7f7f7f), [1] = rounded count
+  int* wflags = (int*)(h->ws + lo.wflags);
+  INIT_CHECK(hipMemsetAsync(wflags, 0x7f, 4, h->st), "memset");
+  INIT_CHECK(hipMemsetAsync(wflags + 1, 0, 4, h->st), "memset");
+  std::vector<std::string> tensor_names;  // index = the tensor id the conversion reports
   INIT_CHECK(hipMemcpyAsync(h->ws + lo.emb_block, wb + lo.bl_emb_block, (size_t)lo.V * lo.De * lo.tab_elem,
                             hipMemcpyDeviceToDevice, h->st),
              "copy");
@@ -820,12 +834,18 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
                "copy");
   // one [in, out] canonical matrix into rows [row0, row0 + N) and columns [col0, col0 + K) of a
   // repacked [rows][Ktot] weight (element (n = out, k = in) at src[k * N + n])
-  auto put = [&](size_t src, int K, int N, size_t dst, int Ktot, int row0, int col0) -> hipError_t {
-    if (f32) return launch_transpose_convert(wb + src, bf, K, N, h->ws + dst, f32, Ktot, row0, col0, sc, h->st);
-    return launch_pack_frag(wb + src, bf, 1, N, N, N, K, h->ws + dst, Ktot, row0, col0, sc, h->st);
+  auto name_id = [&](const std::string& name) {
+    tensor_names.push_back(name);
+    return (int)tensor_names.size() - 1;
   };
-  // xl: index of a token layer with a cross-attention branch, else -1
-  auto repack_layer = [&](const Layout::BlobLayer& s, const LayerOff& d, int xl) -> hipError_t {
+  auto put = [&](const std::string& name, size_t src, int K, int N, size_t dst, int Ktot, int row0,
+                 int col0) -> hipError_t {
+    if (f32) return launch_transpose_convert(wb + src, bf, K, N, h->ws + dst, f32, Ktot, row0, col0, sc, h->st);
+    return launch_pack_frag(wb + src, bf, 1, N, N, N, K, h->ws + dst, Ktot, row0, col0, sc, h->st, wflags,
+                            name_id(name));
+  };
+  // xl: index of a token layer with a cross-attention branch, else -1; pf: the layer's tensor-name prefix
+  auto repack_layer = [&](const Layout::BlobLayer& s, const LayerOff& d, int xl, const std::string& pf) -> hipError_t {
     hipError_t err;
     float* ln = (float*)(h->ws + d.ln);
     if ((err = launch_to_f32(wb + s.ln1g, bf, D, ln, h->st))) return err;
@@ -833,17 +853,17 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     if ((err = launch_to_f32(wb + s.ln2g, bf, D, ln + 2 * D, h->st))) return err;
     if ((err = launch_to_f32(wb + s.ln2b, bf, D, ln + 3 * D, h->st))) return err;
     // w1 rows: q | k | v (| cross-attention q) | up
-    if ((err = put(s.qkvw, D, QW, d.w1, D, 0, 0))) return err;
-    if (xl >= 0 && (err = put(s.xqw, D, D, d.w1, D, QW, 0))) return err;
-    if ((err = put(s.upw, D, F, d.w1, D, d.n1, 0))) return err;
+    if ((err = put(pf + ".attn.qkv.w", s.qkvw, D, QW, d.w1, D, 0, 0))) return err;
+    if (xl >= 0 && (err = put(pf + ".xattn.q.w", s.xqw, D, D, d.w1, D, QW, 0))) return err;
+    if ((err = put(pf + ".mlp.up.w", s.upw, D, F, d.w1, D, d.n1, 0))) return err;
     float* b1 = (float*)(h->ws + d.b1);
     if ((err = launch_to_f32(wb + s.qkvb, bf, QW, b1, h->st))) return err;
     if (xl >= 0 && (err = launch_to_f32(wb + s.xqb, bf, D, b1 + QW, h->st))) return err;
     if ((err = launch_to_f32(wb + s.upb, bf, F, b1 + d.n1, h->st))) return err;
     // w2 columns: attn.out | mlp.down (| cross-attention out)
-    if ((err = put(s.outw, D, D, d.w2, d.k2, 0, 0))) return err;
-    if ((err = put(s.downw, F, D, d.w2, d.k2, 0, D))) return err;
-    if (xl >= 0 && (err = put(s.xow, D, D, d.w2, d.k2, 0, D + F))) return err;
+    if ((err = put(pf + ".attn.out.w", s.outw, D, D, d.w2, d.k2, 0, 0))) return err;
+    if ((err = put(pf + ".mlp.down.w", s.downw, F, D, d.w2, d.k2, 0, D))) return err;
+    if (xl >= 0 && (err = put(pf + ".xattn.out.w", s.xow, D, D, d.w2, d.k2, 0, D + F))) return err;
     float* b2 = (float*)(h->ws + d.b2);
     if ((err = launch_to_f32(wb + s.outb, bf, D, b2, h->st))) return err;
     if ((err = launch_to_f32(wb + s.downb, bf, D, b2 + D, h->st))) return err;
@@ -852,12 +872,14 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     if ((err = launch_to_f32(wb + s.xob, bf, D, b2 + 2 * D, h->st))) return err;
     if ((err = launch_add_f32(b2, b2 + 2 * D, D, h->st))) return err;
     const int xw = 2 * lo.Hkv * lo.dh;
-    if ((err = put(s.xkvw, D, xw, lo.xkv_w, D, xl * xw, 0))) return err;
+    if ((err = put(pf + ".xattn.kv.w", s.xkvw, D, xw, lo.xkv_w, D, xl * xw, 0))) return err;
     return launch_to_f32(wb + s.xkvb, bf, xw, (float*)(h->ws + lo.xkv_b) + (size_t)xl * xw, h->st);
   };
-  for (int l = 0; l < lo.Nb; ++l) INIT_CHECK(repack_layer(lo.bl_blk[l], lo.blk[l], -1), "repack block layer");
+  for (int l = 0; l < lo.Nb; ++l)
+    INIT_CHECK(repack_layer(lo.bl_blk[l], lo.blk[l], -1, "blk." + std::to_string(l)), "repack block layer");
   for (int l = 0; l < lo.Nt; ++l)
-    INIT_CHECK(repack_layer(lo.bl_tok[l], lo.tok[l], lo.mode == BT_CTX_XATTN ? l : -1), "repack token layer");
+    INIT_CHECK(repack_layer(lo.bl_tok[l], lo.tok[l], lo.mode == BT_CTX_XATTN ? l : -1, "tok." + std::to_string(l)),
+               "repack token layer");
   if (!lo.vanilla && lo.mode != BT_CTX_PREFIX)
     INIT_CHECK(launch_to_f32(wb + lo.bl_emb_tok + (size_t)cfg->pad_id * D * lo.tab_elem, bf, D,
                              (float*)(h->ws + lo.pad_emb), h->st),
@@ -875,7 +897,7 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
                  "repack prefix");
     } else {
       INIT_CHECK(launch_pack_frag(wb + lo.bl_prefix_w, bf, 1, (size_t)lo.NC * D, lo.NC * D, lo.NC * D, D,
-                                  h->ws + lo.prefix_w, D, 0, 0, sc, h->st),
+                                  h->ws + lo.prefix_w, D, 0, 0, sc, h->st, wflags, name_id("prefix.w")),
                  "repack prefix");
     }
     INIT_CHECK(launch_to_f32(wb + lo.bl_prefix_b, bf, lo.NC * D, (float*)(h->ws + lo.prefix_b), h->st), "repack");
@@ -885,7 +907,8 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     INIT_CHECK(launch_convert_rows(wb + lo.bl_head, bf, lo.V, D, lo.Vpad, h->ws + lo.head, f32, sc, h->st),
                "repack head");
   } else {
-    INIT_CHECK(launch_pack_frag(wb + lo.bl_head, bf, D, 1, lo.V, lo.Vpad, D, h->ws + lo.head, D, 0, 0, sc, h->st),
+    INIT_CHECK(launch_pack_frag(wb + lo.bl_head, bf, D, 1, lo.V, lo.Vpad, D, h->ws + lo.head, D, 0, 0, sc, h->st,
+                                wflags, name_id("head.w")),
                "repack head");
   }
   INIT_CHECK(launch_rope_table((float2*)(h->ws + lo.rope), lo.npos, lo.dh, cfg->rope_base, h->st), "rope table");
@@ -897,6 +920,20 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     INIT_CHECK(hipEventCreateWithFlags(&h->ptab_ev, hipEventDisableTiming), "page table");
     INIT_CHECK(hipMemcpyAsync(h->ws + lo.ptab, h->ptab_host, tab, hipMemcpyHostToDevice, h->st), "page table");
     INIT_CHECK(hipEventRecord(h->ptab_ev, h->st), "page table");
+  }
+  if (!f32) {
+    // every weight matrix must fit fp16 after the pre-scale: read the conversion flags back
+    int32_t fl[2] = {0, 0};
+    INIT_CHECK(hipMemcpyAsync(fl, wflags, sizeof(fl), hipMemcpyDeviceToHost, h->st), "weight check");
+    INIT_CHECK(hipStreamSynchronize(h->st), "weight check");
+    if (fl[0] != 0x7f7f7f7f) {
+      const std::string name = fl[0] >= 0 && fl[0] < (int)tensor_names.size() ? tensor_names[fl[0]] : "?";
+      bt_destroy(h);
+      return fail(BT_ERR_UNSUPPORTED, "weight tensor " + name +
+                                          " holds a value of magnitude >= 256 or a non-finite value: BT_BF16 "
+                                          "keeps weight matrices as fp16 scaled by 2^8, which cannot hold it");
+    }
+    h->weights_rounded = fl[1];
   }
 #undef INIT_CHECK
   *out = h;
@@ -1084,17 +1121,35 @@ int bt_prefill_rows(bt_handle* h, const int32_t* rows, int32_t B_new, const int3
   return BT_OK;
 }
 
-int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
+namespace {
+
+// Checks shared by the decode-step entry points.
+int decode_precheck(bt_handle* h, int32_t* d_next) {
   if (!h || !d_next) return fail(BT_ERR_INVALID_ARG, "NULL argument");
   if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
   if (!h->ready) return fail(BT_ERR_STATE, "bt_decode_step before bt_prefill");
-  const Layout& lo = h->lo;
   int64_t most = 0;
   for (int64_t t : h->row_tok) most = std::max(most, t);
-  if (most + 1 > lo.max_tokens) return fail(BT_ERR_CAPACITY, "max_tokens reached");
+  if (most + 1 > h->lo.max_tokens) return fail(BT_ERR_CAPACITY, "max_tokens reached");
+  return BT_OK;
+}
+
+// Host bookkeeping after a decode step was enqueued.
+void decode_done(bt_handle* h, int j) {
+  h->g += 1;
+  for (int64_t& t : h->row_tok) t += 1;
+  if (h->lo.pages && j == 0)
+    for (int b = 0; b < h->B; ++b) h->row_n[b] += 1;
+}
+
+}  // namespace
+
+int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
+  int r = decode_precheck(h, d_next);
+  if (r) return r;
+  const Layout& lo = h->lo;
   const int j = h->g % lo.L;
   h->decode_phase = true;
-  int r;
   if (lo.pages && j == 0 && (r = pages_grow(h))) return r;
   // graphs replay everything up to the classifier; the logits variant and profiling run eagerly
   if (h->use_graphs && !d_logits && !h->prof && h->st != nullptr) {
@@ -1129,10 +1184,7 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
   }
   r = run_finalize(h, j, d_next, j == 0 ? 1 : 0);
   if (r) return r;
-  h->g += 1;
-  for (int64_t& t : h->row_tok) t += 1;
-  if (lo.pages && j == 0)
-    for (int b = 0; b < h->B; ++b) h->row_n[b] += 1;
+  decode_done(h, j);
   return BT_OK;
 }
 
@@ -1172,6 +1224,20 @@ int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_k
   if (!h || !block_kv_len || !local_kv_len) return fail(BT_ERR_INVALID_ARG, "NULL argument");
   *block_kv_len = h->ready ? h->n_blocks : 0;
   *local_kv_len = h->ready ? h->local_len : 0;
+  return BT_OK;
+}
+
+int bt_numerics_status(bt_handle* h, int32_t reset, int64_t* status) {
+  if (!h || !status) return fail(BT_ERR_INVALID_ARG, "NULL argument");
+  if (h->broken) return fail(BT_ERR_STATE, "handle unusable after a HIP error");
+  unsigned int f[4] = {0u, 0u, 0u, 0u};
+  BT_CHECK(h, clamp_flag_misc(&f[0], reset != 0, h->st), "clamp flag");
+  BT_CHECK(h, clamp_flag_gemm(&f[1], reset != 0, h->st), "clamp flag");
+  BT_CHECK(h, clamp_flag_gemm_decode(&f[2], reset != 0, h->st), "clamp flag");
+  BT_CHECK(h, clamp_flag_attention(&f[3], reset != 0, h->st), "clamp flag");
+  BT_CHECK(h, hipStreamSynchronize(h->st), "clamp flag");
+  status[0] = h->weights_rounded;
+  status[1] = (f[0] | f[1] | f[2] | f[3]) ? 1 : 0;
   return BT_OK;
 }
 
@@ -1252,8 +1318,8 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
       const int l = i % lo.Nb;
       hipError_t e = launch_block_attn_decode(lo.f32, P_(h, lo.QKV), h->B, (const int*)P_(h, lo.dstate), lo.H,
                                               lo.Hkv, lo.dh, (const float2*)P_(h, lo.rope), block_k(h, l),
-                                              block_v(h, l), lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, (float*)P_(h, lo.part),
-                                              lo.part_bytes, h->dec_nsplit, h->st, page_table(h), lo.ncap / 64);
+                                              block_v(h, l), lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, part_buf(h),
+                                              part_cap(h), h->dec_nsplit, h->st, page_table(h), lo.ncap / 64);
       if (e != hipSuccess) r = hip_fail(h, e, "replay attention");
     } else {
       r = fail(BT_ERR_INVALID_ARG, "kind not replayable");

@@ -1649,4 +1649,6 @@ hipError_t launch_cross_attention(bool f32, const void* QKV, int ldq, int qoff, 
   return hipErrorInvalidValue;
 }
 
+BT_DEFINE_CLAMP_FLAG_ACCESS(clamp_flag_attention)
+
 }  // namespace bt

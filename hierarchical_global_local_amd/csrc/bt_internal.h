@@ -85,6 +85,7 @@ struct Layout {
   size_t dstate;  // int32 [Bmax] device state: block-KV entries of each row (per layer)
   size_t rowmap;  // int32 [Bmax]: cache rows of the rows a join prefills
   size_t lastblk; // int32 [Bmax]: last real prompt block of each prefilled row
+  size_t wflags;  // int32 [2]: weight-conversion flags of bt_init (see launch_pack_frag)
   size_t total;
   size_t block_kv_bytes, local_kv_bytes;
   // canonical blob offsets (bytes)
@@ -109,9 +110,17 @@ hipError_t launch_transpose_convert(const void* src, bool src_bf16, int K, int N
 hipError_t launch_convert_rows(const void* src, bool src_bf16, int rows, int cols, int rows_pad, void* dst,
                                bool dst_f32, float scale, hipStream_t st);
 // fp16 weights in fragment order: destination rows [row0, row0 + N), columns [col0, col0 + K) of a
-// matrix of width Ktot take scale * src[n * sn + k * sk] (zero for rows n >= n_valid).
+// matrix of width Ktot take scale * src[n * sn + k * sk] (zero for rows n >= n_valid).  wflags
+// (weights at bt_init, else null): [0] = min(itself, tensor_id) if a scaled value is beyond fp16's
+// range or not finite, [1] += values fp16 rounds (see k_pack_frag).
 hipError_t launch_pack_frag(const void* src, bool src_bf16, size_t sn, size_t sk, int n_valid, int N, int K,
-                            void* dst, int Ktot, int row0, int col0, float scale, hipStream_t st);
+                            void* dst, int Ktot, int row0, int col0, float scale, hipStream_t st,
+                            int* wflags = nullptr, int tensor_id = 0);
+// Clamp flag of each kernel file (see to_f16): copied to *value (and cleared with reset) on st.
+hipError_t clamp_flag_misc(unsigned int* value, bool reset, hipStream_t st);
+hipError_t clamp_flag_gemm(unsigned int* value, bool reset, hipStream_t st);
+hipError_t clamp_flag_gemm_decode(unsigned int* value, bool reset, hipStream_t st);
+hipError_t clamp_flag_attention(unsigned int* value, bool reset, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool src_bf16, int n, float* dst, hipStream_t st);
 hipError_t launch_add_f32(float* dst, const float* a, int n, hipStream_t st);
 // X[b][:] = base[:] (+ add[b * add_ld + :] when add is not null), rows b < B of width D

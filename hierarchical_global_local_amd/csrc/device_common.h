@@ -21,8 +21,29 @@ __device__ __forceinline__ float load_f32(const float* p) { return *p; }
 __device__ __forceinline__ float load_f32(const f16* p) { return (float)*p; }
 __device__ __forceinline__ float load_f32(const bf16_t* p) { return __uint_as_float((uint32_t)p->bits << 16); }
 
-// fp16 stores saturate at the largest finite value instead of overflowing to infinity.
-__device__ __forceinline__ f16 to_f16(float x) { return (f16)fminf(fmaxf(x, -65504.f), 65504.f); }
+// Set to 1 by any fp16 conversion of an activation or cache value that is out of fp16's range or
+// not finite (and is therefore clamped).  One flag per translation unit (each kernel file has its
+// own copy); BT_DEFINE_CLAMP_FLAG_ACCESS gives the host a reader for it.
+static __device__ unsigned int g_clamped;
+
+// fp16 stores saturate at the largest finite value instead of overflowing to infinity, and record
+// that they did.  (fmaxf/fminf return the other operand for a NaN, so a NaN becomes -65504.)
+__device__ __forceinline__ f16 to_f16(float x) {
+  if (!(fabsf(x) <= 65504.f)) g_clamped = 1u;
+  return (f16)fminf(fmaxf(x, -65504.f), 65504.f);
+}
+
+// Host access to the translation unit's clamp flag: copies it to *value and, with reset, clears it
+// (both enqueued on st; the caller synchronises before reading *value).
+#define BT_DEFINE_CLAMP_FLAG_ACCESS(fn)                                                           \
+  hipError_t fn(unsigned int* value, bool reset, hipStream_t st) {                                \
+    hipError_t e = hipMemcpyFromSymbolAsync(value, HIP_SYMBOL(g_clamped), sizeof(unsigned int), 0, \
+                                            hipMemcpyDeviceToHost, st);                           \
+    if (e != hipSuccess || !reset) return e;                                                      \
+    static const unsigned int zero = 0u;                                                          \
+    return hipMemcpyToSymbolAsync(HIP_SYMBOL(g_clamped), &zero, sizeof(unsigned int), 0,          \
+                                  hipMemcpyHostToDevice, st);                                     \
+  }
 __device__ __forceinline__ void store_from_f32(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_from_f32(f16* p, float v) { *p = to_f16(v); }
 

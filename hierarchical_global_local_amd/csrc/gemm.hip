@@ -652,4 +652,6 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
   return launch_mfma_cfg<32, 32, 2, 2, 6>(A1, A2, W, M, N, K, mode, ep, st);
 }
 
+BT_DEFINE_CLAMP_FLAG_ACCESS(clamp_flag_gemm)
+
 }  // namespace bt

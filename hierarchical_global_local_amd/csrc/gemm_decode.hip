@@ -499,4 +499,6 @@ hipError_t launch_gemm_skinny(const SkinnyPlan& p, const void* A1, const void* A
   return hipErrorInvalidValue;
 }
 
+BT_DEFINE_CLAMP_FLAG_ACCESS(clamp_flag_gemm_decode)
+
 }  // namespace bt

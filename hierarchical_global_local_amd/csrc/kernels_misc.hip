@@ -50,32 +50,46 @@ hipError_t launch_transpose_convert(const void* src, bool src_bf16, int K, int N
 // fp16 weights in fragment order (frag_off): rows [row0, row0 + N) and columns [col0, col0 + K)
 // of a destination of width Ktot receive scale * (element (n, k) of the source, at
 // src[n * sn + k * sk]); rows n >= n_valid are zero.  One thread writes 8 consecutive columns.
+// With wflags (a weight matrix at bt_init): a scaled value beyond fp16's range or not finite sets
+// wflags[0] to at most tensor_id; a value fp16 cannot hold exactly (a magnitude below its
+// subnormal spacing) adds one to wflags[1].  Without it (an activation operand) values are
+// clamped like every other fp16 activation.
 template <typename Tin>
 __global__ __launch_bounds__(256) void k_pack_frag(const Tin* __restrict__ src, size_t sn, size_t sk, int n_valid,
                                                    int N, int K, f16* __restrict__ dst, int Ktot, int row0, int col0,
-                                                   float scale) {
+                                                   float scale, int* __restrict__ wflags, int tensor_id) {
   const size_t total = (size_t)N * (K / 8);
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
     const int n = (int)(i % N), kc = (int)(i / N);
     half8 w;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      w[e] = n < n_valid ? to_f16(load_f32(src + (size_t)n * sn + (size_t)(kc * 8 + e) * sk) * scale) : (f16)0.f;
+    for (int e = 0; e < 8; ++e) {
+      const float v = n < n_valid ? load_f32(src + (size_t)n * sn + (size_t)(kc * 8 + e) * sk) * scale : 0.f;
+      if (wflags) {
+        const f16 hv = (f16)fminf(fmaxf(v, -65504.f), 65504.f);
+        if (!(fabsf(v) <= 65504.f)) atomicMin(&wflags[0], tensor_id);
+        else if ((float)hv != v) atomicAdd(&wflags[1], 1);
+        w[e] = hv;
+      } else {
+        w[e] = to_f16(v);
+      }
+    }
     *(half8*)(dst + frag_off(row0 + n, col0 + kc * 8, Ktot)) = w;
   }
 }
 
 hipError_t launch_pack_frag(const void* src, bool src_bf16, size_t sn, size_t sk, int n_valid, int N, int K,
-                            void* dst, int Ktot, int row0, int col0, float scale, hipStream_t st) {
+                            void* dst, int Ktot, int row0, int col0, float scale, hipStream_t st, int* wflags,
+                            int tensor_id) {
   if (K % 8 || col0 % 8 || Ktot % 32 || row0 % 16) return hipErrorInvalidValue;
   const size_t total = (size_t)N * (K / 8);
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
   if (src_bf16)
     hipLaunchKernelGGL(k_pack_frag<bf16_t>, dim3(blocks), dim3(256), 0, st, (const bf16_t*)src, sn, sk, n_valid, N, K,
-                       (f16*)dst, Ktot, row0, col0, scale);
+                       (f16*)dst, Ktot, row0, col0, scale, wflags, tensor_id);
   else
     hipLaunchKernelGGL(k_pack_frag<float>, dim3(blocks), dim3(256), 0, st, (const float*)src, sn, sk, n_valid, N, K,
-                       (f16*)dst, Ktot, row0, col0, scale);
+                       (f16*)dst, Ktot, row0, col0, scale, wflags, tensor_id);
   return hipGetLastError();
 }
 
@@ -648,5 +662,7 @@ hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, i
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
+
+BT_DEFINE_CLAMP_FLAG_ACCESS(clamp_flag_misc)
 
 }  // namespace bt

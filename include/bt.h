@@ -48,9 +48,15 @@ typedef enum {
 
 typedef enum {
   BT_FP32 = 0, /* weights, activations and caches in fp32                     */
-  BT_BF16 = 1  /* bf16 weights blob; matrix operands and KV caches held as fp16
-                  (exact for every bf16 weight after a 2^8 pre-scale), fp32
-                  accumulation, fp32 residual stream                           */
+  BT_BF16 = 1  /* bf16 weights blob; matrix operands and KV caches held as fp16,
+                  fp32 accumulation, fp32 residual stream.  Weight matrices are
+                  stored as fp16 after a 2^8 pre-scale: exact for every bf16
+                  weight of magnitude in [2^-25, 256) and for every multiple
+                  of 2^-32 below; other magnitudes below 2^-25 round to a
+                  multiple of 2^-32 (counted, see bt_numerics_status); a
+                  magnitude >= 256 or a non-finite value
+                  makes bt_init fail.  Activations and cache entries beyond
+                  fp16's range are clamped to +-65504 (flagged, same call).   */
 } bt_dtype;
 
 /* How the context embedding of the previous block reaches the token decoder (summary page §3.4
@@ -135,7 +141,10 @@ size_t bt_workspace_bytes(const bt_config* cfg);
  * into the workspace (device pointer, ws_bytes >= bt_workspace_bytes, 256-byte
  * aligned) and create a handle bound to hip_stream (a hipStream_t; NULL = the
  * default stream).  Once the stream has synchronised, the caller may free the
- * weights blob; the workspace must outlive the handle. */
+ * weights blob; the workspace must outlive the handle.  BT_BF16: bt_init
+ * synchronises the stream to check the converted weight matrices and returns
+ * BT_ERR_UNSUPPORTED (no handle; bt_last_error names the tensor) if one holds a
+ * magnitude >= 256 or a non-finite value, which the fp16 operands cannot hold. */
 int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size_t ws_bytes,
             void* hip_stream, bt_handle** out);
 
@@ -231,6 +240,15 @@ int bt_cache_lengths(const bt_handle* h, int32_t* block_kv_len, int32_t* local_k
  * n_kv_heads, or n_heads when that is 0; S is P for BT_CTX_PREFIX, else 1 (the start slot). */
 int bt_workspace_region(const bt_config* cfg, int32_t which, size_t* offset, size_t* bytes,
                         int32_t* capacity);
+
+/* Range of the fp16 values of a BT_BF16 handle (for BT_FP32 both entries stay 0).
+ * status[0]: weight elements bt_init rounded when converting them to fp16 (magnitudes below
+ *            2^-25 that are not multiples of 2^-32; the rounding error is at most 2^-33 each);
+ * status[1]: 1 if an activation or cache value was beyond fp16's range or not finite, and was
+ *            clamped to +-65504, since the flag was last cleared; else 0.  The flag is kept per
+ *            device and process and is shared by every handle on the device.
+ * reset != 0 clears the flag after reading it.  Synchronises the handle's stream. */
+int bt_numerics_status(bt_handle* h, int32_t reset, int64_t* status);
 
 /* Free the host handle (no device memory is owned). */
 int bt_destroy(bt_handle* h);
