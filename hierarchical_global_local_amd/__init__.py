@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
     L.bt_block_lengths.argtypes = [c_p, ctypes.POINTER(c_i32)]
     L.bt_page_table.argtypes = [c_p, ctypes.POINTER(c_i32)]
     L.bt_decode_step.argtypes = [c_p, c_p, c_p]
+    L.bt_decode_step_static.argtypes = [c_p, c_p, c_p]
     L.bt_cache_lengths.argtypes = [c_p, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
     L.bt_workspace_region.argtypes = [cfgp, c_i32, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz), ctypes.POINTER(c_i32)]
     L.bt_destroy.argtypes = [c_p]
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
     L.bt_test_fuse_local.argtypes = [c_p, c_i32]
     L.bt_numerics_status.argtypes = [c_p, c_i32, ctypes.POINTER(ctypes.c_int64)]
     for f in ("bt_init", "bt_prefill", "bt_prefill_lengths", "bt_prefill_ragged", "bt_prefill_rows",
-              "bt_block_lengths", "bt_page_table", "bt_decode_step", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
+              "bt_block_lengths", "bt_page_table", "bt_decode_step", "bt_decode_step_static", "bt_cache_lengths", "bt_workspace_region", "bt_destroy",
               "bt_profile_enable", "bt_profile_read", "bt_test_gemm", "bt_set_graphs", "bt_test_replay",
               "bt_test_fuse_local", "bt_numerics_status"):
         getattr(L, f).restype = ctypes.c_int
@@ -248,6 +249,16 @@ class BlockTransformer:
             out = torch.empty(self.batch, dtype=torch.int32, device=self.device)
         self._order(out, logits)
         check(lib().bt_decode_step(self.h, out.data_ptr(), _ptr(logits)))
+        return out
+
+    def decode_step_static(self, out=None, logits=None):
+        """One decode step through bt_decode_step_static: no allocation, no graph of its own, the
+        step's partial results in the library's static scratch (see include/bt.h)."""
+        torch = self.torch
+        if out is None:
+            out = torch.empty(self.batch, dtype=torch.int32, device=self.device)
+        self._order(out, logits)
+        check(lib().bt_decode_step_static(self.h, out.data_ptr(), _ptr(logits)))
         return out
 
     def set_graphs(self, enable: bool) -> None:

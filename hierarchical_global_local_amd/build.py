@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbt.so")
-SOURCES = ["api.cpp", "kernels_misc.hip", "gemm.hip", "gemm_decode.hip", "attention.hip"]
+SOURCES = ["api.cpp", "kernels_misc.hip", "gemm.hip", "gemm_decode.hip", "attention.hip", "scratch.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: no packed fp32 VALU instructions in device code
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",

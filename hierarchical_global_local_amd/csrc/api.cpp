@@ -233,6 +233,12 @@ struct bt_handle {
   int head_nparts = 0;        // column groups of the last classifier launch
   int dec_nsplit = 1;         // key splits of block-attention decode for this batch size
   int64_t weights_rounded = 0;  // weight elements bt_init could not convert to fp16 exactly
+  // bt_decode_step_static: the step's partial results (split-K, split-KV, argmax keys) in the
+  // library's static scratch instead of the workspace (null: the workspace regions)
+  char* scr_rpart = nullptr;
+  char* scr_part = nullptr;
+  char* scr_keys = nullptr;
+  size_t scr_part_bytes = 0;
   // decode steps replayed from HIP graphs, one per in-block offset j (0 = block step)
   bool use_graphs = true;
   // decode steps run the token decoder's local attention inside its [out|down] GEMM where the
@@ -278,11 +284,14 @@ struct Prof {
 
 inline char* P_(bt_handle* h, size_t off) { return h->ws + off; }
 
-// Partial-result buffers of the workspace (split-K, split-KV, classifier keys).
-float* rpart_buf(bt_handle* h) { return (float*)P_(h, h->lo.rpart); }
-float* part_buf(bt_handle* h) { return (float*)P_(h, h->lo.part); }
-size_t part_cap(bt_handle* h) { return h->lo.part_bytes; }
-unsigned long long* keys_buf(bt_handle* h) { return (unsigned long long*)P_(h, h->lo.keys); }
+// Partial-result buffers of the current call: the workspace's, or the static scratch's during
+// bt_decode_step_static.
+float* rpart_buf(bt_handle* h) { return h->scr_rpart ? (float*)h->scr_rpart : (float*)P_(h, h->lo.rpart); }
+float* part_buf(bt_handle* h) { return h->scr_part ? (float*)h->scr_part : (float*)P_(h, h->lo.part); }
+size_t part_cap(bt_handle* h) { return h->scr_keys ? h->scr_part_bytes : h->lo.part_bytes; }
+unsigned long long* keys_buf(bt_handle* h) {
+  return (unsigned long long*)(h->scr_keys ? h->scr_keys : P_(h, h->lo.keys));
+}
 int keys_ld(const Layout& lo) { return lo.Vpad / 4 + 64; }
 
 int hip_fail(bt_handle* h, hipError_t e, const char* what) {
@@ -921,6 +930,11 @@ int bt_init(const bt_config* cfg, const void* d_weights, void* d_workspace, size
     INIT_CHECK(hipMemcpyAsync(h->ws + lo.ptab, h->ptab_host, tab, hipMemcpyHostToDevice, h->st), "page table");
     INIT_CHECK(hipEventRecord(h->ptab_ev, h->st), "page table");
   }
+  {
+    // set-up of the static scratch of bt_decode_step_static on this device (once per device)
+    void* scr = nullptr;
+    INIT_CHECK(static_scratch(&scr), "static scratch");
+  }
   if (!f32) {
     // every weight matrix must fit fp16 after the pre-scale: read the conversion flags back
     int32_t fl[2] = {0, 0};
@@ -1183,6 +1197,42 @@ int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits) {
     if (r) return r;
   }
   r = run_finalize(h, j, d_next, j == 0 ? 1 : 0);
+  if (r) return r;
+  decode_done(h, j);
+  return BT_OK;
+}
+
+int bt_decode_step_static(bt_handle* h, int32_t* d_next, float* d_logits) {
+  int r = decode_precheck(h, d_next);
+  if (r) return r;
+  const Layout& lo = h->lo;
+  if (lo.pages) return fail(BT_ERR_UNSUPPORTED, "bt_decode_step_static does not run a paged block KV");
+  // the step's partial results: split-K products of the [out|down] GEMMs (at most 16 per launch,
+  // for up to B * lead rows), split-KV partials of the block attention, the classifier's keys
+  const int rows = (int)std::min<int64_t>((int64_t)h->B * std::max(1, lo.lead), lo.rpart_rows);
+  const size_t rpart = align_up((size_t)16 * rows * lo.D * 4, 256);
+  const size_t part = align_up(h->dec_nsplit > 1 ? (size_t)h->B * lo.H * h->dec_nsplit * (lo.dh + 2) * 4 : 0, 256);
+  const size_t keys = align_up((size_t)h->B * keys_ld(lo) * 8, 256);
+  if (rpart + part + keys > kStaticScratchBytes)
+    return fail(BT_ERR_CAPACITY, "bt_decode_step_static needs " + std::to_string(rpart + part + keys) +
+                                     " bytes of static scratch at this batch; the maximum is " +
+                                     std::to_string(kStaticScratchBytes));
+  void* scr = nullptr;
+  BT_CHECK(h, static_scratch(&scr), "static scratch");
+  h->scr_rpart = (char*)scr;
+  h->scr_part = (char*)scr + rpart;
+  h->scr_part_bytes = part;
+  h->scr_keys = (char*)scr + rpart + part;
+  // eager launches only: no graph is captured or replayed and no profiling event is created
+  const bool prof = h->prof;
+  h->prof = false;
+  const int j = h->g % lo.L;
+  h->decode_phase = true;
+  r = enqueue_decode(h, j, d_logits);
+  if (!r) r = run_finalize(h, j, d_next, j == 0 ? 1 : 0);
+  h->prof = prof;
+  h->scr_rpart = h->scr_part = h->scr_keys = nullptr;
+  h->scr_part_bytes = 0;
   if (r) return r;
   decode_done(h, j);
   return BT_OK;

@@ -98,6 +98,12 @@ struct Layout {
   std::vector<BlobLayer> bl_blk, bl_tok;
 };
 
+// Static scratch (scratch.hip): kStaticScratchBytes of device memory per GPU, for the partial
+// results of bt_decode_step_static.  static_scratch() returns its address on the current device
+// (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+hipError_t static_scratch(void** ptr);
+
 // Fills `lo` for cfg; returns an empty string or the reason cfg is invalid.
 std::string plan_layout(const bt_config& cfg, Layout& lo);
 

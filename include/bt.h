@@ -214,6 +214,19 @@ int bt_page_table(bt_handle* h, int32_t* table);
  * would exceed max_tokens. */
 int bt_decode_step(bt_handle* h, int32_t* d_next, float* d_logits);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): bt_decode_step with the same arguments, results and errors, bit for
+ * bit, that allocates nothing and captures no graph of its own.  Its kernels are launched
+ * individually on the handle's stream (so the caller may capture them), and the step's partial
+ * results (split-K products, split-KV partials, the classifier's partial maxima) live in a static
+ * device array of the library (64 MiB per GPU, held from the first bt_init on that GPU until the
+ * process ends) instead of the workspace.  The handle's GPU must be the current device.  A batch
+ * whose partial results exceed the array is refused with BT_ERR_CAPACITY before anything is
+ * queued (the d = 768, V = 50304 model needs 9.2 MiB at batch 64 and 36.7 MiB at batch 256);
+ * paged block KV is BT_ERR_UNSUPPORTED.  Every call on one GPU shares the array, which keeps the
+ * last call's contents: calls that overlap on one GPU (other handles, other streams) race. */
+int bt_decode_step_static(bt_handle* h, int32_t* d_next, float* d_logits);
+
 /* Decode steps are replayed from HIP graphs captured on first use (one per position inside a
  * block; recaptured when the batch size changes) unless logits are requested or the stream is the
  * NULL stream.  enable = 0 launches every kernel individually instead (same results, bit for bit).
