@@ -29,6 +29,80 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# ---------------------------------------------------------------- algorithmic cost model
+# The minimal traffic and arithmetic of the method itself (summary page "Block Transformer:
+# Global-to-Local Language Modeling for Fast Inference", §3.4 "The Inference Cost Model": decode is
+# bound by reading parameters and KV caches, prefill by compute): every weight read once per decode
+# step for the whole batch, every cached KV entry read once per use, activations passed between
+# kernels not counted; prefill FLOPs of the linear maps, the causal block attention, the prefix pass
+# and the classifier of the first token.
+
+def _layer_params(cfg, token_layer=False):
+    """Weights and biases of one layer (q|k|v, out, up, down, two LayerNorms; the cross-attention
+    branch of a token layer)."""
+    D, F = cfg.d_model, cfg.d_mlp
+    kvw = cfg.kv_heads * cfg.d_head
+    qw = D + 2 * kvw
+    n = D * qw + qw + D * D + D + 2 * D * F + F + D + 4 * D
+    if token_layer and cfg.context_mode == "xattn":
+        n += D * D + D + D * 2 * kvw + 2 * kvw + D * D + D
+    return n
+
+
+def _layer_matmul_params(cfg):
+    """Weights of the matrices one row of a block layer multiplies (flops = 2 x this per row)."""
+    D, F = cfg.d_model, cfg.d_mlp
+    return D * (D + 2 * cfg.kv_heads * cfg.d_head) + D * D + 2 * D * F
+
+
+def decode_bytes(cfg, G=None):
+    """Algorithmic bytes of the G - 1 decode steps of a generation of G tokens: a step at in-block
+    offset j reads the token decoder's weights, the final LayerNorm and the classifier once, each
+    row's token embedding and its P + j local entries per token layer; a block step (j = 0) also
+    reads the block decoder's weights, the context projection, each row's block embedding and the
+    n + 1 block-KV entries per block layer (n cached before the step)."""
+    G = cfg.gen_len if G is None else G
+    w = 2 if cfg.dtype == "bf16" else 4
+    D, V, B, L = cfg.d_model, cfg.vocab, cfg.batch, cfg.block_len
+    kv = 2 * cfg.kv_heads * cfg.d_head                     # K and V elements of one entry
+    Nb, Nt, lead, NC = cfg.n_block_layers, cfg.n_token_layers, cfg.lead, cfg.n_ctx
+    n0 = -(-max(cfg.prompt_len, L) // L)                   # prompt blocks after left padding
+    head = 2 * D + V * D
+    total = 0
+    for g in range(1, G):
+        j = g % L
+        if Nt:
+            total += w * (Nt * _layer_params(cfg, True) + head) + B * w * (D + Nt * kv * (lead + j))
+        if j == 0:
+            n = n0 + g // L - 1
+            blk = Nb * _layer_params(cfg) + (0 if Nt else head) + (2 * D + D * NC * D + NC * D if Nt else 0)
+            total += w * blk + B * w * (D + Nb * kv * (n + 1) + Nt * kv * lead)
+    return total
+
+
+def prefill_flops(cfg):
+    """Algorithmic FLOPs of a prefill: the block decoder's linear maps over every prompt block and
+    its causal attention, the token decoder over the prefix slots, the classifier of one token."""
+    D, V, B, L = cfg.d_model, cfg.vocab, cfg.batch, cfg.block_len
+    n = -(-max(cfg.prompt_len, L) // L)
+    Nb, Nt = cfg.n_block_layers, cfg.n_token_layers
+    f = 2 * B * n * Nb * _layer_matmul_params(cfg) + Nb * B * 4 * D * (n * (n + 1) // 2)
+    if Nt:
+        f += 2 * B * cfg.lead * Nt * _layer_matmul_params(cfg) + 2 * B * D * cfg.n_ctx * D
+    return f + 2 * B * V * D
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def describe(cfg):
     return (f"{cfg.name}: Block Transformer d={cfg.d_model} {cfg.n_block_layers}+{cfg.n_token_layers} layers "
             f"H={cfg.n_heads}{'' if cfg.kv_heads == cfg.n_heads else f' H_kv={cfg.kv_heads}'} MLP={cfg.d_mlp} "
@@ -38,16 +112,18 @@ def describe(cfg):
 
 
 class Runner:
-    def __init__(self, cfg, prompt_sized=False):
+    def __init__(self, cfg, prompt_sized=False, W=None):
         """prompt_sized: size the prefill activations for this prompt only (max_prompt_tokens), as a
-        server that knows its longest prompt would; the caches are sized for prompt + generation."""
+        server that knows its longest prompt would; the caches are sized for prompt + generation.
+        W: the model's weights if already drawn (wl.make_weights(cfg))."""
         import torch
 
         import bt_workloads as wl
         import hierarchical_global_local_amd as hg
         self.torch, self.cfg = torch, cfg
         self.G = cfg.gen_len
-        W = wl.make_weights(cfg)
+        if W is None:
+            W = wl.make_weights(cfg)
         prompt = wl.make_prompt(cfg)
         Tp = wl.padded_len(cfg, cfg.prompt_len)
         self.model = hg.BlockTransformer(cfg, W, max_batch=cfg.batch, max_tokens=Tp + self.G,
@@ -282,47 +358,72 @@ def cpu_baseline(cfg, rows, tokens):
     return {"value": round(rows * tokens / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{cfg.name}: rows 0..{rows - 1} of the batch, full {cfg.prompt_len}-token prompt, "
                       f"{tokens} generated tokens (numpy fp32 incremental path), {dt:.1f} s wall",
-            "host": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+            "host": cpu_model(), "host_cpus": os.cpu_count(), "blas_threads": int(threads)}
 
 
-def batch_sweep(args):
-    """Throughput against batch size at one prompt / generation shape (the pages measure both
-    models at their largest batch and report batch sensitivity).  Workspaces are sized for the
-    prompt (max_prompt_tokens) so the batch is bounded by the caches; points that do not fit in HBM
-    are reported as such."""
+def sweep_points(base, batches, van=None, van_batches=(), cache=None):
+    """Generated tokens/s against batch size at one prompt / generation shape (the pages measure
+    both models at their largest batch and report batch sensitivity).  Workspaces are sized for the
+    prompt (max_prompt_tokens) so that the batch is bounded by the caches; one untimed and one
+    timed generation per point.  cache: {(model name, batch): tokens/s} measured elsewhere in this
+    run, reused instead of measured again."""
     import torch
 
     import bt_workloads as wl
+    rows = []
+    for cfg0, bs in ((base, batches), (van, van_batches)):
+        if cfg0 is None or not bs:
+            continue
+        W = wl.make_weights(cfg0)
+        for B in bs:
+            cfg = cfg0.with_(batch=int(B))
+            rec = {"model": cfg0.name, "batch": int(B)}
+            if cache and (cfg0.name, int(B)) in cache:
+                rec.update(cache[(cfg0.name, int(B))])
+                rec["note"] = "measured above in this run"
+            else:
+                try:
+                    r = Runner(cfg, prompt_sized=True, W=W)
+                    t = r.timed(1, 1)
+                    rec.update(tokens_per_s=round(cfg.batch * cfg.gen_len / (t["ms_per_step"] * 1e-3), 1),
+                               ms_per_step=round(t["ms_per_step"], 2), prefill_ms=round(t["prefill_ms"], 2),
+                               decode_ms=round(t["decode_ms"], 2),
+                               workspace_gib=round(r.model.workspace.numel() / 2 ** 30, 2))
+                    del r
+                except torch.cuda.OutOfMemoryError:
+                    rec["result"] = "does not fit in HBM"
+                torch.cuda.empty_cache()
+            log(f"[sweep] {rec}")
+            rows.append(rec)
+        del W
+    return rows
+
+
+def batch_sweep(args):
+    import bt_workloads as wl
     base = wl.get_config(args.sweep_config)
-    todo = [(base, int(b)) for b in args.batch_sweep.split(",")]
+    van = None
     if args.sweep_vanilla:
         van = wl.get_config({"c2_decode_heavy": "v2_vanilla_decode_heavy",
                              "c1_prefill_heavy": "v1_vanilla_prefill_heavy"}[args.sweep_config])
-        todo += [(van, int(b)) for b in args.sweep_vanilla.split(",")]
-    rows = []
-    for cfg0, B in todo:
-        cfg = cfg0.with_(batch=B)
-        rec = {"model": cfg0.name, "batch": B}
-        try:
-            r = Runner(cfg, prompt_sized=True)
-            t = r.timed(1, 1)
-            rec.update(tokens_per_s=round(B * cfg.gen_len / (t["ms_per_step"] * 1e-3), 1),
-                       decode_tokens_per_s=round(B * (cfg.gen_len - 1) / (t["decode_ms"] * 1e-3), 1),
-                       ms_per_step=round(t["ms_per_step"], 2), prefill_ms=round(t["prefill_ms"], 2),
-                       decode_ms=round(t["decode_ms"], 2),
-                       workspace_gib=round(r.model.workspace.numel() / 2 ** 30, 2))
-            del r
-        except torch.cuda.OutOfMemoryError:
-            rec["result"] = "does not fit in HBM"
-        torch.cuda.empty_cache()
-        log(f"[sweep] {rec}")
-        rows.append(rec)
+    rows = sweep_points(base, [int(b) for b in args.batch_sweep.split(",")], van,
+                        [int(b) for b in args.sweep_vanilla.split(",")] if args.sweep_vanilla else ())
     line = json.dumps({"batch_sweep": describe(base), "gen_len": base.gen_len, "prompt_len": base.prompt_len,
                        "points": rows})
     print(line, flush=True)
     if args.out:
         with open(args.out, "w") as f:
             f.write(line + "\n")
+
+
+# The pages' headline claim, restated (context only: other hardware, trained models, batch sizes not given).
+PAGES_CLAIM = {
+    "claim": "Block Transformer inference throughput 10 to 20 times that of vanilla (token-level) transformers "
+             "of equal perplexity, at the largest batch that fits in memory, prefill-heavy and decode-heavy",
+    "hardware": "NVIDIA H100 (throughput comparison), a single H100 for the wall-time breakdown; precision not stated",
+    "source": "summary page 'Block Transformer: Global-to-Local Language Modeling for Fast Inference', "
+              "abstract and §5 Main Quantitative Results (throughput comparison)",
+}
 
 
 def main():
@@ -343,8 +444,12 @@ def main():
                     help="HBM traffic of the dominant kernel from two rocprofv3 --pmc runs; writes profiles/")
     ap.add_argument("--kernel", default=None, help="kernel-name pattern for --traffic")
     ap.add_argument("--kernel-class", default="decode/gemm_qkv_up", help="kernel class of --kernel")
-    ap.add_argument("--compare-vanilla", action="store_true",
-                    help="also time token-level transformers of the same width and depth on the same kernels")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the token-level (vanilla) comparison and the batch sweep of the default line")
+    ap.add_argument("--compare-batches", default="1,64,1024,4096",
+                    help="batch sizes of the Block Transformer in the default line's sweep (decode-heavy shape)")
+    ap.add_argument("--compare-vanilla-batches", default="1,64,256,1024",
+                    help="batch sizes of the token-level model in the default line's sweep")
     ap.add_argument("--batch-sweep", default=None, metavar="B1,B2,...",
                     help="only sweep the batch size of --sweep-config (one untimed + one timed generation each) "
                          "and print one JSON line; with --sweep-vanilla also the token-level model")
@@ -387,21 +492,25 @@ def main():
         f"(prefill {t['prefill_ms']:.2f} ms, decode {t['decode_ms']:.2f} ms)")
     B, G = cfg.batch, cfg.gen_len
     value = B * G / (t["ms_per_step"] * 1e-3)
+    dec_gbps = decode_bytes(cfg) / (t["decode_ms"] * 1e-3) / 1e9
+    pre_tf = prefill_flops(cfg) / (t["prefill_ms"] * 1e-3) / 1e12
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(t["ms_per_step"], 3), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "compute": "bf16 weights; matrix operands and KV caches fp16 (exact for bf16 weights after a 2^8 "
-                   "pre-scale), fp32 accumulation, softmax, LayerNorm and residual stream",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 weights, fp16 MFMA operands",
+        "compute": "bf16 weights held as fp16 after a 2^8 pre-scale (exact for magnitudes in [2^-25, 256)); matrix "
+                   "operands and KV caches fp16; fp32 accumulation, softmax, LayerNorm and residual stream",
         "data": "synthetic (random-init N(0,0.02^2) weights, uniform random prompt ids)",
         "config": {"workload": describe(cfg), "global_batch": B, "seq_len": cfg.prompt_len, "gen_len": G},
         "prefill_ms": round(t["prefill_ms"], 3), "decode_ms": round(t["decode_ms"], 3),
+        "prefill_tflops": round(pre_tf, 2), "prefill_mfma_frac": round(pre_tf / MFMA_F16_PEAK_TFLOPS, 4),
+        "decode_hbm_gbps": round(dec_gbps, 1), "decode_hbm_frac": round(dec_gbps / HBM_PEAK_GBS, 4),
+        "rates_from": "algorithmic prefill FLOPs and decode bytes (weights once per step, KV once per use, no "
+                      "inter-kernel activations) over the timed phase durations",
         "roofline": None,
     }
     if not args.no_profile:
         prof, prof_ms = r.profiled(args.steps)
-        dec_bytes = sum(v["bytes"] for k, v in prof.items() if k.startswith("decode/"))
-        pre_flops = sum(v["flops"] for k, v in prof.items() if k.startswith("prefill/"))
         active = {k: v for k, v in prof.items() if v["launches"]}
         dominant = max(active, key=lambda k: active[k]["ms"])
         classes = {k: {"ms_per_step": round(v["ms"], 3), "launches": v["launches"],
@@ -409,14 +518,13 @@ def main():
                    for k, v in sorted(active.items(), key=lambda kv: -kv[1]["ms"])}
         for k, v in classes.items():
             log(f"[bench]   {k:28s} {v['ms_per_step']:9.3f} ms/step  {v['launches']:8.1f} launches  {v['rate']:9.1f} {v['unit']}")
-        result["prefill_tflops"] = round(pre_flops / (t["prefill_ms"] * 1e-3) / 1e12, 2)
-        result["decode_hbm_gbps"] = round(dec_bytes / (t["decode_ms"] * 1e-3) / 1e9, 1)
         result["roofline"] = roofline_of(dominant, prof[dominant])
         result["roofline"]["measured"] = ("HIP events on the library's stream around every launch of the class, "
                                           f"over a profiled repeat of the {args.steps} timed steps")
         if dominant in REPLAYABLE:
             # per-launch events add their own dispatch latency to short kernels: time the same kernel
-            # (same shape, weights cycled over the layers) launched back to back instead
+            # launched back to back instead, its operands cycled so that none is cache-resident from
+            # the previous launch (as inside a step)
             reps = 30 * (cfg.n_token_layers + cfg.n_block_layers)
             us = r.replay_us(REPLAYABLE[dominant], reps)
             roof = result["roofline"]
@@ -426,9 +534,9 @@ def main():
             roof["achieved"] = round(rate / 1e9 if roof["unit"] == "GB/s" else rate / 1e12, 2)
             roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
             roof["measured"] = (f"HIP events on the library's stream around {reps} back-to-back launches of the "
-                                f"class's kernel at the decode shape (bt_test_replay, weights cycled over all "
-                                f"layers of both decoders), after the timed steps; algorithmic bytes per launch from the profiled "
-                                f"repeat of the timed steps")
+                                f"class's kernel at the decode shape (bt_test_replay: weights cycled over all layers "
+                                f"of both decoders, activation operand cycled over distinct rows), after the timed "
+                                f"steps; algorithmic bytes per launch from the profiled repeat of the timed steps")
         tr = stored_traffic(dominant)
         if tr is not None:
             result["roofline"]["traffic"] = round(tr["traffic_bytes_per_launch"], 1)
@@ -438,45 +546,59 @@ def main():
         result["kernel_classes"] = classes
     del r
     torch.cuda.empty_cache()
+    measured = {(cfg.name, cfg.batch): {"tokens_per_s": round(value, 1)}}
     if args.decode_config != "none":
         c2 = wl.get_config(args.decode_config)
         log(f"[bench] {describe(c2)}")
         r2 = Runner(c2)
         t2 = r2.timed(1, 1)
         prof2, _ = r2.profiled(1)
-        d_bytes = sum(v["bytes"] for k, v in prof2.items() if k.startswith("decode/"))
-        att = prof2["decode/attn_block_decode"]
         dom2 = max((k for k in prof2 if prof2[k]["launches"]), key=lambda k: prof2[k]["ms"])
+        d2_gbps = decode_bytes(c2) / (t2["decode_ms"] * 1e-3) / 1e9
+        v2 = c2.batch * c2.gen_len / (t2["ms_per_step"] * 1e-3)
         result["decode_heavy"] = {
-            "workload": describe(c2), "value": round(c2.batch * c2.gen_len / (t2["ms_per_step"] * 1e-3), 1),
+            "workload": describe(c2), "value": round(v2, 1),
             "unit": "tokens/s", "ms_per_step": round(t2["ms_per_step"], 3),
             "prefill_ms": round(t2["prefill_ms"], 3), "decode_ms": round(t2["decode_ms"], 3),
             "decode_tokens_per_s": round(c2.batch * (c2.gen_len - 1) / (t2["decode_ms"] * 1e-3), 1),
-            "decode_hbm_gbps": round(d_bytes / (t2["decode_ms"] * 1e-3) / 1e9, 1),
+            "decode_hbm_gbps": round(d2_gbps, 1), "decode_hbm_frac": round(d2_gbps / HBM_PEAK_GBS, 4),
             "block_attn_decode": attn_replay_roofline(r2, c2),
             "dominant": roofline_of(dom2, prof2[dom2]),
         }
-        log(f"[bench] decode-heavy: {result['decode_heavy']['value']:.0f} tokens/s, "
-            f"decode {result['decode_heavy']['decode_hbm_gbps']} GB/s")
+        measured[(c2.name, c2.batch)] = {"tokens_per_s": round(v2, 1)}
+        log(f"[bench] decode-heavy: {v2:.0f} tokens/s, decode {d2_gbps:.1f} GB/s")
         del r2
         torch.cuda.empty_cache()
-    if args.compare_vanilla:
-        cmp = {}
-        for block_name, van_name in (("c1_prefill_heavy", "v1_vanilla_prefill_heavy"),
-                                     ("c2_decode_heavy", "v2_vanilla_decode_heavy")):
-            row = {}
-            for name in (block_name, van_name):
-                c = wl.get_config(name)
-                rr = Runner(c)
-                tt = rr.timed(1, 1)
-                row[name] = {"tokens_per_s": round(c.batch * c.gen_len / (tt["ms_per_step"] * 1e-3), 1),
-                             "prefill_ms": round(tt["prefill_ms"], 3), "decode_ms": round(tt["decode_ms"], 3)}
-                log(f"[bench] {name}: {row[name]}")
-                del rr
-                torch.cuda.empty_cache()
-            row["block_over_vanilla"] = round(row[block_name]["tokens_per_s"] / row[van_name]["tokens_per_s"], 2)
-            cmp[block_name] = row
+    if not args.no_compare:
+        # the pages' headline comparison: token-level transformers of the same width and total depth
+        # on the same kernels, at the prefill-heavy shape and over the decode-heavy batch sweep
+        van1 = wl.get_config("v1_vanilla_prefill_heavy")
+        rr = Runner(van1)
+        tt = rr.timed(1, 1)
+        v1 = van1.batch * van1.gen_len / (tt["ms_per_step"] * 1e-3)
+        del rr
+        torch.cuda.empty_cache()
+        log(f"[bench] {van1.name}: {v1:.0f} tokens/s")
+        base, van = wl.get_config("c2_decode_heavy"), wl.get_config("v2_vanilla_decode_heavy")
+        pts = sweep_points(base, [int(b) for b in args.compare_batches.split(",")] + [base.batch], van,
+                           [int(b) for b in args.compare_vanilla_batches.split(",")], cache=measured)
+        blk = {p["batch"]: p["tokens_per_s"] for p in pts if p["model"] == base.name and "tokens_per_s" in p}
+        vtk = {p["batch"]: p["tokens_per_s"] for p in pts if p["model"] == van.name and "tokens_per_s" in p}
+        cmp = {"prefill_heavy": {"block": round(value, 1), "vanilla": round(v1, 1),
+                                 "block_over_vanilla": round(value / v1, 2), "workloads": [cfg.name, van1.name]}}
+        if base.batch in blk and base.batch in vtk:
+            cmp["decode_heavy"] = {"block": blk[base.batch], "vanilla": vtk[base.batch],
+                                   "block_over_vanilla": round(blk[base.batch] / vtk[base.batch], 2),
+                                   "workloads": [base.name, van.name]}
+        if blk and vtk:
+            bb, bv = max(blk), max(vtk)
+            cmp["largest_batches_swept"] = {"block_batch": bb, "vanilla_batch": bv,
+                                            "block_over_vanilla": round(blk[bb] / vtk[bv], 2)}
         result["vanilla_comparison"] = cmp
+        result["batch_sweep"] = {"shape": f"decode-heavy: {base.prompt_len}-token prompts, {base.gen_len} generated; "
+                                          "one untimed + one timed generation per point, workspaces sized for the prompt",
+                                 "points": pts}
+        result["pages_claim"] = PAGES_CLAIM
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_rows, cfg.batch), min(args.cpu_tokens, cfg.gen_len))

@@ -14,8 +14,11 @@ LIB = os.path.join(PKG, "libbt.so")
 SOURCES = ["api.cpp", "kernels_misc.hip", "gemm.hip", "gemm_decode.hip", "attention.hip", "scratch.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: no packed fp32 VALU instructions in device code
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary VGPRs (kernels that run VALU math on MFMA
+#   results, such as the attention softmax, otherwise copy them out of and back into AGPRs)
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
+         "-Wno-unused-command-line-argument"]
 
 
 def _run(cmd):

@@ -1348,12 +1348,17 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
   for (int i = 0; i < reps && r == BT_OK; ++i) {
     if (kind == PK_GEMM_QKV) {
       // the decode step's [q|k|v|up] GEMM, cycling over the layers of both decoders (as many
-      // distinct weights as a decode step streams between two uses of one layer)
+      // distinct weights as a decode step streams between two uses of one layer) and over up to 64
+      // distinct row ranges of the LayerNorm outputs (prefill-sized buffers), so that neither operand
+      // is resident in a cache from the previous launch, as inside a decode step
       const int nl = lo.Nb + lo.Nt, l = i % nl;
       const LayerOff& w = l < lo.Nt ? lo.tok[l] : lo.blk[l - lo.Nt];
       const Epi ep = qkv_epi(h, w);
-      hipError_t e = launch_gemm(lo.f32, ln_buf(h, 0), ln_buf(h, 1), lo.D, P_(h, w.w1), h->B, w.n1 + lo.F, lo.D,
-                                 EPI_QKV_GELU, ep, h->st);
+      const int64_t rows16 = (int64_t)align_up((size_t)h->B, 16);
+      const int64_t na = std::max<int64_t>(1, std::min<int64_t>(64, lo.Mpad / rows16));
+      const size_t off = (size_t)((i / nl) % na) * rows16 * lo.D * lo.elem;
+      hipError_t e = launch_gemm(lo.f32, (char*)ln_buf(h, 0) + off, (char*)ln_buf(h, 1) + off, lo.D, P_(h, w.w1), h->B,
+                                 w.n1 + lo.F, lo.D, EPI_QKV_GELU, ep, h->st);
       if (e != hipSuccess) r = hip_fail(h, e, "replay gemm");
     } else if (kind == PK_LOCAL_OUT) {
       // the token decoder's fused local attention + [out|down] launch at the next local slot (not

@@ -3,7 +3,7 @@
 //  * k_rope_scatter: rotary embedding of prompt keys and scatter of K / V into the block-KV cache
 //    (keys [slot][dh]; values in groups of 8 slots, each group transposed [dh][8], so that the
 //    prefill P*V product and the decode value passes read 8 consecutive keys per 16-byte load).
-//  * k_flash_prefill: causal flash attention over block positions with MFMA (fp16 operands, fp32
+//  * k_flash_prefill2: causal flash attention over block positions with MFMA (fp16 operands, fp32
 //    softmax); computes S^T = K Q^T so that the probabilities come out of the MFMA already in the
 //    operand layout of O^T = V^T P^T, with no LDS round trip.
 //  * k_attn_decode_wave: memory-bound block-attention decode, fp16 multi-head: one wave per (row,
@@ -138,6 +138,7 @@ __global__ __launch_bounds__(256) void k_rope_scatter_v(const f16* __restrict__ 
   const int cnt = min(64, min(m, pg.nlim ? pg.nlim[cb] - s0 : m) - i0);
   if (cnt <= 0) return;
   // keys: items (slot si, chunk pair p < NC / 2)
+  uint32_t trk = 0u;
   for (int e = tid; e < cnt * (NC / 2); e += 256) {
     const int si = e / (NC / 2), p = e % (NC / 2), slot = s0 + i0 + si;
     const f16* kr = QKV + ((size_t)b * m + i0 + si) * qw + koff + 8 * p;
@@ -152,14 +153,15 @@ __global__ __launch_bounds__(256) void k_rope_scatter_v(const f16* __restrict__ 
         const int e2 = 2 * q + u;
         const float cs = u ? r.z : r.x, sn = u ? r.w : r.y;
         const float x1 = (float)a[e2], x2 = (float)c[e2];
-        oa[e2] = to_f16(x1 * cs - x2 * sn);
-        oc[e2] = to_f16(x2 * cs + x1 * sn);
+        oa[e2] = to_f16_trk(x1 * cs - x2 * sn, trk);
+        oc[e2] = to_f16_trk(x2 * cs + x1 * sn, trk);
       }
     }
     f16* kd = Kc + kv_key(pg, cb, hk, slot, Hkv, cap, DH) + 8 * p;
     *(half8*)kd = oa;
     *(half8*)(kd + HALF) = oc;
   }
+  clamp_note(trk);
   // values: rows of the tile into LDS (16 bytes per item), then 8-slot runs per dimension
   for (int e = tid; e < cnt * NC; e += 256) {
     const int si = e / NC, c = e % NC;
@@ -207,65 +209,51 @@ hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, 
 }
 
 // ---------------------------------------------------------------- MFMA flash prefill (fp16)
-// grid ceil(n/64) * H * B, 4 waves x 16 queries; query head h reads KV head h / (H / Hkv).  The
-// query tiles of one (row, head) run on one XCD, consecutively and longest first, so that the
+// The query tiles of one (row, head) run on one XCD, consecutively and longest first, so that the
 // row's keys and values come from that XCD's L2 after the first tile instead of from HBM.  Each
 // 64-key tile of K ([key][dh]) and V^T ([dh][key]) is loaded once per workgroup with coalesced
 // 16-byte loads into a double-buffered LDS stage (the next tile's loads are in flight while the
-// current one is used) and read by all four waves.  MFMA 16x16x32 layouts (lane l, g = l / 16):
+// current one is used) and read by all four waves.  S^T = K Q^T, so that the probabilities come out
+// of the MFMA already in the operand layout of O^T = V^T P^T.  MFMA 16x16x32 layouts (lane l,
+// g = l / 16):
 //   A operand: row l % 16, k = 8g..8g+7;  B operand: column l % 16, same k;
 //   result:    column l % 16, rows 4g..4g+3.
-template <int DH>
-__global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ QKV, int n, int H, int Hkv,
-                                                       const float2* __restrict__ rope, const f16* __restrict__ Kc,
-                                                       const f16* __restrict__ VTc, int cap, f16* __restrict__ ACT,
-                                                       int ld_act, float scale_log2, const int* __restrict__ rmap,
-                                                       KvPages pg) {
+// MFMA flash prefill with QG 16-query groups per wave (32 queries at head width 64): each key and
+// value fragment read from LDS serves every group, so the LDS traffic per MFMA drops by QG against
+// 16 queries per wave, and the per-tile softmax bookkeeping (running maxima, rescaling) is amortised
+// over QG times the scores.  grid ceil(n / (64 QG)) * H * B, 4 waves.  Further:
+//  * values are stored in LDS with the keys of each 32-key slice permuted so that the 8 keys a lane
+//    contributes to a P * V MFMA (keys 4g..4g+3 and 16+4g..16+4g+3 of the slice, the probabilities
+//    it holds) are contiguous: one 16-byte LDS read per value fragment;
+//  * the row sums come from an MFMA of a ones operand with the probabilities (no per-score adds);
+//  * the accumulators are rescaled only when some running maximum of the wave grew (rescaling by
+//    exp2(0) = 1 is exact, so skipping it changes nothing);
+//  * a wave skips the key tiles that lie entirely after its last query.
+template <int DH, int QG>
+__global__ __launch_bounds__(256) void k_flash_prefill2(const f16* __restrict__ QKV, int n, int H, int Hkv,
+                                                        const float2* __restrict__ rope, const f16* __restrict__ Kc,
+                                                        const f16* __restrict__ VTc, int cap, f16* __restrict__ ACT,
+                                                        int ld_act, float scale_log2, const int* __restrict__ rmap,
+                                                        KvPages pg) {
   constexpr int KS = DH / 32;   // 32-wide dh slices of q and k
   constexpr int MT = DH / 16;   // 16-row dh tiles of O^T
-  constexpr int KLD = DH + 8;   // LDS row strides (+16 B: conflict-free fragment reads)
+  constexpr int QT = 64 * QG;   // queries per workgroup (QG 16-query groups per wave)
+  constexpr int KLD = DH + 8;   // LDS row strides (+16 B)
   constexpr int VLD = 64 + 8;
   constexpr int CK = 64 * DH / 8 / 256;  // 16-byte chunks per thread of a K tile
   constexpr int CV = DH * 64 / 8 / 256;  // ... and of a V^T tile
   __shared__ __attribute__((aligned(16))) f16 Ks[2][64 * KLD];
   __shared__ __attribute__((aligned(16))) f16 Vs[2][DH * VLD];
 
-  const int nq = (n + 63) / 64, lt = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int nq = (n + QT - 1) / QT, lt = xcd_contiguous_tile(blockIdx.x, gridDim.x);
   const int pair = lt / nq, qt = nq - 1 - lt % nq;  // longest (latest) query tiles first
   const int h = pair % H, b = pair / H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int q0 = qt * 64 + wave * 16;
-  const int qi = q0 + c16;
-  const int qrow = min(qi, n - 1);
+  const int qw0 = qt * QT + wave * 16 * QG;  // first query of this wave
   const int cb = rmap ? rmap[b] : b, hk = h / (H / Hkv);
-  if (pg.nlim && qt * 64 >= pg.nlim[cb]) return;  // queries past the row's length: nothing reads them
+  if (pg.nlim && qt * QT >= pg.nlim[cb]) return;  // queries past the row's length: nothing reads them
 
-  // q^T fragments with the rotary embedding and the softmax scale (log2 units) folded in: lane
-  // holds dh indices 32*ks + 8g + e; the rotation partner (index +- DH/2) sits in slice ks +- KS/2
-  // of the same lane.
-  half8 qf[KS];
-  {
-    float x[KS][8];
-    const f16* qp = QKV + ((size_t)b * n + qrow) * (H + 2 * Hkv) * DH + h * DH;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load8(qp + 32 * ks + 8 * g, x[ks]);
-    const float2* rp = rope + (size_t)qrow * (DH / 2);
-#pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 cs = rp[32 * ks + 8 * g + e];
-        const float x1 = x[ks][e], x2 = x[ks + KS / 2][e];
-        qf[ks][e] = to_f16((x1 * cs.x - x2 * cs.y) * scale_log2);
-        qf[ks + KS / 2][e] = to_f16((x2 * cs.x + x1 * cs.y) * scale_log2);
-      }
-  }
-
-  // cooperative tile loads (keys beyond the cache capacity never occur: cap is a multiple of 64)
   half8 rk[CK], rv[CV];
-  // a 64-key tile is 8 value groups ([8][DH][8], contiguous; one page of a paged cache): item
-  // (group cc, dimension r) is 16 bytes at (cc * DH + r) * 8, consecutive lanes taking consecutive
-  // dimensions
   auto gload = [&](int kb) {
     const f16* __restrict__ Kt = Kc + kv_key(pg, cb, hk, kb, Hkv, cap, DH);
     const f16* __restrict__ Vt = VTc + kv_val(pg, cb, hk, 0, kb, Hkv, cap, DH);
@@ -280,6 +268,8 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
       rv[i] = *(const half8*)(Vt + ((size_t)cc * DH + r) * 8);
     }
   };
+  // value chunk cc (keys 8cc..8cc+7 of dimension r): its first four keys go to LDS column base,
+  // the last four to base + 8, base = 32 (cc / 4) + 16 (cc % 2) + 4 ((cc / 2) % 2)
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
@@ -289,98 +279,143 @@ __global__ __launch_bounds__(256) void k_flash_prefill(const f16* __restrict__ Q
 #pragma unroll
     for (int i = 0; i < CV; ++i) {
       const int c = tid + i * 256, r = c % DH, cc = c / DH;
-      *(half8*)&Vs[buf][r * VLD + cc * 8] = rv[i];
+      const int base = 32 * (cc >> 2) + 16 * (cc & 1) + 4 * ((cc >> 1) & 1);
+      half4 lo4, hi4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lo4[e] = rv[i][e], hi4[e] = rv[i][4 + e];
+      *(half4*)&Vs[buf][r * VLD + base] = lo4;
+      *(half4*)&Vs[buf][r * VLD + base + 8] = hi4;
     }
   };
 
-  float4_ o[MT];
+  float4_ o[QG][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) o[mt] = float4_{0.f, 0.f, 0.f, 0.f};
-  float mrun = -INFINITY, lrun = 0.f;
-  const int ntiles = qt + 1;  // key tiles 0..qt (causal)
+  for (int grp = 0; grp < QG; ++grp)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[grp][mt] = float4_{0.f, 0.f, 0.f, 0.f};
+  // running maxima; the row sums accumulate on the MFMA: a 16 x 32 operand of ones times P^T gives,
+  // in every lane, the sum of its query's 32 probabilities of the slice (the same fp16 values the
+  // P * V product uses)
+  float mrun[QG];
+  float4_ lacc[QG];
+#pragma unroll
+  for (int grp = 0; grp < QG; ++grp) mrun[grp] = -INFINITY, lacc[grp] = float4_{0.f, 0.f, 0.f, 0.f};
+  half8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (f16)1.0f;
+  const int kmax = min(n, qt * QT + QT) - 1;                  // last key any query here needs
+  const int ntiles = kmax / 64 + 1;
+  const int wtiles = qw0 <= kmax ? min(qw0 + 16 * QG - 1, kmax) / 64 + 1 : 0;  // tiles this wave uses
 
-  gload(0);
+  gload(0);  // the first key / value tile is in flight while the queries are prepared
+  // q^T fragments (rotary and softmax scale folded in), one set per query group
+  half8 qf[QG][KS];
+#pragma unroll
+  for (int grp = 0; grp < QG; ++grp) {
+    const int qrow = min(qw0 + 16 * grp + c16, n - 1);
+    float x[KS][8];
+    const f16* qp = QKV + ((size_t)b * n + qrow) * (H + 2 * Hkv) * DH + h * DH;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) load8(qp + 32 * ks + 8 * g, x[ks]);
+    const float2* rp = rope + (size_t)qrow * (DH / 2);
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 cs = rp[32 * ks + 8 * g + e];
+        const float x1 = x[ks][e], x2 = x[ks + KS / 2][e];
+        qf[grp][ks][e] = to_f16_bounded((x1 * cs.x - x2 * cs.y) * scale_log2);
+        qf[grp][ks + KS / 2][e] = to_f16_bounded((x2 * cs.x + x1 * cs.y) * scale_log2);
+      }
+  }
+
   sstore(0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1, kb = t * 64;
     if (t + 1 < ntiles) gload(kb + 64);
-    float4_ s[4];
+    if (t < wtiles) {
+      float4_ s[QG][4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      s[nt] = float4_{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < 4; ++nt) {
+        half8 kf[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const half8 kf = *(const half8*)&Ks[buf][(nt * 16 + c16) * KLD + 32 * ks + 8 * g];
-        s[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], s[nt], 0, 0, 0);
-      }
-    }
-    // causal mask (only the diagonal tile, the last one, has masked keys) and the tile maximum of
-    // this lane's query (the scores are already scaled, through q)
-    float mx = -INFINITY;
-    if (t == ntiles - 1) {
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const half8*)&Ks[buf][(nt * 16 + c16) * KLD + 32 * ks + 8 * g];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+        for (int grp = 0; grp < QG; ++grp) {
+          s[grp][nt] = float4_{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[nt][i] = kb + nt * 16 + 4 * g + i <= qi ? s[nt][i] : -INFINITY;
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[nt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrun, mx);
-    const float corr = __builtin_amdgcn_exp2f(mrun - mnew);
-    float ls = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[nt][i] - mnew);
-        s[nt][i] = p;
-        ls += p;
-      }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    lrun = lrun * corr + ls;
-    mrun = mnew;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] *= corr;
-    // O^T += V^T P^T over two 32-key slices; slot e of the k dimension is key
-    // 32*sl + 4g + e (e < 4) or 32*sl + 16 + 4g + (e - 4), for both operands.
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      half8 pf;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = (f16)s[2 * sl][e];
-        pf[4 + e] = (f16)s[2 * sl + 1][e];
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f16* vp = &Vs[buf][(mt * 16 + c16) * VLD + 32 * sl + 4 * g];
-        const half4 v0 = *(const half4*)vp;
-        const half4 v1 = *(const half4*)(vp + 16);
-        half8 vf;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[e] = v0[e];
-          vf[4 + e] = v1[e];
+          for (int ks = 0; ks < KS; ++ks)
+            s[grp][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qf[grp][ks], s[grp][nt], 0, 0, 0);
         }
-        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, o[mt], 0, 0, 0);
+      }
+      if (kb + 63 > qw0) {  // the tile reaches past the wave's first query: causal mask
+#pragma unroll
+        for (int grp = 0; grp < QG; ++grp)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              s[grp][nt][i] = kb + nt * 16 + 4 * g + i <= qw0 + 16 * grp + c16 ? s[grp][nt][i] : -INFINITY;
+      }
+#pragma unroll
+      for (int grp = 0; grp < QG; ++grp) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) mx = fmaxf(fmaxf(mx, fmaxf(s[grp][nt][0], s[grp][nt][1])), fmaxf(s[grp][nt][2], s[grp][nt][3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(mrun[grp], mx);
+        const float corr = __builtin_amdgcn_exp2f(mrun[grp] - mnew);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[grp][nt][i] = __builtin_amdgcn_exp2f(s[grp][nt][i] - mnew);
+        mrun[grp] = mnew;
+        // corr is exactly 1 where the maximum did not grow: rescale only if some lane's did
+        if (__ballot(corr != 1.0f) != 0ull) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) o[grp][mt] *= corr;
+          lacc[grp] *= corr;
+        }
+      }
+      // O^T += V^T P^T over two 32-key slices
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        half8 pf[QG];
+#pragma unroll
+        for (int grp = 0; grp < QG; ++grp)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pf[grp][e] = (f16)s[grp][2 * sl][e];
+            pf[grp][4 + e] = (f16)s[grp][2 * sl + 1][e];
+          }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const half8 vf = *(const half8*)&Vs[buf][(mt * 16 + c16) * VLD + 32 * sl + 8 * g];
+#pragma unroll
+          for (int grp = 0; grp < QG; ++grp)
+            o[grp][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[grp], o[grp][mt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int grp = 0; grp < QG; ++grp)
+          lacc[grp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[grp], lacc[grp], 0, 0, 0);
       }
     }
     if (t + 1 < ntiles) sstore(buf ^ 1);
     __syncthreads();
   }
-  if (qi < n) {
-    const float inv = 1.0f / lrun;
-    const int row = b * n + qi;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      store4(ACT, frag_off(row, h * DH + mt * 16 + 4 * g, ld_act), o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv,
-             o[mt][3] * inv);
+  for (int grp = 0; grp < QG; ++grp) {
+    const int qi = qw0 + 16 * grp + c16;
+    if (qi < n) {
+      const float inv = 1.0f / lacc[grp][0];
+      const int row = b * n + qi;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        store4_bounded(ACT, frag_off(row, h * DH + mt * 16 + 4 * g, ld_act), o[grp][mt][0] * inv,
+                       o[grp][mt][1] * inv, o[grp][mt][2] * inv, o[grp][mt][3] * inv);
+    }
   }
 }
 
@@ -445,13 +480,17 @@ hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int
                        (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale, rmap, pg);
     return hipGetLastError();
   }
-  dim3 grid((n + 63) / 64 * H * B);
-  if (dh == 64)
-    hipLaunchKernelGGL(k_flash_prefill<64>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
-                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
+  // 32 queries per wave except for head width 64 below 2048 positions, where the 64-query
+  // workgroups' shorter tile ranges measured faster (more workgroups, less causal imbalance)
+  if (dh == 64 && n < 2048)
+    hipLaunchKernelGGL((k_flash_prefill2<64, 1>), dim3((n + 63) / 64 * H * B), dim3(256), 0, st, (const f16*)QKV, n,
+                       H, Hkv, rope, (const f16*)Kc, (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
+  else if (dh == 64)
+    hipLaunchKernelGGL((k_flash_prefill2<64, 2>), dim3((n + 127) / 128 * H * B), dim3(256), 0, st, (const f16*)QKV, n,
+                       H, Hkv, rope, (const f16*)Kc, (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
   else if (dh == 128)
-    hipLaunchKernelGGL(k_flash_prefill<128>, grid, dim3(256), 0, st, (const f16*)QKV, n, H, Hkv, rope, (const f16*)Kc,
-                       (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
+    hipLaunchKernelGGL((k_flash_prefill2<128, 2>), dim3((n + 127) / 128 * H * B), dim3(256), 0, st, (const f16*)QKV, n,
+                       H, Hkv, rope, (const f16*)Kc, (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -882,7 +921,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
   if (nsplit == 1) {
     half8 o;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) o[r] = to_f16(acc[r] / l);
+    for (int r = 0; r < 8; ++r) o[r] = to_f16_bounded(acc[r] / l);
     *(half8*)(ACT + frag_off(b, h * DH + 8 * pp, ld_act)) = o;
   } else {
     float* q = part + ((size_t)bh * nsplit + s) * (DH + 2);
@@ -922,7 +961,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
 // so that lane group g ends up holding the probabilities of 8 consecutive keys of each 32-key
 // slice -- exactly its B operand of the P V product -- and its V^T operand is one 16-byte read of
 // the same 8 keys; the probabilities never leave registers.  Keys past the cached range get score -inf and value 0; the new entry (slot n, appended by
-// split 0) joins the softmax at the end, from registers.  MFMA layouts as in k_flash_prefill.
+// split 0) joins the softmax at the end, from registers.  MFMA layouts as in k_flash_prefill2.
 template <int DH, int WPU, bool PAGED>
 __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict__ QKV, const int* __restrict__ n_ptr,
                                                           int B, int H, int Hkv, const float2* __restrict__ rope,
@@ -1018,7 +1057,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) VTc[vofs + (size_t)(16 * mt + 4 * g + i) * vstr] = to_f16(vn[mt][i]);
+        for (int i = 0; i < 4; ++i) VTc[vofs + (size_t)(16 * mt + 4 * g + i) * vstr] = to_f16_bounded(vn[mt][i]);
     }
   }
 
@@ -1115,8 +1154,8 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
       half8 pf;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pf[e] = to_f16(sv[2 * sl][e]);
-        pf[4 + e] = to_f16(sv[2 * sl + 1][e]);
+        pf[e] = to_f16_bounded(sv[2 * sl][e]);
+        pf[4 + e] = to_f16_bounded(sv[2 * sl + 1][e]);
       }
       const bool tail = 32 * sl + 8 * g + 8 > lim;  // values past the cached keys must be 0, not junk
 #pragma unroll
@@ -1162,7 +1201,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
           O += f * so[w][cc][d];
         }
       if (nsplit == 1) {
-        ACT[frag_off(b, h * DH + d, ld_act)] = to_f16(O / L);
+        ACT[frag_off(b, h * DH + d, ld_act)] = to_f16_bounded(O / L);
       } else {
         float* pp = part + (((size_t)b * H + h) * nsplit + s) * (DH + 2);
         pp[2 + d] = O;
@@ -1176,7 +1215,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_mfma(const f16* __restrict_
     const float inv = 1.0f / l;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      store4(ACT, frag_off(b, hq * DH + 16 * mt + 4 * g, ld_act), o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv,
+      store4_bounded(ACT, frag_off(b, hq * DH + 16 * mt + 4 * g, ld_act), o[mt][0] * inv, o[mt][1] * inv, o[mt][2] * inv,
              o[mt][3] * inv);
   } else {
     float* pp = part + (((size_t)b * H + hq) * nsplit + s) * (DH + 2);

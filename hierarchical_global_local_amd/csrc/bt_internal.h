@@ -188,8 +188,11 @@ struct SkinnyPlan {
   bool ok;             // the shape runs on the skinny kernel
   int mg, mw, ng, kw;  // row groups per wave, waves along M, column groups per wave, waves along K
   int splits;          // K splits over workgroups (EPI_RESID)
+  int rg = 1;          // workgroups along M (each 16 mg mw rows)
+  int depth = 2;       // K steps in flight per wave
 };
-SkinnyPlan skinny_plan(int M, int N, int K, EpiMode mode);
+// row_groups = false: one workgroup covers all M rows (the fused local attention + [out|down] launch)
+SkinnyPlan skinny_plan(int M, int N, int K, EpiMode mode, bool row_groups = true);
 hipError_t launch_gemm_skinny(const SkinnyPlan& p, const void* A1, const void* A2, const void* W, int M, int N, int K,
                               EpiMode mode, const Epi& ep, hipStream_t st);
 hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const void* W, int M, int N,

@@ -26,11 +26,27 @@ __device__ __forceinline__ float load_f32(const bf16_t* p) { return __uint_as_fl
 // own copy); BT_DEFINE_CLAMP_FLAG_ACCESS gives the host a reader for it.
 static __device__ unsigned int g_clamped;
 
-// fp16 stores saturate at the largest finite value instead of overflowing to infinity, and record
-// that they did.  (fmaxf/fminf return the other operand for a NaN, so a NaN becomes -65504.)
+// fp16 stores saturate at the largest finite value instead of overflowing to infinity.  (fmaxf and
+// fminf return the other operand for a NaN, so a NaN becomes -65504.)  This form does not record
+// the clamp: it is for values that cannot leave fp16's range by construction (attention outputs,
+// convex combinations of fp16 values; probabilities; queries scaled by at most 1).
+__device__ __forceinline__ f16 to_f16_bounded(float x) { return (f16)fminf(fmaxf(x, -65504.f), 65504.f); }
+
+// The same conversion, recording a clamp (magnitude beyond 65504, or NaN) in the flag.
 __device__ __forceinline__ f16 to_f16(float x) {
   if (!(fabsf(x) <= 65504.f)) g_clamped = 1u;
-  return (f16)fminf(fmaxf(x, -65504.f), 65504.f);
+  return to_f16_bounded(x);
+}
+
+// Branch-free form for kernels that convert many values per thread: trk keeps the largest
+// magnitude seen, as its bits shifted left by one (the sign dropped; infinities and NaN compare above
+// every finite value), and clamp_note(trk) at the end of the kernel sets the flag once.
+__device__ __forceinline__ f16 to_f16_trk(float x, uint32_t& trk) {
+  trk = max(trk, __float_as_uint(x) << 1);
+  return to_f16_bounded(x);
+}
+__device__ __forceinline__ void clamp_note(uint32_t trk) {
+  if (trk > (0x477fe000u << 1)) g_clamped = 1u;  // 0x477fe000: the bits of 65504.0f
 }
 
 // Host access to the translation unit's clamp flag: copies it to *value and, with reset, clears it
@@ -89,6 +105,30 @@ __device__ __forceinline__ void store4(f16* base, size_t idx, float a, float b, 
   w[1] = to_f16(b);
   w[2] = to_f16(c);
   w[3] = to_f16(d);
+  *(half4*)(base + idx) = w;
+}
+// ... with the clamp recorded in a tracker (see to_f16_trk)
+__device__ __forceinline__ void store4(float* base, size_t idx, float a, float b, float c, float d, uint32_t&) {
+  store4(base, idx, a, b, c, d);
+}
+__device__ __forceinline__ void store4(f16* base, size_t idx, float a, float b, float c, float d, uint32_t& trk) {
+  half4 w;
+  w[0] = to_f16_trk(a, trk);
+  w[1] = to_f16_trk(b, trk);
+  w[2] = to_f16_trk(c, trk);
+  w[3] = to_f16_trk(d, trk);
+  *(half4*)(base + idx) = w;
+}
+// ... of values bounded by construction (attention outputs)
+__device__ __forceinline__ void store4_bounded(float* base, size_t idx, float a, float b, float c, float d) {
+  store4(base, idx, a, b, c, d);
+}
+__device__ __forceinline__ void store4_bounded(f16* base, size_t idx, float a, float b, float c, float d) {
+  half4 w;
+  w[0] = to_f16_bounded(a);
+  w[1] = to_f16_bounded(b);
+  w[2] = to_f16_bounded(c);
+  w[3] = to_f16_bounded(d);
   *(half4*)(base + idx) = w;
 }
 

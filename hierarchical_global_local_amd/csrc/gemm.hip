@@ -171,6 +171,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
       // q|k|v columns: row-major [M][ld0]; GELU columns: the [attn | gelu] operand in fragment order
       const bool gelu = n0 >= ep.n_split;
       constexpr int CH = (BM * BN / 8 + 255) / 256;  // 8-wide chunks per thread
+      uint32_t trk = 0u;
 #pragma unroll
       for (int q = 0; q < CH; ++q) {
         const int c = tid + q * 256, rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
@@ -179,13 +180,14 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
         if (row < M) {
           half8 w;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) w[e] = to_f16(Cs[rl * CLD + cl + e]);
+          for (int e = 0; e < 8; ++e) w[e] = to_f16_trk(Cs[rl * CLD + cl + e], trk);
           if (gelu)
             *(half8*)((f16*)ep.out1 + frag_off(row, ep.act_col0 + (n0 - ep.n_split) + cl, ep.ld1)) = w;
           else
             *(half8*)((f16*)ep.out0 + (size_t)row * ep.ld0 + n0 + cl) = w;
         }
       }
+      clamp_note(trk);
     } else {
       constexpr int CH = (BM * BN / 4 + 255) / 256;  // 4-wide chunks per thread
       float* X = (float*)ep.out0;
@@ -423,6 +425,7 @@ __global__ __launch_bounds__(256, BN == 128 ? 2 : 1) void k_gemm_big(const f16* 
     const int r0 = m0 + s * SR;
     if constexpr (MODE == EPI_QKV_GELU) {
       constexpr int CH = SR * BN / 8 / 256;
+      uint32_t trk = 0u;
 #pragma unroll 4
       for (int q = 0; q < CH; ++q) {
         const int c = tid + q * 256, rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
@@ -431,15 +434,16 @@ __global__ __launch_bounds__(256, BN == 128 ? 2 : 1) void k_gemm_big(const f16* 
           half8 w;
           if (gelu) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = to_f16(gelu_erf(Cs[rl * CLD + cl + e]));
+            for (int e = 0; e < 8; ++e) w[e] = to_f16_trk(gelu_erf(Cs[rl * CLD + cl + e]), trk);
             *(half8*)((f16*)ep.out1 + frag_off(row, ep.act_col0 + (n0 - ep.n_split) + cl, ep.ld1)) = w;
           } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = to_f16(Cs[rl * CLD + cl + e]);
+            for (int e = 0; e < 8; ++e) w[e] = to_f16_trk(Cs[rl * CLD + cl + e], trk);
             *(half8*)((f16*)ep.out0 + (size_t)row * ep.ld0 + n0 + cl) = w;
           }
         }
       }
+      clamp_note(trk);
     } else {
       // residual rows in groups of 8 float4 per thread: all loads of a group before its stores
       constexpr int CH = SR * BN / 4 / 256, G = 8;

@@ -387,6 +387,7 @@ __global__ __launch_bounds__(256) void k_layernorm_g16(const float* __restrict__
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, grp = blockIdx.x;
   const int nch = D >> 2;
   float4 g1[CPT], b1[CPT], g2[CPT], b2[CPT], v[4][CPT];
+  uint32_t trk = 0u;
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const int cc = 4 * min(lane + 64 * j, nch - 1);
@@ -430,13 +431,14 @@ __global__ __launch_bounds__(256) void k_layernorm_g16(const float* __restrict__
         const float y2 = (v[rr][j].z - mean) * rstd, y3 = (v[rr][j].w - mean) * rstd;
         const size_t o = frag_off(r, 4 * c, D);
         store4(tiles[0], o, y0 * g1[j].x + b1[j].x, y1 * g1[j].y + b1[j].y, y2 * g1[j].z + b1[j].z,
-               y3 * g1[j].w + b1[j].w);
+               y3 * g1[j].w + b1[j].w, trk);
         if (o2)
           store4(tiles[1], o, y0 * g2[j].x + b2[j].x, y1 * g2[j].y + b2[j].y, y2 * g2[j].z + b2[j].z,
-                 y3 * g2[j].w + b2[j].w);
+                 y3 * g2[j].w + b2[j].w, trk);
       }
     }
   }
+  clamp_note(trk);
   __syncthreads();
   const size_t base = (size_t)grp * 16 * D;
   for (int i = threadIdx.x; i < 2 * D; i += 256) {  // 16 D halves = 2 D chunks of 16 bytes

@@ -37,7 +37,8 @@ int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* la
 /* Launch again, `reps` times back to back on the handle's stream, the kernel of one decode launch
  * class at the batch of the last prefill, for timing it without per-launch events.  kind (profile
  * class index): 2 = the decode [q|k|v|up] GEMM, cycling over the weights of all token- and
- * block-decoder layers; 8 = block-attention decode at the current block-KV length, cycling over
+ * block-decoder layers and over up to 64 row ranges of the LayerNorm outputs (operands not left in a
+ * cache by the previous launch); 8 = block-attention decode at the current block-KV length, cycling over
  * the block-decoder layers; 12 = the token decoder's local attention inside its [out|down] GEMM
  * (see bt_test_fuse_local) at the next local slot, cycling over the token-decoder layers
  * (BT_ERR_UNSUPPORTED where decode steps do not run it).  Only activations and split-K partials
