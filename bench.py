@@ -215,8 +215,10 @@ def attn_replay_roofline(runner, cfg):
     D, B, kvw = cfg.d_model, cfg.batch, cfg.kv_heads * cfg.d_head
     per_launch = B * n * kvw * 2 * 2 + B * (2 * D + 4 * kvw) * 2
     achieved = per_launch / (us * 1e-6) / 1e9
+    tr = stored_traffic("decode/attn_block_decode")
     return {"kernel_class": "decode/attn_block_decode", "bound": "hbm", "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": round(tr["traffic_bytes_per_launch"], 1) if tr and tr.get("workload") == cfg.name else None,
             "block_kv_entries": n, "avg_launch_us": round(us, 3), "algorithmic_per_launch": per_launch,
             "measured": f"HIP events around {reps} back-to-back launches (bt_test_replay) at n = {n}"}
 
@@ -242,7 +244,6 @@ PROFILES = os.path.join(ROOT, "profiles")
 def traffic_json(kernel_class):
     """Counter-measured traffic of a decode kernel class, e.g. profiles/traffic_decode_gemm_qkv_up.json."""
     return os.path.join(PROFILES, "traffic_" + kernel_class.replace("/", "_") + ".json")
-GEMM_SOURCE = os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", "gemm_decode.hip")
 
 
 def _rocprof_db(d):
@@ -253,8 +254,11 @@ def _rocprof_db(d):
     return found[0]
 
 
-def summarize_rocprof(d, top=25):
-    """Per-kernel totals of a rocprofv3 --kernel-trace run (the same figures --stats reports)."""
+def summarize_rocprof(d, top=25, run=32):
+    """Per-kernel totals of a rocprofv3 --kernel-trace run (the same figures --stats reports), then,
+    for the kernels with the most time, the launches made back to back (runs of at least `run`
+    consecutive dispatches of the same kernel: bt_test_replay) separated from those inside the
+    generation steps."""
     import sqlite3
     cur = sqlite3.connect(_rocprof_db(d)).cursor()
     rows = list(cur.execute("select name, count(*), sum(end-start), avg(end-start), min(end-start), max(end-start) "
@@ -263,7 +267,55 @@ def summarize_rocprof(d, top=25):
     out = [f"{'total_ms':>10} {'pct':>6} {'calls':>7} {'avg_us':>9} {'min_us':>9} {'max_us':>9}  kernel"]
     for name, n, tot, avg, mn, mx in rows[:top]:
         out.append(f"{tot / 1e6:10.3f} {100 * tot / total:6.2f} {n:7d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f}  {name[:140]}")
+    seq = list(cur.execute("select name, end - start from kernels order by start"))
+    groups, i = {}, 0
+    while i < len(seq):
+        j = i
+        while j < len(seq) and seq[j][0] == seq[i][0]:
+            j += 1
+        key = "back_to_back" if j - i >= run else "in_step"
+        g = groups.setdefault(seq[i][0], {"in_step": [], "back_to_back": []})
+        g[key] += [t for _, t in seq[i:j]]
+        i = j
+    out.append(f"# launches in runs of >= {run} consecutive dispatches of one kernel (back to back) vs the rest:")
+    out.append(f"{'in_step_calls':>13} {'in_step_avg_us':>14} {'b2b_calls':>9} {'b2b_avg_us':>10}  kernel")
+    for name, *_ in rows[:8]:
+        g = groups[name]
+        a, bb = g["in_step"], g["back_to_back"]
+        out.append(f"{len(a):13d} {sum(a) / max(len(a), 1) / 1e3:14.2f} {len(bb):9d} "
+                   f"{(sum(bb) / len(bb) / 1e3 if bb else 0.0):10.2f}  {name[:140]}")
     return "\n".join(out)
+
+
+def mfma_from_counters(d, n_xcc=8, n_simd=1024):
+    """Per-kernel MFMA work and busy fraction from a rocprofv3 --pmc run with SQ_INSTS_VALU_MFMA_MOPS_F16,
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (one aggregated value per dispatch and counter):
+    flops = MOPS x 512 (the counter counts multiply-add operations / 512); GRBM_GUI_ACTIVE is summed
+    over the 8 XCDs, so the dispatch's clock cycles are GUI_ACTIVE / 8 (and / duration, the clock);
+    the busy cycles are summed over the 1024 SIMDs, so busy fraction = BUSY / (cycles x 1024)."""
+    import sqlite3
+    cur = sqlite3.connect(_rocprof_db(d)).cursor()
+    per = {}
+    for kname, disp, cname, value, dur in cur.execute(
+            "select kernel_name, dispatch_id, counter_name, sum(value), max(duration) from counters_collection "
+            "group by dispatch_id, counter_name"):
+        e = per.setdefault(kname, {}).setdefault(disp, {"duration_ns": float(dur)})
+        e[cname] = float(value)
+    res = []
+    for kname, disps in per.items():
+        v = list(disps.values())
+        mops = sum(x.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) for x in v)
+        if not mops:
+            continue
+        busy = sum(x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in v)
+        cyc = sum(x.get("GRBM_GUI_ACTIVE", 0.0) for x in v) / n_xcc
+        dur = sum(x["duration_ns"] for x in v)
+        n = len(v)
+        res.append({"kernel": kname, "dispatches": n, "mfma_flops_per_dispatch": 512.0 * mops / n,
+                    "avg_duration_us": dur / n / 1e3, "tflops": 512.0 * mops / (dur * 1e-9) / 1e12,
+                    "clock_ghz": cyc / dur, "mfma_busy": busy / max(cyc * n_simd, 1.0)})
+    res.sort(key=lambda r: -r["mfma_flops_per_dispatch"] * r["dispatches"])
+    return res
 
 
 def _counter_per_dispatch(d, counter):
@@ -277,17 +329,28 @@ def _counter_per_dispatch(d, counter):
     return per
 
 
-def source_hash(path=GEMM_SOURCE):
+# the source file holding each replayable kernel class and its launch configuration
+CLASS_SOURCE = {"decode/gemm_qkv_up": "gemm_decode.hip", "decode/local_attn_out": "gemm_decode.hip",
+                "decode/attn_block_decode": "attention.hip"}
+
+
+def source_hash(kernel_class):
+    """Hash of the kernel's source file and of the build flags: stored counter results are used only
+    while both are unchanged."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", CLASS_SOURCE[kernel_class]), "rb") as f:
+        h.update(f.read())
+    from hierarchical_global_local_amd import build as _b
+    h.update(" ".join(_b.FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
-def traffic_from_counters(fetch_dir, write_dir, kernel_pattern, kernel_class):
+def traffic_from_counters(fetch_dir, write_dir, kernel_pattern, kernel_class, workload, command):
     """Average HBM bytes per dispatch of the kernel matching kernel_pattern (of class kernel_class),
     from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
     for the 1 GiB reference copy (--copy-calibration).  Written to profiles/ with the hash of the
-    decode GEMM source (which holds both decode GEMM kernels and their configuration tables)."""
+    kernel's source and the build flags."""
     fetch, write = _counter_per_dispatch(fetch_dir, "FETCH_SIZE"), _counter_per_dispatch(write_dir, "WRITE_SIZE")
     copy_f = next(v for k, v in fetch.items() if "copy" in k.lower() or "elementwise" in k.lower())
     copy_w = next(v for k, v in write.items() if "copy" in k.lower() or "elementwise" in k.lower())
@@ -301,19 +364,19 @@ def traffic_from_counters(fetch_dir, write_dir, kernel_pattern, kernel_class):
     wb = sum(write[name]) / len(write[name]) * 1024.0 * w_scale
     res = {"kernel": name, "dispatches": len(fetch[name]), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
            "traffic_bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
-           "kernel_class": kernel_class, "gemm_source_sha256_16": source_hash()}
+           "kernel_class": kernel_class, "workload": workload, "source_sha256_16": source_hash(kernel_class)}
     os.makedirs(PROFILES, exist_ok=True)
     out_json = traffic_json(kernel_class)
     with open(out_json, "w") as f:
         json.dump(res, f, indent=1)
     # readable summary of the two counter runs next to it
-    lines = [f"# HBM traffic of the {kernel_class} kernel ({name[:60]}...) in c1_prefill_heavy",
+    lines = [f"# HBM traffic of the {kernel_class} kernel ({name[:60]}...) in {workload}",
              "# commands (two passes, one counter each; the 1 GiB reference copy precedes the workload):",
              "#   cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT"]
     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        lines.append(f"#   rocprofv3 --pmc {c} -d {d} -o run -- python3 bench.py --steps 1 --warmup 0 "
-                     "--decode-config none --no-cpu-baseline --no-profile --copy-calibration")
-    lines.append(f"#   python bench.py --traffic {fetch_dir} {write_dir} --kernel {kernel_pattern} --kernel-class {kernel_class}")
+        lines.append(f"#   rocprofv3 --pmc {c} -d {d} -o run -- {command}")
+    lines.append(f"#   python bench.py --traffic {fetch_dir} {write_dir} --kernel {kernel_pattern} --kernel-class {kernel_class} "
+                 f"--workload {workload} --command '{command}'")
     lines.append(f"# scaling: FETCH_SIZE of the 1 GiB copy reads {max(copy_f):.0f} KiB (x{f_scale:.3f}), "
                  f"WRITE_SIZE {max(copy_w):.0f} KiB (x{w_scale:.3f})")
     lines.append("# per-kernel averages (KiB per dispatch, unscaled), the 10 most frequent kernels:")
@@ -322,20 +385,22 @@ def traffic_from_counters(fetch_dir, write_dir, kernel_pattern, kernel_class):
             lines.append(f"{cname}  {len(vs):6d}  {sum(vs) / len(vs):10.1f}  {k[:110]}")
     lines.append(f"# result ({os.path.relpath(out_json, ROOT)}): fetch {fb / 1e6:.2f} MB + write {wb / 1e6:.2f} MB "
                  f"per launch = {(fb + wb) / 1e6:.2f} MB")
-    with open(os.path.join(PROFILES, "counters_" + kernel_class.replace("/", "_") + "_c1.txt"), "w") as f:
+    with open(os.path.join(PROFILES, "counters_" + kernel_class.replace("/", "_") + "_" + workload + ".txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     return res
 
 
 def stored_traffic(kernel_class):
-    """Counter-measured bytes per launch of a decode kernel class, or None if absent or if the decode
-    GEMM source changed since the counters were taken."""
+    """Counter-measured bytes per launch of a decode kernel class, or None if absent or if the
+    kernel's source or the build flags changed since the counters were taken."""
+    if kernel_class not in CLASS_SOURCE:
+        return None
     try:
         with open(traffic_json(kernel_class)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    return t if t.get("gemm_source_sha256_16") == source_hash() else None
+    return t if t.get("source_sha256_16") == source_hash(kernel_class) else None
 
 
 def cpu_baseline(cfg, rows, tokens):
@@ -442,8 +507,12 @@ def main():
     ap.add_argument("--summarize", metavar="ROCPROF_DIR", help="print a kernel summary of a rocprofv3 run and exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="HBM traffic of the dominant kernel from two rocprofv3 --pmc runs; writes profiles/")
+    ap.add_argument("--mfma", metavar="ROCPROF_DIR",
+                    help="per-kernel MFMA flops and busy fraction of a rocprofv3 --pmc run and exit")
     ap.add_argument("--kernel", default=None, help="kernel-name pattern for --traffic")
     ap.add_argument("--kernel-class", default="decode/gemm_qkv_up", help="kernel class of --kernel")
+    ap.add_argument("--workload", default="c1_prefill_heavy", help="workload of the --traffic counter runs")
+    ap.add_argument("--command", default="", help="the bench command the --traffic counter runs profiled")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the token-level (vanilla) comparison and the batch sweep of the default line")
     ap.add_argument("--compare-batches", default="1,64,1024,4096",
@@ -462,9 +531,15 @@ def main():
     if args.summarize:
         print(summarize_rocprof(args.summarize))
         return
+    if args.mfma:
+        print(f"{'calls':>7} {'GFLOP/call':>11} {'avg_us':>9} {'TFLOP/s':>8} {'GHz':>5} {'busy':>6}  kernel")
+        for r in mfma_from_counters(args.mfma):
+            print(f"{r['dispatches']:7d} {r['mfma_flops_per_dispatch'] / 1e9:11.3f} {r['avg_duration_us']:9.2f} "
+                  f"{r['tflops']:8.1f} {r['clock_ghz']:5.2f} {r['mfma_busy']:6.3f}  {r['kernel'][:110]}")
+        return
     if args.traffic:
-        print(json.dumps(traffic_from_counters(args.traffic[0], args.traffic[1], args.kernel, args.kernel_class),
-                         indent=1))
+        print(json.dumps(traffic_from_counters(args.traffic[0], args.traffic[1], args.kernel, args.kernel_class,
+                                               args.workload, args.command), indent=1))
         return
     if args.batch_sweep:
         batch_sweep(args)
