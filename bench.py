@@ -7,6 +7,9 @@ classifier).  Inputs are resident in HBM before the timed region starts.  Prints
 Workloads (synthetic random-init weights N(0, 0.02^2), uniform random prompt ids):
   c1_prefill_heavy  d=768, 6+6 layers, L_B=4, P=1, V=50304, batch 64, 2048-token prompt, 128 generated
   c2_decode_heavy   same model, batch 256, 128-token prompt, 2048 generated (reported alongside)
+The default line also carries the roofline of the dominant kernel class, the token-level
+transformers of the same shapes on the same kernels, a batch sweep of the decode-heavy shape, and
+the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
