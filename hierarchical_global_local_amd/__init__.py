@@ -18,7 +18,8 @@ __all__ = ["BtConfig", "BlockTransformer", "lib", "pack_weights", "weight_names"
            "BT_FP32", "BT_BF16", "PROFILE_KINDS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libbt.so")
+# BT_LIBRARY names another build of the same library (for instance one with host sanitizers)
+_LIB_PATH = os.environ.get("BT_LIBRARY") or os.path.join(_PKG, "libbt.so")
 
 BT_FP32, BT_BF16 = 0, 1
 # bt_context_mode values of the workload names
