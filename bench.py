@@ -345,7 +345,8 @@ def source_hash(kernel_class):
     with open(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", CLASS_SOURCE[kernel_class]), "rb") as f:
         h.update(f.read())
     from hierarchical_global_local_amd import build as _b
-    h.update(" ".join(_b.FLAGS).encode())
+    # the code-generation flags only: include paths name this checkout's location
+    h.update(" ".join(f for f in _b.FLAGS if not f.startswith("-I")).encode())
     return h.hexdigest()[:16]
 
 
@@ -611,6 +612,14 @@ def main():
             rate = roof["algorithmic_per_launch"] / (us * 1e-6)
             roof["achieved"] = round(rate / 1e9 if roof["unit"] == "GB/s" else rate / 1e12, 2)
             roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+            # the fixed cost of one dependent launch on the same stream (an empty kernel launched back to
+            # back): even a kernel that moved its bytes at peak bandwidth would last this long plus
+            # bytes / peak, which bounds the fraction one launch of this size can reach
+            floor = r.replay_us("empty", reps)
+            roof["launch_floor_us"] = round(floor, 3)
+            per = roof["algorithmic_per_launch"]
+            peak_rate = roof["peak"] * (1e9 if roof["unit"] == "GB/s" else 1e12)
+            roof["frac_ceiling_at_floor"] = round(per / (floor * 1e-6 + per / peak_rate) / peak_rate, 4)
             roof["measured"] = (f"HIP events on the library's stream around {reps} back-to-back launches of the "
                                 f"class's kernel at the decode shape (bt_test_replay: weights cycled over all layers "
                                 f"of both decoders, activation operand cycled over distinct rows), after the timed "

@@ -316,9 +316,10 @@ class BlockTransformer:
         check(lib().bt_profile_enable(self.h, 1 if on else 0))
 
     def replay(self, kind: str, reps: int) -> None:
-        """Launch the decode kernel of class `kind` ("gemm_qkv_up" or "attn_block_decode") `reps` times
-        back to back on the model's stream (see bt_test_replay in include/bt_test.h)."""
-        check(lib().bt_test_replay(self.h, PROFILE_KINDS.index(kind), reps))
+        """Launch the decode kernel of class `kind` ("gemm_qkv_up", "attn_block_decode",
+        "local_attn_out", or "empty" for a kernel that does nothing) `reps` times back to back on the
+        model's stream (see bt_test_replay in include/bt_test.h)."""
+        check(lib().bt_test_replay(self.h, -1 if kind == "empty" else PROFILE_KINDS.index(kind), reps))
 
     def profile_read(self) -> Dict[str, dict]:
         """{phase/kind: {"ms", "launches", "bytes", "flops"}} since profile(True); phase is prefill or decode."""

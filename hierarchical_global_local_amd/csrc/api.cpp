@@ -1376,6 +1376,9 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps) {
                                               block_v(h, l), lo.ncap, P_(h, lo.ACT), lo.blk[l].k2, part_buf(h),
                                               part_cap(h), h->dec_nsplit, h->st, page_table(h), lo.ncap / 64);
       if (e != hipSuccess) r = hip_fail(h, e, "replay attention");
+    } else if (kind == -1) {
+      hipError_t e = launch_empty(256, h->st);
+      if (e != hipSuccess) r = hip_fail(h, e, "replay empty kernel");
     } else {
       r = fail(BT_ERR_INVALID_ARG, "kind not replayable");
     }

@@ -226,8 +226,12 @@ hipError_t launch_rope_scatter(bool f32, const void* QKV, int B, int m, int s0, 
 //    contributes to a P * V MFMA (keys 4g..4g+3 and 16+4g..16+4g+3 of the slice, the probabilities
 //    it holds) are contiguous: one 16-byte LDS read per value fragment;
 //  * the row sums come from an MFMA of a ones operand with the probabilities (no per-score adds);
-//  * the accumulators are rescaled only when some running maximum of the wave grew (rescaling by
-//    exp2(0) = 1 is exact, so skipping it changes nothing);
+//  * the score MFMAs start from minus a per-query offset (the running maximum as of the last
+//    rescale), so no subtraction precedes the exp2, and the accumulators are rescaled only when a
+//    score exceeds its offset by more than 2^8 (probabilities up to 256 in fp16), not whenever a
+//    running maximum grows: the exp2 and the fp16 conversion are most of the per-score VALU work,
+//    which bounds this kernel at head width 64;
+//  * the per-lane maxima use the three-operand maximum (no quieting of the MFMA results);
 //  * a wave skips the key tiles that lie entirely after its last query.
 template <int DH, int QG>
 __global__ __launch_bounds__(256) void k_flash_prefill2(const f16* __restrict__ QKV, int n, int H, int Hkv,
@@ -293,13 +297,20 @@ __global__ __launch_bounds__(256) void k_flash_prefill2(const f16* __restrict__ 
   for (int grp = 0; grp < QG; ++grp)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[grp][mt] = float4_{0.f, 0.f, 0.f, 0.f};
-  // running maxima; the row sums accumulate on the MFMA: a 16 x 32 operand of ones times P^T gives,
-  // in every lane, the sum of its query's 32 probabilities of the slice (the same fp16 values the
-  // P * V product uses)
-  float mrun[QG];
+  // Scores are taken relative to an offset mref per query: the exact running maximum as of the last
+  // rescale (0 before the first tile).  The score MFMAs start from -mref, so they produce s - mref
+  // directly, and a tile is rescaled only when one of its scores exceeds mref by more than
+  // kSlackLog2 (or on the first tile, which sets mref exactly); otherwise its probabilities
+  // exp2(s - mref) are at most 2^kSlackLog2, well inside fp16, and the running sums stay as they are.
+  // The normalised output is the same softmax; only the common factor of each query's numerator and
+  // denominator differs.  The row sums accumulate on the MFMA: a 16 x 32 operand of ones times P^T
+  // gives, in every lane, the sum of its query's 32 probabilities of the slice (the same fp16 values
+  // the P * V product uses).
+  constexpr float kSlackLog2 = 8.f;
+  float mref[QG];
   float4_ lacc[QG];
 #pragma unroll
-  for (int grp = 0; grp < QG; ++grp) mrun[grp] = -INFINITY, lacc[grp] = float4_{0.f, 0.f, 0.f, 0.f};
+  for (int grp = 0; grp < QG; ++grp) mref[grp] = 0.f, lacc[grp] = float4_{0.f, 0.f, 0.f, 0.f};
   half8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (f16)1.0f;
@@ -343,7 +354,7 @@ __global__ __launch_bounds__(256) void k_flash_prefill2(const f16* __restrict__ 
         for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const half8*)&Ks[buf][(nt * 16 + c16) * KLD + 32 * ks + 8 * g];
 #pragma unroll
         for (int grp = 0; grp < QG; ++grp) {
-          s[grp][nt] = float4_{0.f, 0.f, 0.f, 0.f};
+          s[grp][nt] = float4_{-mref[grp], -mref[grp], -mref[grp], -mref[grp]};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
             s[grp][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qf[grp][ks], s[grp][nt], 0, 0, 0);
@@ -360,24 +371,34 @@ __global__ __launch_bounds__(256) void k_flash_prefill2(const f16* __restrict__ 
       }
 #pragma unroll
       for (int grp = 0; grp < QG; ++grp) {
+        // (elementwise maximum: three-operand instructions, no quieting of the MFMA results)
         float mx = -INFINITY;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) mx = fmaxf(fmaxf(mx, fmaxf(s[grp][nt][0], s[grp][nt][1])), fmaxf(s[grp][nt][2], s[grp][nt][3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(mrun[grp], mx);
-        const float corr = __builtin_amdgcn_exp2f(mrun[grp] - mnew);
+        for (int nt = 0; nt < 4; ++nt)
+          mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[grp][nt][0]),
+                                             __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[grp][nt][1], s[grp][nt][2]),
+                                                                           s[grp][nt][3]));
+        if (t == 0 || __ballot(mx > kSlackLog2) != 0ull) {
+          // every key tile of a wave holds a valid key for each of its queries, so the maximum is finite
+          mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16, 64));
+          mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+          const float d = t == 0 ? mx : fmaxf(mx, 0.f);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[grp][nt][i] -= d;
+          if (t != 0 && __ballot(d > 0.f) != 0ull) {
+            const float corr = __builtin_amdgcn_exp2f(-d);  // exactly 1 where d = 0
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) o[grp][mt] *= corr;
+            lacc[grp] *= corr;
+          }
+          mref[grp] += d;
+        }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[grp][nt][i] = __builtin_amdgcn_exp2f(s[grp][nt][i] - mnew);
-        mrun[grp] = mnew;
-        // corr is exactly 1 where the maximum did not grow: rescale only if some lane's did
-        if (__ballot(corr != 1.0f) != 0ull) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) o[grp][mt] *= corr;
-          lacc[grp] *= corr;
-        }
+          for (int i = 0; i < 4; ++i) s[grp][nt][i] = __builtin_amdgcn_exp2f(s[grp][nt][i]);
       }
       // O^T += V^T P^T over two 32-key slices
 #pragma unroll
@@ -480,12 +501,8 @@ hipError_t launch_prefill_attention(bool f32, const void* QKV, int B, int n, int
                        (const float*)Kc, (const float*)Vc, cap, (float*)ACT, ld_act, scale, rmap, pg);
     return hipGetLastError();
   }
-  // 32 queries per wave except for head width 64 below 2048 positions, where the 64-query
-  // workgroups' shorter tile ranges measured faster (more workgroups, less causal imbalance)
-  if (dh == 64 && n < 2048)
-    hipLaunchKernelGGL((k_flash_prefill2<64, 1>), dim3((n + 63) / 64 * H * B), dim3(256), 0, st, (const f16*)QKV, n,
-                       H, Hkv, rope, (const f16*)Kc, (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
-  else if (dh == 64)
+  // 32 queries per wave (measured faster than 16 at 512 and 8192 positions)
+  if (dh == 64)
     hipLaunchKernelGGL((k_flash_prefill2<64, 2>), dim3((n + 127) / 128 * H * B), dim3(256), 0, st, (const f16*)QKV, n,
                        H, Hkv, rope, (const f16*)Kc, (const f16*)Vc, cap, (f16*)ACT, ld_act, scale * kLog2e, rmap, pg);
   else if (dh == 128)

@@ -127,6 +127,7 @@ hipError_t clamp_flag_misc(unsigned int* value, bool reset, hipStream_t st);
 hipError_t clamp_flag_gemm(unsigned int* value, bool reset, hipStream_t st);
 hipError_t clamp_flag_gemm_decode(unsigned int* value, bool reset, hipStream_t st);
 hipError_t clamp_flag_attention(unsigned int* value, bool reset, hipStream_t st);
+hipError_t launch_empty(int workgroups, hipStream_t st);
 hipError_t launch_to_f32(const void* src, bool src_bf16, int n, float* dst, hipStream_t st);
 hipError_t launch_add_f32(float* dst, const float* a, int n, hipStream_t st);
 // X[b][:] = base[:] (+ add[b * add_ld + :] when add is not null), rows b < B of width D

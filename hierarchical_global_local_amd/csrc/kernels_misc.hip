@@ -665,6 +665,16 @@ hipError_t launch_finalize(const unsigned long long* keys, int nparts, int ld, i
   return hipGetLastError();
 }
 
+// A kernel that does nothing: its back-to-back launches time the fixed cost of one dependent launch
+// on the stream (dispatch, workgroup launch, end-of-kernel release), the floor under every decode
+// kernel's duration.
+__global__ __launch_bounds__(256) void k_empty() {}
+
+hipError_t launch_empty(int workgroups, hipStream_t st) {
+  hipLaunchKernelGGL(k_empty, dim3(workgroups), dim3(256), 0, st);
+  return hipGetLastError();
+}
+
 BT_DEFINE_CLAMP_FLAG_ACCESS(clamp_flag_misc)
 
 }  // namespace bt

@@ -41,7 +41,9 @@ int bt_profile_read(bt_handle* h, int32_t n_kinds, double* total_ms, int64_t* la
  * cache by the previous launch); 8 = block-attention decode at the current block-KV length, cycling over
  * the block-decoder layers; 12 = the token decoder's local attention inside its [out|down] GEMM
  * (see bt_test_fuse_local) at the next local slot, cycling over the token-decoder layers
- * (BT_ERR_UNSUPPORTED where decode steps do not run it).  Only activations and split-K partials
+ * (BT_ERR_UNSUPPORTED where decode steps do not run it); -1 = an empty kernel of 256 workgroups of
+ * 256 threads, whose back-to-back launches time the fixed cost of one dependent launch on the stream
+ * (the floor under the duration of every decode launch).  Only activations and split-K partials
  * are overwritten, plus the cache entry each kind appends (kind 8: the block-KV entry at the
  * current length; kind 12: the local-KV entry at the next local slot), which is not yet valid and is
  * written again by the next step that uses it, so decoding can continue afterwards.

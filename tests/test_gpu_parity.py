@@ -376,6 +376,7 @@ def test_kernel_replay_leaves_decoding_unchanged():
                 model.replay("gemm_qkv_up", 5)
                 model.replay("local_attn_out", 5)
                 model.replay("attn_block_decode", 5)
+                model.replay("empty", 5)
             model.decode_step(ids[g])
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy().T, ref)
