@@ -58,12 +58,13 @@ def _layer_matmul_params(cfg):
     return D * (D + 2 * cfg.kv_heads * cfg.d_head) + D * D + 2 * D * F
 
 
-def decode_bytes(cfg, G=None):
-    """Algorithmic bytes of the G - 1 decode steps of a generation of G tokens: a step at in-block
-    offset j reads the token decoder's weights, the final LayerNorm and the classifier once, each
-    row's token embedding and its P + j local entries per token layer; a block step (j = 0) also
-    reads the block decoder's weights, the context projection, each row's block embedding and the
-    n + 1 block-KV entries per block layer (n cached before the step)."""
+def decode_bytes_parts(cfg, G=None):
+    """Algorithmic bytes of the G - 1 decode steps of a generation of G tokens, by kind: a step at
+    in-block offset j reads the token decoder's weights, the final LayerNorm and the classifier once
+    ("weights"), each row's token embedding ("embeddings") and its P + j local entries per token
+    layer ("local_kv"); a block step (j = 0) also reads the block decoder's weights, the context
+    projection, each row's block embedding, the n + 1 block-KV entries per block layer ("block_kv",
+    n cached before the step) and the P new prefix entries per token layer."""
     G = cfg.gen_len if G is None else G
     w = 2 if cfg.dtype == "bf16" else 4
     D, V, B, L = cfg.d_model, cfg.vocab, cfg.batch, cfg.block_len
@@ -71,16 +72,26 @@ def decode_bytes(cfg, G=None):
     Nb, Nt, lead, NC = cfg.n_block_layers, cfg.n_token_layers, cfg.lead, cfg.n_ctx
     n0 = -(-max(cfg.prompt_len, L) // L)                   # prompt blocks after left padding
     head = 2 * D + V * D
-    total = 0
+    parts = {"weights": 0, "embeddings": 0, "local_kv": 0, "block_kv": 0}
     for g in range(1, G):
         j = g % L
         if Nt:
-            total += w * (Nt * _layer_params(cfg, True) + head) + B * w * (D + Nt * kv * (lead + j))
+            parts["weights"] += w * (Nt * _layer_params(cfg, True) + head)
+            parts["embeddings"] += B * w * D
+            parts["local_kv"] += B * w * Nt * kv * (lead + j)
         if j == 0:
             n = n0 + g // L - 1
-            blk = Nb * _layer_params(cfg) + (0 if Nt else head) + (2 * D + D * NC * D + NC * D if Nt else 0)
-            total += w * blk + B * w * (D + Nb * kv * (n + 1) + Nt * kv * lead)
-    return total
+            parts["weights"] += w * (Nb * _layer_params(cfg) + (0 if Nt else head) +
+                                     (2 * D + D * NC * D + NC * D if Nt else 0))
+            parts["embeddings"] += B * w * D
+            parts["block_kv"] += B * w * Nb * kv * (n + 1)
+            parts["local_kv"] += B * w * Nt * kv * lead
+    return parts
+
+
+def decode_bytes(cfg, G=None):
+    """Algorithmic bytes of the G - 1 decode steps of a generation of G tokens (decode_bytes_parts)."""
+    return sum(decode_bytes_parts(cfg, G).values())
 
 
 def prefill_flops(cfg):
@@ -389,9 +400,65 @@ def traffic_from_counters(fetch_dir, write_dir, kernel_pattern, kernel_class, wo
             lines.append(f"{cname}  {len(vs):6d}  {sum(vs) / len(vs):10.1f}  {k[:110]}")
     lines.append(f"# result ({os.path.relpath(out_json, ROOT)}): fetch {fb / 1e6:.2f} MB + write {wb / 1e6:.2f} MB "
                  f"per launch = {(fb + wb) / 1e6:.2f} MB")
+    # every decode kernel of the generation, for the decode phase's counter-measured rate
+    import bt_workloads as wl
+    cfg = wl.get_config(workload)
+    ds = decode_step_traffic(fetch_dir, write_dir, workload, f_scale, w_scale, cfg.gen_len - 1)
+    lines.append(f"# all {ds['dispatches']} decode dispatches of the generation ({ds['decode_steps']} steps, every kernel): "
+                 f"fetch {ds['fetch_bytes'] / 1e9:.2f} GB + write {ds['write_bytes'] / 1e9:.2f} GB = "
+                 f"{ds['traffic_bytes'] / 1e9:.2f} GB (profiles/traffic_decode_steps.json)")
     with open(os.path.join(PROFILES, "counters_" + kernel_class.replace("/", "_") + "_" + workload + ".txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     return res
+
+
+def _decode_phase_kib(d, counter):
+    """Sum of a counter (KiB) over the dispatches of the decode steps of one generation: those
+    after the prefill's greedy-id finalisation (the first k_finalize dispatch), and their count."""
+    import sqlite3
+    cur = sqlite3.connect(_rocprof_db(d)).cursor()
+    rows = list(cur.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection "
+                            "order by dispatch_id"))
+    first = min(r[0] for r in rows if "k_finalize" in r[1])
+    sel = [r for r in rows if r[0] > first and r[2].startswith(counter)]
+    return sum(float(r[3]) for r in sel), len({r[0] for r in sel})
+
+
+def all_sources_hash():
+    """Hash of every library source and header and of the code-generation flags."""
+    import hashlib
+    from hierarchical_global_local_amd import build as _b
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc"))):
+        with open(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(f for f in _b.FLAGS if not f.startswith("-I")).encode())
+    return h.hexdigest()[:16]
+
+
+def decode_step_traffic(fetch_dir, write_dir, workload, f_scale, w_scale, steps):
+    """HBM bytes of all decode steps of one generation (every kernel, counter-measured), stored for
+    the benchmark line's decode_counter_gbps."""
+    fk, nf = _decode_phase_kib(fetch_dir, "FETCH_SIZE")
+    wk, nw = _decode_phase_kib(write_dir, "WRITE_SIZE")
+    res = {"workload": workload, "decode_steps": steps, "dispatches": nf, "fetch_bytes": fk * 1024.0 * f_scale,
+           "write_bytes": wk * 1024.0 * w_scale, "traffic_bytes": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale,
+           "fetch_scale": f_scale, "write_scale": w_scale, "source_sha256_16": all_sources_hash()}
+    with open(os.path.join(PROFILES, "traffic_decode_steps.json"), "w") as f:
+        json.dump(res, f, indent=1)
+    return res
+
+
+def stored_decode_step_traffic(workload):
+    """The counter-measured bytes of all decode steps of one generation of `workload`, or None if
+    absent, taken on another workload, or taken before any library source or flag changed."""
+    try:
+        with open(os.path.join(PROFILES, "traffic_decode_steps.json")) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ok = t.get("workload") == workload and t.get("source_sha256_16") == all_sources_hash()
+    return t if ok else None
 
 
 def stored_traffic(kernel_class):
@@ -588,6 +655,16 @@ def main():
                       "inter-kernel activations) over the timed phase durations",
         "roofline": None,
     }
+    ds = stored_decode_step_traffic(cfg.name)
+    if ds is not None:
+        # every decode kernel's counter-measured HBM bytes (FETCH_SIZE + WRITE_SIZE of one generation,
+        # stored by --traffic) over the decode phase timed here
+        cg = ds["traffic_bytes"] / (t["decode_ms"] * 1e-3) / 1e9
+        result["decode_counter_gbps"] = round(cg, 1)
+        result["decode_counter_frac"] = round(cg / HBM_PEAK_GBS, 4)
+        result["decode_counter_source"] = ("profiles/traffic_decode_steps.json: FETCH_SIZE + WRITE_SIZE over the "
+                                           f"{ds['dispatches']} decode dispatches of one generation "
+                                           f"({ds['traffic_bytes'] / 1e9:.2f} GB)")
     if not args.no_profile:
         prof, prof_ms = r.profiled(args.steps)
         active = {k: v for k, v in prof.items() if v["launches"]}
