@@ -461,6 +461,25 @@ def stored_decode_step_traffic(workload):
     return t if ok else None
 
 
+def trace_in_step_us(workload, kernel_name):
+    """Average in-step duration (us) of a kernel in the committed trace summary of the workload's
+    bench command (profiles/kernels_<workload>.txt: launches outside back-to-back replays), or None."""
+    try:
+        with open(os.path.join(PROFILES, f"kernels_{workload}.txt")) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    try:
+        start = next(i for i, l in enumerate(lines) if l.lstrip().startswith("in_step_calls"))
+    except StopIteration:
+        return None
+    for l in lines[start + 1:]:
+        parts = l.split()
+        if len(parts) == 5 and kernel_name.startswith(parts[4]) and int(parts[0]) > 0:
+            return float(parts[1])
+    return None
+
+
 def stored_traffic(kernel_class):
     """Counter-measured bytes per launch of a decode kernel class, or None if absent or if the
     kernel's source or the build flags changed since the counters were taken."""
@@ -703,6 +722,15 @@ def main():
                                 f"steps; algorithmic bytes per launch from the profiled repeat of the timed steps")
         tr = stored_traffic(dominant)
         if tr is not None:
+            # the same kernel's in-step average from the committed trace of this command (taken with
+            # the counters, on the same kernel source): the duration inside the generation steps
+            tus = trace_in_step_us(cfg.name, tr["kernel"])
+            if tus is not None:
+                roof = result["roofline"]
+                peak_rate = roof["peak"] * (1e9 if roof["unit"] == "GB/s" else 1e12)
+                roof["in_step_trace_avg_launch_us"] = tus
+                roof["in_step_trace_frac"] = round(roof["algorithmic_per_launch"] / (tus * 1e-6) / peak_rate, 4)
+                roof["in_step_trace_source"] = f"profiles/kernels_{cfg.name}.txt"
             result["roofline"]["traffic"] = round(tr["traffic_bytes_per_launch"], 1)
             result["roofline"]["traffic_source"] = (os.path.relpath(traffic_json(dominant), ROOT) +
                                                     " (FETCH_SIZE + WRITE_SIZE)")

@@ -100,3 +100,18 @@ def test_stored_decode_traffic_is_tied_to_workload_and_sources(tmp_path, monkeyp
     rec["source_sha256_16"] = "0" * 16
     (tmp_path / "traffic_decode_steps.json").write_text(json.dumps(rec))
     assert bench.stored_decode_step_traffic("c1_prefill_heavy") is None
+
+
+def test_trace_in_step_duration_is_read_from_the_committed_summary(tmp_path, monkeypatch):
+    """The in-step average is the first column pair of the back-to-back table, matched by the
+    (possibly truncated) kernel name."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    (tmp_path / "kernels_c1_prefill_heavy.txt").write_text(
+        "# header\n  total_ms    pct   calls    avg_us    min_us    max_us  kernel\n"
+        "in_step_calls in_step_avg_us b2b_calls b2b_avg_us  kernel\n"
+        "         6678           5.21       370       5.02  _ZN2bt13k_gemm_skinnyILi4E\n"
+        "         5376           6.21         0       0.00  _ZN2bt10k_attn_outILi4E\n")
+    assert bench.trace_in_step_us("c1_prefill_heavy", "_ZN2bt13k_gemm_skinnyILi4ELi1E") == 5.21
+    assert bench.trace_in_step_us("c1_prefill_heavy", "_ZN2bt10k_attn_outILi4ELi1E") == 6.21
+    assert bench.trace_in_step_us("c1_prefill_heavy", "_ZN2bt11k_layernorm") is None
+    assert bench.trace_in_step_us("c2_decode_heavy", "_ZN2bt13k_gemm_skinnyILi4ELi1E") is None
