@@ -644,6 +644,9 @@ hipError_t launch_gemm(bool f32, const void* A1, const void* A2, int lda, const 
   // the classifier of a batch above the skinny kernel's 128 rows: the weights stream once
   if (mode == EPI_ARGMAX && M > 128 && K % 64 == 0 && N % 128 == 0)
     return launch_big_cfg<128, 3>(A1, A2, W, M, N, K, mode, ep, st);
+  // 65-128 rows: one row tile of 128 x 128 (skinny_plan leaves these shapes to this kernel)
+  if (mode == EPI_ARGMAX && M > 64 && K % 64 == 0 && N % 128 == 0)
+    return launch_mfma_cfg<128, 128, 2, 2, 1>(A1, A2, W, M, N, K, mode, ep, st);
   // LDS-tiled kernel: K % 64 == 0, N % 32 == 0 and n_split on a tile boundary (checked at plan time)
   const bool split_ok128 = (mode != EPI_QKV_GELU) || (ep.n_split % 128 == 0);
   if ((M > 1024 || (M >= 256 && mode == EPI_ARGMAX)) && N % 128 == 0 && split_ok128 && ep.splits == 1)
