@@ -474,16 +474,18 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
   return BT_OK;
 }
 
-// Partial count of the token decoder's fused local attention + [out|down] launch for one new
-// slot per row (attn_out_splits), 0 where it runs as two launches: fp32, head width other than
-// 64, cross-attention, or more rows than the partial buffer or the fused kernel take.
+// Partial count of the token decoder's fused local attention (and cross-attention) + [out|down]
+// launch for one new slot per row (attn_out_splits over the GELU columns' K range), 0 where it runs
+// as separate launches: fp32, head width other than 64, more rows than the partial buffer or the
+// fused kernel take, or cross-attention above 128 rows (there the 1024-thread workgroups have no
+// registers left to issue the cross-attention loads early: 164 instead of 160 ms of decode at 256
+// rows x 512 tokens, while at 64 and 128 rows the fused launch saves 19-20 %).
 int fused_local_splits(bt_handle* h, int m) {
   const Layout& lo = h->lo;
   const int rows = h->B * m;
-  if (m != 1 || !h->fuse_local || lo.f32 || lo.dh != 64 || lo.mode == BT_CTX_XATTN || rows > lo.rpart_rows ||
-      lo.Nt == 0)
-    return 0;
-  return attn_out_splits(rows, lo.D, lo.tok[0].k2, lo.H);
+  if (m != 1 || !h->fuse_local || lo.f32 || lo.dh != 64 || rows > lo.rpart_rows || lo.Nt == 0) return 0;
+  if (lo.mode == BT_CTX_XATTN && rows > 128) return 0;
+  return attn_out_splits(rows, lo.D, lo.D + lo.F, lo.H);
 }
 
 // Token layer l, one new slot s0 per row: local attention inside the [out|down] GEMM; its
@@ -504,13 +506,26 @@ int run_fused_local_out(bt_handle* h, int l, int s0, int splits) {
   ls.cap = lo.lcap;
   ls.rmap = h->rmap;
   ls.scale_log2 = 1.4426950408889634f / sqrtf((float)lo.dh);
+  ls.k_mlp = lo.D + lo.F;
+  if (lo.mode == BT_CTX_XATTN) {
+    // the cross-attention of this layer: its query columns follow q|k|v, its encoder keys and
+    // values are the layer's slice of the per-block K|V projection
+    ls.xkv = (const float*)P_(h, lo.xkv);
+    ls.xkv_ld = lo.xkv_ld;
+    ls.xkv_off = l * 2 * lo.Hkv * lo.dh;
+    ls.P = lo.P;
+    ls.xq_off = (int)lo.QW;
+  }
   const Epi ep = resid_epi(h, w, rows, splits);
   const double E = (double)lo.elem, D = lo.D, Bd = h->B, KVW = (double)lo.Hkv * lo.dh, F = lo.F;
   // weights, the GELU columns, q|k|v, cached K/V read and the new K/V written, the residual
   // stream read and written (fp32) and both biases
+  // (cross-attention: its query columns and the P encoder keys and values, fp32, per row)
+  const double xa = lo.mode == BT_CTX_XATTN ? rows * (D * E + lo.P * 2.0 * KVW * 4.0) : 0.0;
   Prof p(h, PK_LOCAL_OUT,
-         D * w.k2 * E + rows * F * E + (Bd * s0 * 2.0 * KVW + rows * (D + 4.0 * KVW)) * E + 8.0 * rows * D + 8.0 * D,
-         2.0 * rows * D * w.k2 + 4.0 * Bd * lo.H * lo.dh * (s0 + 1));
+         D * w.k2 * E + rows * F * E + (Bd * s0 * 2.0 * KVW + rows * (D + 4.0 * KVW)) * E + 8.0 * rows * D + 8.0 * D +
+             xa,
+         2.0 * rows * D * w.k2 + 4.0 * Bd * lo.H * lo.dh * (s0 + 1 + (lo.mode == BT_CTX_XATTN ? lo.P : 0)));
   BT_CHECK(h, launch_attn_out_decode(P_(h, lo.ACT), P_(h, w.w2), rows, lo.D, w.k2, ep, ls, h->st),
            "local attention + out|down");
   return BT_OK;

@@ -213,6 +213,12 @@ struct LocalStep {
   int cap;
   const int* rmap;  // cache row of activation row b (null: b)
   float scale_log2;  // log2(e) / sqrt(64)
+  // cross-attention context (xkv null: none): query head h of row b at qkv column xq_off + 64 h;
+  // keys and values of its P encoder states (fp32) in xkv rows b P + p, columns xkv_off + 64 hk and
+  // xkv_off + 64 (Hkv + hk); the output multiplies the W rows of K range [k_mlp, k_mlp + 64 H)
+  const float* xkv;
+  int xkv_ld, xkv_off, P, xq_off;
+  int k_mlp;  // end of the GELU columns' K range (the whole K without cross-attention)
 };
 int attn_out_splits(int M, int N, int K, int H);
 hipError_t launch_attn_out_decode(const void* ACT, const void* W, int M, int N, int K, const Epi& ep,

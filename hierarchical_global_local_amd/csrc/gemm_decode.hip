@@ -215,14 +215,16 @@ __device__ __forceinline__ void h8_to_f(const half8& v, float* o) {
   for (int e = 0; e < 8; ++e) o[e] = (float)v[e];
 }
 
-template <int MG, int MW, int NG, int KW>
+template <int MG, int MW, int NG, int KW, bool XA>
 __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict__ ACT, const f16* __restrict__ W,
                                                            int M, int N, int K, Epi ep, LocalStep ls, int n_attn,
                                                            int n_cp, int mlp_splits, int spread) {
   // attention tiles of RB rows: WPI waves per head (8 rows each), two heads
   constexpr int NWAVE = MW * KW, RB = 4 * NWAVE, RG = RB / 16, WPI = NWAVE / 2;
   static_assert(NWAVE == 8 || NWAVE == 16, "8 or 16 waves");
-  constexpr int LDS_GEMM = skinny_lds_floats<MG, MW, NG, KW>(), LDS_A = RG * 4 * 256, LDS_ATT = LDS_A + 64;
+  // (XA: a second set of A tiles holds the cross-attention outputs)
+  constexpr int LDS_GEMM = skinny_lds_floats<MG, MW, NG, KW>(), LDS_A = RG * 4 * 256,
+                LDS_ATT = (XA ? 2 : 1) * LDS_A + 64;
   __shared__ __attribute__((aligned(16))) float lds[LDS_GEMM > LDS_ATT ? LDS_GEMM : LDS_ATT];
   const int n_hp = ls.H / 2;
   // Workgroup id -> tile.  Workgroup ids x, x + 8, ... run on XCD x.  Attention group a = (rb, hp)
@@ -244,8 +246,9 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
   }
   if (t >= n_attn) {
     const int u = t - n_attn, slabs = N / (16 * NG);
-    skinny_tile<MG, MW, NG, KW, EPI_RESID, 2>(ACT, nullptr, W, M, N, K, ep, u % slabs, ls.H * 2, K / 32,
-                                              u / slabs, mlp_splits, true, n_hp + u / slabs, lds);
+    skinny_tile<MG, MW, NG, KW, EPI_RESID, 2>(ACT, nullptr, W, M, N, K, ep, u % slabs, ls.H * 2,
+                                              (XA ? ls.k_mlp : K) / 32, u / slabs, mlp_splits, true,
+                                              n_hp + u / slabs, lds);
     return;
   }
   const int cp = t % n_cp, hp = (t / n_cp) % n_hp, rb = t / (n_cp * n_hp);
@@ -273,11 +276,32 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
   }
   float rv = 0.f;
   if (threadIdx.x < 64) rv = ((const float*)(ls.rope + (size_t)s0 * 32))[threadIdx.x];
-  half8 rw[4];
+  // cross-attention operands: this lane's 8 dimensions of the query and, where the register
+  // budget allows (8 waves: 256 registers a lane), of the first encoder state's key and value
+  // (fp32) and the cross-attention weight tiles, issued with the rest
+  constexpr bool XE = XA && NWAVE == 8;
+  half8 xqh;
+  float4 xk0[2], xv0[2];
+  const float* xkb = nullptr;
+  if constexpr (XA) {
+    xqh = *(const half8*)(ls.qkv + (size_t)rc * ls.ldq + ls.xq_off + h * 64 + 8 * g);
+    xkb = ls.xkv + (size_t)rc * ls.P * ls.xkv_ld + ls.xkv_off + hk * 64 + 8 * g;
+  }
+  if constexpr (XE) {
+    xk0[0] = *(const float4*)xkb, xk0[1] = *(const float4*)(xkb + 4);
+    xv0[0] = *(const float4*)(xkb + ls.Hkv * 64), xv0[1] = *(const float4*)(xkb + ls.Hkv * 64 + 4);
+  }
+  half8 rw[4], rwx[4];
+  auto load_rwx = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      rwx[ks] = *(const half8*)(W + (((size_t)ng * KS + ls.k_mlp / 32 + 4 * hp + ks) * 64 + lane) * 8);
+  };
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) rw[ks] = *(const half8*)(W + (((size_t)ng * KS + 4 * hp + ks) * 64 + lane) * 8);
+  if constexpr (XE) load_rwx();
   __builtin_amdgcn_sched_barrier(0);
-  float* __restrict__ rope_s = lds + LDS_A;
+  float* __restrict__ rope_s = lds + (XA ? 2 : 1) * LDS_A;
   if (threadIdx.x < 64) rope_s[threadIdx.x] = rv;
   __syncthreads();
   float cs[8], sn[8];
@@ -360,6 +384,45 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
   for (int e = 0; e < 8; ++e) ov[e] = to_f16_bounded(o[e] * inv);
   // A tile (row group lr / 16, K step 2 it + g / 4): element (row lr % 16, column 8 (g % 4) + e)
   *(half8*)(at + ((lr >> 4) * 4 + 2 * it + (g >> 2)) * 512 + ((g & 3) * 16 + (lr & 15)) * 8) = ov;
+  if constexpr (XA) {
+    // cross-attention of the same (row, head) over the P encoder states (no rotary embedding),
+    // online softmax in base 2; the output goes to the second set of A tiles
+    if constexpr (!XE) load_rwx();
+    float xq[8];
+    h8_to_f(xqh, xq);
+    float xm = -INFINITY, xl = 0.f, xo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xo[e] = 0.f;
+    for (int p = 0; p < ls.P; ++p) {
+      float4 k4[2], v4[2];
+      if (XE && p == 0) {
+        k4[0] = xk0[0], k4[1] = xk0[1], v4[0] = xv0[0], v4[1] = xv0[1];
+      } else {
+        const float* kp = xkb + (size_t)p * ls.xkv_ld;
+        k4[0] = *(const float4*)kp, k4[1] = *(const float4*)(kp + 4);
+        v4[0] = *(const float4*)(kp + ls.Hkv * 64), v4[1] = *(const float4*)(kp + ls.Hkv * 64 + 4);
+      }
+      const float kk[8] = {k4[0].x, k4[0].y, k4[0].z, k4[0].w, k4[1].x, k4[1].y, k4[1].z, k4[1].w};
+      const float vv[8] = {v4[0].x, v4[0].y, v4[0].z, v4[0].w, v4[1].x, v4[1].y, v4[1].z, v4[1].w};
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(xq[e], kk[e], dot);
+      dot += __shfl_xor(dot, 1, 64);
+      dot += __shfl_xor(dot, 2, 64);
+      dot += __shfl_xor(dot, 4, 64);
+      const float sc = dot * ls.scale_log2, mn = fmaxf(xm, sc);
+      const float corr = __builtin_amdgcn_exp2f(xm - mn), pr = __builtin_amdgcn_exp2f(sc - mn);
+      xl = xl * corr + pr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xo[e] = xo[e] * corr + pr * vv[e];
+      xm = mn;
+    }
+    const float xinv = live ? 1.0f / xl : 0.f;
+    half8 xov;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xov[e] = to_f16_bounded(xo[e] * xinv);
+    *(half8*)(at + LDS_A * 2 + ((lr >> 4) * 4 + 2 * it + (g >> 2)) * 512 + ((g & 3) * 16 + (lr & 15)) * 8) = xov;
+  }
   __syncthreads();
   // the 16 x 16 output tiles (row groups rg0, rg0 + 1; column group ng) over the heads' 4 K steps
   const int rg0 = (wave >> 3) * 2;
@@ -371,6 +434,12 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
     for (int ks = 0; ks < 4; ++ks)
       acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const half8*)(at + ((rg0 + i) * 4 + ks) * 512 + lane * 8),
                                                       rw[ks], acc[i], 0, 0, 0);
+    if constexpr (XA) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            *(const half8*)(at + LDS_A * 2 + ((rg0 + i) * 4 + ks) * 512 + lane * 8), rwx[ks], acc[i], 0, 0, 0);
+    }
   }
   const int col = ng * 16 + (lane & 15);
 #pragma unroll
@@ -382,14 +451,14 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
     }
 }
 
-template <int MG, int MW, int NG, int KW>
+template <int MG, int MW, int NG, int KW, bool XA>
 static hipError_t launch_attn_out_cfg(const void* ACT, const void* W, int M, int N, int K, const Epi& ep,
                                       const LocalStep& ls, int mlp_splits, hipStream_t st) {
   constexpr int RB = 4 * MW * KW;
   const int n_cp = N / 128, n_attn = (M + RB - 1) / RB * (ls.H / 2) * n_cp;
   const int n_gemm = N / (16 * NG) * mlp_splits, nb = n_attn + n_gemm, n_grp = n_attn / n_cp;
   const int spread = (n_grp + 7) / 8 * n_cp <= nb / 8;
-  hipLaunchKernelGGL((k_attn_out<MG, MW, NG, KW>), dim3(nb), dim3(64 * MW * KW), 0, st, (const f16*)ACT,
+  hipLaunchKernelGGL((k_attn_out<MG, MW, NG, KW, XA>), dim3(nb), dim3(64 * MW * KW), 0, st, (const f16*)ACT,
                      (const f16*)W, M, N, K, ep, ls, n_attn, n_cp, mlp_splits, spread);
   return hipGetLastError();
 }
@@ -417,14 +486,20 @@ int attn_out_splits(int M, int N, int K, int H) {
 
 hipError_t launch_attn_out_decode(const void* ACT, const void* W, int M, int N, int K, const Epi& ep,
                                   const LocalStep& ls, hipStream_t st) {
-  const int total = attn_out_splits(M, N, K, ls.H);
+  const bool xa = ls.xkv != nullptr;
+  const int total = attn_out_splits(M, N, xa ? ls.k_mlp : K, ls.H);
   if (total <= ls.H / 2 || total > 16 || !ep.part || ls.Hkv < 1 || ls.H % ls.Hkv || ls.s0 < 0 ||
       ls.s0 >= ls.cap || ls.ldq < (ls.H + 2 * ls.Hkv) * 64 || ls.ldq % 8)
     return hipErrorInvalidValue;
+  if (xa && (ls.P < 1 || ls.k_mlp % 32 || ls.k_mlp + N != K || ls.xq_off % 8 || ls.xq_off + N > ls.ldq ||
+             ls.xkv_ld % 4 || ls.xkv_off % 4))
+    return hipErrorInvalidValue;
   const int mlp_splits = total - ls.H / 2;
-  const SkinnyPlan p = skinny_plan(M, N, K, EPI_RESID, false);
-#define BT_AO(MG, MW, NG, KW) \
-  if (p.mg == MG && p.mw == MW && p.ng == NG && p.kw == KW) return launch_attn_out_cfg<MG, MW, NG, KW>(ACT, W, M, N, K, ep, ls, mlp_splits, st);
+  const SkinnyPlan p = skinny_plan(M, N, xa ? ls.k_mlp : K, EPI_RESID, false);
+#define BT_AO(MG, MW, NG, KW)                                                                               \
+  if (p.mg == MG && p.mw == MW && p.ng == NG && p.kw == KW)                                               \
+    return xa ? launch_attn_out_cfg<MG, MW, NG, KW, true>(ACT, W, M, N, K, ep, ls, mlp_splits, st)        \
+              : launch_attn_out_cfg<MG, MW, NG, KW, false>(ACT, W, M, N, K, ep, ls, mlp_splits, st);
   BT_AO(1, 1, 2, 8)
   BT_AO(2, 1, 2, 8)
   BT_AO(4, 1, 2, 8)
