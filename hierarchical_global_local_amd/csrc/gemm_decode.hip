@@ -245,10 +245,12 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
     }
   }
   if (t >= n_attn) {
-    const int u = t - n_attn, slabs = N / (16 * NG);
+    // GEMM tile u: row group u / (slabs x splits) of 16 MG MW rows, then K split, then column slab
+    const int slabs = N / (16 * NG), per_rg = slabs * mlp_splits;
+    const int u = (t - n_attn) % per_rg, rg = (t - n_attn) / per_rg;
     skinny_tile<MG, MW, NG, KW, EPI_RESID, 2>(ACT, nullptr, W, M, N, K, ep, u % slabs, ls.H * 2,
                                               (XA ? ls.k_mlp : K) / 32, u / slabs, mlp_splits, true,
-                                              n_hp + u / slabs, lds);
+                                              n_hp + u / slabs, lds, rg * MG * MW);
     return;
   }
   const int cp = t % n_cp, hp = (t / n_cp) % n_hp, rb = t / (n_cp * n_hp);
@@ -454,9 +456,9 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
 template <int MG, int MW, int NG, int KW, bool XA>
 static hipError_t launch_attn_out_cfg(const void* ACT, const void* W, int M, int N, int K, const Epi& ep,
                                       const LocalStep& ls, int mlp_splits, hipStream_t st) {
-  constexpr int RB = 4 * MW * KW;
+  constexpr int RB = 4 * MW * KW, RW = 16 * MG * MW;  // attention rows, GEMM rows per workgroup
   const int n_cp = N / 128, n_attn = (M + RB - 1) / RB * (ls.H / 2) * n_cp;
-  const int n_gemm = N / (16 * NG) * mlp_splits, nb = n_attn + n_gemm, n_grp = n_attn / n_cp;
+  const int n_gemm = N / (16 * NG) * mlp_splits * ((M + RW - 1) / RW), nb = n_attn + n_gemm, n_grp = n_attn / n_cp;
   const int spread = (n_grp + 7) / 8 * n_cp <= nb / 8;
   hipLaunchKernelGGL((k_attn_out<MG, MW, NG, KW, XA>), dim3(nb), dim3(64 * MW * KW), 0, st, (const f16*)ACT,
                      (const f16*)W, M, N, K, ep, ls, n_attn, n_cp, mlp_splits, spread);
@@ -467,15 +469,23 @@ static hipError_t launch_attn_out_cfg(const void* ACT, const void* W, int M, int
 // the GELU columns' K split so that attention and GEMM tiles together take at most about one
 // workgroup per CU and each wave about 3 K steps (every split owning at least one K step, at most
 // 16 partials).
+// Workgroup shape of the fused launch: the skinny plan with all rows per workgroup up to 128 rows;
+// above, 64-row GEMM workgroups (row groups) of 8 waves along K, and 32-row attention blocks.
+static SkinnyPlan fused_plan(int M, int N, int K) {
+  SkinnyPlan p = skinny_plan(M, N, K, EPI_RESID, false);
+  if (p.ok && M > 128) p.mg = 4, p.mw = 1, p.ng = 2, p.kw = 8, p.rg = (M + 63) / 64;
+  return p;
+}
+
 int attn_out_splits(int M, int N, int K, int H) {
   if (M < 1 || M > 256 || H < 2 || H % 2 || H > 30 || N != 64 * H || K <= N || (K - N) % 32) return 0;
-  const SkinnyPlan p = skinny_plan(M, N, K, EPI_RESID, false);
+  const SkinnyPlan p = fused_plan(M, N, K);
   if (!p.ok) return 0;
   const int rb = 4 * p.mw * p.kw, n_attn = (M + rb - 1) / rb * (H / 2) * (N / 128);
-  const int slabs = N / (16 * p.ng), ks = (K - N) / 32;
+  const int slabs = N / (16 * p.ng) * ((M + 16 * p.mg * p.mw - 1) / (16 * p.mg * p.mw)), ks = (K - N) / 32;
   // (measured: fewer, longer splits win once each wave has about 3 K steps -- C1 decode 23.27 ->
   // 23.10 ms at 4 splits instead of 7 -- the next LayerNorm then folds fewer partials)
-  int s = std::min(16 - H / 2, std::max(1, (256 - n_attn) / slabs));
+  int s = M > 128 ? 16 - H / 2 : std::min(16 - H / 2, std::max(1, (256 - n_attn) / slabs));
   s = std::min(s, std::max(1, ks / (3 * p.kw)));
   s = std::max(1, std::min(s, ks / p.kw));
   const int per = (ks + s - 1) / s;
@@ -495,7 +505,7 @@ hipError_t launch_attn_out_decode(const void* ACT, const void* W, int M, int N, 
              ls.xkv_ld % 4 || ls.xkv_off % 4))
     return hipErrorInvalidValue;
   const int mlp_splits = total - ls.H / 2;
-  const SkinnyPlan p = skinny_plan(M, N, xa ? ls.k_mlp : K, EPI_RESID, false);
+  const SkinnyPlan p = fused_plan(M, N, xa ? ls.k_mlp : K);
 #define BT_AO(MG, MW, NG, KW)                                                                               \
   if (p.mg == MG && p.mw == MW && p.ng == NG && p.kw == KW)                                               \
     return xa ? launch_attn_out_cfg<MG, MW, NG, KW, true>(ACT, W, M, N, K, ep, ls, mlp_splits, st)        \
