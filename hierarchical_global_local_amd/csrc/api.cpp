@@ -476,15 +476,12 @@ int run_out(bt_handle* h, const LayerOff& w, int rows) {
 
 // Partial count of the token decoder's fused local attention (and cross-attention) + [out|down]
 // launch for one new slot per row (attn_out_splits over the GELU columns' K range), 0 where it runs
-// as separate launches: fp32, head width other than 64, more rows than the partial buffer or the
-// fused kernel take, or cross-attention above 128 rows (there the 1024-thread workgroups have no
-// registers left to issue the cross-attention loads early: 164 instead of 160 ms of decode at 256
-// rows x 512 tokens, while at 64 and 128 rows the fused launch saves 19-20 %).
+// as separate launches: fp32, head width other than 64, or more rows than the partial buffer or the
+// fused kernel take.
 int fused_local_splits(bt_handle* h, int m) {
   const Layout& lo = h->lo;
   const int rows = h->B * m;
   if (m != 1 || !h->fuse_local || lo.f32 || lo.dh != 64 || rows > lo.rpart_rows || lo.Nt == 0) return 0;
-  if (lo.mode == BT_CTX_XATTN && rows > 128) return 0;
   return attn_out_splits(rows, lo.D, lo.D + lo.F, lo.H);
 }
 

@@ -514,7 +514,6 @@ hipError_t launch_attn_out_decode(const void* ACT, const void* W, int M, int N, 
   BT_AO(2, 1, 2, 8)
   BT_AO(4, 1, 2, 8)
   BT_AO(4, 2, 2, 4)
-  BT_AO(4, 4, 2, 4)
 #undef BT_AO
   return hipErrorInvalidValue;
 }

@@ -52,8 +52,7 @@ int bt_test_replay(bt_handle* h, int32_t kind, int32_t reps);
 
 /* enable = 0: decode steps launch the token decoder's local attention (and, with cross-attention
  * injection, the cross-attention) separately from its [out|down] GEMM instead of inside it (the
- * default where the shape allows: fp16, head width 64, at most 256 rows, at most 128 with
- * cross-attention).  Same results up to the summation order of the
+ * default where the shape allows: fp16, head width 64, at most 256 rows).  Same results up to the summation order of the
  * residual update.  Drops captured decode graphs when the setting changes. */
 int bt_test_fuse_local(bt_handle* h, int32_t enable);
 

@@ -141,7 +141,7 @@ def test_bf16_small_every_step(kw, max_tokens):
                                   (dict(d_model=384, n_heads=6, n_kv_heads=1, d_mlp=768), 200),
                                   (dict(context_mode="sum"), 70), (dict(block_len=8, prefix_len=3), 130),
                                   (dict(context_mode="xattn", prefix_len=2), 70),
-                                  (dict(context_mode="xattn", prefix_len=3, d_model=256, n_heads=4, n_kv_heads=2), 128)])
+                                  (dict(context_mode="xattn", prefix_len=3, d_model=256, n_heads=4, n_kv_heads=2), 130)])
 def test_fused_local_attention_out_gemm(kw, B):
     """The token decoder's local attention (and, with cross-attention injection, the
     cross-attention over the P encoder states) computed inside its [out|down] GEMM (the default
