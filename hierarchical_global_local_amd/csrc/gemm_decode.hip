@@ -483,9 +483,11 @@ int attn_out_splits(int M, int N, int K, int H) {
   if (!p.ok) return 0;
   const int rb = 4 * p.mw * p.kw, n_attn = (M + rb - 1) / rb * (H / 2) * (N / 128);
   const int slabs = N / (16 * p.ng) * ((M + 16 * p.mg * p.mw - 1) / (16 * p.mg * p.mw)), ks = (K - N) / 32;
-  // (measured: fewer, longer splits win once each wave has about 3 K steps -- C1 decode 23.27 ->
-  // 23.10 ms at 4 splits instead of 7 -- the next LayerNorm then folds fewer partials)
-  int s = M > 128 ? 16 - H / 2 : std::min(16 - H / 2, std::max(1, (256 - n_attn) / slabs));
+  // (measured: fewer, longer splits win once each wave has about 3 K steps -- 64-row d=768 decode
+  // 23.27 -> 23.10 ms at 4 splits instead of 7 -- the next LayerNorm then folds fewer partials; above
+  // 128 rows the row groups already fill the chip and 2 splits beat 1, 3, 4 and 6: 256-row d=768
+  // decode 583.5 -> 560.8 ms against 4, while 2 or 1 splits lose at 64 rows)
+  int s = M > 128 ? 2 : std::min(16 - H / 2, std::max(1, (256 - n_attn) / slabs));
   s = std::min(s, std::max(1, ks / (3 * p.kw)));
   s = std::max(1, std::min(s, ks / p.kw));
   const int per = (ks + s - 1) / s;
