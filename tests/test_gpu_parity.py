@@ -141,14 +141,18 @@ def test_bf16_small_every_step(kw, max_tokens):
                                   (dict(d_model=384, n_heads=6, n_kv_heads=1, d_mlp=768), 200),
                                   (dict(context_mode="sum"), 70), (dict(block_len=8, prefix_len=3), 130),
                                   (dict(context_mode="xattn", prefix_len=2), 70),
-                                  (dict(context_mode="xattn", prefix_len=3, d_model=256, n_heads=4, n_kv_heads=2), 130)])
+                                  (dict(context_mode="xattn", prefix_len=3, d_model=256, n_heads=4, n_kv_heads=2), 130),
+                                  (dict(d_model=256, n_heads=4, d_mlp=1536), 256),
+                                  (dict(context_mode="xattn", prefix_len=2, d_model=256, n_heads=4, d_mlp=1536), 256)])
 def test_fused_local_attention_out_gemm(kw, B):
     """The token decoder's local attention (and, with cross-attention injection, the
     cross-attention over the P encoder states) computed inside its [out|down] GEMM (the default
     decode path for fp16 with head width 64) against the oracle at every step, and against the
-    separate launches: batches of 1 to 200 rows cover every workgroup shape of the fused kernel (8
-    and 16 waves, one to four 64-row attention blocks), local windows up to 11 entries take the
-    loop over cached keys past its first group of four."""
+    separate launches. Batches of 1 to 256 rows cover every workgroup shape of the fused kernel
+    (16, 32, 64 and 128 rows per workgroup up to 128 rows; above that, 64-row workgroups over row
+    groups), one to eight 32-row attention blocks, and one, two and several K splits of the GELU
+    columns (256 rows with a 1536-wide MLP: two splits, the largest batch the fused launch takes).
+    Local windows up to 11 entries take the loop over cached keys past its first group of four."""
     torch = require_gpu()
     import hierarchical_global_local_amd as hg
     cfg = SMALL_BF16.with_(batch=B, **kw)
