@@ -196,7 +196,8 @@ __global__ __launch_bounds__(64 * MW * KW) void k_gemm_skinny(const f16* __restr
 // decoder's attention over its local window (prefix + the current block's tokens, summary page
 // §3.4, The Token Decoder) is computed inside the [out|down] GEMM that consumes it, so that its
 // latency overlaps the weight stream of the same launch instead of costing a launch of its own.
-//  * attention workgroups (rb, hp, cp): rows [RB rb, RB rb + RB) (RB = 4 x waves: 32 or 64),
+//  * attention workgroups (rb, hp, cp): rows [RB rb, RB rb + RB) (RB = 4 x waves: 32 with the 8-wave workgroups of
+//    every plan),
 //    query heads 2hp and 2hp + 1, output columns [128 cp, 128 cp + 128).  Half the waves take
 //    each head, 8 rows per wave: lane = (row, 8 dimensions), rotary at the new slot, the new key
 //    and value from the q | k | v row and the s0 cached ones from the local cache, softmax in base
