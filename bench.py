@@ -17,6 +17,7 @@ import argparse
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -348,13 +349,25 @@ CLASS_SOURCE = {"decode/gemm_qkv_up": "gemm_decode.hip", "decode/local_attn_out"
                 "decode/attn_block_decode": "attention.hip"}
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(path):
+    """A source file's code without its comments, trailing blanks and empty lines (string and
+    character literals kept whole): what decides the compiled kernels, so that a stored counter
+    result outlives an edit of the comments but not one of the code."""
+    with open(path) as f:
+        src = f.read()
+    src = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", src)
+    return "\n".join(l.rstrip() for l in src.splitlines() if l.strip()).encode()
+
+
 def source_hash(kernel_class):
-    """Hash of the kernel's source file and of the build flags: stored counter results are used only
+    """Hash of the kernel's source code and of the build flags: stored counter results are used only
     while both are unchanged."""
     import hashlib
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", CLASS_SOURCE[kernel_class]), "rb") as f:
-        h.update(f.read())
+    h.update(code_text(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", CLASS_SOURCE[kernel_class])))
     from hierarchical_global_local_amd import build as _b
     # the code-generation flags only: include paths name this checkout's location
     h.update(" ".join(f for f in _b.FLAGS if not f.startswith("-I")).encode())
@@ -425,13 +438,12 @@ def _decode_phase_kib(d, counter):
 
 
 def all_sources_hash():
-    """Hash of every library source and header and of the code-generation flags."""
+    """Hash of the code of every library source and header and of the code-generation flags."""
     import hashlib
     from hierarchical_global_local_amd import build as _b
     h = hashlib.sha256()
     for fn in sorted(os.listdir(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc"))):
-        with open(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
+        h.update(code_text(os.path.join(ROOT, "hierarchical_global_local_amd", "csrc", fn)))
     h.update(" ".join(f for f in _b.FLAGS if not f.startswith("-I")).encode())
     return h.hexdigest()[:16]
 

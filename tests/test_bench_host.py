@@ -115,3 +115,16 @@ def test_trace_in_step_duration_is_read_from_the_committed_summary(tmp_path, mon
     assert bench.trace_in_step_us("c1_prefill_heavy", "_ZN2bt10k_attn_outILi4ELi1E") == 6.21
     assert bench.trace_in_step_us("c1_prefill_heavy", "_ZN2bt11k_layernorm") is None
     assert bench.trace_in_step_us("c2_decode_heavy", "_ZN2bt13k_gemm_skinnyILi4ELi1E") is None
+
+
+def test_code_hash_ignores_comments_but_not_code(tmp_path):
+    """Stored counters stay valid across an edit of a source's comments and lapse with any change of
+    its code (string literals that hold comment markers are code)."""
+    a, b, c, d = (tmp_path / n for n in ("a.hip", "b.hip", "c.hip", "d.hip"))
+    a.write_text('int f(int x) {  // scaled\n  return 2 * x; /* twice */\n}\nconst char* s = "a // b";\n')
+    b.write_text('// header\nint f(int x) {\n\n  return 2 * x;\n}  \nconst char* s = "a // b";\n')
+    c.write_text('int f(int x) {  // scaled\n  return 3 * x; /* twice */\n}\nconst char* s = "a // b";\n')
+    d.write_text('int f(int x) {  // scaled\n  return 2 * x; /* twice */\n}\nconst char* s = "a ";\n')
+    assert bench.code_text(str(a)) == bench.code_text(str(b))
+    assert bench.code_text(str(a)) != bench.code_text(str(c))
+    assert bench.code_text(str(a)) != bench.code_text(str(d))
