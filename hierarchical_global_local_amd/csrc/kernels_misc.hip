@@ -447,6 +447,92 @@ __global__ __launch_bounds__(256) void k_layernorm_g16(const float* __restrict__
   }
 }
 
+// Many rows of a wide model (D > 768), fp16 outputs in fragment order: lane l of a wave owns the
+// column octets l, l + 64, ... (C8 of them), so each output write is one 16-byte operand piece, and
+// the 4 consecutive rows of a wave put their pieces of an octet side by side (64 contiguous bytes
+// of a fragment tile), with no LDS staging.  Sums as in the kernels above (per row, centred
+// variance).  Rows of the last 16-row group past `rows` repeat the last row.  D % 32 == 0,
+// D <= 512 C8.
+template <int C8, int RPW>
+__global__ __launch_bounds__(256) void k_layernorm_o8(const float* __restrict__ X, int rows, int D,
+                                                      const float* __restrict__ p1, f16* __restrict__ o1,
+                                                      const float* __restrict__ p2, f16* __restrict__ o2,
+                                                      float eps) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = 4 * RPW * blockIdx.x + RPW * wave, noct = D >> 3;
+  float4 v[RPW][C8][2];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const float* __restrict__ x = X + (size_t)min(r0 + rr, rows - 1) * D;
+#pragma unroll
+    for (int j = 0; j < C8; ++j) {
+      const int c = 8 * min(lane + 64 * j, noct - 1);
+      v[rr][j][0] = *(const float4*)(x + c);
+      v[rr][j][1] = *(const float4*)(x + c + 4);
+    }
+  }
+  float mean[RPW], rstd[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < C8; ++j)
+      if (lane + 64 * j < noct)
+        s += ((v[rr][j][0].x + v[rr][j][0].y) + (v[rr][j][0].z + v[rr][j][0].w)) +
+             ((v[rr][j][1].x + v[rr][j][1].y) + (v[rr][j][1].z + v[rr][j][1].w));
+    mean[rr] = wave_sum(s) / (float)D;
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < C8; ++j) {
+      if (lane + 64 * j < noct) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float d0 = v[rr][j][h].x - mean[rr], d1 = v[rr][j][h].y - mean[rr];
+          const float d2 = v[rr][j][h].z - mean[rr], d3 = v[rr][j][h].w - mean[rr];
+          q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+        }
+      }
+    }
+    rstd[rr] = 1.0f / sqrtf(wave_sum(q) / (float)D + eps);
+  }
+  uint32_t trk = 0u;
+#pragma unroll
+  for (int j = 0; j < C8; ++j) {
+    const int oc = lane + 64 * j;
+    if (oc >= noct) continue;
+    const int c = 8 * oc;
+    float g[8], b[8], g2[8], b2[8];
+    {
+      const float4 a0 = *(const float4*)(p1 + c), a1 = *(const float4*)(p1 + c + 4);
+      const float4 c0 = *(const float4*)(p1 + D + c), c1 = *(const float4*)(p1 + D + c + 4);
+      g[0] = a0.x, g[1] = a0.y, g[2] = a0.z, g[3] = a0.w, g[4] = a1.x, g[5] = a1.y, g[6] = a1.z, g[7] = a1.w;
+      b[0] = c0.x, b[1] = c0.y, b[2] = c0.z, b[3] = c0.w, b[4] = c1.x, b[5] = c1.y, b[6] = c1.z, b[7] = c1.w;
+    }
+    if (o2) {
+      const float4 a0 = *(const float4*)(p2 + c), a1 = *(const float4*)(p2 + c + 4);
+      const float4 c0 = *(const float4*)(p2 + D + c), c1 = *(const float4*)(p2 + D + c + 4);
+      g2[0] = a0.x, g2[1] = a0.y, g2[2] = a0.z, g2[3] = a0.w, g2[4] = a1.x, g2[5] = a1.y, g2[6] = a1.z, g2[7] = a1.w;
+      b2[0] = c0.x, b2[1] = c0.y, b2[2] = c0.z, b2[3] = c0.w, b2[4] = c1.x, b2[5] = c1.y, b2[6] = c1.z, b2[7] = c1.w;
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const float y[8] = {v[rr][j][0].x, v[rr][j][0].y, v[rr][j][0].z, v[rr][j][0].w,
+                          v[rr][j][1].x, v[rr][j][1].y, v[rr][j][1].z, v[rr][j][1].w};
+      const size_t o = frag_off(r0 + rr, c, D);
+      half8 w1, w2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float n = (y[e] - mean[rr]) * rstd[rr];
+        w1[e] = to_f16_trk(n * g[e] + b[e], trk);
+        if (o2) w2[e] = to_f16_trk(n * g2[e] + b2[e], trk);
+      }
+      *(half8*)(o1 + o) = w1;
+      if (o2) *(half8*)(o2 + o) = w2;
+    }
+  }
+  clamp_note(trk);
+}
+
 hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, const float* p1, void* out1,
                             const float* p2, void* out2, bool out_f32, float eps, const ResidPending* resid,
                             hipStream_t st) {
@@ -479,6 +565,19 @@ hipError_t launch_layernorm(float* X, int rows, int D, int stride, int off, cons
         hipLaunchKernelGGL(k_layernorm_g16<2>, grid, dim3(256), 0, st, X, rows, D, p1, (f16*)out1, p2, (f16*)out2, eps);
       else
         hipLaunchKernelGGL(k_layernorm_g16<3>, grid, dim3(256), 0, st, X, rows, D, p1, (f16*)out1, p2, (f16*)out2, eps);
+      return hipGetLastError();
+    }
+    // wider rows: 16-byte operand pieces straight from registers (measured at D = 2048, 65 536
+    // rows: 328 instead of 498 us on the kernel below; 2 or 1 rows a wave, for more waves per
+    // SIMD, were no faster)
+    const int per8 = (D / 8 + 63) / 64;
+    if (!out_f32 && stride == 1 && off == 0 && D % 32 == 0 && per8 <= 4) {
+      constexpr int kRpw = 4;
+      const dim3 grid((rows + 15) / 16 * (4 / kRpw));  // whole 16-row groups, padding rows included
+      if (per8 <= 2)
+        hipLaunchKernelGGL((k_layernorm_o8<2, kRpw>), grid, dim3(256), 0, st, X, rows, D, p1, (f16*)out1, p2, (f16*)out2, eps);
+      else
+        hipLaunchKernelGGL((k_layernorm_o8<4, kRpw>), grid, dim3(256), 0, st, X, rows, D, p1, (f16*)out1, p2, (f16*)out2, eps);
       return hipGetLastError();
     }
     if (per <= 1)

@@ -185,6 +185,32 @@ def test_fused_local_attention_out_gemm(kw, B):
         assert np.abs(gl[:, :first] - gl_s[:, :first]).max() <= BF16_TOL
 
 
+@pytest.mark.parametrize("D", [1024, 1536])
+def test_wide_model_prefill_layernorm(D):
+    """Prefill of more than 1024 block rows at widths above 768: the block decoder's LayerNorms run
+    on the kernel that writes 16-byte operand pieces from registers (1024: two column octets a lane;
+    1536: three of four, the last masked).  Every row's first token and two decode steps against
+    the oracle."""
+    cfg = SMALL_BF16.with_(d_model=D, n_heads=D // 128, d_mlp=512, prefix_len=1, batch=3, prompt_len=1399, gen_len=3)
+    T = wl.padded_len(cfg, cfg.prompt_len)
+    log(f"wide prefill case D={D}: {cfg.batch} x {T // cfg.block_len} block rows")
+    assert cfg.batch * T // cfg.block_len > 1024
+    W = wl.make_weights(cfg, seed=23, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=23)
+    G = cfg.gen_len
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G))
+    model.close()
+    del model
+    worst = 0.0
+    for r in range(cfg.batch):
+        ref = teacher_forced_logits(cfg, W, prompt[r], ids[r], range(G))
+        err = float(np.abs(np.stack([lg[g][r] for g in range(G)]) - ref).max())
+        worst = max(worst, err)
+        check_ids_against(ref, ids[r], BF16_TOL)
+    log(f"  max-abs logit error {worst:.3e} over {cfg.batch} rows x {G} steps")
+    assert worst <= BF16_TOL
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(d_model=256, n_heads=4, n_kv_heads=1)])
 def test_deep_split_kv_long_context(kw):
     """12000 prompt blocks (L_B = 1) in the largest block-KV capacity, 131072 entries: the block
