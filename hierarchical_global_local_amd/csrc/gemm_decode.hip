@@ -594,6 +594,20 @@ SkinnyPlan skinny_plan(int M, int N, int K, EpiMode mode, bool row_groups) {
     const int per = (ks + s - 1) / s;
     p.splits = (ks + per - 1) / per;  // every split owns at least one K step
   }
+  if (row_groups && mgt > 4 && mgt <= 8 &&
+      ((mode == EPI_QKV_GELU && N % 64 == 0 && N / 64 >= 128) || (mode == EPI_RESID && N % 64 == 0 && N >= 2048))) {
+    // 65-128 rows of a wide model: every byte a workgroup loads passes its CU's load path, which
+    // bounds these launches (two row waves each loading the same weight tile, plus the activation
+    // tile every slab re-reads).  One wave holds all 128 rows (no weight tile loaded twice) over 64
+    // columns, 4 waves along K, and the [out|down] GEMM splits K 8 ways so that about 256 of these
+    // workgroups stream its weights.  Measured on the 1.2B model's decode (128 rows, d = 2048):
+    // 2648 -> 2460 ms per generation; [out|down] 22.5 -> 16.5 us per launch, [q|k|v|up] 22.3 -> 21.6.
+    p.mg = 8, p.mw = 1, p.ng = 4, p.kw = 4;
+    if (mode == EPI_RESID) {
+      const int s = std::max(1, std::min(std::min(16, 256 / (N / 64)), ks / p.kw)), per = (ks + s - 1) / s;
+      p.splits = (ks + per - 1) / per;
+    }
+  }
   return p;
 }
 
@@ -613,6 +627,7 @@ hipError_t launch_gemm_skinny(const SkinnyPlan& p, const void* A1, const void* A
   BT_SKINNY(4, 4, 2, 4, 2)
   BT_SKINNY(4, 1, 2, 4, 3)
   BT_SKINNY(4, 1, 4, 2, 3)
+  BT_SKINNY(8, 1, 4, 4, 2)
 #undef BT_SKINNY
   return hipErrorInvalidValue;
 }

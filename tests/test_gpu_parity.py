@@ -185,6 +185,27 @@ def test_fused_local_attention_out_gemm(kw, B):
         assert np.abs(gl[:, :first] - gl_s[:, :first]).max() <= BF16_TOL
 
 
+@pytest.mark.parametrize("B", [65, 100, 128])
+def test_wide_model_decode_gemms_65_to_128_rows(B):
+    """Decode at 65-128 rows of a d = 2048 model: the [q|k|v|up] GEMM (8192 columns) and the
+    [out|down] GEMM (K = 4096, 8 K splits folded by the next LayerNorm) run with one wave holding
+    all rows over 64 columns.  Every step's logits against the oracle on the GPU's ids."""
+    cfg = SMALL_BF16.with_(d_model=2048, n_heads=16, d_mlp=2048, batch=B, prompt_len=9, gen_len=7)
+    log(f"wide decode case B={B}")
+    W = wl.make_weights(cfg, seed=29, ln_jitter=True)
+    prompt = wl.make_prompt(cfg, seed=29)
+    G = cfg.gen_len
+    ids, lg, model = run_gpu(cfg, W, prompt, G, logits_steps=range(G))
+    model.close()
+    del model
+    _, ref_lg, _ = om.generate(om.weights_as(W, np.float64), cfg, prompt, G, keep_logits=True, forced=ids)
+    gl = np.stack([lg[g] for g in range(G)], axis=1)
+    err = np.abs(gl - ref_lg).max()
+    exact = check_ids_against(ref_lg, ids, BF16_TOL)
+    log(f"  max-abs logit error {err:.3e}, exact argmax {exact:.3f}")
+    assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("D", [1024, 1536])
 def test_wide_model_prefill_layernorm(D):
     """Prefill of more than 1024 block rows at widths above 768: the block decoder's LayerNorms run
