@@ -843,9 +843,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
   float sn_new = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) sn_new = fmaf(qr[e], kn[e], sn_new);
-#pragma unroll
-  for (int o = 1; o < LPK; o <<= 1) sn_new += __shfl_xor(sn_new, o, 64);
-  sn_new *= scale_log2;
+  sn_new = sum_lanes<LPK>(sn_new) * scale_log2;
 
   // ---- cached keys, online softmax: m (running maximum, log2 units), l (this lane group's sum of
   // weights), acc[r] (value row 8 pp + r weighted by this lane group's keys)
@@ -861,8 +859,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) d = fmaf(qr[e], (float)kr[u][e], d);
-#pragma unroll
-      for (int o = 1; o < LPK; o <<= 1) d += __shfl_xor(d, o, 64);
+      d = sum_lanes<LPK>(d);
       sv[u] = jb + kl * 8 + u < jc_end ? d * scale_log2 : -INFINITY;
     }
     float cm = sv[0];
@@ -1548,8 +1545,7 @@ __global__ __launch_bounds__(256) void k_local_attn_step(const T* __restrict__ Q
     float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dot = fmaf(q[e], isnew ? kn[e] : kc[e], dot);
-#pragma unroll
-    for (int w = 1; w < LPK; w <<= 1) dot += __shfl_xor(dot, w, 64);
+    dot = sum_lanes<LPK>(dot);
     const float sc = j < nkeys ? dot * scale_log2 : -INFINITY;
     const float mn = fmaxf(mrun, sc);
     const float corr = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
@@ -1652,8 +1648,7 @@ __global__ __launch_bounds__(256) void k_cross_attn(const T* __restrict__ QKV, i
     float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kc[e], dot);
-#pragma unroll
-    for (int w = 1; w < LPK; w <<= 1) dot += __shfl_xor(dot, w, 64);
+    dot = sum_lanes<LPK>(dot);
     const float sc = p < P ? dot * scale_log2 : -INFINITY;
     const float mn = fmaxf(mrun, sc);
     const float corr = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);

@@ -80,6 +80,32 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
+// Sum over each aligned group of 8 lanes on the DPP network (no LDS crossbar round trips): swap
+// neighbours, swap pairs, then add the half-row mirror (lane i of a group reads lane 7 - i, which
+// holds the other quad's sum).  The pairing is that of xor-shuffles by 1, 2 and 4, so every lane of
+// the group gets the same, bit-identical sum.
+__device__ __forceinline__ float sum8(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // half mirror
+  return v;
+}
+// Sum over each aligned group of N lanes (N = 8 or 16 on the DPP network, the 16-lane step adding
+// the row mirror: lane i of a row reads lane 15 - i, the other half's sum; otherwise xor-shuffles),
+// with the pairing of xor-shuffles by 1, 2, 4, ... so every lane of a group holds the same sum.
+template <int N>
+__device__ __forceinline__ float sum_lanes(float v) {
+  if constexpr (N == 8) {
+    return sum8(v);
+  } else if constexpr (N == 16) {
+    v = sum8(v);
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row mirror
+  } else {
+#pragma unroll
+    for (int o = 1; o < N; o <<= 1) v += __shfl_xor(v, o, 64);
+    return v;
+  }
+}
 
 // Operand layout of the fp16 GEMMs ("fragment order").  An M x K operand (weights: N x K) is cut
 // into tiles of 16 rows x 32 columns; tile (g, s) holds 512 contiguous elements starting at

@@ -268,6 +268,11 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
   const half8 qh = *(const half8*)(qrow + h * 64);
   const half8 kh = *(const half8*)(qrow + (ls.H + hk) * 64);
   const half8 vh = *(const half8*)(qrow + (ls.H + ls.Hkv + hk) * 64);
+  // the rotary partners of this lane's dimensions (32 apart: lane g ^ 4 of the row's group of 8),
+  // loaded rather than exchanged between lanes
+  const int gp = 8 * ((g ^ 4) - g);
+  const half8 qph = *(const half8*)(qrow + h * 64 + gp);
+  const half8 kph = *(const half8*)(qrow + (ls.H + hk) * 64 + gp);
   // element offset of (cache row, KV head, entry 0, dimension 8g) in the local caches
   const size_t base = ((size_t)crow * ls.Hkv + hk) * ls.cap * 64 + 8 * g;
   half8 ch[8];  // cached keys 0..3, values 0..3 of the first group of four entries
@@ -316,10 +321,12 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
   const bool first = g < 4;  // dimensions [0, 32): rotated with -sin
   const bool live = r < M;
   f16* __restrict__ at = (f16*)lds;  // A tiles [RG][4 K steps][512]
-  float q[8], kn[8], vn[8];
+  float q[8], kn[8], vn[8], qpf[8], kpf[8];
   h8_to_f(qh, q);
   h8_to_f(kh, kn);
   h8_to_f(vh, vn);
+  h8_to_f(qph, qpf);
+  h8_to_f(kph, kpf);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float qp = __shfl_xor(q[e], 4, 64), kp = __shfl_xor(kn[e], 4, 64);
@@ -354,9 +361,7 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kv[e], dot);
-      dot += __shfl_xor(dot, 1, 64);
-      dot += __shfl_xor(dot, 2, 64);
-      dot += __shfl_xor(dot, 4, 64);
+      dot = sum8(dot);
       if (j0 + u < s0) {
         const float sc = dot * ls.scale_log2, mn = fmaxf(mrun, sc);
         const float corr = __builtin_amdgcn_exp2f(mrun - mn), p = __builtin_amdgcn_exp2f(sc - mn);
@@ -372,9 +377,7 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
     float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dot = fmaf(q[e], kn[e], dot);
-    dot += __shfl_xor(dot, 1, 64);
-    dot += __shfl_xor(dot, 2, 64);
-    dot += __shfl_xor(dot, 4, 64);
+    dot = sum8(dot);
     const float sc = dot * ls.scale_log2, mn = fmaxf(mrun, sc);
     const float corr = __builtin_amdgcn_exp2f(mrun - mn), p = __builtin_amdgcn_exp2f(sc - mn);
     lrun = lrun * corr + p;
@@ -410,9 +413,7 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf(xq[e], kk[e], dot);
-      dot += __shfl_xor(dot, 1, 64);
-      dot += __shfl_xor(dot, 2, 64);
-      dot += __shfl_xor(dot, 4, 64);
+      dot = sum8(dot);
       const float sc = dot * ls.scale_log2, mn = fmaxf(xm, sc);
       const float corr = __builtin_amdgcn_exp2f(xm - mn), pr = __builtin_amdgcn_exp2f(sc - mn);
       xl = xl * corr + pr;
