@@ -70,16 +70,6 @@ __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ f16 from_f32<f16>(float v) { return to_f16(v); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
 // Sum over each aligned group of 8 lanes on the DPP network (no LDS crossbar round trips): swap
 // neighbours, swap pairs, then add the half-row mirror (lane i of a group reads lane 7 - i, which
 // holds the other quad's sum).  The pairing is that of xor-shuffles by 1, 2 and 4, so every lane of
@@ -105,6 +95,50 @@ __device__ __forceinline__ float sum_lanes(float v) {
     for (int o = 1; o < N; o <<= 1) v += __shfl_xor(v, o, 64);
     return v;
   }
+}
+
+// One DPP move of a 32-bit value: lanes of the rows in ROWS read lane CTRL's source, the others
+// keep `old`.  0x142 / 0x143 broadcast lane 15 of each row to the next row / lane 31 to rows 2-3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+// Sum and maximum over the whole wave, in every lane: the 16-lane sums of sum_lanes, then row 1 adds
+// row 0's and row 3 row 2's, row 3 adds row 1's (rows 0-1), and lane 63 is broadcast.  The pairing
+// at every level is that of an xor butterfly, so the result does not depend on the lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum_lanes<16>(v);
+  v += __uint_as_float(dpp_u32<0x142, 0xA>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x143, 0x8>(0u, __float_as_uint(v)));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  v = fmaxf(v, __uint_as_float(dpp_u32<0xB1, 0xF>(u, u)));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x4E, 0xF>(__float_as_uint(v), __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x141, 0xF>(__float_as_uint(v), __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x140, 0xF>(__float_as_uint(v), __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x142, 0xA>(__float_as_uint(v), __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x143, 0x8>(__float_as_uint(v), __float_as_uint(v))));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+// Largest 64-bit key of the wave, in every lane (the same levels as wave_max on both halves).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_max_u64(unsigned long long v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const unsigned long long o = ((unsigned long long)dpp_u32<CTRL, ROWS>(hi, hi) << 32) | dpp_u32<CTRL, ROWS>(lo, lo);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = dpp_max_u64<0xB1, 0xF>(v);
+  v = dpp_max_u64<0x4E, 0xF>(v);
+  v = dpp_max_u64<0x141, 0xF>(v);
+  v = dpp_max_u64<0x140, 0xF>(v);
+  v = dpp_max_u64<0x142, 0xA>(v);
+  v = dpp_max_u64<0x143, 0x8>(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 // Operand layout of the fp16 GEMMs ("fragment order").  An M x K operand (weights: N x K) is cut

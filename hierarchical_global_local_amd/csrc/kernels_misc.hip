@@ -643,11 +643,7 @@ __global__ __launch_bounds__(256) void k_finalize(const unsigned long long* __re
 #pragma unroll
       for (int u = 0; u < 8; ++u) best = k[u] > best ? k[u] : best;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long k = shfl_xor_u64(best, o);
-      best = k > best ? k : best;
-    }
+    best = wave_max_u64(best);
     if ((tid & 63) == 0) red[tid >> 6] = best;
     __syncthreads();
     best = red[0];
