@@ -865,8 +865,7 @@ __global__ __launch_bounds__(256) void k_attn_decode_wave(const f16* __restrict_
     float cm = sv[0];
 #pragma unroll
     for (int u = 1; u < 8; ++u) cm = fmaxf(cm, sv[u]);
-#pragma unroll
-    for (int o = LPK; o < 64; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o, 64));
+    cm = wave_max(cm);  // (the lanes of a lane group hold the same value)
     const float mn = fmaxf(m, cm);  // finite: every step holds a cached key
     const float al = __builtin_amdgcn_exp2f(m - mn);
     m = mn;

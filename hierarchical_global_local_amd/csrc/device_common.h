@@ -130,6 +130,16 @@ __device__ __forceinline__ unsigned long long dpp_max_u64(unsigned long long v) 
   const unsigned long long o = ((unsigned long long)dpp_u32<CTRL, ROWS>(hi, hi) << 32) | dpp_u32<CTRL, ROWS>(lo, lo);
   return o > v ? o : v;
 }
+// Largest 64-bit key over each aligned group of N lanes (N = 2, 4, 8, 16), in every lane of it.
+template <int N>
+__device__ __forceinline__ unsigned long long max_lanes_u64(unsigned long long v) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "lane group");
+  v = dpp_max_u64<0xB1, 0xF>(v);
+  if constexpr (N >= 4) v = dpp_max_u64<0x4E, 0xF>(v);
+  if constexpr (N >= 8) v = dpp_max_u64<0x141, 0xF>(v);
+  if constexpr (N >= 16) v = dpp_max_u64<0x140, 0xF>(v);
+  return v;
+}
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
   v = dpp_max_u64<0xB1, 0xF>(v);
   v = dpp_max_u64<0x4E, 0xF>(v);

@@ -224,11 +224,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const f16* __restrict__ A1, c
             best = k > best ? k : best;
           }
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          unsigned long long other = shfl_xor_u64(best, o);
-          best = other > best ? other : best;
-        }
+        best = max_lanes_u64<16>(best);
         if ((lane & 15) == 0 && row < M) ep.keys[(size_t)row * ep.keys_ld + tn * WN + wn] = best;
       }
   } else if constexpr (MODE == EPI_RESID) {
@@ -387,11 +383,7 @@ __global__ __launch_bounds__(256, BN == 128 ? 2 : 1) void k_gemm_big(const f16* 
             best = k > best ? k : best;
           }
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const unsigned long long other = shfl_xor_u64(best, o);
-          best = other > best ? other : best;
-        }
+        best = max_lanes_u64<16>(best);
         if ((lane & 15) == 0 && row < M) ep.keys[(size_t)row * ep.keys_ld + tn * WN + wn] = best;
       }
     return;

@@ -169,11 +169,7 @@ __device__ __forceinline__ void skinny_tile(const f16* __restrict__ A1, const f1
         for (int e = 0; e < 8; ++e)
           if (col + e < ep.n_valid) o[col + e] = v[e];
       }
-#pragma unroll
-      for (int o = 1; o < CPR; o <<= 1) {
-        const unsigned long long other = shfl_xor_u64(best, o);
-        best = other > best ? other : best;
-      }
+      best = max_lanes_u64<CPR>(best);
       if (live && cl == 0) ep.keys[(size_t)row * ep.keys_ld + slab] = best;
     }
   }
