@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
   static_assert(NWAVE == 8 || NWAVE == 16, "8 or 16 waves");
   // (XA: a second set of A tiles holds the cross-attention outputs)
   constexpr int LDS_GEMM = skinny_lds_floats<MG, MW, NG, KW>(), LDS_A = RG * 4 * 256,
-                LDS_ATT = (XA ? 2 : 1) * LDS_A + 64;
+                LDS_ATT = (XA ? 2 : 1) * LDS_A + 64 * NWAVE;
   __shared__ __attribute__((aligned(16))) float lds[LDS_GEMM > LDS_ATT ? LDS_GEMM : LDS_ATT];
   const int n_hp = ls.H / 2;
   // Workgroup id -> tile.  Workgroup ids x, x + 8, ... run on XCD x.  Attention group a = (rb, hp)
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
   const int G = ls.H / ls.Hkv, s0 = ls.s0, h = 2 * hp + it, hk = h / G;
   const int crow = ls.rmap ? ls.rmap[rc] : rc;
   // Loads in the order they are consumed (a wait for one load is a wait for every earlier one):
-  // q | k | v, the cached entries, the rotary row (one float per thread of the first wave), then
+  // q | k | v, the cached entries, the rotary row (one float per lane of every wave), then
   // the weight tiles, which only the MFMAs at the end need.
   const f16* __restrict__ qrow = ls.qkv + (size_t)rc * ls.ldq + 8 * g;
   const half8 qh = *(const half8*)(qrow + h * 64);
@@ -278,8 +278,7 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
     ch[u] = *(const half8*)(ls.kc + base + (size_t)j * 64);
     ch[4 + u] = *(const half8*)(ls.vc + base + (size_t)j * 64);
   }
-  float rv = 0.f;
-  if (threadIdx.x < 64) rv = ((const float*)(ls.rope + (size_t)s0 * 32))[threadIdx.x];
+  const float rv = ((const float*)(ls.rope + (size_t)s0 * 32))[lane];
   // cross-attention operands: this lane's 8 dimensions of the query and, where the register
   // budget allows (8 waves: 256 registers a lane), of the first encoder state's key and value
   // (fp32) and the cross-attention weight tiles, issued with the rest
@@ -305,9 +304,10 @@ __global__ __launch_bounds__(64 * MW * KW) void k_attn_out(const f16* __restrict
   for (int ks = 0; ks < 4; ++ks) rw[ks] = *(const half8*)(W + (((size_t)ng * KS + 4 * hp + ks) * 64 + lane) * 8);
   if constexpr (XE) load_rwx();
   __builtin_amdgcn_sched_barrier(0);
-  float* __restrict__ rope_s = lds + (XA ? 2 : 1) * LDS_A;
-  if (threadIdx.x < 64) rope_s[threadIdx.x] = rv;
-  __syncthreads();
+  // each wave stages the rotary row in its own LDS slice (a wave's LDS accesses complete in order,
+  // so no barrier: C1 decode 20.84 -> 20.76 ms against one staging for the workgroup)
+  float* __restrict__ rope_s = lds + (XA ? 2 : 1) * LDS_A + 64 * wave;
+  rope_s[lane] = rv;
   float cs[8], sn[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
