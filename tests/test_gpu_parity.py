@@ -353,6 +353,14 @@ def test_host_side_errors():
     with pytest.raises(hg.BtError) as e:
         model.prefill(torch.zeros((1, 16), dtype=torch.int32, device="cuda"))
     assert e.value.code == -2
+    # empty inputs: no rows, or rows without a token, are argument errors (nothing is queued)
+    for shape in ((0, 8), (2, 0)):
+        with pytest.raises(hg.BtError) as e:
+            model.prefill(torch.zeros(shape, dtype=torch.int32, device="cuda"))
+        assert e.value.code == -1
+    with pytest.raises(hg.BtError) as e:
+        model.decode_step(out=torch.empty(2, dtype=torch.int32, device="cuda"))
+    assert e.value.code == -3   # still no prefill
     short = hg.BlockTransformer(cfg, W, max_batch=2, max_tokens=16, max_prompt_tokens=8)
     with pytest.raises(hg.BtError) as e:
         short.prefill(torch.zeros((2, 9), dtype=torch.int32, device="cuda"))   # padded to 12 > 8
