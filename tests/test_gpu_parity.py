@@ -42,7 +42,11 @@ def test_c0_tiny_fp32_full():
                                       (dict(block_len=2, prefix_len=2), 3, 11, 10),
                                       (dict(block_len=8, prefix_len=2), 2, 19, 18),
                                       (dict(d_model=128, n_heads=2), 2, 8, 9),
-                                      (dict(d_model=256, n_heads=2, d_mlp=320), 2, 12, 6)])
+                                      (dict(d_model=256, n_heads=2, d_mlp=320), 2, 12, 6),
+                                      # degenerate sizes: one row, a one-token prompt (one block, all
+                                      # but its last slot padding), no decode step or a few
+                                      (dict(), 1, 1, 1), (dict(), 1, 1, 9),
+                                      (dict(block_len=8, prefix_len=2), 1, 1, 3)])
 def test_fp32_variants(kw, B, T, G):
     _fp32_case(wl.get_config("c0_tiny", **kw), B, T, G, seed=1)
 
@@ -117,7 +121,7 @@ def test_bf16_grouped_query_attention(kw, max_tokens):
 
 @pytest.mark.parametrize("kw,max_tokens", [(dict(), None), (dict(d_model=256, n_heads=2), None),
                                            (dict(block_len=1, prefix_len=1), None), (dict(block_len=8, prefix_len=2), None),
-                                           (dict(), 4096)])
+                                           (dict(), 4096), (dict(batch=1, prompt_len=1, gen_len=9), None)])
 def test_bf16_small_every_step(kw, max_tokens):
     """max_tokens=4096 gives the block attention several key splits, most of them still empty."""
     cfg = SMALL_BF16.with_(**kw)
